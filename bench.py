@@ -1,0 +1,291 @@
+"""Benchmark of the paged KV-cache hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Workload: the decode batch -- 32 sequences, seq_len ~ U[128, 2048], block
+size 16, a 16384-block 32-layer bf16 pool (16 GiB each for K and V), 8 kv
+heads, head_dim 128, 32 query heads.  One step is one decode step of the
+serving loop, all on the device: the slot of every sequence's new token
+(kv_slot_mapping), the scatter of its K/V row into the pool (kv_scatter),
+and fused paged decode attention over every cached token (paged_attn_decode).
+Step i works on layer i % 32 with the same tables, so consecutive steps read
+disjoint memory (4.5 GB per 32-step cycle) and the 256 MB last-level cache
+cannot serve repeats.
+
+Printed: one JSON line.  `value` is decode-attention KV bytes per second of
+whole-step time.  `roofline` describes the decode call (its partial and
+merge kernels, timed together with HIP events on the launch stream).
+`cpu_baseline` times the CPU oracle on the same decode batch.  `ops` reports
+the scatter and gather rates on the prefill shape (8 x 1024 rows, 10%
+padding) for reference.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "paged decode-attn KV GB/s & % HBM peak; scatter/gather GB/s"
+HBM_PEAK_GBS = 8000.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def decode_bytes(w, lens):
+    """Algorithmic bytes of one decode call: every cached K and V element
+    once, q and out once, the used block-table entries, lengths, offsets."""
+    e = w.k_pool.element_size()
+    kv = int(lens.sum()) * w.num_kv_heads * w.head_dim * e * 2
+    qo = 2 * w.num_seqs * w.num_q_heads * w.head_dim * e
+    offs = w.offsets.cpu().numpy().astype("int64")
+    tables = int(((offs + lens.astype("int64") + w.block_size - 1) // w.block_size).sum()) * 4
+    return kv, kv + qo + tables + 8 * w.num_seqs
+
+
+def time_op(fn, reps, layers, warm=3):
+    """Median and mean of per-call HIP-event times (ms) of fn(layer), with
+    the layer rotated so repeats touch different memory."""
+    import torch
+
+    for i in range(warm):
+        fn(layers[i % len(layers)])
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    for i in range(reps):
+        starts[i].record()
+        fn(layers[i % len(layers)])
+        ends[i].record()
+    torch.cuda.synchronize()
+    ts = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    return ts[len(ts) // 2], sum(ts) / len(ts)
+
+
+def cpu_baseline(w, lens):
+    """The CPU oracle on the same decode batch (layer 0); host copies of the
+    referenced blocks are made before the clock starts."""
+    import numpy as np
+    import torch
+
+    import oracle as O
+
+    bt = w.block_tables.cpu()
+    ids = torch.unique(bt[bt >= 0]).to(torch.int64)
+    dev_ids = ids.to(w.k_pool.device)
+
+    def host(t):
+        t = t.contiguous().cpu()
+        return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+
+    k_c = host(w.k_pool[:, 0].index_select(0, dev_ids).unsqueeze(1))
+    v_c = host(w.v_pool[:, 0].index_select(0, dev_ids).unsqueeze(1))
+    pos = torch.searchsorted(ids, bt.clamp(min=0).to(torch.int64)).to(torch.int32)
+    bt_c = torch.where(bt >= 0, pos, torch.full_like(pos, -1)).numpy()
+    threads = max(1, min(16, os.cpu_count() or 1))
+    args = (k_c, v_c, 0, host(w.q), bt_c, host(w.seq_lens), host(w.offsets), w.scale)
+    t0 = time.perf_counter()
+    O.decode(*args, num_threads=threads)
+    dt = time.perf_counter() - t0
+    kv, _ = decode_bytes(w, lens)
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": kv / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"one full decode step of the {w.num_seqs}-sequence batch at layer 0 "
+                      f"({int(lens.sum())} cached tokens), float64 gather-then-attention, "
+                      f"{dt:.2f} s wall",
+            "seconds": dt, "host_cpu": model, "host_cpus_visible": os.cpu_count()}
+
+
+def prefill_ops(w_dec, N, W):
+    """Scatter and gather rates on the prefill shape, run in the decode
+    batch's pool (same shape: 16384 x 32 x 16 x 8 x 128 bf16)."""
+    import torch
+
+    pf = W.prefill(device=w_dec.k_pool.device, with_pools=False)
+    slots = N.kv_slot_mapping(pf.block_tables, pf.offsets, pf.token_seq, pf.token_pos,
+                              pf.block_size)
+    valid = int((pf.token_seq >= 0).sum())
+    rows = pf.k_new.shape[0]
+    row = pf.row_bytes
+    layers = list(range(w_dec.num_layers))
+    scat_bytes = valid * row * 2 * 2 + rows * 8
+    t_s, _ = time_op(lambda l: N.kv_scatter(w_dec.k_pool, w_dec.v_pool, l, pf.k_new, pf.v_new,
+                                            slots), 64, layers)
+    total = int(pf.seq_lens.sum())
+    k_out = torch.empty((total, pf.num_kv_heads, pf.head_dim), dtype=pf.dtype,
+                        device=pf.k_new.device)
+    v_out = torch.empty_like(k_out)
+    starts = torch.cumsum(pf.seq_lens.to(torch.int64), 0) - pf.seq_lens.to(torch.int64)
+    mx = pf.max_seq_len
+    gath_bytes = total * row * 2 * 2
+    t_g, _ = time_op(lambda l: N.kv_gather(w_dec.k_pool, w_dec.v_pool, l, pf.block_tables,
+                                           pf.seq_lens, pf.offsets, starts, mx, k_out, v_out),
+                     64, layers)
+    return {
+        "scatter_prefill": {"rows": rows, "valid_rows": valid, "bytes": scat_bytes,
+                            "ms": t_s, "GB/s": scat_bytes / t_s / 1e6},
+        "gather_prefill": {"rows": total, "bytes": gath_bytes, "ms": t_g,
+                           "GB/s": gath_bytes / t_g / 1e6},
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ops", action="store_true")
+    ap.add_argument("--split-tokens", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the hot path "
+              "shards by sequence or kv head with no exchange, so there is no multi-GPU "
+              "measurement to make here", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np  # noqa: F401
+    import torch
+
+    from paged_attention_decode_scatter_amd import native as N
+    from paged_attention_decode_scatter_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    N.load_library()
+    log("building the decode-batch workload (2 x 16 GiB pools)")
+    w = W.decode_tokens(W.decode_batch(device=dev))
+    lens = w.seq_lens.cpu().numpy()
+    mx = w.max_seq_len
+    kv_bytes, alg_bytes = decode_bytes(w, lens)
+    split = args.split_tokens or N.paged_attn_decode_split_tokens(w.num_seqs, w.num_kv_heads, mx,
+                                                                  w.block_size)
+    ws_bytes = N.paged_attn_decode_workspace_size(w.num_seqs, w.num_kv_heads, w.num_q_heads,
+                                                  w.head_dim, mx, w.block_size, split)
+    workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(w.q)
+    slots = torch.empty(w.token_seq.shape[0], dtype=torch.int64, device=dev)
+    dec_start = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    dec_end = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+
+    # The step issues the three C-ABI calls with arguments marshalled once
+    # up front (same values the binding would pass), so host-side Python
+    # does not starve the ~30 us device step.
+    import ctypes
+
+    lib = N.load_library()
+    pool = N.make_pool(w.k_pool, w.v_pool)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    slot_args = (P(w.block_tables), w.block_tables.shape[1], P(w.offsets), w.num_seqs,
+                 P(w.token_seq), P(w.token_pos), w.token_seq.shape[0], w.block_size, P(slots),
+                 stream)
+    scat_args = [(ctypes.byref(pool), l, P(w.k_new), P(w.v_new), P(slots), slots.shape[0], stream)
+                 for l in range(w.num_layers)]
+    dec_args = [(ctypes.byref(pool), l, P(w.q), w.num_q_heads, P(w.block_tables),
+                 w.block_tables.shape[1], P(w.seq_lens), P(w.offsets), w.num_seqs, mx,
+                 ctypes.c_float(w.scale), split, P(out), P(workspace), workspace.numel(), stream)
+                for l in range(w.num_layers)]
+    f_slot, f_scat, f_dec = lib.kv_slot_mapping, lib.kv_scatter, lib.paged_attn_decode
+
+    def step(i, timed=False):
+        layer = i % w.num_layers
+        rc = f_slot(*slot_args) | f_scat(*scat_args[layer])
+        if timed:
+            dec_start[i].record()
+        rc |= f_dec(*dec_args[layer])
+        if timed:
+            dec_end[i].record()
+        if rc:
+            raise RuntimeError(f"a library call failed in step {i}")
+
+    log(f"warmup {args.warmup} steps (split_tokens={split}, workspace={ws_bytes} B)")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(args.steps):
+        step(i, timed=True)
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / args.steps
+    dec_ms = [s.elapsed_time(e) for s, e in zip(dec_start, dec_end)]
+    dec_avg = sum(dec_ms) / len(dec_ms)
+    dec_med = sorted(dec_ms)[len(dec_ms) // 2]
+    achieved = alg_bytes / (dec_avg * 1e-3) / 1e9
+    log(f"step {ms_step * 1e3:.1f} us, decode avg {dec_avg * 1e3:.1f} us "
+        f"(median {dec_med * 1e3:.1f} us), {achieved:.0f} GB/s")
+
+    result = {
+        "metric": METRIC,
+        "value": kv_bytes / (ms_step * 1e-3) / 1e9,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "decode_batch",
+            "num_seqs": w.num_seqs,
+            "seq_len": "U[128,2048]",
+            "cached_tokens": int(lens.sum()),
+            "block_size": w.block_size,
+            "pool_blocks": w.num_blocks,
+            "num_layers": w.num_layers,
+            "num_kv_heads": w.num_kv_heads,
+            "head_dim": w.head_dim,
+            "num_q_heads": w.num_q_heads,
+            "split_tokens": split,
+            "kv_bytes_per_step": kv_bytes,
+            "step": "kv_slot_mapping + kv_scatter (1 new token/seq) + paged_attn_decode, "
+                    "layer rotated over 32",
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "kernel": "paged_attn_decode (decode_kernel + reduce_kernel)",
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": None,
+            "algorithmic_bytes_per_launch": alg_bytes,
+            "avg_launch_us": dec_avg * 1e3,
+            "median_launch_us": dec_med * 1e3,
+        },
+    }
+    if not args.no_ops:
+        log("scatter/gather on the prefill shape")
+        result["ops"] = prefill_ops(w, N, W)
+    if not args.no_cpu_baseline:
+        log("CPU oracle baseline")
+        result["cpu_baseline"] = cpu_baseline(w, lens)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,246 @@
+/*
+ * pagedkv.h -- C ABI of the MI355X (gfx950) paged KV-cache library
+ * (libpagedkv.so).
+ *
+ * The library implements block-table-indirected access to a paged KV cache:
+ * the slot computation, the slot_mapping scatter of new K/V rows into the
+ * pool, the block_table gather into contiguous K/V, and fused paged decode
+ * attention that reads the scattered blocks in place.
+ *
+ * Sources (three web pages on paged KV caches):
+ *   [P1] mini-vllm tutorial, "step14_2 - index_select gather"
+ *   [P2] "vLLM PagedAttention source notes" (minivLLM Task 6 background)
+ *   [P3] mini-runtime, chapter 12 "Paged KV Cache"
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pool layout [P2 sec. 2.2]: K and V are separate, each a contiguous
+ *   (num_blocks, num_layers, block_size, num_kv_heads, head_dim) array in
+ *   device memory.  One "row" is the num_kv_heads*head_dim elements of one
+ *   token at one layer.  block_size must be a power of two.
+ * - Element types: PKV_F32 (float) or PKV_BF16 (bfloat16 bit patterns).
+ * - A block table is a row of int32 physical block ids in logical order
+ *   [P3 sec. 2.2]; tables are stored (num_seqs, bt_stride) row-major.  Each
+ *   sequence also has a first-block start offset in [0, block_size) (prefix
+ *   sharing creates it [P3 sec. 2.2]): logical token t of the sequence sits
+ *   at flat position offset + t of its table, i.e. in block
+ *   table[(offset+t) / block_size] at slot (offset+t) % block_size.
+ *   A table holds len*block_size - offset tokens [P3 sec. 2.2].
+ * - Pointers named "device" are device memory owned by the caller; the
+ *   library allocates and frees nothing, keeps no per-call state and never
+ *   synchronises (except where stated).  All work is enqueued on `stream`
+ *   (a hipStream_t; NULL = the default stream); the return value covers
+ *   argument checks and the launch only.
+ * - Every base pointer that the kernels read or write in 16-byte pieces
+ *   (pools, q, K/V sources and outputs, workspace) must be 16-byte aligned,
+ *   and a row (num_kv_heads*head_dim*element size) must be a multiple of 16
+ *   bytes; otherwise PKV_ERR_ALIGN.
+ * - Arguments are checked on the host before any HIP call; a failed check
+ *   returns a negative status and enqueues nothing.  No exception or abort
+ *   crosses this ABI.
+ * - Device-resident ids are not range-checked by the fast entry points'
+ *   contract.  For safety the kernels still never touch memory outside the
+ *   pool, the tables or the outputs: a slot or block id that is out of range
+ *   is treated as padding (scatter skips the row, gather writes a zero row,
+ *   decode masks the token).  kv_validate counts such violations.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_API __attribute__((visibility("default")))
+
+/* element types */
+enum { PKV_F32 = 0, PKV_BF16 = 1 };
+
+/* status codes */
+enum {
+    PKV_OK = 0,
+    PKV_ERR_NULL = -1,        /* a required pointer is NULL                    */
+    PKV_ERR_DTYPE = -2,       /* unknown element type                          */
+    PKV_ERR_SHAPE = -3,       /* negative/zero size, non power-of-two block    */
+                              /* size, num_q_heads % num_kv_heads != 0, ...    */
+    PKV_ERR_LAYER = -4,       /* layer outside [0, num_layers)                 */
+    PKV_ERR_ALIGN = -5,       /* pointer or row not 16-byte aligned            */
+    PKV_ERR_WORKSPACE = -6,   /* workspace missing or smaller than required    */
+    PKV_ERR_LAUNCH = -7,      /* the HIP launch reported an error              */
+    PKV_ERR_UNSUPPORTED = -8, /* head_dim / query-group size not compiled in   */
+    PKV_ERR_DEVICE = -9       /* no usable HIP device                          */
+};
+
+/* A paged KV pool: caller-owned device memory, only read or written during
+ * a call.  dtype is PKV_F32 or PKV_BF16; `reserved` must be 0. */
+typedef struct pkv_pool {
+    void *k;
+    void *v;
+    int64_t num_blocks;
+    int64_t num_layers;
+    int64_t block_size;
+    int64_t num_kv_heads;
+    int64_t head_dim;
+    int32_t dtype;
+    int32_t reserved;
+} pkv_pool;
+
+/*
+ * kv_slot_mapping -- the slot of every new token [P2 sec. 2.2: slot =
+ * block_table[block index] * block_size + position inside the block, int64,
+ * -1 = padding], with the first-block offset of [P3 sec. 2.2].
+ *
+ *   block_tables  device int32 [num_seqs, bt_stride]
+ *   offsets       device int32 [num_seqs]
+ *   token_seq     device int32 [num_tokens]: sequence of token i, or -1 for
+ *                 a padding row
+ *   token_pos     device int32 [num_tokens]: logical position of token i in
+ *                 its sequence
+ *   slot_mapping  device int64 [num_tokens], written:
+ *                 table[seq][(off+pos)/bs]*bs + (off+pos)%bs, or -1 for a
+ *                 padding row or a position outside the table
+ * Errors: PKV_ERR_NULL, PKV_ERR_SHAPE (sizes < 0, block_size not a power of
+ * two), PKV_ERR_LAUNCH.  num_tokens == 0 enqueues nothing.
+ */
+PKV_API int kv_slot_mapping(const int32_t *block_tables, int32_t bt_stride,
+                            const int32_t *offsets, int32_t num_seqs,
+                            const int32_t *token_seq, const int32_t *token_pos,
+                            int64_t num_tokens, int32_t block_size,
+                            int64_t *slot_mapping, void *stream);
+
+/*
+ * kv_scatter -- write new K/V rows into the pool at `layer`
+ * [P1 "relation to step14_1": kv_pool[blocks, slots] = K; P2 sec. 2.2:
+ * writes indexed (block_id, layer, offset inside block), slot -1 = padding].
+ *
+ *   k_src, v_src  device [num_tokens, num_kv_heads, head_dim], pool dtype,
+ *                 contiguous.  v_src may be NULL to write K only (then the
+ *                 pool's v may be NULL too).
+ *   slot_mapping  device int64 [num_tokens]; row i goes to block slot/bs,
+ *                 slot slot%bs.  Negative or out-of-pool slots are skipped.
+ * Only the addressed rows of `layer` are written; every other byte of the
+ * pool is left as it was.  Duplicate slots are a caller error (the row that
+ * lands last is unspecified).
+ * Errors: PKV_ERR_NULL, _DTYPE, _SHAPE, _LAYER, _ALIGN, _LAUNCH.
+ */
+PKV_API int kv_scatter(const pkv_pool *pool, int32_t layer,
+                       const void *k_src, const void *v_src,
+                       const int64_t *slot_mapping, int64_t num_tokens,
+                       void *stream);
+
+/*
+ * kv_gather -- contiguous K/V of each sequence from its block table
+ * [P1 "Problem" and "Solution": pool[table[pos/bs], pos%bs] -> (seq_len,
+ * num_heads, head_dim); P3 sec. 2.2: reads start at the first-block offset].
+ *
+ *   block_tables   device int32 [num_seqs, bt_stride]
+ *   seq_lens       device int32 [num_seqs]
+ *   offsets        device int32 [num_seqs], each in [0, block_size)
+ *   out_row_start  device int64 [num_seqs]: first output row of each
+ *                  sequence (rows of different sequences must not overlap)
+ *   max_seq_len    host bound on every seq_len (sizes the grid)
+ *   k_out, v_out   device [out_rows, num_kv_heads, head_dim]; row
+ *                  out_row_start[s] + t receives logical token t of s.
+ *                  v_out may be NULL to gather K only.
+ *   out_rows       rows k_out (and v_out) can hold; a row that would land
+ *                  outside [0, out_rows) is not written.
+ * A token whose table entry is missing or out of range reads as a zero row.
+ * Errors: PKV_ERR_NULL, _DTYPE, _SHAPE, _LAYER, _ALIGN, _LAUNCH.
+ */
+PKV_API int kv_gather(const pkv_pool *pool, int32_t layer,
+                      const int32_t *block_tables, int32_t bt_stride,
+                      const int32_t *seq_lens, const int32_t *offsets,
+                      const int64_t *out_row_start, int32_t num_seqs,
+                      int32_t max_seq_len, void *k_out, void *v_out,
+                      int64_t out_rows, void *stream);
+
+/*
+ * paged_attn_decode_split_tokens -- the split size (tokens per work item)
+ * that paged_attn_decode uses when called with split_tokens = 0.  Depends
+ * on the sizes and on the current device's compute-unit count (256 is
+ * assumed when no device can be queried).  Returns a positive multiple of
+ * 16, or a negative status for bad sizes.
+ */
+PKV_API int32_t paged_attn_decode_split_tokens(int32_t num_seqs, int32_t num_kv_heads,
+                                               int32_t max_seq_len, int32_t block_size);
+
+/*
+ * paged_attn_decode_workspace_size -- bytes of device workspace that
+ * paged_attn_decode needs for these sizes and this split_tokens (0 = the
+ * automatic choice above).  0 means no workspace is needed (every sequence
+ * fits one split).  Returns (size_t)-1 for bad sizes.
+ */
+PKV_API size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_kv_heads,
+                                                int32_t num_q_heads, int32_t head_dim,
+                                                int32_t max_seq_len, int32_t block_size,
+                                                int32_t split_tokens);
+
+/*
+ * paged_attn_decode -- one decode step of attention for every sequence,
+ * reading K/V in place through the block tables (the fused paged kernel of
+ * [P1 "comparison with vLLM"; P3 sec. 3.1]: the result of gather followed
+ * by standard attention [P2 sec. 2.3], without the gathered copy).
+ *
+ * For sequence s and query head h, with G = num_q_heads/num_kv_heads and kv
+ * head g = h / G (contiguous query-head groups):
+ *   out[s,h,:] = softmax_t(scale * q[s,h,:] . K_t[g,:]) . V_t[g,:]
+ * over the seq_lens[s] logical tokens t (no causal mask: the one query sees
+ * every cached token).  Accumulation is fp32; out is rounded (nearest-even)
+ * to the pool dtype.  A sequence of length 0 gives zeros.
+ *
+ *   q             device [num_seqs, num_q_heads, head_dim], pool dtype
+ *   block_tables, seq_lens, offsets  as for kv_gather
+ *   max_seq_len   host bound on every seq_len
+ *   scale         softmax scale (e.g. 1/sqrt(head_dim))
+ *   split_tokens  tokens per split-K work item: 0 = automatic, else a
+ *                 positive multiple of 16 with split_tokens/block_size + 2
+ *                 <= 1024.  Sequences longer than one split are processed as
+ *                 independent partial softmaxes merged by a second pass
+ *                 (log-sum-exp); the partition and merge order are fixed, so
+ *                 results are bitwise reproducible run to run.
+ *   out           device [num_seqs, num_q_heads, head_dim], pool dtype
+ *   workspace     device scratch of at least
+ *                 paged_attn_decode_workspace_size(...) bytes (may be NULL
+ *                 when that size is 0); overwritten.
+ * Supported: head_dim in {64, 128}, G in {1, 2, 4, 8}.
+ * Errors: PKV_ERR_NULL, _DTYPE, _SHAPE, _LAYER, _ALIGN, _WORKSPACE,
+ * _UNSUPPORTED, _LAUNCH.
+ */
+PKV_API int paged_attn_decode(const pkv_pool *pool, int32_t layer,
+                              const void *q, int32_t num_q_heads,
+                              const int32_t *block_tables, int32_t bt_stride,
+                              const int32_t *seq_lens, const int32_t *offsets,
+                              int32_t num_seqs, int32_t max_seq_len, float scale,
+                              int32_t split_tokens, void *out,
+                              void *workspace, size_t workspace_bytes,
+                              void *stream);
+
+/*
+ * kv_validate -- count violations of the caller contract, for debugging:
+ * offsets outside [0, block_size); seq_len < 0, > max_seq_len (when
+ * max_seq_len >= 0) or > the table's capacity bt_stride*block_size - offset
+ * [P3 sec. 2.2]; block ids outside [0, num_blocks) among the entries a
+ * sequence uses; slots that are neither -1 nor inside the pool
+ * [P2 sec. 2.2].  Tables or slot_mapping may be NULL (with num_seqs or
+ * num_tokens 0) to skip that part.
+ *   violations  device int64 [1]: zeroed, then incremented by the kernels
+ *               (asynchronous; read it after the stream completes).
+ * Errors: PKV_ERR_NULL, _SHAPE, _LAUNCH.
+ */
+PKV_API int kv_validate(const pkv_pool *pool, const int32_t *block_tables,
+                        int32_t bt_stride, const int32_t *seq_lens,
+                        const int32_t *offsets, int32_t num_seqs,
+                        int32_t max_seq_len, const int64_t *slot_mapping,
+                        int64_t num_tokens, int64_t *violations, void *stream);
+
+/* pkv_status_string -- static text for a status code (never NULL). */
+PKV_API const char *pkv_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

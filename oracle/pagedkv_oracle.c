@@ -170,8 +170,8 @@ int64_t orc_gather(const uint8_t *pool, int64_t num_blocks, int64_t num_layers,
  * in double.  A sequence of length 0 yields zeros.
  * q: (num_seqs, num_q_heads, head_dim) in the pool dtype.
  * out: (num_seqs, num_q_heads, head_dim) double.
- * The (s, h) outputs are independent; `num_threads` worker threads each
- * take whole (s, h) items, so threading changes no arithmetic.
+ * The (s, g) work items are independent; `num_threads` worker threads each
+ * take whole items, so threading changes no arithmetic.
  * Returns 0, or -1 on bad arguments.
  * ---------------------------------------------------------------------- */
 typedef struct {
@@ -192,15 +192,17 @@ typedef struct {
     int failed;
 } decode_job;
 
-static int decode_one(decode_job *J, int64_t s, int64_t h) {
+/* One work item: sequence s and kv head g.  The sequence is gathered once,
+ * then every query head of group g (h = g*G .. g*G+G-1, i.e. h / G == g)
+ * attends over it. */
+static int decode_group(decode_job *J, int64_t s, int64_t g) {
     const int64_t D = J->head_dim;
     const int64_t e = elem_size(J->dtype);
     const int64_t row_bytes = J->num_kv_heads * D * e;
     const int64_t G = J->num_q_heads / J->num_kv_heads;
-    const int64_t g = h / G;
-    double *o = J->out + (s * J->num_q_heads + h) * D;
     const int64_t L = J->seq_lens[s];
-    for (int64_t d = 0; d < D; d++) o[d] = 0.0;
+    for (int64_t h = g * G; h < (g + 1) * G; h++)
+        for (int64_t d = 0; d < D; d++) J->out[(s * J->num_q_heads + h) * D + d] = 0.0;
     if (L == 0) return 0;
 
     /* gather the whole sequence (all kv heads) with the definition above */
@@ -220,25 +222,28 @@ static int decode_one(decode_job *J, int64_t s, int64_t h) {
         goto done;
     }
 
-    const uint8_t *qh = J->q + (s * J->num_q_heads + h) * D * e;
-    double mx = -INFINITY;
-    for (int64_t t = 0; t < L; t++) {
-        const uint8_t *kt = krows + t * row_bytes + g * D * e;
-        double dot = 0.0;
-        for (int64_t d = 0; d < D; d++)
-            dot += load_elem(qh + d * e, J->dtype) * load_elem(kt + d * e, J->dtype);
-        score[t] = J->scale * dot;
-        if (score[t] > mx) mx = score[t];
+    for (int64_t h = g * G; h < (g + 1) * G; h++) {
+        const uint8_t *qh = J->q + (s * J->num_q_heads + h) * D * e;
+        double *o = J->out + (s * J->num_q_heads + h) * D;
+        double mx = -INFINITY;
+        for (int64_t t = 0; t < L; t++) {
+            const uint8_t *kt = krows + t * row_bytes + g * D * e;
+            double dot = 0.0;
+            for (int64_t d = 0; d < D; d++)
+                dot += load_elem(qh + d * e, J->dtype) * load_elem(kt + d * e, J->dtype);
+            score[t] = J->scale * dot;
+            if (score[t] > mx) mx = score[t];
+        }
+        double den = 0.0;
+        for (int64_t d = 0; d < D; d++) num[d] = 0.0;
+        for (int64_t t = 0; t < L; t++) {
+            double w = exp(score[t] - mx);
+            den += w;
+            const uint8_t *vt = vrows + t * row_bytes + g * D * e;
+            for (int64_t d = 0; d < D; d++) num[d] += w * load_elem(vt + d * e, J->dtype);
+        }
+        for (int64_t d = 0; d < D; d++) o[d] = num[d] / den;
     }
-    double den = 0.0;
-    for (int64_t d = 0; d < D; d++) num[d] = 0.0;
-    for (int64_t t = 0; t < L; t++) {
-        double w = exp(score[t] - mx);
-        den += w;
-        const uint8_t *vt = vrows + t * row_bytes + g * D * e;
-        for (int64_t d = 0; d < D; d++) num[d] += w * load_elem(vt + d * e, J->dtype);
-    }
-    for (int64_t d = 0; d < D; d++) o[d] = num[d] / den;
 
 done:
     free(krows);
@@ -250,13 +255,13 @@ done:
 
 static void *decode_worker(void *arg) {
     decode_job *J = (decode_job *)arg;
-    const int64_t total = J->num_seqs * J->num_q_heads;
+    const int64_t total = J->num_seqs * J->num_kv_heads;
     for (;;) {
         pthread_mutex_lock(&J->lock);
         int64_t item = J->next_item++;
         pthread_mutex_unlock(&J->lock);
         if (item >= total) break;
-        if (decode_one(J, item / J->num_q_heads, item % J->num_q_heads) != 0) {
+        if (decode_group(J, item / J->num_kv_heads, item % J->num_kv_heads) != 0) {
             pthread_mutex_lock(&J->lock);
             J->failed = 1;
             pthread_mutex_unlock(&J->lock);

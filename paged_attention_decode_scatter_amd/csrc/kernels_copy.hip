@@ -1,0 +1,255 @@
+// kernels_copy.hip -- integer-index kernels for gfx950: slot computation,
+// slot_mapping scatter, block_table gather, contract validation.
+//
+// Sources:
+//   [P1] mini-vllm tutorial, "step14_2 - index_select gather"
+//   [P2] "vLLM PagedAttention source notes"
+//   [P3] mini-runtime, chapter 12 "Paged KV Cache"
+//
+// Scatter and gather are pure byte moves: every lane moves whole 16-byte
+// pieces of a row (global_load/store_dwordx4), consecutive lanes cover
+// consecutive pieces of a row, so each wavefront instruction touches full
+// 128-byte lines.  Several pieces are loaded before any is stored to keep
+// enough bytes in flight per CU for HBM.
+#include "pkv_internal.h"
+
+namespace pkv {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x4 ld16(const char *p) {
+    return *reinterpret_cast<const u32x4 *>(p);
+}
+__device__ __forceinline__ u32x4 ld16_stream(const char *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
+__device__ __forceinline__ void st16(char *p, u32x4 v) {
+    *reinterpret_cast<u32x4 *>(p) = v;
+}
+
+// Unroll depth of the copy loops (16-byte pieces per tensor in flight per
+// lane before the first store).
+constexpr int kUnroll = 4;
+
+// ---------------------------------------------------------------------------
+// Slot of each new token: table[seq][(off+pos) >> lbs] << lbs | (off+pos) & bsm
+// [P2 sec. 2.2 slot formula; P3 sec. 2.2 first-block offset].
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void slot_mapping_kernel(SlotArgs a) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= a.num_tokens) return;
+    const int32_t seq = a.token_seq[i];
+    int64_t slot = -1;
+    if (seq >= 0 && seq < a.num_seqs) {
+        const int64_t pos = a.token_pos[i];
+        const int64_t p = (int64_t)a.offsets[seq] + pos;
+        const int64_t j = p >> a.lbs;
+        if (pos >= 0 && p >= 0 && j < a.bt_stride) {
+            const int32_t b = a.block_tables[(int64_t)seq * a.bt_stride + j];
+            if (b >= 0) slot = ((int64_t)b << a.lbs) | (p & ((1 << a.lbs) - 1));
+        }
+    }
+    a.slots[i] = slot;
+}
+
+hipError_t launch_slot_mapping(const SlotArgs &a, hipStream_t s) {
+    const int64_t blocks = (a.num_tokens + 255) / 256;
+    hipLaunchKernelGGL(slot_mapping_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Scatter [P1 "relation to step14_1"; P2 sec. 2.2]: row i of k_src/v_src ->
+// pool row (slot >> lbs, layer, slot & bsm).  A workgroup moves tok_per_wg
+// consecutive rows; piece idx of the workgroup is (row idx / cpr, piece
+// idx % cpr) so a wavefront's lanes cover consecutive pieces of a row.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kCopyThreads) void scatter_kernel(ScatterArgs a) {
+    const int64_t tok0 = (int64_t)blockIdx.x * a.tok_per_wg;
+    const int64_t left = a.num_tokens - tok0;
+    const int ntok = left < a.tok_per_wg ? (int)left : a.tok_per_wg;
+    const int cpr = a.row_bytes >> 4;
+    const int n = ntok * cpr;
+    const int64_t bsm = (1ll << a.lbs) - 1;
+    const bool has_v = a.v_src != nullptr;
+    for (int base = threadIdx.x; base < n; base += kCopyThreads * kUnroll) {
+        u32x4 kk[kUnroll], vv[kUnroll];
+        int64_t dst[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int idx = base + u * kCopyThreads;
+            dst[u] = -1;
+            if (idx < n) {
+                int tt, ch;
+                if (a.lcpr >= 0) {
+                    tt = idx >> a.lcpr;
+                    ch = idx & (cpr - 1);
+                } else {
+                    tt = idx / cpr;
+                    ch = idx - tt * cpr;
+                }
+                const int64_t t = tok0 + tt;
+                const int64_t slot = a.slots[t];
+                if (slot >= 0 && slot < a.total_slots) {
+                    dst[u] = (slot >> a.lbs) * a.block_stride + a.layer_off +
+                             (slot & bsm) * a.row_bytes + ((int64_t)ch << 4);
+                    const int64_t src = t * a.row_bytes + ((int64_t)ch << 4);
+                    kk[u] = ld16_stream(a.k_src + src);
+                    if (has_v) vv[u] = ld16_stream(a.v_src + src);
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            if (dst[u] >= 0) {
+                st16(a.kpool + dst[u], kk[u]);
+                if (has_v) st16(a.vpool + dst[u], vv[u]);
+            }
+        }
+    }
+}
+
+hipError_t launch_scatter(const ScatterArgs &a, hipStream_t s) {
+    const int64_t blocks = (a.num_tokens + a.tok_per_wg - 1) / a.tok_per_wg;
+    hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)blocks), dim3(kCopyThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Gather [P1 "Problem"/"Solution"; P3 sec. 2.2]: out row (row_start + t) <-
+// pool row (table[(off+t) >> lbs], layer, (off+t) & bsm) for t < seq_len.
+// Workgroup (seq, tile) covers tokens [tile*T, tile*T + T); the table
+// entries that range touches are staged in LDS first.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kCopyThreads) void gather_kernel(GatherArgs a) {
+    __shared__ int32_t bt_s[kBtLds];
+    const int seq = blockIdx.x / a.tiles_per_seq;
+    const int tile = blockIdx.x - seq * a.tiles_per_seq;
+    const int L = a.seq_lens[seq];
+    const int t0 = tile * a.tok_per_wg;
+    if (t0 >= L) return;  // uniform across the workgroup
+    const int t1 = min(L, t0 + a.tok_per_wg);
+    const int64_t off = a.offsets[seq];
+    const int lbs = a.pool.lbs;
+    const int64_t bsm = (1ll << lbs) - 1;
+    const int64_t jb0 = (off + t0) >> lbs;
+    const int nbt = (int)(((off + t1 - 1) >> lbs) - jb0 + 1);
+    for (int i = threadIdx.x; i < nbt; i += kCopyThreads) {
+        const int64_t j = jb0 + i;
+        int32_t b = -1;
+        if (j >= 0 && j < a.bt_stride) {
+            b = a.block_tables[(int64_t)seq * a.bt_stride + j];
+            if (b < 0 || b >= a.pool.num_blocks) b = -1;
+        }
+        bt_s[i] = b;
+    }
+    __syncthreads();
+
+    const int cpr = a.pool.row_bytes >> 4;
+    const int n = (t1 - t0) * cpr;
+    const int64_t row0 = a.out_row_start[seq];
+    const bool has_v = a.v_out != nullptr;
+    for (int base = threadIdx.x; base < n; base += kCopyThreads * kUnroll) {
+        u32x4 kk[kUnroll], vv[kUnroll];
+        int64_t dst[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int idx = base + u * kCopyThreads;
+            dst[u] = -1;
+            kk[u] = u32x4{0, 0, 0, 0};
+            vv[u] = u32x4{0, 0, 0, 0};
+            if (idx < n) {
+                int tt, ch;
+                if (a.lcpr >= 0) {
+                    tt = idx >> a.lcpr;
+                    ch = idx & (cpr - 1);
+                } else {
+                    tt = idx / cpr;
+                    ch = idx - tt * cpr;
+                }
+                const int t = t0 + tt;
+                const int64_t p = off + t;
+                const int64_t orow = row0 + t;
+                if (orow < 0 || orow >= a.out_rows) continue;
+                dst[u] = orow * a.pool.row_bytes + ((int64_t)ch << 4);
+                const int32_t b = bt_s[(int)((p >> lbs) - jb0)];
+                if (b >= 0) {
+                    const int64_t src = (int64_t)b * a.pool.block_stride + a.pool.layer_off +
+                                        (int64_t)(p & bsm) * a.pool.row_bytes + ((int64_t)ch << 4);
+                    kk[u] = ld16(a.pool.k + src);
+                    if (has_v) vv[u] = ld16(a.pool.v + src);
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            if (dst[u] >= 0) {
+                st16(a.k_out + dst[u], kk[u]);
+                if (has_v) st16(a.v_out + dst[u], vv[u]);
+            }
+        }
+    }
+}
+
+hipError_t launch_gather(const GatherArgs &a, hipStream_t s) {
+    const int64_t blocks = (int64_t)a.num_seqs * a.tiles_per_seq;
+    hipLaunchKernelGGL(gather_kernel, dim3((unsigned)blocks), dim3(kCopyThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Contract validation (debug): counts offsets outside [0, bs), seq_len
+// outside [0, min(capacity, max_seq_len)] with capacity = bt_stride*bs - off
+// [P3 sec. 2.2], used table entries outside [0, num_blocks), and slots that
+// are neither -1 nor inside the pool [P2 sec. 2.2].
+// ---------------------------------------------------------------------------
+__global__ void zero_u64_kernel(unsigned long long *p) {
+    if (threadIdx.x == 0 && blockIdx.x == 0) *p = 0ull;
+}
+
+__global__ __launch_bounds__(256) void validate_kernel(ValidateArgs a) {
+    unsigned long long bad = 0;
+    const int64_t nthreads = (int64_t)gridDim.x * blockDim.x;
+    const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    // per sequence: offset and length against the table's capacity
+    for (int64_t s = tid; s < a.num_seqs; s += nthreads) {
+        const int64_t off = a.offsets[s];
+        const int64_t L = a.seq_lens[s];
+        if (off < 0 || off >= a.block_size) ++bad;
+        const int64_t cap = (int64_t)a.bt_stride * a.block_size - off;
+        if (L < 0 || L > cap || (a.max_seq_len >= 0 && L > a.max_seq_len)) ++bad;
+    }
+    // per used table entry: (seq, j) with j <= (off + L - 1) / bs
+    const int64_t pairs = (int64_t)a.num_seqs * a.bt_stride;
+    for (int64_t k = tid; k < pairs; k += nthreads) {
+        const int64_t s = k / a.bt_stride;
+        const int64_t j = k - s * a.bt_stride;
+        const int64_t off = a.offsets[s];
+        const int64_t L = a.seq_lens[s];
+        if (off >= 0 && off < a.block_size && L > 0 && j <= (off + L - 1) / a.block_size) {
+            const int32_t b = a.block_tables[k];
+            if (b < 0 || b >= a.num_blocks) ++bad;
+        }
+    }
+    for (int64_t i = tid; i < a.num_tokens; i += nthreads) {
+        const int64_t sl = a.slots[i];
+        if (sl != -1 && (sl < 0 || sl >= a.total_slots)) ++bad;
+    }
+    if (bad) atomicAdd(a.count, bad);
+}
+
+hipError_t launch_validate(const ValidateArgs &a, hipStream_t s) {
+    hipLaunchKernelGGL(zero_u64_kernel, dim3(1), dim3(64), 0, s, a.count);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    int64_t work = (int64_t)a.num_seqs * a.bt_stride;
+    if (work < a.num_tokens) work = a.num_tokens;
+    if (work < a.num_seqs) work = a.num_seqs;
+    int64_t blocks = (work + 255) / 256;
+    if (blocks < 1) blocks = 1;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(validate_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace pkv

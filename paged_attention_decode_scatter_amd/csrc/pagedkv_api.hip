@@ -1,0 +1,346 @@
+// pagedkv_api.hip -- the C ABI of libpagedkv.so (declared in pagedkv.h):
+// host-side argument checks, launch geometry, dispatch to the kernels.
+// Every check runs before the first HIP call, so a rejected call enqueues
+// nothing and needs no device.
+#include <atomic>
+#include <stdint.h>
+
+#include "pagedkv.h"
+#include "pkv_internal.h"
+
+namespace {
+
+using namespace pkv;
+
+bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int ilog2(int64_t x) {
+    int l = 0;
+    while ((int64_t(1) << l) < x) ++l;
+    return l;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t elem_bytes(int32_t dtype) { return dtype == PKV_BF16 ? 2 : 4; }
+
+int64_t pow2_or_neg(int64_t x) { return is_pow2(x) ? ilog2(x) : -1; }
+
+// Common pool checks.  need_v: the call reads or writes V.
+int check_pool(const pkv_pool *pool, bool need_v) {
+    if (!pool) return PKV_ERR_NULL;
+    if (pool->dtype != PKV_F32 && pool->dtype != PKV_BF16) return PKV_ERR_DTYPE;
+    if (pool->reserved != 0) return PKV_ERR_SHAPE;
+    if (pool->num_blocks <= 0 || pool->num_blocks > INT32_MAX || pool->num_layers <= 0 ||
+        pool->num_kv_heads <= 0 || pool->head_dim <= 0 || !is_pow2(pool->block_size) ||
+        pool->block_size > (1 << 20))
+        return PKV_ERR_SHAPE;
+    const int64_t row = pool->num_kv_heads * pool->head_dim * elem_bytes(pool->dtype);
+    if (row > (int64_t(1) << 24)) return PKV_ERR_SHAPE;
+    if (row % 16) return PKV_ERR_ALIGN;
+    if (!pool->k || (need_v && !pool->v)) return PKV_ERR_NULL;
+    if (!aligned16(pool->k) || (pool->v && !aligned16(pool->v))) return PKV_ERR_ALIGN;
+    return PKV_OK;
+}
+
+PoolView make_view(const pkv_pool *pool, int32_t layer) {
+    PoolView v{};
+    const int64_t row = pool->num_kv_heads * pool->head_dim * elem_bytes(pool->dtype);
+    v.k = static_cast<const char *>(pool->k);
+    v.v = static_cast<const char *>(pool->v);
+    v.row_bytes = (int32_t)row;
+    v.block_stride = pool->num_layers * pool->block_size * row;
+    v.layer_off = (int64_t)layer * pool->block_size * row;
+    v.num_blocks = (int32_t)pool->num_blocks;
+    v.lbs = ilog2(pool->block_size);
+    return v;
+}
+
+// Compute units of the current device, queried once per device (256 when no
+// device answers, e.g. on a build host).
+int cu_count() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0) {
+        (void)hipGetLastError();
+        n = 256;
+    }
+    cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+// Largest split (multiple of 16 tokens) whose block-table entries fit the
+// LDS staging buffer: ceil(S / bs) + 1 <= kBtLds.
+int64_t max_split_tokens(int64_t bs) {
+    int64_t s = (kBtLds - 2) * bs;
+    if (s > (int64_t(1) << 20)) s = int64_t(1) << 20;
+    return s - s % kChunkTokens;
+}
+
+bool split_ok(int64_t s, int64_t bs) {
+    return s > 0 && s % kChunkTokens == 0 && s <= max_split_tokens(bs);
+}
+
+// Automatic split: the smallest power-of-two split >= 64 tokens that keeps the
+// work items (one wavefront each) at or below 16 per compute unit at
+// max_seq_len.
+int64_t auto_split(int64_t num_seqs, int64_t hkv, int64_t max_len, int64_t bs) {
+    const int64_t target = 16ll * cu_count();
+    const int64_t smax = max_split_tokens(bs);
+    int64_t s = 64;
+    if (s > smax) s = smax;
+    while (s * 2 <= smax && num_seqs * hkv * ((max_len + s - 1) / s) > target) s *= 2;
+    return s;
+}
+
+struct DecodePlan {
+    int64_t split;
+    int64_t max_splits;
+    int64_t ml_bytes;   // (m, l) partials, padded to 256 bytes
+    int64_t acc_bytes;  // acc partials
+};
+
+int plan_decode(int64_t num_seqs, int64_t hkv, int64_t hq, int64_t head_dim, int64_t max_len,
+                int64_t bs, int64_t split_req, DecodePlan *p) {
+    if (num_seqs < 0 || hkv <= 0 || hq <= 0 || head_dim <= 0 || max_len < 0 || !is_pow2(bs))
+        return PKV_ERR_SHAPE;
+    const int64_t split = split_req == 0 ? auto_split(num_seqs, hkv, max_len, bs) : split_req;
+    if (!split_ok(split, bs)) return PKV_ERR_SHAPE;
+    p->split = split;
+    p->max_splits = max_len > 0 ? (max_len + split - 1) / split : 1;
+    if (p->max_splits <= 1) {
+        p->max_splits = 1;
+        p->ml_bytes = p->acc_bytes = 0;
+    } else {
+        const int64_t items = num_seqs * p->max_splits * hq;
+        p->ml_bytes = (items * 2 * 4 + 255) / 256 * 256;
+        p->acc_bytes = items * head_dim * 4;
+    }
+    return PKV_OK;
+}
+
+int status_of(hipError_t e) {
+    if (e == hipSuccess) return PKV_OK;
+    (void)hipGetLastError();
+    return PKV_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+PKV_API int kv_slot_mapping(const int32_t *block_tables, int32_t bt_stride, const int32_t *offsets,
+                            int32_t num_seqs, const int32_t *token_seq, const int32_t *token_pos,
+                            int64_t num_tokens, int32_t block_size, int64_t *slot_mapping,
+                            void *stream) {
+    if (num_tokens < 0 || num_seqs < 0 || bt_stride < 0 || !is_pow2(block_size))
+        return PKV_ERR_SHAPE;
+    if (num_tokens == 0) return PKV_OK;
+    if (!token_seq || !token_pos || !slot_mapping) return PKV_ERR_NULL;
+    if (num_seqs > 0 && (!block_tables || !offsets)) return PKV_ERR_NULL;
+    if (num_tokens > (int64_t(1) << 40)) return PKV_ERR_SHAPE;
+    SlotArgs a{};
+    a.block_tables = block_tables;
+    a.offsets = offsets;
+    a.token_seq = token_seq;
+    a.token_pos = token_pos;
+    a.slots = slot_mapping;
+    a.num_tokens = num_tokens;
+    a.bt_stride = bt_stride;
+    a.num_seqs = num_seqs;
+    a.lbs = ilog2(block_size);
+    return status_of(launch_slot_mapping(a, static_cast<hipStream_t>(stream)));
+}
+
+PKV_API int kv_scatter(const pkv_pool *pool, int32_t layer, const void *k_src, const void *v_src,
+                       const int64_t *slot_mapping, int64_t num_tokens, void *stream) {
+    const bool has_v = v_src != nullptr;
+    int st = check_pool(pool, has_v);
+    if (st) return st;
+    if (layer < 0 || layer >= pool->num_layers) return PKV_ERR_LAYER;
+    if (num_tokens < 0) return PKV_ERR_SHAPE;
+    if (num_tokens == 0) return PKV_OK;
+    if (!k_src || !slot_mapping) return PKV_ERR_NULL;
+    if (!aligned16(k_src) || (has_v && !aligned16(v_src))) return PKV_ERR_ALIGN;
+    const PoolView v = make_view(pool, layer);
+    ScatterArgs a{};
+    a.kpool = static_cast<char *>(pool->k);
+    a.vpool = static_cast<char *>(pool->v);
+    a.k_src = static_cast<const char *>(k_src);
+    a.v_src = static_cast<const char *>(v_src);
+    a.slots = slot_mapping;
+    a.num_tokens = num_tokens;
+    a.total_slots = pool->num_blocks * pool->block_size;
+    a.block_stride = v.block_stride;
+    a.layer_off = v.layer_off;
+    a.row_bytes = v.row_bytes;
+    a.lbs = v.lbs;
+    const int64_t cpr = v.row_bytes / 16;
+    // about 2048 16-byte pieces (32 KiB per tensor) per workgroup
+    int64_t tpw = 2048 / cpr;
+    if (tpw < 1) tpw = 1;
+    a.tok_per_wg = (int32_t)tpw;
+    a.lcpr = (int32_t)pow2_or_neg(cpr);
+    if (cpr * tpw > INT32_MAX / 2) return PKV_ERR_SHAPE;
+    return status_of(launch_scatter(a, static_cast<hipStream_t>(stream)));
+}
+
+PKV_API int kv_gather(const pkv_pool *pool, int32_t layer, const int32_t *block_tables,
+                      int32_t bt_stride, const int32_t *seq_lens, const int32_t *offsets,
+                      const int64_t *out_row_start, int32_t num_seqs, int32_t max_seq_len,
+                      void *k_out, void *v_out, int64_t out_rows, void *stream) {
+    const bool has_v = v_out != nullptr;
+    int st = check_pool(pool, has_v);
+    if (st) return st;
+    if (layer < 0 || layer >= pool->num_layers) return PKV_ERR_LAYER;
+    if (num_seqs < 0 || max_seq_len < 0 || bt_stride < 0 || out_rows < 0) return PKV_ERR_SHAPE;
+    if (num_seqs == 0 || max_seq_len == 0 || out_rows == 0) return PKV_OK;
+    if (!block_tables || !seq_lens || !offsets || !out_row_start || !k_out) return PKV_ERR_NULL;
+    if (!aligned16(k_out) || (has_v && !aligned16(v_out))) return PKV_ERR_ALIGN;
+    GatherArgs a{};
+    a.pool = make_view(pool, layer);
+    a.block_tables = block_tables;
+    a.seq_lens = seq_lens;
+    a.offsets = offsets;
+    a.out_row_start = out_row_start;
+    a.k_out = static_cast<char *>(k_out);
+    a.v_out = static_cast<char *>(v_out);
+    a.out_rows = out_rows;
+    a.bt_stride = bt_stride;
+    a.num_seqs = num_seqs;
+    const int64_t cpr = a.pool.row_bytes / 16;
+    int64_t tpw = 2048 / cpr;
+    if (tpw < 1) tpw = 1;
+    const int64_t tmax = (kBtLds - 2) * pool->block_size;  // LDS table capacity
+    if (tpw > tmax) tpw = tmax;
+    a.tok_per_wg = (int32_t)tpw;
+    a.tiles_per_seq = (int32_t)((max_seq_len + tpw - 1) / tpw);
+    a.lcpr = (int32_t)pow2_or_neg(cpr);
+    if ((int64_t)num_seqs * a.tiles_per_seq > INT32_MAX || cpr * tpw > INT32_MAX / 2)
+        return PKV_ERR_SHAPE;
+    return status_of(launch_gather(a, static_cast<hipStream_t>(stream)));
+}
+
+PKV_API int32_t paged_attn_decode_split_tokens(int32_t num_seqs, int32_t num_kv_heads,
+                                               int32_t max_seq_len, int32_t block_size) {
+    DecodePlan p;
+    const int st = plan_decode(num_seqs, num_kv_heads, num_kv_heads, 64, max_seq_len, block_size,
+                               0, &p);
+    return st ? st : (int32_t)p.split;
+}
+
+PKV_API size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_kv_heads,
+                                                int32_t num_q_heads, int32_t head_dim,
+                                                int32_t max_seq_len, int32_t block_size,
+                                                int32_t split_tokens) {
+    DecodePlan p;
+    if (num_kv_heads <= 0 || num_q_heads % num_kv_heads) return (size_t)-1;
+    if (plan_decode(num_seqs, num_kv_heads, num_q_heads, head_dim, max_seq_len, block_size,
+                    split_tokens, &p))
+        return (size_t)-1;
+    return (size_t)(p.ml_bytes + p.acc_bytes);
+}
+
+PKV_API int paged_attn_decode(const pkv_pool *pool, int32_t layer, const void *q,
+                              int32_t num_q_heads, const int32_t *block_tables, int32_t bt_stride,
+                              const int32_t *seq_lens, const int32_t *offsets, int32_t num_seqs,
+                              int32_t max_seq_len, float scale, int32_t split_tokens, void *out,
+                              void *workspace, size_t workspace_bytes, void *stream) {
+    int st = check_pool(pool, true);
+    if (st) return st;
+    if (layer < 0 || layer >= pool->num_layers) return PKV_ERR_LAYER;
+    if (num_seqs < 0 || max_seq_len < 0 || bt_stride < 0 || num_q_heads <= 0 ||
+        num_q_heads % pool->num_kv_heads != 0 || split_tokens < 0)
+        return PKV_ERR_SHAPE;
+    const int group = (int)(num_q_heads / pool->num_kv_heads);
+    if (!decode_supported(pool->dtype, (int)pool->head_dim, group)) return PKV_ERR_UNSUPPORTED;
+    if (num_seqs == 0) return PKV_OK;
+    if (!q || !out || !seq_lens || !offsets || (max_seq_len > 0 && !block_tables))
+        return PKV_ERR_NULL;
+    if (!aligned16(q) || !aligned16(out)) return PKV_ERR_ALIGN;
+    DecodePlan p;
+    st = plan_decode(num_seqs, pool->num_kv_heads, num_q_heads, pool->head_dim, max_seq_len,
+                     pool->block_size, split_tokens, &p);
+    if (st) return st;
+    const int64_t need = p.ml_bytes + p.acc_bytes;
+    if (need > 0) {
+        if (!workspace || (int64_t)workspace_bytes < need) return PKV_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return PKV_ERR_ALIGN;
+    }
+    const int64_t hkv = pool->num_kv_heads;
+    const int64_t hpw = hkv % 4 == 0 ? 4 : (hkv % 2 == 0 ? 2 : 1);
+    const int64_t groups = hkv / hpw;
+    if (groups * p.max_splits * num_seqs > INT32_MAX) return PKV_ERR_SHAPE;
+    DecodeArgs a{};
+    a.pool = make_view(pool, layer);
+    a.q = static_cast<const char *>(q);
+    a.block_tables = block_tables;
+    a.seq_lens = seq_lens;
+    a.offsets = offsets;
+    a.out = static_cast<char *>(out);
+    a.ws_ml = need > 0 ? static_cast<float *>(workspace) : nullptr;
+    a.ws_acc = need > 0 ? reinterpret_cast<float *>(static_cast<char *>(workspace) + p.ml_bytes)
+                        : nullptr;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.bt_stride = bt_stride;
+    a.num_seqs = num_seqs;
+    a.num_kv_heads = (int32_t)hkv;
+    a.num_q_heads = num_q_heads;
+    a.split_tokens = (int32_t)p.split;
+    a.max_splits = (int32_t)p.max_splits;
+    a.heads_per_wg = (int32_t)hpw;
+    a.head_groups = (int32_t)groups;
+    return status_of(launch_decode(a, pool->dtype, (int)pool->head_dim, group,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+PKV_API int kv_validate(const pkv_pool *pool, const int32_t *block_tables, int32_t bt_stride,
+                        const int32_t *seq_lens, const int32_t *offsets, int32_t num_seqs,
+                        int32_t max_seq_len, const int64_t *slot_mapping, int64_t num_tokens,
+                        int64_t *violations, void *stream) {
+    if (!pool || !violations) return PKV_ERR_NULL;
+    if (pool->num_blocks <= 0 || pool->num_blocks > INT32_MAX || !is_pow2(pool->block_size))
+        return PKV_ERR_SHAPE;
+    if (num_seqs < 0 || bt_stride < 0 || num_tokens < 0) return PKV_ERR_SHAPE;
+    if (num_seqs > 0 && (!block_tables || !seq_lens || !offsets)) return PKV_ERR_NULL;
+    if (num_tokens > 0 && !slot_mapping) return PKV_ERR_NULL;
+    ValidateArgs a{};
+    a.block_tables = block_tables;
+    a.seq_lens = seq_lens;
+    a.offsets = offsets;
+    a.slots = slot_mapping;
+    a.count = reinterpret_cast<unsigned long long *>(violations);
+    a.num_tokens = num_tokens;
+    a.total_slots = pool->num_blocks * pool->block_size;
+    a.bt_stride = bt_stride;
+    a.num_seqs = num_seqs;
+    a.num_blocks = (int32_t)pool->num_blocks;
+    a.block_size = (int32_t)pool->block_size;
+    a.max_seq_len = max_seq_len;
+    return status_of(launch_validate(a, static_cast<hipStream_t>(stream)));
+}
+
+PKV_API const char *pkv_status_string(int status) {
+    switch (status) {
+        case PKV_OK: return "ok";
+        case PKV_ERR_NULL: return "a required pointer is NULL";
+        case PKV_ERR_DTYPE: return "unknown element type";
+        case PKV_ERR_SHAPE: return "invalid size or shape";
+        case PKV_ERR_LAYER: return "layer outside [0, num_layers)";
+        case PKV_ERR_ALIGN: return "pointer or row not 16-byte aligned";
+        case PKV_ERR_WORKSPACE: return "workspace missing or too small";
+        case PKV_ERR_LAUNCH: return "HIP kernel launch failed";
+        case PKV_ERR_UNSUPPORTED: return "head_dim or query-group size not supported";
+        case PKV_ERR_DEVICE: return "no usable HIP device";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,119 @@
+// pkv_internal.h -- argument blocks and launchers shared by the HIP sources
+// of libpagedkv.so (not part of the public ABI; see include/pagedkv.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+// Tokens one wavefront of the decode kernel consumes per iteration.
+constexpr int kChunkTokens = 16;
+// Block-table entries a decode or gather workgroup stages in LDS.
+constexpr int kBtLds = 1024;
+// Gather/scatter workgroup size.
+constexpr int kCopyThreads = 256;
+
+// A pool as the kernels see it: byte addresses of (block b, layer, slot s)
+// rows are base + b*block_stride + layer_off + s*row_bytes.
+struct PoolView {
+    const char *k;
+    const char *v;
+    int64_t block_stride;  // num_layers * block_size * row_bytes
+    int64_t layer_off;     // layer * block_size * row_bytes
+    int32_t row_bytes;     // num_kv_heads * head_dim * element size
+    int32_t num_blocks;
+    int32_t lbs;           // log2(block_size)
+    int32_t pad_;
+};
+
+struct SlotArgs {
+    const int32_t *block_tables;
+    const int32_t *offsets;
+    const int32_t *token_seq;
+    const int32_t *token_pos;
+    int64_t *slots;
+    int64_t num_tokens;
+    int32_t bt_stride;
+    int32_t num_seqs;
+    int32_t lbs;
+};
+
+struct ScatterArgs {
+    char *kpool;
+    char *vpool;
+    const char *k_src;
+    const char *v_src;
+    const int64_t *slots;
+    int64_t num_tokens;
+    int64_t total_slots;   // num_blocks * block_size
+    int64_t block_stride;
+    int64_t layer_off;
+    int32_t row_bytes;
+    int32_t lbs;
+    int32_t tok_per_wg;
+    int32_t lcpr;          // log2(row_bytes/16), or -1 if not a power of two
+};
+
+struct GatherArgs {
+    PoolView pool;
+    const int32_t *block_tables;
+    const int32_t *seq_lens;
+    const int32_t *offsets;
+    const int64_t *out_row_start;
+    char *k_out;
+    char *v_out;
+    int64_t out_rows;      // rows k_out/v_out can hold; rows beyond are skipped
+    int32_t bt_stride;
+    int32_t num_seqs;
+    int32_t tok_per_wg;
+    int32_t tiles_per_seq;
+    int32_t lcpr;
+};
+
+struct DecodeArgs {
+    PoolView pool;
+    const char *q;
+    const int32_t *block_tables;
+    const int32_t *seq_lens;
+    const int32_t *offsets;
+    char *out;
+    float *ws_ml;          // [num_seqs][max_splits][num_q_heads][2]  (m, l)
+    float *ws_acc;         // [num_seqs][max_splits][num_q_heads][head_dim]
+    float scale_log2;      // scale * log2(e): scores live in the exp2 domain
+    int32_t bt_stride;
+    int32_t num_seqs;
+    int32_t num_kv_heads;
+    int32_t num_q_heads;
+    int32_t split_tokens;
+    int32_t max_splits;
+    int32_t heads_per_wg;
+    int32_t head_groups;
+};
+
+struct ValidateArgs {
+    const int32_t *block_tables;
+    const int32_t *seq_lens;
+    const int32_t *offsets;
+    const int64_t *slots;
+    unsigned long long *count;
+    int64_t num_tokens;
+    int64_t total_slots;
+    int32_t bt_stride;
+    int32_t num_seqs;
+    int32_t num_blocks;
+    int32_t block_size;
+    int32_t max_seq_len;
+};
+
+hipError_t launch_slot_mapping(const SlotArgs &a, hipStream_t s);
+hipError_t launch_scatter(const ScatterArgs &a, hipStream_t s);
+hipError_t launch_gather(const GatherArgs &a, hipStream_t s);
+hipError_t launch_validate(const ValidateArgs &a, hipStream_t s);
+// Returns hipErrorInvalidValue when (dtype, head_dim, group) is not built.
+hipError_t launch_decode(const DecodeArgs &a, int dtype, int head_dim, int group,
+                         hipStream_t s);
+bool decode_supported(int dtype, int head_dim, int group);
+
+}  // namespace pkv

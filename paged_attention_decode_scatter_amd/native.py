@@ -1,0 +1,239 @@
+"""ctypes binding of libpagedkv.so (declared in include/pagedkv.h).
+
+Argument marshalling only: tensors become device pointers, the current torch
+stream becomes the hipStream_t, and a negative status becomes a PagedKVError.
+Every step of the hot path runs in the library's HIP kernels; there is no
+fallback.  If the library has not been built, or cannot be loaded, the first
+call raises.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
+
+PKV_F32 = 0
+PKV_BF16 = 1
+
+_DTYPES = {torch.float32: PKV_F32, torch.bfloat16: PKV_BF16}
+
+# the exported symbols, in header order
+SYMBOLS = (
+    "kv_slot_mapping",
+    "kv_scatter",
+    "kv_gather",
+    "paged_attn_decode_split_tokens",
+    "paged_attn_decode_workspace_size",
+    "paged_attn_decode",
+    "kv_validate",
+    "pkv_status_string",
+)
+
+
+class PagedKVError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn}: {status_string(status)} (status {status})")
+
+
+class PkvPool(ctypes.Structure):
+    _fields_ = [
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("num_blocks", ctypes.c_int64),
+        ("num_layers", ctypes.c_int64),
+        ("block_size", ctypes.c_int64),
+        ("num_kv_heads", ctypes.c_int64),
+        ("head_dim", ctypes.c_int64),
+        ("dtype", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libpagedkv.so once.  torch is imported first so the HIP runtime
+    torch ships is the one the library binds to (same soname)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m paged_attention_decode_scatter_amd.build` "
+            "(or __graft_entry__.build()); there is no non-HIP fallback")
+    lib = ctypes.CDLL(path)
+    i32, i64, p, f32, sz = (ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float,
+                            ctypes.c_size_t)
+    pp = ctypes.POINTER(PkvPool)
+    lib.kv_slot_mapping.restype = ctypes.c_int
+    lib.kv_slot_mapping.argtypes = [p, i32, p, i32, p, p, i64, i32, p, p]
+    lib.kv_scatter.restype = ctypes.c_int
+    lib.kv_scatter.argtypes = [pp, i32, p, p, p, i64, p]
+    lib.kv_gather.restype = ctypes.c_int
+    lib.kv_gather.argtypes = [pp, i32, p, i32, p, p, p, i32, i32, p, p, i64, p]
+    lib.paged_attn_decode_split_tokens.restype = i32
+    lib.paged_attn_decode_split_tokens.argtypes = [i32, i32, i32, i32]
+    lib.paged_attn_decode_workspace_size.restype = sz
+    lib.paged_attn_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+    lib.paged_attn_decode.restype = ctypes.c_int
+    lib.paged_attn_decode.argtypes = [pp, i32, p, i32, p, i32, p, p, i32, i32, f32, i32, p, p,
+                                      sz, p]
+    lib.kv_validate.restype = ctypes.c_int
+    lib.kv_validate.argtypes = [pp, p, i32, p, p, i32, i32, p, i64, p, p]
+    lib.pkv_status_string.restype = ctypes.c_char_p
+    lib.pkv_status_string.argtypes = [ctypes.c_int]
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().pkv_status_string(int(status)).decode()
+
+
+def _check(fn, status):
+    if status != 0:
+        raise PagedKVError(fn, status)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t):
+    if t is not None and t.is_cuda:
+        return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+    return None
+
+
+def _need(t, dtype, name):
+    if t is None:
+        return
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def make_pool(k_pool, v_pool=None) -> PkvPool:
+    """Describe a (num_blocks, num_layers, block_size, num_kv_heads, head_dim)
+    K/V pool pair for the C ABI."""
+    if k_pool.dim() != 5:
+        raise ValueError("pool must be (num_blocks, num_layers, block_size, num_kv_heads, head_dim)")
+    if k_pool.dtype not in _DTYPES:
+        raise TypeError(f"pool dtype must be float32 or bfloat16, got {k_pool.dtype}")
+    _need(k_pool, k_pool.dtype, "k_pool")
+    if v_pool is not None:
+        _need(v_pool, k_pool.dtype, "v_pool")
+        if v_pool.shape != k_pool.shape:
+            raise ValueError("k_pool and v_pool shapes differ")
+    nb, nl, bs, h, d = k_pool.shape
+    return PkvPool(k_pool.data_ptr(), None if v_pool is None else v_pool.data_ptr(),
+                   nb, nl, bs, h, d, _DTYPES[k_pool.dtype], 0)
+
+
+def kv_slot_mapping(block_tables, offsets, token_seq, token_pos, block_size, out=None):
+    """int64 slot per new token (-1 = padding) computed on the device."""
+    for t, n in ((block_tables, "block_tables"), (offsets, "offsets"),
+                 (token_seq, "token_seq"), (token_pos, "token_pos")):
+        _need(t, torch.int32, n)
+    n = token_seq.shape[0]
+    if out is None:
+        out = torch.empty(n, dtype=torch.int64, device=token_seq.device)
+    _need(out, torch.int64, "out")
+    st = load_library().kv_slot_mapping(
+        _ptr(block_tables), block_tables.shape[1], _ptr(offsets), block_tables.shape[0],
+        _ptr(token_seq), _ptr(token_pos), n, block_size, _ptr(out), _stream(token_seq))
+    _check("kv_slot_mapping", st)
+    return out
+
+
+def kv_scatter(k_pool, v_pool, layer, k_src, v_src, slot_mapping):
+    pool = make_pool(k_pool, v_pool)
+    _need(k_src, k_pool.dtype, "k_src")
+    _need(v_src, k_pool.dtype, "v_src")
+    _need(slot_mapping, torch.int64, "slot_mapping")
+    st = load_library().kv_scatter(ctypes.byref(pool), layer, _ptr(k_src), _ptr(v_src),
+                                   _ptr(slot_mapping), slot_mapping.shape[0], _stream(k_pool))
+    _check("kv_scatter", st)
+
+
+def kv_gather(k_pool, v_pool, layer, block_tables, seq_lens, offsets, out_row_start,
+              max_seq_len, k_out, v_out=None):
+    pool = make_pool(k_pool, v_pool if v_out is not None else None)
+    for t, n in ((block_tables, "block_tables"), (seq_lens, "seq_lens"), (offsets, "offsets")):
+        _need(t, torch.int32, n)
+    _need(out_row_start, torch.int64, "out_row_start")
+    _need(k_out, k_pool.dtype, "k_out")
+    _need(v_out, k_pool.dtype, "v_out")
+    if v_out is not None and v_out.shape[0] != k_out.shape[0]:
+        raise ValueError("k_out and v_out row counts differ")
+    st = load_library().kv_gather(
+        ctypes.byref(pool), layer, _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens),
+        _ptr(offsets), _ptr(out_row_start), seq_lens.shape[0], int(max_seq_len), _ptr(k_out),
+        _ptr(v_out), k_out.shape[0], _stream(k_pool))
+    _check("kv_gather", st)
+
+
+def paged_attn_decode_split_tokens(num_seqs, num_kv_heads, max_seq_len, block_size):
+    v = load_library().paged_attn_decode_split_tokens(num_seqs, num_kv_heads, int(max_seq_len),
+                                                      block_size)
+    if v < 0:
+        raise PagedKVError("paged_attn_decode_split_tokens", v)
+    return v
+
+
+def paged_attn_decode_workspace_size(num_seqs, num_kv_heads, num_q_heads, head_dim, max_seq_len,
+                                     block_size, split_tokens=0):
+    v = load_library().paged_attn_decode_workspace_size(num_seqs, num_kv_heads, num_q_heads,
+                                                        head_dim, int(max_seq_len), block_size,
+                                                        split_tokens)
+    if v == ctypes.c_size_t(-1).value:
+        raise PagedKVError("paged_attn_decode_workspace_size", -3)
+    return v
+
+
+def paged_attn_decode(k_pool, v_pool, layer, q, block_tables, seq_lens, offsets, max_seq_len,
+                      scale, split_tokens=0, out=None, workspace=None):
+    """out[s, h] = softmax(scale * q[s, h] . K) . V over the sequence's cached
+    tokens, read in place through the block tables.  `workspace` (uint8,
+    device) is allocated here when not given."""
+    pool = make_pool(k_pool, v_pool)
+    _need(q, k_pool.dtype, "q")
+    for t, n in ((block_tables, "block_tables"), (seq_lens, "seq_lens"), (offsets, "offsets")):
+        _need(t, torch.int32, n)
+    num_seqs, hq, d = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, k_pool.dtype, "out")
+    need = paged_attn_decode_workspace_size(num_seqs, k_pool.shape[3], hq, d, max_seq_len,
+                                            k_pool.shape[2], split_tokens)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load_library().paged_attn_decode(
+        ctypes.byref(pool), layer, _ptr(q), hq, _ptr(block_tables), block_tables.shape[1],
+        _ptr(seq_lens), _ptr(offsets), num_seqs, int(max_seq_len), float(scale), split_tokens,
+        _ptr(out), _ptr(workspace), ws_bytes, _stream(q))
+    _check("paged_attn_decode", st)
+    return out
+
+
+def kv_validate(k_pool, block_tables, seq_lens, offsets, max_seq_len=-1, slot_mapping=None,
+                counter=None):
+    """Number of caller-contract violations (synchronises to read it)."""
+    pool = make_pool(k_pool, None)
+    dev = k_pool.device
+    if counter is None:
+        counter = torch.empty(1, dtype=torch.int64, device=dev)
+    ns = 0 if seq_lens is None else seq_lens.shape[0]
+    stride = 0 if block_tables is None else block_tables.shape[1]
+    nt = 0 if slot_mapping is None else slot_mapping.shape[0]
+    st = load_library().kv_validate(ctypes.byref(pool), _ptr(block_tables), stride,
+                                    _ptr(seq_lens), _ptr(offsets), ns, int(max_seq_len),
+                                    _ptr(slot_mapping), nt, _ptr(counter), _stream(k_pool))
+    _check("kv_validate", st)
+    return int(counter.item())

@@ -1,0 +1,164 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad
+arguments on the host before any HIP call (no GPU needed: every call here
+fails its argument checks, so nothing is enqueued)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from paged_attention_decode_scatter_amd import native as N
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pagedkv.h")
+
+OK, NULL, DTYPE, SHAPE, LAYER, ALIGN, WORKSPACE, LAUNCH, UNSUP = 0, -1, -2, -3, -4, -5, -6, -7, -8
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"PKV_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(N.LIB_PATH):
+        from paged_attention_decode_scatter_amd import build
+        build.build()
+    return N.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) == 8
+    assert set(names) == set(N.SYMBOLS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_only_declared_symbols_are_exported(lib):
+    import subprocess
+
+    out = subprocess.run(["nm", "-D", "--defined-only", N.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert exported == set(declared_functions())
+
+
+def test_status_strings(lib):
+    for st in (OK, NULL, DTYPE, SHAPE, LAYER, ALIGN, WORKSPACE, LAUNCH, UNSUP, -9):
+        assert N.status_string(st)
+    assert N.status_string(12345) == "unknown status"
+
+
+def pool(k=0x1000, v=0x2000, nb=16, nl=2, bs=16, h=8, d=128, dtype=1, reserved=0):
+    return N.PkvPool(k, v, nb, nl, bs, h, d, dtype, reserved)
+
+
+A = 0x10000  # an aligned fake device address; never dereferenced on these paths
+
+
+def test_scatter_argument_checks(lib):
+    f = lib.kv_scatter
+    by = ctypes.byref
+    assert f(None, 0, A, A, A, 4, None) == NULL
+    assert f(by(pool(k=None)), 0, A, A, A, 4, None) == NULL
+    assert f(by(pool(dtype=7)), 0, A, A, A, 4, None) == DTYPE
+    assert f(by(pool(bs=12)), 0, A, A, A, 4, None) == SHAPE
+    assert f(by(pool(nb=0)), 0, A, A, A, 4, None) == SHAPE
+    assert f(by(pool(reserved=1)), 0, A, A, A, 4, None) == SHAPE
+    assert f(by(pool(h=1, d=3, dtype=0)), 0, A, A, A, 4, None) == ALIGN  # 12-byte rows
+    assert f(by(pool(k=0x1004)), 0, A, A, A, 4, None) == ALIGN
+    assert f(by(pool()), 2, A, A, A, 4, None) == LAYER
+    assert f(by(pool()), -1, A, A, A, 4, None) == LAYER
+    assert f(by(pool()), 0, A, A, A, -1, None) == SHAPE
+    assert f(by(pool()), 0, A, A, A, 0, None) == OK          # nothing to do, nothing enqueued
+    assert f(by(pool()), 0, None, A, A, 4, None) == NULL
+    assert f(by(pool()), 0, A, A, None, 4, None) == NULL
+    assert f(by(pool()), 0, A + 8, A, A, 4, None) == ALIGN
+    assert f(by(pool(v=None)), 0, A, A, A, 4, None) == NULL  # V source given, V pool missing
+
+
+def test_gather_argument_checks(lib):
+    f = lib.kv_gather
+    by = ctypes.byref
+    args = lambda **kw: dict(dict(layer=0, bt=A, stride=4, sl=A, off=A, rs=A, ns=2, mx=10,
+                                  ko=A, vo=A, rows=20), **kw)
+
+    def call(p, **kw):
+        a = args(**kw)
+        return f(by(p), a["layer"], a["bt"], a["stride"], a["sl"], a["off"], a["rs"], a["ns"],
+                 a["mx"], a["ko"], a["vo"], a["rows"], None)
+
+    assert call(pool(), layer=5) == LAYER
+    assert call(pool(), ns=-1) == SHAPE
+    assert call(pool(), mx=-1) == SHAPE
+    assert call(pool(), rows=-1) == SHAPE
+    assert call(pool(), ns=0) == OK
+    assert call(pool(), mx=0) == OK
+    assert call(pool(), bt=None) == NULL
+    assert call(pool(), rs=None) == NULL
+    assert call(pool(), ko=None) == NULL
+    assert call(pool(), ko=A + 4) == ALIGN
+    assert call(pool(v=None)) == NULL
+
+
+def test_slot_mapping_argument_checks(lib):
+    f = lib.kv_slot_mapping
+    assert f(A, 4, A, 2, A, A, 10, 12, A, None) == SHAPE    # block_size not a power of two
+    assert f(A, 4, A, 2, A, A, -1, 16, A, None) == SHAPE
+    assert f(A, 4, A, 2, A, A, 0, 16, A, None) == OK
+    assert f(A, 4, A, 2, None, A, 10, 16, A, None) == NULL
+    assert f(None, 4, A, 2, A, A, 10, 16, A, None) == NULL
+    assert f(A, 4, A, 2, A, A, 10, 16, None, None) == NULL
+
+
+def test_decode_argument_checks(lib):
+    f = lib.paged_attn_decode
+    by = ctypes.byref
+
+    def call(p=None, hq=32, ns=4, mx=100, split=0, q=A, out=A, ws=A, wsb=1 << 30, layer=0):
+        return f(by(p or pool()), layer, q, hq, A, 8, A, A, ns, mx, 0.1, split, out, ws, wsb, None)
+
+    assert call(hq=30) == SHAPE        # not a multiple of num_kv_heads
+    assert call(hq=24) == UNSUP        # G = 3
+    assert call(p=pool(d=96)) == UNSUP
+    assert call(layer=3) == LAYER
+    assert call(split=24) == SHAPE     # not a multiple of 16
+    assert call(split=-16) == SHAPE
+    assert call(ns=0) == OK
+    assert call(q=None) == NULL
+    assert call(out=A + 2) == ALIGN
+    # needs a workspace when a sequence spans several splits
+    need = lib.paged_attn_decode_workspace_size(4, 8, 32, 128, 100, 16, 16)
+    assert need > 0
+    assert call(split=16, ws=None, wsb=0) == WORKSPACE
+    assert call(split=16, wsb=need - 1) == WORKSPACE
+    assert call(split=16, ws=A + 4, wsb=need) == ALIGN
+
+
+def test_workspace_size_and_split_choice(lib):
+    ws = lib.paged_attn_decode_workspace_size
+    # one split covers everything: no workspace
+    assert ws(1, 2, 4, 64, 30, 16, 0) == 0
+    # (m, l) block padded to 256 bytes, then the fp32 accumulators
+    n = 8 * 4 * 64                     # seqs x splits x q heads at split 8192, len 32768
+    assert ws(8, 8, 64, 128, 32768, 16, 8192) == (n * 8 + 255) // 256 * 256 + n * 128 * 4
+    assert ws(8, 8, 64, 128, 32768, 16, 24) == ctypes.c_size_t(-1).value
+    split = lib.paged_attn_decode_split_tokens
+    for args in ((32, 8, 2048, 16), (64, 8, 4096, 16), (8, 8, 32768, 16), (1, 2, 30, 16),
+                 (3, 1, 5000, 1)):
+        s = split(*args)
+        assert s > 0 and s % 16 == 0
+        assert s // args[3] + 2 <= 1024
+    assert split(4, 8, 100, 12) == SHAPE
+
+
+def test_validate_argument_checks(lib):
+    f = lib.kv_validate
+    by = ctypes.byref
+    assert f(None, A, 4, A, A, 2, 10, A, 3, A, None) == NULL
+    assert f(by(pool()), A, 4, A, A, 2, 10, A, 3, None, None) == NULL
+    assert f(by(pool(bs=6)), A, 4, A, A, 2, 10, A, 3, A, None) == SHAPE
+    assert f(by(pool()), None, 4, A, A, 2, 10, A, 3, A, None) == NULL
+    assert f(by(pool()), A, 4, A, A, 2, 10, None, 3, A, None) == NULL
