@@ -75,6 +75,11 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
     return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+// A 32-bit word as a pair of bf16.  The word is passed by value on
+// purpose: applying __builtin_bit_cast directly to an ext_vector element
+// (q.y, q.z, ...) makes this compiler read element .x every time.
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t w) { return __builtin_bit_cast(bf16x2, w); }
+
 // Dot product of one 16-byte piece of q with one 16-byte piece of K.
 template <int DT>
 __device__ __forceinline__ float dot16(u32x4 q, u32x4 k);
@@ -82,14 +87,10 @@ __device__ __forceinline__ float dot16(u32x4 q, u32x4 k);
 template <>
 __device__ __forceinline__ float dot16<1>(u32x4 q, u32x4 k) {
     float s = 0.0f;
-    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.x),
-                                        __builtin_bit_cast(bf16x2, k.x), s, false);
-    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.y),
-                                        __builtin_bit_cast(bf16x2, k.y), s, false);
-    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.z),
-                                        __builtin_bit_cast(bf16x2, k.z), s, false);
-    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.w),
-                                        __builtin_bit_cast(bf16x2, k.w), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q.x), as_bf16x2(k.x), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q.y), as_bf16x2(k.y), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q.z), as_bf16x2(k.z), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q.w), as_bf16x2(k.w), s, false);
     return s;
 }
 

@@ -108,9 +108,9 @@ def test_scatter_small_pool_bit_exact(dev, dtype, hkv, d, bs):
     lo, hi = (-(1 << 15), 1 << 15) if ity == torch.int16 else (-(1 << 31), 1 << 31)
     k = torch.randint(lo, hi, shape, generator=g, dtype=ity).view(dtype).to(dev)
     v = torch.randint(lo, hi, shape, generator=g, dtype=ity).view(dtype).to(dev)
-    n = 300
+    n = min(300, nb * bs - 8)
     slots = torch.randperm(nb * bs, generator=g)[:n].to(torch.int64)
-    slots[torch.randperm(n, generator=g)[:40]] = -1
+    slots[torch.randperm(n, generator=g)[:n // 8]] = -1
     ks = torch.randint(lo, hi, (n, hkv, d), generator=g, dtype=ity).view(dtype).to(dev)
     vs = torch.randint(lo, hi, (n, hkv, d), generator=g, dtype=ity).view(dtype).to(dev)
     ref_k, ref_v = host(k).copy(), host(v).copy()
