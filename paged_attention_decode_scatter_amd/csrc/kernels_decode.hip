@@ -12,31 +12,41 @@
 //   [P3] mini-runtime, chapter 12 "Paged KV Cache"
 //
 // Work decomposition
-//   A work item is (sequence, kv head, split): split j covers logical tokens
-//   [j*S, (j+1)*S).  One wavefront (64 lanes) owns one work item and all G
-//   query heads of its kv head, so each K/V row is read from HBM once and
-//   used G times.  A workgroup holds up to 4 wavefronts = 4 kv heads of the
-//   same (sequence, split): they share the block-table entries, which are
-//   staged in LDS once per workgroup, and read neighbouring 256-byte head
-//   segments of the same token rows.
+//   Splits are ranges of flat table positions: split j of a sequence covers
+//   positions [j*S, (j+1)*S) intersected with [offset, offset + seq_len)
+//   (logical token t sits at flat position offset + t).  A work item is
+//   (sequence, kv head, split); one wavefront owns it and all G query heads
+//   of that kv head, so every K/V row is read from HBM once and used G
+//   times.  A workgroup holds up to 8 wavefronts (4 for fp32) = the kv
+//   heads of one (sequence, split): they share the block-table entries,
+//   staged in LDS once per workgroup, and together read each block's layer
+//   slice (block_size x all heads, contiguous) at the same time.  Workgroups are renumbered so that neighbours in the logical
+//   order (same split, consecutive sequences: a shared prefix) land on the
+//   same XCD and share its L2.
 //
-// Lane layout ("row layout")
-//   A kv-head row of one token is D*E bytes = LPR lanes x 16 bytes.  Lane
-//   (r, c) = (lane / LPR, lane % LPR) loads piece c of the row of token
-//   chunk_base + i*RPI + r for pass i (RPI = 64/LPR rows per wavefront
-//   instruction), so every load instruction covers RPI whole rows.
-//   QK:  partial dot over the lane's VEC elements (v_dot2_f32_bf16 for
-//        bf16), then an all-reduce over the LPR lanes of the row with DPP
-//        (quad_perm, row_half_mirror, row_mirror): every lane of the row
-//        ends with the same fp32 score.
-//   softmax: scores are kept in the exp2 domain (scale*log2 e folded in);
-//        per 16-token chunk the wavefront takes one max per query head
-//        (shared by all lanes), so m is wave-uniform; l and the P.V
-//        accumulators are per-lane partials over the lane's own rows and are
-//        summed across row groups once at the end.
-//   PV:  acc[g][e] += p * V[row][c*VEC + e] in fp32.
-//   Masked tokens (past seq_len, or an invalid table entry) get score -inf
-//   and are never loaded, so poisoned (NaN) pool slots cannot leak in.
+// bf16 kernel (MFMA QK^T, VALU PV), per 16-position chunk of one block:
+//   QK:  S^T = K_chunk (16 x D) . Q^T (D x 16 heads, G real) with
+//        v_mfma_f32_16x16x32_bf16.  Lane l loads K row l%16, elements
+//        32j + 8*(l/16) .. +8 for step j -- exactly the MFMA operand layout,
+//        so K goes from HBM to the matrix core with no shuffling.  Lane l
+//        then holds the scores of tokens 4*(l/16) .. +3 for head l%16.
+//   softmax: scores live in the exp2 domain (scale*log2 e folded in).  Each
+//        head keeps a reference max m that only moves when a chunk's max
+//        exceeds it by more than 8 (so p <= 256; the result is exact
+//        whatever the reference, since acc and l share it); the P.V
+//        accumulators are rescaled only on such a move (a wave-uniform
+//        branch, rare after the first chunks).
+//   PV:  P goes through LDS to the "row layout": lane (r, c) holds 16 bytes
+//        (8 elements) of V row 4i + r for pass i, so every V load
+//        instruction covers whole rows; acc[h][e] += p * V in fp32.
+//   Masked positions (before the offset, past seq_len, invalid table entry)
+//   get score -inf and their rows are never loaded, so poisoned (NaN) pool
+//   slots cannot leak in.
+//   The next chunk's K and V are loaded before the current one is computed.
+//
+// fp32 kernel (VALU): row layout for K and V, dot products reduced over the
+//   lanes of a row with DPP, per-chunk wave-uniform max; used for the fp32
+//   pool dtype.
 //
 // Split-K: with more than one split per sequence, each work item writes its
 // unnormalised (m, l, acc) to the workspace and a second kernel merges the
@@ -176,43 +186,60 @@ __device__ __forceinline__ float cross_rows_sum(float v) {
     return v;
 }
 
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-template <int DT, int D, int G>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
-    constexpr int E = Elem<DT>::kBytes;
-    constexpr int VEC = 16 / E;               // elements per 16-byte piece
-    constexpr int LPR = D / VEC;              // lanes per kv-head row
-    constexpr int RPI = 64 / LPR;             // rows per wavefront pass
-    constexpr int NP = kChunkTokens / RPI;    // passes per chunk
-    static_assert(LPR >= 4 && LPR <= 64 && RPI <= kChunkTokens, "head_dim out of range");
-    constexpr float kNegInf = -__builtin_huge_valf();
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-    __shared__ int32_t bt_s[kBtLds];
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-    // Workgroups are dealt round-robin to the 8 XCDs; renumber them so that
-    // consecutive logical items (same head group and split, consecutive
-    // sequences: a shared prefix is read by neighbours) share an XCD's L2.
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// (sequence, split, head group) of this workgroup.  Workgroups are dealt
+// round-robin to the 8 XCDs; renumber them so that consecutive logical
+// items share an XCD.  Logical order: head group, split, sequence.
+struct Item {
+    int seq, split, hg;
+};
+
+__device__ __forceinline__ Item work_item(const DecodeArgs &a) {
     const int nwg = gridDim.x;
     const int bid = blockIdx.x;
     const int xcd = bid & 7;
     const int per = nwg >> 3, rem = nwg & 7;
     const int lid = xcd * per + min(xcd, rem) + (bid >> 3);
-    const int seq = lid % a.num_seqs;
+    Item it;
+    it.seq = lid % a.num_seqs;
     const int rest = lid / a.num_seqs;
-    const int split = rest % a.max_splits;
-    const int hg = rest / a.max_splits;
+    it.split = rest % a.max_splits;
+    it.hg = rest / a.max_splits;
+    return it;
+}
 
-    const int L = a.seq_lens[seq];
-    const int t0 = split * a.split_tokens;
-    const bool direct = a.max_splits == 1;
-    if (!direct && t0 >= L) return;  // this split is empty (uniform per workgroup)
-    const int t1 = min(L, t0 + a.split_tokens);
-    const int64_t off = a.offsets[seq];
+// Flat-position range [lo, hi) of split j: [j*S, (j+1)*S) n [off, off+L).
+struct Range {
+    int64_t lo, hi, off;
+};
+
+__device__ __forceinline__ Range split_range(const DecodeArgs &a, int seq, int split) {
+    Range R;
+    const int64_t L = a.seq_lens[seq];
+    R.off = a.offsets[seq];
+    const int64_t S = a.split_tokens;
+    R.lo = max((int64_t)split * S, R.off);
+    R.hi = min((int64_t)(split + 1) * S, R.off + L);
+    return R;
+}
+
+// Stage the table entries that cover [lo, hi) into bt_s (entry jb0 first);
+// ids outside the pool or past the table become -1.  All threads of the
+// workgroup call this.
+__device__ __forceinline__ int64_t stage_table(const DecodeArgs &a, int seq, const Range &R,
+                                               int32_t *bt_s) {
     const int lbs = a.pool.lbs;
-    const int64_t bsm = (1ll << lbs) - 1;
-    const int64_t jb0 = (off + t0) >> lbs;
-    const int nbt = t1 > t0 ? (int)(((off + t1 - 1) >> lbs) - jb0 + 1) : 0;
+    const int64_t jb0 = R.lo >> lbs;
+    const int nbt = R.hi > R.lo ? (int)(((R.hi - 1) >> lbs) - jb0 + 1) : 0;
     for (int i = threadIdx.x; i < nbt; i += blockDim.x) {
         const int64_t j = jb0 + i;
         int32_t b = -1;
@@ -223,14 +250,46 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         bt_s[i] = b;
     }
     __syncthreads();
+    return jb0;
+}
+
+// Keep the compiler from moving LDS accesses across this point; the LDS
+// unit itself serves one wavefront's requests in order.
+__device__ __forceinline__ void wave_lds_order() {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
+// ---------------------------------------------------------------------------
+// fp32 pools: VALU kernel.
+// ---------------------------------------------------------------------------
+template <int DT, int D, int G>
+__global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
+    constexpr int E = Elem<DT>::kBytes;
+    constexpr int VEC = 16 / E;               // elements per 16-byte piece
+    constexpr int LPR = D / VEC;              // lanes per kv-head row
+    constexpr int RPI = 64 / LPR;             // rows per wavefront pass
+    constexpr int NP = kChunkTokens / RPI;    // passes per chunk
+    static_assert(LPR >= 4 && LPR <= 64 && RPI <= kChunkTokens, "head_dim out of range");
+
+    __shared__ int32_t bt_s[kBtLds];
+
+    const Item it = work_item(a);
+    const Range R = split_range(a, it.seq, it.split);
+    const bool direct = a.max_splits == 1;
+    if (!direct && R.hi <= R.lo) return;  // not a live split (uniform per workgroup)
+    const int64_t jb0 = stage_table(a, it.seq, R, bt_s);
 
     const int w = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
-    const int h = hg * a.heads_per_wg + w;
+    const int h = it.hg * a.heads_per_wg + w;
     if (h >= a.num_kv_heads) return;
     const int r = lane / LPR;
     const int c = lane % LPR;
     const int hq0 = h * G;
+    const int seq = it.seq;
+    const int lbs = a.pool.lbs;
+    const int64_t bsm = (1ll << lbs) - 1;
 
     u32x4 qv[G];
     {
@@ -251,17 +310,16 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     const char *kb = a.pool.k + a.pool.layer_off + (int64_t)h * (D * E) + c * 16;
     const char *vb = a.pool.v + a.pool.layer_off + (int64_t)h * (D * E) + c * 16;
 
-    for (int tc = t0; tc < t1; tc += kChunkTokens) {
+    for (int64_t pc = R.lo; pc < R.hi; pc += kChunkTokens) {
         u32x4 kx[NP], vx[NP];
         bool ok[NP];
 #pragma unroll
         for (int i = 0; i < NP; ++i) {
-            const int t = tc + i * RPI + r;
+            const int64_t p = pc + i * RPI + r;
             ok[i] = false;
             kx[i] = u32x4{0, 0, 0, 0};
             vx[i] = u32x4{0, 0, 0, 0};
-            if (t < t1) {
-                const int64_t p = off + t;
+            if (p < R.hi) {
                 const int32_t b = bt_s[(int)((p >> lbs) - jb0)];
                 if (b >= 0) {
                     ok[i] = true;
@@ -334,7 +392,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     } else {
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-            const int64_t item = ((int64_t)seq * a.max_splits + split) * a.num_q_heads + hq0 + g;
+            const int64_t item = ((int64_t)seq * a.max_splits + it.split) * a.num_q_heads + hq0 + g;
             float *wa = a.ws_acc + item * D + c * VEC;
 #pragma unroll
             for (int e = 0; e < VEC; e += 4)
@@ -345,35 +403,315 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     }
 }
 
-// Second pass: merge the splits of one (sequence, query head).
+// ---------------------------------------------------------------------------
+// bf16 pools: QK^T and P.V both on the matrix core.
+// UB: block_size >= 16, so a 16-position chunk lies inside one block and its
+// block id is wave-uniform (scalar address arithmetic).
+//
+// Per 16-position chunk and wavefront (one kv head):
+//   1. K and V rows arrive from HBM in "row layout" (lane (r, c) holds the
+//      16-byte piece c of row i*RPI + r: every load instruction covers whole
+//      rows) into a three-deep register ring, and are copied into this
+//      wave's LDS tiles [16 rows][D] with the 16-byte pieces of row t XOR-
+//      swizzled by t, so the column reads below hit distinct banks.
+//   2. QK^T: S^T (16 tokens x 16 heads) = K (16 x D) . Q^T (D x 16, heads
+//      >= G zero) with v_mfma_f32_16x16x32_bf16; the K operand is read from
+//      the tile (lane l: row l%16, elements 32j + 8*(l/16) ..).  Lane l then
+//      holds the scores of tokens 4*(l/16) .. +3 for head l%16.
+//   3. softmax in registers (exp2 domain, lazy reference max); the lane's 4
+//      probabilities, rounded to bf16, are exactly its A operand for P.V.
+//   4. P.V: O (16 heads x D) += P (16 x 16 tokens) . V (16 tokens x D) with
+//      v_mfma_f32_16x16x16_bf16, D/16 column slabs.  The V operand (4
+//      consecutive tokens of one column per lane) comes from the tile with
+//      ds_read_b64_tr_b16, the transposing LDS read.  Lane l accumulates
+//      O[head 4*(l/16) + i][16*slab + l%16].
+// Rows without a live token are zeroed in V (a 0 * NaN product would poison
+// the sum) and get score -inf.
+template <int D, int G, bool UB>
+__global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
+    constexpr int E = 2;
+    constexpr int ROWB = D * E;          // bytes of one kv-head row
+    constexpr int PPR = ROWB / 16;       // 16-byte pieces per row
+    constexpr int RPI = 64 / PPR;        // rows per load instruction
+    constexpr int NP = 16 / RPI;         // load instructions per tensor per chunk
+    constexpr int KS = D / 32;           // QK^T steps (k = 32)
+    constexpr int NV = D / 16;           // P.V column slabs (n = 16)
+    constexpr float kLazy = 8.0f;        // reference-max slack, log2 units
+    static_assert(D % 32 == 0 && PPR >= 4 && PPR <= 16 && G >= 1 && G <= 16, "shape");
+
+    __shared__ int32_t bt_s[kBtLds];
+    __shared__ __attribute__((aligned(16))) char tiles[4][2][16 * ROWB];  // per wave: K, V
+
+    const Item it = work_item(a);
+    const Range R = split_range(a, it.seq, it.split);
+    const bool direct = a.max_splits == 1;
+    if (!direct && R.hi <= R.lo) return;
+    const int64_t jb0 = stage_table(a, it.seq, R, bt_s);
+
+    const int w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int h = it.hg * a.heads_per_wg + w;
+    if (h >= a.num_kv_heads) return;
+    const int seq = it.seq;
+    const int n = lane & 15;       // MFMA: row / column index
+    const int g4 = lane >> 4;      // MFMA: k group
+    const int r = lane / PPR;      // row layout: row within an instruction
+    const int c = lane % PPR;      // row layout: piece of the row
+    const int lbs = a.pool.lbs;
+    const int64_t bsm = (1ll << lbs) - 1;
+    const int64_t row_bytes = a.pool.row_bytes;
+    const float sl2 = a.scale_log2;
+    char *tk = tiles[w][0];
+    char *tv = tiles[w][1];
+
+    // Q^T fragments (B operand of QK^T): head n, elements 32j + 8*g4 .. +8.
+    u32x4 qf[KS];
+    {
+        const char *qp = a.q + (((int64_t)seq * a.num_q_heads + (int64_t)h * G + n) * D + 8 * g4) * E;
+#pragma unroll
+        for (int j = 0; j < KS; ++j) qf[j] = n < G ? ld16(qp + 64 * j) : u32x4{0, 0, 0, 0};
+    }
+
+    float m_h = kNegInf;  // reference max of head n (same in its 4 lanes)
+    float l_h = 0.0f;     // this lane's share of head n's denominator
+    f32x4 acc[NV];
+#pragma unroll
+    for (int s = 0; s < NV; ++s) acc[s] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    const char *kh = a.pool.k + a.pool.layer_off + (int64_t)h * ROWB + 16 * c;
+    const char *vh = a.pool.v + a.pool.layer_off + (int64_t)h * ROWB + 16 * c;
+
+    // Loads of one chunk (every lane, unconditionally, in bounds: a missing
+    // block reads block 0 and is masked later), so the compiler waits only
+    // for the chunk about to be used.
+    auto load_chunk = [&](int64_t pc, u32x4 *kx, u32x4 *vx) {
+        if constexpr (UB) {
+            int32_t b = bt_s[(int)((pc >> lbs) - jb0)];
+            b = __builtin_amdgcn_readfirstlane(b);
+            const int64_t base = (int64_t)(b >= 0 ? b : 0) * a.pool.block_stride + (pc & bsm) * row_bytes;
+#pragma unroll
+            for (int i = 0; i < NP; ++i) {
+                const int64_t o = base + (i * RPI + r) * row_bytes;
+                kx[i] = ld16(kh + o);
+                vx[i] = ld16(vh + o);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < NP; ++i) {
+                const int64_t p = pc + i * RPI + r;
+                const bool in = p >= R.lo && p < R.hi;
+                const int32_t b = in ? bt_s[(int)((p >> lbs) - jb0)] : -1;
+                const int64_t o = (int64_t)(b >= 0 ? b : 0) * a.pool.block_stride + (p & bsm) * row_bytes;
+                kx[i] = ld16(kh + o);
+                vx[i] = ld16(vh + o);
+            }
+        }
+    };
+    auto live = [&](int64_t pc, int row) -> bool {
+        const int64_t p = pc + row;
+        if (p < R.lo || p >= R.hi) return false;
+        return bt_s[(int)((p >> lbs) - jb0)] >= 0;
+    };
+    // tile byte offset of 16-byte piece `piece` of row `row` (swizzled)
+    auto tile_off = [](int row, int piece) -> int { return row * ROWB + ((piece ^ (row & (PPR - 1))) << 4); };
+
+    auto compute = [&](int64_t pc, const u32x4 *kc, const u32x4 *vc) {
+        // block of this chunk present? (uniform when UB)
+        bool bok = true;
+        if constexpr (UB) bok = __builtin_amdgcn_readfirstlane(bt_s[(int)((pc >> lbs) - jb0)]) >= 0;
+        // whether chunk row `row` holds a live token
+        auto row_live = [&](int row) -> bool {
+            if constexpr (UB) {
+                const int64_t p = pc + row;
+                return bok && p >= R.lo && p < R.hi;
+            } else {
+                return live(pc, row);
+            }
+        };
+        // 1. stage the chunk in LDS
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+            const int row = i * RPI + r;
+            const u32x4 vrow = row_live(row) ? vc[i] : u32x4{0, 0, 0, 0};
+            *reinterpret_cast<u32x4 *>(tk + tile_off(row, c)) = kc[i];
+            *reinterpret_cast<u32x4 *>(tv + tile_off(row, c)) = vrow;
+        }
+        wave_lds_order();
+        // 2. scores: lane holds S[token 4*g4 + i][head n]
+        f32x4 sacc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int j = 0; j < KS; ++j) {
+            const u32x4 kf = *reinterpret_cast<const u32x4 *>(tk + tile_off(n, 4 * j + g4));
+            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf), as_bf16x8(qf[j]), sacc, 0, 0, 0);
+        }
+        // 3. softmax update
+        float s[4];
+        float cm = kNegInf;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            s[i] = row_live(4 * g4 + i) ? sacc[i] * sl2 : kNegInf;
+            cm = fmaxf(cm, s[i]);
+        }
+        cm = fmaxf(cm, __shfl_xor(cm, 16));
+        cm = fmaxf(cm, __shfl_xor(cm, 32));
+        float alpha = 1.0f;
+        if (cm > m_h + kLazy) {
+            alpha = m_h == kNegInf ? 0.0f : fast_exp2(m_h - cm);
+            m_h = cm;
+        }
+        float pr[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pr[i] = s[i] == kNegInf ? 0.0f : fast_exp2(s[i] - m_h);
+        // P in bf16 (the P.V A operand); the denominator uses the same
+        // rounded values
+        const uint32_t p01 = f32_to_bf16_bits(pr[0]) | (f32_to_bf16_bits(pr[1]) << 16);
+        const uint32_t p23 = f32_to_bf16_bits(pr[2]) | (f32_to_bf16_bits(pr[3]) << 16);
+        l_h = fmaf(l_h, alpha, (bf16_lo(p01) + bf16_hi(p01)) + (bf16_lo(p23) + bf16_hi(p23)));
+        if (__any(n < G && alpha != 1.0f)) {
+            // rescale O rows (heads 4*g4 + i) by their heads' alpha
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float al = __shfl(alpha, 4 * g4 + i);
+#pragma unroll
+                for (int sl = 0; sl < NV; ++sl) acc[sl][i] *= al;
+            }
+        }
+        // 4. P.V
+        typedef short s16x4 __attribute__((ext_vector_type(4)));
+        const s16x4 pa = __builtin_bit_cast(s16x4, (uint64_t)p01 | ((uint64_t)p23 << 32));
+        const int vrow = 4 * g4 + (n >> 2);
+        const int vhalf = (n & 3) * 8;  // byte offset of the 4-element group in its 16-B piece pair
+#pragma unroll
+        for (int sl = 0; sl < NV; ++sl) {
+            const int byte = 32 * sl + vhalf;  // column 16*sl + 4*(n&3), in bytes
+            const int off = tile_off(vrow, byte >> 4) + (byte & 15);
+            const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4 *)(
+                    (__attribute__((address_space(3))) char *)(tv) + off));
+            acc[sl] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, acc[sl], 0, 0, 0);
+        }
+        wave_lds_order();
+    };
+
+    // Two-stage register ring: while chunk c is computed, chunk c+1 is in
+    // flight; the prefetch past the last chunk re-reads the last chunk
+    // (cache hits) so every step issues the same loads.
+    const int64_t first = R.lo & ~int64_t(15);
+    if (first < R.hi) {
+        const int64_t last = (R.hi - 1) & ~int64_t(15);
+        u32x4 k0[NP], v0[NP], k1[NP], v1[NP];
+        load_chunk(first, k0, v0);
+        for (int64_t pc = first;;) {
+            load_chunk(min(pc + 16, last), k1, v1);
+            compute(pc, k0, v0);
+            pc += 16;
+            if (pc > last) break;
+            load_chunk(min(pc + 16, last), k0, v0);
+            compute(pc, k1, v1);
+            pc += 16;
+            if (pc > last) break;
+        }
+    }
+
+    // totals: l over the token groups; lane (g4, n) then holds head n's l
+    l_h += __shfl_xor(l_h, 16);
+    l_h += __shfl_xor(l_h, 32);
+    float lrow[4];  // l of the heads this lane's O rows belong to
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lrow[i] = __shfl(l_h, 4 * g4 + i);
+
+    if (direct) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int hd = 4 * g4 + i;
+            if (hd < G) {
+                const float inv = lrow[i] > 0.0f ? 1.0f / lrow[i] : 0.0f;
+                uint16_t *o = reinterpret_cast<uint16_t *>(a.out) +
+                              ((int64_t)seq * a.num_q_heads + (int64_t)h * G + hd) * D + n;
+#pragma unroll
+                for (int sl = 0; sl < NV; ++sl)
+                    o[16 * sl] = (uint16_t)f32_to_bf16_bits(lrow[i] > 0.0f ? acc[sl][i] / lrow[i] : 0.0f * inv);
+            }
+        }
+    } else {
+        const int64_t item0 = ((int64_t)seq * a.max_splits + it.split) * a.num_q_heads + (int64_t)h * G;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int hd = 4 * g4 + i;
+            if (hd < G) {
+                float *wa = a.ws_acc + (item0 + hd) * D + n;
+#pragma unroll
+                for (int sl = 0; sl < NV; ++sl) wa[16 * sl] = acc[sl][i];
+            }
+        }
+        if (g4 == 0 && n < G)
+            *reinterpret_cast<float2 *>(a.ws_ml + (item0 + n) * 2) = make_float2(m_h, l_h);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Second pass: merge the live splits of one (sequence, query head), in
+// split order.  Lane j of the wavefront first takes splits j, j+64, ... to
+// find the max and the weights; the weighted sum over splits then runs with
+// every lane owning D/64 output elements.
+// ---------------------------------------------------------------------------
 template <int DT, int D>
 __global__ __launch_bounds__(64) void reduce_kernel(DecodeArgs a) {
     constexpr int E = Elem<DT>::kBytes;
-    constexpr int DPT = D / 64;  // elements per lane
-    constexpr float kNegInf = -__builtin_huge_valf();
+    constexpr int DPT = D / 64;  // output elements per lane
+    extern __shared__ float w_s[];  // max_splits weights
+
     const int seq = blockIdx.x / a.num_q_heads;
     const int hq = blockIdx.x - seq * a.num_q_heads;
-    const int64_t L = a.seq_lens[seq];
-    int64_t ns = L > 0 ? (L + a.split_tokens - 1) / a.split_tokens : 0;
-    if (ns > a.max_splits) ns = a.max_splits;
     const int64_t item0 = (int64_t)seq * a.max_splits * a.num_q_heads + hq;
     const int64_t step = a.num_q_heads;
+    const int ns = a.max_splits;
 
+    // live splits: same rule as the partial kernel
     float M = kNegInf;
-    for (int64_t j = 0; j < ns; ++j) M = fmaxf(M, a.ws_ml[(item0 + j * step) * 2]);
+    for (int j = threadIdx.x; j < ns; j += 64) {
+        const Range R = split_range(a, seq, j);
+        if (R.hi > R.lo) M = fmaxf(M, a.ws_ml[(item0 + j * step) * 2]);
+    }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) M = fmaxf(M, __shfl_xor(M, m));
     float den = 0.0f;
+    for (int j = threadIdx.x; j < ns; j += 64) {
+        const Range R = split_range(a, seq, j);
+        float wj = 0.0f;
+        if (R.hi > R.lo) {
+            const float2 ml = *reinterpret_cast<const float2 *>(a.ws_ml + (item0 + j * step) * 2);
+            wj = ml.x == kNegInf ? 0.0f : fast_exp2(ml.x - M);
+            den = fmaf(ml.y, wj, den);
+        }
+        w_s[j] = wj;
+    }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) den += __shfl_xor(den, m);
+    __syncthreads();
+
     float o[DPT];
 #pragma unroll
     for (int k = 0; k < DPT; ++k) o[k] = 0.0f;
-    for (int64_t j = 0; j < ns; ++j) {
-        const int64_t item = item0 + j * step;
-        const float mj = a.ws_ml[item * 2];
-        const float lj = a.ws_ml[item * 2 + 1];
-        const float wj = mj == kNegInf ? 0.0f : fast_exp2(mj - M);
-        den = fmaf(lj, wj, den);
-        const float *src = a.ws_acc + item * D + threadIdx.x * DPT;
+    const float *src = a.ws_acc + item0 * D + threadIdx.x * DPT;
+    int j = 0;
+    for (; j + 4 <= ns; j += 4) {
+        float x[4][DPT];
 #pragma unroll
-        for (int k = 0; k < DPT; ++k) o[k] = fmaf(src[k], wj, o[k]);
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int k = 0; k < DPT; ++k) x[u][k] = w_s[j + u] != 0.0f ? src[(j + u) * step * D + k] : 0.0f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int k = 0; k < DPT; ++k) o[k] = fmaf(x[u][k], w_s[j + u], o[k]);
+    }
+    for (; j < ns; ++j) {
+        const float wj = w_s[j];
+        if (wj != 0.0f) {
+#pragma unroll
+            for (int k = 0; k < DPT; ++k) o[k] = fmaf(src[j * step * D + k], wj, o[k]);
+        }
     }
     char *dst = a.out + (((int64_t)seq * a.num_q_heads + hq) * D + threadIdx.x * DPT) * E;
 #pragma unroll
@@ -390,12 +728,19 @@ __global__ __launch_bounds__(64) void reduce_kernel(DecodeArgs a) {
 template <int DT, int D, int G>
 static hipError_t run_decode(const DecodeArgs &a, hipStream_t s) {
     const int64_t nwg = (int64_t)a.head_groups * a.max_splits * a.num_seqs;
-    hipLaunchKernelGGL((decode_kernel<DT, D, G>), dim3((unsigned)nwg), dim3(64 * a.heads_per_wg),
-                       0, s, a);
+    const dim3 grid((unsigned)nwg), block(64 * a.heads_per_wg);
+    if constexpr (DT == 1) {
+        if (a.pool.lbs >= 4)
+            hipLaunchKernelGGL((decode_mfma_kernel<D, G, true>), grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL((decode_mfma_kernel<D, G, false>), grid, block, 0, s, a);
+    } else {
+        hipLaunchKernelGGL((decode_valu_kernel<DT, D, G>), grid, block, 0, s, a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.max_splits == 1) return e;
     hipLaunchKernelGGL((reduce_kernel<DT, D>), dim3((unsigned)((int64_t)a.num_seqs * a.num_q_heads)),
-                       dim3(64), 0, s, a);
+                       dim3(64), (size_t)a.max_splits * sizeof(float), s, a);
     return hipGetLastError();
 }
 

@@ -88,15 +88,22 @@ bool split_ok(int64_t s, int64_t bs) {
     return s > 0 && s % kChunkTokens == 0 && s <= max_split_tokens(bs);
 }
 
-// Automatic split: the smallest power-of-two split >= 64 tokens that keeps the
-// work items (one wavefront each) at or below 16 per compute unit at
+// Flat table positions a sequence of max_len tokens can span (its first
+// block may start at any offset < bs).
+int64_t max_positions(int64_t max_len, int64_t bs) { return max_len > 0 ? max_len + bs - 1 : 0; }
+
+// Automatic split: the smallest power-of-two split >= 64 positions that keeps
+// the work items (one wavefront each) at or below 16 per compute unit at
 // max_seq_len.
 int64_t auto_split(int64_t num_seqs, int64_t hkv, int64_t max_len, int64_t bs) {
     const int64_t target = 16ll * cu_count();
     const int64_t smax = max_split_tokens(bs);
+    const int64_t span = max_positions(max_len, bs);
     int64_t s = 64;
     if (s > smax) s = smax;
-    while (s * 2 <= smax && num_seqs * hkv * ((max_len + s - 1) / s) > target) s *= 2;
+    while (s * 2 <= smax &&
+           (num_seqs * hkv * ((span + s - 1) / s) > target || (span + s - 1) / s > kMaxSplits))
+        s *= 2;
     return s;
 }
 
@@ -114,7 +121,9 @@ int plan_decode(int64_t num_seqs, int64_t hkv, int64_t hq, int64_t head_dim, int
     const int64_t split = split_req == 0 ? auto_split(num_seqs, hkv, max_len, bs) : split_req;
     if (!split_ok(split, bs)) return PKV_ERR_SHAPE;
     p->split = split;
-    p->max_splits = max_len > 0 ? (max_len + split - 1) / split : 1;
+    const int64_t span = max_positions(max_len, bs);
+    p->max_splits = span > 0 ? (span + split - 1) / split : 1;
+    if (p->max_splits > kMaxSplits) return PKV_ERR_SHAPE;
     if (p->max_splits <= 1) {
         p->max_splits = 1;
         p->ml_bytes = p->acc_bytes = 0;
@@ -275,7 +284,10 @@ PKV_API int paged_attn_decode(const pkv_pool *pool, int32_t layer, const void *q
         if (!aligned16(workspace)) return PKV_ERR_ALIGN;
     }
     const int64_t hkv = pool->num_kv_heads;
-    const int64_t hpw = hkv % 4 == 0 ? 4 : (hkv % 2 == 0 ? 2 : 1);
+    // kv heads (wavefronts) per workgroup
+    const int64_t hmax = 4;
+    int64_t hpw = 1;
+    while (hpw * 2 <= hmax && hkv % (hpw * 2) == 0) hpw *= 2;
     const int64_t groups = hkv / hpw;
     if (groups * p.max_splits * num_seqs > INT32_MAX) return PKV_ERR_SHAPE;
     DecodeArgs a{};

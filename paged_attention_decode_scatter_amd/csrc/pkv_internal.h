@@ -12,6 +12,9 @@ namespace pkv {
 constexpr int kChunkTokens = 16;
 // Block-table entries a decode or gather workgroup stages in LDS.
 constexpr int kBtLds = 1024;
+// Most splits per sequence (the merge pass keeps one weight per split in
+// LDS).
+constexpr int kMaxSplits = 4096;
 // Gather/scatter workgroup size.
 constexpr int kCopyThreads = 256;
 

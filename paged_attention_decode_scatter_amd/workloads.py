@@ -162,20 +162,20 @@ def tiny(device="cpu", seed=1000, **kw) -> PagedWorkload:
 def decode_batch(device="cpu", seed=1001, num_seqs=32, min_len=128, max_len=2048,
                  num_blocks=POOL_BLOCKS, num_layers=32, num_kv_heads=8, head_dim=128,
                  num_q_heads=32, dtype=torch.bfloat16, layer=0, with_pools=True,
-                 offsets=None) -> PagedWorkload:
+                 offsets=None, block_size=BLOCK_SIZE) -> PagedWorkload:
     g = _cpu_gen(seed)
     lens = torch.randint(min_len, max_len + 1, (num_seqs,), generator=g, dtype=torch.int64)
     if offsets is None:
         offs = torch.zeros(num_seqs, dtype=torch.int64)
     elif offsets == "random":
-        offs = torch.randint(0, BLOCK_SIZE, (num_seqs,), generator=g, dtype=torch.int64)
+        offs = torch.randint(0, block_size, (num_seqs,), generator=g, dtype=torch.int64)
     else:
         offs = torch.as_tensor(offsets, dtype=torch.int64)
     perm = torch.randperm(num_blocks, generator=g).to(torch.int32)
-    counts = [_n_blocks(int(l) + int(o), BLOCK_SIZE) for l, o in zip(lens, offs)]
+    counts = [_n_blocks(int(l) + int(o), block_size) for l, o in zip(lens, offs)]
     w = PagedWorkload(
         name="decode_batch", dtype=dtype, num_blocks=num_blocks, num_layers=num_layers,
-        block_size=BLOCK_SIZE, num_kv_heads=num_kv_heads, head_dim=head_dim,
+        block_size=block_size, num_kv_heads=num_kv_heads, head_dim=head_dim,
         num_q_heads=num_q_heads, layer=layer, scale=1.0 / math.sqrt(head_dim), seed=seed,
         block_tables=_tables_from_counts(counts, perm),
         seq_lens=lens.to(torch.int32), offsets=offs.to(torch.int32))

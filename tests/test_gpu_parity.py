@@ -236,6 +236,22 @@ def test_decode_small_grid(dev, dtype, head_dim, group):
         assert err <= TOL[dtype], (split, err)
 
 
+@pytest.mark.parametrize("bs", [1, 4, 32])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_decode_other_block_sizes(dev, bs, dtype):
+    """block_size below 16 (a 16-position chunk spans several blocks) and
+    above it (a chunk is part of one block), with random offsets."""
+    w = W.decode_batch(device=dev, seed=60 + bs, num_seqs=5, min_len=1, max_len=300,
+                       num_blocks=2048 // bs + 64, num_layers=2, num_kv_heads=2, head_dim=128,
+                       num_q_heads=8, dtype=dtype, layer=1, offsets="random", block_size=bs)
+    ref = oracle_decode_for(w)
+    for split in (16, 64, 0):
+        if split and split // bs + 2 > 1024:
+            continue
+        got = run_decode(w, split)
+        assert max_abs_err(got, ref) <= TOL[dtype], split
+
+
 @pytest.mark.parametrize("split", [16, 32, 0])
 def test_decode_edge_lengths_and_offsets(dev, split):
     w = small_decode(dev, seed=40, num_seqs=18, min_len=40, max_len=40, offsets=None)
