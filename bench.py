@@ -141,6 +141,72 @@ def prefill_ops(w_dec, N, W):
     }
 
 
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "decode_batch_traffic.json")
+DECODE_SOURCES = [os.path.join(ROOT, "paged_attention_decode_scatter_amd", "csrc", f)
+                  for f in ("kernels_decode.hip", "pagedkv_api.hip", "pkv_internal.h")]
+
+
+def decode_source_hash():
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in DECODE_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per decode launch from the committed counter record, or
+    None when the record is missing or the decode sources changed since."""
+    try:
+        with open(TRAFFIC_RECORD) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != decode_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def pmc_target(which, reps):
+    """Run only what a counter pass should see: the decode call on the
+    decode batch (layer rotated), or a plain device copy of 1 GiB (the
+    calibration for FETCH_SIZE / WRITE_SIZE)."""
+    import torch
+
+    from paged_attention_decode_scatter_amd import native as N
+    from paged_attention_decode_scatter_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    if which == "copy":
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        src.fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(reps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copied {reps} x 1 GiB")
+        return
+    N.load_library()
+    w = W.decode_batch(device=dev)
+    mx = w.max_seq_len
+    out = torch.empty_like(w.q)
+    split = N.paged_attn_decode_split_tokens(w.num_seqs, w.num_kv_heads, mx, w.block_size)
+    ws = torch.empty(max(16, N.paged_attn_decode_workspace_size(
+        w.num_seqs, w.num_kv_heads, w.num_q_heads, w.head_dim, mx, w.block_size, split)),
+        dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    for i in range(reps):
+        N.paged_attn_decode(w.k_pool, w.v_pool, i % w.num_layers, w.q, w.block_tables,
+                            w.seq_lens, w.offsets, mx, w.scale, split_tokens=split, out=out,
+                            workspace=ws)
+    torch.cuda.synchronize()
+    _, alg = decode_bytes(w, w.seq_lens.cpu().numpy())
+    log(f"ran {reps} decode launches, {alg} algorithmic bytes each, split {split}")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -149,6 +215,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ops", action="store_true")
     ap.add_argument("--split-tokens", type=int, default=0)
+    ap.add_argument("--pmc-target", choices=["decode", "copy"], default=None,
+                    help="run only the decode launches (or a 1 GiB copy) for counter passes")
+    ap.add_argument("--pmc-reps", type=int, default=20)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the hot path "
@@ -165,6 +234,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.pmc_target:
+        pmc_target(args.pmc_target, args.pmc_reps)
+        return
     dev = torch.device("cuda:0")
     N.load_library()
     log("building the decode-batch workload (2 x 16 GiB pools)")
@@ -272,7 +344,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": measured_traffic(),
             "algorithmic_bytes_per_launch": alg_bytes,
             "avg_launch_us": dec_avg * 1e3,
             "median_launch_us": dec_med * 1e3,

@@ -196,6 +196,13 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 
 constexpr float kNegInf = -__builtin_huge_valf();
 
+#ifndef PKV_DECODE_RING
+#define PKV_DECODE_RING 3
+#endif
+// Pipeline depth of the bf16 decode kernel (chunks in flight + the one
+// being computed).
+constexpr int kDecodeRing = PKV_DECODE_RING;
+
 // (sequence, split, head group) of this workgroup.  Workgroups are dealt
 // round-robin to the 8 XCDs; renumber them so that consecutive logical
 // items share an XCD.  Logical order: head group, split, sequence.
@@ -251,6 +258,14 @@ __device__ __forceinline__ int64_t stage_table(const DecodeArgs &a, int seq, con
     }
     __syncthreads();
     return jb0;
+}
+
+// Copy 16 bytes per lane from global memory straight into LDS: lane i's
+// bytes land at lds_wave_base + 16*i (global_load_lds_dwordx4).  The LDS
+// address must be the same in every lane.
+__device__ __forceinline__ void lds_copy16(const char *src, char *lds_wave_base) {
+    __builtin_amdgcn_global_load_lds(const_cast<char *>(src),
+                                     (__attribute__((address_space(3))) void *)lds_wave_base, 16, 0, 0);
 }
 
 // Keep the compiler from moving LDS accesses across this point; the LDS
@@ -409,38 +424,50 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
 // block id is wave-uniform (scalar address arithmetic).
 //
 // Per 16-position chunk and wavefront (one kv head):
-//   1. K and V rows arrive from HBM in "row layout" (lane (r, c) holds the
-//      16-byte piece c of row i*RPI + r: every load instruction covers whole
-//      rows) into a three-deep register ring, and are copied into this
-//      wave's LDS tiles [16 rows][D] with the 16-byte pieces of row t XOR-
-//      swizzled by t, so the column reads below hit distinct banks.
-//   2. QK^T: S^T (16 tokens x 16 heads) = K (16 x D) . Q^T (D x 16, heads
-//      >= G zero) with v_mfma_f32_16x16x32_bf16; the K operand is read from
-//      the tile (lane l: row l%16, elements 32j + 8*(l/16) ..).  Lane l then
-//      holds the scores of tokens 4*(l/16) .. +3 for head l%16.
-//   3. softmax in registers (exp2 domain, lazy reference max); the lane's 4
+//   Loads: K and V rows are read in "row layout" -- each load instruction
+//      moves four whole 256-byte rows (lane (r, c) takes 16-byte piece c of
+//      row r), the pattern the L1 and its TLB serve best.  K goes into a
+//      register ring, V straight into an LDS ring (global_load_lds_dwordx4),
+//      both NSLOT-1 chunks ahead of the chunk being computed.
+//   QK^T: the K chunk is written to a per-wave LDS tile and read back in the
+//      MFMA A-operand layout (lane l: row l%16, elements 32j + 8*(l/16) ..);
+//      S^T (16 tokens x 16 heads) = K . Q^T (heads >= G zero) with
+//      v_mfma_f32_16x16x32_bf16.  Lane l then holds the scores of tokens
+//      4*(l/16) .. +3 for head l%16.
+//   softmax in registers (exp2 domain, lazy reference max); the lane's four
 //      probabilities, rounded to bf16, are exactly its A operand for P.V.
-//   4. P.V: O (16 heads x D) += P (16 x 16 tokens) . V (16 tokens x D) with
-//      v_mfma_f32_16x16x16_bf16, D/16 column slabs.  The V operand (4
-//      consecutive tokens of one column per lane) comes from the tile with
-//      ds_read_b64_tr_b16, the transposing LDS read.  Lane l accumulates
-//      O[head 4*(l/16) + i][16*slab + l%16].
-// Rows without a live token are zeroed in V (a 0 * NaN product would poison
-// the sum) and get score -inf.
+//   P.V: the B operand (four consecutive tokens of one column per lane)
+//      comes from the V tile with ds_read_b64_tr_b16, the transposing LDS
+//      read; O (16 heads x D) += P . V with v_mfma_f32_16x16x16_bf16 per
+//      16-column slab; lane l accumulates O[head 4*(l/16) + i][16*slab + l%16].
+//   Both tiles are padded so the column-wise operand reads hit distinct LDS
+//      banks while every address stays one base register plus constants.
+//   Every load is issued unconditionally from an in-bounds address (a
+//   missing block reads block 0), so the waits stay exact.  Rows without a
+//   live token are zeroed in the V tile (a 0 * NaN product would poison the
+//   sum) and get score -inf.
 template <int D, int G, bool UB>
 __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     constexpr int E = 2;
     constexpr int ROWB = D * E;          // bytes of one kv-head row
     constexpr int PPR = ROWB / 16;       // 16-byte pieces per row
-    constexpr int RPI = 64 / PPR;        // rows per load instruction
-    constexpr int NP = 16 / RPI;         // load instructions per tensor per chunk
+    constexpr int RPI = 64 / PPR;        // rows per tile-load instruction
+    constexpr int NP = 16 / RPI;         // tile-load instructions per chunk
     constexpr int KS = D / 32;           // QK^T steps (k = 32)
     constexpr int NV = D / 16;           // P.V column slabs (n = 16)
+    constexpr int VSLAB = 1024 + 32;      // one tile-load instruction + padding
+    constexpr int VTILE = NP * VSLAB;     // V tile of one ring slot
+    constexpr int KROW = ROWB + 16;       // padded K-tile row
+    constexpr int KTILE = 16 * KROW;
+    constexpr int NSLOT = kDecodeRing;   // pipeline stages (chunks in flight + 1)
+    constexpr int LOADS = 2 * NP;        // vector-memory ops per chunk
     constexpr float kLazy = 8.0f;        // reference-max slack, log2 units
-    static_assert(D % 32 == 0 && PPR >= 4 && PPR <= 16 && G >= 1 && G <= 16, "shape");
+    static_assert(D % 32 == 0 && PPR >= 4 && PPR <= 16 && RPI * ROWB == 1024 && G >= 1 && G <= 16,
+                  "shape");
 
     __shared__ int32_t bt_s[kBtLds];
-    __shared__ __attribute__((aligned(16))) char tiles[4][2][16 * ROWB];  // per wave: K, V
+    __shared__ __attribute__((aligned(16))) char vtiles[4][NSLOT][VTILE];
+    __shared__ __attribute__((aligned(16))) char ktiles[4][KTILE];
 
     const Item it = work_item(a);
     const Range R = split_range(a, it.seq, it.split);
@@ -448,21 +475,19 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     if (!direct && R.hi <= R.lo) return;
     const int64_t jb0 = stage_table(a, it.seq, R, bt_s);
 
-    const int w = threadIdx.x >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int h = it.hg * a.heads_per_wg + w;
     if (h >= a.num_kv_heads) return;
     const int seq = it.seq;
     const int n = lane & 15;       // MFMA: row / column index
     const int g4 = lane >> 4;      // MFMA: k group
-    const int r = lane / PPR;      // row layout: row within an instruction
-    const int c = lane % PPR;      // row layout: piece of the row
     const int lbs = a.pool.lbs;
     const int64_t bsm = (1ll << lbs) - 1;
     const int64_t row_bytes = a.pool.row_bytes;
     const float sl2 = a.scale_log2;
-    char *tk = tiles[w][0];
-    char *tv = tiles[w][1];
+    char *vring = vtiles[w][0];
+    char *kt = ktiles[w];
 
     // Q^T fragments (B operand of QK^T): head n, elements 32j + 8*g4 .. +8.
     u32x4 qf[KS];
@@ -478,78 +503,84 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int s = 0; s < NV; ++s) acc[s] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    const char *kh = a.pool.k + a.pool.layer_off + (int64_t)h * ROWB + 16 * c;
-    const char *vh = a.pool.v + a.pool.layer_off + (int64_t)h * ROWB + 16 * c;
+    const char *kh = a.pool.k + a.pool.layer_off + (int64_t)h * ROWB;
+    const char *vh = a.pool.v + a.pool.layer_off + (int64_t)h * ROWB;
+    // Row-layout load role: load instruction i moves rows i + NP*q,
+    // q = lane / PPR, and this lane takes their 16-byte piece lane % PPR.
+    // In the V tile instruction i's 1 KiB lands at slab i (slabs padded so
+    // the four rows a P.V operand read touches sit in different banks); the
+    // K tile has padded rows for the same reason.
+    const int trow = lane / PPR;
+    const int tpp = lane % PPR;
 
-    // Loads of one chunk (every lane, unconditionally, in bounds: a missing
-    // block reads block 0 and is masked later), so the compiler waits only
-    // for the chunk about to be used.
-    auto load_chunk = [&](int64_t pc, u32x4 *kx, u32x4 *vx) {
+    // Issue the loads of chunk pc into K registers kx and V ring slot `slot`.
+    auto load_chunk = [&](int64_t pc, u32x4 *kx, int slot) {
+        char *dst = vring + slot * VTILE;
         if constexpr (UB) {
-            int32_t b = bt_s[(int)((pc >> lbs) - jb0)];
-            b = __builtin_amdgcn_readfirstlane(b);
+            int32_t b = __builtin_amdgcn_readfirstlane(bt_s[(int)((pc >> lbs) - jb0)]);
             const int64_t base = (int64_t)(b >= 0 ? b : 0) * a.pool.block_stride + (pc & bsm) * row_bytes;
+            const char *kb = kh + base;
+            const char *vb = vh + base;
 #pragma unroll
             for (int i = 0; i < NP; ++i) {
-                const int64_t o = base + (i * RPI + r) * row_bytes;
-                kx[i] = ld16(kh + o);
-                vx[i] = ld16(vh + o);
+                const uint32_t o = (uint32_t)((i + NP * trow) * row_bytes + 16 * tpp);
+                kx[i] = ld16(kb + o);
+                lds_copy16(vb + o, dst + i * VSLAB);
             }
         } else {
 #pragma unroll
             for (int i = 0; i < NP; ++i) {
-                const int64_t p = pc + i * RPI + r;
+                const int64_t p = pc + i + NP * trow;
                 const bool in = p >= R.lo && p < R.hi;
                 const int32_t b = in ? bt_s[(int)((p >> lbs) - jb0)] : -1;
-                const int64_t o = (int64_t)(b >= 0 ? b : 0) * a.pool.block_stride + (p & bsm) * row_bytes;
+                const int64_t o = (int64_t)(b >= 0 ? b : 0) * a.pool.block_stride + (p & bsm) * row_bytes + 16 * tpp;
                 kx[i] = ld16(kh + o);
-                vx[i] = ld16(vh + o);
+                lds_copy16(vh + o, dst + i * VSLAB);
             }
         }
     };
-    auto live = [&](int64_t pc, int row) -> bool {
-        const int64_t p = pc + row;
-        if (p < R.lo || p >= R.hi) return false;
-        return bt_s[(int)((p >> lbs) - jb0)] >= 0;
-    };
-    // tile byte offset of 16-byte piece `piece` of row `row` (swizzled)
-    auto tile_off = [](int row, int piece) -> int { return row * ROWB + ((piece ^ (row & (PPR - 1))) << 4); };
-
-    auto compute = [&](int64_t pc, const u32x4 *kc, const u32x4 *vc) {
-        // block of this chunk present? (uniform when UB)
+    auto compute = [&](int64_t pc, const u32x4 *kc, int slot) {
+        // This chunk's loads were issued two chunks ago; wait for them (the
+        // V tile is written by the copy engine, which the compiler does not
+        // track) while the next two chunks' loads stay in flight.
+        constexpr int ahead = (NSLOT - 1) * LOADS;
+        __builtin_amdgcn_s_waitcnt((ahead & 15) | ((ahead >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+        wave_lds_order();
+        char *vt = vring + slot * VTILE;
         bool bok = true;
         if constexpr (UB) bok = __builtin_amdgcn_readfirstlane(bt_s[(int)((pc >> lbs) - jb0)]) >= 0;
-        // whether chunk row `row` holds a live token
         auto row_live = [&](int row) -> bool {
-            if constexpr (UB) {
-                const int64_t p = pc + row;
-                return bok && p >= R.lo && p < R.hi;
-            } else {
-                return live(pc, row);
-            }
+            const int64_t p = pc + row;
+            const bool in = p >= R.lo && p < R.hi;
+            return UB ? (bok && in) : (in && bt_s[(int)((p >> lbs) - jb0)] >= 0);
         };
-        // 1. stage the chunk in LDS
+        const bool full = UB ? (bok && pc >= R.lo && pc + 16 <= R.hi) : false;
+        if (!full) {
+            // zero the tile rows that hold no live token
 #pragma unroll
-        for (int i = 0; i < NP; ++i) {
-            const int row = i * RPI + r;
-            const u32x4 vrow = row_live(row) ? vc[i] : u32x4{0, 0, 0, 0};
-            *reinterpret_cast<u32x4 *>(tk + tile_off(row, c)) = kc[i];
-            *reinterpret_cast<u32x4 *>(tv + tile_off(row, c)) = vrow;
+            for (int i = 0; i < NP; ++i) {
+                if (!row_live(i + NP * trow))
+                    *reinterpret_cast<u32x4 *>(vt + i * VSLAB + 16 * lane) = u32x4{0, 0, 0, 0};
+            }
+            wave_lds_order();
         }
+        // K chunk into the K tile, then back in operand layout
+#pragma unroll
+        for (int i = 0; i < NP; ++i)
+            *reinterpret_cast<u32x4 *>(kt + (i + NP * trow) * KROW + 16 * tpp) = kc[i];
         wave_lds_order();
-        // 2. scores: lane holds S[token 4*g4 + i][head n]
+        // scores: lane holds S[token 4*g4 + i][head n]
         f32x4 sacc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int j = 0; j < KS; ++j) {
-            const u32x4 kf = *reinterpret_cast<const u32x4 *>(tk + tile_off(n, 4 * j + g4));
+            const u32x4 kf = *reinterpret_cast<const u32x4 *>(kt + n * KROW + 16 * g4 + 64 * j);
             sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf), as_bf16x8(qf[j]), sacc, 0, 0, 0);
         }
-        // 3. softmax update
         float s[4];
         float cm = kNegInf;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            s[i] = row_live(4 * g4 + i) ? sacc[i] * sl2 : kNegInf;
+            s[i] = (full || row_live(4 * g4 + i)) ? sacc[i] * sl2 : kNegInf;
             cm = fmaxf(cm, s[i]);
         }
         cm = fmaxf(cm, __shfl_xor(cm, 16));
@@ -576,41 +607,46 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
                 for (int sl = 0; sl < NV; ++sl) acc[sl][i] *= al;
             }
         }
-        // 4. P.V
         typedef short s16x4 __attribute__((ext_vector_type(4)));
         const s16x4 pa = __builtin_bit_cast(s16x4, (uint64_t)p01 | ((uint64_t)p23 << 32));
+        // this lane's operand rows: token 4*g4 + (n >> 2), columns 16*sl + 4*(n&3)
         const int vrow = 4 * g4 + (n >> 2);
-        const int vhalf = (n & 3) * 8;  // byte offset of the 4-element group in its 16-B piece pair
+        const int vbase = (vrow % NP) * VSLAB + (vrow / NP) * ROWB + 8 * (n & 3);
 #pragma unroll
         for (int sl = 0; sl < NV; ++sl) {
-            const int byte = 32 * sl + vhalf;  // column 16*sl + 4*(n&3), in bytes
-            const int off = tile_off(vrow, byte >> 4) + (byte & 15);
+            const int off = vbase + 32 * sl;
             const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4 *)(
-                    (__attribute__((address_space(3))) char *)(tv) + off));
+                (__attribute__((address_space(3))) s16x4 *)((__attribute__((address_space(3))) char *)(vt) + off));
             acc[sl] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, acc[sl], 0, 0, 0);
         }
         wave_lds_order();
     };
 
-    // Two-stage register ring: while chunk c is computed, chunk c+1 is in
-    // flight; the prefetch past the last chunk re-reads the last chunk
-    // (cache hits) so every step issues the same loads.
+    // Ring of NSLOT stages: while chunk c is computed, chunks c+1 ..
+    // c+NSLOT-1 are in flight; prefetches past the last chunk re-read the
+    // last chunk (cache hits) so every step issues the same loads.  The
+    // inner loop is unrolled so ring indices are compile-time constants.
     const int64_t first = R.lo & ~int64_t(15);
     if (first < R.hi) {
         const int64_t last = (R.hi - 1) & ~int64_t(15);
-        u32x4 k0[NP], v0[NP], k1[NP], v1[NP];
-        load_chunk(first, k0, v0);
-        for (int64_t pc = first;;) {
-            load_chunk(min(pc + 16, last), k1, v1);
-            compute(pc, k0, v0);
-            pc += 16;
-            if (pc > last) break;
-            load_chunk(min(pc + 16, last), k0, v0);
-            compute(pc, k1, v1);
-            pc += 16;
-            if (pc > last) break;
+        u32x4 kring[NSLOT][NP];
+#pragma unroll
+        for (int q = 0; q < NSLOT - 1; ++q) load_chunk(min(first + 16 * q, last), kring[q], q);
+        bool done = false;
+        for (int64_t pc = first; !done;) {
+#pragma unroll
+            for (int q = 0; q < NSLOT; ++q) {
+                if (!done) {
+                    const int nq = (q + NSLOT - 1) % NSLOT;
+                    load_chunk(min(pc + 16 * (NSLOT - 1), last), kring[nq], nq);
+                    compute(pc, kring[q], q);
+                    pc += 16;
+                    done = pc > last;
+                }
+            }
         }
+        // drain the copy engine before the tiles' memory is released
+        __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xF << 8));
     }
 
     // totals: l over the token groups; lane (g4, n) then holds head n's l
@@ -625,12 +661,11 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
         for (int i = 0; i < 4; ++i) {
             const int hd = 4 * g4 + i;
             if (hd < G) {
-                const float inv = lrow[i] > 0.0f ? 1.0f / lrow[i] : 0.0f;
                 uint16_t *o = reinterpret_cast<uint16_t *>(a.out) +
                               ((int64_t)seq * a.num_q_heads + (int64_t)h * G + hd) * D + n;
 #pragma unroll
                 for (int sl = 0; sl < NV; ++sl)
-                    o[16 * sl] = (uint16_t)f32_to_bf16_bits(lrow[i] > 0.0f ? acc[sl][i] / lrow[i] : 0.0f * inv);
+                    o[16 * sl] = (uint16_t)f32_to_bf16_bits(lrow[i] > 0.0f ? acc[sl][i] / lrow[i] : 0.0f);
             }
         }
     } else {
@@ -650,33 +685,52 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Second pass: merge the live splits of one (sequence, query head), in
-// split order.  Lane j of the wavefront first takes splits j, j+64, ... to
-// find the max and the weights; the weighted sum over splits then runs with
-// every lane owning D/64 output elements.
+// Second pass: merge the live splits of one (sequence, query head):
+//   M = max_j m_j,  w_j = 2^(m_j - M),  L = sum_j l_j w_j,
+//   out = (sum_j w_j acc_j) / L.
+// One 256-thread workgroup per (sequence, query head).  The split weights
+// are computed once into LDS; thread t then owns output element t % D and
+// the splits j = t / D, t / D + NG, ... (NG = 256 / D groups), with its
+// loads unrolled so many are in flight; the NG group sums are added in
+// group order through LDS.  The partition is fixed, so results are
+// bitwise reproducible.
 // ---------------------------------------------------------------------------
+constexpr int kReduceThreads = 256;
+
 template <int DT, int D>
-__global__ __launch_bounds__(64) void reduce_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kReduceThreads) void reduce_kernel(DecodeArgs a) {
     constexpr int E = Elem<DT>::kBytes;
-    constexpr int DPT = D / 64;  // output elements per lane
-    extern __shared__ float w_s[];  // max_splits weights
+    constexpr int NG = kReduceThreads / D;  // split groups
+    static_assert(NG >= 1 && kReduceThreads % D == 0, "head_dim");
+    extern __shared__ float w_s[];          // max_splits weights
+    __shared__ float red_s[kReduceThreads / 64];
+    __shared__ float part_s[NG][D];
 
     const int seq = blockIdx.x / a.num_q_heads;
     const int hq = blockIdx.x - seq * a.num_q_heads;
     const int64_t item0 = (int64_t)seq * a.max_splits * a.num_q_heads + hq;
     const int64_t step = a.num_q_heads;
     const int ns = a.max_splits;
+    const int t = threadIdx.x;
+    const int wv = t >> 6;
 
-    // live splits: same rule as the partial kernel
+    // 1. max over live splits (same liveness rule as the partial kernel)
     float M = kNegInf;
-    for (int j = threadIdx.x; j < ns; j += 64) {
+    for (int j = t; j < ns; j += kReduceThreads) {
         const Range R = split_range(a, seq, j);
         if (R.hi > R.lo) M = fmaxf(M, a.ws_ml[(item0 + j * step) * 2]);
     }
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) M = fmaxf(M, __shfl_xor(M, m));
+    if ((t & 63) == 0) red_s[wv] = M;
+    __syncthreads();
+    M = red_s[0];
+#pragma unroll
+    for (int k = 1; k < kReduceThreads / 64; ++k) M = fmaxf(M, red_s[k]);
+    __syncthreads();
+    // 2. weights and denominator
     float den = 0.0f;
-    for (int j = threadIdx.x; j < ns; j += 64) {
+    for (int j = t; j < ns; j += kReduceThreads) {
         const Range R = split_range(a, seq, j);
         float wj = 0.0f;
         if (R.hi > R.lo) {
@@ -688,39 +742,47 @@ __global__ __launch_bounds__(64) void reduce_kernel(DecodeArgs a) {
     }
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) den += __shfl_xor(den, m);
+    if ((t & 63) == 0) red_s[wv] = den;
     __syncthreads();
+    den = red_s[0];
+#pragma unroll
+    for (int k = 1; k < kReduceThreads / 64; ++k) den += red_s[k];
 
-    float o[DPT];
+    // 3. weighted sum of this thread's splits for element d
+    const int d = t % D;
+    const int grp = t / D;
+    const float *src = a.ws_acc + item0 * D + d;
+    const int64_t jstride = step * D;
+    float o = 0.0f;
+    int j = grp;
+    constexpr int U = 8;
+    for (; j + (U - 1) * NG < ns; j += U * NG) {
+        float x[U], wu[U];
 #pragma unroll
-    for (int k = 0; k < DPT; ++k) o[k] = 0.0f;
-    const float *src = a.ws_acc + item0 * D + threadIdx.x * DPT;
-    int j = 0;
-    for (; j + 4 <= ns; j += 4) {
-        float x[4][DPT];
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-            for (int k = 0; k < DPT; ++k) x[u][k] = w_s[j + u] != 0.0f ? src[(j + u) * step * D + k] : 0.0f;
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-            for (int k = 0; k < DPT; ++k) o[k] = fmaf(x[u][k], w_s[j + u], o[k]);
-    }
-    for (; j < ns; ++j) {
-        const float wj = w_s[j];
-        if (wj != 0.0f) {
-#pragma unroll
-            for (int k = 0; k < DPT; ++k) o[k] = fmaf(src[j * step * D + k], wj, o[k]);
+        for (int u = 0; u < U; ++u) {
+            wu[u] = w_s[j + u * NG];
+            x[u] = src[(int64_t)(j + u * NG) * jstride];
         }
-    }
-    char *dst = a.out + (((int64_t)seq * a.num_q_heads + hq) * D + threadIdx.x * DPT) * E;
 #pragma unroll
-    for (int k = 0; k < DPT; ++k) {
-        const float v = den > 0.0f ? o[k] / den : 0.0f;
+        for (int u = 0; u < U; ++u) o = fmaf(wu[u] != 0.0f ? x[u] : 0.0f, wu[u], o);
+    }
+    for (; j < ns; j += NG) {
+        const float wj = w_s[j];
+        const float x = src[(int64_t)j * jstride];
+        o = fmaf(wj != 0.0f ? x : 0.0f, wj, o);
+    }
+    part_s[grp][d] = o;
+    __syncthreads();
+    if (grp == 0) {
+        float tot = part_s[0][d];
+#pragma unroll
+        for (int g = 1; g < NG; ++g) tot += part_s[g][d];
+        const float v = den > 0.0f ? tot / den : 0.0f;
+        char *dst = a.out + (((int64_t)seq * a.num_q_heads + hq) * D + d) * E;
         if constexpr (DT == 1) {
-            reinterpret_cast<uint16_t *>(dst)[k] = (uint16_t)f32_to_bf16_bits(v);
+            *reinterpret_cast<uint16_t *>(dst) = (uint16_t)f32_to_bf16_bits(v);
         } else {
-            reinterpret_cast<float *>(dst)[k] = v;
+            *reinterpret_cast<float *>(dst) = v;
         }
     }
 }
@@ -740,7 +802,7 @@ static hipError_t run_decode(const DecodeArgs &a, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.max_splits == 1) return e;
     hipLaunchKernelGGL((reduce_kernel<DT, D>), dim3((unsigned)((int64_t)a.num_seqs * a.num_q_heads)),
-                       dim3(64), (size_t)a.max_splits * sizeof(float), s, a);
+                       dim3(kReduceThreads), (size_t)a.max_splits * sizeof(float), s, a);
     return hipGetLastError();
 }
 

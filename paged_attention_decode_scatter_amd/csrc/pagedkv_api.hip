@@ -93,10 +93,11 @@ bool split_ok(int64_t s, int64_t bs) {
 int64_t max_positions(int64_t max_len, int64_t bs) { return max_len > 0 ? max_len + bs - 1 : 0; }
 
 // Automatic split: the smallest power-of-two split >= 64 positions that keeps
-// the work items (one wavefront each) at or below 16 per compute unit at
+// the work items (one wavefront each) at or below 10 per compute unit (about
+// what stays resident at once) at
 // max_seq_len.
 int64_t auto_split(int64_t num_seqs, int64_t hkv, int64_t max_len, int64_t bs) {
-    const int64_t target = 16ll * cu_count();
+    const int64_t target = 10ll * cu_count();
     const int64_t smax = max_split_tokens(bs);
     const int64_t span = max_positions(max_len, bs);
     int64_t s = 64;
@@ -192,8 +193,13 @@ PKV_API int kv_scatter(const pkv_pool *pool, int32_t layer, const void *k_src, c
     a.row_bytes = v.row_bytes;
     a.lbs = v.lbs;
     const int64_t cpr = v.row_bytes / 16;
-    // about 2048 16-byte pieces (32 KiB per tensor) per workgroup
+    // about 2048 16-byte pieces (32 KiB per tensor) per workgroup, but no
+    // fewer workgroups than a few per CU can absorb: a small scatter (one
+    // decode step's tokens) then runs one row per workgroup, each lane
+    // moving a single piece, so its latency is one load and one store
     int64_t tpw = 2048 / cpr;
+    const int64_t wide = (num_tokens + 1023) / 1024;
+    if (tpw > wide) tpw = wide;
     if (tpw < 1) tpw = 1;
     a.tok_per_wg = (int32_t)tpw;
     a.lcpr = (int32_t)pow2_or_neg(cpr);
