@@ -142,7 +142,9 @@ def test_workspace_size_and_split_choice(lib):
     # one split covers everything: no workspace
     assert ws(1, 2, 4, 64, 30, 16, 0) == 0
     # (m, l) block padded to 256 bytes, then the fp32 accumulators
-    n = 8 * 4 * 64                     # seqs x splits x q heads at split 8192, len 32768
+    # splits cover flat table positions, so a first-block offset of up to
+    # block_size - 1 can add one: ceil((32768 + 15) / 8192) = 5
+    n = 8 * 5 * 64                     # seqs x splits x q heads at split 8192, len 32768
     assert ws(8, 8, 64, 128, 32768, 16, 8192) == (n * 8 + 255) // 256 * 256 + n * 128 * 4
     assert ws(8, 8, 64, 128, 32768, 16, 24) == ctypes.c_size_t(-1).value
     split = lib.paged_attn_decode_split_tokens
