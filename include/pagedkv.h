@@ -198,13 +198,18 @@ PKV_API size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_kv
  *   split_tokens  tokens per split-K work item: 0 = automatic, else a
  *                 positive multiple of 16 with split_tokens/block_size + 2
  *                 <= 1024.  Sequences longer than one split are processed as
- *                 independent partial softmaxes merged by a second pass
- *                 (log-sum-exp); the partition and merge order are fixed, so
- *                 results are bitwise reproducible run to run.
+ *                 independent partial softmaxes, merged (log-sum-exp) by
+ *                 the work item that finishes last, in split order; the
+ *                 partition and merge order are fixed, so results are
+ *                 bitwise reproducible run to run.
  *   out           device [num_seqs, num_q_heads, head_dim], pool dtype
  *   workspace     device scratch of at least
  *                 paged_attn_decode_workspace_size(...) bytes (may be NULL
- *                 when that size is 0); overwritten.
+ *                 when that size is 0).  It must be all zero before its
+ *                 first use (e.g. one hipMemset after allocation); each call
+ *                 leaves its counters zero again, so a workspace is reused
+ *                 as is.  Calls that share a workspace must not overlap
+ *                 (issue them on one stream).
  * Supported: head_dim in {64, 128}, G in {1, 2, 4, 8}.
  * Errors: PKV_ERR_NULL, _DTYPE, _SHAPE, _LAYER, _ALIGN, _WORKSPACE,
  * _UNSUPPORTED, _LAUNCH.

@@ -226,12 +226,13 @@ __device__ __forceinline__ Item work_item(const DecodeArgs &a) {
 
 // Flat-position range [lo, hi) of split j: [j*S, (j+1)*S) n [off, off+L).
 struct Range {
-    int64_t lo, hi, off;
+    int64_t lo, hi, off, len;
 };
 
 __device__ __forceinline__ Range split_range(const DecodeArgs &a, int seq, int split) {
     Range R;
     const int64_t L = a.seq_lens[seq];
+    R.len = L;
     R.off = a.offsets[seq];
     const int64_t S = a.split_tokens;
     R.lo = max((int64_t)split * S, R.off);
@@ -275,6 +276,187 @@ __device__ __forceinline__ void wave_lds_order() {
     __builtin_amdgcn_wave_barrier();
 }
 
+template <int DT>
+__device__ __forceinline__ void store_out(char *dst, const float *v, int n);
+template <>
+__device__ __forceinline__ void store_out<0>(char *dst, const float *v, int n) {
+    if (n == 2)
+        *reinterpret_cast<float2 *>(dst) = make_float2(v[0], v[1]);
+    else
+        *reinterpret_cast<float *>(dst) = v[0];
+}
+template <>
+__device__ __forceinline__ void store_out<1>(char *dst, const float *v, int n) {
+    if (n == 2)
+        *reinterpret_cast<uint32_t *>(dst) = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+    else
+        *reinterpret_cast<uint16_t *>(dst) = (uint16_t)f32_to_bf16_bits(v[0]);
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
+    return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+    return x;
+}
+
+__device__ __forceinline__ float lane_value(float x, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
+}
+
+// Split partials are shared between workgroups that may run on different
+// XCDs, each with its own L2.  They are written and read with device-scope
+// accesses (stores write through, loads bypass the non-coherent caches), so
+// no cache writeback or invalidation is needed around the hand-over.
+__device__ __forceinline__ void st_dev(float *p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev2(float *p, float x, float y) {
+    const uint64_t u = (uint64_t)__float_as_uint(x) | ((uint64_t)__float_as_uint(y) << 32);
+    __hip_atomic_store(reinterpret_cast<uint64_t *>(p), u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float *p) {
+    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 ld_dev2(const float *p) {
+    const uint64_t u = __hip_atomic_load(reinterpret_cast<uint64_t *>(const_cast<float *>(p)),
+                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return make_float2(__uint_as_float((uint32_t)u), __uint_as_float((uint32_t)(u >> 32)));
+}
+
+// A sequence with no tokens attends to nothing: its output rows are zero.
+// Written by the split-0 workgroup of each head group (multi-split case).
+template <int DT, int D, int G>
+__device__ void zero_outputs(const DecodeArgs &a, int seq, int hg) {
+    constexpr int E = Elem<DT>::kBytes;
+    const int64_t n = (int64_t)a.heads_per_wg * G * D * E / 4;
+    uint32_t *o = reinterpret_cast<uint32_t *>(
+        a.out + ((int64_t)seq * a.num_q_heads + (int64_t)hg * a.heads_per_wg * G) * D * E);
+    for (int64_t i = threadIdx.x; i < n; i += blockDim.x) o[i] = 0u;
+}
+
+// Merge of the splits of one (sequence, kv head) into out, for its G query
+// heads:  M = max_j m_j,  w_j = 2^(m_j - M),
+//         out = (sum_j w_j acc_j) / (sum_j w_j l_j),
+// over the live splits j0 .. j1 (a contiguous run).  One wavefront; lane
+// covers D/64 consecutive output elements.  Splits are summed in index
+// order, so the result does not depend on which workgroup runs the merge.
+template <int DT, int D, int G>
+__device__ void merge_splits(const DecodeArgs &a, int seq, int h, int j0, int j1) {
+    constexpr int E = Elem<DT>::kBytes;
+    constexpr int PL = D / 64;
+    static_assert(PL == 1 || PL == 2, "head_dim");
+    const int lane = threadIdx.x & 63;
+    const int64_t hq0 = (int64_t)h * G;
+    const int64_t jstride = a.num_q_heads;  // items between consecutive splits
+    const int64_t item0 = (int64_t)seq * a.max_splits * a.num_q_heads + hq0;
+    const float *ml = a.ws_ml + item0 * 2;
+
+    float M[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) M[g] = kNegInf;
+    for (int j = j0 + lane; j <= j1; j += 64) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) M[g] = fmaxf(M[g], ld_dev(ml + (j * jstride + g) * 2));
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) M[g] = wave_max(M[g]);
+
+    float den[G], o[G][PL];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        den[g] = 0.0f;
+#pragma unroll
+        for (int e = 0; e < PL; ++e) o[g][e] = 0.0f;
+    }
+    const float *acc = a.ws_acc + item0 * D + lane * PL;
+    for (int jc = j0; jc <= j1; jc += 64) {
+        const int j = jc + lane;
+        float w[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            w[g] = 0.0f;
+            if (j <= j1) {
+                const float2 v = ld_dev2(ml + (j * jstride + g) * 2);
+                if (v.x != kNegInf) w[g] = fast_exp2(v.x - M[g]);
+                den[g] = fmaf(v.y, w[g], den[g]);
+            }
+        }
+        // four splits per step so their loads are in flight together; the
+        // steps past the last split repeat it with weight 0
+        const int nu = min(64, j1 - jc + 1);
+        for (int u0 = 0; u0 < nu; u0 += 4) {
+            float x[4][G][PL], wu[4][G];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int u = min(u0 + k, nu - 1);
+                const float *src = acc + (int64_t)(jc + u) * jstride * D;
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    wu[k][g] = u0 + k < nu ? lane_value(w[g], u) : 0.0f;
+                    if constexpr (PL == 2) {
+                        const float2 t = ld_dev2(src + g * D);
+                        x[k][g][0] = t.x;
+                        x[k][g][1] = t.y;
+                    } else {
+                        x[k][g][0] = ld_dev(src + g * D);
+                    }
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+#pragma unroll
+                    for (int e = 0; e < PL; ++e)
+                        o[g][e] = fmaf(wu[k][g] != 0.0f ? x[k][g][e] : 0.0f, wu[k][g], o[g][e]);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        const float L = wave_sum(den[g]);
+        float v[PL];
+#pragma unroll
+        for (int e = 0; e < PL; ++e) v[e] = L > 0.0f ? o[g][e] / L : 0.0f;
+        store_out<DT>(a.out + (((int64_t)seq * a.num_q_heads + hq0 + g) * D + lane * PL) * E, v, PL);
+    }
+}
+
+// End of a multi-split work item, run by every thread of the workgroup once
+// its partials are stored (device-scope stores): count the split in for
+// (sequence, head group); the workgroup that completes the count merges all
+// live splits.  Each wavefront waits until its partial stores are complete
+// before the barrier, so they are visible device-wide before the count is
+// published.  The finishing workgroup puts the counter back to zero for
+// the next call.
+template <int DT, int D, int G>
+__device__ void finish_split(const DecodeArgs &a, const Item &it, const Range &R) {
+    __shared__ int last_s;
+    const int64_t S = a.split_tokens;
+    const int j0 = (int)(R.off / S);
+    const int j1 = (int)((R.off + R.len - 1) / S);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t *cnt = a.ws_cnt + (int64_t)it.seq * a.head_groups + it.hg;
+        const uint32_t done = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = done == (uint32_t)(j1 - j0);
+        if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last_s = last;
+    }
+    __syncthreads();
+    if (!last_s) return;
+    const int w = threadIdx.x >> 6;
+    merge_splits<DT, D, G>(a, it.seq, it.hg * a.heads_per_wg + w, j0, j1);
+}
+
 // ---------------------------------------------------------------------------
 // fp32 pools: VALU kernel.
 // ---------------------------------------------------------------------------
@@ -292,13 +474,15 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
     const Item it = work_item(a);
     const Range R = split_range(a, it.seq, it.split);
     const bool direct = a.max_splits == 1;
-    if (!direct && R.hi <= R.lo) return;  // not a live split (uniform per workgroup)
+    if (!direct && R.hi <= R.lo) {  // not a live split (uniform per workgroup)
+        if (a.fused_merge && R.len <= 0 && it.split == 0) zero_outputs<DT, D, G>(a, it.seq, it.hg);
+        return;
+    }
     const int64_t jb0 = stage_table(a, it.seq, R, bt_s);
 
     const int w = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
-    const int h = it.hg * a.heads_per_wg + w;
-    if (h >= a.num_kv_heads) return;
+    const int h = it.hg * a.heads_per_wg + w;  // < num_kv_heads: head groups tile the heads
     const int r = lane / LPR;
     const int c = lane % LPR;
     const int hq0 = h * G;
@@ -394,9 +578,8 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
 #pragma unroll
         for (int e = 0; e < VEC; ++e) acc[g][e] = cross_rows_sum<LPR>(acc[g][e]);
     }
-    if (r != 0) return;
-
     if (direct) {
+        if (r != 0) return;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             float o[VEC];
@@ -404,18 +587,19 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
             for (int e = 0; e < VEC; ++e) o[e] = l[g] > 0.0f ? acc[g][e] / l[g] : 0.0f;
             store16<DT>(a.out + (((int64_t)seq * a.num_q_heads + hq0 + g) * D + c * VEC) * E, o);
         }
-    } else {
+        return;
+    }
+    if (r == 0) {
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             const int64_t item = ((int64_t)seq * a.max_splits + it.split) * a.num_q_heads + hq0 + g;
             float *wa = a.ws_acc + item * D + c * VEC;
 #pragma unroll
-            for (int e = 0; e < VEC; e += 4)
-                *reinterpret_cast<float4 *>(wa + e) =
-                    make_float4(acc[g][e], acc[g][e + 1], acc[g][e + 2], acc[g][e + 3]);
-            if (c == 0) *reinterpret_cast<float2 *>(a.ws_ml + item * 2) = make_float2(m[g], l[g]);
+            for (int e = 0; e < VEC; e += 2) st_dev2(wa + e, acc[g][e], acc[g][e + 1]);
+            if (c == 0) st_dev2(a.ws_ml + item * 2, m[g], l[g]);
         }
     }
+    if (a.fused_merge) finish_split<DT, D, G>(a, it, R);
 }
 
 // ---------------------------------------------------------------------------
@@ -472,13 +656,15 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     const Item it = work_item(a);
     const Range R = split_range(a, it.seq, it.split);
     const bool direct = a.max_splits == 1;
-    if (!direct && R.hi <= R.lo) return;
+    if (!direct && R.hi <= R.lo) {
+        if (a.fused_merge && R.len <= 0 && it.split == 0) zero_outputs<1, D, G>(a, it.seq, it.hg);
+        return;
+    }
     const int64_t jb0 = stage_table(a, it.seq, R, bt_s);
 
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    const int h = it.hg * a.heads_per_wg + w;
-    if (h >= a.num_kv_heads) return;
+    const int h = it.hg * a.heads_per_wg + w;  // < num_kv_heads: head groups tile the heads
     const int seq = it.seq;
     const int n = lane & 15;       // MFMA: row / column index
     const int g4 = lane >> 4;      // MFMA: k group
@@ -676,16 +862,17 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
             if (hd < G) {
                 float *wa = a.ws_acc + (item0 + hd) * D + n;
 #pragma unroll
-                for (int sl = 0; sl < NV; ++sl) wa[16 * sl] = acc[sl][i];
+                for (int sl = 0; sl < NV; ++sl) st_dev(wa + 16 * sl, acc[sl][i]);
             }
         }
-        if (g4 == 0 && n < G)
-            *reinterpret_cast<float2 *>(a.ws_ml + (item0 + n) * 2) = make_float2(m_h, l_h);
+        if (g4 == 0 && n < G) st_dev2(a.ws_ml + (item0 + n) * 2, m_h, l_h);
+        if (a.fused_merge) finish_split<1, D, G>(a, it, R);
     }
 }
 
 // ---------------------------------------------------------------------------
-// Second pass: merge the live splits of one (sequence, query head):
+// Merge kernel, used when sequences span many splits: merge the live
+// splits of one (sequence, query head):
 //   M = max_j m_j,  w_j = 2^(m_j - M),  L = sum_j l_j w_j,
 //   out = (sum_j w_j acc_j) / L.
 // One 256-thread workgroup per (sequence, query head).  The split weights
@@ -800,7 +987,7 @@ static hipError_t run_decode(const DecodeArgs &a, hipStream_t s) {
         hipLaunchKernelGGL((decode_valu_kernel<DT, D, G>), grid, block, 0, s, a);
     }
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || a.max_splits == 1) return e;
+    if (e != hipSuccess || a.max_splits == 1 || a.fused_merge) return e;
     hipLaunchKernelGGL((reduce_kernel<DT, D>), dim3((unsigned)((int64_t)a.num_seqs * a.num_q_heads)),
                        dim3(kReduceThreads), (size_t)a.max_splits * sizeof(float), s, a);
     return hipGetLastError();

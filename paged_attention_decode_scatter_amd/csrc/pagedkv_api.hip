@@ -92,18 +92,22 @@ bool split_ok(int64_t s, int64_t bs) {
 // block may start at any offset < bs).
 int64_t max_positions(int64_t max_len, int64_t bs) { return max_len > 0 ? max_len + bs - 1 : 0; }
 
-// Automatic split: the smallest power-of-two split >= 64 positions that keeps
-// the work items (one wavefront each) at or below 10 per compute unit (about
-// what stays resident at once) at
-// max_seq_len.
+// Automatic split (a power of two >= 64 positions), from measured decode
+// times on MI355X: grow the split while the work items (one wavefront each
+// per (sequence, kv head, split) at max_seq_len) exceed 20 per compute unit,
+// and keep growing it up to 256 positions while that still leaves at least
+// 2 items per compute unit (shorter splits cost more per token in pipeline
+// start-up and partials than they gain in balance).
 int64_t auto_split(int64_t num_seqs, int64_t hkv, int64_t max_len, int64_t bs) {
-    const int64_t target = 10ll * cu_count();
+    const int64_t cus = cu_count();
     const int64_t smax = max_split_tokens(bs);
     const int64_t span = max_positions(max_len, bs);
+    auto items = [&](int64_t s) { return num_seqs * hkv * ((span + s - 1) / s); };
+    auto splits = [&](int64_t s) { return (span + s - 1) / s; };
     int64_t s = 64;
     if (s > smax) s = smax;
-    while (s * 2 <= smax &&
-           (num_seqs * hkv * ((span + s - 1) / s) > target || (span + s - 1) / s > kMaxSplits))
+    while (s * 2 <= smax && (items(s) > 20 * cus || splits(s) > kMaxSplits ||
+                             (s < 256 && items(s * 2) >= 2 * cus)))
         s *= 2;
     return s;
 }
@@ -111,8 +115,10 @@ int64_t auto_split(int64_t num_seqs, int64_t hkv, int64_t max_len, int64_t bs) {
 struct DecodePlan {
     int64_t split;
     int64_t max_splits;
+    int64_t cnt_bytes;  // per (sequence, head group) split counters, padded to 256 bytes
     int64_t ml_bytes;   // (m, l) partials, padded to 256 bytes
     int64_t acc_bytes;  // acc partials
+    int64_t total() const { return cnt_bytes + ml_bytes + acc_bytes; }
 };
 
 int plan_decode(int64_t num_seqs, int64_t hkv, int64_t hq, int64_t head_dim, int64_t max_len,
@@ -127,8 +133,10 @@ int plan_decode(int64_t num_seqs, int64_t hkv, int64_t hq, int64_t head_dim, int
     if (p->max_splits > kMaxSplits) return PKV_ERR_SHAPE;
     if (p->max_splits <= 1) {
         p->max_splits = 1;
-        p->ml_bytes = p->acc_bytes = 0;
+        p->cnt_bytes = p->ml_bytes = p->acc_bytes = 0;
     } else {
+        // sized for one kv head per group, the most groups there can be
+        p->cnt_bytes = (num_seqs * hkv * 4 + 255) / 256 * 256;
         const int64_t items = num_seqs * p->max_splits * hq;
         p->ml_bytes = (items * 2 * 4 + 255) / 256 * 256;
         p->acc_bytes = items * head_dim * 4;
@@ -260,7 +268,7 @@ PKV_API size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_kv
     if (plan_decode(num_seqs, num_kv_heads, num_q_heads, head_dim, max_seq_len, block_size,
                     split_tokens, &p))
         return (size_t)-1;
-    return (size_t)(p.ml_bytes + p.acc_bytes);
+    return (size_t)p.total();
 }
 
 PKV_API int paged_attn_decode(const pkv_pool *pool, int32_t layer, const void *q,
@@ -284,7 +292,7 @@ PKV_API int paged_attn_decode(const pkv_pool *pool, int32_t layer, const void *q
     st = plan_decode(num_seqs, pool->num_kv_heads, num_q_heads, pool->head_dim, max_seq_len,
                      pool->block_size, split_tokens, &p);
     if (st) return st;
-    const int64_t need = p.ml_bytes + p.acc_bytes;
+    const int64_t need = p.total();
     if (need > 0) {
         if (!workspace || (int64_t)workspace_bytes < need) return PKV_ERR_WORKSPACE;
         if (!aligned16(workspace)) return PKV_ERR_ALIGN;
@@ -303,9 +311,10 @@ PKV_API int paged_attn_decode(const pkv_pool *pool, int32_t layer, const void *q
     a.seq_lens = seq_lens;
     a.offsets = offsets;
     a.out = static_cast<char *>(out);
-    a.ws_ml = need > 0 ? static_cast<float *>(workspace) : nullptr;
-    a.ws_acc = need > 0 ? reinterpret_cast<float *>(static_cast<char *>(workspace) + p.ml_bytes)
-                        : nullptr;
+    char *ws = need > 0 ? static_cast<char *>(workspace) : nullptr;
+    a.ws_cnt = ws ? reinterpret_cast<uint32_t *>(ws) : nullptr;
+    a.ws_ml = ws ? reinterpret_cast<float *>(ws + p.cnt_bytes) : nullptr;
+    a.ws_acc = ws ? reinterpret_cast<float *>(ws + p.cnt_bytes + p.ml_bytes) : nullptr;
     a.scale_log2 = scale * 1.4426950408889634f;
     a.bt_stride = bt_stride;
     a.num_seqs = num_seqs;
@@ -315,6 +324,7 @@ PKV_API int paged_attn_decode(const pkv_pool *pool, int32_t layer, const void *q
     a.max_splits = (int32_t)p.max_splits;
     a.heads_per_wg = (int32_t)hpw;
     a.head_groups = (int32_t)groups;
+    a.fused_merge = p.max_splits <= kFusedMergeMaxSplits;
     return status_of(launch_decode(a, pool->dtype, (int)pool->head_dim, group,
                                    static_cast<hipStream_t>(stream)));
 }

@@ -82,6 +82,7 @@ struct DecodeArgs {
     const int32_t *seq_lens;
     const int32_t *offsets;
     char *out;
+    uint32_t *ws_cnt;      // [num_seqs][head_groups] finished splits (zero between calls)
     float *ws_ml;          // [num_seqs][max_splits][num_q_heads][2]  (m, l)
     float *ws_acc;         // [num_seqs][max_splits][num_q_heads][head_dim]
     float scale_log2;      // scale * log2(e): scores live in the exp2 domain
@@ -93,7 +94,12 @@ struct DecodeArgs {
     int32_t max_splits;
     int32_t heads_per_wg;
     int32_t head_groups;
+    int32_t fused_merge;   // 1: the last split of a (sequence, head group) merges; 0: merge kernel
 };
+
+// Most splits per sequence merged by the last finishing workgroup; beyond
+// this a separate, wider merge kernel is faster.
+constexpr int kFusedMergeMaxSplits = 16;
 
 struct ValidateArgs {
     const int32_t *block_tables;

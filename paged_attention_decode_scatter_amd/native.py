@@ -200,7 +200,8 @@ def paged_attn_decode(k_pool, v_pool, layer, q, block_tables, seq_lens, offsets,
                       scale, split_tokens=0, out=None, workspace=None):
     """out[s, h] = softmax(scale * q[s, h] . K) . V over the sequence's cached
     tokens, read in place through the block tables.  `workspace` (uint8,
-    device) is allocated here when not given."""
+    device, zero before its first use; each call leaves it reusable) is
+    allocated here, zeroed, when not given."""
     pool = make_pool(k_pool, v_pool)
     _need(q, k_pool.dtype, "q")
     for t, n in ((block_tables, "block_tables"), (seq_lens, "seq_lens"), (offsets, "offsets")):
@@ -212,7 +213,7 @@ def paged_attn_decode(k_pool, v_pool, layer, q, block_tables, seq_lens, offsets,
     need = paged_attn_decode_workspace_size(num_seqs, k_pool.shape[3], hq, d, max_seq_len,
                                             k_pool.shape[2], split_tokens)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = load_library().paged_attn_decode(
         ctypes.byref(pool), layer, _ptr(q), hq, _ptr(block_tables), block_tables.shape[1],

@@ -141,11 +141,13 @@ def test_workspace_size_and_split_choice(lib):
     ws = lib.paged_attn_decode_workspace_size
     # one split covers everything: no workspace
     assert ws(1, 2, 4, 64, 30, 16, 0) == 0
-    # (m, l) block padded to 256 bytes, then the fp32 accumulators
-    # splits cover flat table positions, so a first-block offset of up to
-    # block_size - 1 can add one: ceil((32768 + 15) / 8192) = 5
+    # split counters (seqs x kv heads) and the (m, l) block, each padded to
+    # 256 bytes, then the fp32 accumulators.  Splits cover flat table
+    # positions, so a first-block offset of up to block_size - 1 can add
+    # one: ceil((32768 + 15) / 8192) = 5
     n = 8 * 5 * 64                     # seqs x splits x q heads at split 8192, len 32768
-    assert ws(8, 8, 64, 128, 32768, 16, 8192) == (n * 8 + 255) // 256 * 256 + n * 128 * 4
+    cnt = (8 * 8 * 4 + 255) // 256 * 256
+    assert ws(8, 8, 64, 128, 32768, 16, 8192) == cnt + (n * 8 + 255) // 256 * 256 + n * 128 * 4
     assert ws(8, 8, 64, 128, 32768, 16, 24) == ctypes.c_size_t(-1).value
     split = lib.paged_attn_decode_split_tokens
     for args in ((32, 8, 2048, 16), (64, 8, 4096, 16), (8, 8, 32768, 16), (1, 2, 30, 16),

@@ -59,10 +59,14 @@ def set_lens(w, lens, offsets):
     return w
 
 
-def run_decode(w, split=0, q=None):
-    return N.paged_attn_decode(w.k_pool, w.v_pool, w.layer, w.q if q is None else q,
-                               w.block_tables, w.seq_lens, w.offsets, w.max_seq_len, w.scale,
-                               split_tokens=split)
+def run_decode(w, split=0, q=None, workspace=None):
+    """Decode through the C ABI into an output prefilled with NaN, so any
+    element the kernels fail to write shows up."""
+    q = w.q if q is None else q
+    out = torch.full_like(q, float("nan"))
+    return N.paged_attn_decode(w.k_pool, w.v_pool, w.layer, q, w.block_tables, w.seq_lens,
+                               w.offsets, w.max_seq_len, w.scale, split_tokens=split, out=out,
+                               workspace=workspace)
 
 
 # ---------------------------------------------------------------------------
@@ -357,6 +361,33 @@ def test_validate_counts_violations(dev):
     # count too + 2 bad slots
     pad3 = int((bt[3] < 0).sum())
     assert n == 5 + pad3, (n, pad3)
+
+
+@pytest.mark.parametrize("split", [64, 16])
+def test_decode_workspace_reuse_leaves_counters_zero(dev, split):
+    """One zeroed workspace serves successive calls of different shapes: each
+    call gives the same bits as a call with a fresh workspace and leaves the
+    split counters (the first bytes of the workspace) zero again.  Split 64
+    keeps every sequence within 16 splits (merged by the last split's
+    workgroup); split 16 goes past that (merged by the merge kernel)."""
+    cases = [small_decode(dev, seed=60, num_seqs=12, max_len=300),
+             small_decode(dev, seed=61, num_seqs=5, min_len=100, max_len=500, num_kv_heads=8,
+                          group=1),
+             set_lens(small_decode(dev, seed=62, num_seqs=6, min_len=300, max_len=300),
+                      [0, 300, 1, 17, 0, 250], [3, 0, 15, 2, 0, 9])]
+    need = max(N.paged_attn_decode_workspace_size(w.num_seqs, w.num_kv_heads, w.num_q_heads,
+                                                  w.head_dim, w.max_seq_len, w.block_size, split)
+               for w in cases)
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+    for w in cases:
+        for _ in range(2):
+            got = run_decode(w, split, workspace=ws)
+            ref = run_decode(w, split)
+            itype = torch.int16 if got.element_size() == 2 else torch.int32
+            assert torch.equal(got.view(itype), ref.view(itype))
+            cnt = (w.num_seqs * w.num_kv_heads * 4 + 255) // 256 * 256
+            assert int(torch.count_nonzero(ws[:cnt])) == 0
+        assert max_abs_err(got, oracle_decode_for(w)) <= TOL[w.dtype]
 
 
 def test_decode_rejects_unsupported_group(dev):
