@@ -48,16 +48,74 @@ def decode_bytes(w, lens):
     return kv, kv + qo + tables + 8 * w.num_seqs
 
 
-def decode_kernel_label(w, split):
-    """Name of what one paged_attn_decode call launches for this batch."""
-    max_splits = -(-(w.max_seq_len + w.block_size - 1) // split)
+def decode_schedule(N, w, split_req):
+    """(split tokens or 0 for the balanced schedule, kernel label) of one
+    paged_attn_decode call on this batch."""
+    sched = N.paged_attn_decode_schedule(w.num_seqs, w.num_kv_heads, w.num_q_heads, w.head_dim,
+                                         w.max_seq_len, w.block_size, w.dtype, split_req)
     g = w.num_q_heads // w.num_kv_heads
+    if sched == 0:
+        return sched, f"decode_stream_kernel<D={w.head_dim},G={g}> (balanced schedule)"
     name = f"decode_mfma_kernel<D={w.head_dim},G={g}>"
+    max_splits = -(-(w.max_seq_len + w.block_size - 1) // sched)
     if max_splits == 1:
-        return name + " (one split per sequence)"
+        return sched, name + f" (split {sched}: one split per sequence)"
     if max_splits <= 16:
-        return name + f" (up to {max_splits} splits/seq, merged inside the kernel)"
-    return name + " + reduce_kernel (split merge)"
+        return sched, name + f" (split {sched}: up to {max_splits} splits/seq, merged in the kernel)"
+    return sched, name + f" + reduce_kernel (split {sched})"
+
+
+def other_decode_configs(w, N, W, reps=32):
+    """Decode alone on the prefix-sharing and long-context batches, over the
+    same pools (same geometry), back to back with the layer rotated."""
+    import ctypes
+
+    import torch
+
+    out = {}
+    for name in ("prefix_sharing", "long_context"):
+        o = W.PRESETS[name](device=w.k_pool.device, with_pools=False)
+        o.k_pool, o.v_pool = w.k_pool, w.v_pool
+        lens = o.seq_lens.cpu().numpy()
+        kv, alg = decode_bytes(o, lens)
+        need = N.paged_attn_decode_workspace_size(o.num_seqs, o.num_kv_heads, o.num_q_heads,
+                                                  o.head_dim, o.max_seq_len, o.block_size, 0)
+        ws = torch.zeros(max(need, 16), dtype=torch.uint8, device=o.q.device)
+        res = torch.empty_like(o.q)
+        # arguments marshalled once, as in the timed step
+        lib = N.load_library()
+        pool = N.make_pool(o.k_pool, o.v_pool)
+        stream = ctypes.c_void_p(torch.cuda.current_stream(o.q.device).cuda_stream)
+        P = lambda t: ctypes.c_void_p(t.data_ptr())
+        args = [(ctypes.byref(pool), l, P(o.q), o.num_q_heads, P(o.block_tables),
+                 o.block_tables.shape[1], P(o.seq_lens), P(o.offsets), o.num_seqs, o.max_seq_len,
+                 ctypes.c_float(o.scale), 0, P(res), P(ws), ws.numel(), stream)
+                for l in range(o.num_layers)]
+
+        def f(layer):
+            if lib.paged_attn_decode(*args[layer]):
+                raise RuntimeError(f"paged_attn_decode failed on {name}")
+
+        for i in range(3):
+            f(i)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for i in range(reps):
+            f(i % o.num_layers)
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) / reps * 1e3
+        sched, label = decode_schedule(N, o, 0)
+        entry = {"us": us, "algorithmic_bytes": alg, "GB/s": alg / us / 1e3,
+                 "frac": alg / us / 1e3 / HBM_PEAK_GBS, "kernel": label}
+        if name == "prefix_sharing":
+            bt = o.block_tables.cpu()
+            uniq = int(torch.unique(bt[bt >= 0]).numel())
+            entry["unique_kv_bytes"] = uniq * o.block_size * o.num_kv_heads * o.head_dim * 4
+        out[name] = entry
+        del o, ws, res
+    return out
 
 
 def time_op(fn, reps, layers, warm=3):
@@ -219,7 +277,7 @@ def pmc_target(which, reps):
     w = W.decode_batch(device=dev)
     mx = w.max_seq_len
     out = torch.empty_like(w.q)
-    split = N.paged_attn_decode_split_tokens(w.num_seqs, w.num_kv_heads, mx, w.block_size)
+    split = 0  # the automatic schedule, as in the timed run
     ws = torch.zeros(max(16, N.paged_attn_decode_workspace_size(
         w.num_seqs, w.num_kv_heads, w.num_q_heads, w.head_dim, mx, w.block_size, split)),
         dtype=torch.uint8, device=dev)
@@ -270,8 +328,8 @@ def main():
     lens = w.seq_lens.cpu().numpy()
     mx = w.max_seq_len
     kv_bytes, alg_bytes = decode_bytes(w, lens)
-    split = args.split_tokens or N.paged_attn_decode_split_tokens(w.num_seqs, w.num_kv_heads, mx,
-                                                                  w.block_size)
+    split = args.split_tokens
+    sched, kernel_label = decode_schedule(N, w, split)
     ws_bytes = N.paged_attn_decode_workspace_size(w.num_seqs, w.num_kv_heads, w.num_q_heads,
                                                   w.head_dim, mx, w.block_size, split)
     workspace = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
@@ -373,14 +431,14 @@ def main():
             "num_kv_heads": w.num_kv_heads,
             "head_dim": w.head_dim,
             "num_q_heads": w.num_q_heads,
-            "split_tokens": split,
+            "split_tokens": sched if sched > 0 else "balanced",
             "kv_bytes_per_step": kv_bytes,
             "step": "kv_slot_mapping + kv_scatter (1 new token/seq) + paged_attn_decode, "
                     "layer rotated over 32",
             "parallelism": "single GPU",
         },
         "roofline": {
-            "kernel": decode_kernel_label(w, split),
+            "kernel": kernel_label,
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
@@ -397,6 +455,8 @@ def main():
     if not args.no_ops:
         log("scatter/gather on the prefill shape")
         result["ops"] = prefill_ops(w, N, W)
+        log("decode on the prefix-sharing and long-context batches")
+        result["other_decode"] = other_decode_configs(w, N, W)
     if not args.no_cpu_baseline:
         log("CPU oracle baseline")
         result["cpu_baseline"] = cpu_baseline(w, lens)

@@ -157,21 +157,48 @@ PKV_API int kv_gather(const pkv_pool *pool, int32_t layer,
                       int32_t max_seq_len, void *k_out, void *v_out,
                       int64_t out_rows, void *stream);
 
+/* split_tokens value that asks paged_attn_decode for the balanced schedule */
+#define PKV_SPLIT_BALANCED (-1)
+
 /*
  * paged_attn_decode_split_tokens -- the split size (tokens per work item)
- * that paged_attn_decode uses when called with split_tokens = 0.  Depends
- * on the sizes and on the current device's compute-unit count (256 is
- * assumed when no device can be queried).  Returns a positive multiple of
- * 16, or a negative status for bad sizes.
+ * of the split schedule when paged_attn_decode is called with
+ * split_tokens = 0 and does not take the balanced schedule (see
+ * paged_attn_decode_schedule).  Depends on the sizes and on the current
+ * device's compute-unit count (256 is assumed when no device can be
+ * queried).  Returns a positive multiple of 16, or a negative status for
+ * bad sizes.
  */
 PKV_API int32_t paged_attn_decode_split_tokens(int32_t num_seqs, int32_t num_kv_heads,
                                                int32_t max_seq_len, int32_t block_size);
 
 /*
+ * paged_attn_decode_schedule -- which work schedule paged_attn_decode takes
+ * for these sizes, pool dtype (PKV_F32 / PKV_BF16) and split_tokens:
+ *   > 0  the split schedule with this many tokens per split: one workgroup
+ *        per (sequence, split of split_tokens flat positions, group of kv
+ *        heads);
+ *     0  the balanced schedule: one resident generation of workgroups, each
+ *        taking an equal share of all (kv-head group, sequence,
+ *        16-position chunk) units.  Taken for bf16 pools with at most 4096
+ *        sequences when split_tokens = PKV_SPLIT_BALANCED, or when
+ *        split_tokens = 0 and the batch holds at least 512 MiB of K/V at
+ *        max_seq_len;
+ *   < 0  a status for bad sizes or dtype (PKV_ERR_UNSUPPORTED for a
+ *        balanced request on an fp32 pool or more than 4096 sequences).
+ * Both compute the same function; they differ only in fp32 rounding order.
+ */
+PKV_API int32_t paged_attn_decode_schedule(int32_t num_seqs, int32_t num_kv_heads,
+                                           int32_t num_q_heads, int32_t head_dim,
+                                           int32_t max_seq_len, int32_t block_size,
+                                           int32_t dtype, int32_t split_tokens);
+
+/*
  * paged_attn_decode_workspace_size -- bytes of device workspace that
- * paged_attn_decode needs for these sizes and this split_tokens (0 = the
- * automatic choice above).  0 means no workspace is needed (every sequence
- * fits one split).  Returns (size_t)-1 for bad sizes.
+ * paged_attn_decode needs for these sizes and this split_tokens.  With
+ * split_tokens = 0 it covers either schedule.  0 means no workspace is
+ * needed (every sequence fits one split).  Returns (size_t)-1 for bad
+ * sizes.
  */
 PKV_API size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_kv_heads,
                                                 int32_t num_q_heads, int32_t head_dim,
@@ -195,13 +222,17 @@ PKV_API size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_kv
  *   block_tables, seq_lens, offsets  as for kv_gather
  *   max_seq_len   host bound on every seq_len
  *   scale         softmax scale (e.g. 1/sqrt(head_dim))
- *   split_tokens  tokens per split-K work item: 0 = automatic, else a
- *                 positive multiple of 16 with split_tokens/block_size + 2
- *                 <= 1024.  Sequences longer than one split are processed as
- *                 independent partial softmaxes, merged (log-sum-exp) by
- *                 the work item that finishes last, in split order; the
- *                 partition and merge order are fixed, so results are
- *                 bitwise reproducible run to run.
+ *   split_tokens  0 = automatic (see paged_attn_decode_schedule);
+ *                 PKV_SPLIT_BALANCED = the balanced schedule (bf16 pools, at
+ *                 most 4096 sequences, else PKV_ERR_UNSUPPORTED); else the
+ *                 tokens per split-K work item, a positive multiple of 16
+ *                 with split_tokens/block_size + 2 <= 1024.  A sequence
+ *                 spread over several work items is computed as partial
+ *                 softmaxes, merged (log-sum-exp) by the work item that
+ *                 finishes last (or, past 16 splits, by a second kernel),
+ *                 in a fixed order; the partition depends only on the
+ *                 sizes and the device's compute-unit count, so results
+ *                 are bitwise reproducible run to run.
  *   out           device [num_seqs, num_q_heads, head_dim], pool dtype
  *   workspace     device scratch of at least
  *                 paged_attn_decode_workspace_size(...) bytes (may be NULL

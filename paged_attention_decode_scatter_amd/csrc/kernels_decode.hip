@@ -340,29 +340,29 @@ __device__ void zero_outputs(const DecodeArgs &a, int seq, int hg) {
     for (int64_t i = threadIdx.x; i < n; i += blockDim.x) o[i] = 0u;
 }
 
-// Merge of the splits of one (sequence, kv head) into out, for its G query
-// heads:  M = max_j m_j,  w_j = 2^(m_j - M),
-//         out = (sum_j w_j acc_j) / (sum_j w_j l_j),
-// over the live splits j0 .. j1 (a contiguous run).  One wavefront; lane
-// covers D/64 consecutive output elements.  Splits are summed in index
-// order, so the result does not depend on which workgroup runs the merge.
-template <int DT, int D, int G>
-__device__ void merge_splits(const DecodeArgs &a, int seq, int h, int j0, int j1) {
+// Merge of partial results into out for the G query heads of one kv head:
+//   M = max_i m_i,  w_i = 2^(m_i - M),
+//   out = (sum_i w_i acc_i) / (sum_i w_i l_i)
+// over n records.  Record i of query head g has its (m, l) at
+// ml + (slot(i) * hstride + g) * 2 and its acc row at
+// acc + (slot(i) * hstride + g) * D.  One wavefront; lane covers D/64
+// consecutive output elements.  Records are summed in index order, so the
+// result does not depend on which workgroup runs the merge.
+template <int DT, int D, int G, typename Slot>
+__device__ void merge_records(char *out_row0, const float *ml, const float *accb, int64_t hstride,
+                              int n, Slot slot) {
     constexpr int E = Elem<DT>::kBytes;
     constexpr int PL = D / 64;
     static_assert(PL == 1 || PL == 2, "head_dim");
     const int lane = threadIdx.x & 63;
-    const int64_t hq0 = (int64_t)h * G;
-    const int64_t jstride = a.num_q_heads;  // items between consecutive splits
-    const int64_t item0 = (int64_t)seq * a.max_splits * a.num_q_heads + hq0;
-    const float *ml = a.ws_ml + item0 * 2;
 
     float M[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) M[g] = kNegInf;
-    for (int j = j0 + lane; j <= j1; j += 64) {
+    for (int i = lane; i < n; i += 64) {
+        const int64_t r = slot(i) * hstride;
 #pragma unroll
-        for (int g = 0; g < G; ++g) M[g] = fmaxf(M[g], ld_dev(ml + (j * jstride + g) * 2));
+        for (int g = 0; g < G; ++g) M[g] = fmaxf(M[g], ld_dev(ml + (r + g) * 2));
     }
 #pragma unroll
     for (int g = 0; g < G; ++g) M[g] = wave_max(M[g]);
@@ -374,28 +374,28 @@ __device__ void merge_splits(const DecodeArgs &a, int seq, int h, int j0, int j1
 #pragma unroll
         for (int e = 0; e < PL; ++e) o[g][e] = 0.0f;
     }
-    const float *acc = a.ws_acc + item0 * D + lane * PL;
-    for (int jc = j0; jc <= j1; jc += 64) {
-        const int j = jc + lane;
+    const float *acc = accb + lane * PL;
+    for (int ic = 0; ic < n; ic += 64) {
+        const int i = ic + lane;
         float w[G];
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             w[g] = 0.0f;
-            if (j <= j1) {
-                const float2 v = ld_dev2(ml + (j * jstride + g) * 2);
+            if (i < n) {
+                const float2 v = ld_dev2(ml + (slot(i) * hstride + g) * 2);
                 if (v.x != kNegInf) w[g] = fast_exp2(v.x - M[g]);
                 den[g] = fmaf(v.y, w[g], den[g]);
             }
         }
-        // four splits per step so their loads are in flight together; the
-        // steps past the last split repeat it with weight 0
-        const int nu = min(64, j1 - jc + 1);
+        // four records per step so their loads are in flight together; the
+        // steps past the last record repeat it with weight 0
+        const int nu = min(64, n - ic);
         for (int u0 = 0; u0 < nu; u0 += 4) {
             float x[4][G][PL], wu[4][G];
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const int u = min(u0 + k, nu - 1);
-                const float *src = acc + (int64_t)(jc + u) * jstride * D;
+                const float *src = acc + slot(ic + u) * hstride * D;
 #pragma unroll
                 for (int g = 0; g < G; ++g) {
                     wu[k][g] = u0 + k < nu ? lane_value(w[g], u) : 0.0f;
@@ -425,36 +425,47 @@ __device__ void merge_splits(const DecodeArgs &a, int seq, int h, int j0, int j1
         float v[PL];
 #pragma unroll
         for (int e = 0; e < PL; ++e) v[e] = L > 0.0f ? o[g][e] / L : 0.0f;
-        store_out<DT>(a.out + (((int64_t)seq * a.num_q_heads + hq0 + g) * D + lane * PL) * E, v, PL);
+        store_out<DT>(out_row0 + ((int64_t)g * D + lane * PL) * E, v, PL);
     }
 }
 
-// End of a multi-split work item, run by every thread of the workgroup once
-// its partials are stored (device-scope stores): count the split in for
-// (sequence, head group); the workgroup that completes the count merges all
-// live splits.  Each wavefront waits until its partial stores are complete
-// before the barrier, so they are visible device-wide before the count is
-// published.  The finishing workgroup puts the counter back to zero for
-// the next call.
-template <int DT, int D, int G>
-__device__ void finish_split(const DecodeArgs &a, const Item &it, const Range &R) {
+// Count one finished contribution to a merge group; true, in every thread,
+// for the workgroup that completes the count of `expected`.  Partials are
+// written with device-scope stores and each wavefront waits until its
+// stores are complete before the barrier, so they are visible device-wide
+// before the count is published.  The completing workgroup puts the counter
+// back to zero for the next call.  Called by all threads of the workgroup.
+__device__ bool count_in(uint32_t *cnt, uint32_t expected) {
     __shared__ int last_s;
-    const int64_t S = a.split_tokens;
-    const int j0 = (int)(R.off / S);
-    const int j1 = (int)((R.off + R.len - 1) / S);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (threadIdx.x == 0) {
-        uint32_t *cnt = a.ws_cnt + (int64_t)it.seq * a.head_groups + it.hg;
         const uint32_t done = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const bool last = done == (uint32_t)(j1 - j0);
+        const bool last = done + 1 == expected;
         if (last) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         last_s = last;
     }
     __syncthreads();
-    if (!last_s) return;
-    const int w = threadIdx.x >> 6;
-    merge_splits<DT, D, G>(a, it.seq, it.hg * a.heads_per_wg + w, j0, j1);
+    return last_s != 0;
+}
+
+// End of a multi-split work item (split schedule): count the split in for
+// (sequence, head group); the workgroup that completes the count merges the
+// live splits j0 .. j1 of the sequence, each wavefront the G query heads of
+// its kv head.
+template <int DT, int D, int G>
+__device__ void finish_split(const DecodeArgs &a, const Item &it, const Range &R) {
+    constexpr int E = Elem<DT>::kBytes;
+    const int64_t S = a.split_tokens;
+    const int j0 = (int)(R.off / S);
+    const int j1 = (int)((R.off + R.len - 1) / S);
+    if (!count_in(a.ws_cnt + (int64_t)it.seq * a.head_groups + it.hg, (uint32_t)(j1 - j0 + 1))) return;
+    const int h = it.hg * a.heads_per_wg + (threadIdx.x >> 6);
+    const int64_t hq0 = (int64_t)h * G;
+    const int64_t item0 = (int64_t)it.seq * a.max_splits * a.num_q_heads + hq0;
+    merge_records<DT, D, G>(a.out + ((int64_t)it.seq * a.num_q_heads + hq0) * D * E, a.ws_ml + item0 * 2,
+                            a.ws_acc + item0 * D, a.num_q_heads, j1 - j0 + 1,
+                            [=](int i) { return (int64_t)(j0 + i); });
 }
 
 // ---------------------------------------------------------------------------
@@ -630,64 +641,56 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
 //   missing block reads block 0), so the waits stay exact.  Rows without a
 //   live token are zeroed in the V tile (a 0 * NaN product would poison the
 //   sum) and get score -inf.
-template <int D, int G, bool UB>
-__global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
-    constexpr int E = 2;
-    constexpr int ROWB = D * E;          // bytes of one kv-head row
-    constexpr int PPR = ROWB / 16;       // 16-byte pieces per row
-    constexpr int RPI = 64 / PPR;        // rows per tile-load instruction
-    constexpr int NP = 16 / RPI;         // tile-load instructions per chunk
-    constexpr int KS = D / 32;           // QK^T steps (k = 32)
-    constexpr int NV = D / 16;           // P.V column slabs (n = 16)
-    constexpr int VSLAB = 1024 + 32;      // one tile-load instruction + padding
-    constexpr int VTILE = NP * VSLAB;     // V tile of one ring slot
-    constexpr int KROW = ROWB + 16;       // padded K-tile row
-    constexpr int KTILE = 16 * KROW;
-    constexpr int NSLOT = kDecodeRing;   // pipeline stages (chunks in flight + 1)
-    constexpr int LOADS = 2 * NP;        // vector-memory ops per chunk
-    constexpr float kLazy = 8.0f;        // reference-max slack, log2 units
-    static_assert(D % 32 == 0 && PPR >= 4 && PPR <= 16 && RPI * ROWB == 1024 && G >= 1 && G <= 16,
-                  "shape");
+template <int D>
+struct MfmaShape {
+    static constexpr int E = 2;
+    static constexpr int ROWB = D * E;           // bytes of one kv-head row
+    static constexpr int PPR = ROWB / 16;        // 16-byte pieces per row
+    static constexpr int RPI = 64 / PPR;         // rows per tile-load instruction
+    static constexpr int NP = 16 / RPI;          // tile-load instructions per chunk
+    static constexpr int KS = D / 32;            // QK^T steps (k = 32)
+    static constexpr int NV = D / 16;            // P.V column slabs (n = 16)
+    static constexpr int VSLAB = 1024 + 32;      // one tile-load instruction + padding
+    static constexpr int VTILE = NP * VSLAB;     // V tile of one ring slot
+    static constexpr int KROW = ROWB + 16;       // padded K-tile row
+    static constexpr int KTILE = 16 * KROW;
+    static constexpr int NSLOT = kDecodeRing;    // pipeline stages (chunks in flight + 1)
+    static constexpr int LOADS = 2 * NP;         // vector-memory ops per chunk
+    static_assert(D % 32 == 0 && PPR >= 4 && PPR <= 16 && RPI * ROWB == 1024, "shape");
+};
 
-    __shared__ int32_t bt_s[kBtLds];
-    __shared__ __attribute__((aligned(16))) char vtiles[4][NSLOT][VTILE];
-    __shared__ __attribute__((aligned(16))) char ktiles[4][KTILE];
-
-    const Item it = work_item(a);
-    const Range R = split_range(a, it.seq, it.split);
-    const bool direct = a.max_splits == 1;
-    if (!direct && R.hi <= R.lo) {
-        if (a.fused_merge && R.len <= 0 && it.split == 0) zero_outputs<1, D, G>(a, it.seq, it.hg);
-        return;
-    }
-    const int64_t jb0 = stage_table(a, it.seq, R, bt_s);
-
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+// Q^T fragments of kv head h's G query heads (B operand of QK^T): lane l
+// holds head l%16 (zero for heads >= G), elements 32j + 8*(l/16) .. +8.
+template <int D, int G>
+__device__ __forceinline__ void load_q(const DecodeArgs &a, int seq, int h,
+                                       u32x4 (&qf)[MfmaShape<D>::KS]) {
     const int lane = threadIdx.x & 63;
-    const int h = it.hg * a.heads_per_wg + w;  // < num_kv_heads: head groups tile the heads
-    const int seq = it.seq;
+    const int n = lane & 15, g4 = lane >> 4;
+    const char *qp = a.q + (((int64_t)seq * a.num_q_heads + (int64_t)h * G + n) * D + 8 * g4) * 2;
+#pragma unroll
+    for (int j = 0; j < MfmaShape<D>::KS; ++j) qf[j] = n < G ? ld16(qp + 64 * j) : u32x4{0, 0, 0, 0};
+}
+
+// Attention of one wavefront's kv head h over the flat positions [R.lo, R.hi)
+// of one sequence, accumulated into (m_h, l_h, acc): the per-chunk pipeline
+// described above.  bt_s holds the table entries from jb0 on.
+template <int D, int G, bool UB>
+__device__ __forceinline__ void attend_range(const DecodeArgs &a, const Range &R, int64_t jb0,
+                                             const int32_t *bt_s, char *vring, char *kt, int h,
+                                             const u32x4 (&qf)[MfmaShape<D>::KS], float &m_h,
+                                             float &l_h, f32x4 (&acc)[MfmaShape<D>::NV]) {
+    using S = MfmaShape<D>;
+    constexpr int ROWB = S::ROWB, PPR = S::PPR, NP = S::NP, KS = S::KS, NV = S::NV;
+    constexpr int VSLAB = S::VSLAB, VTILE = S::VTILE, KROW = S::KROW, NSLOT = S::NSLOT;
+    constexpr int LOADS = S::LOADS;
+    constexpr float kLazy = 8.0f;  // reference-max slack, log2 units
+    const int lane = threadIdx.x & 63;
     const int n = lane & 15;       // MFMA: row / column index
     const int g4 = lane >> 4;      // MFMA: k group
     const int lbs = a.pool.lbs;
     const int64_t bsm = (1ll << lbs) - 1;
     const int64_t row_bytes = a.pool.row_bytes;
     const float sl2 = a.scale_log2;
-    char *vring = vtiles[w][0];
-    char *kt = ktiles[w];
-
-    // Q^T fragments (B operand of QK^T): head n, elements 32j + 8*g4 .. +8.
-    u32x4 qf[KS];
-    {
-        const char *qp = a.q + (((int64_t)seq * a.num_q_heads + (int64_t)h * G + n) * D + 8 * g4) * E;
-#pragma unroll
-        for (int j = 0; j < KS; ++j) qf[j] = n < G ? ld16(qp + 64 * j) : u32x4{0, 0, 0, 0};
-    }
-
-    float m_h = kNegInf;  // reference max of head n (same in its 4 lanes)
-    float l_h = 0.0f;     // this lane's share of head n's denominator
-    f32x4 acc[NV];
-#pragma unroll
-    for (int s = 0; s < NV; ++s) acc[s] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
     const char *kh = a.pool.k + a.pool.layer_off + (int64_t)h * ROWB;
     const char *vh = a.pool.v + a.pool.layer_off + (int64_t)h * ROWB;
@@ -831,42 +834,271 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
                 }
             }
         }
-        // drain the copy engine before the tiles' memory is released
+        // drain the copy engine before the tiles are reused
         __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xF << 8));
     }
+}
 
-    // totals: l over the token groups; lane (g4, n) then holds head n's l
+// Denominators: l over the token groups (lane (g4, n) then holds head n's l
+// in l_h), and lrow[i] = l of head 4*g4 + i, the head of this lane's O row i.
+__device__ __forceinline__ void head_denominators(float &l_h, float (&lrow)[4]) {
+    const int g4 = (threadIdx.x & 63) >> 4;
     l_h += __shfl_xor(l_h, 16);
     l_h += __shfl_xor(l_h, 32);
-    float lrow[4];  // l of the heads this lane's O rows belong to
 #pragma unroll
     for (int i = 0; i < 4; ++i) lrow[i] = __shfl(l_h, 4 * g4 + i);
+}
 
+// out[seq, h*G + hd, :] = acc / l, rounded to bf16.
+template <int D, int G>
+__device__ __forceinline__ void write_direct(const DecodeArgs &a, int seq, int h,
+                                             const f32x4 (&acc)[MfmaShape<D>::NV], const float (&lrow)[4]) {
+    const int lane = threadIdx.x & 63;
+    const int n = lane & 15, g4 = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int hd = 4 * g4 + i;
+        if (hd < G) {
+            uint16_t *o = reinterpret_cast<uint16_t *>(a.out) + ((int64_t)seq * a.num_q_heads + (int64_t)h * G + hd) * D + n;
+#pragma unroll
+            for (int sl = 0; sl < MfmaShape<D>::NV; ++sl)
+                o[16 * sl] = (uint16_t)f32_to_bf16_bits(lrow[i] > 0.0f ? acc[sl][i] / lrow[i] : 0.0f);
+        }
+    }
+}
+
+// Unnormalised partial of the wave's G heads: acc rows at accp + hd*D and
+// (m, l) pairs at ml + 2*hd, written with device-scope stores.
+template <int D, int G>
+__device__ __forceinline__ void write_partial(float *ml, float *accp, const f32x4 (&acc)[MfmaShape<D>::NV],
+                                              float m_h, float l_h) {
+    const int lane = threadIdx.x & 63;
+    const int n = lane & 15, g4 = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int hd = 4 * g4 + i;
+        if (hd < G) {
+            float *wa = accp + hd * D + n;
+#pragma unroll
+            for (int sl = 0; sl < MfmaShape<D>::NV; ++sl) st_dev(wa + 16 * sl, acc[sl][i]);
+        }
+    }
+    if (g4 == 0 && n < G) st_dev2(ml + 2 * n, m_h, l_h);
+}
+
+// Split schedule: one workgroup per (sequence, split, head group).
+template <int D, int G, bool UB>
+__global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
+    using S = MfmaShape<D>;
+    static_assert(G >= 1 && G <= 16, "group");
+    __shared__ int32_t bt_s[kBtLds];
+    __shared__ __attribute__((aligned(16))) char vtiles[4][S::NSLOT][S::VTILE];
+    __shared__ __attribute__((aligned(16))) char ktiles[4][S::KTILE];
+
+    const Item it = work_item(a);
+    const Range R = split_range(a, it.seq, it.split);
+    const bool direct = a.max_splits == 1;
+    if (!direct && R.hi <= R.lo) {
+        if (a.fused_merge && R.len <= 0 && it.split == 0) zero_outputs<1, D, G>(a, it.seq, it.hg);
+        return;
+    }
+    const int64_t jb0 = stage_table(a, it.seq, R, bt_s);
+
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int h = it.hg * a.heads_per_wg + w;  // < num_kv_heads: head groups tile the heads
+    u32x4 qf[S::KS];
+    load_q<D, G>(a, it.seq, h, qf);
+    float m_h = kNegInf;  // reference max of head n (same in its 4 lanes)
+    float l_h = 0.0f;     // this lane's share of head n's denominator
+    f32x4 acc[S::NV];
+#pragma unroll
+    for (int sl = 0; sl < S::NV; ++sl) acc[sl] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    attend_range<D, G, UB>(a, R, jb0, bt_s, vtiles[w][0], ktiles[w], h, qf, m_h, l_h, acc);
+    float lrow[4];
+    head_denominators(l_h, lrow);
     if (direct) {
+        write_direct<D, G>(a, it.seq, h, acc, lrow);
+        return;
+    }
+    const int64_t item0 = ((int64_t)it.seq * a.max_splits + it.split) * a.num_q_heads + (int64_t)h * G;
+    write_partial<D, G>(a.ws_ml + item0 * 2, a.ws_acc + item0 * D, acc, m_h, l_h);
+    if (a.fused_merge) finish_split<1, D, G>(a, it, R);
+}
+
+// ---------------------------------------------------------------------------
+// Balanced schedule (bf16): the grid is the number of workgroups that stay
+// resident together, and every workgroup takes an equal share of the work.
+// The work is flattened into units (head group, sequence, chunk): chunk c
+// of a sequence with offset off covers the 16 flat positions starting at
+// 16 * (off/16 + c), so a sequence of length L > 0 has
+// ((off + L - 1)/16 - off/16 + 1) chunks; C = their sum, U = head_groups * C.
+// Workgroup w takes units [U w / P, U (w+1) / P), P = min(grid, U), and walks
+// them as segments, one per (head group, sequence) it touches.  A segment
+// that holds a whole (sequence, head group) writes the output directly;
+// otherwise it stores its partial in one of the workgroup's two record
+// slots (2w: the segment began before the range, 2w+1: it runs past the
+// range end) and the workgroup that completes the count of the pair's
+// contributors merges them in workgroup order.  No workgroup waits on
+// another, and all of them start together and finish together.
+// ---------------------------------------------------------------------------
+
+// Chunks spanned by sequence s (and its offset and length).
+__device__ __forceinline__ int64_t seq_chunks(const DecodeArgs &a, int s, int64_t &off, int64_t &len) {
+    len = a.seq_lens[s];
+    off = a.offsets[s];
+    return len > 0 ? ((off + len - 1) >> 4) - (off >> 4) + 1 : 0;
+}
+
+// Workgroup whose range holds unit u: the largest w with U w / P <= u.
+__device__ __forceinline__ int64_t owner_of(int64_t u, int64_t U, int64_t P) {
+    return ((u + 1) * P - 1) / U;
+}
+
+template <int D, int G, bool UB>
+__global__ __launch_bounds__(256) void decode_stream_kernel(DecodeArgs a) {
+    using S = MfmaShape<D>;
+    static_assert(G >= 1 && G <= 16, "group");
+    __shared__ int32_t bt_s[kBtLds];
+    __shared__ __attribute__((aligned(16))) char vtiles[4][S::NSLOT][S::VTILE];
+    __shared__ __attribute__((aligned(16))) char ktiles[4][S::KTILE];
+    __shared__ int64_t wave_sum_s[4];
+    __shared__ int64_t start_s[2];
+
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wv = t >> 6;
+    const int nwaves = blockDim.x >> 6;
+    const int ns = a.num_seqs;
+    // logical workgroup index: consecutive ranges share an XCD
+    const int nwg = gridDim.x;
+    const int bid = blockIdx.x;
+    const int xcd = bid & 7;
+    const int lw = xcd * (nwg >> 3) + min(xcd, nwg & 7) + (bid >> 3);
+
+    // Sequences with no tokens attend to nothing: zero rows.
+    for (int s = lw; s < ns; s += nwg) {
+        if (a.seq_lens[s] <= 0) {
+            uint32_t *o = reinterpret_cast<uint32_t *>(a.out + (int64_t)s * a.num_q_heads * D * 2);
+            for (int i = t; i < a.num_q_heads * D / 2; i += blockDim.x) o[i] = 0u;
+        }
+    }
+
+    // Chunk counts: thread t owns sequences [t*per, (t+1)*per); exclusive
+    // prefix over threads by a wave scan and the wave totals.
+    const int per = (ns + (int)blockDim.x - 1) / (int)blockDim.x;
+    int64_t mine = 0;
+    for (int i = 0; i < per; ++i) {
+        const int sq = t * per + i;
+        if (sq < ns) {
+            int64_t o, l;
+            mine += seq_chunks(a, sq, o, l);
+        }
+    }
+    int64_t incl = mine;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int hd = 4 * g4 + i;
-            if (hd < G) {
-                uint16_t *o = reinterpret_cast<uint16_t *>(a.out) +
-                              ((int64_t)seq * a.num_q_heads + (int64_t)h * G + hd) * D + n;
-#pragma unroll
-                for (int sl = 0; sl < NV; ++sl)
-                    o[16 * sl] = (uint16_t)f32_to_bf16_bits(lrow[i] > 0.0f ? acc[sl][i] / lrow[i] : 0.0f);
+    for (int d = 1; d < 64; d <<= 1) {
+        const int64_t y = __shfl_up(incl, d);
+        if (lane >= d) incl += y;
+    }
+    if (lane == 63) wave_sum_s[wv] = incl;
+    __syncthreads();
+    int64_t C = 0, before = 0;
+    for (int k = 0; k < nwaves; ++k) {
+        if (k < wv) before += wave_sum_s[k];
+        C += wave_sum_s[k];
+    }
+    const int64_t U = C * a.head_groups;
+    const int64_t P = min((int64_t)nwg, U);
+    if (lw >= P) return;  // uniform: no work for this workgroup
+    const int64_t u0 = U * lw / P, u1 = U * (lw + 1) / P;
+    {
+        const int64_t r0 = u0 % C;
+        const int64_t excl = before + incl - mine;
+        if (r0 >= excl && r0 < excl + mine) {
+            int64_t pre = excl;
+            for (int i = 0; i < per; ++i) {
+                const int sq = t * per + i;
+                if (sq >= ns) break;
+                int64_t o, l;
+                const int64_t c = seq_chunks(a, sq, o, l);
+                if (r0 < pre + c) {
+                    start_s[0] = sq;
+                    start_s[1] = pre;
+                    break;
+                }
+                pre += c;
             }
         }
-    } else {
-        const int64_t item0 = ((int64_t)seq * a.max_splits + it.split) * a.num_q_heads + (int64_t)h * G;
+    }
+    __syncthreads();
+    int seq = (int)start_s[0];
+    int64_t pre = start_s[1];    // chunks of the sequences before seq
+    int hg = (int)(u0 / C);
+
+    const int w = __builtin_amdgcn_readfirstlane(wv);
+    const int hqw = a.heads_per_wg * G;  // query heads of one head group
+    int64_t u = u0;
+    while (u < u1) {
+        int64_t off, len;
+        int64_t nch = seq_chunks(a, seq, off, len);
+        while (nch == 0) {  // empty sequences hold no units
+            if (++seq == ns) {
+                seq = 0;
+                pre = 0;
+                ++hg;
+            }
+            nch = seq_chunks(a, seq, off, len);
+        }
+        const int64_t pstart = (int64_t)hg * C + pre;
+        const int64_t pend = pstart + nch;
+        const int64_t seg_end = min(u1, pend);
+        const int h = hg * a.heads_per_wg + w;
+        u32x4 qf[S::KS];
+        load_q<D, G>(a, seq, h, qf);
+        float m_h = kNegInf;
+        float l_h = 0.0f;
+        f32x4 acc[S::NV];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int hd = 4 * g4 + i;
-            if (hd < G) {
-                float *wa = a.ws_acc + (item0 + hd) * D + n;
-#pragma unroll
-                for (int sl = 0; sl < NV; ++sl) st_dev(wa + 16 * sl, acc[sl][i]);
+        for (int sl = 0; sl < S::NV; ++sl) acc[sl] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        const int64_t f0 = off >> 4;
+        for (int64_t cp = u - pstart; cp < seg_end - pstart; cp += a.seg_chunks) {
+            const int64_t ce = min(cp + (int64_t)a.seg_chunks, seg_end - pstart);
+            Range R;
+            R.off = off;
+            R.len = len;
+            R.lo = max(16 * (f0 + cp), off);
+            R.hi = min(16 * (f0 + ce), off + len);
+            __syncthreads();  // every wave is done with the previous table entries
+            const int64_t jb0 = stage_table(a, seq, R, bt_s);
+            attend_range<D, G, UB>(a, R, jb0, bt_s, vtiles[w][0], ktiles[w], h, qf, m_h, l_h, acc);
+        }
+        float lrow[4];
+        head_denominators(l_h, lrow);
+        if (pstart >= u0 && pend <= u1) {
+            write_direct<D, G>(a, seq, h, acc, lrow);
+        } else {
+            const int64_t slot = pstart < u0 ? 2 * (int64_t)lw : 2 * (int64_t)lw + 1;
+            const int64_t rec = slot * hqw + (int64_t)w * G;
+            write_partial<D, G>(a.ws_ml + rec * 2, a.ws_acc + rec * D, acc, m_h, l_h);
+            const int64_t wa = owner_of(pstart, U, P);
+            const int64_t wb = owner_of(pend - 1, U, P);
+            if (count_in(a.ws_cnt + (int64_t)seq * a.head_groups + hg, (uint32_t)(wb - wa + 1))) {
+                const int64_t hq0 = (int64_t)h * G;
+                merge_records<1, D, G>(a.out + ((int64_t)seq * a.num_q_heads + hq0) * D * 2,
+                                       a.ws_ml + (int64_t)w * G * 2, a.ws_acc + (int64_t)w * G * D, hqw,
+                                       (int)(wb - wa + 1),
+                                       [=](int i) { return i == 0 ? 2 * wa + 1 : 2 * (wa + i); });
             }
         }
-        if (g4 == 0 && n < G) st_dev2(a.ws_ml + (item0 + n) * 2, m_h, l_h);
-        if (a.fused_merge) finish_split<1, D, G>(a, it, R);
+        u = seg_end;
+        if (u == pend) {
+            pre += nch;
+            if (++seq == ns) {
+                seq = 0;
+                pre = 0;
+                ++hg;
+            }
+        }
     }
 }
 
@@ -976,8 +1208,19 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(DecodeArgs a) {
 
 template <int DT, int D, int G>
 static hipError_t run_decode(const DecodeArgs &a, hipStream_t s) {
+    const dim3 block(64 * a.heads_per_wg);
+    if constexpr (DT == 1) {
+        if (a.stream_wgs > 0) {
+            const dim3 sgrid((unsigned)a.stream_wgs);
+            if (a.pool.lbs >= 4)
+                hipLaunchKernelGGL((decode_stream_kernel<D, G, true>), sgrid, block, 0, s, a);
+            else
+                hipLaunchKernelGGL((decode_stream_kernel<D, G, false>), sgrid, block, 0, s, a);
+            return hipGetLastError();
+        }
+    }
     const int64_t nwg = (int64_t)a.head_groups * a.max_splits * a.num_seqs;
-    const dim3 grid((unsigned)nwg), block(64 * a.heads_per_wg);
+    const dim3 grid((unsigned)nwg);
     if constexpr (DT == 1) {
         if (a.pool.lbs >= 4)
             hipLaunchKernelGGL((decode_mfma_kernel<D, G, true>), grid, block, 0, s, a);

@@ -95,6 +95,8 @@ struct DecodeArgs {
     int32_t heads_per_wg;
     int32_t head_groups;
     int32_t fused_merge;   // 1: the last split of a (sequence, head group) merges; 0: merge kernel
+    int32_t stream_wgs;    // > 0: balanced schedule with this many workgroups (bf16)
+    int32_t seg_chunks;    // balanced schedule: most chunks staged at once
 };
 
 // Most splits per sequence merged by the last finishing workgroup; beyond

@@ -25,11 +25,16 @@ SYMBOLS = (
     "kv_scatter",
     "kv_gather",
     "paged_attn_decode_split_tokens",
+    "paged_attn_decode_schedule",
     "paged_attn_decode_workspace_size",
     "paged_attn_decode",
     "kv_validate",
     "pkv_status_string",
 )
+
+
+# split_tokens value asking paged_attn_decode for the balanced schedule
+SPLIT_BALANCED = -1
 
 
 class PagedKVError(RuntimeError):
@@ -77,6 +82,8 @@ def load_library(path: str = LIB_PATH):
     lib.kv_gather.argtypes = [pp, i32, p, i32, p, p, p, i32, i32, p, p, i64, p]
     lib.paged_attn_decode_split_tokens.restype = i32
     lib.paged_attn_decode_split_tokens.argtypes = [i32, i32, i32, i32]
+    lib.paged_attn_decode_schedule.restype = i32
+    lib.paged_attn_decode_schedule.argtypes = [i32] * 8
     lib.paged_attn_decode_workspace_size.restype = sz
     lib.paged_attn_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
     lib.paged_attn_decode.restype = ctypes.c_int
@@ -183,6 +190,20 @@ def paged_attn_decode_split_tokens(num_seqs, num_kv_heads, max_seq_len, block_si
                                                       block_size)
     if v < 0:
         raise PagedKVError("paged_attn_decode_split_tokens", v)
+    return v
+
+
+def paged_attn_decode_schedule(num_seqs, num_kv_heads, num_q_heads, head_dim, max_seq_len,
+                               block_size, dtype, split_tokens=0):
+    """Tokens per split of the split schedule, or 0 for the balanced
+    schedule, for a pool of torch dtype `dtype`."""
+    code = {torch.float32: 0, torch.bfloat16: 1}.get(dtype)
+    if code is None:
+        raise PagedKVError("paged_attn_decode_schedule", -2)
+    v = load_library().paged_attn_decode_schedule(num_seqs, num_kv_heads, num_q_heads, head_dim,
+                                                  int(max_seq_len), block_size, code, split_tokens)
+    if v < 0:
+        raise PagedKVError("paged_attn_decode_schedule", v)
     return v
 
 

@@ -30,7 +30,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 8
+    assert len(names) == 9
     assert set(names) == set(N.SYMBOLS)
     for n in names:
         assert hasattr(lib, n), n
@@ -126,6 +126,7 @@ def test_decode_argument_checks(lib):
     assert call(layer=3) == LAYER
     assert call(split=24) == SHAPE     # not a multiple of 16
     assert call(split=-16) == SHAPE
+    assert call(split=-1, p=pool(dtype=0)) == UNSUP   # balanced schedule: bf16 only
     assert call(ns=0) == OK
     assert call(q=None) == NULL
     assert call(out=A + 2) == ALIGN
@@ -140,7 +141,13 @@ def test_decode_argument_checks(lib):
 def test_workspace_size_and_split_choice(lib):
     ws = lib.paged_attn_decode_workspace_size
     # one split covers everything: no workspace
-    assert ws(1, 2, 4, 64, 30, 16, 0) == 0
+    assert ws(1, 2, 4, 64, 30, 16, 64) == 0
+    # automatic choice: room for the balanced schedule of bf16 pools (two
+    # record slots per workgroup) or for the automatic split of fp32 pools,
+    # whichever is larger
+    split = lib.paged_attn_decode_split_tokens
+    assert ws(1, 2, 4, 64, 30, 16, 0) > 0
+    assert ws(8, 8, 64, 128, 32768, 16, 0) >= ws(8, 8, 64, 128, 32768, 16, split(8, 8, 32768, 16))
     # split counters (seqs x kv heads) and the (m, l) block, each padded to
     # 256 bytes, then the fp32 accumulators.  Splits cover flat table
     # positions, so a first-block offset of up to block_size - 1 can add
@@ -149,13 +156,31 @@ def test_workspace_size_and_split_choice(lib):
     cnt = (8 * 8 * 4 + 255) // 256 * 256
     assert ws(8, 8, 64, 128, 32768, 16, 8192) == cnt + (n * 8 + 255) // 256 * 256 + n * 128 * 4
     assert ws(8, 8, 64, 128, 32768, 16, 24) == ctypes.c_size_t(-1).value
-    split = lib.paged_attn_decode_split_tokens
     for args in ((32, 8, 2048, 16), (64, 8, 4096, 16), (8, 8, 32768, 16), (1, 2, 30, 16),
                  (3, 1, 5000, 1)):
         s = split(*args)
         assert s > 0 and s % 16 == 0
         assert s // args[3] + 2 <= 1024
     assert split(4, 8, 100, 12) == SHAPE
+
+
+def test_decode_schedule_choice(lib):
+    """The automatic schedule: balanced for bf16 batches with at least
+    512 MiB of K/V at max_seq_len (and at most 4096 sequences), the
+    automatic split otherwise; an explicit split is always kept."""
+    f = lib.paged_attn_decode_schedule
+    F32, BF16 = 0, 1
+    split = lib.paged_attn_decode_split_tokens
+    assert f(32, 8, 32, 128, 2048, 16, BF16, 0) == split(32, 8, 2048, 16)  # 256 MiB
+    assert f(64, 8, 32, 128, 4096, 16, BF16, 0) == 0                       # 1 GiB
+    assert f(8, 8, 64, 128, 32768, 16, BF16, 0) == 0
+    assert f(8, 8, 64, 128, 32768, 16, F32, 0) == split(8, 8, 32768, 16)
+    assert f(8, 8, 64, 128, 32768, 16, BF16, 512) == 512
+    assert f(5000, 8, 32, 128, 4096, 16, BF16, 0) == split(5000, 8, 4096, 16)
+    assert f(8, 8, 64, 128, 32768, 16, 7, 0) == DTYPE
+    assert f(8, 8, 60, 128, 32768, 16, BF16, 0) == SHAPE
+    assert f(2, 2, 8, 128, 100, 16, BF16, -1) == 0                         # asked for
+    assert f(2, 2, 8, 128, 100, 16, F32, -1) == UNSUP
 
 
 def test_validate_argument_checks(lib):
