@@ -298,6 +298,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ops", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time the step as eager calls only (no HIP graph replay)")
     ap.add_argument("--split-tokens", type=int, default=0)
     ap.add_argument("--pmc-target", choices=["decode", "copy"], default=None,
                     help="run only the decode launches (or a 1 GiB copy) for counter passes")
@@ -347,20 +349,20 @@ def main():
     pool = N.make_pool(w.k_pool, w.v_pool)
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
     P = lambda t: ctypes.c_void_p(t.data_ptr())
-    slot_args = (P(w.block_tables), w.block_tables.shape[1], P(w.offsets), w.num_seqs,
-                 P(w.token_seq), P(w.token_pos), w.token_seq.shape[0], w.block_size, P(slots),
-                 stream)
-    scat_args = [(ctypes.byref(pool), l, P(w.k_new), P(w.v_new), P(slots), slots.shape[0], stream)
-                 for l in range(w.num_layers)]
+    # the new tokens' slots (a1) and their scatter (a2) in one kernel
+    app_args = [(ctypes.byref(pool), l, P(w.k_new), P(w.v_new), P(w.block_tables),
+                 w.block_tables.shape[1], P(w.offsets), w.num_seqs, P(w.token_seq),
+                 P(w.token_pos), w.token_seq.shape[0], P(slots), stream)
+                for l in range(w.num_layers)]
     dec_args = [(ctypes.byref(pool), l, P(w.q), w.num_q_heads, P(w.block_tables),
                  w.block_tables.shape[1], P(w.seq_lens), P(w.offsets), w.num_seqs, mx,
                  ctypes.c_float(w.scale), split, P(out), P(workspace), workspace.numel(), stream)
                 for l in range(w.num_layers)]
-    f_slot, f_scat, f_dec = lib.kv_slot_mapping, lib.kv_scatter, lib.paged_attn_decode
+    f_app, f_dec = lib.kv_append, lib.paged_attn_decode
 
     def step(i, timed=False):
         layer = i % w.num_layers
-        rc = f_slot(*slot_args) | f_scat(*scat_args[layer])
+        rc = f_app(*app_args[layer])
         if timed:
             dec_start[i].record()
         rc |= f_dec(*dec_args[layer])
@@ -368,6 +370,28 @@ def main():
             dec_end[i].record()
         if rc:
             raise RuntimeError(f"a library call failed in step {i}")
+
+    # The same step captured as one HIP graph per layer (the three calls,
+    # marshalled for the capture stream), replayed per step.
+    graphs = []
+    if not args.no_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(3):
+                step(i)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        for layer in range(w.num_layers):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                cs = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+                rc = f_app(*app_args[layer][:-1], cs)
+                rc |= f_dec(*dec_args[layer][:-1], cs)
+            if rc:
+                raise RuntimeError(f"a library call failed while capturing layer {layer}")
+            graphs.append(g)
+        torch.cuda.synchronize()
 
     log(f"warmup {args.warmup} steps (split_tokens={split}, workspace={ws_bytes} B)")
     for i in range(args.warmup):
@@ -383,11 +407,25 @@ def main():
     t_end.record()
     torch.cuda.synchronize()
     ms_total = t_start.elapsed_time(t_end)
-    ms_step = ms_total / args.steps
+    ms_step_eager = ms_total / args.steps
+    ms_step = ms_step_eager
+    if graphs:
+        for i in range(args.warmup):
+            graphs[i % w.num_layers].replay()
+        torch.cuda.synchronize()
+        g_start = torch.cuda.Event(enable_timing=True)
+        g_end = torch.cuda.Event(enable_timing=True)
+        g_start.record()
+        for i in range(args.steps):
+            graphs[i % w.num_layers].replay()
+        g_end.record()
+        torch.cuda.synchronize()
+        ms_step = g_start.elapsed_time(g_end) / args.steps
+        log(f"step as graph replay {ms_step * 1e3:.1f} us (eager calls {ms_step_eager * 1e3:.1f} us)")
     dec_ms = [s.elapsed_time(e) for s, e in zip(dec_start, dec_end)]
     dec_avg = sum(dec_ms) / len(dec_ms)
     dec_med = sorted(dec_ms)[len(dec_ms) // 2]
-    log(f"step {ms_step * 1e3:.1f} us, decode call inside the step avg {dec_avg * 1e3:.1f} us "
+    log(f"eager step {ms_step_eager * 1e3:.1f} us, decode call inside it avg {dec_avg * 1e3:.1f} us "
         f"(median {dec_med * 1e3:.1f} us)")
 
     # The decode kernel's own rate: the same calls back to back (layer
@@ -433,8 +471,10 @@ def main():
             "num_q_heads": w.num_q_heads,
             "split_tokens": sched if sched > 0 else "balanced",
             "kv_bytes_per_step": kv_bytes,
-            "step": "kv_slot_mapping + kv_scatter (1 new token/seq) + paged_attn_decode, "
+            "step": "kv_append (slot mapping + scatter of 1 new token/seq) + paged_attn_decode, "
                     "layer rotated over 32",
+            "step_launch": "HIP graph per layer, replayed" if graphs else "eager C-ABI calls",
+            "eager_ms_per_step": ms_step_eager,
             "parallelism": "single GPU",
         },
         "roofline": {

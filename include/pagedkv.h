@@ -132,6 +132,31 @@ PKV_API int kv_scatter(const pkv_pool *pool, int32_t layer,
                        void *stream);
 
 /*
+ * kv_append -- kv_slot_mapping and kv_scatter in one pass: row i of
+ * k_src/v_src is written at the slot of logical position token_pos[i] of
+ * sequence token_seq[i] [P2 sec. 2.2 slot_mapping; P3 sec. 2.2 offset;
+ * P1 "relation to step14_1"], with exactly the slot kv_slot_mapping
+ * computes and the skipping rules of both (token_seq < 0, a position
+ * outside the table, a slot outside the pool).  The decode step's write of
+ * the new tokens, as one kernel instead of two.
+ *
+ *   k_src, v_src  as for kv_scatter (v_src may be NULL)
+ *   block_tables, bt_stride, offsets, num_seqs, token_seq, token_pos,
+ *   num_tokens    as for kv_slot_mapping (block_size is the pool's)
+ *   slot_mapping_out  device int64 [num_tokens] receiving the slots (-1 for
+ *                 skipped rows), or NULL
+ * Errors: PKV_ERR_NULL, _DTYPE, _SHAPE, _LAYER, _ALIGN, _LAUNCH.
+ * num_tokens == 0 enqueues nothing.
+ */
+PKV_API int kv_append(const pkv_pool *pool, int32_t layer,
+                      const void *k_src, const void *v_src,
+                      const int32_t *block_tables, int32_t bt_stride,
+                      const int32_t *offsets, int32_t num_seqs,
+                      const int32_t *token_seq, const int32_t *token_pos,
+                      int64_t num_tokens, int64_t *slot_mapping_out,
+                      void *stream);
+
+/*
  * kv_gather -- contiguous K/V of each sequence from its block table
  * [P1 "Problem" and "Solution": pool[table[pos/bs], pos%bs] -> (seq_len,
  * num_heads, head_dim); P3 sec. 2.2: reads start at the first-block offset].

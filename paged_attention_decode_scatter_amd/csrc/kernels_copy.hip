@@ -116,6 +116,76 @@ hipError_t launch_scatter(const ScatterArgs &a, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
+// Append: the slot computation of slot_mapping_kernel and the scatter of
+// scatter_kernel for one row per token, in one kernel.  The source pieces
+// are loaded while the slot is still being looked up (they depend only on
+// the row), so the chain to the store is the token's sequence and position,
+// its offset, its table entry.  The lane holding piece 0 of a row writes
+// the slot when slots_out is given.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kCopyThreads) void append_kernel(AppendArgs a) {
+    const ScatterArgs &c = a.sc;
+    const int64_t tok0 = (int64_t)blockIdx.x * c.tok_per_wg;
+    const int64_t left = c.num_tokens - tok0;
+    const int ntok = left < c.tok_per_wg ? (int)left : c.tok_per_wg;
+    const int cpr = c.row_bytes >> 4;
+    const int n = ntok * cpr;
+    const int64_t bsm = (1ll << c.lbs) - 1;
+    const bool has_v = c.v_src != nullptr;
+    for (int base = threadIdx.x; base < n; base += kCopyThreads * kUnroll) {
+        u32x4 kk[kUnroll], vv[kUnroll];
+        int64_t dst[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int idx = base + u * kCopyThreads;
+            dst[u] = -1;
+            if (idx < n) {
+                int tt, ch;
+                if (c.lcpr >= 0) {
+                    tt = idx >> c.lcpr;
+                    ch = idx & (cpr - 1);
+                } else {
+                    tt = idx / cpr;
+                    ch = idx - tt * cpr;
+                }
+                const int64_t t = tok0 + tt;
+                const int64_t src = t * c.row_bytes + ((int64_t)ch << 4);
+                kk[u] = ld16_stream(c.k_src + src);
+                if (has_v) vv[u] = ld16_stream(c.v_src + src);
+                const int32_t seq = a.token_seq[t];
+                int64_t slot = -1;
+                if (seq >= 0 && seq < a.num_seqs) {
+                    const int64_t pos = a.token_pos[t];
+                    const int64_t p = (int64_t)a.offsets[seq] + pos;
+                    const int64_t j = p >> c.lbs;
+                    if (pos >= 0 && p >= 0 && j < a.bt_stride) {
+                        const int32_t b = a.block_tables[(int64_t)seq * a.bt_stride + j];
+                        if (b >= 0) slot = ((int64_t)b << c.lbs) | (p & bsm);
+                    }
+                }
+                if (ch == 0 && a.slots_out) a.slots_out[t] = slot;
+                if (slot >= 0 && slot < c.total_slots)
+                    dst[u] = (slot >> c.lbs) * c.block_stride + c.layer_off + (slot & bsm) * c.row_bytes +
+                             ((int64_t)ch << 4);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            if (dst[u] >= 0) {
+                st16(c.kpool + dst[u], kk[u]);
+                if (has_v) st16(c.vpool + dst[u], vv[u]);
+            }
+        }
+    }
+}
+
+hipError_t launch_append(const AppendArgs &a, hipStream_t s) {
+    const int64_t blocks = (a.sc.num_tokens + a.sc.tok_per_wg - 1) / a.sc.tok_per_wg;
+    hipLaunchKernelGGL(append_kernel, dim3((unsigned)blocks), dim3(kCopyThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Gather [P1 "Problem"/"Solution"; P3 sec. 2.2]: out row (row_start + t) <-
 // pool row (table[(off+t) >> lbs], layer, (off+t) & bsm) for t < seq_len.
 // Workgroup (seq, tile) covers tokens [tile*T, tile*T + T); the table

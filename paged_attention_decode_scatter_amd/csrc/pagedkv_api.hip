@@ -236,6 +236,19 @@ PKV_API int kv_slot_mapping(const int32_t *block_tables, int32_t bt_stride, cons
     return status_of(launch_slot_mapping(a, static_cast<hipStream_t>(stream)));
 }
 
+// Workgroup sizing shared by the scatter and the append: about 2048 16-byte
+// pieces (32 KiB per tensor) per workgroup, but no fewer workgroups than a
+// few per CU can absorb: a small scatter (one decode step's tokens) then
+// runs one row per workgroup, each lane moving a single piece, so its
+// latency is one load and one store.
+static int64_t rows_per_wg(int64_t num_tokens, int64_t cpr) {
+    int64_t tpw = 2048 / cpr;
+    const int64_t wide = (num_tokens + 1023) / 1024;
+    if (tpw > wide) tpw = wide;
+    if (tpw < 1) tpw = 1;
+    return tpw;
+}
+
 PKV_API int kv_scatter(const pkv_pool *pool, int32_t layer, const void *k_src, const void *v_src,
                        const int64_t *slot_mapping, int64_t num_tokens, void *stream) {
     const bool has_v = v_src != nullptr;
@@ -260,18 +273,51 @@ PKV_API int kv_scatter(const pkv_pool *pool, int32_t layer, const void *k_src, c
     a.row_bytes = v.row_bytes;
     a.lbs = v.lbs;
     const int64_t cpr = v.row_bytes / 16;
-    // about 2048 16-byte pieces (32 KiB per tensor) per workgroup, but no
-    // fewer workgroups than a few per CU can absorb: a small scatter (one
-    // decode step's tokens) then runs one row per workgroup, each lane
-    // moving a single piece, so its latency is one load and one store
-    int64_t tpw = 2048 / cpr;
-    const int64_t wide = (num_tokens + 1023) / 1024;
-    if (tpw > wide) tpw = wide;
-    if (tpw < 1) tpw = 1;
+    const int64_t tpw = rows_per_wg(num_tokens, cpr);
     a.tok_per_wg = (int32_t)tpw;
     a.lcpr = (int32_t)pow2_or_neg(cpr);
     if (cpr * tpw > INT32_MAX / 2) return PKV_ERR_SHAPE;
     return status_of(launch_scatter(a, static_cast<hipStream_t>(stream)));
+}
+
+PKV_API int kv_append(const pkv_pool *pool, int32_t layer, const void *k_src, const void *v_src,
+                      const int32_t *block_tables, int32_t bt_stride, const int32_t *offsets,
+                      int32_t num_seqs, const int32_t *token_seq, const int32_t *token_pos,
+                      int64_t num_tokens, int64_t *slot_mapping_out, void *stream) {
+    const bool has_v = v_src != nullptr;
+    int st = check_pool(pool, has_v);
+    if (st) return st;
+    if (layer < 0 || layer >= pool->num_layers) return PKV_ERR_LAYER;
+    if (num_tokens < 0 || num_seqs < 0 || bt_stride < 0) return PKV_ERR_SHAPE;
+    if (num_tokens == 0) return PKV_OK;
+    if (!k_src || !token_seq || !token_pos || (num_seqs > 0 && (!block_tables || !offsets)))
+        return PKV_ERR_NULL;
+    if (!aligned16(k_src) || (has_v && !aligned16(v_src))) return PKV_ERR_ALIGN;
+    const PoolView v = make_view(pool, layer);
+    AppendArgs a{};
+    a.sc.kpool = static_cast<char *>(pool->k);
+    a.sc.vpool = static_cast<char *>(pool->v);
+    a.sc.k_src = static_cast<const char *>(k_src);
+    a.sc.v_src = static_cast<const char *>(v_src);
+    a.sc.num_tokens = num_tokens;
+    a.sc.total_slots = pool->num_blocks * pool->block_size;
+    a.sc.block_stride = v.block_stride;
+    a.sc.layer_off = v.layer_off;
+    a.sc.row_bytes = v.row_bytes;
+    a.sc.lbs = v.lbs;
+    const int64_t cpr = v.row_bytes / 16;
+    const int64_t tpw = rows_per_wg(num_tokens, cpr);
+    a.sc.tok_per_wg = (int32_t)tpw;
+    a.sc.lcpr = (int32_t)pow2_or_neg(cpr);
+    if (cpr * tpw > INT32_MAX / 2) return PKV_ERR_SHAPE;
+    a.block_tables = block_tables;
+    a.offsets = offsets;
+    a.token_seq = token_seq;
+    a.token_pos = token_pos;
+    a.slots_out = slot_mapping_out;
+    a.bt_stride = bt_stride;
+    a.num_seqs = num_seqs;
+    return status_of(launch_append(a, static_cast<hipStream_t>(stream)));
 }
 
 PKV_API int kv_gather(const pkv_pool *pool, int32_t layer, const int32_t *block_tables,

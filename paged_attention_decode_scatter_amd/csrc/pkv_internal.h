@@ -59,6 +59,18 @@ struct ScatterArgs {
     int32_t lcpr;          // log2(row_bytes/16), or -1 if not a power of two
 };
 
+// Slot computation and scatter in one pass (kv_append).
+struct AppendArgs {
+    ScatterArgs sc;              // slots unused; everything else as for the scatter
+    const int32_t *block_tables;
+    const int32_t *offsets;
+    const int32_t *token_seq;
+    const int32_t *token_pos;
+    int64_t *slots_out;          // may be null
+    int32_t bt_stride;
+    int32_t num_seqs;
+};
+
 struct GatherArgs {
     PoolView pool;
     const int32_t *block_tables;
@@ -120,6 +132,7 @@ struct ValidateArgs {
 
 hipError_t launch_slot_mapping(const SlotArgs &a, hipStream_t s);
 hipError_t launch_scatter(const ScatterArgs &a, hipStream_t s);
+hipError_t launch_append(const AppendArgs &a, hipStream_t s);
 hipError_t launch_gather(const GatherArgs &a, hipStream_t s);
 hipError_t launch_validate(const ValidateArgs &a, hipStream_t s);
 // Returns hipErrorInvalidValue when (dtype, head_dim, group) is not built.

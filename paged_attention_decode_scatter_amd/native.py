@@ -23,6 +23,7 @@ _DTYPES = {torch.float32: PKV_F32, torch.bfloat16: PKV_BF16}
 SYMBOLS = (
     "kv_slot_mapping",
     "kv_scatter",
+    "kv_append",
     "kv_gather",
     "paged_attn_decode_split_tokens",
     "paged_attn_decode_schedule",
@@ -78,6 +79,8 @@ def load_library(path: str = LIB_PATH):
     lib.kv_slot_mapping.argtypes = [p, i32, p, i32, p, p, i64, i32, p, p]
     lib.kv_scatter.restype = ctypes.c_int
     lib.kv_scatter.argtypes = [pp, i32, p, p, p, i64, p]
+    lib.kv_append.restype = ctypes.c_int
+    lib.kv_append.argtypes = [pp, i32, p, p, p, i32, p, i32, p, p, i64, p, p]
     lib.kv_gather.restype = ctypes.c_int
     lib.kv_gather.argtypes = [pp, i32, p, i32, p, p, p, i32, i32, p, p, i64, p]
     lib.paged_attn_decode_split_tokens.restype = i32
@@ -166,6 +169,29 @@ def kv_scatter(k_pool, v_pool, layer, k_src, v_src, slot_mapping):
     st = load_library().kv_scatter(ctypes.byref(pool), layer, _ptr(k_src), _ptr(v_src),
                                    _ptr(slot_mapping), slot_mapping.shape[0], _stream(k_pool))
     _check("kv_scatter", st)
+
+
+def kv_append(k_pool, v_pool, layer, k_src, v_src, block_tables, offsets, token_seq, token_pos,
+              slot_mapping_out=None):
+    """Write row i of k_src/v_src at logical position token_pos[i] of
+    sequence token_seq[i] (slot computed on the device, as kv_slot_mapping
+    does; skipped rows as there).  Optionally also returns the slots in
+    slot_mapping_out (int64)."""
+    pool = make_pool(k_pool, v_pool)
+    _need(k_src, k_pool.dtype, "k_src")
+    if v_src is not None:
+        _need(v_src, k_pool.dtype, "v_src")
+    for t, n in ((block_tables, "block_tables"), (offsets, "offsets"),
+                 (token_seq, "token_seq"), (token_pos, "token_pos")):
+        _need(t, torch.int32, n)
+    if slot_mapping_out is not None:
+        _need(slot_mapping_out, torch.int64, "slot_mapping_out")
+    st = load_library().kv_append(
+        ctypes.byref(pool), layer, _ptr(k_src), _ptr(v_src), _ptr(block_tables),
+        block_tables.shape[1], _ptr(offsets), block_tables.shape[0], _ptr(token_seq),
+        _ptr(token_pos), token_seq.shape[0], _ptr(slot_mapping_out), _stream(k_pool))
+    _check("kv_append", st)
+    return slot_mapping_out
 
 
 def kv_gather(k_pool, v_pool, layer, block_tables, seq_lens, offsets, out_row_start,

@@ -30,7 +30,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 9
+    assert len(names) == 10
     assert set(names) == set(N.SYMBOLS)
     for n in names:
         assert hasattr(lib, n), n
@@ -162,6 +162,29 @@ def test_workspace_size_and_split_choice(lib):
         assert s > 0 and s % 16 == 0
         assert s // args[3] + 2 <= 1024
     assert split(4, 8, 100, 12) == SHAPE
+
+
+def test_append_argument_checks(lib):
+    f = lib.kv_append
+    by = ctypes.byref
+
+    def call(p=None, layer=0, k=A, v=A, bt=A, stride=8, off=A, ns=2, ts=A, tp=A, n=4, out=None):
+        return f(by(p or pool()), layer, k, v, bt, stride, off, ns, ts, tp, n, out, None)
+
+    assert call(layer=2) == LAYER
+    assert call(n=-1) == SHAPE
+    assert call(ns=-1) == SHAPE
+    assert call(stride=-1) == SHAPE
+    assert call(n=0) == OK
+    assert call(k=None) == NULL
+    assert call(ts=None) == NULL
+    assert call(tp=None) == NULL
+    assert call(bt=None) == NULL
+    assert call(off=None) == NULL
+    assert call(k=A + 8) == ALIGN
+    assert call(p=pool(bs=6)) == SHAPE
+    assert call(p=pool(dtype=5)) == DTYPE
+    assert call(p=pool(v=0)) == NULL       # V rows given but no V pool
 
 
 def test_decode_schedule_choice(lib):

@@ -1,0 +1,82 @@
+"""A decode step -- slot mapping of the new tokens and their scatter into
+the pool (two calls, or kv_append), paged decode attention -- captured into
+a HIP graph and replayed
+gives the same bits as the same calls issued eagerly.  Replays alternate
+with eager work (a new q each time) and synchronisations, and every replay
+is checked against an eager run on the same inputs."""
+import pytest
+import torch
+
+from paged_attention_decode_scatter_amd import native as N
+from paged_attention_decode_scatter_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    N.load_library()
+    return torch.device("cuda:0")
+
+
+def ibits(t):
+    return t.view(torch.int16) if t.element_size() == 2 else t.view(torch.int32)
+
+
+@pytest.mark.parametrize("fused_append", [False, True])
+@pytest.mark.parametrize("split", [0, 64, N.SPLIT_BALANCED])
+def test_decode_step_graph_replays_match_eager(dev, split, fused_append):
+    w = W.decode_tokens(W.decode_batch(device=dev, seed=81, num_seqs=12, min_len=1, max_len=700,
+                                       num_blocks=1024, num_layers=3, num_kv_heads=2,
+                                       head_dim=128, num_q_heads=8, layer=1, offsets="random"))
+    n = w.token_seq.shape[0]
+    mx = w.max_seq_len  # a host read: not allowed while capturing
+    need = N.paged_attn_decode_workspace_size(w.num_seqs, w.num_kv_heads, w.num_q_heads,
+                                              w.head_dim, mx, w.block_size, split)
+    slots = torch.empty(n, dtype=torch.int64, device=dev)
+    out = torch.empty_like(w.q)
+    ws = torch.zeros(max(need, 16), dtype=torch.uint8, device=dev)
+    # separate buffers for the eager reference runs
+    slots_e = torch.empty_like(slots)
+    out_e = torch.empty_like(out)
+    ws_e = torch.zeros_like(ws)
+
+    def step(slots, out, ws):
+        if fused_append:
+            N.kv_append(w.k_pool, w.v_pool, w.layer, w.k_new, w.v_new, w.block_tables, w.offsets,
+                        w.token_seq, w.token_pos, slot_mapping_out=slots)
+        else:
+            N.kv_slot_mapping(w.block_tables, w.offsets, w.token_seq, w.token_pos, w.block_size,
+                              out=slots)
+            N.kv_scatter(w.k_pool, w.v_pool, w.layer, w.k_new, w.v_new, slots)
+        N.paged_attn_decode(w.k_pool, w.v_pool, w.layer, w.q, w.block_tables, w.seq_lens,
+                            w.offsets, mx, w.scale, split_tokens=split, out=out, workspace=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(slots, out, ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(slots, out, ws)
+    torch.cuda.synchronize()
+
+    gen = torch.Generator(device=dev).manual_seed(5)
+    for r in range(4):
+        w.q.copy_(torch.randn(w.q.shape, generator=gen, device=dev, dtype=torch.float32))
+        out.fill_(float("nan"))
+        slots.fill_(-7)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        step(slots_e, out_e, ws_e)
+        torch.cuda.synchronize()
+        assert torch.equal(slots, slots_e), r
+        assert torch.equal(ibits(out), ibits(out_e)), r
+        assert not torch.isnan(out.float()).any(), r
+        rows = w.k_pool[:, w.layer].reshape(-1, w.num_kv_heads, w.head_dim)[slots_e]
+        assert torch.equal(ibits(rows), ibits(w.k_new)), r

@@ -182,6 +182,79 @@ def test_scatter_prefill_full_size(dev, random_padding):
 
 
 # ---------------------------------------------------------------------------
+# append (slot mapping + scatter in one kernel)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["tiny", "prefill_randpad", "decode_batch"])
+def test_append_bit_exact(dev, name):
+    """kv_append writes exactly what the oracle's slot mapping followed by
+    its scatter writes (compact copy of the touched blocks, all layers) and
+    returns the oracle's slots; untouched blocks keep their bytes."""
+    if name == "tiny":
+        w = W.tiny(device=dev)
+    elif name == "prefill_randpad":
+        w = W.prefill(device=dev, random_padding=True)
+    else:
+        w = W.decode_tokens(W.decode_batch(device=dev, offsets="random"))
+    # rows past the table and padding rows must be skipped, too
+    ts, tp = w.token_seq.clone(), w.token_pos.clone()
+    past = None
+    if ts.shape[0] > 4:
+        ts[1] = -1
+        past = 2
+        tp[past] = w.block_tables.shape[1] * w.block_size
+    # the oracle refuses a position outside the table; the kernel marks it -1
+    keep = np.ones(ts.shape[0], dtype=bool)
+    if past is not None:
+        keep[past] = False
+
+    def oracle_slots(bt_np):
+        out = np.full(ts.shape[0], -1, dtype=np.int64)
+        out[keep] = O.slot_mapping(bt_np, host(w.offsets), host(ts)[keep], host(tp)[keep],
+                                   w.block_size)
+        return out
+
+    slots_np = oracle_slots(host(w.block_tables))
+    bt = w.block_tables.cpu()
+    ids = torch.unique(bt[bt >= 0]).to(torch.int64)
+    dev_ids = ids.to(dev)
+    k_ref = host(w.k_pool.index_select(0, dev_ids))
+    v_ref = host(w.v_pool.index_select(0, dev_ids))
+    untouched = torch.ones(w.num_blocks, dtype=torch.bool)
+    untouched[ids] = False
+    untouched = untouched.to(dev)
+    ku_before = w.k_pool[untouched].clone()
+    pos = torch.searchsorted(ids, bt.clamp(min=0).to(torch.int64)).to(torch.int32)
+    bt_c = torch.where(bt >= 0, pos, torch.full_like(pos, -1)).numpy()
+    slots_c = oracle_slots(bt_c)
+    O.scatter(k_ref, w.layer, host(w.k_new), slots_c)
+    O.scatter(v_ref, w.layer, host(w.v_new), slots_c)
+
+    got = torch.full((ts.shape[0],), 12345, dtype=torch.int64, device=dev)
+    N.kv_append(w.k_pool, w.v_pool, w.layer, w.k_new, w.v_new, w.block_tables, w.offsets, ts, tp,
+                slot_mapping_out=got)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(got), slots_np)
+    assert np.array_equal(bits(host(w.k_pool.index_select(0, dev_ids))), bits(k_ref))
+    assert np.array_equal(bits(host(w.v_pool.index_select(0, dev_ids))), bits(v_ref))
+    ity = torch.int16 if w.dtype == torch.bfloat16 else torch.int32
+    assert torch.equal(w.k_pool[untouched].view(ity), ku_before.view(ity))
+
+
+def test_append_k_only_without_slots_out(dev):
+    w = W.tiny(device=dev)
+    k_ref = host(w.k_pool).copy()
+    slots = O.slot_mapping(host(w.block_tables), host(w.offsets), host(w.token_seq),
+                           host(w.token_pos), w.block_size)
+    O.scatter(k_ref, w.layer, host(w.k_new), slots)
+    v_before = w.v_pool.clone()
+    N.kv_append(w.k_pool, None, w.layer, w.k_new, None, w.block_tables, w.offsets, w.token_seq,
+                w.token_pos)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(host(w.k_pool)), bits(k_ref))
+    assert torch.equal(w.v_pool.view(torch.int32), v_before.view(torch.int32))
+
+
+# ---------------------------------------------------------------------------
 # gather
 # ---------------------------------------------------------------------------
 def gather_both(w):
