@@ -25,3 +25,4 @@ from .oracle import (  # noqa: F401
     scatter_index_put,
     slot_mapping,
 )
+from .block_manager import BlockManagerOracle  # noqa: F401
