@@ -65,6 +65,33 @@ def decode_schedule(N, w, split_req):
     return sched, name + f" + reduce_kernel (split {sched})"
 
 
+def block_manager_host(N, W, steps=2000):
+    """The native block manager's bookkeeping for one decode step of the
+    decode batch, on the host: one new slot for each of the 32 sequences
+    (append_slots) and the export of their tables, lengths and offsets for
+    the kernels, called from Python through ctypes."""
+    import numpy as np
+
+    w = W.decode_batch(device="cpu", with_pools=False)
+    lens = w.seq_lens.numpy()
+    m = N.BlockManager(w.num_blocks, w.block_size)
+    ids = np.arange(w.num_seqs, dtype=np.int64)
+    for i, ln in enumerate(lens):
+        assert m.allocate(i, int(ln))
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        n, _slots = m.append_slots(ids)
+        if n != w.num_seqs:
+            raise RuntimeError("block manager ran out of blocks")
+        m.tables(ids)
+    dt = time.perf_counter() - t0
+    st = m.stats()
+    return {"us_per_step": dt / steps * 1e6, "steps": steps, "num_seqs": w.num_seqs,
+            "utilization_after": st["utilization"], "peak_used_blocks": st["peak_used"],
+            "what": "append_slots for every sequence + table/length/offset export, "
+                    "native manager called from Python"}
+
+
 def other_decode_configs(w, N, W, reps=32):
     """Decode alone on the prefix-sharing and long-context batches, over the
     same pools (same geometry), back to back with the layer rotated."""
@@ -497,6 +524,8 @@ def main():
         result["ops"] = prefill_ops(w, N, W)
         log("decode on the prefix-sharing and long-context batches")
         result["other_decode"] = other_decode_configs(w, N, W)
+        log("host block manager")
+        result["block_manager"] = block_manager_host(N, W)
     if not args.no_cpu_baseline:
         log("CPU oracle baseline")
         result["cpu_baseline"] = cpu_baseline(w, lens)

@@ -71,7 +71,12 @@ enum {
     PKV_ERR_WORKSPACE = -6,   /* workspace missing or smaller than required    */
     PKV_ERR_LAUNCH = -7,      /* the HIP launch reported an error              */
     PKV_ERR_UNSUPPORTED = -8, /* head_dim / query-group size not compiled in   */
-    PKV_ERR_DEVICE = -9       /* no usable HIP device                          */
+    PKV_ERR_DEVICE = -9,      /* no usable HIP device                          */
+    PKV_ERR_SEQ = -10,        /* block manager: unknown or duplicate sequence  */
+    PKV_ERR_BLOCK = -11,      /* block manager: block id out of range or free  */
+    PKV_ERR_HOST = -12,       /* host memory could not be allocated            */
+    PKV_NO_SPACE = 1          /* block manager: too few free blocks; nothing   */
+                              /* was changed (not an error)                    */
 };
 
 /* A paged KV pool: caller-owned device memory, only read or written during

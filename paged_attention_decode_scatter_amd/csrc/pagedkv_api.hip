@@ -504,6 +504,10 @@ PKV_API const char *pkv_status_string(int status) {
         case PKV_ERR_LAUNCH: return "HIP kernel launch failed";
         case PKV_ERR_UNSUPPORTED: return "head_dim or query-group size not supported";
         case PKV_ERR_DEVICE: return "no usable HIP device";
+        case PKV_ERR_SEQ: return "unknown or duplicate sequence id";
+        case PKV_ERR_BLOCK: return "block id out of range or free";
+        case PKV_ERR_HOST: return "host memory could not be allocated";
+        case PKV_NO_SPACE: return "too few free blocks (nothing changed)";
         default: return "unknown status";
     }
 }

@@ -285,3 +285,192 @@ def kv_validate(k_pool, block_tables, seq_lens, offsets, max_seq_len=-1, slot_ma
                                     _ptr(slot_mapping), nt, _ptr(counter), _stream(k_pool))
     _check("kv_validate", st)
     return int(counter.item())
+
+
+# ---------------------------------------------------------------------------
+# host block manager (pkv_block_manager.h)
+# ---------------------------------------------------------------------------
+BM_SYMBOLS = (
+    "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_can_allocate", "pkv_bm_allocate", "pkv_bm_share",
+    "pkv_bm_append_slot", "pkv_bm_append_slots", "pkv_bm_free", "pkv_bm_inc_ref",
+    "pkv_bm_dec_ref", "pkv_bm_seq_len", "pkv_bm_max_blocks", "pkv_bm_tables",
+    "pkv_bm_free_queue", "pkv_bm_ref_counts", "pkv_bm_get_stats",
+)
+NO_SPACE = 1
+
+
+class BmStats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in ("num_blocks", "block_size", "free_blocks",
+                                              "used_blocks", "peak_used_blocks", "live_tokens",
+                                              "num_seqs")]
+
+
+def _bm_lib():
+    lib = load_library()
+    if getattr(lib, "_bm_ready", False):
+        return lib
+    i32, i64, p = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+    lib.pkv_bm_create.restype = p
+    lib.pkv_bm_create.argtypes = [i32, i32]
+    lib.pkv_bm_destroy.restype = None
+    lib.pkv_bm_destroy.argtypes = [p]
+    lib.pkv_bm_can_allocate.restype = ctypes.c_int
+    lib.pkv_bm_can_allocate.argtypes = [p, i64, i32]
+    lib.pkv_bm_allocate.restype = ctypes.c_int
+    lib.pkv_bm_allocate.argtypes = [p, i64, i64, i32]
+    lib.pkv_bm_share.restype = ctypes.c_int
+    lib.pkv_bm_share.argtypes = [p, i64, i64, i32]
+    lib.pkv_bm_append_slot.restype = ctypes.c_int
+    lib.pkv_bm_append_slot.argtypes = [p, i64, p]
+    lib.pkv_bm_append_slots.restype = i32
+    lib.pkv_bm_append_slots.argtypes = [p, p, i32, p]
+    lib.pkv_bm_free.restype = ctypes.c_int
+    lib.pkv_bm_free.argtypes = [p, i64]
+    lib.pkv_bm_inc_ref.restype = ctypes.c_int
+    lib.pkv_bm_inc_ref.argtypes = [p, i32]
+    lib.pkv_bm_dec_ref.restype = ctypes.c_int
+    lib.pkv_bm_dec_ref.argtypes = [p, i32]
+    lib.pkv_bm_seq_len.restype = i64
+    lib.pkv_bm_seq_len.argtypes = [p, i64]
+    lib.pkv_bm_max_blocks.restype = i32
+    lib.pkv_bm_max_blocks.argtypes = [p, p, i32]
+    lib.pkv_bm_tables.restype = ctypes.c_int
+    lib.pkv_bm_tables.argtypes = [p, p, i32, p, i32, p, p]
+    lib.pkv_bm_free_queue.restype = i32
+    lib.pkv_bm_free_queue.argtypes = [p, p, i32]
+    lib.pkv_bm_ref_counts.restype = i32
+    lib.pkv_bm_ref_counts.argtypes = [p, p, i32]
+    lib.pkv_bm_get_stats.restype = ctypes.c_int
+    lib.pkv_bm_get_stats.argtypes = [p, ctypes.POINTER(BmStats)]
+    lib._bm_ready = True
+    return lib
+
+
+class _SeqView:
+    """`seq in manager.seqs` for the native manager."""
+
+    def __init__(self, bm):
+        self._bm = bm
+
+    def __contains__(self, seq):
+        return self._bm._lib.pkv_bm_seq_len(self._bm._h, int(seq)) >= 0
+
+
+class BlockManager:
+    """The native host block manager (FIFO free queue, reference counts,
+    per-sequence tables with a first-block offset).  Sequence ids are
+    integers.  allocate / append_slot answer False / None, changing nothing,
+    when the free queue is short."""
+
+    def __init__(self, num_blocks, block_size):
+        self._lib = _bm_lib()
+        self._h = self._lib.pkv_bm_create(num_blocks, block_size)
+        if not self._h:
+            raise PagedKVError("pkv_bm_create", -3)
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+        self.seqs = _SeqView(self)
+
+    def __del__(self):
+        h, self._h = getattr(self, "_h", None), None
+        if h:
+            self._lib.pkv_bm_destroy(h)
+
+    def _ok(self, fn, st):
+        if st < 0:
+            raise PagedKVError(fn, st)
+        return st
+
+    def can_allocate(self, num_tokens, offset=0):
+        return bool(self._ok("pkv_bm_can_allocate",
+                             self._lib.pkv_bm_can_allocate(self._h, num_tokens, offset)))
+
+    def allocate(self, seq, num_tokens, offset=0):
+        return self._ok("pkv_bm_allocate",
+                        self._lib.pkv_bm_allocate(self._h, seq, num_tokens, offset)) == 0
+
+    def share(self, src, dst, num_blocks):
+        self._ok("pkv_bm_share", self._lib.pkv_bm_share(self._h, src, dst, num_blocks))
+
+    def append_slot(self, seq):
+        slot = ctypes.c_int64(-1)
+        st = self._ok("pkv_bm_append_slot",
+                      self._lib.pkv_bm_append_slot(self._h, seq, ctypes.byref(slot)))
+        return None if st == NO_SPACE else slot.value
+
+    def append_slots(self, seqs):
+        """Slots of one new token for each of seqs (int64 array), in order;
+        returns (number appended, slots)."""
+        import numpy as np
+
+        ids = np.ascontiguousarray(seqs, dtype=np.int64)
+        out = np.full(ids.shape[0], -1, dtype=np.int64)
+        n = self._ok("pkv_bm_append_slots", self._lib.pkv_bm_append_slots(
+            self._h, ids.ctypes.data, ids.shape[0], out.ctypes.data))
+        return n, out
+
+    def free(self, seq):
+        self._ok("pkv_bm_free", self._lib.pkv_bm_free(self._h, seq))
+
+    def inc_ref(self, block):
+        self._ok("pkv_bm_inc_ref", self._lib.pkv_bm_inc_ref(self._h, block))
+
+    def dec_ref(self, block):
+        self._ok("pkv_bm_dec_ref", self._lib.pkv_bm_dec_ref(self._h, block))
+
+    def seq_len(self, seq):
+        return self._ok("pkv_bm_seq_len", self._lib.pkv_bm_seq_len(self._h, seq))
+
+    def tables(self, seqs, stride=None):
+        """(tables [n, stride] int32 padded with -1, seq_lens, offsets) for
+        the kernels, as host numpy arrays."""
+        import numpy as np
+
+        ids = np.ascontiguousarray(seqs, dtype=np.int64)
+        n = ids.shape[0]
+        need = self._ok("pkv_bm_max_blocks", self._lib.pkv_bm_max_blocks(self._h, ids.ctypes.data, n))
+        stride = max(need, 1) if stride is None else stride
+        tab = np.empty((n, stride), dtype=np.int32)
+        lens = np.empty(n, dtype=np.int32)
+        offs = np.empty(n, dtype=np.int32)
+        self._ok("pkv_bm_tables", self._lib.pkv_bm_tables(
+            self._h, ids.ctypes.data, n, tab.ctypes.data, stride, lens.ctypes.data,
+            offs.ctypes.data))
+        return tab, lens, offs
+
+    def table(self, seq):
+        tab, _, _ = self.tables([seq])
+        return [int(b) for b in tab[0] if b >= 0]
+
+    def capacity(self, seq):
+        tab, _, offs = self.tables([seq])
+        return int((tab[0] >= 0).sum()) * self.block_size - int(offs[0])
+
+    @property
+    def free_ids(self):
+        import numpy as np
+
+        buf = np.empty(self.num_blocks, dtype=np.int32)
+        n = self._ok("pkv_bm_free_queue",
+                     self._lib.pkv_bm_free_queue(self._h, buf.ctypes.data, self.num_blocks))
+        return [int(b) for b in buf[:n]]
+
+    @property
+    def ref_count(self):
+        import numpy as np
+
+        buf = np.empty(self.num_blocks, dtype=np.int32)
+        self._ok("pkv_bm_ref_counts",
+                 self._lib.pkv_bm_ref_counts(self._h, buf.ctypes.data, self.num_blocks))
+        return [int(c) for c in buf]
+
+    def used(self):
+        return self.stats()["used"]
+
+    def stats(self):
+        st = BmStats()
+        self._ok("pkv_bm_get_stats", self._lib.pkv_bm_get_stats(self._h, ctypes.byref(st)))
+        used = st.used_blocks
+        util = st.live_tokens / (used * st.block_size) if used else 0.0
+        return {"free": st.free_blocks, "used": used, "peak_used": st.peak_used_blocks,
+                "live_tokens": st.live_tokens, "utilization": util}

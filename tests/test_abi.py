@@ -2,6 +2,7 @@
 arguments on the host before any HIP call (no GPU needed: every call here
 fails its argument checks, so nothing is enqueued)."""
 import ctypes
+import glob
 import os
 import re
 
@@ -10,14 +11,16 @@ import pytest
 from paged_attention_decode_scatter_amd import native as N
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "pagedkv.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 OK, NULL, DTYPE, SHAPE, LAYER, ALIGN, WORKSPACE, LAUNCH, UNSUP = 0, -1, -2, -3, -4, -5, -6, -7, -8
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    return re.findall(r"PKV_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
+    names = []
+    for h in HEADERS:
+        names += re.findall(r"PKV_API\s+[\w\s\*]+?\b(\w+)\s*\(", open(h).read())
+    return names
 
 
 @pytest.fixture(scope="module")
@@ -30,8 +33,8 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 10
-    assert set(names) == set(N.SYMBOLS)
+    assert len(names) == len(set(names)) == 26
+    assert set(names) == set(N.SYMBOLS) | set(N.BM_SYMBOLS)
     for n in names:
         assert hasattr(lib, n), n
 
