@@ -21,6 +21,7 @@ from .oracle import (  # noqa: F401
     gather_loop_cat,
     last_block_fill,
     library_path,
+    prefill,
     scatter,
     scatter_index_put,
     slot_mapping,

@@ -47,6 +47,9 @@ def _load():
     lib.orc_scatter.argtypes = [p, i64, i64, i64, i64, i64, p, p, i64]
     lib.orc_gather.restype = i64
     lib.orc_gather.argtypes = [p, i64, i64, i64, i64, i64, p, i64, p, p, i64, p]
+    lib.orc_prefill.restype = i64
+    lib.orc_prefill.argtypes = [p, p, i64, i64, i64, i64, i64, i64, i64, p, p, i64, p, i64,
+                                p, p, i64, ctypes.c_double, p, i64]
     lib.orc_decode.restype = i64
     lib.orc_decode.argtypes = [p, p, i64, i64, i64, i64, i64, i64, i64, p, i64,
                                p, i64, p, p, i64, ctypes.c_double, p, i64]
@@ -144,6 +147,35 @@ def decode(k_pool, v_pool, layer, q, block_tables, seq_lens, offsets, scale,
                             float(scale), _ptr(out), int(num_threads))
     if rc != 0:
         raise ValueError("oracle decode: bad arguments or table")
+    return out
+
+
+def prefill(k_pool, v_pool, layer, q, q_start, block_tables, seq_lens, offsets, scale,
+            num_threads=1):
+    """Causal attention of each sequence's last n = q_start[s+1]-q_start[s]
+    tokens (rows q_start[s].. of q) over its cached tokens, in double;
+    returns float64 (rows, Hq, D).  [P2 sec. 2.4 prefill; sec. 2.3]"""
+    k_pool = _c(k_pool, k_pool.dtype)
+    v_pool = _c(v_pool, k_pool.dtype)
+    dt = _dtype_code(k_pool)
+    nb, nl, bs, hkv, d = k_pool.shape
+    q = _c(q, k_pool.dtype)
+    rows, hq, dq = q.shape
+    if dq != d:
+        raise ValueError("q head_dim mismatch")
+    qs = _c(q_start, np.int32)
+    bt = _c(block_tables, np.int32)
+    sl = _c(seq_lens, np.int32)
+    off = _c(offsets, np.int32)
+    ns = sl.shape[0]
+    if qs.shape[0] != ns + 1 or int(qs[-1]) != rows:
+        raise ValueError("q_start must have num_seqs + 1 entries ending at the row count")
+    out = np.empty((rows, hq, d), dtype=np.float64)
+    rc = _load().orc_prefill(_ptr(k_pool), _ptr(v_pool), nb, nl, bs, hkv, d, dt, layer, _ptr(q),
+                             _ptr(qs), hq, _ptr(bt), bt.shape[1], _ptr(sl), _ptr(off), ns,
+                             float(scale), _ptr(out), int(num_threads))
+    if rc != 0:
+        raise ValueError("oracle prefill: bad arguments or table")
     return out
 
 

@@ -156,20 +156,29 @@ int64_t orc_gather(const uint8_t *pool, int64_t num_blocks, int64_t num_layers,
 }
 
 /* ------------------------------------------------------------------------
- * Decode attention, as "gather, then standard multi-head attention"
+ * Attention, as "gather, then standard multi-head attention"
  * [P2 sec. 2.3; P3 sec. 3.1: gather into a contiguous tensor, then SDPA].
  * The fused paged kernel only removes the copy [P1 "comparison with vLLM"],
  * so this is the result it must reproduce.
  *
- * For sequence s and query head h, with G = num_q_heads / num_kv_heads and
- * kv head g = h / G (contiguous GQA groups; G = 1 is plain MHA):
+ * Queries of sequence s (L = seq_lens[s] cached tokens):
+ *   decode  (q_start == NULL): one query, row s of q, at logical position
+ *           L - 1 -- it sees every cached token (no mask);
+ *   prefill (q_start given): the rows q_start[s] .. q_start[s+1]-1 of q are
+ *           the sequence's last n tokens [P2 sec. 2.4 "prefill batch": the
+ *           prompt tokens' K/V are written, then attended]; query i sits at
+ *           logical position L - n + i and sees tokens 0 .. L - n + i
+ *           (causal).  A query whose position would be negative sees
+ *           nothing and yields zeros.
+ * For a query at position P and query head h, with G = num_q_heads /
+ * num_kv_heads and kv head g = h / G (contiguous GQA groups; G = 1 is MHA):
  *   Kc, Vc = gather(s) restricted to kv head g       (seq_len x head_dim)
- *   score_t = scale * sum_d q[s,h,d] * Kc[t,d]
+ *   score_t = scale * sum_d q[row,h,d] * Kc[t,d]      for t = 0 .. P
  *   w_t     = exp(score_t - max_t score_t)
- *   out[s,h,:] = sum_t w_t * Vc[t,:] / sum_t w_t
+ *   out[row,h,:] = sum_t w_t * Vc[t,:] / sum_t w_t
  * in double.  A sequence of length 0 yields zeros.
- * q: (num_seqs, num_q_heads, head_dim) in the pool dtype.
- * out: (num_seqs, num_q_heads, head_dim) double.
+ * q: (rows, num_q_heads, head_dim) in the pool dtype.
+ * out: (rows, num_q_heads, head_dim) double.
  * The (s, g) work items are independent; `num_threads` worker threads each
  * take whole items, so threading changes no arithmetic.
  * Returns 0, or -1 on bad arguments.
@@ -180,6 +189,7 @@ typedef struct {
     int dtype;
     int64_t layer;
     const uint8_t *q;
+    const int32_t *q_start;   /* NULL: decode */
     int64_t num_q_heads;
     const int32_t *block_tables;
     int64_t bt_stride;
@@ -193,16 +203,19 @@ typedef struct {
 } decode_job;
 
 /* One work item: sequence s and kv head g.  The sequence is gathered once,
- * then every query head of group g (h = g*G .. g*G+G-1, i.e. h / G == g)
- * attends over it. */
+ * then every query of the sequence, for every query head of group g
+ * (h = g*G .. g*G+G-1, i.e. h / G == g), attends over its visible tokens. */
 static int decode_group(decode_job *J, int64_t s, int64_t g) {
     const int64_t D = J->head_dim;
     const int64_t e = elem_size(J->dtype);
     const int64_t row_bytes = J->num_kv_heads * D * e;
     const int64_t G = J->num_q_heads / J->num_kv_heads;
     const int64_t L = J->seq_lens[s];
-    for (int64_t h = g * G; h < (g + 1) * G; h++)
-        for (int64_t d = 0; d < D; d++) J->out[(s * J->num_q_heads + h) * D + d] = 0.0;
+    const int64_t n = J->q_start ? (int64_t)J->q_start[s + 1] - J->q_start[s] : 1;
+    const int64_t row0 = J->q_start ? J->q_start[s] : s;
+    for (int64_t i = 0; i < n; i++)
+        for (int64_t h = g * G; h < (g + 1) * G; h++)
+            for (int64_t d = 0; d < D; d++) J->out[((row0 + i) * J->num_q_heads + h) * D + d] = 0.0;
     if (L == 0) return 0;
 
     /* gather the whole sequence (all kv heads) with the definition above */
@@ -222,27 +235,32 @@ static int decode_group(decode_job *J, int64_t s, int64_t g) {
         goto done;
     }
 
-    for (int64_t h = g * G; h < (g + 1) * G; h++) {
-        const uint8_t *qh = J->q + (s * J->num_q_heads + h) * D * e;
-        double *o = J->out + (s * J->num_q_heads + h) * D;
-        double mx = -INFINITY;
-        for (int64_t t = 0; t < L; t++) {
-            const uint8_t *kt = krows + t * row_bytes + g * D * e;
-            double dot = 0.0;
-            for (int64_t d = 0; d < D; d++)
-                dot += load_elem(qh + d * e, J->dtype) * load_elem(kt + d * e, J->dtype);
-            score[t] = J->scale * dot;
-            if (score[t] > mx) mx = score[t];
+    for (int64_t i = 0; i < n; i++) {
+        const int64_t P = L - n + i;   /* the query's logical position */
+        if (P < 0) continue;           /* sees no token: zeros */
+        const int64_t row = row0 + i;
+        for (int64_t h = g * G; h < (g + 1) * G; h++) {
+            const uint8_t *qh = J->q + (row * J->num_q_heads + h) * D * e;
+            double *o = J->out + (row * J->num_q_heads + h) * D;
+            double mx = -INFINITY;
+            for (int64_t t = 0; t <= P; t++) {
+                const uint8_t *kt = krows + t * row_bytes + g * D * e;
+                double dot = 0.0;
+                for (int64_t d = 0; d < D; d++)
+                    dot += load_elem(qh + d * e, J->dtype) * load_elem(kt + d * e, J->dtype);
+                score[t] = J->scale * dot;
+                if (score[t] > mx) mx = score[t];
+            }
+            double den = 0.0;
+            for (int64_t d = 0; d < D; d++) num[d] = 0.0;
+            for (int64_t t = 0; t <= P; t++) {
+                double w = exp(score[t] - mx);
+                den += w;
+                const uint8_t *vt = vrows + t * row_bytes + g * D * e;
+                for (int64_t d = 0; d < D; d++) num[d] += w * load_elem(vt + d * e, J->dtype);
+            }
+            for (int64_t d = 0; d < D; d++) o[d] = num[d] / den;
         }
-        double den = 0.0;
-        for (int64_t d = 0; d < D; d++) num[d] = 0.0;
-        for (int64_t t = 0; t < L; t++) {
-            double w = exp(score[t] - mx);
-            den += w;
-            const uint8_t *vt = vrows + t * row_bytes + g * D * e;
-            for (int64_t d = 0; d < D; d++) num[d] += w * load_elem(vt + d * e, J->dtype);
-        }
-        for (int64_t d = 0; d < D; d++) o[d] = num[d] / den;
     }
 
 done:
@@ -270,12 +288,13 @@ static void *decode_worker(void *arg) {
     return NULL;
 }
 
-int64_t orc_decode(const uint8_t *kpool, const uint8_t *vpool, int64_t num_blocks,
-                   int64_t num_layers, int64_t block_size, int64_t num_kv_heads,
-                   int64_t head_dim, int64_t dtype, int64_t layer, const uint8_t *q,
-                   int64_t num_q_heads, const int32_t *block_tables, int64_t bt_stride,
-                   const int32_t *seq_lens, const int32_t *offsets, int64_t num_seqs,
-                   double scale, double *out, int64_t num_threads) {
+static int64_t run_attention(const uint8_t *kpool, const uint8_t *vpool, int64_t num_blocks,
+                             int64_t num_layers, int64_t block_size, int64_t num_kv_heads,
+                             int64_t head_dim, int64_t dtype, int64_t layer, const uint8_t *q,
+                             const int32_t *q_start, int64_t num_q_heads,
+                             const int32_t *block_tables, int64_t bt_stride,
+                             const int32_t *seq_lens, const int32_t *offsets, int64_t num_seqs,
+                             double scale, double *out, int64_t num_threads) {
     if (dtype != ORC_F32 && dtype != ORC_BF16) return -1;
     if (num_kv_heads <= 0 || num_q_heads <= 0 || num_q_heads % num_kv_heads != 0) return -1;
     if (layer < 0 || layer >= num_layers || head_dim <= 0) return -1;
@@ -283,7 +302,7 @@ int64_t orc_decode(const uint8_t *kpool, const uint8_t *vpool, int64_t num_block
     J.kpool = kpool; J.vpool = vpool;
     J.num_blocks = num_blocks; J.num_layers = num_layers; J.block_size = block_size;
     J.num_kv_heads = num_kv_heads; J.head_dim = head_dim; J.dtype = (int)dtype;
-    J.layer = layer; J.q = q; J.num_q_heads = num_q_heads;
+    J.layer = layer; J.q = q; J.q_start = q_start; J.num_q_heads = num_q_heads;
     J.block_tables = block_tables; J.bt_stride = bt_stride;
     J.seq_lens = seq_lens; J.offsets = offsets; J.num_seqs = num_seqs;
     J.scale = scale; J.out = out; J.next_item = 0; J.failed = 0;
@@ -300,4 +319,31 @@ int64_t orc_decode(const uint8_t *kpool, const uint8_t *vpool, int64_t num_block
     for (int64_t i = 1; i <= started; i++) pthread_join(tid[i], NULL);
     pthread_mutex_destroy(&J.lock);
     return J.failed ? -1 : 0;
+}
+
+int64_t orc_decode(const uint8_t *kpool, const uint8_t *vpool, int64_t num_blocks,
+                   int64_t num_layers, int64_t block_size, int64_t num_kv_heads,
+                   int64_t head_dim, int64_t dtype, int64_t layer, const uint8_t *q,
+                   int64_t num_q_heads, const int32_t *block_tables, int64_t bt_stride,
+                   const int32_t *seq_lens, const int32_t *offsets, int64_t num_seqs,
+                   double scale, double *out, int64_t num_threads) {
+    return run_attention(kpool, vpool, num_blocks, num_layers, block_size, num_kv_heads,
+                         head_dim, dtype, layer, q, NULL, num_q_heads, block_tables, bt_stride,
+                         seq_lens, offsets, num_seqs, scale, out, num_threads);
+}
+
+/* Prefill / append attention (see above): q_start[num_seqs + 1] are row
+ * offsets into q and out, nondecreasing from q_start[0] = 0. */
+int64_t orc_prefill(const uint8_t *kpool, const uint8_t *vpool, int64_t num_blocks,
+                    int64_t num_layers, int64_t block_size, int64_t num_kv_heads,
+                    int64_t head_dim, int64_t dtype, int64_t layer, const uint8_t *q,
+                    const int32_t *q_start, int64_t num_q_heads, const int32_t *block_tables,
+                    int64_t bt_stride, const int32_t *seq_lens, const int32_t *offsets,
+                    int64_t num_seqs, double scale, double *out, int64_t num_threads) {
+    if (!q_start || q_start[0] != 0) return -1;
+    for (int64_t s = 0; s < num_seqs; s++)
+        if (q_start[s + 1] < q_start[s]) return -1;
+    return run_attention(kpool, vpool, num_blocks, num_layers, block_size, num_kv_heads,
+                         head_dim, dtype, layer, q, q_start, num_q_heads, block_tables, bt_stride,
+                         seq_lens, offsets, num_seqs, scale, out, num_threads);
 }

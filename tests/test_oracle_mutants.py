@@ -44,8 +44,9 @@ MUTANTS = {
         "uint32_t bits = ((uint32_t)h) << 16;",
         "uint32_t bits = ((uint32_t)h) << 15;"),
     "gqa_interleaved_heads": (
-        "    for (int64_t h = g * G; h < (g + 1) * G; h++) {\n        const uint8_t *qh",
-        "    for (int64_t h = g; h < J->num_q_heads; h += J->num_kv_heads) {\n        const uint8_t *qh"),
+        "        for (int64_t h = g * G; h < (g + 1) * G; h++) {\n            const uint8_t *qh",
+        "        for (int64_t h = g; h < J->num_q_heads; h += J->num_kv_heads) {\n"
+        "            const uint8_t *qh"),
     "decode_drops_scale": (
         "score[t] = J->scale * dot;",
         "score[t] = dot;"),
@@ -56,8 +57,14 @@ MUTANTS = {
         "const uint8_t *vt = vrows + t * row_bytes + g * D * e;",
         "const uint8_t *vt = krows + t * row_bytes + g * D * e;"),
     "decode_off_by_one_token": (
-        "for (int64_t t = 0; t < L; t++) {\n            double w",
-        "for (int64_t t = 0; t + 1 < L; t++) {\n            double w"),
+        "for (int64_t t = 0; t <= P; t++) {\n                double w",
+        "for (int64_t t = 0; t < P; t++) {\n                double w"),
+    "prefill_ignores_prefix": (
+        "const int64_t P = L - n + i;",
+        "const int64_t P = i;"),
+    "prefill_without_causal_mask": (
+        "const int64_t P = L - n + i;",
+        "const int64_t P = L - 1;"),
 }
 
 

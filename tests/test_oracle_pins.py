@@ -428,3 +428,90 @@ def test_decode_threads_do_not_change_results():
     a = O.decode(k, v, 0, q, bt, lens, offs, 0.35, num_threads=1)
     b = O.decode(k, v, 0, q, bt, lens, offs, 0.35, num_threads=5)
     assert np.array_equal(a, b)
+
+
+# ---------------------------------------------------------------------------
+# prefill / append attention (causal, queries = each sequence's last tokens)
+# ---------------------------------------------------------------------------
+def make_prefill_case(rng, nseq, hkv, G, d, bs, bf16, max_len=40, nl=2):
+    k, v, _, bt, lens, offs = make_decode_case(rng, nseq, hkv, G, d, bs, bf16, max_len, nl)
+    nq = np.array([rng.integers(1, int(l) + 1) for l in lens], dtype=np.int32)
+    q_start = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+    qf = rng.standard_normal((int(q_start[-1]), hkv * G, d)).astype(np.float32)
+    q = f32_to_bf16_bits(qf) if bf16 else qf
+    return k, v, q, q_start, bt, lens, offs
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("G", [1, 2, 4])
+def test_prefill_matches_torch_sdpa_with_causal_mask(bf16, G):
+    """[P2 sec. 2.4 prefill; sec. 2.3] each sequence's last n tokens attend
+    causally over its gathered K/V: compared with torch's
+    scaled_dot_product_attention in float64 with an explicit boolean mask
+    (query i at position L - n + i sees keys 0 .. L - n + i)."""
+    rng = np.random.default_rng(200 + G + 10 * bf16)
+    hkv, d, bs, layer = 2, 16, 4, 1
+    k, v, q, q_start, bt, lens, offs = make_prefill_case(rng, 5, hkv, G, d, bs, bf16)
+    scale = 0.3
+    got = O.prefill(k, v, layer, q, q_start, bt, lens, offs, scale, num_threads=3)
+    for s in range(len(lens)):
+        L, n = int(lens[s]), int(q_start[s + 1] - q_start[s])
+        kc = to_f64(O.gather_flat_index(k[:, layer], bt[s], L, bs, int(offs[s])))
+        vc = to_f64(O.gather_flat_index(v[:, layer], bt[s], L, bs, int(offs[s])))
+        K = torch.from_numpy(kc).permute(1, 0, 2).repeat_interleave(G, dim=0)   # (Hq, L, D)
+        V = torch.from_numpy(vc).permute(1, 0, 2).repeat_interleave(G, dim=0)
+        Q = torch.from_numpy(to_f64(q[q_start[s]:q_start[s + 1]])).permute(1, 0, 2)  # (Hq, n, D)
+        pos = torch.arange(L - n, L)[:, None]
+        mask = torch.arange(L)[None, :] <= pos                                    # (n, L)
+        ref = torch.nn.functional.scaled_dot_product_attention(Q, K, V, attn_mask=mask,
+                                                               scale=scale)
+        np.testing.assert_allclose(got[q_start[s]:q_start[s + 1]], ref.permute(1, 0, 2).numpy(),
+                                   rtol=0, atol=1e-12)
+
+
+def test_prefill_without_prefix_is_torch_causal():
+    """n = L (the whole prompt is new): plain causal attention, torch's
+    is_causal form."""
+    rng = np.random.default_rng(21)
+    hkv, G, d, bs = 2, 2, 16, 4
+    k, v, _, bt, lens, offs = make_decode_case(rng, 3, hkv, G, d, bs, False)
+    q_start = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    q = rng.standard_normal((int(q_start[-1]), hkv * G, d)).astype(np.float32)
+    got = O.prefill(k, v, 0, q, q_start, bt, lens, offs, 0.4)
+    for s in range(3):
+        L = int(lens[s])
+        kc = O.gather_flat_index(k[:, 0], bt[s], L, bs, int(offs[s])).astype(np.float64)
+        vc = O.gather_flat_index(v[:, 0], bt[s], L, bs, int(offs[s])).astype(np.float64)
+        K = torch.from_numpy(kc).permute(1, 0, 2).repeat_interleave(G, dim=0)
+        V = torch.from_numpy(vc).permute(1, 0, 2).repeat_interleave(G, dim=0)
+        Q = torch.from_numpy(q[q_start[s]:q_start[s + 1]].astype(np.float64)).permute(1, 0, 2)
+        ref = torch.nn.functional.scaled_dot_product_attention(Q, K, V, is_causal=True, scale=0.4)
+        np.testing.assert_allclose(got[q_start[s]:q_start[s + 1]], ref.permute(1, 0, 2).numpy(),
+                                   rtol=0, atol=1e-12)
+        # the prompt's first token sees only itself: out = V[0] exactly
+        assert np.array_equal(got[q_start[s]], np.repeat(vc[0], G, axis=0))
+
+
+def test_prefill_of_one_query_is_decode():
+    """n = 1: the last token sees every cached token -- the decode result,
+    bit for bit."""
+    rng = np.random.default_rng(22)
+    k, v, q, bt, lens, offs = make_decode_case(rng, 6, 2, 4, 8, 4, True)
+    q_start = np.arange(7, dtype=np.int32)
+    a = O.prefill(k, v, 1, q, q_start, bt, lens, offs, 0.35)
+    b = O.decode(k, v, 1, q, bt, lens, offs, 0.35)
+    assert np.array_equal(a, b)
+
+
+def test_prefill_queries_beyond_the_sequence_are_zero():
+    """More queries than cached tokens: the leading queries would sit at a
+    negative position, see nothing and give zeros; the rest are unchanged."""
+    rng = np.random.default_rng(23)
+    k, v, _, bt, lens, offs = make_decode_case(rng, 2, 2, 2, 8, 4, False)
+    L0, L1 = int(lens[0]), int(lens[1])
+    q_start = np.array([0, L0 + 3, L0 + 3 + L1], np.int32)   # 3 extra queries for seq 0
+    q = rng.standard_normal((L0 + 3 + L1, 4, 8)).astype(np.float32)
+    got = O.prefill(k, v, 0, q, q_start, bt, lens, offs, 0.5)
+    assert np.all(got[:3] == 0)
+    ref = O.prefill(k, v, 0, q[3:], np.array([0, L0, L0 + L1], np.int32), bt, lens, offs, 0.5)
+    assert np.array_equal(got[3:], ref)
