@@ -285,6 +285,35 @@ PKV_API int paged_attn_decode(const pkv_pool *pool, int32_t layer,
                               void *stream);
 
 /*
+ * paged_attn_prefill -- prefill / append attention: the queries of
+ * sequence s are its last n_s = q_start[s+1] - q_start[s] cached tokens
+ * (their K/V already written, e.g. by kv_append) [P2 sec. 2.4 "prefill
+ * batch"]; query i of s sits at logical position P = seq_lens[s] - n_s + i
+ * and attends causally to the sequence's tokens 0 .. P, read in place
+ * through its block table and first-block offset [P3 sec. 2.2] -- so a
+ * request whose first blocks are a shared prefix attends to them without a
+ * copy.  For query head h (kv head h / G, as for decode):
+ *   out[row,h,:] = softmax_t<=P(scale * q[row,h,:] . K_t) . V_t
+ * fp32 accumulation, out rounded to the pool dtype.  A query with P < 0
+ * (more queries than tokens) gives zeros.  n_s = 1 is paged_attn_decode.
+ *
+ *   q, out        device [num_q_rows, num_q_heads, head_dim], pool dtype
+ *   q_start       device int32 [num_seqs + 1]: q_start[0] = 0, nondecreasing,
+ *                 q_start[num_seqs] = num_q_rows (caller contract)
+ *   max_q_len     host bound on every n_s (rows of a sequence past it are
+ *                 left unwritten)
+ *   block_tables, seq_lens, offsets  as for paged_attn_decode
+ * Supported: head_dim in {64, 128}, G in {1, 2, 4, 8}.
+ * Errors: PKV_ERR_NULL, _DTYPE, _SHAPE, _LAYER, _ALIGN, _UNSUPPORTED, _LAUNCH.
+ */
+PKV_API int paged_attn_prefill(const pkv_pool *pool, int32_t layer,
+                               const void *q, int32_t num_q_heads,
+                               const int32_t *q_start, int32_t num_q_rows, int32_t max_q_len,
+                               const int32_t *block_tables, int32_t bt_stride,
+                               const int32_t *seq_lens, const int32_t *offsets,
+                               int32_t num_seqs, float scale, void *out, void *stream);
+
+/*
  * kv_validate -- count violations of the caller contract, for debugging:
  * offsets outside [0, block_size); seq_len < 0, > max_seq_len (when
  * max_seq_len >= 0) or > the table's capacity bt_stride*block_size - offset

@@ -1,0 +1,207 @@
+// attn_common.h -- device helpers shared by the attention kernels
+// (kernels_decode.hip, kernels_prefill.hip): vector types, bf16 <-> fp32
+// conversions, 16-byte dot products, cross-lane reductions, the direct
+// global -> LDS copy, and the tile geometry of the bf16 matrix-core path.
+// Everything here is inline or a template.
+#pragma once
+
+#include "pkv_internal.h"
+
+namespace pkv {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+template <int DT>
+struct Elem;
+template <>
+struct Elem<0> {  // PKV_F32
+    static constexpr int kBytes = 4;
+};
+template <>
+struct Elem<1> {  // PKV_BF16
+    static constexpr int kBytes = 2;
+};
+
+__device__ __forceinline__ u32x4 ld16(const char *p) {
+    return *reinterpret_cast<const u32x4 *>(p);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Round-to-nearest-even float -> bf16 bits (quiet NaN kept NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// A 32-bit word as a pair of bf16.  The word is passed by value on
+// purpose: applying __builtin_bit_cast directly to an ext_vector element
+// (q.y, q.z, ...) makes this compiler read element .x every time.
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t w) { return __builtin_bit_cast(bf16x2, w); }
+
+// Dot product of one 16-byte piece of q with one 16-byte piece of K.
+template <int DT>
+__device__ __forceinline__ float dot16(u32x4 q, u32x4 k);
+
+template <>
+__device__ __forceinline__ float dot16<1>(u32x4 q, u32x4 k) {
+    float s = 0.0f;
+    s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q.x), as_bf16x2(k.x), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q.y), as_bf16x2(k.y), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q.z), as_bf16x2(k.z), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q.w), as_bf16x2(k.w), s, false);
+    return s;
+}
+
+template <>
+__device__ __forceinline__ float dot16<0>(u32x4 q, u32x4 k) {
+    float s = __uint_as_float(q.x) * __uint_as_float(k.x);
+    s = fmaf(__uint_as_float(q.y), __uint_as_float(k.y), s);
+    s = fmaf(__uint_as_float(q.z), __uint_as_float(k.z), s);
+    s = fmaf(__uint_as_float(q.w), __uint_as_float(k.w), s);
+    return s;
+}
+
+// The VEC fp32 values of one 16-byte piece.
+template <int DT>
+__device__ __forceinline__ void unpack16(u32x4 x, float *f);
+
+template <>
+__device__ __forceinline__ void unpack16<1>(u32x4 x, float *f) {
+    f[0] = bf16_lo(x.x); f[1] = bf16_hi(x.x);
+    f[2] = bf16_lo(x.y); f[3] = bf16_hi(x.y);
+    f[4] = bf16_lo(x.z); f[5] = bf16_hi(x.z);
+    f[6] = bf16_lo(x.w); f[7] = bf16_hi(x.w);
+}
+
+template <>
+__device__ __forceinline__ void unpack16<0>(u32x4 x, float *f) {
+    f[0] = __uint_as_float(x.x); f[1] = __uint_as_float(x.y);
+    f[2] = __uint_as_float(x.z); f[3] = __uint_as_float(x.w);
+}
+
+// Store VEC fp32 values as one 16-byte piece of the output dtype.
+template <int DT>
+__device__ __forceinline__ void store16(char *p, const float *f);
+
+template <>
+__device__ __forceinline__ void store16<1>(char *p, const float *f) {
+    u32x4 x;
+    x.x = f32_to_bf16_bits(f[0]) | (f32_to_bf16_bits(f[1]) << 16);
+    x.y = f32_to_bf16_bits(f[2]) | (f32_to_bf16_bits(f[3]) << 16);
+    x.z = f32_to_bf16_bits(f[4]) | (f32_to_bf16_bits(f[5]) << 16);
+    x.w = f32_to_bf16_bits(f[6]) | (f32_to_bf16_bits(f[7]) << 16);
+    *reinterpret_cast<u32x4 *>(p) = x;
+}
+
+template <>
+__device__ __forceinline__ void store16<0>(char *p, const float *f) {
+    u32x4 x;
+    x.x = __float_as_uint(f[0]); x.y = __float_as_uint(f[1]);
+    x.z = __float_as_uint(f[2]); x.w = __float_as_uint(f[3]);
+    *reinterpret_cast<u32x4 *>(p) = x;
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the W consecutive lanes of a row group (W a power of two <= 64);
+// every lane of the group gets the same bits (each step adds two equal
+// partial sums in both orders, and fp addition commutes).
+template <int W>
+__device__ __forceinline__ float row_allsum(float v) {
+    if constexpr (W >= 2) v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+    if constexpr (W >= 4) v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+    if constexpr (W >= 8) v += dpp<0x141>(v);  // row_half_mirror
+    if constexpr (W >= 16) v += dpp<0x140>(v); // row_mirror
+    if constexpr (W >= 32) v += __shfl_xor(v, 16);
+    if constexpr (W >= 64) v += __shfl_xor(v, 32);
+    return v;
+}
+
+// Reduce across the row groups of a wavefront (lanes equal mod W).
+template <int W>
+__device__ __forceinline__ float cross_rows_max(float v) {
+#pragma unroll
+    for (int m = W; m < 64; m <<= 1) v = fmaxf(v, __shfl_xor(v, m));
+    return v;
+}
+template <int W>
+__device__ __forceinline__ float cross_rows_sum(float v) {
+#pragma unroll
+    for (int m = W; m < 64; m <<= 1) v += __shfl_xor(v, m);
+    return v;
+}
+
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+constexpr float kNegInf = -__builtin_huge_valf();
+
+#ifndef PKV_DECODE_RING
+#define PKV_DECODE_RING 3
+#endif
+// Pipeline depth of the bf16 decode kernel (chunks in flight + the one
+// being computed).
+constexpr int kDecodeRing = PKV_DECODE_RING;
+
+// Copy 16 bytes per lane from global memory straight into LDS: lane i's
+// bytes land at lds_wave_base + 16*i (global_load_lds_dwordx4).  The LDS
+// address must be the same in every lane.
+__device__ __forceinline__ void lds_copy16(const char *src, char *lds_wave_base) {
+    __builtin_amdgcn_global_load_lds(const_cast<char *>(src),
+                                     (__attribute__((address_space(3))) void *)lds_wave_base, 16, 0, 0);
+}
+
+// Keep the compiler from moving LDS accesses across this point; the LDS
+// unit itself serves one wavefront's requests in order.
+__device__ __forceinline__ void wave_lds_order() {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
+    return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+    return x;
+}
+
+__device__ __forceinline__ float lane_value(float x, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
+}
+
+template <int D>
+struct MfmaShape {
+    static constexpr int E = 2;
+    static constexpr int ROWB = D * E;           // bytes of one kv-head row
+    static constexpr int PPR = ROWB / 16;        // 16-byte pieces per row
+    static constexpr int RPI = 64 / PPR;         // rows per tile-load instruction
+    static constexpr int NP = 16 / RPI;          // tile-load instructions per chunk
+    static constexpr int KS = D / 32;            // QK^T steps (k = 32)
+    static constexpr int NV = D / 16;            // P.V column slabs (n = 16)
+    static constexpr int VSLAB = 1024 + 32;      // one tile-load instruction + padding
+    static constexpr int VTILE = NP * VSLAB;     // V tile of one ring slot
+    static constexpr int KROW = ROWB + 16;       // padded K-tile row
+    static constexpr int KTILE = 16 * KROW;
+    static constexpr int NSLOT = kDecodeRing;    // pipeline stages (chunks in flight + 1)
+    static constexpr int LOADS = 2 * NP;         // vector-memory ops per chunk
+    static_assert(D % 32 == 0 && PPR >= 4 && PPR <= 16 && RPI * ROWB == 1024, "shape");
+};
+
+}  // namespace pkv

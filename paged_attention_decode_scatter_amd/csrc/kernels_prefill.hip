@@ -1,0 +1,446 @@
+// kernels_prefill.hip -- prefill / append attention over the paged pool.
+//
+// The last n = q_start[s+1] - q_start[s] tokens of sequence s are its
+// queries; query i sits at logical position P_i = L - n + i and attends
+// causally to logical tokens 0 .. P_i, read in place through the block
+// table (first-block offset honoured) -- the prefill of "vLLM PagedAttention
+// source notes" sec. 2.4 (the prompt's K/V written, then attended) over the
+// tables of mini-runtime ch. 12 sec. 2.2, so that a request whose prefix
+// blocks are shared attends to them without copies.  A query with P_i < 0
+// (more queries than tokens) sees nothing and gets zeros.  n = 1 is decode.
+//
+// bf16 kernel (matrix cores).  Workgroup = (kv head, sequence, tile of 16
+// queries), G wavefronts; wavefront w handles query head kv*G + w, and its
+// 16 MFMA columns are the tile's 16 queries.  Per 16-position chunk of keys:
+//   the workgroup loads the chunk's K rows (registers, then a padded LDS
+//   tile) and V rows (straight into LDS) once for all G wavefronts, three
+//   chunks in a ring so two are in flight; one barrier per chunk;
+//   every wavefront then does S^T = K . Q^T (v_mfma_f32_16x16x32_bf16),
+//   masks per element (outside the sequence, missing block, or key after
+//   the query), runs the online softmax per query column (lazy reference
+//   max, exp2 domain) and O += P . V (v_mfma_f32_16x16x16_bf16 with the
+//   transposing LDS read) -- the decode kernel's per-chunk step, with
+//   queries in place of heads.
+// fp32 kernel (VALU): one work item per (query row, group of kv heads), the
+//   decode VALU loop over the keys the query sees.
+#include "attn_common.h"
+
+namespace pkv {
+
+namespace {
+
+// Table entries covering flat positions [lo, hi) into bt_s (entry jb0
+// first); ids outside the pool or past the table become -1.  Whole
+// workgroup; ends with a barrier.
+__device__ __forceinline__ int64_t stage_entries(const PrefillArgs &a, int seq, int64_t lo,
+                                                 int64_t hi, int32_t *bt_s) {
+    const int lbs = a.pool.lbs;
+    const int64_t jb0 = lo >> lbs;
+    const int nbt = hi > lo ? (int)(((hi - 1) >> lbs) - jb0 + 1) : 0;
+    for (int i = threadIdx.x; i < nbt; i += blockDim.x) {
+        const int64_t j = jb0 + i;
+        int32_t b = -1;
+        if (j >= 0 && j < a.bt_stride) {
+            b = a.block_tables[(int64_t)seq * a.bt_stride + j];
+            if (b < 0 || b >= a.pool.num_blocks) b = -1;
+        }
+        bt_s[i] = b;
+    }
+    __syncthreads();
+    return jb0;
+}
+
+}  // namespace
+
+template <int D, int G, bool UB>
+__global__ __launch_bounds__(64 * G) void prefill_mfma_kernel(PrefillArgs a) {
+    using S = MfmaShape<D>;
+    constexpr int ROWB = S::ROWB, PPR = S::PPR, NP = S::NP, KS = S::KS, NV = S::NV;
+    constexpr int VSLAB = S::VSLAB, VTILE = S::VTILE, KROW = S::KROW, KTILE = S::KTILE;
+    constexpr int NB = 3;                       // chunks in the LDS ring
+    constexpr int LPW = (NP + G - 1) / G;       // tile-load instructions per loading wave
+    constexpr float kLazy = 8.0f;
+    __shared__ int32_t bt_s[kBtLds];
+    __shared__ __attribute__((aligned(16))) char ktile[NB][KTILE];
+    __shared__ __attribute__((aligned(16))) char vtile[NB][VTILE];
+
+    // (kv head, sequence, tile), tile fastest; neighbours share an XCD so
+    // the tiles of one sequence reuse its K/V in one L2
+    const int nwg = gridDim.x;
+    const int bid = blockIdx.x;
+    const int xcd = bid & 7;
+    const int lid = xcd * (nwg >> 3) + min(xcd, nwg & 7) + (bid >> 3);
+    const int tile = lid % a.q_tiles;
+    const int rest = lid / a.q_tiles;
+    const int seq = rest % a.num_seqs;
+    const int hk = rest / a.num_seqs;
+    const int64_t row0 = a.q_start[seq];
+    const int64_t n = (int64_t)a.q_start[seq + 1] - row0;
+    const int q0 = 16 * tile;
+    if (q0 >= n) return;  // uniform
+    const int nq = (int)min((int64_t)16, n - q0);
+    const int64_t L = a.seq_lens[seq];
+    const int64_t off = a.offsets[seq];
+    const int64_t pmax = L - n + q0 + nq - 1;   // last query's position
+
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int cn = lane & 15;   // MFMA column: query q0 + cn / output column
+    const int g4 = lane >> 4;
+    const int hq = hk * G + w;
+    const int64_t qpos = cn < nq ? L - n + q0 + cn : -1;   // this column's query position
+
+    // Q^T fragments: column cn = query q0 + cn of head hq
+    u32x4 qf[KS];
+    {
+        const char *qp = a.q + ((row0 + q0 + cn) * a.num_q_heads + hq) * (int64_t)(D * 2) + 16 * g4;
+#pragma unroll
+        for (int j = 0; j < KS; ++j) qf[j] = cn < nq ? ld16(qp + 64 * j) : u32x4{0, 0, 0, 0};
+    }
+    float m_h = kNegInf, l_h = 0.0f;
+    f32x4 acc[NV];
+#pragma unroll
+    for (int sl = 0; sl < NV; ++sl) acc[sl] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    const int lbs = a.pool.lbs;
+    const int64_t bsm = (1ll << lbs) - 1;
+    const int64_t row_bytes = a.pool.row_bytes;
+    const float sl2 = a.scale_log2;
+    const char *kh = a.pool.k + a.pool.layer_off + (int64_t)hk * ROWB;
+    const char *vh = a.pool.v + a.pool.layer_off + (int64_t)hk * ROWB;
+    const int trow = lane / PPR;
+    const int tpp = lane % PPR;
+    const bool loader = w < NP;   // waves past NP load nothing (G > NP)
+
+    if (pmax >= 0) {
+        // keys: logical 0 .. pmax = flat [off, off + pmax + 1), staged in pieces
+        const int64_t klo = off, khi = off + pmax + 1;
+        for (int64_t plo = klo & ~int64_t(15); plo < khi; plo += 16ll * a.seg_chunks) {
+            const int64_t phi = min(khi, plo + 16ll * a.seg_chunks);
+            const int64_t lo = max(plo, klo);
+            __syncthreads();  // the previous piece's entries and tiles are done with
+            const int64_t jb0 = stage_entries(a, seq, lo, phi, bt_s);
+            const int64_t first = lo & ~int64_t(15);
+            const int64_t last = (phi - 1) & ~int64_t(15);
+
+            // this wave's share of a chunk's loads: instructions i = w, w+G, ..
+            auto load_chunk = [&](int64_t pc, u32x4 *kx, int slot) {
+                if (!loader) return;
+                char *dst = vtile[slot];
+#pragma unroll
+                for (int k = 0; k < LPW; ++k) {
+                    const int i = w + G * k;
+                    if (i < NP) {
+                        const int64_t p = pc + i + NP * trow;
+                        int32_t b;
+                        if constexpr (UB) {
+                            b = bt_s[(int)((pc >> lbs) - jb0)];
+                        } else {
+                            const bool in = p >= lo && p < phi;
+                            b = in ? bt_s[(int)((p >> lbs) - jb0)] : -1;
+                        }
+                        const int64_t o = (int64_t)(b >= 0 ? b : 0) * a.pool.block_stride + (p & bsm) * row_bytes +
+                                          16 * tpp;
+                        kx[k] = ld16(kh + o);
+                        lds_copy16(vh + o, dst + i * VSLAB);
+                    }
+                }
+            };
+            // rows of chunk pc that hold a token of the sequence
+            auto row_ok = [&](int64_t pc, int row) -> bool {
+                const int64_t p = pc + row;
+                if (p < lo || p >= phi) return false;
+                return bt_s[(int)((p >> lbs) - jb0)] >= 0;
+            };
+
+            u32x4 kring[NB][LPW];
+#pragma unroll
+            for (int q = 0; q < NB - 1; ++q) load_chunk(min(first + 16 * q, last), kring[q], q);
+            bool done = false;
+            for (int64_t pc = first; !done;) {
+#pragma unroll
+                for (int q = 0; q < NB; ++q) {
+                    if (!done) {
+                        // chunk pc's loads done (the next chunk's stay in flight)
+                        if (loader) {
+                            constexpr int ahead = 2 * LPW;
+                            __builtin_amdgcn_s_waitcnt((ahead & 15) | ((ahead >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+                        }
+                        wave_lds_order();
+                        if (loader) {
+#pragma unroll
+                            for (int k = 0; k < LPW; ++k) {
+                                const int i = w + G * k;
+                                if (i < NP) {
+                                    *reinterpret_cast<u32x4 *>(ktile[q] + (i + NP * trow) * KROW + 16 * tpp) =
+                                        kring[q][k];
+                                    if (!row_ok(pc, i + NP * trow))
+                                        *reinterpret_cast<u32x4 *>(vtile[q] + i * VSLAB + 16 * lane) =
+                                            u32x4{0, 0, 0, 0};
+                                }
+                            }
+                        }
+                        __syncthreads();  // chunk pc's tiles complete; slot (q+2)%NB free
+                        const int nq2 = (q + NB - 1) % NB;
+                        load_chunk(min(pc + 16 * (NB - 1), last), kring[nq2], nq2);
+
+                        // S^T: lane holds S[token 4*g4 + i][query cn]
+                        const char *kt = ktile[q];
+                        const char *vt = vtile[q];
+                        f32x4 sacc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                        for (int j = 0; j < KS; ++j) {
+                            const u32x4 kf = *reinterpret_cast<const u32x4 *>(kt + cn * KROW + 16 * g4 + 64 * j);
+                            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf), as_bf16x8(qf[j]), sacc, 0,
+                                                                           0, 0);
+                        }
+                        float s[4];
+                        float cm = kNegInf;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int row = 4 * g4 + i;
+                            const bool live = row_ok(pc, row) && pc + row - off <= qpos;
+                            s[i] = live ? sacc[i] * sl2 : kNegInf;
+                            cm = fmaxf(cm, s[i]);
+                        }
+                        cm = fmaxf(cm, __shfl_xor(cm, 16));
+                        cm = fmaxf(cm, __shfl_xor(cm, 32));
+                        float alpha = 1.0f;
+                        if (cm > m_h + kLazy) {
+                            alpha = m_h == kNegInf ? 0.0f : fast_exp2(m_h - cm);
+                            m_h = cm;
+                        }
+                        float pr[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) pr[i] = s[i] == kNegInf ? 0.0f : fast_exp2(s[i] - m_h);
+                        const uint32_t p01 = f32_to_bf16_bits(pr[0]) | (f32_to_bf16_bits(pr[1]) << 16);
+                        const uint32_t p23 = f32_to_bf16_bits(pr[2]) | (f32_to_bf16_bits(pr[3]) << 16);
+                        l_h = fmaf(l_h, alpha, (bf16_lo(p01) + bf16_hi(p01)) + (bf16_lo(p23) + bf16_hi(p23)));
+                        if (__any(alpha != 1.0f)) {
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                const float al = __shfl(alpha, 4 * g4 + i);
+#pragma unroll
+                                for (int sl = 0; sl < NV; ++sl) acc[sl][i] *= al;
+                            }
+                        }
+                        typedef short s16x4 __attribute__((ext_vector_type(4)));
+                        const s16x4 pa = __builtin_bit_cast(s16x4, (uint64_t)p01 | ((uint64_t)p23 << 32));
+                        const int vrow = 4 * g4 + (cn >> 2);
+                        const int vbase = (vrow % NP) * VSLAB + (vrow / NP) * ROWB + 8 * (cn & 3);
+#pragma unroll
+                        for (int sl = 0; sl < NV; ++sl) {
+                            const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                (__attribute__((address_space(3))) s16x4 *)((__attribute__((address_space(3))) char *)(
+                                                                               const_cast<char *>(vt)) +
+                                                                           vbase + 32 * sl));
+                            acc[sl] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, acc[sl], 0, 0, 0);
+                        }
+                        pc += 16;
+                        done = pc > last;
+                    }
+                }
+            }
+            // drain the copies before the tiles are restaged or released
+            __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xF << 8));
+        }
+    }
+
+    // out[row, hq, :] = acc / l for the tile's queries (rows 4*g4 + i)
+    l_h += __shfl_xor(l_h, 16);
+    l_h += __shfl_xor(l_h, 32);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int qi = 4 * g4 + i;
+        const float lq = __shfl(l_h, qi);
+        if (qi < nq) {
+            uint16_t *o = reinterpret_cast<uint16_t *>(a.out) + ((row0 + q0 + qi) * a.num_q_heads + hq) * D + cn;
+#pragma unroll
+            for (int sl = 0; sl < NV; ++sl)
+                o[16 * sl] = (uint16_t)f32_to_bf16_bits(lq > 0.0f ? acc[sl][i] / lq : 0.0f);
+        }
+    }
+}
+
+// fp32 pools: one workgroup per (query row, group of heads_per_wg kv heads);
+// wavefront = one kv head with its G query heads, the decode VALU loop over
+// the keys the query sees.
+template <int DT, int D, int G>
+__global__ __launch_bounds__(256) void prefill_valu_kernel(PrefillArgs a) {
+    constexpr int E = Elem<DT>::kBytes;
+    constexpr int VEC = 16 / E;
+    constexpr int LPR = D / VEC;
+    constexpr int RPI = 64 / LPR;
+    constexpr int NP = kChunkTokens / RPI;
+    static_assert(LPR >= 4 && LPR <= 64 && RPI <= kChunkTokens, "head_dim out of range");
+    __shared__ int32_t bt_s[kBtLds];
+
+    const int64_t row = blockIdx.x / a.head_groups;
+    const int hg = blockIdx.x - (int)(row * a.head_groups);
+    // the sequence of this row: q_start[seq] <= row < q_start[seq + 1]
+    int lo = 0, hi = a.num_seqs;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (a.q_start[mid] <= row) lo = mid;
+        else hi = mid;
+    }
+    const int seq = lo;
+    const int64_t n = (int64_t)a.q_start[seq + 1] - a.q_start[seq];
+    const int64_t qi = row - a.q_start[seq];
+    const int64_t L = a.seq_lens[seq];
+    const int64_t off = a.offsets[seq];
+    const int64_t P = L - n + qi;
+
+    const int w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int h = hg * a.heads_per_wg + w;
+    const int r = lane / LPR;
+    const int c = lane % LPR;
+    const int hq0 = h * G;
+    const int lbs = a.pool.lbs;
+    const int64_t bsm = (1ll << lbs) - 1;
+
+    float m[G], l[G], acc[G][VEC];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        m[g] = kNegInf;
+        l[g] = 0.0f;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[g][e] = 0.0f;
+    }
+    u32x4 qv[G];
+    {
+        const char *qp = a.q + (row * a.num_q_heads + hq0) * (int64_t)(D * E) + c * 16;
+#pragma unroll
+        for (int g = 0; g < G; ++g) qv[g] = ld16(qp + g * (D * E));
+    }
+    const char *kb = a.pool.k + a.pool.layer_off + (int64_t)h * (D * E) + c * 16;
+    const char *vb = a.pool.v + a.pool.layer_off + (int64_t)h * (D * E) + c * 16;
+
+    const int64_t klo = off, khi = P >= 0 ? off + P + 1 : off;
+    for (int64_t plo = klo; plo < khi; plo += 16ll * a.seg_chunks) {
+        const int64_t phi = min(khi, plo + 16ll * a.seg_chunks);
+        __syncthreads();
+        const int64_t jb0 = stage_entries(a, seq, plo, phi, bt_s);
+        for (int64_t pc = plo; pc < phi; pc += kChunkTokens) {
+            u32x4 kx[NP], vx[NP];
+            bool ok[NP];
+#pragma unroll
+            for (int i = 0; i < NP; ++i) {
+                const int64_t p = pc + i * RPI + r;
+                ok[i] = false;
+                kx[i] = u32x4{0, 0, 0, 0};
+                vx[i] = u32x4{0, 0, 0, 0};
+                if (p < phi) {
+                    const int32_t b = bt_s[(int)((p >> lbs) - jb0)];
+                    if (b >= 0) {
+                        ok[i] = true;
+                        const int64_t o = (int64_t)b * a.pool.block_stride + (p & bsm) * a.pool.row_bytes;
+                        kx[i] = ld16(kb + o);
+                        vx[i] = ld16(vb + o);
+                    }
+                }
+            }
+            float s[NP][G];
+#pragma unroll
+            for (int i = 0; i < NP; ++i) {
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    const float d = row_allsum<LPR>(dot16<DT>(qv[g], kx[i]));
+                    s[i][g] = ok[i] ? d * a.scale_log2 : kNegInf;
+                }
+            }
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                float cm = s[0][g];
+#pragma unroll
+                for (int i = 1; i < NP; ++i) cm = fmaxf(cm, s[i][g]);
+                cm = cross_rows_max<LPR>(cm);
+                const float mn = fmaxf(m[g], cm);
+                const float alpha = mn == kNegInf ? 1.0f : fast_exp2(m[g] - mn);
+                float ps = 0.0f;
+                float p[NP];
+#pragma unroll
+                for (int i = 0; i < NP; ++i) {
+                    p[i] = s[i][g] == kNegInf ? 0.0f : fast_exp2(s[i][g] - mn);
+                    ps += p[i];
+                }
+                l[g] = fmaf(l[g], alpha, ps);
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) acc[g][e] *= alpha;
+                m[g] = mn;
+#pragma unroll
+                for (int i = 0; i < NP; ++i) {
+                    float vf[VEC];
+                    unpack16<DT>(vx[i], vf);
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) acc[g][e] = fmaf(p[i], vf[e], acc[g][e]);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        l[g] = cross_rows_sum<LPR>(l[g]);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[g][e] = cross_rows_sum<LPR>(acc[g][e]);
+    }
+    if (r != 0) return;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        float o[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) o[e] = l[g] > 0.0f ? acc[g][e] / l[g] : 0.0f;
+        store16<DT>(a.out + ((row * a.num_q_heads + hq0 + g) * D + c * VEC) * E, o);
+    }
+}
+
+namespace {
+
+template <int DT, int D, int G>
+hipError_t run_prefill(const PrefillArgs &a, hipStream_t s) {
+    if constexpr (DT == 1) {
+        const int64_t nwg = (int64_t)a.q_tiles * a.num_seqs * a.num_kv_heads;
+        if (a.pool.lbs >= 4)
+            hipLaunchKernelGGL((prefill_mfma_kernel<D, G, true>), dim3((unsigned)nwg), dim3(64 * G), 0, s, a);
+        else
+            hipLaunchKernelGGL((prefill_mfma_kernel<D, G, false>), dim3((unsigned)nwg), dim3(64 * G), 0, s, a);
+    } else {
+        const int64_t nwg = (int64_t)a.num_q_rows * a.head_groups;
+        hipLaunchKernelGGL((prefill_valu_kernel<DT, D, G>), dim3((unsigned)nwg), dim3(64 * a.heads_per_wg), 0, s,
+                           a);
+    }
+    return hipGetLastError();
+}
+
+typedef hipError_t (*PrefillFn)(const PrefillArgs &, hipStream_t);
+
+template <int DT, int D>
+PrefillFn pick_group(int group) {
+    switch (group) {
+        case 1: return run_prefill<DT, D, 1>;
+        case 2: return run_prefill<DT, D, 2>;
+        case 4: return run_prefill<DT, D, 4>;
+        case 8: return run_prefill<DT, D, 8>;
+        default: return nullptr;
+    }
+}
+
+PrefillFn pick(int dtype, int head_dim, int group) {
+    if (dtype != 0 && dtype != 1) return nullptr;
+    if (head_dim == 64) return dtype ? pick_group<1, 64>(group) : pick_group<0, 64>(group);
+    if (head_dim == 128) return dtype ? pick_group<1, 128>(group) : pick_group<0, 128>(group);
+    return nullptr;
+}
+
+}  // namespace
+
+bool prefill_supported(int dtype, int head_dim, int group) { return pick(dtype, head_dim, group) != nullptr; }
+
+hipError_t launch_prefill(const PrefillArgs &a, int dtype, int head_dim, int group, hipStream_t s) {
+    PrefillFn f = pick(dtype, head_dim, group);
+    if (!f) return hipErrorInvalidValue;
+    return f(a, s);
+}
+
+}  // namespace pkv

@@ -466,6 +466,50 @@ PKV_API int paged_attn_decode(const pkv_pool *pool, int32_t layer, const void *q
                                    static_cast<hipStream_t>(stream)));
 }
 
+PKV_API int paged_attn_prefill(const pkv_pool *pool, int32_t layer, const void *q,
+                               int32_t num_q_heads, const int32_t *q_start, int32_t num_q_rows,
+                               int32_t max_q_len, const int32_t *block_tables, int32_t bt_stride,
+                               const int32_t *seq_lens, const int32_t *offsets, int32_t num_seqs,
+                               float scale, void *out, void *stream) {
+    int st = check_pool(pool, true);
+    if (st) return st;
+    if (layer < 0 || layer >= pool->num_layers) return PKV_ERR_LAYER;
+    if (num_seqs < 0 || num_q_rows < 0 || max_q_len < 0 || bt_stride < 0 || num_q_heads <= 0 ||
+        num_q_heads % pool->num_kv_heads != 0)
+        return PKV_ERR_SHAPE;
+    const int group = (int)(num_q_heads / pool->num_kv_heads);
+    if (!prefill_supported(pool->dtype, (int)pool->head_dim, group)) return PKV_ERR_UNSUPPORTED;
+    if (num_seqs == 0 || num_q_rows == 0) return PKV_OK;
+    if (!q || !out || !q_start || !seq_lens || !offsets || !block_tables) return PKV_ERR_NULL;
+    if (!aligned16(q) || !aligned16(out)) return PKV_ERR_ALIGN;
+    const int64_t hkv = pool->num_kv_heads;
+    const int64_t hpw = heads_per_wg(hkv);
+    const int64_t q_tiles = ((int64_t)max_q_len + 15) / 16;
+    if (q_tiles * num_seqs * hkv > INT32_MAX || (int64_t)num_q_rows * (hkv / hpw) > INT32_MAX)
+        return PKV_ERR_SHAPE;
+    if (q_tiles == 0) return PKV_OK;
+    PrefillArgs a{};
+    a.pool = make_view(pool, layer);
+    a.q = static_cast<const char *>(q);
+    a.q_start = q_start;
+    a.block_tables = block_tables;
+    a.seq_lens = seq_lens;
+    a.offsets = offsets;
+    a.out = static_cast<char *>(out);
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.bt_stride = bt_stride;
+    a.num_seqs = num_seqs;
+    a.num_kv_heads = (int32_t)hkv;
+    a.num_q_heads = num_q_heads;
+    a.num_q_rows = num_q_rows;
+    a.q_tiles = (int32_t)q_tiles;
+    a.heads_per_wg = (int32_t)hpw;
+    a.head_groups = (int32_t)(hkv / hpw);
+    a.seg_chunks = (int32_t)(max_split_tokens(pool->block_size) / kChunkTokens);
+    return status_of(launch_prefill(a, pool->dtype, (int)pool->head_dim, group,
+                                    static_cast<hipStream_t>(stream)));
+}
+
 PKV_API int kv_validate(const pkv_pool *pool, const int32_t *block_tables, int32_t bt_stride,
                         const int32_t *seq_lens, const int32_t *offsets, int32_t num_seqs,
                         int32_t max_seq_len, const int64_t *slot_mapping, int64_t num_tokens,

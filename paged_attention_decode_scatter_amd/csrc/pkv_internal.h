@@ -115,6 +115,28 @@ struct DecodeArgs {
 // this a separate, wider merge kernel is faster.
 constexpr int kFusedMergeMaxSplits = 16;
 
+// Prefill / append attention: the last n_s = q_start[s+1] - q_start[s]
+// tokens of sequence s are its queries (rows q_start[s].. of q and out).
+struct PrefillArgs {
+    PoolView pool;
+    const char *q;
+    const int32_t *q_start;
+    const int32_t *block_tables;
+    const int32_t *seq_lens;
+    const int32_t *offsets;
+    char *out;
+    float scale_log2;
+    int32_t bt_stride;
+    int32_t num_seqs;
+    int32_t num_kv_heads;
+    int32_t num_q_heads;
+    int32_t num_q_rows;
+    int32_t q_tiles;       // 16-query tiles per sequence in the grid
+    int32_t heads_per_wg;  // fp32 kernel: kv heads per workgroup
+    int32_t head_groups;
+    int32_t seg_chunks;    // most 16-position chunks staged at once
+};
+
 struct ValidateArgs {
     const int32_t *block_tables;
     const int32_t *seq_lens;
@@ -133,6 +155,8 @@ struct ValidateArgs {
 hipError_t launch_slot_mapping(const SlotArgs &a, hipStream_t s);
 hipError_t launch_scatter(const ScatterArgs &a, hipStream_t s);
 hipError_t launch_append(const AppendArgs &a, hipStream_t s);
+bool prefill_supported(int dtype, int head_dim, int group);
+hipError_t launch_prefill(const PrefillArgs &a, int dtype, int head_dim, int group, hipStream_t s);
 hipError_t launch_gather(const GatherArgs &a, hipStream_t s);
 hipError_t launch_validate(const ValidateArgs &a, hipStream_t s);
 // Returns hipErrorInvalidValue when (dtype, head_dim, group) is not built.

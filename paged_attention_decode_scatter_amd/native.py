@@ -29,6 +29,7 @@ SYMBOLS = (
     "paged_attn_decode_schedule",
     "paged_attn_decode_workspace_size",
     "paged_attn_decode",
+    "paged_attn_prefill",
     "kv_validate",
     "pkv_status_string",
 )
@@ -87,6 +88,8 @@ def load_library(path: str = LIB_PATH):
     lib.paged_attn_decode_split_tokens.argtypes = [i32, i32, i32, i32]
     lib.paged_attn_decode_schedule.restype = i32
     lib.paged_attn_decode_schedule.argtypes = [i32] * 8
+    lib.paged_attn_prefill.restype = ctypes.c_int
+    lib.paged_attn_prefill.argtypes = [pp, i32, p, i32, p, i32, i32, p, i32, p, p, i32, f32, p, p]
     lib.paged_attn_decode_workspace_size.restype = sz
     lib.paged_attn_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
     lib.paged_attn_decode.restype = ctypes.c_int
@@ -267,6 +270,28 @@ def paged_attn_decode(k_pool, v_pool, layer, q, block_tables, seq_lens, offsets,
         _ptr(seq_lens), _ptr(offsets), num_seqs, int(max_seq_len), float(scale), split_tokens,
         _ptr(out), _ptr(workspace), ws_bytes, _stream(q))
     _check("paged_attn_decode", st)
+    return out
+
+
+def paged_attn_prefill(k_pool, v_pool, layer, q, q_start, block_tables, seq_lens, offsets,
+                       max_q_len, scale, out=None):
+    """Causal attention of each sequence's last n_s = q_start[s+1] - q_start[s]
+    tokens (rows q_start[s].. of q) over its cached tokens, read in place
+    through the block tables."""
+    pool = make_pool(k_pool, v_pool)
+    _need(q, k_pool.dtype, "q")
+    for t, n in ((q_start, "q_start"), (block_tables, "block_tables"), (seq_lens, "seq_lens"),
+                 (offsets, "offsets")):
+        _need(t, torch.int32, n)
+    rows, hq, d = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, k_pool.dtype, "out")
+    st = load_library().paged_attn_prefill(
+        ctypes.byref(pool), layer, _ptr(q), hq, _ptr(q_start), rows, int(max_q_len),
+        _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), _ptr(offsets),
+        seq_lens.shape[0], float(scale), _ptr(out), _stream(q))
+    _check("paged_attn_prefill", st)
     return out
 
 

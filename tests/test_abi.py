@@ -33,7 +33,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == len(set(names)) == 26
+    assert len(names) == len(set(names)) == 27
     assert set(names) == set(N.SYMBOLS) | set(N.BM_SYMBOLS)
     for n in names:
         assert hasattr(lib, n), n
@@ -188,6 +188,27 @@ def test_append_argument_checks(lib):
     assert call(p=pool(bs=6)) == SHAPE
     assert call(p=pool(dtype=5)) == DTYPE
     assert call(p=pool(v=0)) == NULL       # V rows given but no V pool
+
+
+def test_prefill_argument_checks(lib):
+    f = lib.paged_attn_prefill
+    by = ctypes.byref
+
+    def call(p=None, layer=0, q=A, hq=32, qs=A, rows=64, mq=16, bt=A, stride=8, sl=A, off=A, ns=4,
+             out=A):
+        return f(by(p or pool()), layer, q, hq, qs, rows, mq, bt, stride, sl, off, ns, 0.1, out, None)
+
+    assert call(layer=2) == LAYER
+    assert call(hq=30) == SHAPE
+    assert call(rows=-1) == SHAPE
+    assert call(mq=-1) == SHAPE
+    assert call(p=pool(d=96)) == UNSUP
+    assert call(hq=8 * 16) == UNSUP          # G = 16
+    assert call(ns=0) == OK
+    assert call(rows=0) == OK
+    assert call(q=None) == NULL
+    assert call(qs=None) == NULL
+    assert call(out=A + 2) == ALIGN
 
 
 def test_decode_schedule_choice(lib):
