@@ -58,9 +58,13 @@
 namespace pkv {
 
 
-// (sequence, split, head group) of this workgroup.  Workgroups are dealt
-// round-robin to the 8 XCDs; renumber them so that consecutive logical
-// items share an XCD.  Logical order: head group, split, sequence.
+// (sequence, split, head group) of this workgroup.  Logical order: split
+// slowest, then head group, then sequence, so the splits that exist only
+// for long sequences (most of them empty) are dispatched last.  Workgroups
+// are dealt round-robin to the 8 XCDs (XCD = blockIdx % 8); within each
+// aligned group of 8 logical items the XCD is rotated by the group's
+// (split, head group) index, so the splits of one sequence land on
+// different XCDs and every XCD gets a like share of the live work.
 struct Item {
     int seq, split, hg;
 };
@@ -68,14 +72,14 @@ struct Item {
 __device__ __forceinline__ Item work_item(const DecodeArgs &a) {
     const int nwg = gridDim.x;
     const int bid = blockIdx.x;
-    const int xcd = bid & 7;
-    const int per = nwg >> 3, rem = nwg & 7;
-    const int lid = xcd * per + min(xcd, rem) + (bid >> 3);
+    const int row = bid & ~7;
+    int lid = bid;
+    if (row + 8 <= nwg) lid = row | ((bid - row / a.num_seqs) & 7);
     Item it;
     it.seq = lid % a.num_seqs;
     const int rest = lid / a.num_seqs;
-    it.split = rest % a.max_splits;
-    it.hg = rest / a.max_splits;
+    it.hg = rest % a.head_groups;
+    it.split = rest / a.head_groups;
     return it;
 }
 
@@ -173,75 +177,115 @@ __device__ void zero_outputs(const DecodeArgs &a, int seq, int hg) {
 // ml + (slot(i) * hstride + g) * 2 and its acc row at
 // acc + (slot(i) * hstride + g) * D.  One wavefront; lane covers D/64
 // consecutive output elements.  Records are summed in index order, so the
-// result does not depend on which workgroup runs the merge.
+// result does not depend on which workgroup runs the merge.  Up to 64
+// records, the (m, l) pairs (lane i: record i) and the first RB records'
+// acc rows are loaded together, so the merge costs one memory round trip
+// per RB records.
 template <int DT, int D, int G, typename Slot>
 __device__ void merge_records(char *out_row0, const float *ml, const float *accb, int64_t hstride,
                               int n, Slot slot) {
     constexpr int E = Elem<DT>::kBytes;
     constexpr int PL = D / 64;
+    // acc records per batch: 64 values per lane, so the merge needs no more
+    // registers than the attention loop (occupancy stays at 2 waves/SIMD)
+    constexpr int RB = (64 / (G * PL)) < 16 ? (64 / (G * PL) > 0 ? 64 / (G * PL) : 1) : 16;
     static_assert(PL == 1 || PL == 2, "head_dim");
     const int lane = threadIdx.x & 63;
+    const float *acc = accb + lane * PL;
 
-    float M[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) M[g] = kNegInf;
-    for (int i = lane; i < n; i += 64) {
-        const int64_t r = slot(i) * hstride;
-#pragma unroll
-        for (int g = 0; g < G; ++g) M[g] = fmaxf(M[g], ld_dev(ml + (r + g) * 2));
-    }
-#pragma unroll
-    for (int g = 0; g < G; ++g) M[g] = wave_max(M[g]);
-
-    float den[G], o[G][PL];
+    float M[G], w[G], den[G], o[G][PL];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
+        M[g] = kNegInf;
         den[g] = 0.0f;
 #pragma unroll
         for (int e = 0; e < PL; ++e) o[g][e] = 0.0f;
     }
-    const float *acc = accb + lane * PL;
-    for (int ic = 0; ic < n; ic += 64) {
-        const int i = ic + lane;
-        float w[G];
+    // acc rows of records b .. b+RB-1 (none past the last record)
+    auto load_batch = [&](int b, float (&x)[RB][G][PL]) {
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            w[g] = 0.0f;
-            if (i < n) {
-                const float2 v = ld_dev2(ml + (slot(i) * hstride + g) * 2);
-                if (v.x != kNegInf) w[g] = fast_exp2(v.x - M[g]);
-                den[g] = fmaf(v.y, w[g], den[g]);
+        for (int k = 0; k < RB; ++k) {
+            const float *src = acc + slot(min(b + k, n - 1)) * hstride * D;
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                if (b + k >= n) {
+#pragma unroll
+                    for (int e = 0; e < PL; ++e) x[k][g][e] = 0.0f;
+                } else if constexpr (PL == 2) {
+                    const float2 t = ld_dev2(src + g * D);
+                    x[k][g][0] = t.x;
+                    x[k][g][1] = t.y;
+                } else {
+                    x[k][g][0] = ld_dev(src + g * D);
+                }
             }
         }
-        // four records per step so their loads are in flight together; the
-        // steps past the last record repeat it with weight 0
-        const int nu = min(64, n - ic);
-        for (int u0 = 0; u0 < nu; u0 += 4) {
-            float x[4][G][PL], wu[4][G];
+    };
+    auto add_batch = [&](int b, const float (&x)[RB][G][PL], const float (&wl)[G]) {
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int u = min(u0 + k, nu - 1);
-                const float *src = acc + slot(ic + u) * hstride * D;
+        for (int k = 0; k < RB; ++k) {
 #pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    wu[k][g] = u0 + k < nu ? lane_value(w[g], u) : 0.0f;
-                    if constexpr (PL == 2) {
-                        const float2 t = ld_dev2(src + g * D);
-                        x[k][g][0] = t.x;
-                        x[k][g][1] = t.y;
-                    } else {
-                        x[k][g][0] = ld_dev(src + g * D);
-                    }
+            for (int g = 0; g < G; ++g) {
+                // weight of record b + k: lane (b + k) % 64 holds it
+                const float wk = b + k < n ? lane_value(wl[g], (b + k) & 63) : 0.0f;
+#pragma unroll
+                for (int e = 0; e < PL; ++e) o[g][e] = fmaf(wk != 0.0f ? x[k][g][e] : 0.0f, wk, o[g][e]);
+            }
+        }
+    };
+
+    if (n <= 64) {
+        float mv[G], lv[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            mv[g] = kNegInf;
+            lv[g] = 0.0f;
+        }
+        if (lane < n) {
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const float2 v = ld_dev2(ml + (slot(lane) * hstride + g) * 2);
+                mv[g] = v.x;
+                lv[g] = v.y;
+            }
+        }
+        float x[RB][G][PL];
+        load_batch(0, x);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            M[g] = wave_max(mv[g]);
+            w[g] = mv[g] != kNegInf ? fast_exp2(mv[g] - M[g]) : 0.0f;
+            den[g] = lane < n ? lv[g] * w[g] : 0.0f;
+        }
+        add_batch(0, x, w);
+        for (int b = RB; b < n; b += RB) {
+            load_batch(b, x);
+            add_batch(b, x, w);
+        }
+    } else {
+        for (int i = lane; i < n; i += 64) {
+            const int64_t r = slot(i) * hstride;
+#pragma unroll
+            for (int g = 0; g < G; ++g) M[g] = fmaxf(M[g], ld_dev(ml + (r + g) * 2));
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) M[g] = wave_max(M[g]);
+        for (int ic = 0; ic < n; ic += 64) {
+            const int i = ic + lane;
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                w[g] = 0.0f;
+                if (i < n) {
+                    const float2 v = ld_dev2(ml + (slot(i) * hstride + g) * 2);
+                    if (v.x != kNegInf) w[g] = fast_exp2(v.x - M[g]);
+                    den[g] = fmaf(v.y, w[g], den[g]);
                 }
             }
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-#pragma unroll
-                for (int g = 0; g < G; ++g) {
-#pragma unroll
-                    for (int e = 0; e < PL; ++e)
-                        o[g][e] = fmaf(wu[k][g] != 0.0f ? x[k][g][e] : 0.0f, wu[k][g], o[g][e]);
-                }
+            const int nu = min(64, n - ic);
+            float x[RB][G][PL];
+            for (int b = 0; b < nu; b += RB) {
+                load_batch(ic + b, x);
+                add_batch(ic + b, x, w);
             }
         }
     }
