@@ -5,16 +5,18 @@
 Workload: the decode batch -- 32 sequences, seq_len ~ U[128, 2048], block
 size 16, a 16384-block 32-layer bf16 pool (16 GiB each for K and V), 8 kv
 heads, head_dim 128, 32 query heads.  One step is one decode step of the
-serving loop, all on the device: the slot of every sequence's new token
-(kv_slot_mapping), the scatter of its K/V row into the pool (kv_scatter),
-and fused paged decode attention over every cached token (paged_attn_decode).
+serving loop, all on the device and in one launch (paged_attn_decode_append):
+the slot of every sequence's new token, the write of its K/V row into the
+pool, and fused paged decode attention over every cached token, the new one
+included.  The same step as two calls (kv_append, then paged_attn_decode) is
+timed too.
 Step i works on layer i % 32 with the same tables, so consecutive steps read
 disjoint memory (4.5 GB per 32-step cycle) and the 256 MB last-level cache
 cannot serve repeats.
 
 Printed: one JSON line.  `value` is decode-attention KV bytes per second of
-whole-step time.  `roofline` describes the decode call (its partial and
-merge kernels, timed together with HIP events on the launch stream).
+whole-step time.  `roofline` describes the step's one kernel (timed with HIP
+events on the launch stream, back to back).
 `cpu_baseline` times the CPU oracle on the same decode batch.  `ops` reports
 the scatter and gather rates on the prefill shape (8 x 1024 rows, 10%
 padding) for reference.
@@ -46,6 +48,13 @@ def decode_bytes(w, lens):
     offs = w.offsets.cpu().numpy().astype("int64")
     tables = int(((offs + lens.astype("int64") + w.block_size - 1) // w.block_size).sum()) * 4
     return kv, kv + qo + tables + 8 * w.num_seqs
+
+
+def append_bytes(w):
+    """Extra algorithmic bytes of the in-kernel append: each sequence's new
+    K and V rows read once and written once."""
+    row = w.num_kv_heads * w.head_dim * w.k_pool.element_size()
+    return 2 * 2 * row * int((w.seq_lens > 0).sum())
 
 
 def decode_schedule(N, w, split_req):
@@ -301,7 +310,7 @@ def pmc_target(which, reps):
         log(f"copied {reps} x 1 GiB")
         return
     N.load_library()
-    w = W.decode_batch(device=dev)
+    w = W.decode_tokens(W.decode_batch(device=dev))
     mx = w.max_seq_len
     out = torch.empty_like(w.q)
     split = 0  # the automatic schedule, as in the timed run
@@ -310,12 +319,13 @@ def pmc_target(which, reps):
         dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     for i in range(reps):
-        N.paged_attn_decode(w.k_pool, w.v_pool, i % w.num_layers, w.q, w.block_tables,
-                            w.seq_lens, w.offsets, mx, w.scale, split_tokens=split, out=out,
-                            workspace=ws)
+        N.paged_attn_decode_append(w.k_pool, w.v_pool, i % w.num_layers, w.q, w.k_new, w.v_new,
+                                   w.block_tables, w.seq_lens, w.offsets, mx, w.scale,
+                                   split_tokens=split, out=out, workspace=ws)
     torch.cuda.synchronize()
     _, alg = decode_bytes(w, w.seq_lens.cpu().numpy())
-    log(f"ran {reps} decode launches, {alg} algorithmic bytes each, split {split}")
+    log(f"ran {reps} step launches (decode with append), {alg + append_bytes(w)} algorithmic "
+        f"bytes each, split {split}")
 
 
 def main():
@@ -367,16 +377,24 @@ def main():
     dec_start = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     dec_end = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
 
-    # The step issues the three C-ABI calls with arguments marshalled once
-    # up front (same values the binding would pass), so host-side Python
-    # does not starve the ~30 us device step.
+    # The step issues its C-ABI call with arguments marshalled once up
+    # front (the values the binding would pass), so host-side Python does
+    # not starve the ~40 us device step.
     import ctypes
 
     lib = N.load_library()
     pool = N.make_pool(w.k_pool, w.v_pool)
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
     P = lambda t: ctypes.c_void_p(t.data_ptr())
-    # the new tokens' slots (a1) and their scatter (a2) in one kernel
+    # one new K/V row per sequence (all 32 have tokens), in sequence order
+    assert torch.equal(w.token_seq.cpu(), torch.arange(w.num_seqs, dtype=torch.int32))
+    # the step: the new tokens' slots and writes + decode, one launch
+    step_args = [(ctypes.byref(pool), l, P(w.q), w.num_q_heads, P(w.k_new), P(w.v_new),
+                  P(w.block_tables), w.block_tables.shape[1], P(w.seq_lens), P(w.offsets),
+                  w.num_seqs, mx, ctypes.c_float(w.scale), split, P(out), P(workspace),
+                  workspace.numel(), stream)
+                 for l in range(w.num_layers)]
+    # the same step as two calls: slots + scatter (kv_append), then decode
     app_args = [(ctypes.byref(pool), l, P(w.k_new), P(w.v_new), P(w.block_tables),
                  w.block_tables.shape[1], P(w.offsets), w.num_seqs, P(w.token_seq),
                  P(w.token_pos), w.token_seq.shape[0], P(slots), stream)
@@ -385,92 +403,116 @@ def main():
                  w.block_tables.shape[1], P(w.seq_lens), P(w.offsets), w.num_seqs, mx,
                  ctypes.c_float(w.scale), split, P(out), P(workspace), workspace.numel(), stream)
                 for l in range(w.num_layers)]
-    f_app, f_dec = lib.kv_append, lib.paged_attn_decode
+    f_step, f_app, f_dec = lib.paged_attn_decode_append, lib.kv_append, lib.paged_attn_decode
 
     def step(i, timed=False):
         layer = i % w.num_layers
-        rc = f_app(*app_args[layer])
         if timed:
             dec_start[i].record()
-        rc |= f_dec(*dec_args[layer])
+        rc = f_step(*step_args[layer])
         if timed:
             dec_end[i].record()
         if rc:
             raise RuntimeError(f"a library call failed in step {i}")
 
-    # The same step captured as one HIP graph per layer (the three calls,
-    # marshalled for the capture stream), replayed per step.
-    graphs = []
-    if not args.no_graph:
+    def two_call_step(i):
+        layer = i % w.num_layers
+        if f_app(*app_args[layer]) | f_dec(*dec_args[layer]):
+            raise RuntimeError(f"a library call failed in step {i}")
+
+    def capture(calls):
+        """One HIP graph per layer holding `calls(layer, stream)`."""
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
             for i in range(3):
-                step(i)
+                cs = ctypes.c_void_p(side.cuda_stream)
+                calls(i % w.num_layers, cs)
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
+        gs = []
         for layer in range(w.num_layers):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                cs = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
-                rc = f_app(*app_args[layer][:-1], cs)
-                rc |= f_dec(*dec_args[layer][:-1], cs)
-            if rc:
-                raise RuntimeError(f"a library call failed while capturing layer {layer}")
-            graphs.append(g)
+                calls(layer, ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream))
+            gs.append(g)
         torch.cuda.synchronize()
+        return gs
+
+    def fused_calls(layer, cs):
+        if f_step(*step_args[layer][:-1], cs):
+            raise RuntimeError(f"paged_attn_decode_append failed while capturing layer {layer}")
+
+    def two_calls(layer, cs):
+        if f_app(*app_args[layer][:-1], cs) | f_dec(*dec_args[layer][:-1], cs):
+            raise RuntimeError(f"a library call failed while capturing layer {layer}")
+
+    def time_graphs(gs):
+        for i in range(args.warmup):
+            gs[i % w.num_layers].replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(args.steps):
+            gs[i % w.num_layers].replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / args.steps
+
+    def time_eager(fn):
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(args.steps):
+            fn(i)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / args.steps
 
     log(f"warmup {args.warmup} steps (split_tokens={split}, workspace={ws_bytes} B)")
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    # The timed steps: K calls back to back on the stream (layer rotated),
+    # one event pair around all of them.
     log(f"timing {args.steps} steps")
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record()
+    ms_step = time_eager(step)
+    alg_step = alg_bytes + append_bytes(w)
+    achieved = alg_step / (ms_step * 1e-3) / 1e9
+    log(f"step {ms_step * 1e3:.1f} us ({achieved:.0f} GB/s algorithmic)")
+    # the same calls with an event pair around each (adds per-call latency)
     for i in range(args.steps):
         step(i, timed=True)
-    t_end.record()
     torch.cuda.synchronize()
-    ms_total = t_start.elapsed_time(t_end)
-    ms_step_eager = ms_total / args.steps
-    ms_step = ms_step_eager
-    if graphs:
-        for i in range(args.warmup):
-            graphs[i % w.num_layers].replay()
-        torch.cuda.synchronize()
-        g_start = torch.cuda.Event(enable_timing=True)
-        g_end = torch.cuda.Event(enable_timing=True)
-        g_start.record()
-        for i in range(args.steps):
-            graphs[i % w.num_layers].replay()
-        g_end.record()
-        torch.cuda.synchronize()
-        ms_step = g_start.elapsed_time(g_end) / args.steps
-        log(f"step as graph replay {ms_step * 1e3:.1f} us (eager calls {ms_step_eager * 1e3:.1f} us)")
     dec_ms = [s.elapsed_time(e) for s, e in zip(dec_start, dec_end)]
     dec_avg = sum(dec_ms) / len(dec_ms)
     dec_med = sorted(dec_ms)[len(dec_ms) // 2]
-    log(f"eager step {ms_step_eager * 1e3:.1f} us, decode call inside it avg {dec_avg * 1e3:.1f} us "
-        f"(median {dec_med * 1e3:.1f} us)")
+    # the step replayed as one HIP graph per layer
+    graph_ms = None if args.no_graph else time_graphs(capture(fused_calls))
+    us = lambda ms: "n/a" if ms is None else f"{ms * 1e3:.1f}"
+    log(f"per-call events avg {dec_avg * 1e3:.1f} us (median {dec_med * 1e3:.1f}); graph replay "
+        f"{us(graph_ms)} us")
 
-    # The decode kernel's own rate: the same calls back to back (layer
-    # rotated), one event pair around all of them, so per-call event and
-    # launch latency do not count against the kernel.
-    for i in range(3):
-        f_dec(*dec_args[i % w.num_layers])
+    # The same step as two calls (append kernel, then decode), for comparison.
+    two_eager = time_eager(two_call_step)
+    two_graph = None if args.no_graph else time_graphs(capture(two_calls))
+    log(f"two-call step: eager {us(two_eager)} us, graph {us(two_graph)} us")
+    dec_b2b = ms_step
     d_start = torch.cuda.Event(enable_timing=True)
     d_end = torch.cuda.Event(enable_timing=True)
+    # and decode alone (no append), the same way
+    for i in range(3):
+        f_dec(*dec_args[i % w.num_layers])
     torch.cuda.synchronize()
     d_start.record()
     for i in range(args.steps):
         f_dec(*dec_args[i % w.num_layers])
     d_end.record()
     torch.cuda.synchronize()
-    dec_b2b = d_start.elapsed_time(d_end) / args.steps
-    achieved = alg_bytes / (dec_b2b * 1e-3) / 1e9
-    log(f"decode back to back {dec_b2b * 1e3:.1f} us per call, {achieved:.0f} GB/s")
+    dec_only = d_start.elapsed_time(d_end) / args.steps
+    log(f"decode alone back to back {dec_only * 1e3:.1f} us per call")
 
     result = {
         "metric": METRIC,
@@ -498,25 +540,30 @@ def main():
             "num_q_heads": w.num_q_heads,
             "split_tokens": sched if sched > 0 else "balanced",
             "kv_bytes_per_step": kv_bytes,
-            "step": "kv_append (slot mapping + scatter of 1 new token/seq) + paged_attn_decode, "
-                    "layer rotated over 32",
-            "step_launch": "HIP graph per layer, replayed" if graphs else "eager C-ABI calls",
-            "eager_ms_per_step": ms_step_eager,
+            "step": "paged_attn_decode_append: slot + write of 1 new K/V row per sequence and "
+                    "paged decode attention in one launch, layer rotated over 32",
+            "step_launch": "one C-ABI call per step, issued back to back",
+            "graph_replay_ms_per_step": graph_ms,
+            "two_call_step": {"calls": "kv_append + paged_attn_decode",
+                              "ms_per_step": two_eager, "graph_replay_ms_per_step": two_graph},
             "parallelism": "single GPU",
         },
         "roofline": {
-            "kernel": kernel_label,
+            "kernel": kernel_label + ", with the new-token write",
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": measured_traffic(),
-            "algorithmic_bytes_per_launch": alg_bytes,
+            "algorithmic_bytes_per_launch": alg_step,
             "avg_launch_us": dec_b2b * 1e3,
-            "timing": f"HIP events around {args.steps} back-to-back decode calls on the launch stream",
-            "in_step_call_avg_us": dec_avg * 1e3,
-            "in_step_call_median_us": dec_med * 1e3,
+            "timing": f"HIP events around the {args.steps} back-to-back step calls on the launch "
+                      "stream (the timed steps themselves)",
+            "decode_alone_us": dec_only * 1e3,
+            "decode_alone_GBps": alg_bytes / (dec_only * 1e-3) / 1e9,
+            "per_call_events_avg_us": dec_avg * 1e3,
+            "per_call_events_median_us": dec_med * 1e3,
         },
     }
     if not args.no_ops:

@@ -285,6 +285,39 @@ PKV_API int paged_attn_decode(const pkv_pool *pool, int32_t layer,
                               void *stream);
 
 /*
+ * paged_attn_decode_append -- one whole decode step in one launch: each
+ * sequence's new token is written into the pool, then attended to with the
+ * rest.  For every sequence s with seq_lens[s] > 0, the new token sits at
+ * logical position seq_lens[s] - 1 (its K/V row is already counted in
+ * seq_lens): its slot is block_tables[s][(p)/block_size] * block_size +
+ * p % block_size with p = offsets[s] + seq_lens[s] - 1 [P2 sec. 2.2 slot
+ * formula; P3 sec. 2.2 offset], and
+ *   K pool [slot/bs, layer, slot%bs, :, :] = k_new[s, :, :]
+ *   V pool [slot/bs, layer, slot%bs, :, :] = v_new[s, :, :]
+ * exactly as kv_append with token_seq[s] = s, token_pos[s] = seq_lens[s]-1
+ * writes them [P1 "relation to step14_1" scatter]; out is then what
+ * paged_attn_decode computes over tokens 0 .. seq_lens[s]-1 of the updated
+ * pool.  A table entry of -1 at that position writes nothing (the
+ * position is masked, as in decode).  The write happens inside the
+ * attention kernel, by the work item whose range ends the sequence, before
+ * it reads that row; no other work item reads it.
+ *
+ *   k_new, v_new  device [num_seqs, num_kv_heads, head_dim], pool dtype,
+ *                 16-byte aligned; both required
+ *   everything else as for paged_attn_decode (same workspace size)
+ * Errors: as paged_attn_decode; PKV_ERR_NULL when k_new or v_new is NULL.
+ */
+PKV_API int paged_attn_decode_append(const pkv_pool *pool, int32_t layer,
+                                     const void *q, int32_t num_q_heads,
+                                     const void *k_new, const void *v_new,
+                                     const int32_t *block_tables, int32_t bt_stride,
+                                     const int32_t *seq_lens, const int32_t *offsets,
+                                     int32_t num_seqs, int32_t max_seq_len, float scale,
+                                     int32_t split_tokens, void *out,
+                                     void *workspace, size_t workspace_bytes,
+                                     void *stream);
+
+/*
  * paged_attn_prefill -- prefill / append attention: the queries of
  * sequence s are its last n_s = q_start[s+1] - q_start[s] cached tokens
  * (their K/V already written, e.g. by kv_append) [P2 sec. 2.4 "prefill

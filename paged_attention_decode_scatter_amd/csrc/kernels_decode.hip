@@ -390,6 +390,22 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
     const char *kb = a.pool.k + a.pool.layer_off + (int64_t)h * (D * E) + c * 16;
     const char *vb = a.pool.v + a.pool.layer_off + (int64_t)h * (D * E) + c * 16;
 
+    // Decode with append: the work item that ends the sequence first writes
+    // the new token's K/V row (logical position len - 1); each piece is
+    // stored by the lane whose load below reads it back.
+    if (a.k_new != nullptr && R.len > 0 && R.hi == R.off + R.len) {
+        const int64_t pn = R.hi - 1;
+        if (r == (int)((pn - R.lo) % kChunkTokens) % RPI) {
+            const int32_t b = bt_s[(int)((pn >> lbs) - jb0)];
+            if (b >= 0) {
+                const int64_t src = ((int64_t)seq * a.num_kv_heads + h) * (D * E) + c * 16;
+                const int64_t o = (int64_t)b * a.pool.block_stride + (pn & bsm) * a.pool.row_bytes;
+                *reinterpret_cast<u32x4 *>(const_cast<char *>(kb) + o) = ld16(a.k_new + src);
+                *reinterpret_cast<u32x4 *>(const_cast<char *>(vb) + o) = ld16(a.v_new + src);
+            }
+        }
+    }
+
     for (int64_t pc = R.lo; pc < R.hi; pc += kChunkTokens) {
         u32x4 kx[NP], vx[NP];
         bool ok[NP];
@@ -528,7 +544,7 @@ __device__ __forceinline__ void load_q(const DecodeArgs &a, int seq, int h,
 // of one sequence, accumulated into (m_h, l_h, acc): the per-chunk pipeline
 // described above.  bt_s holds the table entries from jb0 on.
 template <int D, int G, bool UB>
-__device__ __forceinline__ void attend_range(const DecodeArgs &a, const Range &R, int64_t jb0,
+__device__ __forceinline__ void attend_range(const DecodeArgs &a, int seq, const Range &R, int64_t jb0,
                                              const int32_t *bt_s, char *vring, char *kt, int h,
                                              const u32x4 (&qf)[MfmaShape<D>::KS], float &m_h,
                                              float &l_h, f32x4 (&acc)[MfmaShape<D>::NV]) {
@@ -671,9 +687,36 @@ __device__ __forceinline__ void attend_range(const DecodeArgs &a, const Range &R
     const int64_t first = R.lo & ~int64_t(15);
     if (first < R.hi) {
         const int64_t last = (R.hi - 1) & ~int64_t(15);
+        // Decode with append: the range that ends the sequence first writes
+        // the new token's K/V row (logical position len - 1, in chunk
+        // `last`) into the pool.  Each 16-byte piece is stored by the lane
+        // whose ring load reads it back, before that load in program order,
+        // so the load sees it.  The new rows are fetched before the ring's
+        // first loads; the store waits only for them, and goes after the
+        // first loads unless those already cover chunk `last`.
+        const bool app = a.k_new != nullptr && R.len > 0 && R.hi == R.off + R.len;
+        const int64_t pn = R.hi - 1;
+        const bool app_lane = app && trow == (int)(pn & 15) / NP;
+        u32x4 kn = {0, 0, 0, 0}, vn = {0, 0, 0, 0};
+        if (app_lane) {
+            const int64_t src = ((int64_t)seq * a.num_kv_heads + h) * ROWB + 16 * tpp;
+            kn = ld16(a.k_new + src);
+            vn = ld16(a.v_new + src);
+        }
+        auto store_new = [&]() {
+            if (!app_lane) return;
+            const int32_t b = bt_s[(int)((pn >> lbs) - jb0)];
+            if (b < 0) return;  // no block at that position: nothing to write (its score is masked)
+            const int64_t o = (int64_t)b * a.pool.block_stride + (pn & bsm) * row_bytes + 16 * tpp;
+            *reinterpret_cast<u32x4 *>(const_cast<char *>(kh) + o) = kn;
+            *reinterpret_cast<u32x4 *>(const_cast<char *>(vh) + o) = vn;
+        };
+        const bool store_early = last - first < 16 * (NSLOT - 1);
+        if (store_early) store_new();
         u32x4 kring[NSLOT][NP];
 #pragma unroll
         for (int q = 0; q < NSLOT - 1; ++q) load_chunk(min(first + 16 * q, last), kring[q], q);
+        if (!store_early) store_new();
         bool done = false;
         for (int64_t pc = first; !done;) {
 #pragma unroll
@@ -766,7 +809,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     f32x4 acc[S::NV];
 #pragma unroll
     for (int sl = 0; sl < S::NV; ++sl) acc[sl] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    attend_range<D, G, UB>(a, R, jb0, bt_s, vtiles[w][0], ktiles[w], h, qf, m_h, l_h, acc);
+    attend_range<D, G, UB>(a, it.seq, R, jb0, bt_s, vtiles[w][0], ktiles[w], h, qf, m_h, l_h, acc);
     float lrow[4];
     head_denominators(l_h, lrow);
     if (direct) {
@@ -923,7 +966,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeArgs a) {
             R.hi = min(16 * (f0 + ce), off + len);
             __syncthreads();  // every wave is done with the previous table entries
             const int64_t jb0 = stage_table(a, seq, R, bt_s);
-            attend_range<D, G, UB>(a, R, jb0, bt_s, vtiles[w][0], ktiles[w], h, qf, m_h, l_h, acc);
+            attend_range<D, G, UB>(a, seq, R, jb0, bt_s, vtiles[w][0], ktiles[w], h, qf, m_h, l_h, acc);
         }
         float lrow[4];
         head_denominators(l_h, lrow);

@@ -399,11 +399,16 @@ PKV_API int32_t paged_attn_decode_schedule(int32_t num_seqs, int32_t num_kv_head
     return (int32_t)p.split;
 }
 
-PKV_API int paged_attn_decode(const pkv_pool *pool, int32_t layer, const void *q,
-                              int32_t num_q_heads, const int32_t *block_tables, int32_t bt_stride,
-                              const int32_t *seq_lens, const int32_t *offsets, int32_t num_seqs,
-                              int32_t max_seq_len, float scale, int32_t split_tokens, void *out,
-                              void *workspace, size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// paged_attn_decode, and paged_attn_decode_append when k_new is given.
+int decode_impl(const pkv_pool *pool, int32_t layer, const void *q, int32_t num_q_heads,
+                const void *k_new, const void *v_new, const int32_t *block_tables, int32_t bt_stride,
+                const int32_t *seq_lens, const int32_t *offsets, int32_t num_seqs,
+                int32_t max_seq_len, float scale, int32_t split_tokens, void *out,
+                void *workspace, size_t workspace_bytes, void *stream) {
     int st = check_pool(pool, true);
     if (st) return st;
     if (layer < 0 || layer >= pool->num_layers) return PKV_ERR_LAYER;
@@ -417,6 +422,8 @@ PKV_API int paged_attn_decode(const pkv_pool *pool, int32_t layer, const void *q
     if (!q || !out || !seq_lens || !offsets || (max_seq_len > 0 && !block_tables))
         return PKV_ERR_NULL;
     if (!aligned16(q) || !aligned16(out)) return PKV_ERR_ALIGN;
+    if (k_new && !v_new) return PKV_ERR_NULL;
+    if (k_new && (!aligned16(k_new) || !aligned16(v_new))) return PKV_ERR_ALIGN;
     DecodePlan p;
     st = plan_decode(num_seqs, pool->num_kv_heads, num_q_heads, pool->head_dim, max_seq_len,
                      pool->block_size, split_tokens, &p);
@@ -444,6 +451,8 @@ PKV_API int paged_attn_decode(const pkv_pool *pool, int32_t layer, const void *q
     a.seq_lens = seq_lens;
     a.offsets = offsets;
     a.out = static_cast<char *>(out);
+    a.k_new = static_cast<const char *>(k_new);
+    a.v_new = static_cast<const char *>(v_new);
     char *ws = need > 0 ? static_cast<char *>(workspace) : nullptr;
     const int64_t cnt_bytes = balanced ? sp.cnt_bytes : p.cnt_bytes;
     const int64_t ml_bytes = balanced ? sp.ml_bytes : p.ml_bytes;
@@ -464,6 +473,33 @@ PKV_API int paged_attn_decode(const pkv_pool *pool, int32_t layer, const void *q
     a.seg_chunks = (int32_t)(max_split_tokens(pool->block_size) / kChunkTokens);
     return status_of(launch_decode(a, pool->dtype, (int)pool->head_dim, group,
                                    static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+PKV_API int paged_attn_decode(const pkv_pool *pool, int32_t layer, const void *q,
+                              int32_t num_q_heads, const int32_t *block_tables, int32_t bt_stride,
+                              const int32_t *seq_lens, const int32_t *offsets, int32_t num_seqs,
+                              int32_t max_seq_len, float scale, int32_t split_tokens, void *out,
+                              void *workspace, size_t workspace_bytes, void *stream) {
+    return decode_impl(pool, layer, q, num_q_heads, nullptr, nullptr, block_tables, bt_stride,
+                       seq_lens, offsets, num_seqs, max_seq_len, scale, split_tokens, out, workspace,
+                       workspace_bytes, stream);
+}
+
+PKV_API int paged_attn_decode_append(const pkv_pool *pool, int32_t layer, const void *q,
+                                     int32_t num_q_heads, const void *k_new, const void *v_new,
+                                     const int32_t *block_tables, int32_t bt_stride,
+                                     const int32_t *seq_lens, const int32_t *offsets,
+                                     int32_t num_seqs, int32_t max_seq_len, float scale,
+                                     int32_t split_tokens, void *out, void *workspace,
+                                     size_t workspace_bytes, void *stream) {
+    if (num_seqs > 0 && (!k_new || !v_new)) return PKV_ERR_NULL;
+    return decode_impl(pool, layer, q, num_q_heads, k_new, v_new, block_tables, bt_stride, seq_lens,
+                       offsets, num_seqs, max_seq_len, scale, split_tokens, out, workspace,
+                       workspace_bytes, stream);
 }
 
 PKV_API int paged_attn_prefill(const pkv_pool *pool, int32_t layer, const void *q,

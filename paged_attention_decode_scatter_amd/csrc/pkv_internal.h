@@ -94,6 +94,8 @@ struct DecodeArgs {
     const int32_t *seq_lens;
     const int32_t *offsets;
     char *out;
+    const char *k_new;     // decode with append: [num_seqs][num_kv_heads][head_dim] new rows
+    const char *v_new;     //   (position seq_len - 1); null for plain decode
     uint32_t *ws_cnt;      // [num_seqs][head_groups] finished splits (zero between calls)
     float *ws_ml;          // [num_seqs][max_splits][num_q_heads][2]  (m, l)
     float *ws_acc;         // [num_seqs][max_splits][num_q_heads][head_dim]

@@ -29,6 +29,7 @@ SYMBOLS = (
     "paged_attn_decode_schedule",
     "paged_attn_decode_workspace_size",
     "paged_attn_decode",
+    "paged_attn_decode_append",
     "paged_attn_prefill",
     "kv_validate",
     "pkv_status_string",
@@ -92,6 +93,9 @@ def load_library(path: str = LIB_PATH):
     lib.paged_attn_prefill.argtypes = [pp, i32, p, i32, p, i32, i32, p, i32, p, p, i32, f32, p, p]
     lib.paged_attn_decode_workspace_size.restype = sz
     lib.paged_attn_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+    lib.paged_attn_decode_append.restype = ctypes.c_int
+    lib.paged_attn_decode_append.argtypes = [pp, i32, p, i32, p, p, p, i32, p, p, i32, i32, f32,
+                                             i32, p, p, sz, p]
     lib.paged_attn_decode.restype = ctypes.c_int
     lib.paged_attn_decode.argtypes = [pp, i32, p, i32, p, i32, p, p, i32, i32, f32, i32, p, p,
                                       sz, p]
@@ -270,6 +274,37 @@ def paged_attn_decode(k_pool, v_pool, layer, q, block_tables, seq_lens, offsets,
         _ptr(seq_lens), _ptr(offsets), num_seqs, int(max_seq_len), float(scale), split_tokens,
         _ptr(out), _ptr(workspace), ws_bytes, _stream(q))
     _check("paged_attn_decode", st)
+    return out
+
+
+def paged_attn_decode_append(k_pool, v_pool, layer, q, k_new, v_new, block_tables, seq_lens,
+                             offsets, max_seq_len, scale, split_tokens=0, out=None,
+                             workspace=None):
+    """One decode step in one launch: write k_new[s]/v_new[s] at logical
+    position seq_lens[s] - 1 of each sequence, then paged_attn_decode over
+    its tokens (the new one included)."""
+    pool = make_pool(k_pool, v_pool)
+    _need(q, k_pool.dtype, "q")
+    _need(k_new, k_pool.dtype, "k_new")
+    _need(v_new, k_pool.dtype, "v_new")
+    for t, n in ((block_tables, "block_tables"), (seq_lens, "seq_lens"), (offsets, "offsets")):
+        _need(t, torch.int32, n)
+    num_seqs, hq, d = q.shape
+    if tuple(k_new.shape) != (num_seqs, k_pool.shape[3], d) or k_new.shape != v_new.shape:
+        raise ValueError("k_new/v_new must be [num_seqs, num_kv_heads, head_dim]")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, k_pool.dtype, "out")
+    need = paged_attn_decode_workspace_size(num_seqs, k_pool.shape[3], hq, d, max_seq_len,
+                                            k_pool.shape[2], split_tokens)
+    if workspace is None and need > 0:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load_library().paged_attn_decode_append(
+        ctypes.byref(pool), layer, _ptr(q), hq, _ptr(k_new), _ptr(v_new), _ptr(block_tables),
+        block_tables.shape[1], _ptr(seq_lens), _ptr(offsets), num_seqs, int(max_seq_len),
+        float(scale), split_tokens, _ptr(out), _ptr(workspace), ws_bytes, _stream(q))
+    _check("paged_attn_decode_append", st)
     return out
 
 

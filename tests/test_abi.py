@@ -33,7 +33,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == len(set(names)) == 27
+    assert len(names) == len(set(names)) == 28
     assert set(names) == set(N.SYMBOLS) | set(N.BM_SYMBOLS)
     for n in names:
         assert hasattr(lib, n), n
@@ -139,6 +139,26 @@ def test_decode_argument_checks(lib):
     assert call(split=16, ws=None, wsb=0) == WORKSPACE
     assert call(split=16, wsb=need - 1) == WORKSPACE
     assert call(split=16, ws=A + 4, wsb=need) == ALIGN
+
+
+def test_decode_append_argument_checks(lib):
+    f = lib.paged_attn_decode_append
+    by = ctypes.byref
+
+    def call(p=None, hq=32, ns=4, mx=100, split=0, q=A, kn=A, vn=A, out=A, ws=A, wsb=1 << 30,
+             layer=0):
+        return f(by(p or pool()), layer, q, hq, kn, vn, A, 8, A, A, ns, mx, 0.1, split, out, ws,
+                 wsb, None)
+
+    assert call(kn=None) == NULL
+    assert call(vn=None) == NULL
+    assert call(kn=A + 8) == ALIGN
+    assert call(vn=A + 4) == ALIGN
+    assert call(hq=24) == UNSUP
+    assert call(layer=3) == LAYER
+    assert call(split=24) == SHAPE
+    assert call(ns=0, kn=None, vn=None) == OK
+    assert call(split=16, ws=None, wsb=0) == WORKSPACE
 
 
 def test_workspace_size_and_split_choice(lib):
