@@ -94,19 +94,21 @@ int64_t max_positions(int64_t max_len, int64_t bs) { return max_len > 0 ? max_le
 
 // Automatic split (a power of two >= 64 positions), from measured decode
 // times on MI355X: grow the split while the work items (one wavefront each
-// per (sequence, kv head, split) at max_seq_len) exceed 20 per compute unit,
-// and keep growing it up to 256 positions while that still leaves at least
-// 2 items per compute unit (shorter splits cost more per token in pipeline
-// start-up and partials than they gain in balance).
+// per (sequence, kv head, split) of max_seq_len tokens) exceed 8 per compute
+// unit -- two resident workgroups of four -- and keep growing it up to 256
+// positions while that still leaves at least 2 items per compute unit
+// (shorter splits cost more per token in pipeline start-up and partials
+// than they gain in balance).  On the decode batch (32 x <= 2048 tokens)
+// this picks 256; on 8 x 32768 tokens, 1024.
 int64_t auto_split(int64_t num_seqs, int64_t hkv, int64_t max_len, int64_t bs) {
     const int64_t cus = cu_count();
     const int64_t smax = max_split_tokens(bs);
     const int64_t span = max_positions(max_len, bs);
-    auto items = [&](int64_t s) { return num_seqs * hkv * ((span + s - 1) / s); };
+    auto items = [&](int64_t s) { return num_seqs * hkv * ((max_len + s - 1) / s); };
     auto splits = [&](int64_t s) { return (span + s - 1) / s; };
     int64_t s = 64;
     if (s > smax) s = smax;
-    while (s * 2 <= smax && (items(s) > 20 * cus || splits(s) > kMaxSplits ||
+    while (s * 2 <= smax && (items(s) > 8 * cus || splits(s) > kMaxSplits ||
                              (s < 256 && items(s * 2) >= 2 * cus)))
         s *= 2;
     return s;
@@ -158,25 +160,20 @@ int64_t heads_per_wg(int64_t hkv) {
 
 // Balanced decode schedule (bf16, split_tokens = 0): one resident
 // generation of workgroups (2 per compute unit; the LDS of one workgroup is
-// about 72 KiB), never more than the work units can fill, and the two
-// record slots per workgroup.  Chosen automatically for large batches:
-// measured on MI355X it beats the best split from about 0.5 GB of K/V per
-// call, and loses below (each workgroup then holds only a few chunks).
-constexpr int64_t kStreamMaxSeqs = 4096;  // each workgroup scans every length
+// about 74 KiB), never more than the work units can fill, and the two
+// record slots per workgroup.  Each workgroup reads every sequence length
+// (at most kStreamSeqsPerThread per thread) and handles its share in one
+// pass, which must fit kSegMax pairs and the LDS table buffer; past that
+// the grid grows (more than one generation) until it does.  Chosen
+// automatically for large batches of many sequences: measured on MI355X it
+// beats the automatic split from about 0.5 GB of K/V per call when the
+// lengths vary over at least 32 sequences (64 sequences sharing a prefix,
+// up to 4096 tokens), and loses to it on a few long sequences of equal
+// length (8 x 32768 tokens) and on smaller batches.
 constexpr int64_t kStreamMinBytes = 512ll << 20;
+constexpr int64_t kStreamMinSeqs = 32;
 
-bool use_balanced(int64_t num_seqs, int64_t hkv, int64_t head_dim, int64_t max_len, int32_t dtype,
-                  int64_t split_req) {
-    if (dtype != PKV_BF16 || num_seqs > kStreamMaxSeqs) return false;
-    if (split_req == PKV_SPLIT_BALANCED) return true;
-    return split_req == 0 && num_seqs * hkv * max_len * head_dim * 2 * 2 >= kStreamMinBytes;
-}
-
-// A balanced-schedule request that cannot be honoured (fp32 pool, too many
-// sequences).
-bool balanced_refused(int64_t num_seqs, int32_t dtype, int64_t split_req) {
-    return split_req == PKV_SPLIT_BALANCED && (dtype != PKV_BF16 || num_seqs > kStreamMaxSeqs);
-}
+int64_t stream_max_seqs(int64_t hkv) { return kStreamSeqsPerThread * 64 * heads_per_wg(hkv); }
 
 struct StreamPlan {
     int64_t wgs;
@@ -185,17 +182,56 @@ struct StreamPlan {
 };
 
 int plan_stream(int64_t num_seqs, int64_t hkv, int64_t hq, int64_t head_dim, int64_t max_len,
-                StreamPlan *p) {
-    if (num_seqs < 0 || hkv <= 0 || hq <= 0 || hq % hkv || head_dim <= 0 || max_len < 0)
+                int64_t bs, StreamPlan *p);
+
+// Whether the balanced schedule can run this batch: bf16, few enough
+// sequences for the length scan, and a grid that fits every share.
+bool balanced_possible(int64_t num_seqs, int64_t hkv, int64_t head_dim, int64_t max_len,
+                       int64_t bs, int32_t dtype) {
+    if (dtype != PKV_BF16 || num_seqs > stream_max_seqs(hkv)) return false;
+    StreamPlan sp;
+    return plan_stream(num_seqs, hkv, hkv, head_dim, max_len, bs, &sp) == PKV_OK;
+}
+
+bool use_balanced(int64_t num_seqs, int64_t hkv, int64_t head_dim, int64_t max_len, int64_t bs,
+                  int32_t dtype, int64_t split_req) {
+    if (!balanced_possible(num_seqs, hkv, head_dim, max_len, bs, dtype)) return false;
+    if (split_req == PKV_SPLIT_BALANCED) return true;
+    return split_req == 0 && num_seqs >= kStreamMinSeqs &&
+           num_seqs * hkv * max_len * head_dim * 2 * 2 >= kStreamMinBytes;
+}
+
+// A balanced-schedule request that cannot be honoured (fp32 pool, too many
+// sequences, a batch no grid fits).
+bool balanced_refused(int64_t num_seqs, int64_t hkv, int64_t head_dim, int64_t max_len, int64_t bs,
+                      int32_t dtype, int64_t split_req) {
+    return split_req == PKV_SPLIT_BALANCED &&
+           !balanced_possible(num_seqs, hkv, head_dim, max_len, bs, dtype);
+}
+
+int plan_stream(int64_t num_seqs, int64_t hkv, int64_t hq, int64_t head_dim, int64_t max_len,
+                int64_t bs, StreamPlan *p) {
+    if (num_seqs < 0 || hkv <= 0 || hq <= 0 || hq % hkv || head_dim <= 0 || max_len < 0 ||
+        !is_pow2(bs))
         return PKV_ERR_SHAPE;
     const int64_t hpw = heads_per_wg(hkv);
     const int64_t groups = hkv / hpw;
     const int64_t hqw = hpw * (hq / hkv);
-    const int64_t chunks_max = max_len > 0 ? (max_len + 30) / 16 + 1 : 0;
-    int64_t wgs = 2ll * cu_count();
+    // chunks of one sequence: ((off + L - 1) >> 4) - (off >> 4) + 1 <= (L + 14) / 16 + 1
+    const int64_t chunks_max = max_len > 0 ? (max_len + 14) / 16 + 1 : 0;
     const int64_t units_max = num_seqs * groups * chunks_max;
+    // a workgroup's share of u units spans at most min(u, pairs) pairs and
+    // at most u * (16 / bs) table entries (bs < 16), u entries otherwise
+    const int64_t per_unit = bs >= 16 ? 1 : 16 / bs;
+    int64_t cap = (kBtLds - 1) / per_unit;
+    if (num_seqs * groups > kSegMax && cap > kSegMax) cap = kSegMax;
+    int64_t wgs = 2ll * cu_count();
+    if (units_max > wgs * cap) wgs = (units_max + cap - 1) / cap;
     if (wgs > units_max) wgs = units_max;
     if (wgs < 1) wgs = 1;
+    // the kernel forms units * workgroup index products in 64 bits
+    if (wgs > INT32_MAX / 2 || (units_max > 0 && wgs > (int64_t(1) << 62) / units_max))
+        return PKV_ERR_SHAPE;
     p->wgs = wgs;
     p->cnt_bytes = (num_seqs * hkv * 4 + 255) / 256 * 256;
     p->ml_bytes = (2 * wgs * hqw * 2 * 4 + 255) / 256 * 256;
@@ -374,10 +410,11 @@ PKV_API size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_kv
                     split_tokens, &p))
         return (size_t)-1;
     int64_t need = p.total();
-    if ((split_tokens == 0 || split_tokens == PKV_SPLIT_BALANCED) && num_seqs <= kStreamMaxSeqs) {
+    if ((split_tokens == 0 || split_tokens == PKV_SPLIT_BALANCED) &&
+        num_seqs <= stream_max_seqs(num_kv_heads)) {
         // the balanced schedule (bf16 pools) or the automatic split (fp32)
         StreamPlan sp;
-        if (plan_stream(num_seqs, num_kv_heads, num_q_heads, head_dim, max_seq_len, &sp))
+        if (plan_stream(num_seqs, num_kv_heads, num_q_heads, head_dim, max_seq_len, block_size, &sp))
             return (size_t)-1;
         if (sp.total() > need) need = sp.total();
     }
@@ -394,8 +431,11 @@ PKV_API int32_t paged_attn_decode_schedule(int32_t num_seqs, int32_t num_kv_head
     const int st = plan_decode(num_seqs, num_kv_heads, num_q_heads, head_dim, max_seq_len,
                                block_size, split_tokens, &p);
     if (st) return st;
-    if (balanced_refused(num_seqs, dtype, split_tokens)) return PKV_ERR_UNSUPPORTED;
-    if (use_balanced(num_seqs, num_kv_heads, head_dim, max_seq_len, dtype, split_tokens)) return 0;
+    if (balanced_refused(num_seqs, num_kv_heads, head_dim, max_seq_len, block_size, dtype,
+                         split_tokens))
+        return PKV_ERR_UNSUPPORTED;
+    if (use_balanced(num_seqs, num_kv_heads, head_dim, max_seq_len, block_size, dtype, split_tokens))
+        return 0;
     return (int32_t)p.split;
 }
 
@@ -417,7 +457,9 @@ int decode_impl(const pkv_pool *pool, int32_t layer, const void *q, int32_t num_
         return PKV_ERR_SHAPE;
     const int group = (int)(num_q_heads / pool->num_kv_heads);
     if (!decode_supported(pool->dtype, (int)pool->head_dim, group)) return PKV_ERR_UNSUPPORTED;
-    if (balanced_refused(num_seqs, pool->dtype, split_tokens)) return PKV_ERR_UNSUPPORTED;
+    if (balanced_refused(num_seqs, pool->num_kv_heads, pool->head_dim, max_seq_len, pool->block_size,
+                         pool->dtype, split_tokens))
+        return PKV_ERR_UNSUPPORTED;
     if (num_seqs == 0) return PKV_OK;
     if (!q || !out || !seq_lens || !offsets || (max_seq_len > 0 && !block_tables))
         return PKV_ERR_NULL;
@@ -429,10 +471,11 @@ int decode_impl(const pkv_pool *pool, int32_t layer, const void *q, int32_t num_
                      pool->block_size, split_tokens, &p);
     if (st) return st;
     const bool balanced = use_balanced(num_seqs, pool->num_kv_heads, pool->head_dim, max_seq_len,
-                                       pool->dtype, split_tokens);
+                                       pool->block_size, pool->dtype, split_tokens);
     StreamPlan sp{};
     if (balanced) {
-        st = plan_stream(num_seqs, pool->num_kv_heads, num_q_heads, pool->head_dim, max_seq_len, &sp);
+        st = plan_stream(num_seqs, pool->num_kv_heads, num_q_heads, pool->head_dim, max_seq_len,
+                         pool->block_size, &sp);
         if (st) return st;
     }
     const int64_t need = balanced ? sp.total() : p.total();

@@ -117,6 +117,13 @@ struct DecodeArgs {
 // this a separate, wider merge kernel is faster.
 constexpr int kFusedMergeMaxSplits = 16;
 
+// Balanced decode schedule: every workgroup reads every sequence length
+// (at most kStreamSeqsPerThread per thread) and lists the (head group,
+// sequence) pairs its share of the work touches, at most kSegMax of them;
+// its share must fit the LDS table buffer (the host sizes the grid so).
+constexpr int kStreamSeqsPerThread = 4;
+constexpr int kSegMax = 80;
+
 // Prefill / append attention: the last n_s = q_start[s+1] - q_start[s]
 // tokens of sequence s are its queries (rows q_start[s].. of q and out).
 struct PrefillArgs {

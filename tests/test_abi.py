@@ -185,6 +185,9 @@ def test_workspace_size_and_split_choice(lib):
         assert s > 0 and s % 16 == 0
         assert s // args[3] + 2 <= 1024
     assert split(4, 8, 100, 12) == SHAPE
+    # the choices on 256 compute units (the count assumed without a device)
+    assert split(32, 8, 2048, 16) == 256
+    assert split(8, 8, 32768, 16) == 1024
 
 
 def test_append_argument_checks(lib):
@@ -232,15 +235,16 @@ def test_prefill_argument_checks(lib):
 
 
 def test_decode_schedule_choice(lib):
-    """The automatic schedule: balanced for bf16 batches with at least
-    512 MiB of K/V at max_seq_len (and at most 4096 sequences), the
-    automatic split otherwise; an explicit split is always kept."""
+    """The automatic schedule: balanced for bf16 batches of at least 32
+    sequences with at least 512 MiB of K/V at max_seq_len (and few enough
+    sequences for the length scan: 4 per thread), the automatic split
+    otherwise; an explicit split is always kept."""
     f = lib.paged_attn_decode_schedule
     F32, BF16 = 0, 1
     split = lib.paged_attn_decode_split_tokens
     assert f(32, 8, 32, 128, 2048, 16, BF16, 0) == split(32, 8, 2048, 16)  # 256 MiB
     assert f(64, 8, 32, 128, 4096, 16, BF16, 0) == 0                       # 1 GiB
-    assert f(8, 8, 64, 128, 32768, 16, BF16, 0) == 0
+    assert f(8, 8, 64, 128, 32768, 16, BF16, 0) == split(8, 8, 32768, 16)  # few sequences
     assert f(8, 8, 64, 128, 32768, 16, F32, 0) == split(8, 8, 32768, 16)
     assert f(8, 8, 64, 128, 32768, 16, BF16, 512) == 512
     assert f(5000, 8, 32, 128, 4096, 16, BF16, 0) == split(5000, 8, 4096, 16)
