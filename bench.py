@@ -263,7 +263,7 @@ def prefill_ops(w_dec, N, W):
 
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "decode_batch_traffic.json")
 DECODE_SOURCES = [os.path.join(ROOT, "paged_attention_decode_scatter_amd", "csrc", f)
-                  for f in ("kernels_decode.hip", "pagedkv_api.hip", "pkv_internal.h")]
+                  for f in ("kernels_decode.hip", "attn_common.h", "pagedkv_api.hip", "pkv_internal.h")]
 
 
 def decode_source_hash():
@@ -277,8 +277,9 @@ def decode_source_hash():
 
 
 def measured_traffic():
-    """HBM bytes per decode launch from the committed counter record, or
-    None when the record is missing or the decode sources changed since."""
+    """HBM bytes per step launch (decode with append) from the committed
+    counter record, or None when the record is missing or the decode sources
+    changed since."""
     try:
         with open(TRAFFIC_RECORD) as f:
             rec = json.load(f)
