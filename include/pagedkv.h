@@ -208,14 +208,16 @@ PKV_API int32_t paged_attn_decode_split_tokens(int32_t num_seqs, int32_t num_kv_
  *   > 0  the split schedule with this many tokens per split: one workgroup
  *        per (sequence, split of split_tokens flat positions, group of kv
  *        heads);
- *     0  the balanced schedule: one resident generation of workgroups, each
- *        taking an equal share of all (kv-head group, sequence,
- *        16-position chunk) units.  Taken for bf16 pools with at most 4096
- *        sequences when split_tokens = PKV_SPLIT_BALANCED, or when
- *        split_tokens = 0 and the batch holds at least 512 MiB of K/V at
+ *     0  the balanced schedule: one resident generation of workgroups (more
+ *        when a share would not fit one pass), each taking an equal share
+ *        of all (kv-head group, sequence, 16-position chunk) units.  Taken
+ *        for bf16 pools with at most 256 * (kv heads per workgroup: 4, 2
+ *        or 1, the largest dividing num_kv_heads) sequences when
+ *        split_tokens = PKV_SPLIT_BALANCED, or when split_tokens = 0 and
+ *        the batch has at least 32 sequences and 512 MiB of K/V at
  *        max_seq_len;
  *   < 0  a status for bad sizes or dtype (PKV_ERR_UNSUPPORTED for a
- *        balanced request on an fp32 pool or more than 4096 sequences).
+ *        balanced request on an fp32 pool or too many sequences).
  * Both compute the same function; they differ only in fp32 rounding order.
  */
 PKV_API int32_t paged_attn_decode_schedule(int32_t num_seqs, int32_t num_kv_heads,
@@ -253,8 +255,8 @@ PKV_API size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_kv
  *   max_seq_len   host bound on every seq_len
  *   scale         softmax scale (e.g. 1/sqrt(head_dim))
  *   split_tokens  0 = automatic (see paged_attn_decode_schedule);
- *                 PKV_SPLIT_BALANCED = the balanced schedule (bf16 pools, at
- *                 most 4096 sequences, else PKV_ERR_UNSUPPORTED); else the
+ *                 PKV_SPLIT_BALANCED = the balanced schedule (bf16 pools,
+ *                 sequence limit as above, else PKV_ERR_UNSUPPORTED); else the
  *                 tokens per split-K work item, a positive multiple of 16
  *                 with split_tokens/block_size + 2 <= 1024.  A sequence
  *                 spread over several work items is computed as partial
