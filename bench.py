@@ -228,9 +228,14 @@ def cpu_baseline(w, lens, min_seconds=10.0, layers=8):
             "host_cpu": model, "host_cpus_visible": os.cpu_count()}
 
 
-def prefill_ops(w_dec, N, W):
+def prefill_ops(w_dec, N, W, reps=64):
     """Scatter and gather rates on the prefill shape, run in the decode
-    batch's pool (same shape: 16384 x 32 x 16 x 8 x 128 bf16)."""
+    batch's pool (same shape: 16384 x 32 x 16 x 8 x 128 bf16).  Like the
+    step, each op's C-ABI call is marshalled once and issued `reps` times
+    back to back (layer rotated), one event pair around all of them; the
+    median of per-call event pairs is reported beside it."""
+    import ctypes
+
     import torch
 
     pf = W.prefill(device=w_dec.k_pool.device, with_pools=False)
@@ -241,8 +246,6 @@ def prefill_ops(w_dec, N, W):
     row = pf.row_bytes
     layers = list(range(w_dec.num_layers))
     scat_bytes = valid * row * 2 * 2 + rows * 8
-    t_s, _ = time_op(lambda l: N.kv_scatter(w_dec.k_pool, w_dec.v_pool, l, pf.k_new, pf.v_new,
-                                            slots), 64, layers)
     total = int(pf.seq_lens.sum())
     k_out = torch.empty((total, pf.num_kv_heads, pf.head_dim), dtype=pf.dtype,
                         device=pf.k_new.device)
@@ -250,14 +253,41 @@ def prefill_ops(w_dec, N, W):
     starts = torch.cumsum(pf.seq_lens.to(torch.int64), 0) - pf.seq_lens.to(torch.int64)
     mx = pf.max_seq_len
     gath_bytes = total * row * 2 * 2
-    t_g, _ = time_op(lambda l: N.kv_gather(w_dec.k_pool, w_dec.v_pool, l, pf.block_tables,
-                                           pf.seq_lens, pf.offsets, starts, mx, k_out, v_out),
-                     64, layers)
+
+    lib = N.load_library()
+    pool = N.make_pool(w_dec.k_pool, w_dec.v_pool)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(w_dec.k_pool.device).cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    sc_args = [(ctypes.byref(pool), l, P(pf.k_new), P(pf.v_new), P(slots), rows, stream)
+               for l in layers]
+    ga_args = [(ctypes.byref(pool), l, P(pf.block_tables), pf.block_tables.shape[1],
+                P(pf.seq_lens), P(pf.offsets), P(starts), pf.num_seqs, mx, P(k_out), P(v_out),
+                total, stream) for l in layers]
+
+    def back_to_back(f, args):
+        for i in range(3):
+            if f(*args[i % len(args)]):
+                raise RuntimeError("library call failed")
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(reps):
+            f(*args[i % len(args)])
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    t_s = back_to_back(lib.kv_scatter, sc_args)
+    t_g = back_to_back(lib.kv_gather, ga_args)
+    t_s_med, _ = time_op(lambda l: lib.kv_scatter(*sc_args[l]), reps, layers)
+    t_g_med, _ = time_op(lambda l: lib.kv_gather(*ga_args[l]), reps, layers)
     return {
         "scatter_prefill": {"rows": rows, "valid_rows": valid, "bytes": scat_bytes,
-                            "ms": t_s, "GB/s": scat_bytes / t_s / 1e6},
+                            "ms": t_s, "GB/s": scat_bytes / t_s / 1e6,
+                            "per_call_events_median_ms": t_s_med},
         "gather_prefill": {"rows": total, "bytes": gath_bytes, "ms": t_g,
-                           "GB/s": gath_bytes / t_g / 1e6},
+                           "GB/s": gath_bytes / t_g / 1e6, "per_call_events_median_ms": t_g_med},
+        "timing": f"{reps} back-to-back C-ABI calls, layer rotated, one event pair around them",
     }
 
 
