@@ -200,7 +200,7 @@ struct MfmaShape {
     static constexpr int KROW = ROWB + 16;       // padded K-tile row
     static constexpr int KTILE = 16 * KROW;
     static constexpr int NSLOT = kDecodeRing;    // pipeline stages (chunks in flight + 1)
-    static constexpr int LOADS = 2 * NP;         // vector-memory ops per chunk
+    static constexpr int LOADS = KS + NP;        // vector-memory ops per chunk (K in operand layout, V rows)
     static_assert(D % 32 == 0 && PPR >= 4 && PPR <= 16 && RPI * ROWB == 1024, "shape");
 };
 

@@ -545,12 +545,12 @@ __device__ __forceinline__ void load_q(const DecodeArgs &a, int seq, int h,
 // described above.  bt_s holds the table entries from jb0 on.
 template <int D, int G, bool UB>
 __device__ __forceinline__ void attend_range(const DecodeArgs &a, int seq, const Range &R, int64_t jb0,
-                                             const int32_t *bt_s, char *vring, char *kt, int h,
+                                             const int32_t *bt_s, char *vring, int h,
                                              const u32x4 (&qf)[MfmaShape<D>::KS], float &m_h,
                                              float &l_h, f32x4 (&acc)[MfmaShape<D>::NV]) {
     using S = MfmaShape<D>;
     constexpr int ROWB = S::ROWB, PPR = S::PPR, NP = S::NP, KS = S::KS, NV = S::NV;
-    constexpr int VSLAB = S::VSLAB, VTILE = S::VTILE, KROW = S::KROW, NSLOT = S::NSLOT;
+    constexpr int VSLAB = S::VSLAB, VTILE = S::VTILE, NSLOT = S::NSLOT;
     constexpr int LOADS = S::LOADS;
     constexpr float kLazy = 8.0f;  // reference-max slack, log2 units
     const int lane = threadIdx.x & 63;
@@ -563,36 +563,43 @@ __device__ __forceinline__ void attend_range(const DecodeArgs &a, int seq, const
 
     const char *kh = a.pool.k + a.pool.layer_off + (int64_t)h * ROWB;
     const char *vh = a.pool.v + a.pool.layer_off + (int64_t)h * ROWB;
-    // Row-layout load role: load instruction i moves rows i + NP*q,
+    // V row-layout load role: load instruction i moves rows i + NP*q,
     // q = lane / PPR, and this lane takes their 16-byte piece lane % PPR.
     // In the V tile instruction i's 1 KiB lands at slab i (slabs padded so
-    // the four rows a P.V operand read touches sit in different banks); the
-    // K tile has padded rows for the same reason.
+    // the four rows a P.V operand read touches sit in different banks).
     const int trow = lane / PPR;
     const int tpp = lane % PPR;
 
-    // Issue the loads of chunk pc into K registers kx and V ring slot `slot`.
+    // Issue the loads of chunk pc: K straight into registers in the MFMA
+    // A-operand layout (lane (n, g4) takes row n, bytes 64 j + 16 g4 .. +16
+    // for step j), V into ring slot `slot` in row layout.
     auto load_chunk = [&](int64_t pc, u32x4 *kx, int slot) {
         char *dst = vring + slot * VTILE;
         if constexpr (UB) {
             int32_t b = __builtin_amdgcn_readfirstlane(bt_s[(int)((pc >> lbs) - jb0)]);
             const int64_t base = (int64_t)(b >= 0 ? b : 0) * a.pool.block_stride + (pc & bsm) * row_bytes;
-            const char *kb = kh + base;
+            const char *kb = kh + base + (uint32_t)(n * row_bytes + 16 * g4);
             const char *vb = vh + base;
 #pragma unroll
-            for (int i = 0; i < NP; ++i) {
-                const uint32_t o = (uint32_t)((i + NP * trow) * row_bytes + 16 * tpp);
-                kx[i] = ld16(kb + o);
-                lds_copy16(vb + o, dst + i * VSLAB);
-            }
+            for (int j = 0; j < KS; ++j) kx[j] = ld16(kb + 64 * j);
+#pragma unroll
+            for (int i = 0; i < NP; ++i)
+                lds_copy16(vb + (uint32_t)((i + NP * trow) * row_bytes + 16 * tpp), dst + i * VSLAB);
         } else {
+            {
+                const int64_t p = pc + n;
+                const bool in = p >= R.lo && p < R.hi;
+                const int32_t b = in ? bt_s[(int)((p >> lbs) - jb0)] : -1;
+                const char *kb = kh + (int64_t)(b >= 0 ? b : 0) * a.pool.block_stride + (p & bsm) * row_bytes + 16 * g4;
+#pragma unroll
+                for (int j = 0; j < KS; ++j) kx[j] = ld16(kb + 64 * j);
+            }
 #pragma unroll
             for (int i = 0; i < NP; ++i) {
                 const int64_t p = pc + i + NP * trow;
                 const bool in = p >= R.lo && p < R.hi;
                 const int32_t b = in ? bt_s[(int)((p >> lbs) - jb0)] : -1;
                 const int64_t o = (int64_t)(b >= 0 ? b : 0) * a.pool.block_stride + (p & bsm) * row_bytes + 16 * tpp;
-                kx[i] = ld16(kh + o);
                 lds_copy16(vh + o, dst + i * VSLAB);
             }
         }
@@ -622,18 +629,11 @@ __device__ __forceinline__ void attend_range(const DecodeArgs &a, int seq, const
             }
             wave_lds_order();
         }
-        // K chunk into the K tile, then back in operand layout
-#pragma unroll
-        for (int i = 0; i < NP; ++i)
-            *reinterpret_cast<u32x4 *>(kt + (i + NP * trow) * KROW + 16 * tpp) = kc[i];
-        wave_lds_order();
         // scores: lane holds S[token 4*g4 + i][head n]
         f32x4 sacc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int j = 0; j < KS; ++j) {
-            const u32x4 kf = *reinterpret_cast<const u32x4 *>(kt + n * KROW + 16 * g4 + 64 * j);
-            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf), as_bf16x8(qf[j]), sacc, 0, 0, 0);
-        }
+        for (int j = 0; j < KS; ++j)
+            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kc[j]), as_bf16x8(qf[j]), sacc, 0, 0, 0);
         float s[4];
         float cm = kNegInf;
 #pragma unroll
@@ -696,24 +696,29 @@ __device__ __forceinline__ void attend_range(const DecodeArgs &a, int seq, const
         // first loads unless those already cover chunk `last`.
         const bool app = a.k_new != nullptr && R.len > 0 && R.hi == R.off + R.len;
         const int64_t pn = R.hi - 1;
-        const bool app_lane = app && trow == (int)(pn & 15) / NP;
-        u32x4 kn = {0, 0, 0, 0}, vn = {0, 0, 0, 0};
-        if (app_lane) {
-            const int64_t src = ((int64_t)seq * a.num_kv_heads + h) * ROWB + 16 * tpp;
-            kn = ld16(a.k_new + src);
-            vn = ld16(a.v_new + src);
-        }
+        const int rn = (int)(pn & 15);               // the new row within its chunk
+        const bool k_lane = app && n == rn;          // loads K pieces 4 j + g4 of that row
+        const bool v_lane = app && trow == rn / NP;  // loads V piece tpp of that row
+        const int64_t src = ((int64_t)seq * a.num_kv_heads + h) * ROWB;
+        u32x4 kn[KS], vn = {0, 0, 0, 0};
+#pragma unroll
+        for (int j = 0; j < KS; ++j) kn[j] = k_lane ? ld16(a.k_new + src + 64 * j + 16 * g4) : u32x4{0, 0, 0, 0};
+        if (v_lane) vn = ld16(a.v_new + src + 16 * tpp);
         auto store_new = [&]() {
-            if (!app_lane) return;
+            if (!k_lane && !v_lane) return;
             const int32_t b = bt_s[(int)((pn >> lbs) - jb0)];
             if (b < 0) return;  // no block at that position: nothing to write (its score is masked)
-            const int64_t o = (int64_t)b * a.pool.block_stride + (pn & bsm) * row_bytes + 16 * tpp;
-            *reinterpret_cast<u32x4 *>(const_cast<char *>(kh) + o) = kn;
-            *reinterpret_cast<u32x4 *>(const_cast<char *>(vh) + o) = vn;
+            const int64_t o = (int64_t)b * a.pool.block_stride + (pn & bsm) * row_bytes;
+            if (k_lane) {
+#pragma unroll
+                for (int j = 0; j < KS; ++j)
+                    *reinterpret_cast<u32x4 *>(const_cast<char *>(kh) + o + 64 * j + 16 * g4) = kn[j];
+            }
+            if (v_lane) *reinterpret_cast<u32x4 *>(const_cast<char *>(vh) + o + 16 * tpp) = vn;
         };
         const bool store_early = last - first < 16 * (NSLOT - 1);
         if (store_early) store_new();
-        u32x4 kring[NSLOT][NP];
+        u32x4 kring[NSLOT][KS];
 #pragma unroll
         for (int q = 0; q < NSLOT - 1; ++q) load_chunk(min(first + 16 * q, last), kring[q], q);
         if (!store_early) store_new();
@@ -789,7 +794,6 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     static_assert(G >= 1 && G <= 16, "group");
     __shared__ int32_t bt_s[kBtLds];
     __shared__ __attribute__((aligned(16))) char vtiles[4][S::NSLOT][S::VTILE];
-    __shared__ __attribute__((aligned(16))) char ktiles[4][S::KTILE];
 
     const Item it = work_item(a);
     const Range R = split_range(a, it.seq, it.split);
@@ -809,7 +813,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     f32x4 acc[S::NV];
 #pragma unroll
     for (int sl = 0; sl < S::NV; ++sl) acc[sl] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    attend_range<D, G, UB>(a, it.seq, R, jb0, bt_s, vtiles[w][0], ktiles[w], h, qf, m_h, l_h, acc);
+    attend_range<D, G, UB>(a, it.seq, R, jb0, bt_s, vtiles[w][0], h, qf, m_h, l_h, acc);
     float lrow[4];
     head_denominators(l_h, lrow);
     if (direct) {
@@ -887,7 +891,7 @@ template <int D, int G, bool UB>
 __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeArgs a) {
     using S = MfmaShape<D>;
     constexpr int ROWB = S::ROWB, PPR = S::PPR, NP = S::NP, KS = S::KS, NV = S::NV;
-    constexpr int VSLAB = S::VSLAB, VTILE = S::VTILE, KROW = S::KROW, NSLOT = S::NSLOT;
+    constexpr int VSLAB = S::VSLAB, VTILE = S::VTILE, NSLOT = S::NSLOT;
     constexpr int LOADS = S::LOADS;
     constexpr int PER = kStreamSeqsPerThread;  // sequences per thread, at most
     constexpr int SLOTS = 4;                   // table entries per thread per pass
@@ -897,7 +901,6 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeArgs a) {
     constexpr int SBATCH = SPI * (NSLOT * VTILE / 1024);  // segments staged at once in the V ring
     __shared__ int32_t bt_s[kBtLds];
     __shared__ __attribute__((aligned(16))) char vtiles[4][NSLOT][VTILE];
-    __shared__ __attribute__((aligned(16))) char ktiles[4][S::KTILE];
     __shared__ RoundLds R;
 
     const int t = threadIdx.x;
@@ -917,7 +920,6 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeArgs a) {
     const int trow = lane / PPR;
     const int tpp = lane % PPR;
     char *vring = vtiles[w][0];
-    char *kt = ktiles[w];
     // logical workgroup index: consecutive ranges share an XCD
     const int nwg = gridDim.x;
     const int bid = blockIdx.x;
@@ -1180,15 +1182,21 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeArgs a) {
                         const int64_t pn = R.hi[i] - 1;
                         const int bi = R.base[i] + (int)((pn >> lbs) - (R.lo[i] >> lbs));
                         const int32_t b = bi < kBtLds ? bt_s[bi] : -1;
-                        if (trow == (int)(pn & 15) / NP && b >= 0) {
+                        const int rn = (int)(pn & 15);
+                        if (b >= 0 && (n16 == rn || trow == rn / NP)) {
                             const int64_t o = a.pool.layer_off + (int64_t)b * a.pool.block_stride +
                                               (pn & bsm) * row_bytes +
-                                              (int64_t)(R.hg[i] * a.heads_per_wg + w) * ROWB + 16 * tpp;
+                                              (int64_t)(R.hg[i] * a.heads_per_wg + w) * ROWB;
                             const char *st = vring + ((i - b0) / SPI) * 1024 + ((i - b0) % SPI) * (2 * PPR) * 16;
-                            *reinterpret_cast<u32x4 *>(const_cast<char *>(a.pool.k) + o) =
-                                *reinterpret_cast<const u32x4 *>(st + 16 * tpp);
-                            *reinterpret_cast<u32x4 *>(const_cast<char *>(a.pool.v) + o) =
-                                *reinterpret_cast<const u32x4 *>(st + 16 * (PPR + tpp));
+                            if (n16 == rn) {  // the lanes that load this row's K pieces 4 j + g4
+#pragma unroll
+                                for (int j = 0; j < KS; ++j)
+                                    *reinterpret_cast<u32x4 *>(const_cast<char *>(a.pool.k) + o + 64 * j + 16 * g4) =
+                                        *reinterpret_cast<const u32x4 *>(st + 64 * j + 16 * g4);
+                            }
+                            if (trow == rn / NP)  // the lanes that load this row's V piece tpp
+                                *reinterpret_cast<u32x4 *>(const_cast<char *>(a.pool.v) + o + 16 * tpp) =
+                                    *reinterpret_cast<const u32x4 *>(st + 16 * (PPR + tpp));
                         }
                     }
                 }
@@ -1233,17 +1241,29 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeArgs a) {
             const char *kh = a.pool.k + L.hoff;
             const char *vh = a.pool.v + L.hoff;
             char *dst = vring + slot * VTILE;
+            // K straight into registers in the MFMA A-operand layout (lane
+            // (n16, g4): row n16, bytes 64 j + 16 g4 .. +16 of step j), V into
+            // ring slot `slot` in row layout
             if constexpr (UB) {
                 const int bi = L.base + (int)((pc >> lbs) - L.jb0);
                 const int32_t b = __builtin_amdgcn_readfirstlane(bi < kBtLds ? bt_s[bi] : -1);
                 const int64_t bb = (int64_t)(b >= 0 ? b : 0) * a.pool.block_stride + (pc & bsm) * row_bytes;
+                const char *kb = kh + bb + (uint32_t)(n16 * row_bytes + 16 * g4);
 #pragma unroll
-                for (int i = 0; i < NP; ++i) {
-                    const uint32_t o = (uint32_t)((i + NP * trow) * row_bytes + 16 * tpp);
-                    kx[i] = ld16(kh + bb + o);
-                    lds_copy16(vh + bb + o, dst + i * VSLAB);
-                }
+                for (int j = 0; j < KS; ++j) kx[j] = ld16(kb + 64 * j);
+#pragma unroll
+                for (int i = 0; i < NP; ++i)
+                    lds_copy16(vh + bb + (uint32_t)((i + NP * trow) * row_bytes + 16 * tpp), dst + i * VSLAB);
             } else {
+                {
+                    const int64_t p = pc + n16;
+                    const int bi = L.base + (int)((p >> lbs) - L.jb0);
+                    const bool in = p >= L.lo && p < L.hi && bi < kBtLds;
+                    const int32_t b = in ? bt_s[bi] : -1;
+                    const char *kb = kh + (int64_t)(b >= 0 ? b : 0) * a.pool.block_stride + (p & bsm) * row_bytes + 16 * g4;
+#pragma unroll
+                    for (int j = 0; j < KS; ++j) kx[j] = ld16(kb + 64 * j);
+                }
 #pragma unroll
                 for (int i = 0; i < NP; ++i) {
                     const int64_t p = pc + i + NP * trow;
@@ -1251,7 +1271,6 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeArgs a) {
                     const bool in = p >= L.lo && p < L.hi && bi < kBtLds;
                     const int32_t b = in ? bt_s[bi] : -1;
                     const int64_t o = (int64_t)(b >= 0 ? b : 0) * a.pool.block_stride + (p & bsm) * row_bytes + 16 * tpp;
-                    kx[i] = ld16(kh + o);
                     lds_copy16(vh + o, dst + i * VSLAB);
                 }
             }
@@ -1289,16 +1308,10 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeArgs a) {
                 }
                 wave_lds_order();
             }
-#pragma unroll
-            for (int i = 0; i < NP; ++i)
-                *reinterpret_cast<u32x4 *>(kt + (i + NP * trow) * KROW + 16 * tpp) = kc[i];
-            wave_lds_order();
             f32x4 sacc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int j = 0; j < KS; ++j) {
-                const u32x4 kf = *reinterpret_cast<const u32x4 *>(kt + n16 * KROW + 16 * g4 + 64 * j);
-                sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf), as_bf16x8(qf[j]), sacc, 0, 0, 0);
-            }
+            for (int j = 0; j < KS; ++j)
+                sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kc[j]), as_bf16x8(qf[j]), sacc, 0, 0, 0);
             float s[4];
             float cm = kNegInf;
 #pragma unroll
@@ -1341,7 +1354,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeArgs a) {
             wave_lds_order();
         };
 
-        u32x4 kring[NSLOT][NP];
+        u32x4 kring[NSLOT][KS];
 #pragma unroll
         for (int q = 0; q < NSLOT - 1; ++q) issue(q, kring[q], q);
         for (int k = 0; k < T;) {
