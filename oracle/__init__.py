@@ -14,6 +14,7 @@ from .oracle import (  # noqa: F401
     ORC_F32,
     blocks_needed,
     capacity,
+    copy_blocks,
     decode,
     fragmentation_ratio,
     gather,
@@ -25,5 +26,7 @@ from .oracle import (  # noqa: F401
     scatter,
     scatter_index_put,
     slot_mapping,
+    swap_in,
+    swap_out,
 )
 from .block_manager import BlockManagerOracle  # noqa: F401

@@ -32,7 +32,16 @@ Readings where the pages are silent (stated, not invented):
     they can carry (whole-block sharing, as prefix sharing needs);
   * statistics: used = blocks not in the free queue; peak = the largest
     used count seen; utilisation = live tokens / (distinct used blocks *
-    bs), live tokens counting each (block, slot) once.
+    bs), live tokens counting each (block, slot) once;
+  * cow(seq, j), the copy-on-write that "vLLM PagedAttention" sharing adds
+    to ref_count (ch. 12, 3.1 industrial implementations, the sharing row):
+    before a sequence writes into table entry j whose block other holders
+    share (count > 1), it takes a new block from the free queue's front,
+    the same FIFO take as allocate, puts it at entry j, and gives up one
+    reference to the old block (which keeps its other holders); the caller
+    copies the block's contents from old to new.  An unshared block needs
+    no copy (the answer is (b, b), nothing changes); with an empty free
+    queue the answer is False and nothing changes, as for allocate.
 
 Parity unpinned: nothing (pins in tests/test_block_manager.py).
 """
@@ -115,6 +124,25 @@ class BlockManagerOracle:
             self._note_peak()
         st["len"] += 1
         return st["blocks"][j] * self.block_size + s
+
+    def cow(self, seq, index):
+        """Copy-on-write of table entry `index` of `seq`: (old, new) block
+        ids (old == new when the block is not shared), or False with
+        nothing changed when a copy is needed and no block is free."""
+        st = self.seqs[seq]
+        if not 0 <= index < len(st["blocks"]):
+            raise ValueError("bad table index")
+        b = st["blocks"][index]
+        if self.ref_count[b] <= 1:
+            return (b, b)
+        if not self.free_ids:
+            return False
+        nb = self.free_ids.popleft()
+        self.ref_count[nb] = 1
+        st["blocks"][index] = nb
+        self.dec_ref(b)
+        self._note_peak()
+        return (b, nb)
 
     # ---- release ---------------------------------------------------------
     def inc_ref(self, block):

@@ -180,6 +180,46 @@ def prefill(k_pool, v_pool, layer, q, q_start, block_tables, seq_lens, offsets, 
 
 
 # --------------------------------------------------------------------------
+# Whole-block moves: the copy of copy-on-write and the swap of preemption
+# --------------------------------------------------------------------------
+def copy_blocks(pool, src_blocks, dst_blocks):
+    """In place: for each pair in order, every layer of block src[i] is
+    copied to block dst[i] (pool: (num_blocks, num_layers, bs, H, D)); a
+    pair with an id outside the pool is skipped.  The copy a writer makes
+    of a shared block before writing into it ("vLLM PagedAttention" in
+    ch. 12, 3.1: sharing by copy-on-write + ref_count)."""
+    nb = pool.shape[0]
+    for s, d in zip(np.asarray(src_blocks).tolist(), np.asarray(dst_blocks).tolist()):
+        if 0 <= s < nb and 0 <= d < nb:
+            pool[d] = pool[s].copy()
+    return pool
+
+
+def swap_out(pool, block_ids):
+    """The blocks' contents, all layers, in the order given: a host array
+    (n, num_layers, bs, H, D).  The GPU -> CPU move of preemption ("vLLM
+    PagedAttention source notes", 2.4 scheduler integration)."""
+    ids = np.asarray(block_ids, dtype=np.int64)
+    if ids.size and (ids.min() < 0 or ids.max() >= pool.shape[0]):
+        raise ValueError("block id outside the pool")
+    return np.stack([pool[b].copy() for b in ids.tolist()]) if ids.size else \
+        np.empty((0,) + pool.shape[1:], dtype=pool.dtype)
+
+
+def swap_in(pool, block_ids, host):
+    """In place: block ids[i] of the pool takes host[i] (all layers): the
+    CPU -> GPU move that brings a swapped-out sequence back."""
+    ids = np.asarray(block_ids, dtype=np.int64)
+    if ids.size and (ids.min() < 0 or ids.max() >= pool.shape[0]):
+        raise ValueError("block id outside the pool")
+    if host.shape != (ids.size,) + pool.shape[1:]:
+        raise ValueError("host buffer shape")
+    for i, b in enumerate(ids.tolist()):
+        pool[b] = host[i]
+    return pool
+
+
+# --------------------------------------------------------------------------
 # Pure-Python / numpy forms (tiny inputs; second formulations for the pins)
 # --------------------------------------------------------------------------
 def gather_loop_cat(pool_layer, block_table, seq_len, block_size, offset=0):

@@ -141,6 +141,127 @@ def test_oracle_pins(pin):
     pin(BlockManagerOracle)
 
 
+# ---------------------------------------------------------------------------
+# copy-on-write (ch. 12, 3.1: sharing by copy-on-write + ref_count; 2.3 the
+# FIFO take and its False; 2.4 reference counts)
+# ---------------------------------------------------------------------------
+def cow_state(m, seqs):
+    return (list(m.free_ids), list(m.ref_count), {q: m.table(q) for q in seqs})
+
+
+def pin_cow_unshared_is_noop(cls):
+    """A block held by one table needs no copy: (b, b), nothing changes."""
+    m = cls(6, 4)
+    assert m.allocate(1, 10)
+    before = cow_state(m, [1])
+    b = m.table(1)[2]
+    assert m.cow(1, 2) == (b, b)
+    assert cow_state(m, [1]) == before
+
+
+def pin_cow_moves_one_reference_to_the_fifo_front(cls):
+    """The writer of a shared block takes the free queue's front block in
+    its table, the old block keeps its other holder, counts 1 and 1."""
+    m = cls(8, 4)
+    assert m.allocate(1, 12)          # blocks 0, 1, 2
+    m.share(1, 2, 2)                  # 2 holds 0, 1 (counts 2, 2, 1)
+    front = m.free_ids[0]
+    t1 = m.table(1)
+    assert m.cow(2, 1) == (t1[1], front)
+    assert m.table(2) == [t1[0], front] and m.table(1) == t1
+    assert m.ref_count[t1[1]] == 1 and m.ref_count[front] == 1 and m.ref_count[t1[0]] == 2
+    assert front not in m.free_ids
+
+
+def pin_cow_short_queue_changes_nothing(cls):
+    """Shared block, empty free queue: False, nothing taken or moved."""
+    m = cls(3, 4)
+    assert m.allocate(1, 12)          # all three blocks
+    m.share(1, 2, 3)
+    before = cow_state(m, [1, 2])
+    assert m.cow(2, 0) is False
+    assert cow_state(m, [1, 2]) == before
+
+
+def pin_cow_then_free_returns_every_block(cls):
+    """After copies, freeing every holder frees every block."""
+    m = cls(10, 4)
+    assert m.allocate(1, 16)
+    m.share(1, 2, 4)
+    m.share(1, 3, 2)
+    for q, j in [(2, 3), (3, 0), (3, 1), (2, 0)]:
+        assert m.cow(q, j)
+    for q in (1, 2, 3):
+        m.free(q)
+    assert all(r == 0 for r in m.ref_count) and sorted(m.free_ids) == list(range(10))
+
+
+def pin_cow_then_append_writes_the_private_block(cls):
+    """A sequence sharing a partly filled last block copies it and then
+    appends into its own copy, not into the shared one."""
+    m = cls(8, 4)
+    assert m.allocate(1, 6)           # blocks 0, 1; block 1 holds 2 tokens
+    m.share(1, 2, 2)                  # 2 holds the same 8 slots; len 8
+    m2_last = m.table(2)[1]
+    old, new = m.cow(1, 1)
+    assert old == m2_last and new != old
+    slot = m.append_slot(1)           # token 6 of sequence 1
+    assert slot // 4 == new and slot % 4 == 2
+
+
+COW_PINS = [pin_cow_unshared_is_noop, pin_cow_moves_one_reference_to_the_fifo_front,
+            pin_cow_short_queue_changes_nothing, pin_cow_then_free_returns_every_block,
+            pin_cow_then_append_writes_the_private_block]
+
+
+@pytest.mark.parametrize("pin", COW_PINS, ids=lambda f: f.__name__)
+def test_oracle_cow_pins(pin):
+    pin(BlockManagerOracle)
+
+
+class _CowKeepsOldReference(BlockManagerOracle):
+    def cow(self, seq, index):
+        st = self.seqs[seq]
+        b = st["blocks"][index]
+        if self.ref_count[b] <= 1:
+            return (b, b)
+        if not self.free_ids:
+            return False
+        nb = self.free_ids.popleft()
+        self.ref_count[nb] = 1
+        st["blocks"][index] = nb
+        return (b, nb)
+
+
+class _CowFromTheBack(BlockManagerOracle):
+    def cow(self, seq, index):
+        if self.free_ids:
+            self.free_ids.rotate(-1)  # the back id comes to the front
+        return super().cow(seq, index)
+
+
+class _CowAlwaysCopies(BlockManagerOracle):
+    def cow(self, seq, index):
+        st = self.seqs[seq]
+        b = st["blocks"][index]
+        if not self.free_ids:
+            return False
+        self.ref_count[b] += 1
+        return super().cow(seq, index)
+
+
+@pytest.mark.parametrize("mutant", [_CowKeepsOldReference, _CowFromTheBack, _CowAlwaysCopies],
+                         ids=lambda c: c.__name__)
+def test_planted_cow_mistake_fails_a_pin(mutant):
+    failed = 0
+    for pin in COW_PINS:
+        try:
+            pin(mutant)
+        except (AssertionError, ValueError, IndexError, KeyError, TypeError):
+            failed += 1
+    assert failed > 0
+
+
 # Plausible mistakes planted in copies of the oracle: each must fail a pin.
 class _Lifo(BlockManagerOracle):
     def dec_ref(self, block):

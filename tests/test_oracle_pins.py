@@ -515,3 +515,63 @@ def test_prefill_queries_beyond_the_sequence_are_zero():
     assert np.all(got[:3] == 0)
     ref = O.prefill(k, v, 0, q[3:], np.array([0, L0, L0 + L1], np.int32), bt, lens, offs, 0.5)
     assert np.array_equal(got[3:], ref)
+
+
+# ---------------------------------------------------------------------------
+# whole-block moves: the copy of copy-on-write, the swap of preemption
+# ---------------------------------------------------------------------------
+def gather_all_layers(pool, table, L, bs, off):
+    return np.stack([O.gather_flat_index(pool[:, l], table, L, bs, off)
+                     for l in range(pool.shape[1])])
+
+
+@pytest.mark.parametrize("bs", [1, 4, 16])
+def test_copy_blocks_gives_writers_the_same_tokens(bs):
+    """ch. 12, 3.1 (sharing by copy-on-write): after copying each block of
+    a table to a fresh block, the table remapped to the copies gathers the
+    same K/V at every layer as the original, bit for bit; blocks that were
+    neither source nor destination keep their bytes; a pair naming a block
+    outside the pool is skipped."""
+    rng = np.random.default_rng(300 + bs)
+    k, _, _, bt, lens, offs = make_decode_case(rng, 3, 2, 1, 8, bs, True, max_len=30, nl=3)
+    nb = k.shape[0]
+    extra = rng.standard_normal((nb,) + k.shape[1:]).astype(np.float32)
+    pool = np.concatenate([k, f32_to_bf16_bits(extra)])      # fresh blocks nb .. 2nb-1
+    used = sorted({int(b) for b in bt[bt >= 0]})
+    dst = [nb + i for i in range(len(used))]
+    before = pool.copy()
+    O.copy_blocks(pool, used + [2 * nb + 5], dst + [0])
+    remap = {s: d for s, d in zip(used, dst)}
+    for s in range(3):
+        L, off = int(lens[s]), int(offs[s])
+        t2 = np.array([remap.get(int(b), -1) for b in bt[s]], np.int32)
+        assert np.array_equal(gather_all_layers(pool, t2, L, bs, off),
+                              gather_all_layers(before, bt[s], L, bs, off))
+    untouched = [b for b in range(2 * nb) if b not in dst]
+    assert np.array_equal(pool[untouched], before[untouched])
+
+
+def test_swap_out_holds_each_blocks_tokens_and_swap_in_restores_them():
+    """P2 2.4 (preemption swaps KV GPU -> CPU and back): swap_out's i-th
+    entry at layer l is what a one-block table gathers at layer l (all bs
+    slots); swapping those blocks back in at other ids gives the same gather
+    through the remapped table as the original, bit for bit."""
+    rng = np.random.default_rng(31)
+    bs = 4
+    k, _, _, bt, lens, offs = make_decode_case(rng, 2, 2, 1, 8, bs, False, max_len=20, nl=2)
+    nb = k.shape[0]
+    ids = [int(b) for b in bt[0] if b >= 0]
+    host = O.swap_out(k, ids)
+    assert host.shape == (len(ids),) + k.shape[1:]
+    for i, b in enumerate(ids):
+        one = np.array([b], np.int32)
+        assert np.array_equal(host[i], gather_all_layers(k, one, bs, bs, 0))
+    pool = np.concatenate([k, np.zeros_like(k)])
+    new_ids = [nb + i for i in range(len(ids))]
+    O.swap_in(pool, new_ids, host)
+    t2 = np.array([nb + ids.index(int(b)) if b >= 0 else -1 for b in bt[0]], np.int32)
+    L, off = int(lens[0]), int(offs[0])
+    assert np.array_equal(gather_all_layers(pool, t2, L, bs, off),
+                          gather_all_layers(k, bt[0], L, bs, off))
+    with pytest.raises(ValueError):
+        O.swap_out(k, [nb])
