@@ -80,7 +80,15 @@ enum {
 };
 
 /* A paged KV pool: caller-owned device memory, only read or written during
- * a call.  dtype is PKV_F32 or PKV_BF16; `reserved` must be 0. */
+ * a call.  dtype is PKV_F32 or PKV_BF16; `reserved` must be 0.  K and V are
+ * each laid out as (num_blocks, num_layers, block_size, num_kv_heads,
+ * head_dim) [P2 sec. 2.2]; block_stride is the byte distance from one block
+ * of a tensor to the next, 0 meaning the dense layout (num_layers *
+ * block_size * num_kv_heads * head_dim * element bytes).  The combined
+ * layout (num_blocks, 2, num_layers, block_size, num_kv_heads, head_dim)
+ * of the same section is k = its base, v = base + one dense block,
+ * block_stride = two dense blocks.  A nonzero block_stride must be a
+ * multiple of 16 and at least one dense block. */
 typedef struct pkv_pool {
     void *k;
     void *v;
@@ -91,6 +99,7 @@ typedef struct pkv_pool {
     int64_t head_dim;
     int32_t dtype;
     int32_t reserved;
+    int64_t block_stride;
 } pkv_pool;
 
 /*
@@ -347,6 +356,47 @@ PKV_API int paged_attn_prefill(const pkv_pool *pool, int32_t layer,
                                const int32_t *block_tables, int32_t bt_stride,
                                const int32_t *seq_lens, const int32_t *offsets,
                                int32_t num_seqs, float scale, void *out, void *stream);
+
+/*
+ * kv_copy_blocks -- whole-block copies: for i < num_pairs, every layer of K
+ * and of V of block src_blocks[i] is copied to block dst_blocks[i].  This
+ * is the copy of copy-on-write [P3 sec. 3.1: vLLM shares blocks by
+ * copy-on-write + ref_count; sec. 2.4 ref_count]: before a sequence writes
+ * into a block other tables also hold, it takes a new block (pkv_bm_cow)
+ * and the block's contents are copied here.
+ *
+ *   src_blocks, dst_blocks  device int32 [num_pairs]; a pair with an id
+ *                 outside [0, num_blocks) is skipped.  Destinations must be
+ *                 distinct and none may be another pair's source (caller
+ *                 contract; pkv_bm_cow's pairs meet it).
+ * V is copied when pool->v is set.  Asynchronous on `stream`.
+ * Errors: PKV_ERR_NULL, _DTYPE, _SHAPE, _ALIGN, _LAUNCH.
+ */
+PKV_API int kv_copy_blocks(const pkv_pool *pool, const int32_t *src_blocks,
+                           const int32_t *dst_blocks, int64_t num_pairs, void *stream);
+
+/*
+ * kv_swap_out / kv_swap_in -- move whole blocks between the pool and host
+ * memory: the swap of preemption [P2 sec. 2.4: when free blocks run short
+ * the scheduler can move a sequence's KV from GPU to CPU, or drop it and
+ * recompute].  Block i of the list is one dense block per tensor
+ * (num_layers * block_size * num_kv_heads * head_dim elements) at
+ * k_host / v_host + i * that many bytes.
+ *
+ *   block_ids     HOST int32 [n], each in [0, num_blocks), else
+ *                 PKV_ERR_BLOCK before any copy
+ *   k_host, v_host  host buffers of n dense blocks each; v_host is used
+ *                 (and required) when pool->v is set.  Pinned host memory
+ *                 (hipHostMalloc, torch pin_memory) keeps the copies
+ *                 asynchronous on `stream`; pageable memory works, but the
+ *                 copies then finish before the call returns.
+ * Runs of consecutive ids in a dense pool move as one copy.
+ * Errors: PKV_ERR_NULL, _DTYPE, _SHAPE, _ALIGN, _BLOCK, _LAUNCH.
+ */
+PKV_API int kv_swap_out(const pkv_pool *pool, const int32_t *block_ids, int64_t n,
+                        void *k_host, void *v_host, void *stream);
+PKV_API int kv_swap_in(const pkv_pool *pool, const int32_t *block_ids, int64_t n,
+                       const void *k_host, const void *v_host, void *stream);
 
 /*
  * kv_validate -- count violations of the caller contract, for debugging:

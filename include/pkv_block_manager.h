@@ -16,6 +16,8 @@
  *     taken (PKV_NO_SPACE here).
  *   [P3 sec. 2.4] reference counts: a block shared by several tables goes
  *     back to the free queue (at its back) only when its count reaches 0.
+ *   [P3 sec. 3.1] copy-on-write: a sequence about to write into a shared
+ *     block first gets a private copy (pkv_bm_cow, then kv_copy_blocks).
  *
  * Sequences are named by caller-chosen int64 ids.  A manager is plain host
  * memory; calls on one manager must not overlap (it has no lock).  All
@@ -81,6 +83,19 @@ PKV_API int32_t pkv_bm_append_slots(pkv_block_manager *bm, const int64_t *seqs, 
  * blocks whose count reaches 0 join the back of the free queue.
  * Errors: PKV_ERR_NULL, _SEQ. */
 PKV_API int pkv_bm_free(pkv_block_manager *bm, int64_t seq);
+
+/* Copy-on-write of table entry `index` of `seq` [P3 sec. 3.1: sharing by
+ * copy-on-write + ref_count], before the sequence writes into that block.
+ * When the block has other holders (count > 1), the free queue's front
+ * block takes its place in this table (count 1, as in allocate
+ * [P3 sec. 2.3]) and the old block loses one reference [P3 sec. 2.4];
+ * *src_block / *dst_block receive old and new: copy its contents with
+ * kv_copy_blocks.  An unshared block needs no copy: both receive it and
+ * nothing changes.  PKV_NO_SPACE (nothing changed) when a copy is needed
+ * and no block is free.  Errors: PKV_ERR_NULL, _SEQ, _SHAPE (index outside
+ * the table). */
+PKV_API int pkv_bm_cow(pkv_block_manager *bm, int64_t seq, int32_t index, int32_t *src_block,
+                       int32_t *dst_block);
 
 /* One more / one less holder of a used block [P3 sec. 2.4]; dec_ref to 0
  * frees it.  Errors: PKV_ERR_NULL, _BLOCK (out of range or free). */

@@ -195,6 +195,27 @@ PKV_API int pkv_bm_free(pkv_block_manager *bm, int64_t seq) {
     return PKV_OK;
 }
 
+PKV_API int pkv_bm_cow(pkv_block_manager *bm, int64_t seq, int32_t index, int32_t *src_block,
+                       int32_t *dst_block) {
+    if (!bm || !src_block || !dst_block) return PKV_ERR_NULL;
+    pkv_block_manager::Seq *s = bm->find(seq);
+    if (!s) return PKV_ERR_SEQ;
+    if (index < 0 || index >= (int64_t)s->blocks.size()) return PKV_ERR_SHAPE;
+    const int32_t b = s->blocks[index];
+    if (bm->ref[b] <= 1) {  // unshared: written in place
+        *src_block = *dst_block = b;
+        return PKV_OK;
+    }
+    if (bm->free_q.empty()) return PKV_NO_SPACE;
+    const int32_t nb = bm->take();
+    s->blocks[index] = nb;
+    bm->drop(b);  // still held by the other tables: stays out of the queue
+    bm->note_peak();
+    *src_block = b;
+    *dst_block = nb;
+    return PKV_OK;
+}
+
 PKV_API int pkv_bm_inc_ref(pkv_block_manager *bm, int32_t block) {
     if (!bm) return PKV_ERR_NULL;
     if (block < 0 || block >= bm->num_blocks || bm->ref[block] <= 0) return PKV_ERR_BLOCK;

@@ -1,5 +1,6 @@
 // kernels_copy.hip -- integer-index kernels for gfx950: slot computation,
-// slot_mapping scatter, block_table gather, contract validation.
+// slot_mapping scatter, block_table gather, whole-block copies, contract
+// validation.
 //
 // Sources:
 //   [P1] mini-vllm tutorial, "step14_2 - index_select gather"
@@ -270,6 +271,52 @@ __global__ __launch_bounds__(kCopyThreads) void gather_kernel(GatherArgs a) {
 hipError_t launch_gather(const GatherArgs &a, hipStream_t s) {
     const int64_t blocks = (int64_t)a.num_seqs * a.tiles_per_seq;
     hipLaunchKernelGGL(gather_kernel, dim3((unsigned)blocks), dim3(kCopyThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Whole-block copies of copy-on-write [P3 sec. 3.1]: workgroup w copies
+// piece w % pieces (kCopyBlockPiece bytes) of every layer's K and V of pair
+// w / pieces.  Block contents are contiguous per tensor (all layers of a
+// block follow one another), so a piece is one contiguous byte range.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(CopyBlocksArgs a) {
+    const int64_t pair = blockIdx.x / a.pieces;
+    const int64_t piece = blockIdx.x - pair * a.pieces;
+    const int32_t sb = a.src[pair];
+    const int32_t db = a.dst[pair];
+    if (sb < 0 || sb >= a.num_blocks || db < 0 || db >= a.num_blocks || sb == db) return;
+    const int64_t start = piece * kCopyBlockPiece;
+    int64_t len = a.block_bytes - start;
+    if (len > kCopyBlockPiece) len = kCopyBlockPiece;
+    const int n = (int)(len >> 4);
+    const int64_t so = (int64_t)sb * a.block_stride + start;
+    const int64_t dof = (int64_t)db * a.block_stride + start;
+    const bool has_v = a.v != nullptr;
+    for (int base = threadIdx.x; base < n; base += kCopyThreads * kUnroll) {
+        u32x4 kk[kUnroll], vv[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int i = base + u * kCopyThreads;
+            if (i < n) {
+                kk[u] = ld16_stream(a.k + so + 16 * (int64_t)i);
+                if (has_v) vv[u] = ld16_stream(a.v + so + 16 * (int64_t)i);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int i = base + u * kCopyThreads;
+            if (i < n) {
+                st16_stream(a.k + dof + 16 * (int64_t)i, kk[u]);
+                if (has_v) st16_stream(a.v + dof + 16 * (int64_t)i, vv[u]);
+            }
+        }
+    }
+}
+
+hipError_t launch_copy_blocks(const CopyBlocksArgs &a, hipStream_t s) {
+    const int64_t blocks = a.num_pairs * a.pieces;
+    hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)blocks), dim3(kCopyThreads), 0, s, a);
     return hipGetLastError();
 }
 

@@ -40,7 +40,21 @@ int check_pool(const pkv_pool *pool, bool need_v) {
     if (row % 16) return PKV_ERR_ALIGN;
     if (!pool->k || (need_v && !pool->v)) return PKV_ERR_NULL;
     if (!aligned16(pool->k) || (pool->v && !aligned16(pool->v))) return PKV_ERR_ALIGN;
+    if (pool->block_stride != 0) {
+        if (pool->block_stride < pool->num_layers * pool->block_size * row) return PKV_ERR_SHAPE;
+        if (pool->block_stride % 16) return PKV_ERR_ALIGN;
+    }
     return PKV_OK;
+}
+
+// Bytes of one block of one tensor (all layers) and the distance between
+// consecutive blocks.
+int64_t dense_block_bytes(const pkv_pool *pool) {
+    return pool->num_layers * pool->block_size * pool->num_kv_heads * pool->head_dim *
+           elem_bytes(pool->dtype);
+}
+int64_t block_stride_of(const pkv_pool *pool) {
+    return pool->block_stride ? pool->block_stride : dense_block_bytes(pool);
 }
 
 PoolView make_view(const pkv_pool *pool, int32_t layer) {
@@ -49,7 +63,7 @@ PoolView make_view(const pkv_pool *pool, int32_t layer) {
     v.k = static_cast<const char *>(pool->k);
     v.v = static_cast<const char *>(pool->v);
     v.row_bytes = (int32_t)row;
-    v.block_stride = pool->num_layers * pool->block_size * row;
+    v.block_stride = block_stride_of(pool);
     v.layer_off = (int64_t)layer * pool->block_size * row;
     v.num_blocks = (int32_t)pool->num_blocks;
     v.lbs = ilog2(pool->block_size);
@@ -587,6 +601,77 @@ PKV_API int paged_attn_prefill(const pkv_pool *pool, int32_t layer, const void *
     a.seg_chunks = (int32_t)(max_split_tokens(pool->block_size) / kChunkTokens);
     return status_of(launch_prefill(a, pool->dtype, (int)pool->head_dim, group,
                                     static_cast<hipStream_t>(stream)));
+}
+
+PKV_API int kv_copy_blocks(const pkv_pool *pool, const int32_t *src_blocks,
+                           const int32_t *dst_blocks, int64_t num_pairs, void *stream) {
+    int st = check_pool(pool, false);
+    if (st) return st;
+    if (num_pairs < 0) return PKV_ERR_SHAPE;
+    if (num_pairs == 0) return PKV_OK;
+    if (!src_blocks || !dst_blocks) return PKV_ERR_NULL;
+    CopyBlocksArgs a{};
+    a.k = static_cast<char *>(pool->k);
+    a.v = static_cast<char *>(pool->v);
+    a.src = src_blocks;
+    a.dst = dst_blocks;
+    a.num_pairs = num_pairs;
+    a.num_blocks = pool->num_blocks;
+    a.block_bytes = dense_block_bytes(pool);
+    a.block_stride = block_stride_of(pool);
+    a.pieces = (a.block_bytes + kCopyBlockPiece - 1) / kCopyBlockPiece;
+    if (a.pieces * num_pairs > INT32_MAX) return PKV_ERR_SHAPE;
+    return status_of(launch_copy_blocks(a, static_cast<hipStream_t>(stream)));
+}
+
+namespace {
+
+// Host <-> pool block moves: runs of consecutive ids in a dense pool as one
+// copy each.
+int swap_impl(const pkv_pool *pool, const int32_t *ids, int64_t n, char *kh, char *vh,
+              bool to_host, void *stream) {
+    int st = check_pool(pool, false);
+    if (st) return st;
+    if (n < 0) return PKV_ERR_SHAPE;
+    if (n == 0) return PKV_OK;
+    if (!ids || !kh || (pool->v && !vh)) return PKV_ERR_NULL;
+    for (int64_t i = 0; i < n; ++i)
+        if (ids[i] < 0 || ids[i] >= pool->num_blocks) return PKV_ERR_BLOCK;
+    const int64_t bb = dense_block_bytes(pool);
+    const int64_t stride = block_stride_of(pool);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipMemcpyKind kind = to_host ? hipMemcpyDeviceToHost : hipMemcpyHostToDevice;
+    for (int64_t i = 0; i < n;) {
+        int64_t j = i + 1;
+        while (stride == bb && j < n && ids[j] == ids[j - 1] + 1) ++j;
+        const int64_t bytes = (j - i) * bb;
+        for (int t = 0; t < 2; ++t) {
+            char *dev = static_cast<char *>(t == 0 ? pool->k : pool->v);
+            char *host = t == 0 ? kh : vh;
+            if (!dev) continue;
+            char *d = dev + (int64_t)ids[i] * stride;
+            char *h = host + i * bb;
+            const hipError_t e = to_host ? hipMemcpyAsync(h, d, bytes, kind, s)
+                                         : hipMemcpyAsync(d, h, bytes, kind, s);
+            if (e != hipSuccess) return status_of(e);
+        }
+        i = j;
+    }
+    return PKV_OK;
+}
+
+}  // namespace
+
+PKV_API int kv_swap_out(const pkv_pool *pool, const int32_t *block_ids, int64_t n, void *k_host,
+                        void *v_host, void *stream) {
+    return swap_impl(pool, block_ids, n, static_cast<char *>(k_host), static_cast<char *>(v_host),
+                     true, stream);
+}
+
+PKV_API int kv_swap_in(const pkv_pool *pool, const int32_t *block_ids, int64_t n,
+                       const void *k_host, const void *v_host, void *stream) {
+    return swap_impl(pool, block_ids, n, static_cast<char *>(const_cast<void *>(k_host)),
+                     static_cast<char *>(const_cast<void *>(v_host)), false, stream);
 }
 
 PKV_API int kv_validate(const pkv_pool *pool, const int32_t *block_tables, int32_t bt_stride,

@@ -146,6 +146,21 @@ struct PrefillArgs {
     int32_t seg_chunks;    // most 16-position chunks staged at once
 };
 
+// Whole-block copies (copy-on-write): one workgroup per (pair, piece of
+// kCopyBlockPiece bytes of the block).
+constexpr int64_t kCopyBlockPiece = 64 * 1024;
+struct CopyBlocksArgs {
+    char *k;
+    char *v;
+    const int32_t *src;
+    const int32_t *dst;
+    int64_t num_pairs;
+    int64_t num_blocks;
+    int64_t block_bytes;   // one block of one tensor, all layers
+    int64_t block_stride;
+    int64_t pieces;        // ceil(block_bytes / kCopyBlockPiece)
+};
+
 struct ValidateArgs {
     const int32_t *block_tables;
     const int32_t *seq_lens;
@@ -167,6 +182,7 @@ hipError_t launch_append(const AppendArgs &a, hipStream_t s);
 bool prefill_supported(int dtype, int head_dim, int group);
 hipError_t launch_prefill(const PrefillArgs &a, int dtype, int head_dim, int group, hipStream_t s);
 hipError_t launch_gather(const GatherArgs &a, hipStream_t s);
+hipError_t launch_copy_blocks(const CopyBlocksArgs &a, hipStream_t s);
 hipError_t launch_validate(const ValidateArgs &a, hipStream_t s);
 // Returns hipErrorInvalidValue when (dtype, head_dim, group) is not built.
 hipError_t launch_decode(const DecodeArgs &a, int dtype, int head_dim, int group,

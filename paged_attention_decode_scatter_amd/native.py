@@ -31,6 +31,9 @@ SYMBOLS = (
     "paged_attn_decode",
     "paged_attn_decode_append",
     "paged_attn_prefill",
+    "kv_copy_blocks",
+    "kv_swap_out",
+    "kv_swap_in",
     "kv_validate",
     "pkv_status_string",
 )
@@ -57,6 +60,7 @@ class PkvPool(ctypes.Structure):
         ("head_dim", ctypes.c_int64),
         ("dtype", ctypes.c_int32),
         ("reserved", ctypes.c_int32),
+        ("block_stride", ctypes.c_int64),
     ]
 
 
@@ -99,6 +103,12 @@ def load_library(path: str = LIB_PATH):
     lib.paged_attn_decode.restype = ctypes.c_int
     lib.paged_attn_decode.argtypes = [pp, i32, p, i32, p, i32, p, p, i32, i32, f32, i32, p, p,
                                       sz, p]
+    lib.kv_copy_blocks.restype = ctypes.c_int
+    lib.kv_copy_blocks.argtypes = [pp, p, p, i64, p]
+    lib.kv_swap_out.restype = ctypes.c_int
+    lib.kv_swap_out.argtypes = [pp, p, i64, p, p, p]
+    lib.kv_swap_in.restype = ctypes.c_int
+    lib.kv_swap_in.argtypes = [pp, p, i64, p, p, p]
     lib.kv_validate.restype = ctypes.c_int
     lib.kv_validate.argtypes = [pp, p, i32, p, p, i32, i32, p, i64, p, p]
     lib.pkv_status_string.restype = ctypes.c_char_p
@@ -137,19 +147,44 @@ def _need(t, dtype, name):
 
 def make_pool(k_pool, v_pool=None) -> PkvPool:
     """Describe a (num_blocks, num_layers, block_size, num_kv_heads, head_dim)
-    K/V pool pair for the C ABI."""
+    K/V pool pair for the C ABI.  Each tensor is dense within a block; the
+    block (first) dimension may have a larger stride, as the K and V views
+    kv[:, 0] and kv[:, 1] of a combined (num_blocks, 2, num_layers,
+    block_size, num_kv_heads, head_dim) cache have (see combined_views)."""
     if k_pool.dim() != 5:
         raise ValueError("pool must be (num_blocks, num_layers, block_size, num_kv_heads, head_dim)")
     if k_pool.dtype not in _DTYPES:
         raise TypeError(f"pool dtype must be float32 or bfloat16, got {k_pool.dtype}")
-    _need(k_pool, k_pool.dtype, "k_pool")
-    if v_pool is not None:
-        _need(v_pool, k_pool.dtype, "v_pool")
-        if v_pool.shape != k_pool.shape:
-            raise ValueError("k_pool and v_pool shapes differ")
     nb, nl, bs, h, d = k_pool.shape
+    inner = (bs * h * d, h * d, d, 1)
+    dense = nl * bs * h * d
+    for t, name in ((k_pool, "k_pool"), (v_pool, "v_pool")):
+        if t is None:
+            continue
+        if t.dtype != k_pool.dtype:
+            raise TypeError(f"{name} must be {k_pool.dtype}, got {t.dtype}")
+        if t.shape != k_pool.shape:
+            raise ValueError("k_pool and v_pool shapes differ")
+        if tuple(t.stride()[1:]) != inner or (nb > 1 and t.stride(0) < dense):
+            raise ValueError(f"{name} must be dense within a block (only the block stride may "
+                             "exceed the block size)")
+    if v_pool is not None and nb > 1 and v_pool.stride(0) != k_pool.stride(0):
+        raise ValueError("k_pool and v_pool block strides differ")
+    stride = k_pool.stride(0) if nb > 1 else dense
+    block_stride = 0 if stride == dense else stride * k_pool.element_size()
     return PkvPool(k_pool.data_ptr(), None if v_pool is None else v_pool.data_ptr(),
-                   nb, nl, bs, h, d, _DTYPES[k_pool.dtype], 0)
+                   nb, nl, bs, h, d, _DTYPES[k_pool.dtype], 0, block_stride)
+
+
+def combined_views(kv):
+    """K and V views of a combined cache (num_blocks, 2, num_layers,
+    block_size, num_kv_heads, head_dim): kv[:, 0] and kv[:, 1], each with a
+    block stride of two dense blocks.  Every entry point takes them as its
+    k_pool / v_pool."""
+    if kv.dim() != 6 or kv.shape[1] != 2 or not kv.is_contiguous():
+        raise ValueError("combined cache must be contiguous "
+                         "(num_blocks, 2, num_layers, block_size, num_kv_heads, head_dim)")
+    return kv[:, 0], kv[:, 1]
 
 
 def kv_slot_mapping(block_tables, offsets, token_seq, token_pos, block_size, out=None):
@@ -330,6 +365,79 @@ def paged_attn_prefill(k_pool, v_pool, layer, q, q_start, block_tables, seq_lens
     return out
 
 
+def kv_copy_blocks(k_pool, v_pool, src_blocks, dst_blocks):
+    """Copy every layer of K (and V, if given) of block src_blocks[i] to
+    block dst_blocks[i] (device int32; ids outside the pool skip the pair)."""
+    pool = make_pool(k_pool, v_pool)
+    _need(src_blocks, torch.int32, "src_blocks")
+    _need(dst_blocks, torch.int32, "dst_blocks")
+    if src_blocks.shape != dst_blocks.shape or src_blocks.dim() != 1:
+        raise ValueError("src_blocks and dst_blocks must be 1-D of one length")
+    st = load_library().kv_copy_blocks(ctypes.byref(pool), _ptr(src_blocks), _ptr(dst_blocks),
+                                       src_blocks.shape[0], _stream(k_pool))
+    _check("kv_copy_blocks", st)
+
+
+def _host_ids(block_ids):
+    import numpy as np
+
+    ids = np.ascontiguousarray(
+        block_ids.cpu().numpy() if isinstance(block_ids, torch.Tensor) else block_ids,
+        dtype=np.int32)
+    if ids.ndim != 1:
+        raise ValueError("block_ids must be 1-D")
+    return ids
+
+
+def _host_blocks(t, k_pool, n, name):
+    shape = (n,) + tuple(k_pool.shape[1:])
+    if t.device.type != "cpu" or t.dtype != k_pool.dtype or not t.is_contiguous() \
+            or tuple(t.shape) != shape:
+        raise ValueError(f"{name} must be a contiguous host {k_pool.dtype} tensor of shape {shape}")
+
+
+def kv_swap_out(k_pool, v_pool, block_ids, k_host=None, v_host=None, pin=True):
+    """Copy whole blocks (host int32 ids) from the pool to host tensors of
+    shape (n, num_layers, block_size, num_kv_heads, head_dim), allocated
+    (pinned unless pin=False) when not given.  With pinned memory the copies
+    are asynchronous on the current stream: synchronize before reading."""
+    ids = _host_ids(block_ids)
+    n = ids.shape[0]
+    shape = (n,) + tuple(k_pool.shape[1:])
+    if k_host is None:
+        k_host = torch.empty(shape, dtype=k_pool.dtype, pin_memory=pin)
+    if v_pool is not None and v_host is None:
+        v_host = torch.empty(shape, dtype=k_pool.dtype, pin_memory=pin)
+    _host_blocks(k_host, k_pool, n, "k_host")
+    if v_pool is not None:
+        _host_blocks(v_host, k_pool, n, "v_host")
+    pool = make_pool(k_pool, v_pool)
+    st = load_library().kv_swap_out(ctypes.byref(pool), ids.ctypes.data, n,
+                                    ctypes.c_void_p(k_host.data_ptr()),
+                                    None if v_pool is None else ctypes.c_void_p(v_host.data_ptr()),
+                                    _stream(k_pool))
+    _check("kv_swap_out", st)
+    return k_host, v_host
+
+
+def kv_swap_in(k_pool, v_pool, block_ids, k_host, v_host=None):
+    """Copy host blocks (as kv_swap_out returns them) into pool blocks
+    block_ids (host int32)."""
+    ids = _host_ids(block_ids)
+    n = ids.shape[0]
+    _host_blocks(k_host, k_pool, n, "k_host")
+    if v_pool is not None:
+        if v_host is None:
+            raise ValueError("v_host is required with v_pool")
+        _host_blocks(v_host, k_pool, n, "v_host")
+    pool = make_pool(k_pool, v_pool)
+    st = load_library().kv_swap_in(ctypes.byref(pool), ids.ctypes.data, n,
+                                   ctypes.c_void_p(k_host.data_ptr()),
+                                   None if v_pool is None else ctypes.c_void_p(v_host.data_ptr()),
+                                   _stream(k_pool))
+    _check("kv_swap_in", st)
+
+
 def kv_validate(k_pool, block_tables, seq_lens, offsets, max_seq_len=-1, slot_mapping=None,
                 counter=None):
     """Number of caller-contract violations (synchronises to read it)."""
@@ -352,7 +460,7 @@ def kv_validate(k_pool, block_tables, seq_lens, offsets, max_seq_len=-1, slot_ma
 # ---------------------------------------------------------------------------
 BM_SYMBOLS = (
     "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_can_allocate", "pkv_bm_allocate", "pkv_bm_share",
-    "pkv_bm_append_slot", "pkv_bm_append_slots", "pkv_bm_free", "pkv_bm_inc_ref",
+    "pkv_bm_append_slot", "pkv_bm_append_slots", "pkv_bm_free", "pkv_bm_cow", "pkv_bm_inc_ref",
     "pkv_bm_dec_ref", "pkv_bm_seq_len", "pkv_bm_max_blocks", "pkv_bm_tables",
     "pkv_bm_free_queue", "pkv_bm_ref_counts", "pkv_bm_get_stats",
 )
@@ -386,6 +494,8 @@ def _bm_lib():
     lib.pkv_bm_append_slots.argtypes = [p, p, i32, p]
     lib.pkv_bm_free.restype = ctypes.c_int
     lib.pkv_bm_free.argtypes = [p, i64]
+    lib.pkv_bm_cow.restype = ctypes.c_int
+    lib.pkv_bm_cow.argtypes = [p, i64, i32, p, p]
     lib.pkv_bm_inc_ref.restype = ctypes.c_int
     lib.pkv_bm_inc_ref.argtypes = [p, i32]
     lib.pkv_bm_dec_ref.restype = ctypes.c_int
@@ -471,6 +581,17 @@ class BlockManager:
 
     def free(self, seq):
         self._ok("pkv_bm_free", self._lib.pkv_bm_free(self._h, seq))
+
+    def cow(self, seq, index):
+        """Copy-on-write of table entry `index` of seq: (src, dst) block ids
+        -- equal when the block is not shared (write in place), else dst is
+        a fresh block now in the table and the contents of src must be
+        copied to it (kv_copy_blocks).  False, changing nothing, when no
+        block is free."""
+        src, dst = ctypes.c_int32(-1), ctypes.c_int32(-1)
+        st = self._ok("pkv_bm_cow", self._lib.pkv_bm_cow(self._h, seq, index, ctypes.byref(src),
+                                                          ctypes.byref(dst)))
+        return False if st == NO_SPACE else (src.value, dst.value)
 
     def inc_ref(self, block):
         self._ok("pkv_bm_inc_ref", self._lib.pkv_bm_inc_ref(self._h, block))

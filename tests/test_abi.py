@@ -33,7 +33,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == len(set(names)) == 28
+    assert len(names) == len(set(names)) == 32
     assert set(names) == set(N.SYMBOLS) | set(N.BM_SYMBOLS)
     for n in names:
         assert hasattr(lib, n), n
@@ -54,8 +54,8 @@ def test_status_strings(lib):
     assert N.status_string(12345) == "unknown status"
 
 
-def pool(k=0x1000, v=0x2000, nb=16, nl=2, bs=16, h=8, d=128, dtype=1, reserved=0):
-    return N.PkvPool(k, v, nb, nl, bs, h, d, dtype, reserved)
+def pool(k=0x1000, v=0x2000, nb=16, nl=2, bs=16, h=8, d=128, dtype=1, reserved=0, stride=0):
+    return N.PkvPool(k, v, nb, nl, bs, h, d, dtype, reserved, stride)
 
 
 A = 0x10000  # an aligned fake device address; never dereferenced on these paths
@@ -262,3 +262,71 @@ def test_validate_argument_checks(lib):
     assert f(by(pool(bs=6)), A, 4, A, A, 2, 10, A, 3, A, None) == SHAPE
     assert f(by(pool()), None, 4, A, A, 2, 10, A, 3, A, None) == NULL
     assert f(by(pool()), A, 4, A, A, 2, 10, None, 3, A, None) == NULL
+
+
+def test_block_stride_checks(lib):
+    """A nonzero block stride is at least one dense block (2 layers x 16 x
+    8 x 128 bf16 = 64 KiB here) and a multiple of 16 bytes."""
+    f = lib.kv_scatter
+    by = ctypes.byref
+    dense = 2 * 16 * 8 * 128 * 2
+    assert f(by(pool(stride=dense - 16)), 0, A, A, A, 4, None) == SHAPE
+    assert f(by(pool(stride=dense + 8)), 0, A, A, A, 4, None) == ALIGN
+    assert f(by(pool(stride=2 * dense)), 0, A, A, A, 0, None) == OK
+    assert f(by(pool(stride=dense)), 0, A, A, A, 0, None) == OK
+
+
+def test_copy_blocks_argument_checks(lib):
+    f = lib.kv_copy_blocks
+    by = ctypes.byref
+    assert f(None, A, A, 3, None) == NULL
+    assert f(by(pool(k=None)), A, A, 3, None) == NULL
+    assert f(by(pool(dtype=5)), A, A, 3, None) == DTYPE
+    assert f(by(pool(bs=3)), A, A, 3, None) == SHAPE
+    assert f(by(pool()), A, A, -1, None) == SHAPE
+    assert f(by(pool()), A, A, 0, None) == OK
+    assert f(by(pool()), None, A, 3, None) == NULL
+    assert f(by(pool()), A, None, 3, None) == NULL
+    assert f(by(pool(stride=100)), A, A, 3, None) == SHAPE
+
+
+def test_swap_argument_checks(lib):
+    """Host block ids are checked before any copy: one id outside
+    [0, num_blocks) rejects the whole call."""
+    import numpy as np
+
+    by = ctypes.byref
+    good = np.array([0, 1, 15], np.int32)
+    for f in (lib.kv_swap_out, lib.kv_swap_in):
+        for bad in ([0, 16], [-1], [3, 2, 99]):
+            ids = np.array(bad, np.int32)
+            assert f(by(pool()), ids.ctypes.data, len(bad), A, A, None) == -11
+        assert f(by(pool()), good.ctypes.data, 0, A, A, None) == OK
+        assert f(by(pool()), good.ctypes.data, -1, A, A, None) == SHAPE
+        assert f(by(pool()), None, 3, A, A, None) == NULL
+        assert f(by(pool()), good.ctypes.data, 3, None, A, None) == NULL
+        assert f(by(pool()), good.ctypes.data, 3, A, None, None) == NULL   # V pool set, no V buffer
+        assert f(None, good.ctypes.data, 3, A, A, None) == NULL
+        assert f(by(pool(dtype=9)), good.ctypes.data, 3, A, A, None) == DTYPE
+
+
+def test_make_pool_combined_layout():
+    """The K and V views of a combined (num_blocks, 2, layers, block_size,
+    heads, head_dim) cache: V starts one dense block after K, and both step
+    two dense blocks per block."""
+    import torch
+
+    kv = torch.zeros(5, 2, 3, 16, 2, 64, dtype=torch.bfloat16)
+    k, v = N.combined_views(kv)
+    p = N.make_pool(k, v)
+    dense = 3 * 16 * 2 * 64 * 2
+    assert p.block_stride == 2 * dense
+    assert p.v - p.k == dense
+    assert (p.num_blocks, p.num_layers, p.block_size, p.num_kv_heads, p.head_dim) == (5, 3, 16, 2, 64)
+    assert N.make_pool(torch.zeros(5, 3, 16, 2, 64, dtype=torch.bfloat16)).block_stride == 0
+    with pytest.raises(ValueError):
+        N.make_pool(kv[:, :, 0])                      # not dense within a block
+    with pytest.raises(ValueError):
+        N.make_pool(k, torch.zeros(5, 3, 16, 2, 64, dtype=torch.bfloat16))   # strides differ
+    with pytest.raises(ValueError):
+        N.combined_views(torch.zeros(5, 3, 3, 16, 2, 64))

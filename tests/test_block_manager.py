@@ -327,6 +327,11 @@ def test_native_meets_the_pins(pin):
     pin(N.BlockManager)
 
 
+@pytest.mark.parametrize("pin", COW_PINS, ids=lambda f: f.__name__)
+def test_native_meets_the_cow_pins(pin):
+    pin(N.BlockManager)
+
+
 def state(m, seqs):
     tabs = {q: m.table(q) for q in sorted(seqs)}
     st = m.stats()
@@ -338,8 +343,8 @@ def state(m, seqs):
 
 @pytest.mark.parametrize("seed", range(12))
 def test_native_matches_oracle_on_random_operations(seed):
-    """allocate (with offsets), share, append_slot, free, inc_ref / dec_ref
-    in random order, driven to shortage; after every operation the free
+    """allocate (with offsets), share, append_slot, copy-on-write, free,
+    inc_ref / dec_ref in random order, driven to shortage; after every operation the free
     queue, the reference counts, every table and length, and the statistics
     are identical, and so are the answers (success, slots)."""
     rng = random.Random(seed)
@@ -367,9 +372,15 @@ def test_native_matches_oracle_on_random_operations(seed):
                 n.share(src, next_id, j)
                 live.add(next_id)
                 next_id += 1
-        elif op < 0.75:
+        elif op < 0.65:
             q = rng.choice(sorted(live))
             assert o.append_slot(q) == n.append_slot(q)
+        elif op < 0.75:
+            q = rng.choice(sorted(live))
+            k = len(o.table(q))
+            if k:
+                j = rng.randrange(k)
+                assert o.cow(q, j) == n.cow(q, j)
         elif op < 0.9:
             q = rng.choice(sorted(live))
             o.free(q)
@@ -421,6 +432,13 @@ def test_native_argument_errors():
     with pytest.raises(N.PagedKVError):
         m.share(0, 1, 2)                  # more blocks than src holds
     assert m.allocate(1, 100) is False    # short: not an error
+    with pytest.raises(N.PagedKVError):
+        m.cow(5, 0)                       # unknown sequence
+    with pytest.raises(N.PagedKVError):
+        m.cow(0, 1)                       # past the table
+    with pytest.raises(N.PagedKVError):
+        m.cow(0, -1)
+    assert m.cow(0, 0) == (m.table(0)[0],) * 2
     lib = N.load_library()
     assert lib.pkv_bm_create(0, 16) is None
     assert N.status_string(N.NO_SPACE) == "too few free blocks (nothing changed)"
