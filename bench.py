@@ -291,6 +291,76 @@ def prefill_ops(w_dec, N, W, reps=64):
     }
 
 
+def block_ops(w_dec, N, pairs=64, sets=4, reps=32, swap_blocks=64, swap_reps=6):
+    """Whole-block copies (the copy of copy-on-write) and swaps in the decode
+    batch's pool: `sets` disjoint sets of `pairs` (source: a block the
+    tables use, destination: one they do not), issued back to back with the
+    set rotated; swap out / in of `swap_blocks` blocks to / from pinned host
+    memory (runs of consecutive ids, one copy each)."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    dev = w_dec.k_pool.device
+    nb = w_dec.k_pool.shape[0]
+    bt = w_dec.block_tables.cpu()
+    used = torch.unique(bt[bt >= 0]).numpy()
+    free = np.setdiff1d(np.arange(nb), used)
+    rng = np.random.default_rng(7)
+    src = rng.choice(used, size=(sets, pairs), replace=len(used) < sets * pairs)
+    dst = rng.choice(free, size=(sets, pairs), replace=False)
+    src_d = [torch.from_numpy(src[i].astype(np.int32)).to(dev) for i in range(sets)]
+    dst_d = [torch.from_numpy(dst[i].astype(np.int32)).to(dev) for i in range(sets)]
+    lib = N.load_library()
+    pool = N.make_pool(w_dec.k_pool, w_dec.v_pool)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    block_bytes = w_dec.k_pool[0].numel() * w_dec.k_pool.element_size()
+    args = [(ctypes.byref(pool), ctypes.c_void_p(src_d[i].data_ptr()),
+             ctypes.c_void_p(dst_d[i].data_ptr()), pairs, stream) for i in range(sets)]
+    for i in range(3):
+        if lib.kv_copy_blocks(*args[i % sets]):
+            raise RuntimeError("kv_copy_blocks failed")
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(reps):
+        lib.kv_copy_blocks(*args[i % sets])
+    b.record()
+    torch.cuda.synchronize()
+    t_c = a.elapsed_time(b) / reps
+    copy_bytes = pairs * block_bytes * 2 * 2     # K and V, read + write
+
+    ids = free[:swap_blocks].astype(np.int32)
+    kh = torch.empty((swap_blocks,) + tuple(w_dec.k_pool.shape[1:]), dtype=w_dec.dtype,
+                     pin_memory=True)
+    vh = torch.empty_like(kh, pin_memory=True)
+    swap_bytes = swap_blocks * block_bytes * 2
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(swap_reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / swap_reps
+
+    t_out = timed(lambda: N.kv_swap_out(w_dec.k_pool, w_dec.v_pool, ids, kh, vh))
+    t_in = timed(lambda: N.kv_swap_in(w_dec.k_pool, w_dec.v_pool, ids, kh, vh))
+    return {
+        "copy_blocks": {"pairs": pairs, "block_bytes_per_tensor": block_bytes,
+                        "bytes": copy_bytes, "ms": t_c, "GB/s": copy_bytes / t_c / 1e6,
+                        "timing": f"{reps} back-to-back C-ABI calls over {sets} disjoint pair "
+                                  "sets, one event pair around them"},
+        "swap_out": {"blocks": swap_blocks, "bytes": swap_bytes, "ms": t_out,
+                     "GB/s": swap_bytes / t_out / 1e6, "host": "pinned"},
+        "swap_in": {"blocks": swap_blocks, "bytes": swap_bytes, "ms": t_in,
+                    "GB/s": swap_bytes / t_in / 1e6, "host": "pinned"},
+    }
+
+
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "decode_batch_traffic.json")
 DECODE_SOURCES = [os.path.join(ROOT, "paged_attention_decode_scatter_amd", "csrc", f)
                   for f in ("kernels_decode.hip", "attn_common.h", "pagedkv_api.hip", "pkv_internal.h")]
@@ -600,6 +670,8 @@ def main():
     if not args.no_ops:
         log("scatter/gather on the prefill shape")
         result["ops"] = prefill_ops(w, N, W)
+        log("block copies and swaps")
+        result["ops"].update(block_ops(w, N))
         log("decode on the prefix-sharing and long-context batches")
         result["other_decode"] = other_decode_configs(w, N, W)
         log("host block manager")
