@@ -30,3 +30,4 @@ from .oracle import (  # noqa: F401
     swap_out,
 )
 from .block_manager import BlockManagerOracle  # noqa: F401
+from . import quant  # noqa: F401
