@@ -18,7 +18,8 @@
  *   (num_blocks, num_layers, block_size, num_kv_heads, head_dim) array in
  *   device memory.  One "row" is the num_kv_heads*head_dim elements of one
  *   token at one layer.  block_size must be a power of two.
- * - Element types: PKV_F32 (float) or PKV_BF16 (bfloat16 bit patterns).
+ * - Element types: PKV_F32 (float) or PKV_BF16 (bfloat16 bit patterns),
+ *   or a quantised pool, PKV_I8 (see "Quantised pools" below).
  * - A block table is a row of int32 physical block ids in logical order
  *   [P3 sec. 2.2]; tables are stored (num_seqs, bt_stride) row-major.  Each
  *   sequence also has a first-block start offset in [0, block_size) (prefix
@@ -57,7 +58,7 @@ extern "C" {
 #define PKV_API __attribute__((visibility("default")))
 
 /* element types */
-enum { PKV_F32 = 0, PKV_BF16 = 1 };
+enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_I8 = 2 };
 
 /* status codes */
 enum {
@@ -88,7 +89,25 @@ enum {
  * layout (num_blocks, 2, num_layers, block_size, num_kv_heads, head_dim)
  * of the same section is k = its base, v = base + one dense block,
  * block_stride = two dense blocks.  A nonzero block_stride must be a
- * multiple of 16 and at least one dense block. */
+ * multiple of 16 and at least one dense block.
+ *
+ * Quantised pools (dtype PKV_I8) [P3 sec. 6: quantised KV, int8 / int4, as
+ * the next compression step of a paged cache; the pages give no method, so
+ * this is the plain symmetric reading]: k / v hold int8 codes in the layout
+ * above, and k_scale / v_scale (16-byte aligned, device) one float scale
+ * per (token, kv head) row, laid out dense as
+ * (num_blocks, num_layers, num_kv_heads, block_size), so the scales of one
+ * head's tokens in a block are contiguous.  A row x (head_dim values) is
+ * stored as scale s = max|x| / 127 and codes round-half-even(x / s),
+ * clamped to [-127, 127] (s = 0 and codes 0 for a zero row), both
+ * computed in IEEE float32; its value is code * s.  The rows written into
+ * (k_src / v_src) and the queries and outputs of decode are bfloat16.
+ * Entry points that take a quantised pool: kv_scatter, kv_append
+ * (quantise on write), kv_gather (writes bf16(code * s)),
+ * paged_attn_decode (split schedule; dequantises inside the kernel),
+ * kv_copy_blocks and kv_swap_out / kv_swap_in (codes and scales).  The
+ * others return PKV_ERR_UNSUPPORTED for it.  k_scale / v_scale are ignored
+ * for float pools. */
 typedef struct pkv_pool {
     void *k;
     void *v;
@@ -100,6 +119,8 @@ typedef struct pkv_pool {
     int32_t dtype;
     int32_t reserved;
     int64_t block_stride;
+    void *k_scale;
+    void *v_scale;
 } pkv_pool;
 
 /*
@@ -130,9 +151,10 @@ PKV_API int kv_slot_mapping(const int32_t *block_tables, int32_t bt_stride,
  * [P1 "relation to step14_1": kv_pool[blocks, slots] = K; P2 sec. 2.2:
  * writes indexed (block_id, layer, offset inside block), slot -1 = padding].
  *
- *   k_src, v_src  device [num_tokens, num_kv_heads, head_dim], pool dtype,
- *                 contiguous.  v_src may be NULL to write K only (then the
- *                 pool's v may be NULL too).
+ *   k_src, v_src  device [num_tokens, num_kv_heads, head_dim], pool dtype
+ *                 (bfloat16 for a quantised pool, each (token, kv head)
+ *                 row quantised on write), contiguous.  v_src may be NULL
+ *                 to write K only (then the pool's v may be NULL too).
  *   slot_mapping  device int64 [num_tokens]; row i goes to block slot/bs,
  *                 slot slot%bs.  Negative or out-of-pool slots are skipped.
  * Only the addressed rows of `layer` are written; every other byte of the
@@ -187,6 +209,7 @@ PKV_API int kv_append(const pkv_pool *pool, int32_t layer,
  *   out_rows       rows k_out (and v_out) can hold; a row that would land
  *                  outside [0, out_rows) is not written.
  * A token whose table entry is missing or out of range reads as a zero row.
+ * A quantised pool gathers bfloat16 rows bf16(code * scale).
  * Errors: PKV_ERR_NULL, _DTYPE, _SHAPE, _LAYER, _ALIGN, _LAUNCH.
  */
 PKV_API int kv_gather(const pkv_pool *pool, int32_t layer,
@@ -282,7 +305,9 @@ PKV_API size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_kv
  *                 leaves its counters zero again, so a workspace is reused
  *                 as is.  Calls that share a workspace must not overlap
  *                 (issue them on one stream).
- * Supported: head_dim in {64, 128}, G in {1, 2, 4, 8}.
+ * Supported: head_dim in {64, 128}, G in {1, 2, 4, 8}.  A quantised pool
+ * takes bfloat16 q and out, runs the split schedule (PKV_SPLIT_BALANCED is
+ * PKV_ERR_UNSUPPORTED) and attends to the stored values code * scale.
  * Errors: PKV_ERR_NULL, _DTYPE, _SHAPE, _LAYER, _ALIGN, _WORKSPACE,
  * _UNSUPPORTED, _LAUNCH.
  */
@@ -316,6 +341,8 @@ PKV_API int paged_attn_decode(const pkv_pool *pool, int32_t layer,
  *   k_new, v_new  device [num_seqs, num_kv_heads, head_dim], pool dtype,
  *                 16-byte aligned; both required
  *   everything else as for paged_attn_decode (same workspace size)
+ * Float pools only (PKV_ERR_UNSUPPORTED for a quantised pool: write with
+ * kv_append, then call paged_attn_decode).
  * Errors: as paged_attn_decode; PKV_ERR_NULL when k_new or v_new is NULL.
  */
 PKV_API int paged_attn_decode_append(const pkv_pool *pool, int32_t layer,
@@ -347,7 +374,8 @@ PKV_API int paged_attn_decode_append(const pkv_pool *pool, int32_t layer,
  *   max_q_len     host bound on every n_s (rows of a sequence past it are
  *                 left unwritten)
  *   block_tables, seq_lens, offsets  as for paged_attn_decode
- * Supported: head_dim in {64, 128}, G in {1, 2, 4, 8}.
+ * Supported: head_dim in {64, 128}, G in {1, 2, 4, 8}; float pools only
+ * (PKV_ERR_UNSUPPORTED for a quantised pool).
  * Errors: PKV_ERR_NULL, _DTYPE, _SHAPE, _LAYER, _ALIGN, _UNSUPPORTED, _LAUNCH.
  */
 PKV_API int paged_attn_prefill(const pkv_pool *pool, int32_t layer,
@@ -359,7 +387,8 @@ PKV_API int paged_attn_prefill(const pkv_pool *pool, int32_t layer,
 
 /*
  * kv_copy_blocks -- whole-block copies: for i < num_pairs, every layer of K
- * and of V of block src_blocks[i] is copied to block dst_blocks[i].  This
+ * and of V of block src_blocks[i] is copied to block dst_blocks[i] (codes
+ * and scales for a quantised pool).  This
  * is the copy of copy-on-write [P3 sec. 3.1: vLLM shares blocks by
  * copy-on-write + ref_count; sec. 2.4 ref_count]: before a sequence writes
  * into a block other tables also hold, it takes a new block (pkv_bm_cow)
@@ -386,7 +415,10 @@ PKV_API int kv_copy_blocks(const pkv_pool *pool, const int32_t *src_blocks,
  *   block_ids     HOST int32 [n], each in [0, num_blocks), else
  *                 PKV_ERR_BLOCK before any copy
  *   k_host, v_host  host buffers of n dense blocks each; v_host is used
- *                 (and required) when pool->v is set.  Pinned host memory
+ *                 (and required) when pool->v is set.  For a quantised
+ *                 pool each buffer holds the n blocks' codes, then the n
+ *                 blocks' scales (num_layers * num_kv_heads * block_size
+ *                 floats per block).  Pinned host memory
  *                 (hipHostMalloc, torch pin_memory) keeps the copies
  *                 asynchronous on `stream`; pageable memory works, but the
  *                 copies then finish before the call returns.

@@ -275,6 +275,191 @@ hipError_t launch_gather(const GatherArgs &a, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
+// Quantised pools [P3 sec. 6 names quantised KV; the reading: one float32
+// scale s = max|x| / 127 per (token, kv head) row, codes
+// round-half-even(x / s) clamped to [-127, 127], all in IEEE float32].
+//
+// Quantising scatter / append: LPH = D/8 lanes hold one (token, head) row,
+// 8 bf16 values each; the row's max |x| is reduced over those lanes, and
+// each lane stores its 8 codes (8 bytes); the lane with piece 0 stores the
+// scale.  The slot is given (kv_scatter) or computed as the append does.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+__device__ __forceinline__ uint32_t quant_code(float x, float s) {
+    const float c = s > 0.0f ? fminf(fmaxf(__builtin_rintf(__fdiv_rn(x, s)), -127.0f), 127.0f) : 0.0f;
+    return (uint32_t)(int32_t)c & 0xffu;
+}
+
+// 8 bf16 values (one 16-byte piece) -> 8 int8 codes (two words).
+__device__ __forceinline__ uint2 quant_piece(u32x4 x, float s) {
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+    uint32_t c[2] = {0, 0};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = quant_code(bf16_to_f32(w[i] & 0xffffu), s);
+        const uint32_t hi = quant_code(bf16_to_f32(w[i] >> 16), s);
+        c[i >> 1] |= (lo | (hi << 8)) << (16 * (i & 1));
+    }
+    return make_uint2(c[0], c[1]);
+}
+
+__device__ __forceinline__ float piece_amax(u32x4 x) {
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        m = fmaxf(m, fmaxf(fabsf(bf16_to_f32(w[i] & 0xffffu)), fabsf(bf16_to_f32(w[i] >> 16))));
+    return m;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void scatter_q8_kernel(ScatterQ8Args a) {
+    constexpr int LPH = D / 8;       // lanes per (token, head) row
+    constexpr int RPW = 256 / LPH;   // rows per workgroup
+    const int p = threadIdx.x % LPH;
+    const int64_t H = a.num_kv_heads;
+    const int64_t i = (int64_t)blockIdx.x * RPW + threadIdx.x / LPH;
+    const bool live = i < a.num_tokens * H;
+    const int64_t tok = live ? i / H : 0;
+    const int64_t h = live ? i - tok * H : 0;
+    const int64_t bsm = (1ll << a.lbs) - 1;
+    int64_t slot = -1;
+    if (live) {
+        if (a.slots) {
+            slot = a.slots[tok];
+        } else {
+            const int32_t seq = a.token_seq[tok];
+            if (seq >= 0 && seq < a.num_seqs) {
+                const int64_t pos = a.token_pos[tok];
+                const int64_t q = (int64_t)a.offsets[seq] + pos;
+                const int64_t j = q >> a.lbs;
+                if (pos >= 0 && q >= 0 && j < a.bt_stride) {
+                    const int32_t b = a.block_tables[(int64_t)seq * a.bt_stride + j];
+                    if (b >= 0) slot = ((int64_t)b << a.lbs) | (q & bsm);
+                }
+            }
+            if (h == 0 && p == 0 && a.slots_out) a.slots_out[tok] = slot;
+        }
+    }
+    const bool ok = slot >= 0 && slot < a.total_slots;
+    const bool has_v = a.v_src != nullptr;
+    const int64_t src = (tok * H + h) * (int64_t)(2 * D) + 16 * p;
+    u32x4 kx = {0, 0, 0, 0}, vx = {0, 0, 0, 0};
+    if (ok) {
+        kx = ld16_stream(a.k_src + src);
+        if (has_v) vx = ld16_stream(a.v_src + src);
+    }
+    // every lane takes part in the reductions (rows are LPH-lane aligned)
+    float km = piece_amax(kx), vm = piece_amax(vx);
+#pragma unroll
+    for (int m = 1; m < LPH; m <<= 1) {
+        km = fmaxf(km, __shfl_xor(km, m));
+        vm = fmaxf(vm, __shfl_xor(vm, m));
+    }
+    if (!ok) return;
+    const float ks = __fdiv_rn(km, 127.0f), vs = __fdiv_rn(vm, 127.0f);
+    const int64_t b = slot >> a.lbs, r = slot & bsm;
+    const int64_t dst = b * a.block_stride + a.layer_off + r * (H * D) + h * D + 8 * p;
+    *reinterpret_cast<uint2 *>(a.kpool + dst) = quant_piece(kx, ks);
+    if (has_v) *reinterpret_cast<uint2 *>(a.vpool + dst) = quant_piece(vx, vs);
+    if (p == 0) {
+        const int64_t so = b * a.sc_block + (h << a.lbs) + r;
+        a.ks[so] = ks;
+        if (has_v) a.vs[so] = vs;
+    }
+}
+
+hipError_t launch_scatter_q8(const ScatterQ8Args &a, hipStream_t s) {
+    const int64_t rows = a.num_tokens * a.num_kv_heads;
+    const int64_t rpw = 256 / (a.head_dim / 8);
+    const dim3 grid((unsigned)((rows + rpw - 1) / rpw));
+    if (a.head_dim == 128)
+        hipLaunchKernelGGL(scatter_q8_kernel<128>, grid, dim3(256), 0, s, a);
+    else if (a.head_dim == 64)
+        hipLaunchKernelGGL(scatter_q8_kernel<64>, grid, dim3(256), 0, s, a);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+// Dequantising gather: each lane turns one 16-code piece of a row into 16
+// bf16 values bf16(code * scale) (float32 product, nearest-even).  Tokens
+// whose table entry is missing or out of range give zero rows.
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+template <int D>
+__global__ __launch_bounds__(kCopyThreads) void gather_q8_kernel(GatherArgs a) {
+    const int seq = blockIdx.x / a.tiles_per_seq;
+    const int tile = blockIdx.x - seq * a.tiles_per_seq;
+    const int64_t len = a.seq_lens[seq];
+    const int64_t t0 = (int64_t)tile * a.tok_per_wg;
+    if (t0 >= len) return;
+    const int64_t left = len - t0;
+    const int ntok = left < a.tok_per_wg ? (int)left : a.tok_per_wg;
+    const int cpr = a.pool.row_bytes >> 4;  // 16-code pieces per row
+    const int64_t off = a.offsets[seq];
+    const int64_t row0 = a.out_row_start[seq];
+    const int64_t bsm = (1ll << a.pool.lbs) - 1;
+    const bool has_v = a.v_out != nullptr;
+    for (int idx = threadIdx.x; idx < ntok * cpr; idx += kCopyThreads) {
+        const int tt = idx / cpr;
+        const int ch = idx - tt * cpr;
+        const int64_t t = t0 + tt;
+        const int64_t orow = row0 + t;
+        if (orow < 0 || orow >= a.out_rows) continue;
+        const int64_t p = off + t;
+        const int64_t j = p >> a.pool.lbs;
+        const int32_t b = j < a.bt_stride ? a.block_tables[(int64_t)seq * a.bt_stride + j] : -1;
+        const bool okb = b >= 0 && b < a.pool.num_blocks;
+        const int64_t h = (16 * ch) / D;
+        u32x4 o[2][2] = {};
+        for (int tsr = 0; tsr < (has_v ? 2 : 1); ++tsr) {
+            if (!okb) break;
+            const char *pool = tsr ? a.pool.v : a.pool.k;
+            const float *sc = tsr ? a.pool.vs : a.pool.ks;
+            const u32x4 c = ld16(pool + (int64_t)b * a.pool.block_stride + a.pool.layer_off +
+                                 (p & bsm) * a.pool.row_bytes + 16 * ch);
+            const float s = sc[(int64_t)b * a.pool.sc_block + (h << a.pool.lbs) + (p & bsm)];
+            const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+            uint32_t r[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    const float lo = (float)(int8_t)(w[i] >> (16 * k)) * s;
+                    const float hi = (float)(int8_t)(w[i] >> (16 * k + 8)) * s;
+                    r[2 * i + k] = bf16_rne(lo) | (bf16_rne(hi) << 16);
+                }
+            }
+            o[tsr][0] = u32x4{r[0], r[1], r[2], r[3]};
+            o[tsr][1] = u32x4{r[4], r[5], r[6], r[7]};
+        }
+        const int64_t dst = (orow * (int64_t)cpr + ch) * 32;
+        st16(a.k_out + dst, o[0][0]);
+        st16(a.k_out + dst + 16, o[0][1]);
+        if (has_v) {
+            st16(a.v_out + dst, o[1][0]);
+            st16(a.v_out + dst + 16, o[1][1]);
+        }
+    }
+}
+
+hipError_t launch_gather_q8(const GatherArgs &a, int head_dim, hipStream_t s) {
+    const dim3 grid((unsigned)((int64_t)a.num_seqs * a.tiles_per_seq));
+    if (head_dim == 128)
+        hipLaunchKernelGGL(gather_q8_kernel<128>, grid, dim3(kCopyThreads), 0, s, a);
+    else if (head_dim == 64)
+        hipLaunchKernelGGL(gather_q8_kernel<64>, grid, dim3(kCopyThreads), 0, s, a);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Whole-block copies of copy-on-write [P3 sec. 3.1]: workgroup w copies
 // piece w % pieces (kCopyBlockPiece bytes) of every layer's K and V of pair
 // w / pieces.  Block contents are contiguous per tensor (all layers of a

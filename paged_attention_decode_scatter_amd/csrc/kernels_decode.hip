@@ -826,6 +826,267 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Quantised (int8) pools, split schedule [P3 sec. 6 names quantised KV; the
+// stored value of a (token, kv head) row is code * scale].  The pipeline of
+// decode_mfma_kernel with half the bytes per token:
+//   K: lane (n, g4) loads row n's codes [D/4 g4, D/4 (g4+1)) and converts
+//      them to bf16 in registers (exact: |code| <= 127); QK^T step j takes
+//      codes 8j .. 8j+7 of that range, so the query fragments are loaded in
+//      the same (permuted) order -- a dot product does not care.  The
+//      score of token t is (q . code_t) * kscale_t * scale.
+//   V: each lane loads 16 codes of a row, converts them and writes the
+//      bf16 row pieces into the wave's V tile in the bf16 kernel's tile
+//      layout; P.V then reads it with the same transposing LDS read.  The
+//      value scale folds into the probabilities: P'_t = p_t * vscale_t
+//      (rounded to bf16 as P is); the denominator sums the unscaled p_t.
+//   Scales: the 16 tokens of a chunk are contiguous per head (layout
+//      (block, layer, head, slot)), so lane (n, g4) loads the scales of its
+//      four score rows 4 g4 .. 4 g4 + 3 with one 16-byte load each.
+//   Codes are always finite, so rows without a live token need no zeroing:
+//   their score is -inf and their P' exactly 0.
+// ---------------------------------------------------------------------------
+
+// Two int8 codes (bytes sh/8, sh/8 + 1 of w) as a bf16 pair.
+__device__ __forceinline__ uint32_t i8pair_bf16(uint32_t w, int sh) {
+    const float lo = (float)(int32_t)(int8_t)(w >> sh);
+    const float hi = (float)(int32_t)(int8_t)(w >> (sh + 8));
+    return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+}
+
+// 16 codes -> 16 bf16 values (two 16-byte pieces, in order).
+__device__ __forceinline__ void i8x16_bf16(u32x4 c, u32x4 &lo, u32x4 &hi) {
+    lo = u32x4{i8pair_bf16(c.x, 0), i8pair_bf16(c.x, 16), i8pair_bf16(c.y, 0), i8pair_bf16(c.y, 16)};
+    hi = u32x4{i8pair_bf16(c.z, 0), i8pair_bf16(c.z, 16), i8pair_bf16(c.w, 0), i8pair_bf16(c.w, 16)};
+}
+
+// Q^T fragments in the permuted order: lane (n, g4), step j holds head n's
+// elements D/4 g4 + 8 j .. +8.
+template <int D, int G>
+__device__ __forceinline__ void load_q_q8(const DecodeArgs &a, int seq, int h,
+                                          u32x4 (&qf)[MfmaShape<D>::KS]) {
+    const int lane = threadIdx.x & 63;
+    const int n = lane & 15, g4 = lane >> 4;
+    const char *qp = a.q + (((int64_t)seq * a.num_q_heads + (int64_t)h * G + n) * D + (D / 4) * g4) * 2;
+#pragma unroll
+    for (int j = 0; j < MfmaShape<D>::KS; ++j) qf[j] = n < G ? ld16(qp + 16 * j) : u32x4{0, 0, 0, 0};
+}
+
+template <int D>
+struct Q8Slot {
+    static constexpr int KL = D / 64;        // K loads (16 codes) per lane per chunk
+    static constexpr int VL = D / 64;        // V loads per lane per chunk
+    u32x4 k[KL];
+    u32x4 v[VL];
+    u32x4 ks, vs;                            // scales of tokens 4 g4 .. 4 g4 + 3
+};
+
+template <int D, int G, bool UB>
+__device__ __forceinline__ void attend_range_q8(const DecodeArgs &a, const Range &R, int64_t jb0,
+                                                const int32_t *bt_s, char *vt, int h,
+                                                const u32x4 (&qf)[MfmaShape<D>::KS], float &m_h,
+                                                float &l_h, f32x4 (&acc)[MfmaShape<D>::NV]) {
+    using S = MfmaShape<D>;
+    using Slot = Q8Slot<D>;
+    constexpr int KS = S::KS, NV = S::NV, NP = S::NP, ROWB = S::ROWB, VSLAB = S::VSLAB;
+    constexpr int NSLOT = S::NSLOT;
+    constexpr int KC = D / 4;        // K codes per lane per chunk
+    constexpr int VPR = D / 16;      // 16-code pieces per row
+    constexpr int VRPL = 64 / VPR;   // rows per V load
+    constexpr float kLazy = 8.0f;
+    const int lane = threadIdx.x & 63;
+    const int n = lane & 15, g4 = lane >> 4;
+    const int lbs = a.pool.lbs;
+    const int64_t bsm = (1ll << lbs) - 1;
+    const int64_t row_bytes = a.pool.row_bytes;
+    const float sl2 = a.scale_log2;
+    const char *kh = a.pool.k + a.pool.layer_off + (int64_t)h * D;
+    const char *vh = a.pool.v + a.pool.layer_off + (int64_t)h * D;
+    const float *ksh = a.pool.ks + ((int64_t)h << lbs);
+    const float *vsh = a.pool.vs + ((int64_t)h << lbs);
+    const int vrow = lane / VPR, vpc = lane % VPR;
+
+    auto load_chunk = [&](int64_t pc, Slot &sl) {
+        if constexpr (UB) {
+            const int32_t b = __builtin_amdgcn_readfirstlane(bt_s[(int)((pc >> lbs) - jb0)]);
+            const int64_t bb = b >= 0 ? b : 0;
+            const int64_t base = bb * a.pool.block_stride + (pc & bsm) * row_bytes;
+            const char *kb = kh + base + (uint32_t)(n * row_bytes + KC * g4);
+#pragma unroll
+            for (int i = 0; i < Slot::KL; ++i) sl.k[i] = ld16(kb + 16 * i);
+#pragma unroll
+            for (int i = 0; i < Slot::VL; ++i)
+                sl.v[i] = ld16(vh + base + (uint32_t)((i * VRPL + vrow) * row_bytes + 16 * vpc));
+            const int64_t so = bb * a.pool.sc_block + (pc & bsm) + 4 * g4;
+            sl.ks = ld16(reinterpret_cast<const char *>(ksh + so));
+            sl.vs = ld16(reinterpret_cast<const char *>(vsh + so));
+        } else {
+            {
+                const int64_t p = pc + n;
+                const bool in = p >= R.lo && p < R.hi;
+                const int32_t b = in ? bt_s[(int)((p >> lbs) - jb0)] : -1;
+                const char *kb = kh + (int64_t)(b >= 0 ? b : 0) * a.pool.block_stride + (p & bsm) * row_bytes + KC * g4;
+#pragma unroll
+                for (int i = 0; i < Slot::KL; ++i) sl.k[i] = ld16(kb + 16 * i);
+            }
+#pragma unroll
+            for (int i = 0; i < Slot::VL; ++i) {
+                const int64_t p = pc + i * VRPL + vrow;
+                const bool in = p >= R.lo && p < R.hi;
+                const int32_t b = in ? bt_s[(int)((p >> lbs) - jb0)] : -1;
+                sl.v[i] = ld16(vh + (int64_t)(b >= 0 ? b : 0) * a.pool.block_stride + (p & bsm) * row_bytes + 16 * vpc);
+            }
+            uint32_t kw[4], vw[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t p = pc + 4 * g4 + e;
+                const bool in = p >= R.lo && p < R.hi;
+                const int32_t b = in ? bt_s[(int)((p >> lbs) - jb0)] : -1;
+                const int64_t so = (int64_t)(b >= 0 ? b : 0) * a.pool.sc_block + (p & bsm);
+                kw[e] = __float_as_uint(ksh[so]);
+                vw[e] = __float_as_uint(vsh[so]);
+            }
+            sl.ks = u32x4{kw[0], kw[1], kw[2], kw[3]};
+            sl.vs = u32x4{vw[0], vw[1], vw[2], vw[3]};
+        }
+    };
+
+    auto compute = [&](int64_t pc, const Slot &sl) {
+        bool bok = true;
+        if constexpr (UB) bok = __builtin_amdgcn_readfirstlane(bt_s[(int)((pc >> lbs) - jb0)]) >= 0;
+        auto row_live = [&](int row) -> bool {
+            const int64_t p = pc + row;
+            const bool in = p >= R.lo && p < R.hi;
+            return UB ? (bok && in) : (in && bt_s[(int)((p >> lbs) - jb0)] >= 0);
+        };
+        const bool full = UB ? (bok && pc >= R.lo && pc + 16 <= R.hi) : false;
+        // V codes -> bf16 rows of the tile (the bf16 kernel's slab layout)
+#pragma unroll
+        for (int i = 0; i < Slot::VL; ++i) {
+            const int row = i * VRPL + vrow;
+            u32x4 lo, hi;
+            i8x16_bf16(sl.v[i], lo, hi);
+            char *dst = vt + (row % NP) * VSLAB + (row / NP) * ROWB + 32 * vpc;
+            *reinterpret_cast<u32x4 *>(dst) = lo;
+            *reinterpret_cast<u32x4 *>(dst + 16) = hi;
+        }
+        // K codes -> bf16 operands; scores S[token 4 g4 + i][head n]
+        u32x4 kb[KS];
+#pragma unroll
+        for (int i = 0; i < Slot::KL; ++i) i8x16_bf16(sl.k[i], kb[2 * i], kb[2 * i + 1]);
+        f32x4 sacc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int j = 0; j < KS; ++j)
+            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kb[j]), as_bf16x8(qf[j]), sacc, 0, 0, 0);
+        const float ksf[4] = {__uint_as_float(sl.ks.x), __uint_as_float(sl.ks.y),
+                              __uint_as_float(sl.ks.z), __uint_as_float(sl.ks.w)};
+        const float vsf[4] = {__uint_as_float(sl.vs.x), __uint_as_float(sl.vs.y),
+                              __uint_as_float(sl.vs.z), __uint_as_float(sl.vs.w)};
+        float s[4];
+        float cm = kNegInf;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            s[i] = (full || row_live(4 * g4 + i)) ? sacc[i] * ksf[i] * sl2 : kNegInf;
+            cm = fmaxf(cm, s[i]);
+        }
+        cm = fmaxf(cm, __shfl_xor(cm, 16));
+        cm = fmaxf(cm, __shfl_xor(cm, 32));
+        float alpha = 1.0f;
+        if (cm > m_h + kLazy) {
+            alpha = m_h == kNegInf ? 0.0f : fast_exp2(m_h - cm);
+            m_h = cm;
+        }
+        float pr[4], pv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            pr[i] = s[i] == kNegInf ? 0.0f : fast_exp2(s[i] - m_h);
+            pv[i] = s[i] == kNegInf ? 0.0f : pr[i] * vsf[i];
+        }
+        const uint32_t p01 = f32_to_bf16_bits(pr[0]) | (f32_to_bf16_bits(pr[1]) << 16);
+        const uint32_t p23 = f32_to_bf16_bits(pr[2]) | (f32_to_bf16_bits(pr[3]) << 16);
+        l_h = fmaf(l_h, alpha, (bf16_lo(p01) + bf16_hi(p01)) + (bf16_lo(p23) + bf16_hi(p23)));
+        if (__any(n < G && alpha != 1.0f)) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float al = __shfl(alpha, 4 * g4 + i);
+#pragma unroll
+                for (int sl2i = 0; sl2i < NV; ++sl2i) acc[sl2i][i] *= al;
+            }
+        }
+        const uint32_t q01 = f32_to_bf16_bits(pv[0]) | (f32_to_bf16_bits(pv[1]) << 16);
+        const uint32_t q23 = f32_to_bf16_bits(pv[2]) | (f32_to_bf16_bits(pv[3]) << 16);
+        typedef short s16x4 __attribute__((ext_vector_type(4)));
+        const s16x4 pa = __builtin_bit_cast(s16x4, (uint64_t)q01 | ((uint64_t)q23 << 32));
+        wave_lds_order();
+        const int orow = 4 * g4 + (n >> 2);
+        const int vbase = (orow % NP) * VSLAB + (orow / NP) * ROWB + 8 * (n & 3);
+#pragma unroll
+        for (int sl = 0; sl < NV; ++sl) {
+            const int off = vbase + 32 * sl;
+            const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4 *)((__attribute__((address_space(3))) char *)(vt) + off));
+            acc[sl] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, acc[sl], 0, 0, 0);
+        }
+        wave_lds_order();
+    };
+
+    const int64_t first = R.lo & ~int64_t(15);
+    if (first < R.hi) {
+        const int64_t last = (R.hi - 1) & ~int64_t(15);
+        Slot ring[NSLOT];
+#pragma unroll
+        for (int q = 0; q < NSLOT - 1; ++q) load_chunk(min(first + 16 * q, last), ring[q]);
+        bool done = false;
+        for (int64_t pc = first; !done;) {
+#pragma unroll
+            for (int q = 0; q < NSLOT; ++q) {
+                if (!done) {
+                    load_chunk(min(pc + 16 * (NSLOT - 1), last), ring[(q + NSLOT - 1) % NSLOT]);
+                    compute(pc, ring[q]);
+                    pc += 16;
+                    done = pc > last;
+                }
+            }
+        }
+    }
+}
+
+template <int D, int G, bool UB>
+__global__ __launch_bounds__(256) void decode_q8_kernel(DecodeArgs a) {
+    using S = MfmaShape<D>;
+    static_assert(G >= 1 && G <= 16, "group");
+    __shared__ int32_t bt_s[kBtLds];
+    __shared__ __attribute__((aligned(16))) char vtiles[4][S::VTILE];
+
+    const Item it = work_item(a);
+    const Range R = split_range(a, it.seq, it.split);
+    const bool direct = a.max_splits == 1;
+    if (!direct && R.hi <= R.lo) {
+        if (a.fused_merge && R.len <= 0 && it.split == 0) zero_outputs<1, D, G>(a, it.seq, it.hg);
+        return;
+    }
+    const int64_t jb0 = stage_table(a, it.seq, R, bt_s);
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int h = it.hg * a.heads_per_wg + w;
+    u32x4 qf[S::KS];
+    load_q_q8<D, G>(a, it.seq, h, qf);
+    float m_h = kNegInf;
+    float l_h = 0.0f;
+    f32x4 acc[S::NV];
+#pragma unroll
+    for (int sl = 0; sl < S::NV; ++sl) acc[sl] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    attend_range_q8<D, G, UB>(a, R, jb0, bt_s, vtiles[w], h, qf, m_h, l_h, acc);
+    float lrow[4];
+    head_denominators(l_h, lrow);
+    if (direct) {
+        write_direct<D, G>(a, it.seq, h, acc, lrow);
+        return;
+    }
+    const int64_t item0 = ((int64_t)it.seq * a.max_splits + it.split) * a.num_q_heads + (int64_t)h * G;
+    write_partial<D, G>(a.ws_ml + item0 * 2, a.ws_acc + item0 * D, acc, m_h, l_h);
+    if (a.fused_merge) finish_split<1, D, G>(a, it, R);
+}
+
+// ---------------------------------------------------------------------------
 // Balanced schedule (bf16): the grid is the number of workgroups that stay
 // resident together, and every workgroup takes an equal share of the work.
 // The work is flattened into units (head group, sequence, chunk): chunk c
@@ -1540,6 +1801,33 @@ static hipError_t run_decode(const DecodeArgs &a, hipStream_t s) {
 
 typedef hipError_t (*DecodeFn)(const DecodeArgs &, hipStream_t);
 
+// int8 pools: bf16 queries and outputs, split schedule.
+template <int D, int G>
+static hipError_t run_decode_q8(const DecodeArgs &a, hipStream_t s) {
+    const dim3 block(64 * a.heads_per_wg);
+    const dim3 grid((unsigned)((int64_t)a.head_groups * a.max_splits * a.num_seqs));
+    if (a.pool.lbs >= 4)
+        hipLaunchKernelGGL((decode_q8_kernel<D, G, true>), grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL((decode_q8_kernel<D, G, false>), grid, block, 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.max_splits == 1 || a.fused_merge) return e;
+    hipLaunchKernelGGL((reduce_kernel<1, D>), dim3((unsigned)((int64_t)a.num_seqs * a.num_q_heads)),
+                       dim3(kReduceThreads), (size_t)a.max_splits * sizeof(float), s, a);
+    return hipGetLastError();
+}
+
+template <int D>
+static DecodeFn pick_group_q8(int group) {
+    switch (group) {
+        case 1: return run_decode_q8<D, 1>;
+        case 2: return run_decode_q8<D, 2>;
+        case 4: return run_decode_q8<D, 4>;
+        case 8: return run_decode_q8<D, 8>;
+        default: return nullptr;
+    }
+}
+
 template <int DT, int D>
 static DecodeFn pick_group(int group) {
     switch (group) {
@@ -1563,6 +1851,10 @@ static DecodeFn pick_dim(int head_dim, int group) {
 static DecodeFn pick(int dtype, int head_dim, int group) {
     if (dtype == 0) return pick_dim<0>(head_dim, group);
     if (dtype == 1) return pick_dim<1>(head_dim, group);
+    if (dtype == 2) {
+        if (head_dim == 64) return pick_group_q8<64>(group);
+        if (head_dim == 128) return pick_group_q8<128>(group);
+    }
     return nullptr;
 }
 

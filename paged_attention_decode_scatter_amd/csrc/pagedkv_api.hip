@@ -22,14 +22,15 @@ int ilog2(int64_t x) {
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int64_t elem_bytes(int32_t dtype) { return dtype == PKV_BF16 ? 2 : 4; }
+int64_t elem_bytes(int32_t dtype) { return dtype == PKV_BF16 ? 2 : dtype == PKV_I8 ? 1 : 4; }
 
 int64_t pow2_or_neg(int64_t x) { return is_pow2(x) ? ilog2(x) : -1; }
 
 // Common pool checks.  need_v: the call reads or writes V.
 int check_pool(const pkv_pool *pool, bool need_v) {
     if (!pool) return PKV_ERR_NULL;
-    if (pool->dtype != PKV_F32 && pool->dtype != PKV_BF16) return PKV_ERR_DTYPE;
+    if (pool->dtype != PKV_F32 && pool->dtype != PKV_BF16 && pool->dtype != PKV_I8)
+        return PKV_ERR_DTYPE;
     if (pool->reserved != 0) return PKV_ERR_SHAPE;
     if (pool->num_blocks <= 0 || pool->num_blocks > INT32_MAX || pool->num_layers <= 0 ||
         pool->num_kv_heads <= 0 || pool->head_dim <= 0 || !is_pow2(pool->block_size) ||
@@ -44,7 +45,17 @@ int check_pool(const pkv_pool *pool, bool need_v) {
         if (pool->block_stride < pool->num_layers * pool->block_size * row) return PKV_ERR_SHAPE;
         if (pool->block_stride % 16) return PKV_ERR_ALIGN;
     }
+    if (pool->dtype == PKV_I8) {
+        if (!pool->k_scale || (pool->v && !pool->v_scale)) return PKV_ERR_NULL;
+        if (!aligned16(pool->k_scale) || (pool->v && !aligned16(pool->v_scale)))
+            return PKV_ERR_ALIGN;
+    }
     return PKV_OK;
+}
+
+// Floats of one block's scales (all layers) in a quantised pool.
+int64_t scale_block(const pkv_pool *pool) {
+    return pool->num_layers * pool->num_kv_heads * pool->block_size;
 }
 
 // Bytes of one block of one tensor (all layers) and the distance between
@@ -67,8 +78,16 @@ PoolView make_view(const pkv_pool *pool, int32_t layer) {
     v.layer_off = (int64_t)layer * pool->block_size * row;
     v.num_blocks = (int32_t)pool->num_blocks;
     v.lbs = ilog2(pool->block_size);
+    if (pool->dtype == PKV_I8) {
+        const int64_t lo = (int64_t)layer * pool->num_kv_heads * pool->block_size;
+        v.ks = static_cast<const float *>(pool->k_scale) + lo;
+        v.vs = pool->v_scale ? static_cast<const float *>(pool->v_scale) + lo : nullptr;
+        v.sc_block = scale_block(pool);
+    }
     return v;
 }
+
+bool q8_dim_ok(const pkv_pool *pool) { return pool->head_dim == 64 || pool->head_dim == 128; }
 
 // Compute units of the current device, queried once per device (256 when no
 // device answers, e.g. on a build host).
@@ -299,6 +318,26 @@ static int64_t rows_per_wg(int64_t num_tokens, int64_t cpr) {
     return tpw;
 }
 
+static ScatterQ8Args q8_args(const pkv_pool *pool, const PoolView &v, const void *k_src,
+                             const void *v_src, int64_t num_tokens) {
+    ScatterQ8Args a{};
+    a.kpool = static_cast<char *>(pool->k);
+    a.vpool = v_src ? static_cast<char *>(pool->v) : nullptr;
+    a.ks = const_cast<float *>(v.ks);
+    a.vs = v_src ? const_cast<float *>(v.vs) : nullptr;
+    a.k_src = static_cast<const char *>(k_src);
+    a.v_src = static_cast<const char *>(v_src);
+    a.num_tokens = num_tokens;
+    a.total_slots = pool->num_blocks * pool->block_size;
+    a.block_stride = v.block_stride;
+    a.layer_off = v.layer_off;
+    a.sc_block = v.sc_block;
+    a.num_kv_heads = (int32_t)pool->num_kv_heads;
+    a.head_dim = (int32_t)pool->head_dim;
+    a.lbs = v.lbs;
+    return a;
+}
+
 PKV_API int kv_scatter(const pkv_pool *pool, int32_t layer, const void *k_src, const void *v_src,
                        const int64_t *slot_mapping, int64_t num_tokens, void *stream) {
     const bool has_v = v_src != nullptr;
@@ -310,6 +349,13 @@ PKV_API int kv_scatter(const pkv_pool *pool, int32_t layer, const void *k_src, c
     if (!k_src || !slot_mapping) return PKV_ERR_NULL;
     if (!aligned16(k_src) || (has_v && !aligned16(v_src))) return PKV_ERR_ALIGN;
     const PoolView v = make_view(pool, layer);
+    if (pool->dtype == PKV_I8) {
+        if (!q8_dim_ok(pool)) return PKV_ERR_UNSUPPORTED;
+        if (num_tokens * pool->num_kv_heads > (int64_t)INT32_MAX * 8) return PKV_ERR_SHAPE;
+        ScatterQ8Args a = q8_args(pool, v, k_src, v_src, num_tokens);
+        a.slots = slot_mapping;
+        return status_of(launch_scatter_q8(a, static_cast<hipStream_t>(stream)));
+    }
     ScatterArgs a{};
     a.kpool = static_cast<char *>(pool->k);
     a.vpool = static_cast<char *>(pool->v);
@@ -344,6 +390,19 @@ PKV_API int kv_append(const pkv_pool *pool, int32_t layer, const void *k_src, co
         return PKV_ERR_NULL;
     if (!aligned16(k_src) || (has_v && !aligned16(v_src))) return PKV_ERR_ALIGN;
     const PoolView v = make_view(pool, layer);
+    if (pool->dtype == PKV_I8) {
+        if (!q8_dim_ok(pool)) return PKV_ERR_UNSUPPORTED;
+        if (num_tokens * pool->num_kv_heads > (int64_t)INT32_MAX * 8) return PKV_ERR_SHAPE;
+        ScatterQ8Args a = q8_args(pool, v, k_src, v_src, num_tokens);
+        a.block_tables = block_tables;
+        a.offsets = offsets;
+        a.token_seq = token_seq;
+        a.token_pos = token_pos;
+        a.slots_out = slot_mapping_out;
+        a.bt_stride = bt_stride;
+        a.num_seqs = num_seqs;
+        return status_of(launch_scatter_q8(a, static_cast<hipStream_t>(stream)));
+    }
     AppendArgs a{};
     a.sc.kpool = static_cast<char *>(pool->k);
     a.sc.vpool = static_cast<char *>(pool->v);
@@ -403,6 +462,10 @@ PKV_API int kv_gather(const pkv_pool *pool, int32_t layer, const int32_t *block_
     a.lcpr = (int32_t)pow2_or_neg(cpr);
     if ((int64_t)num_seqs * a.tiles_per_seq > INT32_MAX || cpr * tpw > INT32_MAX / 2)
         return PKV_ERR_SHAPE;
+    if (pool->dtype == PKV_I8) {
+        if (!q8_dim_ok(pool)) return PKV_ERR_UNSUPPORTED;
+        return status_of(launch_gather_q8(a, (int)pool->head_dim, static_cast<hipStream_t>(stream)));
+    }
     return status_of(launch_gather(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -439,7 +502,7 @@ PKV_API int32_t paged_attn_decode_schedule(int32_t num_seqs, int32_t num_kv_head
                                            int32_t num_q_heads, int32_t head_dim,
                                            int32_t max_seq_len, int32_t block_size, int32_t dtype,
                                            int32_t split_tokens) {
-    if (dtype != PKV_F32 && dtype != PKV_BF16) return PKV_ERR_DTYPE;
+    if (dtype != PKV_F32 && dtype != PKV_BF16 && dtype != PKV_I8) return PKV_ERR_DTYPE;
     if (num_kv_heads <= 0 || num_q_heads <= 0 || num_q_heads % num_kv_heads) return PKV_ERR_SHAPE;
     DecodePlan p;
     const int st = plan_decode(num_seqs, num_kv_heads, num_q_heads, head_dim, max_seq_len,
@@ -471,6 +534,7 @@ int decode_impl(const pkv_pool *pool, int32_t layer, const void *q, int32_t num_
         return PKV_ERR_SHAPE;
     const int group = (int)(num_q_heads / pool->num_kv_heads);
     if (!decode_supported(pool->dtype, (int)pool->head_dim, group)) return PKV_ERR_UNSUPPORTED;
+    if (k_new && pool->dtype == PKV_I8) return PKV_ERR_UNSUPPORTED;
     if (balanced_refused(num_seqs, pool->num_kv_heads, pool->head_dim, max_seq_len, pool->block_size,
                          pool->dtype, split_tokens))
         return PKV_ERR_UNSUPPORTED;
@@ -621,6 +685,13 @@ PKV_API int kv_copy_blocks(const pkv_pool *pool, const int32_t *src_blocks,
     a.block_stride = block_stride_of(pool);
     a.pieces = (a.block_bytes + kCopyBlockPiece - 1) / kCopyBlockPiece;
     if (a.pieces * num_pairs > INT32_MAX) return PKV_ERR_SHAPE;
+    st = status_of(launch_copy_blocks(a, static_cast<hipStream_t>(stream)));
+    if (st || pool->dtype != PKV_I8) return st;
+    // the scales of a quantised pool: one dense range per block as well
+    a.k = static_cast<char *>(pool->k_scale);
+    a.v = pool->v ? static_cast<char *>(pool->v_scale) : nullptr;
+    a.block_bytes = a.block_stride = scale_block(pool) * 4;
+    a.pieces = (a.block_bytes + kCopyBlockPiece - 1) / kCopyBlockPiece;
     return status_of(launch_copy_blocks(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -653,6 +724,24 @@ int swap_impl(const pkv_pool *pool, const int32_t *ids, int64_t n, char *kh, cha
             char *h = host + i * bb;
             const hipError_t e = to_host ? hipMemcpyAsync(h, d, bytes, kind, s)
                                          : hipMemcpyAsync(d, h, bytes, kind, s);
+            if (e != hipSuccess) return status_of(e);
+        }
+        i = j;
+    }
+    if (pool->dtype != PKV_I8) return PKV_OK;
+    // quantised pool: the n blocks' scales follow the n blocks' codes
+    const int64_t sb = scale_block(pool) * 4;
+    for (int64_t i = 0; i < n;) {
+        int64_t j = i + 1;
+        while (j < n && ids[j] == ids[j - 1] + 1) ++j;
+        for (int t = 0; t < 2; ++t) {
+            char *dev = static_cast<char *>(t == 0 ? pool->k_scale : (pool->v ? pool->v_scale : nullptr));
+            char *host = t == 0 ? kh : vh;
+            if (!dev) continue;
+            char *d = dev + (int64_t)ids[i] * sb;
+            char *h = host + n * bb + i * sb;
+            const hipError_t e = to_host ? hipMemcpyAsync(h, d, (j - i) * sb, kind, s)
+                                         : hipMemcpyAsync(d, h, (j - i) * sb, kind, s);
             if (e != hipSuccess) return status_of(e);
         }
         i = j;

@@ -29,6 +29,11 @@ struct PoolView {
     int32_t num_blocks;
     int32_t lbs;           // log2(block_size)
     int32_t pad_;
+    // quantised pools: the scales of this layer; the scale of (block b,
+    // kv head h, slot r) is ks[b * sc_block + h * block_size + r]
+    const float *ks;
+    const float *vs;
+    int64_t sc_block;      // num_layers * num_kv_heads * block_size
 };
 
 struct SlotArgs {
@@ -69,6 +74,34 @@ struct AppendArgs {
     int64_t *slots_out;          // may be null
     int32_t bt_stride;
     int32_t num_seqs;
+};
+
+// Quantising scatter (int8 pools): bfloat16 rows in, codes and scales out.
+// slots == null: the slots are computed as kv_append computes them.
+struct ScatterQ8Args {
+    char *kpool;
+    char *vpool;
+    float *ks;             // scales of the layer, as PoolView::ks
+    float *vs;
+    const char *k_src;
+    const char *v_src;
+    const int64_t *slots;
+    const int32_t *block_tables;
+    const int32_t *offsets;
+    const int32_t *token_seq;
+    const int32_t *token_pos;
+    int64_t *slots_out;    // may be null
+    int64_t num_tokens;
+    int64_t total_slots;
+    int64_t block_stride;
+    int64_t layer_off;
+    int64_t sc_block;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t lbs;
+    int32_t bt_stride;
+    int32_t num_seqs;
+    int32_t pad_;
 };
 
 struct GatherArgs {
@@ -183,6 +216,8 @@ bool prefill_supported(int dtype, int head_dim, int group);
 hipError_t launch_prefill(const PrefillArgs &a, int dtype, int head_dim, int group, hipStream_t s);
 hipError_t launch_gather(const GatherArgs &a, hipStream_t s);
 hipError_t launch_copy_blocks(const CopyBlocksArgs &a, hipStream_t s);
+hipError_t launch_scatter_q8(const ScatterQ8Args &a, hipStream_t s);
+hipError_t launch_gather_q8(const GatherArgs &a, int head_dim, hipStream_t s);
 hipError_t launch_validate(const ValidateArgs &a, hipStream_t s);
 // Returns hipErrorInvalidValue when (dtype, head_dim, group) is not built.
 hipError_t launch_decode(const DecodeArgs &a, int dtype, int head_dim, int group,

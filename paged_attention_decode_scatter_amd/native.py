@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
 
 PKV_F32 = 0
 PKV_BF16 = 1
+PKV_I8 = 2
 
 _DTYPES = {torch.float32: PKV_F32, torch.bfloat16: PKV_BF16}
 
@@ -61,6 +62,8 @@ class PkvPool(ctypes.Structure):
         ("dtype", ctypes.c_int32),
         ("reserved", ctypes.c_int32),
         ("block_stride", ctypes.c_int64),
+        ("k_scale", ctypes.c_void_p),
+        ("v_scale", ctypes.c_void_p),
     ]
 
 
@@ -145,15 +148,71 @@ def _need(t, dtype, name):
         raise ValueError(f"{name} must be contiguous")
 
 
+class QuantizedPool:
+    """One tensor of an int8 pool: codes (num_blocks, num_layers,
+    block_size, num_kv_heads, head_dim) int8 and one float32 scale per
+    (token, kv head) row, scales (num_blocks, num_layers, num_kv_heads,
+    block_size).  Passed wherever a K or V pool goes; the rows written into
+    it and the queries and outputs of decode are bfloat16."""
+
+    def __init__(self, codes, scales):
+        if codes.dim() != 5 or codes.dtype != torch.int8:
+            raise ValueError("codes must be int8 (num_blocks, num_layers, block_size, heads, head_dim)")
+        nb, nl, bs, h, _ = codes.shape
+        if scales.dtype != torch.float32 or tuple(scales.shape) != (nb, nl, h, bs) \
+                or not scales.is_contiguous() or scales.device != codes.device:
+            raise ValueError("scales must be contiguous float32 (num_blocks, num_layers, "
+                             "num_kv_heads, block_size) on the codes' device")
+        self.codes = codes
+        self.scales = scales
+
+    @classmethod
+    def empty(cls, num_blocks, num_layers, block_size, num_kv_heads, head_dim, device):
+        codes = torch.zeros((num_blocks, num_layers, block_size, num_kv_heads, head_dim),
+                            dtype=torch.int8, device=device)
+        scales = torch.zeros((num_blocks, num_layers, num_kv_heads, block_size),
+                             dtype=torch.float32, device=device)
+        return cls(codes, scales)
+
+    shape = property(lambda self: self.codes.shape)
+    dtype = property(lambda self: self.codes.dtype)
+    device = property(lambda self: self.codes.device)
+    is_cuda = property(lambda self: self.codes.is_cuda)
+
+    def dim(self):
+        return 5
+
+    def data_ptr(self):
+        return self.codes.data_ptr()
+
+    def stride(self, *a):
+        return self.codes.stride(*a)
+
+    def element_size(self):
+        return 1
+
+    def scale_bytes_per_block(self):
+        return self.scales[0].numel() * 4
+
+
+def _row_dtype(k_pool):
+    """dtype of the rows written into / read from a pool, of q and out."""
+    return torch.bfloat16 if isinstance(k_pool, QuantizedPool) else k_pool.dtype
+
+
 def make_pool(k_pool, v_pool=None) -> PkvPool:
     """Describe a (num_blocks, num_layers, block_size, num_kv_heads, head_dim)
     K/V pool pair for the C ABI.  Each tensor is dense within a block; the
     block (first) dimension may have a larger stride, as the K and V views
     kv[:, 0] and kv[:, 1] of a combined (num_blocks, 2, num_layers,
-    block_size, num_kv_heads, head_dim) cache have (see combined_views)."""
+    block_size, num_kv_heads, head_dim) cache have (see combined_views).
+    Quantised pools are QuantizedPool pairs."""
+    quant = isinstance(k_pool, QuantizedPool)
+    if v_pool is not None and isinstance(v_pool, QuantizedPool) != quant:
+        raise TypeError("k_pool and v_pool must both be quantised or both not")
     if k_pool.dim() != 5:
         raise ValueError("pool must be (num_blocks, num_layers, block_size, num_kv_heads, head_dim)")
-    if k_pool.dtype not in _DTYPES:
+    if not quant and k_pool.dtype not in _DTYPES:
         raise TypeError(f"pool dtype must be float32 or bfloat16, got {k_pool.dtype}")
     nb, nl, bs, h, d = k_pool.shape
     inner = (bs * h * d, h * d, d, 1)
@@ -172,8 +231,11 @@ def make_pool(k_pool, v_pool=None) -> PkvPool:
         raise ValueError("k_pool and v_pool block strides differ")
     stride = k_pool.stride(0) if nb > 1 else dense
     block_stride = 0 if stride == dense else stride * k_pool.element_size()
+    dt = PKV_I8 if quant else _DTYPES[k_pool.dtype]
     return PkvPool(k_pool.data_ptr(), None if v_pool is None else v_pool.data_ptr(),
-                   nb, nl, bs, h, d, _DTYPES[k_pool.dtype], 0, block_stride)
+                   nb, nl, bs, h, d, dt, 0, block_stride,
+                   k_pool.scales.data_ptr() if quant else None,
+                   v_pool.scales.data_ptr() if quant and v_pool is not None else None)
 
 
 def combined_views(kv):
@@ -205,8 +267,8 @@ def kv_slot_mapping(block_tables, offsets, token_seq, token_pos, block_size, out
 
 def kv_scatter(k_pool, v_pool, layer, k_src, v_src, slot_mapping):
     pool = make_pool(k_pool, v_pool)
-    _need(k_src, k_pool.dtype, "k_src")
-    _need(v_src, k_pool.dtype, "v_src")
+    _need(k_src, _row_dtype(k_pool), "k_src")
+    _need(v_src, _row_dtype(k_pool), "v_src")
     _need(slot_mapping, torch.int64, "slot_mapping")
     st = load_library().kv_scatter(ctypes.byref(pool), layer, _ptr(k_src), _ptr(v_src),
                                    _ptr(slot_mapping), slot_mapping.shape[0], _stream(k_pool))
@@ -220,9 +282,9 @@ def kv_append(k_pool, v_pool, layer, k_src, v_src, block_tables, offsets, token_
     does; skipped rows as there).  Optionally also returns the slots in
     slot_mapping_out (int64)."""
     pool = make_pool(k_pool, v_pool)
-    _need(k_src, k_pool.dtype, "k_src")
+    _need(k_src, _row_dtype(k_pool), "k_src")
     if v_src is not None:
-        _need(v_src, k_pool.dtype, "v_src")
+        _need(v_src, _row_dtype(k_pool), "v_src")
     for t, n in ((block_tables, "block_tables"), (offsets, "offsets"),
                  (token_seq, "token_seq"), (token_pos, "token_pos")):
         _need(t, torch.int32, n)
@@ -242,8 +304,8 @@ def kv_gather(k_pool, v_pool, layer, block_tables, seq_lens, offsets, out_row_st
     for t, n in ((block_tables, "block_tables"), (seq_lens, "seq_lens"), (offsets, "offsets")):
         _need(t, torch.int32, n)
     _need(out_row_start, torch.int64, "out_row_start")
-    _need(k_out, k_pool.dtype, "k_out")
-    _need(v_out, k_pool.dtype, "v_out")
+    _need(k_out, _row_dtype(k_pool), "k_out")
+    _need(v_out, _row_dtype(k_pool), "v_out")
     if v_out is not None and v_out.shape[0] != k_out.shape[0]:
         raise ValueError("k_out and v_out row counts differ")
     st = load_library().kv_gather(
@@ -292,13 +354,13 @@ def paged_attn_decode(k_pool, v_pool, layer, q, block_tables, seq_lens, offsets,
     device, zero before its first use; each call leaves it reusable) is
     allocated here, zeroed, when not given."""
     pool = make_pool(k_pool, v_pool)
-    _need(q, k_pool.dtype, "q")
+    _need(q, _row_dtype(k_pool), "q")
     for t, n in ((block_tables, "block_tables"), (seq_lens, "seq_lens"), (offsets, "offsets")):
         _need(t, torch.int32, n)
     num_seqs, hq, d = q.shape
     if out is None:
         out = torch.empty_like(q)
-    _need(out, k_pool.dtype, "out")
+    _need(out, _row_dtype(k_pool), "out")
     need = paged_attn_decode_workspace_size(num_seqs, k_pool.shape[3], hq, d, max_seq_len,
                                             k_pool.shape[2], split_tokens)
     if workspace is None and need > 0:
@@ -319,9 +381,9 @@ def paged_attn_decode_append(k_pool, v_pool, layer, q, k_new, v_new, block_table
     position seq_lens[s] - 1 of each sequence, then paged_attn_decode over
     its tokens (the new one included)."""
     pool = make_pool(k_pool, v_pool)
-    _need(q, k_pool.dtype, "q")
-    _need(k_new, k_pool.dtype, "k_new")
-    _need(v_new, k_pool.dtype, "v_new")
+    _need(q, _row_dtype(k_pool), "q")
+    _need(k_new, _row_dtype(k_pool), "k_new")
+    _need(v_new, _row_dtype(k_pool), "v_new")
     for t, n in ((block_tables, "block_tables"), (seq_lens, "seq_lens"), (offsets, "offsets")):
         _need(t, torch.int32, n)
     num_seqs, hq, d = q.shape
@@ -329,7 +391,7 @@ def paged_attn_decode_append(k_pool, v_pool, layer, q, k_new, v_new, block_table
         raise ValueError("k_new/v_new must be [num_seqs, num_kv_heads, head_dim]")
     if out is None:
         out = torch.empty_like(q)
-    _need(out, k_pool.dtype, "out")
+    _need(out, _row_dtype(k_pool), "out")
     need = paged_attn_decode_workspace_size(num_seqs, k_pool.shape[3], hq, d, max_seq_len,
                                             k_pool.shape[2], split_tokens)
     if workspace is None and need > 0:
@@ -349,14 +411,14 @@ def paged_attn_prefill(k_pool, v_pool, layer, q, q_start, block_tables, seq_lens
     tokens (rows q_start[s].. of q) over its cached tokens, read in place
     through the block tables."""
     pool = make_pool(k_pool, v_pool)
-    _need(q, k_pool.dtype, "q")
+    _need(q, _row_dtype(k_pool), "q")
     for t, n in ((q_start, "q_start"), (block_tables, "block_tables"), (seq_lens, "seq_lens"),
                  (offsets, "offsets")):
         _need(t, torch.int32, n)
     rows, hq, d = q.shape
     if out is None:
         out = torch.empty_like(q)
-    _need(out, k_pool.dtype, "out")
+    _need(out, _row_dtype(k_pool), "out")
     st = load_library().paged_attn_prefill(
         ctypes.byref(pool), layer, _ptr(q), hq, _ptr(q_start), rows, int(max_q_len),
         _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), _ptr(offsets),
@@ -389,25 +451,44 @@ def _host_ids(block_ids):
     return ids
 
 
+def _host_shape(k_pool, n):
+    """Host buffer of n swapped blocks of one tensor: (n, layers, bs, H, D)
+    of the pool dtype, or for a quantised pool a uint8 buffer holding the n
+    blocks' codes, then their scales (split_swapped_q8 views it)."""
+    if isinstance(k_pool, QuantizedPool):
+        return (n * (k_pool.codes[0].numel() + k_pool.scale_bytes_per_block()),), torch.uint8
+    return (n,) + tuple(k_pool.shape[1:]), k_pool.dtype
+
+
+def split_swapped_q8(buf, k_pool, n):
+    """(codes (n, layers, bs, H, D) int8, scales (n, layers, H, bs) float32)
+    views of a quantised pool's swap buffer."""
+    cb = k_pool.codes[0].numel()
+    codes = buf[:n * cb].view(torch.int8).view((n,) + tuple(k_pool.shape[1:]))
+    scales = buf[n * cb:].view(torch.float32).view((n,) + tuple(k_pool.scales.shape[1:]))
+    return codes, scales
+
+
 def _host_blocks(t, k_pool, n, name):
-    shape = (n,) + tuple(k_pool.shape[1:])
-    if t.device.type != "cpu" or t.dtype != k_pool.dtype or not t.is_contiguous() \
+    shape, dt = _host_shape(k_pool, n)
+    if t.device.type != "cpu" or t.dtype != dt or not t.is_contiguous() \
             or tuple(t.shape) != shape:
-        raise ValueError(f"{name} must be a contiguous host {k_pool.dtype} tensor of shape {shape}")
+        raise ValueError(f"{name} must be a contiguous host {dt} tensor of shape {shape}")
 
 
 def kv_swap_out(k_pool, v_pool, block_ids, k_host=None, v_host=None, pin=True):
     """Copy whole blocks (host int32 ids) from the pool to host tensors of
-    shape (n, num_layers, block_size, num_kv_heads, head_dim), allocated
-    (pinned unless pin=False) when not given.  With pinned memory the copies
-    are asynchronous on the current stream: synchronize before reading."""
+    shape (n, num_layers, block_size, num_kv_heads, head_dim) (quantised
+    pools: see split_swapped_q8), allocated (pinned unless pin=False) when
+    not given.  With pinned memory the copies are asynchronous on the
+    current stream: synchronize before reading."""
     ids = _host_ids(block_ids)
     n = ids.shape[0]
-    shape = (n,) + tuple(k_pool.shape[1:])
+    shape, dt = _host_shape(k_pool, n)
     if k_host is None:
-        k_host = torch.empty(shape, dtype=k_pool.dtype, pin_memory=pin)
+        k_host = torch.empty(shape, dtype=dt, pin_memory=pin)
     if v_pool is not None and v_host is None:
-        v_host = torch.empty(shape, dtype=k_pool.dtype, pin_memory=pin)
+        v_host = torch.empty(shape, dtype=dt, pin_memory=pin)
     _host_blocks(k_host, k_pool, n, "k_host")
     if v_pool is not None:
         _host_blocks(v_host, k_pool, n, "v_host")

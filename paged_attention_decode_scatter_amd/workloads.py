@@ -96,6 +96,26 @@ def new_pool(num_blocks, num_layers, block_size, num_kv_heads, head_dim, dtype, 
     return fill_normal_(t, seed)
 
 
+def int8_pool_tensors(num_blocks, num_layers, block_size, num_kv_heads, head_dim, device, seed,
+                      amax=3.0, chunk=1 << 28):
+    """Random stored contents of one tensor of a quantised pool: codes
+    uniform in [-127, 127] (int8, the pool layout) and one float32 scale per
+    (block, layer, kv head, slot) drawn as amax / 127 * U(0.5, 1.5), so the
+    stored values spread over about +-1.5 amax.  Chunked like fill_normal_."""
+    gen = torch.Generator(device=device).manual_seed(seed)
+    codes = torch.empty((num_blocks, num_layers, block_size, num_kv_heads, head_dim),
+                        dtype=torch.int8, device=device)
+    flat = codes.view(-1)
+    for i in range(0, flat.numel(), chunk):
+        m = min(chunk, flat.numel() - i)
+        flat[i:i + m].copy_(torch.randint(-127, 128, (m,), generator=gen, device=device,
+                                          dtype=torch.int32))
+    u = torch.rand((num_blocks, num_layers, num_kv_heads, block_size), generator=gen,
+                   device=device, dtype=torch.float32)
+    scales = (u + 0.5) * (amax / 127.0)
+    return codes, scales
+
+
 def _tables_from_counts(counts, perm, stride=None):
     """Consecutive slices of `perm` as block tables, padded with -1."""
     stride = stride or max(1, max(counts) if counts else 1)

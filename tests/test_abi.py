@@ -54,8 +54,9 @@ def test_status_strings(lib):
     assert N.status_string(12345) == "unknown status"
 
 
-def pool(k=0x1000, v=0x2000, nb=16, nl=2, bs=16, h=8, d=128, dtype=1, reserved=0, stride=0):
-    return N.PkvPool(k, v, nb, nl, bs, h, d, dtype, reserved, stride)
+def pool(k=0x1000, v=0x2000, nb=16, nl=2, bs=16, h=8, d=128, dtype=1, reserved=0, stride=0,
+         ks=0x3000, vs=0x4000):
+    return N.PkvPool(k, v, nb, nl, bs, h, d, dtype, reserved, stride, ks, vs)
 
 
 A = 0x10000  # an aligned fake device address; never dereferenced on these paths
@@ -330,3 +331,58 @@ def test_make_pool_combined_layout():
         N.make_pool(k, torch.zeros(5, 3, 16, 2, 64, dtype=torch.bfloat16))   # strides differ
     with pytest.raises(ValueError):
         N.combined_views(torch.zeros(5, 3, 3, 16, 2, 64))
+
+
+def test_quantized_pool_checks(lib):
+    """An int8 pool needs 16-byte aligned scale arrays; the entry points
+    without an int8 path refuse it; decode takes it on the split schedule
+    only."""
+    by = ctypes.byref
+    I8 = 2
+    sc = lib.kv_scatter
+    assert sc(by(pool(dtype=I8, ks=None)), 0, A, A, A, 4, None) == NULL
+    assert sc(by(pool(dtype=I8, vs=None)), 0, A, A, A, 4, None) == NULL
+    assert sc(by(pool(dtype=I8, v=None, vs=None)), 0, A, None, A, 0, None) == OK
+    assert sc(by(pool(dtype=I8, ks=0x3004)), 0, A, A, A, 4, None) == ALIGN
+    assert sc(by(pool(dtype=I8, d=96)), 0, A, A, A, 4, None) == UNSUP
+    assert sc(by(pool(dtype=I8)), 0, A, A, A, 0, None) == OK
+    assert sc(by(pool(dtype=0, ks=None, vs=None)), 0, A, A, A, 0, None) == OK   # float: ignored
+
+    dec = lib.paged_attn_decode
+
+    def decode(p, split=0, hq=32):
+        return dec(by(p), 0, A, hq, A, 8, A, A, 4, 100, 0.1, split, A, A, 1 << 30, None)
+
+    assert decode(pool(dtype=I8), split=-1) == UNSUP        # no balanced schedule
+    assert decode(pool(dtype=I8, d=96)) == UNSUP
+    assert decode(pool(dtype=I8), hq=24) == UNSUP
+    assert decode(pool(dtype=I8, ks=None)) == NULL
+    app = lib.paged_attn_decode_append
+    assert app(by(pool(dtype=I8)), 0, A, 32, A, A, A, 8, A, A, 4, 100, 0.1, 0, A, A, 1 << 30,
+               None) == UNSUP
+    pre = lib.paged_attn_prefill
+    assert pre(by(pool(dtype=I8)), 0, A, 32, A, 64, 16, A, 8, A, A, 4, 0.1, A, None) == UNSUP
+    f = lib.paged_attn_decode_schedule
+    split = lib.paged_attn_decode_split_tokens
+    assert f(32, 8, 32, 128, 2048, 16, I8, 0) == split(32, 8, 2048, 16)
+    assert f(32, 8, 32, 128, 2048, 16, I8, -1) == UNSUP
+
+
+def test_quantized_pool_binding():
+    """QuantizedPool pairs describe an int8 pool (scale pointers set, dtype
+    PKV_I8); their rows, queries and outputs are bf16; a quantised K with a
+    float V is refused."""
+    import torch
+
+    k = N.QuantizedPool.empty(6, 2, 16, 2, 64, "cpu")
+    v = N.QuantizedPool.empty(6, 2, 16, 2, 64, "cpu")
+    p = N.make_pool(k, v)
+    assert p.dtype == 2 and p.k_scale == k.scales.data_ptr() and p.v_scale == v.scales.data_ptr()
+    assert p.block_stride == 0 and N._row_dtype(k) == torch.bfloat16
+    with pytest.raises(TypeError):
+        N.make_pool(k, torch.zeros(6, 2, 16, 2, 64))
+    with pytest.raises(ValueError):
+        N.QuantizedPool(k.codes, torch.zeros(6, 2, 16, 2))
+    buf = torch.zeros(3 * (2 * 16 * 2 * 64 + 2 * 2 * 16 * 4), dtype=torch.uint8)
+    codes, scales = N.split_swapped_q8(buf, k, 3)
+    assert codes.shape == (3, 2, 16, 2, 64) and scales.shape == (3, 2, 2, 16)
