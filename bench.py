@@ -154,6 +154,62 @@ def other_decode_configs(w, N, W, reps=32):
     return out
 
 
+def int8_decode(w, N, W, reps=32):
+    """Decode over an int8 pool of the decode batch's geometry (16384 blocks
+    x 32 layers x 16 x 8 x 128 codes, one float32 scale per token and kv
+    head), same tables, lengths, offsets and bf16 queries; back to back with
+    the layer rotated.  Algorithmic bytes: every cached token's K and V
+    codes and scales once, q and out (bf16) once, the used table entries,
+    lengths and offsets."""
+    import ctypes
+
+    import torch
+
+    dev = w.q.device
+    shape = (w.num_blocks, w.num_layers, w.block_size, w.num_kv_heads, w.head_dim)
+    k = N.QuantizedPool(*W.int8_pool_tensors(*shape, dev, 8101))
+    v = N.QuantizedPool(*W.int8_pool_tensors(*shape, dev, 8102))
+    lens = w.seq_lens.cpu().numpy()
+    tokens = int(lens.sum())
+    kv = tokens * w.num_kv_heads * (w.head_dim + 4) * 2
+    _, alg_bf16 = decode_bytes(w, lens)
+    kv_bf16 = tokens * w.num_kv_heads * w.head_dim * 2 * 2
+    alg = alg_bf16 - kv_bf16 + kv
+    split = N.paged_attn_decode_schedule(w.num_seqs, w.num_kv_heads, w.num_q_heads, w.head_dim,
+                                         w.max_seq_len, w.block_size, torch.int8, 0)
+    need = N.paged_attn_decode_workspace_size(w.num_seqs, w.num_kv_heads, w.num_q_heads,
+                                              w.head_dim, w.max_seq_len, w.block_size, 0)
+    ws = torch.zeros(max(need, 16), dtype=torch.uint8, device=dev)
+    res = torch.empty_like(w.q)
+    lib = N.load_library()
+    pool = N.make_pool(k, v)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    args = [(ctypes.byref(pool), l, P(w.q), w.num_q_heads, P(w.block_tables),
+             w.block_tables.shape[1], P(w.seq_lens), P(w.offsets), w.num_seqs, w.max_seq_len,
+             ctypes.c_float(w.scale), 0, P(res), P(ws), ws.numel(), stream)
+            for l in range(w.num_layers)]
+    for i in range(3):
+        if lib.paged_attn_decode(*args[i]):
+            raise RuntimeError("int8 paged_attn_decode failed")
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for i in range(reps):
+        lib.paged_attn_decode(*args[i % w.num_layers])
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) / reps * 1e3
+    g = w.num_q_heads // w.num_kv_heads
+    out = {"us": us, "algorithmic_bytes": alg, "GB/s": alg / us / 1e3,
+           "frac": alg / us / 1e3 / HBM_PEAK_GBS,
+           "kernel": f"decode_q8_kernel<D={w.head_dim},G={g}> (split {split})",
+           "kv_bytes_vs_bf16": kv / kv_bf16}
+    del k, v, ws, res
+    torch.cuda.empty_cache()
+    return out
+
+
 def time_op(fn, reps, layers, warm=3):
     """Median and mean of per-call HIP-event times (ms) of fn(layer), with
     the layer rotated so repeats touch different memory."""
@@ -674,6 +730,8 @@ def main():
         result["ops"].update(block_ops(w, N))
         log("decode on the prefix-sharing and long-context batches")
         result["other_decode"] = other_decode_configs(w, N, W)
+        log("int8 pool decode on the decode batch")
+        result["int8_decode"] = int8_decode(w, N, W)
         log("host block manager")
         result["block_manager"] = block_manager_host(N, W)
     if not args.no_cpu_baseline:

@@ -829,11 +829,15 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
 // Quantised (int8) pools, split schedule [P3 sec. 6 names quantised KV; the
 // stored value of a (token, kv head) row is code * scale].  The pipeline of
 // decode_mfma_kernel with half the bytes per token:
-//   K: lane (n, g4) loads row n's codes [D/4 g4, D/4 (g4+1)) and converts
-//      them to bf16 in registers (exact: |code| <= 127); QK^T step j takes
-//      codes 8j .. 8j+7 of that range, so the query fragments are loaded in
-//      the same (permuted) order -- a dot product does not care.  The
-//      score of token t is (q . code_t) * kscale_t * scale.
+//   K: QK^T runs on the int8 matrix cores (v_mfma_i32_16x16x64_i8) on the
+//      codes as loaded: lane (n, g4) loads row n's codes [D/4 g4, D/4 (g4+1))
+//      and step j (64 codes) takes 16 of them; the query operand holds the
+//      same positions of head n, so the exact int32 sums are dot products
+//      whatever order the unit adds them in.  The bf16 query is split per
+//      head into two int8 parts, q ~ qh * sh + ql * sl (sh = max|q| / 127,
+//      sl = sh / 254: |error| <= max|q| / 64516 per element, finer than the
+//      bf16 query itself), so a score is
+//      (sh * (qh . code_t) + sl * (ql . code_t)) * kscale_t * scale.
 //   V: each lane loads 16 codes of a row, converts them and writes the
 //      bf16 row pieces into the wave's V tile in the bf16 kernel's tile
 //      layout; P.V then reads it with the same transposing LDS read.  The
@@ -846,11 +850,12 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
 //   their score is -inf and their P' exactly 0.
 // ---------------------------------------------------------------------------
 
-// Two int8 codes (bytes sh/8, sh/8 + 1 of w) as a bf16 pair.
+// Two int8 codes (bytes sh/8, sh/8 + 1 of w) as a bf16 pair: the high
+// halves of their exact float values.
 __device__ __forceinline__ uint32_t i8pair_bf16(uint32_t w, int sh) {
     const float lo = (float)(int32_t)(int8_t)(w >> sh);
     const float hi = (float)(int32_t)(int8_t)(w >> (sh + 8));
-    return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+    return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
 }
 
 // 16 codes -> 16 bf16 values (two 16-byte pieces, in order).
@@ -859,16 +864,61 @@ __device__ __forceinline__ void i8x16_bf16(u32x4 c, u32x4 &lo, u32x4 &hi) {
     hi = u32x4{i8pair_bf16(c.z, 0), i8pair_bf16(c.z, 16), i8pair_bf16(c.w, 0), i8pair_bf16(c.w, 16)};
 }
 
-// Q^T fragments in the permuted order: lane (n, g4), step j holds head n's
-// elements D/4 g4 + 8 j .. +8.
+typedef int v4i32 __attribute__((ext_vector_type(4)));
+
+// The query of head n as int8 operands: lane (n, g4), step j holds the hi
+// and lo codes of elements D/4 g4 + 16 j .. +16, and every lane of head n
+// the two scales.  Heads >= G are zero.
+template <int D>
+struct Q8Query {
+    static constexpr int KL = D / 64;
+    v4i32 hi[KL], lo[KL];
+    float sh, sl;
+};
+
+__device__ __forceinline__ uint32_t q8_code(float x, float inv) {
+    return (uint32_t)(int32_t)fminf(fmaxf(__builtin_rintf(x * inv), -127.0f), 127.0f) & 0xffu;
+}
+
 template <int D, int G>
-__device__ __forceinline__ void load_q_q8(const DecodeArgs &a, int seq, int h,
-                                          u32x4 (&qf)[MfmaShape<D>::KS]) {
+__device__ __forceinline__ void load_q_q8(const DecodeArgs &a, int seq, int h, Q8Query<D> &qq) {
+    constexpr int KL = D / 64;
     const int lane = threadIdx.x & 63;
     const int n = lane & 15, g4 = lane >> 4;
     const char *qp = a.q + (((int64_t)seq * a.num_q_heads + (int64_t)h * G + n) * D + (D / 4) * g4) * 2;
+    float x[KL][16];
+    float amax = 0.0f;
 #pragma unroll
-    for (int j = 0; j < MfmaShape<D>::KS; ++j) qf[j] = n < G ? ld16(qp + 16 * j) : u32x4{0, 0, 0, 0};
+    for (int j = 0; j < KL; ++j) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const u32x4 w = n < G ? ld16(qp + 32 * j + 16 * c) : u32x4{0, 0, 0, 0};
+            unpack16<1>(w, &x[j][8 * c]);
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(x[j][e]));
+    }
+    amax = fmaxf(amax, __shfl_xor(amax, 16));
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    const float sh = amax / 127.0f;
+    const float sl = sh / 254.0f;
+    const float ih = amax > 0.0f ? 1.0f / sh : 0.0f;
+    const float il = amax > 0.0f ? 1.0f / sl : 0.0f;
+#pragma unroll
+    for (int j = 0; j < KL; ++j) {
+        uint32_t wh[4] = {0, 0, 0, 0}, wl[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const uint32_t ch = q8_code(x[j][e], ih);
+            const float r = x[j][e] - (float)(int32_t)(int8_t)ch * sh;
+            wh[e >> 2] |= ch << (8 * (e & 3));
+            wl[e >> 2] |= q8_code(r, il) << (8 * (e & 3));
+        }
+        qq.hi[j] = v4i32{(int)wh[0], (int)wh[1], (int)wh[2], (int)wh[3]};
+        qq.lo[j] = v4i32{(int)wl[0], (int)wl[1], (int)wl[2], (int)wl[3]};
+    }
+    qq.sh = sh;
+    qq.sl = sl;
 }
 
 template <int D>
@@ -883,7 +933,7 @@ struct Q8Slot {
 template <int D, int G, bool UB>
 __device__ __forceinline__ void attend_range_q8(const DecodeArgs &a, const Range &R, int64_t jb0,
                                                 const int32_t *bt_s, char *vt, int h,
-                                                const u32x4 (&qf)[MfmaShape<D>::KS], float &m_h,
+                                                const Q8Query<D> &qq, float &m_h,
                                                 float &l_h, f32x4 (&acc)[MfmaShape<D>::NV]) {
     using S = MfmaShape<D>;
     using Slot = Q8Slot<D>;
@@ -969,14 +1019,14 @@ __device__ __forceinline__ void attend_range_q8(const DecodeArgs &a, const Range
             *reinterpret_cast<u32x4 *>(dst) = lo;
             *reinterpret_cast<u32x4 *>(dst + 16) = hi;
         }
-        // K codes -> bf16 operands; scores S[token 4 g4 + i][head n]
-        u32x4 kb[KS];
+        // scores S[token 4 g4 + i][head n] from the codes as loaded
+        v4i32 dh = {0, 0, 0, 0}, dl = {0, 0, 0, 0};
 #pragma unroll
-        for (int i = 0; i < Slot::KL; ++i) i8x16_bf16(sl.k[i], kb[2 * i], kb[2 * i + 1]);
-        f32x4 sacc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int j = 0; j < KS; ++j)
-            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kb[j]), as_bf16x8(qf[j]), sacc, 0, 0, 0);
+        for (int j = 0; j < Slot::KL; ++j) {
+            const v4i32 kc = __builtin_bit_cast(v4i32, sl.k[j]);
+            dh = __builtin_amdgcn_mfma_i32_16x16x64_i8(kc, qq.hi[j], dh, 0, 0, 0);
+            dl = __builtin_amdgcn_mfma_i32_16x16x64_i8(kc, qq.lo[j], dl, 0, 0, 0);
+        }
         const float ksf[4] = {__uint_as_float(sl.ks.x), __uint_as_float(sl.ks.y),
                               __uint_as_float(sl.ks.z), __uint_as_float(sl.ks.w)};
         const float vsf[4] = {__uint_as_float(sl.vs.x), __uint_as_float(sl.vs.y),
@@ -985,7 +1035,8 @@ __device__ __forceinline__ void attend_range_q8(const DecodeArgs &a, const Range
         float cm = kNegInf;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            s[i] = (full || row_live(4 * g4 + i)) ? sacc[i] * ksf[i] * sl2 : kNegInf;
+            const float dot = fmaf((float)dh[i], qq.sh, (float)dl[i] * qq.sl);
+            s[i] = (full || row_live(4 * g4 + i)) ? dot * ksf[i] * sl2 : kNegInf;
             cm = fmaxf(cm, s[i]);
         }
         cm = fmaxf(cm, __shfl_xor(cm, 16));
@@ -1067,14 +1118,14 @@ __global__ __launch_bounds__(256) void decode_q8_kernel(DecodeArgs a) {
     const int64_t jb0 = stage_table(a, it.seq, R, bt_s);
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int h = it.hg * a.heads_per_wg + w;
-    u32x4 qf[S::KS];
-    load_q_q8<D, G>(a, it.seq, h, qf);
+    Q8Query<D> qq;
+    load_q_q8<D, G>(a, it.seq, h, qq);
     float m_h = kNegInf;
     float l_h = 0.0f;
     f32x4 acc[S::NV];
 #pragma unroll
     for (int sl = 0; sl < S::NV; ++sl) acc[sl] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    attend_range_q8<D, G, UB>(a, R, jb0, bt_s, vtiles[w], h, qf, m_h, l_h, acc);
+    attend_range_q8<D, G, UB>(a, R, jb0, bt_s, vtiles[w], h, qq, m_h, l_h, acc);
     float lrow[4];
     head_denominators(l_h, lrow);
     if (direct) {

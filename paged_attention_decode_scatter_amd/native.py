@@ -326,8 +326,9 @@ def paged_attn_decode_split_tokens(num_seqs, num_kv_heads, max_seq_len, block_si
 def paged_attn_decode_schedule(num_seqs, num_kv_heads, num_q_heads, head_dim, max_seq_len,
                                block_size, dtype, split_tokens=0):
     """Tokens per split of the split schedule, or 0 for the balanced
-    schedule, for a pool of torch dtype `dtype`."""
-    code = {torch.float32: 0, torch.bfloat16: 1}.get(dtype)
+    schedule, for a pool of torch dtype `dtype` (torch.int8: a quantised
+    pool)."""
+    code = {torch.float32: 0, torch.bfloat16: 1, torch.int8: 2}.get(dtype)
     if code is None:
         raise PagedKVError("paged_attn_decode_schedule", -2)
     v = load_library().paged_attn_decode_schedule(num_seqs, num_kv_heads, num_q_heads, head_dim,
