@@ -33,6 +33,7 @@ if ROOT not in sys.path:
 
 METRIC = "paged decode-attn KV GB/s & % HBM peak; scatter/gather GB/s"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix-core peak of MI355X
 
 
 def log(msg):
@@ -152,6 +153,55 @@ def other_decode_configs(w, N, W, reps=32):
         out[name] = entry
         del o, ws, res
     return out
+
+
+def prefill_attention(w, N, W, reps=6):
+    """Prefill / append attention on the prefix-sharing batch (64 sequences
+    whose first 32 blocks are shared, from a common first-block offset):
+    every suffix token is a query, attending causally to the shared prefix
+    and its own earlier tokens, read in place.  Over the decode batch's
+    pools (same geometry), layer rotated, back to back.  Algorithmic work:
+    4 * head_dim flops per (query, visible key, query head) -- QK^T and P.V
+    -- against the dense bf16 matrix-core peak."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    dev = w.q.device
+    o = W.prefix_sharing(device=dev, with_pools=False)
+    lens = o.seq_lens.cpu().numpy().astype(np.int64)
+    prefix = int(o.meta["shared_blocks"]) * o.block_size
+    counts = np.array([max(1, int(l) - prefix) for l in lens], np.int64)
+    q_start = torch.from_numpy(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)).to(dev)
+    rows = int(counts.sum())
+    q = torch.empty((rows, o.num_q_heads, o.head_dim), dtype=o.dtype, device=dev)
+    W.fill_normal_(q, 8201)
+    out = torch.empty_like(q)
+    # pairs (query, visible key): query i of n sits at position L - n + i
+    pairs = int(sum(n * (l - n) + n * (n + 1) // 2 for n, l in zip(counts, lens)))
+    flops = pairs * o.num_q_heads * 4 * o.head_dim
+    lib = N.load_library()
+    pool = N.make_pool(w.k_pool, w.v_pool)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    args = [(ctypes.byref(pool), l, P(q), o.num_q_heads, P(q_start), rows, int(counts.max()),
+             P(o.block_tables), o.block_tables.shape[1], P(o.seq_lens), P(o.offsets), o.num_seqs,
+             ctypes.c_float(o.scale), P(out), stream) for l in range(w.num_layers)]
+    if lib.paged_attn_prefill(*args[0]):
+        raise RuntimeError("paged_attn_prefill failed")
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for i in range(reps):
+        lib.paged_attn_prefill(*args[(i + 1) % w.num_layers])
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    g = o.num_q_heads // o.num_kv_heads
+    return {"query_rows": rows, "query_key_pairs": pairs, "flops": flops, "ms": ms,
+            "TFLOP/s": flops / ms / 1e9, "frac_of_bf16_mfma_peak": flops / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS,
+            "kernel": f"prefill_mfma_kernel<D={o.head_dim},G={g}>"}
 
 
 def int8_decode(w, N, W, reps=32):
@@ -730,6 +780,8 @@ def main():
         result["ops"].update(block_ops(w, N))
         log("decode on the prefix-sharing and long-context batches")
         result["other_decode"] = other_decode_configs(w, N, W)
+        log("prefill attention on the prefix-sharing batch")
+        result["prefill_attention"] = prefill_attention(w, N, W)
         log("int8 pool decode on the decode batch")
         result["int8_decode"] = int8_decode(w, N, W)
         log("host block manager")

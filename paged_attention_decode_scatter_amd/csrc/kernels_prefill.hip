@@ -9,13 +9,16 @@
 // blocks are shared attends to them without copies.  A query with P_i < 0
 // (more queries than tokens) sees nothing and gets zeros.  n = 1 is decode.
 //
-// bf16 kernel (matrix cores).  Workgroup = (kv head, sequence, tile of 16
-// queries), G wavefronts; wavefront w handles query head kv*G + w, and its
-// 16 MFMA columns are the tile's 16 queries.  Per 16-position chunk of keys:
+// bf16 kernel (matrix cores).  Workgroup = (kv head, sequence, query
+// tile), 8 wavefronts; wavefront w handles query head kv*G + w % G and the
+// tile's (w / G)-th group of 32 or 64 queries, in sub-tiles of 16 that are
+// its MFMA columns.  Per 16-position chunk of keys:
 //   the workgroup loads the chunk's K rows (registers, then a padded LDS
-//   tile) and V rows (straight into LDS) once for all G wavefronts, three
-//   chunks in a ring so two are in flight; one barrier per chunk;
-//   every wavefront then does S^T = K . Q^T (v_mfma_f32_16x16x32_bf16),
+//   tile) and V rows (straight into LDS) once for all 8 wavefronts, a ring
+//   of kPrefillRing chunks so all but one are in flight; one barrier per
+//   chunk; each
+//   wavefront reads the chunk's K and V operand fragments once, and for
+//   each of its sub-tiles does S^T = K . Q^T (v_mfma_f32_16x16x32_bf16),
 //   masks per element (outside the sequence, missing block, or key after
 //   the query), runs the online softmax per query column (lazy reference
 //   max, exp2 domain) and O += P . V (v_mfma_f32_16x16x16_bf16 with the
@@ -53,13 +56,18 @@ __device__ __forceinline__ int64_t stage_entries(const PrefillArgs &a, int seq, 
 }  // namespace
 
 template <int D, int G, bool UB>
-__global__ __launch_bounds__(64 * G) void prefill_mfma_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per_eu(2))) void prefill_mfma_kernel(
+    PrefillArgs a) {
     using S = MfmaShape<D>;
     constexpr int ROWB = S::ROWB, PPR = S::PPR, NP = S::NP, KS = S::KS, NV = S::NV;
     constexpr int VSLAB = S::VSLAB, VTILE = S::VTILE, KROW = S::KROW, KTILE = S::KTILE;
-    constexpr int NB = 3;                       // chunks in the LDS ring
-    constexpr int LPW = (NP + G - 1) / G;       // tile-load instructions per loading wave
+    constexpr int NB = kPrefillRing;            // chunks in the LDS ring
+    constexpr int NW = kPrefillWaves;           // wavefronts: G heads x NW / G query groups
+    constexpr int LPW = (NP + NW - 1) / NW;     // tile-load instructions per loading wave
+    constexpr int QW = kPrefillWaveQueries<D, G>;   // queries per wavefront
+    constexpr int QT = QW / 16;                 // 16-query sub-tiles per wavefront
     constexpr float kLazy = 8.0f;
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
     __shared__ int32_t bt_s[kBtLds];
     __shared__ __attribute__((aligned(16))) char ktile[NB][KTILE];
     __shared__ __attribute__((aligned(16))) char vtile[NB][VTILE];
@@ -76,31 +84,45 @@ __global__ __launch_bounds__(64 * G) void prefill_mfma_kernel(PrefillArgs a) {
     const int hk = rest / a.num_seqs;
     const int64_t row0 = a.q_start[seq];
     const int64_t n = (int64_t)a.q_start[seq + 1] - row0;
-    const int q0 = 16 * tile;
-    if (q0 >= n) return;  // uniform
-    const int nq = (int)min((int64_t)16, n - q0);
+    const int qt0 = kPrefillTile<D, G> * tile;    // the workgroup's first query
+    const int64_t nlim = min(n, (int64_t)a.max_q_len);   // queries computed
+    if (qt0 >= nlim) return;  // uniform
     const int64_t L = a.seq_lens[seq];
     const int64_t off = a.offsets[seq];
-    const int64_t pmax = L - n + q0 + nq - 1;   // last query's position
+    // last query position of the workgroup: the key range it stages
+    const int64_t pmax = L - n + min((int64_t)qt0 + kPrefillTile<D, G>, nlim) - 1;
 
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    const int cn = lane & 15;   // MFMA column: query q0 + cn / output column
+    const int cn = lane & 15;   // MFMA column: query q0 + 16 t + cn / output column
     const int g4 = lane >> 4;
-    const int hq = hk * G + w;
-    const int64_t qpos = cn < nq ? L - n + q0 + cn : -1;   // this column's query position
+    const int hq = hk * G + w % G;
+    // this wavefront's queries: q0 .. q0 + nq - 1 (nq may be <= 0: it then
+    // only helps load and takes part in the barriers)
+    const int q0 = qt0 + QW * (w / G);
+    const int nq = (int)max((int64_t)0, min((int64_t)QW, nlim - q0));
+    const int64_t pmin = L - n + q0;            // its first query's position
 
-    // Q^T fragments: column cn = query q0 + cn of head hq
-    u32x4 qf[KS];
-    {
-        const char *qp = a.q + ((row0 + q0 + cn) * a.num_q_heads + hq) * (int64_t)(D * 2) + 16 * g4;
+    // Q^T fragments of sub-tile t: column cn = query q0 + 16 t + cn of head hq
+    u32x4 qf[QT][KS];
+    int qpos[QT];       // this column's query position in sub-tile t (-1: none)
 #pragma unroll
-        for (int j = 0; j < KS; ++j) qf[j] = cn < nq ? ld16(qp + 64 * j) : u32x4{0, 0, 0, 0};
+    for (int t = 0; t < QT; ++t) {
+        const int qi = 16 * t + cn;
+        qpos[t] = qi < nq ? (int)(pmin + qi) : -1;
+        const char *qp = a.q + ((row0 + q0 + qi) * a.num_q_heads + hq) * (int64_t)(D * 2) + 16 * g4;
+#pragma unroll
+        for (int j = 0; j < KS; ++j) qf[t][j] = qi < nq ? ld16(qp + 64 * j) : u32x4{0, 0, 0, 0};
     }
-    float m_h = kNegInf, l_h = 0.0f;
-    f32x4 acc[NV];
+    float m_h[QT], l_h[QT];
+    f32x4 acc[QT][NV];
 #pragma unroll
-    for (int sl = 0; sl < NV; ++sl) acc[sl] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int t = 0; t < QT; ++t) {
+        m_h[t] = kNegInf;
+        l_h[t] = 0.0f;
+#pragma unroll
+        for (int sl = 0; sl < NV; ++sl) acc[t][sl] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
 
     const int lbs = a.pool.lbs;
     const int64_t bsm = (1ll << lbs) - 1;
@@ -129,7 +151,7 @@ __global__ __launch_bounds__(64 * G) void prefill_mfma_kernel(PrefillArgs a) {
                 char *dst = vtile[slot];
 #pragma unroll
                 for (int k = 0; k < LPW; ++k) {
-                    const int i = w + G * k;
+                    const int i = w + NW * k;
                     if (i < NP) {
                         const int64_t p = pc + i + NP * trow;
                         int32_t b;
@@ -163,14 +185,15 @@ __global__ __launch_bounds__(64 * G) void prefill_mfma_kernel(PrefillArgs a) {
                     if (!done) {
                         // chunk pc's loads done (the next chunk's stay in flight)
                         if (loader) {
-                            constexpr int ahead = 2 * LPW;
+                            constexpr int ahead = (NB - 2) * 2 * LPW;   // later chunks' loads
+                            static_assert(ahead < 64, "vmcnt range");
                             __builtin_amdgcn_s_waitcnt((ahead & 15) | ((ahead >> 4) << 14) | (0x7 << 4) | (0xF << 8));
                         }
                         wave_lds_order();
                         if (loader) {
 #pragma unroll
                             for (int k = 0; k < LPW; ++k) {
-                                const int i = w + G * k;
+                                const int i = w + NW * k;
                                 if (i < NP) {
                                     *reinterpret_cast<u32x4 *>(ktile[q] + (i + NP * trow) * KROW + 16 * tpp) =
                                         kring[q][k];
@@ -180,62 +203,87 @@ __global__ __launch_bounds__(64 * G) void prefill_mfma_kernel(PrefillArgs a) {
                                 }
                             }
                         }
-                        __syncthreads();  // chunk pc's tiles complete; slot (q+2)%NB free
+                        __syncthreads();  // chunk pc's tiles complete; slot (q+NB-1)%NB free
                         const int nq2 = (q + NB - 1) % NB;
                         load_chunk(min(pc + 16 * (NB - 1), last), kring[nq2], nq2);
 
-                        // S^T: lane holds S[token 4*g4 + i][query cn]
+                        // the chunk's K operand (A) and V operand (B) fragments,
+                        // read once and used by every sub-tile
                         const char *kt = ktile[q];
                         const char *vt = vtile[q];
-                        f32x4 sacc = {0.0f, 0.0f, 0.0f, 0.0f};
+                        u32x4 kf[KS];
 #pragma unroll
-                        for (int j = 0; j < KS; ++j) {
-                            const u32x4 kf = *reinterpret_cast<const u32x4 *>(kt + cn * KROW + 16 * g4 + 64 * j);
-                            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf), as_bf16x8(qf[j]), sacc, 0,
-                                                                           0, 0);
+                        for (int j = 0; j < KS; ++j)
+                            kf[j] = *reinterpret_cast<const u32x4 *>(kt + cn * KROW + 16 * g4 + 64 * j);
+                        s16x4 vb[NV];
+                        {
+                            const int vrow = 4 * g4 + (cn >> 2);
+                            const int vbase = (vrow % NP) * VSLAB + (vrow / NP) * ROWB + 8 * (cn & 3);
+#pragma unroll
+                            for (int sl = 0; sl < NV; ++sl)
+                                vb[sl] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                    (__attribute__((address_space(3))) s16x4 *)((__attribute__((address_space(3))) char *)(
+                                                                                   const_cast<char *>(vt)) +
+                                                                               vbase + 32 * sl));
                         }
-                        float s[4];
-                        float cm = kNegInf;
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const int row = 4 * g4 + i;
-                            const bool live = row_ok(pc, row) && pc + row - off <= qpos;
-                            s[i] = live ? sacc[i] * sl2 : kNegInf;
-                            cm = fmaxf(cm, s[i]);
+                        // no mask needed: every row a live token at or before
+                        // the wavefront's first query (wave-uniform); the
+                        // selects below then keep every score
+                        bool full = nq > 0 && pc >= lo && pc + 16 <= phi && pc + 15 - off <= pmin;
+                        if constexpr (UB) {
+                            full = full && bt_s[(int)((pc >> lbs) - jb0)] >= 0;
+                        } else {
+                            full = false;   // rows may sit in different blocks
                         }
-                        cm = fmaxf(cm, __shfl_xor(cm, 16));
-                        cm = fmaxf(cm, __shfl_xor(cm, 32));
-                        float alpha = 1.0f;
-                        if (cm > m_h + kLazy) {
-                            alpha = m_h == kNegInf ? 0.0f : fast_exp2(m_h - cm);
-                            m_h = cm;
-                        }
-                        float pr[4];
+                        // masked chunks: row i of this lane is live and holds the
+                        // key at logical position kp0 + i
+                        const int kp0 = (int)(pc - off) + 4 * g4;
+                        bool rok[4];
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) pr[i] = s[i] == kNegInf ? 0.0f : fast_exp2(s[i] - m_h);
-                        const uint32_t p01 = f32_to_bf16_bits(pr[0]) | (f32_to_bf16_bits(pr[1]) << 16);
-                        const uint32_t p23 = f32_to_bf16_bits(pr[2]) | (f32_to_bf16_bits(pr[3]) << 16);
-                        l_h = fmaf(l_h, alpha, (bf16_lo(p01) + bf16_hi(p01)) + (bf16_lo(p23) + bf16_hi(p23)));
-                        if (__any(alpha != 1.0f)) {
+                        for (int i = 0; i < 4; ++i) rok[i] = !full && row_ok(pc, 4 * g4 + i);
+                        auto subtile = [&](int t) {
+                            // S^T: lane holds S[token 4*g4 + i][query 16 t + cn]
+                            f32x4 sacc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                            for (int i = 0; i < 4; ++i) {
-                                const float al = __shfl(alpha, 4 * g4 + i);
+                            for (int j = 0; j < KS; ++j)
+                                sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[j]), as_bf16x8(qf[t][j]),
+                                                                               sacc, 0, 0, 0);
+                            float s[4];
 #pragma unroll
-                                for (int sl = 0; sl < NV; ++sl) acc[sl][i] *= al;
+                            for (int i = 0; i < 4; ++i)
+                                s[i] = (full || (rok[i] && kp0 + i <= qpos[t])) ? sacc[i] * sl2 : kNegInf;
+                            float cm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+                            cm = fmaxf(cm, __shfl_xor(cm, 16));
+                            cm = fmaxf(cm, __shfl_xor(cm, 32));
+                            float alpha = 1.0f;
+                            if (cm > m_h[t] + kLazy) {
+                                alpha = m_h[t] == kNegInf ? 0.0f : fast_exp2(m_h[t] - cm);
+                                m_h[t] = cm;
                             }
-                        }
-                        typedef short s16x4 __attribute__((ext_vector_type(4)));
-                        const s16x4 pa = __builtin_bit_cast(s16x4, (uint64_t)p01 | ((uint64_t)p23 << 32));
-                        const int vrow = 4 * g4 + (cn >> 2);
-                        const int vbase = (vrow % NP) * VSLAB + (vrow / NP) * ROWB + 8 * (cn & 3);
+                            // exp2(-inf - m) = 0 for the masked entries; a column with
+                            // no live key so far (m = -inf) subtracts 0 instead
+                            const float mr = m_h[t] == kNegInf ? 0.0f : m_h[t];
+                            float pr[4];
 #pragma unroll
-                        for (int sl = 0; sl < NV; ++sl) {
-                            const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                (__attribute__((address_space(3))) s16x4 *)((__attribute__((address_space(3))) char *)(
-                                                                               const_cast<char *>(vt)) +
-                                                                           vbase + 32 * sl));
-                            acc[sl] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, acc[sl], 0, 0, 0);
-                        }
+                            for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(s[i] - mr);
+                            const uint32_t p01 = pack_bf16x2(pr[0], pr[1]);
+                            const uint32_t p23 = pack_bf16x2(pr[2], pr[3]);
+                            l_h[t] = fmaf(l_h[t], alpha, (bf16_lo(p01) + bf16_hi(p01)) + (bf16_lo(p23) + bf16_hi(p23)));
+                            if (__builtin_amdgcn_readfirstlane((int)__any(alpha != 1.0f))) {
+#pragma unroll
+                                for (int i = 0; i < 4; ++i) {
+                                    const float al = __shfl(alpha, 4 * g4 + i);
+#pragma unroll
+                                    for (int sl = 0; sl < NV; ++sl) acc[t][sl][i] *= al;
+                                }
+                            }
+                            const s16x4 pa = __builtin_bit_cast(s16x4, (uint64_t)p01 | ((uint64_t)p23 << 32));
+#pragma unroll
+                            for (int sl = 0; sl < NV; ++sl)
+                                acc[t][sl] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb[sl], acc[t][sl], 0, 0, 0);
+                        };
+#pragma unroll
+                        for (int t = 0; t < QT; ++t) subtile(t);
                         pc += 16;
                         done = pc > last;
                     }
@@ -246,18 +294,22 @@ __global__ __launch_bounds__(64 * G) void prefill_mfma_kernel(PrefillArgs a) {
         }
     }
 
-    // out[row, hq, :] = acc / l for the tile's queries (rows 4*g4 + i)
-    l_h += __shfl_xor(l_h, 16);
-    l_h += __shfl_xor(l_h, 32);
+    // out[row, hq, :] = acc / l for the tile's queries (sub-tile t, rows 4*g4 + i)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int qi = 4 * g4 + i;
-        const float lq = __shfl(l_h, qi);
-        if (qi < nq) {
-            uint16_t *o = reinterpret_cast<uint16_t *>(a.out) + ((row0 + q0 + qi) * a.num_q_heads + hq) * D + cn;
+    for (int t = 0; t < QT; ++t) {
+        float lt = l_h[t];
+        lt += __shfl_xor(lt, 16);
+        lt += __shfl_xor(lt, 32);
 #pragma unroll
-            for (int sl = 0; sl < NV; ++sl)
-                o[16 * sl] = (uint16_t)f32_to_bf16_bits(lq > 0.0f ? acc[sl][i] / lq : 0.0f);
+        for (int i = 0; i < 4; ++i) {
+            const int qi = 16 * t + 4 * g4 + i;
+            const float lq = __shfl(lt, 4 * g4 + i);
+            if (qi < nq) {
+                uint16_t *o = reinterpret_cast<uint16_t *>(a.out) + ((row0 + q0 + qi) * a.num_q_heads + hq) * D + cn;
+#pragma unroll
+                for (int sl = 0; sl < NV; ++sl)
+                    o[16 * sl] = (uint16_t)f32_to_bf16_bits(lq > 0.0f ? acc[t][sl][i] / lq : 0.0f);
+            }
         }
     }
 }
@@ -287,6 +339,7 @@ __global__ __launch_bounds__(256) void prefill_valu_kernel(PrefillArgs a) {
     const int seq = lo;
     const int64_t n = (int64_t)a.q_start[seq + 1] - a.q_start[seq];
     const int64_t qi = row - a.q_start[seq];
+    if (qi >= a.max_q_len) return;  // uniform: queries past max_q_len are not computed
     const int64_t L = a.seq_lens[seq];
     const int64_t off = a.offsets[seq];
     const int64_t P = L - n + qi;
@@ -402,9 +455,9 @@ hipError_t run_prefill(const PrefillArgs &a, hipStream_t s) {
     if constexpr (DT == 1) {
         const int64_t nwg = (int64_t)a.q_tiles * a.num_seqs * a.num_kv_heads;
         if (a.pool.lbs >= 4)
-            hipLaunchKernelGGL((prefill_mfma_kernel<D, G, true>), dim3((unsigned)nwg), dim3(64 * G), 0, s, a);
+            hipLaunchKernelGGL((prefill_mfma_kernel<D, G, true>), dim3((unsigned)nwg), dim3(64 * kPrefillWaves), 0, s, a);
         else
-            hipLaunchKernelGGL((prefill_mfma_kernel<D, G, false>), dim3((unsigned)nwg), dim3(64 * G), 0, s, a);
+            hipLaunchKernelGGL((prefill_mfma_kernel<D, G, false>), dim3((unsigned)nwg), dim3(64 * kPrefillWaves), 0, s, a);
     } else {
         const int64_t nwg = (int64_t)a.num_q_rows * a.head_groups;
         hipLaunchKernelGGL((prefill_valu_kernel<DT, D, G>), dim3((unsigned)nwg), dim3(64 * a.heads_per_wg), 0, s,

@@ -641,7 +641,8 @@ PKV_API int paged_attn_prefill(const pkv_pool *pool, int32_t layer, const void *
     if (!aligned16(q) || !aligned16(out)) return PKV_ERR_ALIGN;
     const int64_t hkv = pool->num_kv_heads;
     const int64_t hpw = heads_per_wg(hkv);
-    const int64_t q_tiles = ((int64_t)max_q_len + 15) / 16;
+    const int64_t tile = pool->dtype == PKV_BF16 ? prefill_tile(pool->head_dim, group) : 16;
+    const int64_t q_tiles = ((int64_t)max_q_len + tile - 1) / tile;
     if (q_tiles * num_seqs * hkv > INT32_MAX || (int64_t)num_q_rows * (hkv / hpw) > INT32_MAX)
         return PKV_ERR_SHAPE;
     if (q_tiles == 0) return PKV_OK;
@@ -660,6 +661,7 @@ PKV_API int paged_attn_prefill(const pkv_pool *pool, int32_t layer, const void *
     a.num_q_heads = num_q_heads;
     a.num_q_rows = num_q_rows;
     a.q_tiles = (int32_t)q_tiles;
+    a.max_q_len = max_q_len;
     a.heads_per_wg = (int32_t)hpw;
     a.head_groups = (int32_t)(hkv / hpw);
     a.seg_chunks = (int32_t)(max_split_tokens(pool->block_size) / kChunkTokens);

@@ -159,6 +159,33 @@ constexpr int kSegMax = 80;
 
 // Prefill / append attention: the last n_s = q_start[s+1] - q_start[s]
 // tokens of sequence s are its queries (rows q_start[s].. of q and out).
+// Prefill (bf16 kernel) workgroups: kPrefillWaves wavefronts, G query heads
+// x kPrefillWaves / G query groups, sharing every staged key chunk.  A
+// wavefront holds kPrefillWaveQueries queries (sub-tiles of 16), as many as
+// fit two wavefronts per SIMD without spills; a workgroup tile is
+// kPrefillTile queries.  Measured on MI355X (prefix-sharing batch, every
+// suffix token a query, head_dim 128, G 4): 16 queries per wavefront
+// 11.2 ms, 32: 8.3 ms, 48: 7.1 ms (64 spills); the depth of the key ring
+// (3 to 8 chunks) changed nothing.
+constexpr int kPrefillWaves = 8;
+#ifndef PKV_PREFILL_WQ64
+#define PKV_PREFILL_WQ64 64
+#endif
+#ifndef PKV_PREFILL_WQ128
+#define PKV_PREFILL_WQ128 48
+#endif
+#ifndef PKV_PREFILL_RING
+#define PKV_PREFILL_RING 3
+#endif
+constexpr int kPrefillRing = PKV_PREFILL_RING;   // key chunks staged in LDS (all but one in flight)
+template <int D, int G>
+inline constexpr int kPrefillWaveQueries = D == 64 ? PKV_PREFILL_WQ64 : PKV_PREFILL_WQ128;
+template <int D, int G>
+inline constexpr int kPrefillTile = kPrefillWaveQueries<D, G> * (kPrefillWaves / G);
+inline int prefill_tile(int64_t head_dim, int64_t group) {
+    return (head_dim == 64 ? PKV_PREFILL_WQ64 : PKV_PREFILL_WQ128) * (kPrefillWaves / (int)group);
+}
+
 struct PrefillArgs {
     PoolView pool;
     const char *q;
@@ -173,7 +200,8 @@ struct PrefillArgs {
     int32_t num_kv_heads;
     int32_t num_q_heads;
     int32_t num_q_rows;
-    int32_t q_tiles;       // 16-query tiles per sequence in the grid
+    int32_t q_tiles;       // query tiles (prefill_tile queries) per sequence in the grid
+    int32_t max_q_len;     // queries past it in a sequence are not computed
     int32_t heads_per_wg;  // fp32 kernel: kv heads per workgroup
     int32_t head_groups;
     int32_t seg_chunks;    // most 16-position chunks staged at once

@@ -88,6 +88,19 @@ def test_prefill_small_grid(dev, dtype, head_dim, group):
     assert max_abs_err(got, ref) <= TOL[dtype]
 
 
+@pytest.mark.parametrize("group,head_dim", [(1, 128), (1, 64), (2, 128), (8, 64)])
+def test_prefill_spans_several_workgroup_tiles(dev, group, head_dim):
+    """Long query runs: several workgroup tiles per sequence (up to 384
+    queries each for G = 1), ragged last tiles and wavefront groups with no
+    query left."""
+    w = small(dev, head_dim=head_dim, group=group, seed=150 + group, num_seqs=3, min_len=900,
+              max_len=1300)
+    lens = host(w.seq_lens)
+    q, qs = queries(w, [int(lens[0]), 800, 397], 250 + group)
+    got = run(w, q, qs)
+    assert max_abs_err(got, oracle_for(w, q, qs)) <= TOL[w.dtype]
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_prefill_whole_prompt(dev, dtype):
     """n = L: the whole prompt is new (plain causal attention); the first
@@ -169,17 +182,20 @@ def test_prefill_ignores_unowned_nan_slots(dev, dtype):
     assert max_abs_err(got, oracle_for(w, q, qs)) <= TOL[dtype]
 
 
-def test_prefill_rows_beyond_max_q_len_are_untouched(dev):
-    """max_q_len bounds the tiles launched; rows of a sequence past it are
-    left as they were (here NaN), the rest are computed."""
-    w = small(dev, seed=140, num_seqs=2, min_len=100, max_len=100, offsets=None)
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("mq", [32, 20])
+def test_prefill_rows_beyond_max_q_len_are_untouched(dev, dtype, mq):
+    """max_q_len bounds the queries computed per sequence: rows of a
+    sequence past it are left as they were (here NaN), the rest are
+    computed (also when max_q_len is not a multiple of the query tile)."""
+    w = small(dev, dtype=dtype, seed=140, num_seqs=2, min_len=100, max_len=100, offsets=None)
     q, qs = queries(w, [40, 10], 240)
-    got = run(w, q, qs, max_q_len=32)
+    got = run(w, q, qs, max_q_len=mq)
     ref = oracle_for(w, q, qs)
-    assert torch.all(torch.isnan(got[32:40]))
+    assert torch.all(torch.isnan(got[mq:40]))
     keep = torch.ones(50, dtype=torch.bool)
-    keep[32:40] = False
-    assert max_abs_err(got[keep.to(dev)], ref[keep.numpy()]) <= 2e-2
+    keep[mq:40] = False
+    assert max_abs_err(got[keep.to(dev)], ref[keep.numpy()]) <= TOL[dtype]
 
 
 def test_prefill_prefix_sharing_full_size(dev):
