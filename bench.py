@@ -66,6 +66,9 @@ def decode_schedule(N, w, split_req):
     g = w.num_q_heads // w.num_kv_heads
     if sched == 0:
         return sched, f"decode_stream_kernel<D={w.head_dim},G={g}> (balanced schedule)"
+    if sched == N.SCHEDULE_PLANNED:
+        return sched, (f"decode_mfma_kernel<D={w.head_dim},G={g}> (device-planned split: pieces fit "
+                       "2 workgroups per CU, merged in the kernel)")
     name = f"decode_mfma_kernel<D={w.head_dim},G={g}>"
     max_splits = -(-(w.max_seq_len + w.block_size - 1) // sched)
     if max_splits == 1:

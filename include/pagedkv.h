@@ -221,6 +221,10 @@ PKV_API int kv_gather(const pkv_pool *pool, int32_t layer,
 
 /* split_tokens value that asks paged_attn_decode for the balanced schedule */
 #define PKV_SPLIT_BALANCED (-1)
+/* split_tokens value that asks paged_attn_decode for the device-planned
+ * split schedule, and the value paged_attn_decode_schedule returns for it */
+#define PKV_SPLIT_PLANNED (-2)
+#define PKV_SCHEDULE_PLANNED 1
 
 /*
  * paged_attn_decode_split_tokens -- the split size (tokens per work item)
@@ -240,17 +244,30 @@ PKV_API int32_t paged_attn_decode_split_tokens(int32_t num_seqs, int32_t num_kv_
  *   > 0  the split schedule with this many tokens per split: one workgroup
  *        per (sequence, split of split_tokens flat positions, group of kv
  *        heads);
+ *     1  (PKV_SCHEDULE_PLANNED) the device-planned split schedule: the
+ *        split schedule with a split size the kernel picks from the actual
+ *        lengths, the smallest multiple of 16 (at least 64 positions, and
+ *        enough for 16 splits per sequence of max_seq_len) whose
+ *        (sequence, split, kv-head group) pieces fit 2 workgroups per
+ *        compute unit; pieces of exactly that many positions take the
+ *        first workgroups, shorter first and last pieces the last ones.
+ *        Taken for bf16 pools when split_tokens = 0 or PKV_SPLIT_PLANNED
+ *        and the batch allows it: at most 64 sequences, at most
+ *        compute units / 2 (sequence, kv-head group) pairs, and
+ *        max_seq_len / 2 + 32 <= the largest split (split_tokens limit
+ *        below);
  *     0  the balanced schedule: one resident generation of workgroups (more
  *        when a share would not fit one pass), each taking an equal share
  *        of all (kv-head group, sequence, 16-position chunk) units.  Taken
  *        for bf16 pools with at most 256 * (kv heads per workgroup: 4, 2
  *        or 1, the largest dividing num_kv_heads) sequences when
- *        split_tokens = PKV_SPLIT_BALANCED, or when split_tokens = 0 and
- *        the batch has at least 32 sequences and 512 MiB of K/V at
- *        max_seq_len;
+ *        split_tokens = PKV_SPLIT_BALANCED, or when split_tokens = 0, the
+ *        planned schedule is not possible, and the batch has at least 32
+ *        sequences and 512 MiB of K/V at max_seq_len;
  *   < 0  a status for bad sizes or dtype (PKV_ERR_UNSUPPORTED for a
- *        balanced request on an fp32 pool or too many sequences).
- * Both compute the same function; they differ only in fp32 rounding order.
+ *        balanced request on an fp32 pool or too many sequences, or a
+ *        planned request the batch does not allow).
+ * All compute the same function; they differ only in fp32 rounding order.
  */
 PKV_API int32_t paged_attn_decode_schedule(int32_t num_seqs, int32_t num_kv_heads,
                                            int32_t num_q_heads, int32_t head_dim,
@@ -288,15 +305,22 @@ PKV_API size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_kv
  *   scale         softmax scale (e.g. 1/sqrt(head_dim))
  *   split_tokens  0 = automatic (see paged_attn_decode_schedule);
  *                 PKV_SPLIT_BALANCED = the balanced schedule (bf16 pools,
- *                 sequence limit as above, else PKV_ERR_UNSUPPORTED); else the
+ *                 sequence limit as above, else PKV_ERR_UNSUPPORTED);
+ *                 PKV_SPLIT_PLANNED = the device-planned split schedule
+ *                 (limits as above, else PKV_ERR_UNSUPPORTED); else the
  *                 tokens per split-K work item, a positive multiple of 16
  *                 with split_tokens/block_size + 2 <= 1024.  A sequence
  *                 spread over several work items is computed as partial
  *                 softmaxes, merged (log-sum-exp) by the work item that
  *                 finishes last (or, past 16 splits, by a second kernel),
  *                 in a fixed order; the partition depends only on the
- *                 sizes and the device's compute-unit count, so results
- *                 are bitwise reproducible run to run.
+ *                 sizes, the lengths and offsets, and the device's
+ *                 compute-unit count, so results are bitwise reproducible
+ *                 run to run.  In the planned schedule a sequence longer
+ *                 than max_seq_len is attended over its first max_seq_len
+ *                 tokens and an offset outside [0, block_size) is clamped
+ *                 into it (both break the contract; no access leaves the
+ *                 buffers).
  *   out           device [num_seqs, num_q_heads, head_dim], pool dtype
  *   workspace     device scratch of at least
  *                 paged_attn_decode_workspace_size(...) bytes (may be NULL

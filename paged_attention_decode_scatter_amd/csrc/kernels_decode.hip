@@ -170,6 +170,200 @@ __device__ void zero_outputs(const DecodeArgs &a, int seq, int hg) {
     for (int64_t i = threadIdx.x; i < n; i += blockDim.x) o[i] = 0u;
 }
 
+// ---------------------------------------------------------------------------
+// Device-planned split schedule (bf16, a.plan = number of workgroups).  The
+// host knows only the largest sequence length, so a split it picks cannot
+// fit the batch: with the lengths of the decode batch the automatic
+// 256-token split leaves 30 of 256 compute units without a live work item
+// while 96 hold two, most of them full.  Here every workgroup reads all
+// lengths and offsets (the memory round trip it already makes for its
+// own), picks the smallest split S (a multiple of 16, at least
+// a.split_tokens) whose pieces -- the splits of "Work decomposition"
+// above, per (sequence, head group) -- fit the grid, and takes piece number
+// blockIdx.x in an order that spreads them: pieces of exactly S positions
+// from the front of the grid, shorter ones (a sequence's first and last)
+// from the back.  With two resident workgroups per compute unit,
+// workgroups b and b + gridDim/2 share one, so a compute unit holds at most
+// two pieces of at most S positions each.
+// The host guarantees a feasible S: gridDim.x >= n * head_groups *
+// a.max_splits (then S = a.split_tokens fits), or gridDim.x >= 4 * n *
+// head_groups (then the bound below fits), n <= kPlanMaxSeqs (one per lane
+// of one wavefront) and positions below 2^24.
+// The whole plan runs in wavefront 0, in registers: this is the latency
+// before the first table entry can be fetched.
+// ---------------------------------------------------------------------------
+
+// floor(x / d) for 0 <= x < 2^24, 16 <= d or x / d < 2^20, d > 0, from an
+// approximate reciprocal (relative error below 2^-22, so the float
+// quotient is within 1 of the true one) and one correction step.
+__device__ __forceinline__ int32_t udiv24(int32_t x, int32_t d, float rcp) {
+    int32_t q = (int32_t)((float)x * rcp);
+    const int32_t r = x - q * d;
+    if (r < 0) --q;
+    else if (r >= d) ++q;
+    return q;
+}
+
+// Pieces of one sequence (offset o, length L) at split S: first and last
+// split index, the first full piece and the number of full pieces (a piece
+// is full when it covers all S positions of its split), and the number of
+// the others (0, 1 or 2: the first and the last piece).
+struct SeqPieces {
+    int32_t j0, j1, jf0, nf, nq;
+};
+
+__device__ __forceinline__ SeqPieces seq_pieces(int32_t L, int32_t o, int32_t S, float rcp) {
+    SeqPieces p{0, -1, 0, 0, 0};
+    if (L <= 0) return p;
+    p.j0 = udiv24(o, S, rcp);
+    p.j1 = udiv24(o + L - 1, S, rcp);
+    const bool f0 = p.j0 * S >= o && (p.j0 + 1) * S <= o + L;
+    const bool f1 = p.j1 * S >= o && (p.j1 + 1) * S <= o + L;
+    p.jf0 = f0 ? p.j0 : p.j0 + 1;
+    const int32_t jf1 = f1 ? p.j1 : p.j1 - 1;
+    p.nf = jf1 >= p.jf0 ? jf1 - p.jf0 + 1 : 0;
+    p.nq = (p.j1 - p.j0 + 1) - p.nf;
+    return p;
+}
+
+// Row shift-right by K within rows of 16 lanes; lanes with no source read 0.
+template <int K>
+__device__ __forceinline__ int32_t row_shr(int32_t v) {
+    return __builtin_amdgcn_update_dpp(0, v, 0x110 + K, 0xf, 0xf, true);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wavefront (DPP within rows
+// of 16, then the row totals from lanes 15, 31 and 47).
+__device__ __forceinline__ int32_t wave_incl_scan(int32_t v) {
+    v += row_shr<1>(v);
+    v += row_shr<2>(v);
+    v += row_shr<4>(v);
+    v += row_shr<8>(v);
+    const int row = (threadIdx.x & 63) >> 4;
+    const int32_t r0 = __builtin_amdgcn_readlane(v, 15);
+    const int32_t r1 = __builtin_amdgcn_readlane(v, 31);
+    const int32_t r2 = __builtin_amdgcn_readlane(v, 47);
+    return v + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
+}
+
+__device__ __forceinline__ int32_t wave_total(int32_t v) {
+    return __builtin_amdgcn_readlane(wave_incl_scan(v), 63);
+}
+
+struct PlanOut {
+    int32_t seq, g, j, len, off, S, have;
+};
+
+// Sets it, R and S of this workgroup; false if it has no piece.  Uses
+// scratch (the table staging buffer, at least kPlanMaxSeqs entries) for
+// the clamped lengths and ends with a barrier, after which scratch may be
+// reused.  Empty sequences' outputs are zeroed here (sequence s by
+// workgroup s % gridDim.x).  All threads of the workgroup call this.
+// Lane t of wavefront 0 holds sequence t (n <= 64).
+template <int D, int G>
+__device__ bool plan_item(const DecodeArgs &a, int32_t *scratch, Item &it, Range &R, int64_t &S_out) {
+    static_assert(kPlanMaxSeqs <= 64, "one sequence per lane");
+    __shared__ PlanOut po;
+    const int n = a.num_seqs;
+    const int nwg = gridDim.x;
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        const int HG = a.head_groups;
+        const int32_t bsm = (1 << a.pool.lbs) - 1;
+        const bool live = lane < n;
+        int32_t L = live ? a.seq_lens[lane] : 0;
+        int32_t O = live ? a.offsets[lane] : 0;
+        L = L < 0 ? 0 : (L > a.max_len ? a.max_len : L);
+        O = O < 0 ? 0 : (O > bsm ? bsm : O);
+        if (live) scratch[lane] = L;
+        // total length: below 64 * 2^24, summed as L / 16 and L % 16 to
+        // stay in int32 (its float value's rounding is within the margins)
+        const float totf = 16.0f * (float)wave_total(L >> 4) + (float)wave_total(L & 15);
+        // pieces of all pairs at split S
+        auto count = [&](int32_t S) -> int32_t {
+            const float rcp = __builtin_amdgcn_rcpf((float)S);
+            const int32_t c = L > 0 ? udiv24(O + L - 1, S, rcp) - udiv24(O, S, rcp) + 1 : 0;
+            return wave_total(c) * HG;
+        };
+        const int32_t smin = a.split_tokens;
+        // lower end: the pieces number at least HG * total / S, so S >=
+        // HG * total / nwg (a float estimate; one 16-step below is safe)
+        int32_t lo = (int32_t)((float)HG * totf / (float)nwg) - 16;
+        lo = lo < smin ? smin : lo;
+        lo = (lo + 15) >> 4;
+        // upper end, feasible: S = smin when the grid holds every pair's
+        // a.max_splits pieces; else pieces <= HG * (total / S + 2 n) <= nwg
+        // for S >= HG * total / (nwg - 2 HG n), rounded up with margin
+        int32_t hi;
+        if (nwg >= n * HG * a.max_splits) {
+            hi = smin >> 4;
+        } else {
+            const float room = (float)(nwg - 2 * HG * n);  // >= 2 HG n (host)
+            hi = (int32_t)((float)HG * totf / room * 1.0001f) + 2;
+            hi = (hi + 15) >> 4;
+            hi = hi < (smin >> 4) ? (smin >> 4) : hi;
+        }
+        if (lo > hi) lo = hi;
+        if (count(lo * 16) > nwg) {
+            ++lo;
+            while (lo < hi) {
+                const int32_t mid = (lo + hi) >> 1;
+                if (count(mid * 16) <= nwg) hi = mid;
+                else lo = mid + 1;
+            }
+        }
+        const int32_t S = lo * 16;
+        const SeqPieces P = seq_pieces(L, O, S, __builtin_amdgcn_rcpf((float)S));
+        // running totals of full (sf) and other (sq) pieces
+        const int32_t sf = wave_incl_scan(P.nf), sq = wave_incl_scan(P.nq);
+        const int32_t Fs = __builtin_amdgcn_readlane(sf, 63), Qs = __builtin_amdgcn_readlane(sq, 63);
+        const int32_t b = blockIdx.x;
+        PlanOut r{0, 0, 0, 0, 0, S, 0};
+        const bool full = b < HG * Fs;
+        if (full || b >= nwg - HG * Qs) {
+            const int32_t tot_p = full ? Fs : Qs;
+            const int32_t x = full ? b : nwg - 1 - b;
+            const int32_t g = udiv24(x, tot_p, __builtin_amdgcn_rcpf((float)tot_p));
+            const int32_t k = x - g * tot_p;  // rank among this head group's pieces
+            const int32_t incl = full ? sf : sq;
+            const int32_t cnt = full ? P.nf : P.nq;
+            const uint64_t hit = __ballot(cnt > 0 && incl - cnt <= k && k < incl);
+            const int ln = __builtin_ctzll(hit);  // exactly one lane
+            const int32_t base = __builtin_amdgcn_readlane(incl - cnt, ln);
+            const int32_t j0 = __builtin_amdgcn_readlane(P.j0, ln);
+            const int32_t j1 = __builtin_amdgcn_readlane(P.j1, ln);
+            const int32_t jf0 = __builtin_amdgcn_readlane(P.jf0, ln);
+            const int32_t nf = __builtin_amdgcn_readlane(P.nf, ln);
+            r.seq = ln;
+            r.g = g;
+            // the others, in order: the first piece unless it is full, then the last
+            r.j = full ? jf0 + (k - base) : ((k == base && !(nf > 0 && jf0 == j0)) ? j0 : j1);
+            r.len = __builtin_amdgcn_readlane(L, ln);
+            r.off = __builtin_amdgcn_readlane(O, ln);
+            r.have = 1;
+        }
+        if (lane == 0) po = r;
+    }
+    __syncthreads();
+    const PlanOut r = po;
+    // outputs of empty sequences
+    for (int t = blockIdx.x; t < n; t += nwg)
+        if (scratch[t] == 0)
+            for (int g = 0; g < a.head_groups; ++g) zero_outputs<1, D, G>(a, t, g);
+    if (r.have) {
+        it.seq = r.seq;
+        it.hg = r.g;
+        it.split = r.j;
+        R.len = r.len;
+        R.off = r.off;
+        R.lo = max((int64_t)r.j * r.S, R.off);
+        R.hi = min((int64_t)(r.j + 1) * r.S, R.off + R.len);
+    }
+    S_out = r.S;
+    __syncthreads();
+    return r.have != 0;
+}
+
 // Merge of partial results into out for the G query heads of one kv head:
 //   M = max_i m_i,  w_i = 2^(m_i - M),
 //   out = (sum_i w_i acc_i) / (sum_i w_i l_i)
@@ -324,9 +518,8 @@ __device__ bool count_in(uint32_t *cnt, uint32_t expected) {
 // live splits j0 .. j1 of the sequence, each wavefront the G query heads of
 // its kv head.
 template <int DT, int D, int G>
-__device__ void finish_split(const DecodeArgs &a, const Item &it, const Range &R) {
+__device__ void finish_split(const DecodeArgs &a, const Item &it, const Range &R, int64_t S) {
     constexpr int E = Elem<DT>::kBytes;
-    const int64_t S = a.split_tokens;
     const int j0 = (int)(R.off / S);
     const int j1 = (int)((R.off + R.len - 1) / S);
     if (!count_in(a.ws_cnt + (int64_t)it.seq * a.head_groups + it.hg, (uint32_t)(j1 - j0 + 1))) return;
@@ -496,7 +689,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
             if (c == 0) st_dev2(a.ws_ml + item * 2, m[g], l[g]);
         }
     }
-    if (a.fused_merge) finish_split<DT, D, G>(a, it, R);
+    if (a.fused_merge) finish_split<DT, D, G>(a, it, R, a.split_tokens);
 }
 
 // ---------------------------------------------------------------------------
@@ -795,12 +988,21 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     __shared__ int32_t bt_s[kBtLds];
     __shared__ __attribute__((aligned(16))) char vtiles[4][S::NSLOT][S::VTILE];
 
-    const Item it = work_item(a);
-    const Range R = split_range(a, it.seq, it.split);
-    const bool direct = a.max_splits == 1;
-    if (!direct && R.hi <= R.lo) {
-        if (a.fused_merge && R.len <= 0 && it.split == 0) zero_outputs<1, D, G>(a, it.seq, it.hg);
-        return;
+    Item it;
+    Range R;
+    int64_t split = a.split_tokens;
+    bool direct;
+    if (a.plan) {
+        if (!plan_item<D, G>(a, bt_s, it, R, split)) return;
+        direct = R.lo == R.off && R.hi == R.off + R.len;  // the sequence's only piece
+    } else {
+        it = work_item(a);
+        R = split_range(a, it.seq, it.split);
+        direct = a.max_splits == 1;
+        if (!direct && R.hi <= R.lo) {
+            if (a.fused_merge && R.len <= 0 && it.split == 0) zero_outputs<1, D, G>(a, it.seq, it.hg);
+            return;
+        }
     }
     const int64_t jb0 = stage_table(a, it.seq, R, bt_s);
 
@@ -822,7 +1024,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     }
     const int64_t item0 = ((int64_t)it.seq * a.max_splits + it.split) * a.num_q_heads + (int64_t)h * G;
     write_partial<D, G>(a.ws_ml + item0 * 2, a.ws_acc + item0 * D, acc, m_h, l_h);
-    if (a.fused_merge) finish_split<1, D, G>(a, it, R);
+    if (a.fused_merge) finish_split<1, D, G>(a, it, R, split);
 }
 
 // ---------------------------------------------------------------------------
@@ -1134,7 +1336,7 @@ __global__ __launch_bounds__(256) void decode_q8_kernel(DecodeArgs a) {
     }
     const int64_t item0 = ((int64_t)it.seq * a.max_splits + it.split) * a.num_q_heads + (int64_t)h * G;
     write_partial<D, G>(a.ws_ml + item0 * 2, a.ws_acc + item0 * D, acc, m_h, l_h);
-    if (a.fused_merge) finish_split<1, D, G>(a, it, R);
+    if (a.fused_merge) finish_split<1, D, G>(a, it, R, a.split_tokens);
 }
 
 // ---------------------------------------------------------------------------
@@ -1833,7 +2035,7 @@ static hipError_t run_decode(const DecodeArgs &a, hipStream_t s) {
             return hipGetLastError();
         }
     }
-    const int64_t nwg = (int64_t)a.head_groups * a.max_splits * a.num_seqs;
+    const int64_t nwg = a.plan > 0 ? a.plan : (int64_t)a.head_groups * a.max_splits * a.num_seqs;
     const dim3 grid((unsigned)nwg);
     if constexpr (DT == 1) {
         if (a.pool.lbs >= 4)

@@ -162,7 +162,8 @@ int plan_decode(int64_t num_seqs, int64_t hkv, int64_t hq, int64_t head_dim, int
         return PKV_ERR_SHAPE;
     // 0 (automatic) and a balanced-schedule request plan the automatic
     // split too: it sizes the fallback and the workspace bound
-    const int64_t split = split_req == 0 || split_req == PKV_SPLIT_BALANCED
+    const int64_t split = split_req == 0 || split_req == PKV_SPLIT_BALANCED ||
+                                  split_req == PKV_SPLIT_PLANNED
                               ? auto_split(num_seqs, hkv, max_len, bs)
                               : split_req;
     if (!split_ok(split, bs)) return PKV_ERR_SHAPE;
@@ -240,6 +241,52 @@ bool balanced_refused(int64_t num_seqs, int64_t hkv, int64_t head_dim, int64_t m
                       int32_t dtype, int64_t split_req) {
     return split_req == PKV_SPLIT_BALANCED &&
            !balanced_possible(num_seqs, hkv, head_dim, max_len, bs, dtype);
+}
+
+// Device-planned split schedule (bf16 pools): the grid is 2 workgroups per
+// compute unit (both resident: the decode kernel's LDS is about 55 KiB),
+// fewer when the pieces at the smallest split cannot fill it; each
+// workgroup picks the split from the actual lengths (kernels_decode.hip).
+// The smallest split keeps every sequence within 16 splits (merged in the
+// kernel), and is at least 64 positions.  Possible when the grid holds 4
+// pieces per (sequence, head group) -- so the device's split bound is at
+// most max_len / 2 + 16 positions, which must fit the LDS table buffer --
+// for at most kPlanMaxSeqs sequences, with positions below 2^24 (the
+// kernel's float-reciprocal division).
+struct SplitPlan {
+    int64_t smin;
+    int64_t wgs;
+};
+
+bool planned_possible(int64_t num_seqs, int64_t hkv, int64_t max_len, int64_t bs, int32_t dtype,
+                      SplitPlan *sp) {
+    if (dtype != PKV_BF16 || num_seqs <= 0 || num_seqs > kPlanMaxSeqs || max_len <= 0 ||
+        !is_pow2(bs))
+        return false;
+    const int64_t groups = hkv / heads_per_wg(hkv);
+    const int64_t wgs_max = 2ll * cu_count();
+    if (num_seqs * groups * 4 > wgs_max) return false;
+    const int64_t span = max_positions(max_len, bs);
+    if (span + bs >= (int64_t(1) << 24)) return false;
+    const int64_t smax = max_split_tokens(bs);
+    int64_t smin = ((span + 15) / 16 + 15) / 16 * 16;
+    if (smin < 64) smin = 64;
+    if (smin > smax || max_len / 2 + 32 > smax) return false;
+    const int64_t max_splits = (span + smin - 1) / smin;
+    const int64_t pieces_max = num_seqs * groups * max_splits;
+    if (sp) {
+        sp->smin = smin;
+        sp->wgs = pieces_max < wgs_max ? pieces_max : wgs_max;
+    }
+    return true;
+}
+
+// Automatic (split_tokens = 0) and explicit (PKV_SPLIT_PLANNED) choice of
+// the device-planned split.
+bool use_planned(int64_t num_seqs, int64_t hkv, int64_t max_len, int64_t bs, int32_t dtype,
+                 int64_t split_req, SplitPlan *sp) {
+    if (split_req != 0 && split_req != PKV_SPLIT_PLANNED) return false;
+    return planned_possible(num_seqs, hkv, max_len, bs, dtype, sp);
 }
 
 int plan_stream(int64_t num_seqs, int64_t hkv, int64_t hq, int64_t head_dim, int64_t max_len,
@@ -487,6 +534,15 @@ PKV_API size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_kv
                     split_tokens, &p))
         return (size_t)-1;
     int64_t need = p.total();
+    SplitPlan sp2;
+    if ((split_tokens == 0 || split_tokens == PKV_SPLIT_PLANNED) &&
+        planned_possible(num_seqs, num_kv_heads, max_seq_len, block_size, PKV_BF16, &sp2)) {
+        DecodePlan pp;
+        if (plan_decode(num_seqs, num_kv_heads, num_q_heads, head_dim, max_seq_len, block_size,
+                        sp2.smin, &pp))
+            return (size_t)-1;
+        if (pp.total() > need) need = pp.total();
+    }
     if ((split_tokens == 0 || split_tokens == PKV_SPLIT_BALANCED) &&
         num_seqs <= stream_max_seqs(num_kv_heads)) {
         // the balanced schedule (bf16 pools) or the automatic split (fp32)
@@ -511,6 +567,9 @@ PKV_API int32_t paged_attn_decode_schedule(int32_t num_seqs, int32_t num_kv_head
     if (balanced_refused(num_seqs, num_kv_heads, head_dim, max_seq_len, block_size, dtype,
                          split_tokens))
         return PKV_ERR_UNSUPPORTED;
+    if (use_planned(num_seqs, num_kv_heads, max_seq_len, block_size, dtype, split_tokens, nullptr))
+        return PKV_SCHEDULE_PLANNED;
+    if (split_tokens == PKV_SPLIT_PLANNED) return PKV_ERR_UNSUPPORTED;
     if (use_balanced(num_seqs, num_kv_heads, head_dim, max_seq_len, block_size, dtype, split_tokens))
         return 0;
     return (int32_t)p.split;
@@ -530,7 +589,8 @@ int decode_impl(const pkv_pool *pool, int32_t layer, const void *q, int32_t num_
     if (st) return st;
     if (layer < 0 || layer >= pool->num_layers) return PKV_ERR_LAYER;
     if (num_seqs < 0 || max_seq_len < 0 || bt_stride < 0 || num_q_heads <= 0 ||
-        num_q_heads % pool->num_kv_heads != 0 || (split_tokens < 0 && split_tokens != PKV_SPLIT_BALANCED))
+        num_q_heads % pool->num_kv_heads != 0 ||
+        (split_tokens < 0 && split_tokens != PKV_SPLIT_BALANCED && split_tokens != PKV_SPLIT_PLANNED))
         return PKV_ERR_SHAPE;
     const int group = (int)(num_q_heads / pool->num_kv_heads);
     if (!decode_supported(pool->dtype, (int)pool->head_dim, group)) return PKV_ERR_UNSUPPORTED;
@@ -538,6 +598,10 @@ int decode_impl(const pkv_pool *pool, int32_t layer, const void *q, int32_t num_
     if (balanced_refused(num_seqs, pool->num_kv_heads, pool->head_dim, max_seq_len, pool->block_size,
                          pool->dtype, split_tokens))
         return PKV_ERR_UNSUPPORTED;
+    SplitPlan spl{};
+    const bool planned = use_planned(num_seqs, pool->num_kv_heads, max_seq_len, pool->block_size,
+                                     pool->dtype, split_tokens, &spl);
+    if (split_tokens == PKV_SPLIT_PLANNED && !planned) return PKV_ERR_UNSUPPORTED;
     if (num_seqs == 0) return PKV_OK;
     if (!q || !out || !seq_lens || !offsets || (max_seq_len > 0 && !block_tables))
         return PKV_ERR_NULL;
@@ -546,10 +610,11 @@ int decode_impl(const pkv_pool *pool, int32_t layer, const void *q, int32_t num_
     if (k_new && (!aligned16(k_new) || !aligned16(v_new))) return PKV_ERR_ALIGN;
     DecodePlan p;
     st = plan_decode(num_seqs, pool->num_kv_heads, num_q_heads, pool->head_dim, max_seq_len,
-                     pool->block_size, split_tokens, &p);
+                     pool->block_size, planned ? (int32_t)spl.smin : split_tokens, &p);
     if (st) return st;
-    const bool balanced = use_balanced(num_seqs, pool->num_kv_heads, pool->head_dim, max_seq_len,
-                                       pool->block_size, pool->dtype, split_tokens);
+    const bool balanced = !planned && use_balanced(num_seqs, pool->num_kv_heads, pool->head_dim,
+                                                   max_seq_len, pool->block_size, pool->dtype,
+                                                   split_tokens);
     StreamPlan sp{};
     if (balanced) {
         st = plan_stream(num_seqs, pool->num_kv_heads, num_q_heads, pool->head_dim, max_seq_len,
@@ -592,6 +657,8 @@ int decode_impl(const pkv_pool *pool, int32_t layer, const void *q, int32_t num_
     a.fused_merge = p.max_splits <= kFusedMergeMaxSplits;
     a.stream_wgs = balanced ? (int32_t)sp.wgs : 0;
     a.seg_chunks = (int32_t)(max_split_tokens(pool->block_size) / kChunkTokens);
+    a.plan = planned ? (int32_t)spl.wgs : 0;
+    a.max_len = max_seq_len;
     return status_of(launch_decode(a, pool->dtype, (int)pool->head_dim, group,
                                    static_cast<hipStream_t>(stream)));
 }

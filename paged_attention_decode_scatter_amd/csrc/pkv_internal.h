@@ -144,11 +144,17 @@ struct DecodeArgs {
     int32_t fused_merge;   // 1: the last split of a (sequence, head group) merges; 0: merge kernel
     int32_t stream_wgs;    // > 0: balanced schedule with this many workgroups (bf16)
     int32_t seg_chunks;    // balanced schedule: most chunks staged at once
+    int32_t plan;          // > 0: device-planned split, this many workgroups (split_tokens: the smallest split)
+    int32_t max_len;       // the caller's max_seq_len (device-planned split clamps to it)
 };
 
 // Most splits per sequence merged by the last finishing workgroup; beyond
 // this a separate, wider merge kernel is faster.
 constexpr int kFusedMergeMaxSplits = 16;
+
+// Device-planned split schedule: at most this many sequences (one per lane
+// of the wavefront that plans).
+constexpr int kPlanMaxSeqs = 64;
 
 // Balanced decode schedule: every workgroup reads every sequence length
 // (at most kStreamSeqsPerThread per thread) and lists the (head group,

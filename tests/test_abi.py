@@ -236,16 +236,27 @@ def test_prefill_argument_checks(lib):
 
 
 def test_decode_schedule_choice(lib):
-    """The automatic schedule: balanced for bf16 batches of at least 32
-    sequences with at least 512 MiB of K/V at max_seq_len (and few enough
-    sequences for the length scan: 4 per thread), the automatic split
-    otherwise; an explicit split is always kept."""
+    """The automatic schedule: the device-planned split for bf16 batches of
+    at most 64 sequences with at most (compute units / 2) (sequence, head
+    group) pairs and max_seq_len / 2 + 32 within the largest split; else
+    balanced for bf16 batches of at least 32 sequences with at least 512 MiB
+    of K/V at max_seq_len (and few enough sequences for the length scan: 4
+    per thread); the automatic split otherwise; an explicit split is always
+    kept.  (No device here: 256 compute units are assumed.)"""
     f = lib.paged_attn_decode_schedule
     F32, BF16 = 0, 1
+    PLANNED, SPLIT_PLANNED = 1, -2
     split = lib.paged_attn_decode_split_tokens
-    assert f(32, 8, 32, 128, 2048, 16, BF16, 0) == split(32, 8, 2048, 16)  # 256 MiB
-    assert f(64, 8, 32, 128, 4096, 16, BF16, 0) == 0                       # 1 GiB
-    assert f(8, 8, 64, 128, 32768, 16, BF16, 0) == split(8, 8, 32768, 16)  # few sequences
+    assert f(32, 8, 32, 128, 2048, 16, BF16, 0) == PLANNED                 # decode batch
+    assert f(64, 8, 32, 128, 4096, 16, BF16, 0) == PLANNED                 # prefix sharing
+    assert f(32, 8, 32, 128, 2048, 16, F32, 0) == split(32, 8, 2048, 16)
+    assert f(65, 8, 32, 128, 4096, 16, BF16, 0) == 0                       # 65 sequences, 1 GiB
+    assert f(65, 8, 32, 128, 1024, 16, BF16, 0) == split(65, 8, 1024, 16)  # 65 sequences, 0.27 GiB
+    assert f(64, 16, 64, 128, 4096, 16, BF16, 0) == 0                      # 4 head groups: 256 pairs
+    assert f(8, 8, 64, 128, 32768, 16, BF16, 0) == split(8, 8, 32768, 16)  # past the largest split
+    assert f(8, 8, 64, 128, 32768, 16, BF16, SPLIT_PLANNED) == UNSUP
+    assert f(2, 2, 8, 128, 100, 16, F32, SPLIT_PLANNED) == UNSUP
+    assert f(2, 2, 8, 128, 100, 16, BF16, SPLIT_PLANNED) == PLANNED
     assert f(8, 8, 64, 128, 32768, 16, F32, 0) == split(8, 8, 32768, 16)
     assert f(8, 8, 64, 128, 32768, 16, BF16, 512) == 512
     assert f(5000, 8, 32, 128, 4096, 16, BF16, 0) == split(5000, 8, 4096, 16)

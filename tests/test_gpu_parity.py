@@ -307,7 +307,7 @@ def test_gather_full_size_bit_exact(dev, name):
 def test_decode_small_grid(dev, dtype, head_dim, group):
     w = small_decode(dev, dtype=dtype, head_dim=head_dim, group=group, seed=30 + group)
     ref = oracle_decode_for(w)
-    for split in (16, 64, 0) + ((N.SPLIT_BALANCED,) if dtype == torch.bfloat16 else ()):
+    for split in (16, 64, 0) + ((N.SPLIT_BALANCED, N.SPLIT_PLANNED) if dtype == torch.bfloat16 else ()):
         got = run_decode(w, split)
         err = max_abs_err(got, ref)
         assert err <= TOL[dtype], (split, err)
@@ -322,14 +322,14 @@ def test_decode_other_block_sizes(dev, bs, dtype):
                        num_blocks=2048 // bs + 64, num_layers=2, num_kv_heads=2, head_dim=128,
                        num_q_heads=8, dtype=dtype, layer=1, offsets="random", block_size=bs)
     ref = oracle_decode_for(w)
-    for split in (16, 64, 0) + ((N.SPLIT_BALANCED,) if dtype == torch.bfloat16 else ()):
+    for split in (16, 64, 0) + ((N.SPLIT_BALANCED, N.SPLIT_PLANNED) if dtype == torch.bfloat16 else ()):
         if split > 0 and split // bs + 2 > 1024:
             continue
         got = run_decode(w, split)
         assert max_abs_err(got, ref) <= TOL[dtype], split
 
 
-@pytest.mark.parametrize("split", [16, 32, 0, N.SPLIT_BALANCED])
+@pytest.mark.parametrize("split", [16, 32, 0, N.SPLIT_BALANCED, N.SPLIT_PLANNED])
 def test_decode_edge_lengths_and_offsets(dev, split):
     w = small_decode(dev, seed=40, num_seqs=18, min_len=40, max_len=40, offsets=None)
     set_lens(w, [0, 1, 15, 16, 17, 33] * 3, [0] * 6 + [1] * 6 + [15] * 6)
@@ -436,7 +436,7 @@ def test_validate_counts_violations(dev):
     assert n == 5 + pad3, (n, pad3)
 
 
-@pytest.mark.parametrize("split", [64, 16, 0, N.SPLIT_BALANCED])
+@pytest.mark.parametrize("split", [64, 16, 0, N.SPLIT_BALANCED, N.SPLIT_PLANNED])
 def test_decode_workspace_reuse_leaves_counters_zero(dev, split):
     """One zeroed workspace serves successive calls of different shapes: each
     call gives the same bits as a call with a fresh workspace and leaves the
@@ -498,6 +498,64 @@ def test_decode_balanced_schedule(dev, num_seqs, max_len, num_blocks):
     assert max_abs_err(got, oracle_decode_for(w)) <= TOL[w.dtype]
     empty = np.flatnonzero(host(w.seq_lens) == 0)
     assert torch.all(got[torch.from_numpy(empty).to(dev)] == 0)
+
+
+@pytest.mark.parametrize("num_seqs,max_len,num_kv_heads,num_blocks,empty_every",
+                         [(1, 3000, 2, 256, 0), (64, 700, 2, 4096, 7), (40, 2048, 2, 5400, 0),
+                          (64, 90, 8, 1024, 3), (32, 2048, 8, 4400, 0), (3, 40, 8, 64, 2)])
+def test_decode_planned_schedule(dev, num_seqs, max_len, num_kv_heads, num_blocks, empty_every):
+    """The device-planned split schedule (the automatic one for these bf16
+    batches): every workgroup reads all lengths, picks the split and takes
+    one (sequence, split, head group) piece -- full pieces from the front of
+    the grid, first/last pieces from the back.  Cases cover a grid that holds
+    every piece at the smallest split (1 and 3 sequences), the bound on the
+    split that fits 2 workgroups per compute unit (64 x 700), head groups of
+    4 kv heads (8 kv heads), random offsets, and empty sequences, whose
+    outputs must be zero.  A second call on the same workspace gives the
+    same bits and leaves the merge counters zero."""
+    w = small_decode(dev, seed=90 + num_seqs, num_seqs=num_seqs, min_len=1, max_len=max_len,
+                     num_kv_heads=num_kv_heads, num_blocks=num_blocks)
+    lens = host(w.seq_lens).copy()
+    if empty_every:
+        lens[1::empty_every] = 0
+    set_lens(w, lens.tolist(), host(w.offsets).tolist())
+    pl = N.SPLIT_PLANNED
+    for split in (0, pl):
+        assert N.paged_attn_decode_schedule(w.num_seqs, w.num_kv_heads, w.num_q_heads, w.head_dim,
+                                            w.max_seq_len, w.block_size, w.dtype,
+                                            split) == N.SCHEDULE_PLANNED
+    need = N.paged_attn_decode_workspace_size(w.num_seqs, w.num_kv_heads, w.num_q_heads,
+                                              w.head_dim, w.max_seq_len, w.block_size, pl)
+    ws = torch.zeros(max(need, 16), dtype=torch.uint8, device=dev)
+    cnt = (w.num_seqs * w.num_kv_heads * 4 + 255) // 256 * 256
+    got = run_decode(w, pl, workspace=ws)
+    assert int(torch.count_nonzero(ws[:cnt])) == 0
+    again = run_decode(w, pl, workspace=ws)
+    assert int(torch.count_nonzero(ws[:cnt])) == 0
+    assert torch.equal(got.view(torch.int16), again.view(torch.int16))
+    assert max_abs_err(got, oracle_decode_for(w)) <= TOL[w.dtype]
+    empty = np.flatnonzero(host(w.seq_lens) == 0)
+    assert torch.all(got[torch.from_numpy(empty).to(dev)] == 0)
+    # the same function as a fixed split
+    assert float((got.float() - run_decode(w, 64).float()).abs().max()) <= TOL[w.dtype]
+
+
+def test_decode_planned_refused_past_its_limits(dev):
+    """More than 64 sequences (or fp32 pools): an explicit planned request is
+    refused, and split_tokens = 0 takes another schedule."""
+    w = small_decode(dev, seed=97, num_seqs=65, max_len=50, num_blocks=512)
+    assert N.paged_attn_decode_schedule(w.num_seqs, w.num_kv_heads, w.num_q_heads, w.head_dim,
+                                        w.max_seq_len, w.block_size, w.dtype,
+                                        0) != N.SCHEDULE_PLANNED
+    with pytest.raises(N.PagedKVError) as e:
+        run_decode(w, N.SPLIT_PLANNED)
+    assert e.value.status == -8
+    w32 = small_decode(dev, dtype=torch.float32, seed=98, num_seqs=4, max_len=50)
+    with pytest.raises(N.PagedKVError) as e:
+        run_decode(w32, N.SPLIT_PLANNED)
+    assert e.value.status == -8
+    got = run_decode(w, 0)
+    assert max_abs_err(got, oracle_decode_for(w)) <= TOL[w.dtype]
 
 
 def test_decode_rejects_unsupported_group(dev):
