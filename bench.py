@@ -256,7 +256,8 @@ def int8_decode(w, N, W, reps=32):
     g = w.num_q_heads // w.num_kv_heads
     out = {"us": us, "algorithmic_bytes": alg, "GB/s": alg / us / 1e3,
            "frac": alg / us / 1e3 / HBM_PEAK_GBS,
-           "kernel": f"decode_q8_kernel<D={w.head_dim},G={g}> (split {split})",
+           "kernel": f"decode_q8_kernel<D={w.head_dim},G={g}> " + (
+               "(device-planned split)" if split == N.SCHEDULE_PLANNED else f"(split {split})"),
            "kv_bytes_vs_bf16": kv / kv_bf16}
     del k, v, ws, res
     torch.cuda.empty_cache()

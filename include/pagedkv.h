@@ -251,7 +251,7 @@ PKV_API int32_t paged_attn_decode_split_tokens(int32_t num_seqs, int32_t num_kv_
  *        (sequence, split, kv-head group) pieces fit 2 workgroups per
  *        compute unit; pieces of exactly that many positions take the
  *        first workgroups, shorter first and last pieces the last ones.
- *        Taken for bf16 pools when split_tokens = 0 or PKV_SPLIT_PLANNED
+ *        Taken for bf16 and int8 pools when split_tokens = 0 or PKV_SPLIT_PLANNED
  *        and the batch allows it: at most 64 sequences, at most
  *        compute units / 2 (sequence, kv-head group) pairs, and
  *        max_seq_len / 2 + 32 <= the largest split (split_tokens limit
@@ -330,8 +330,9 @@ PKV_API size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_kv
  *                 as is.  Calls that share a workspace must not overlap
  *                 (issue them on one stream).
  * Supported: head_dim in {64, 128}, G in {1, 2, 4, 8}.  A quantised pool
- * takes bfloat16 q and out, runs the split schedule (PKV_SPLIT_BALANCED is
- * PKV_ERR_UNSUPPORTED) and attends to the stored values code * scale.
+ * takes bfloat16 q and out, runs the split or the planned schedule
+ * (PKV_SPLIT_BALANCED is PKV_ERR_UNSUPPORTED) and attends to the stored
+ * values code * scale.
  * Errors: PKV_ERR_NULL, _DTYPE, _SHAPE, _LAYER, _ALIGN, _WORKSPACE,
  * _UNSUPPORTED, _LAUNCH.
  */

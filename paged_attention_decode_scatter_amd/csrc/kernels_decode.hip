@@ -171,7 +171,8 @@ __device__ void zero_outputs(const DecodeArgs &a, int seq, int hg) {
 }
 
 // ---------------------------------------------------------------------------
-// Device-planned split schedule (bf16, a.plan = number of workgroups).  The
+// Device-planned split schedule (bf16 and int8 pools, a.plan = number of
+// workgroups).  The
 // host knows only the largest sequence length, so a split it picks cannot
 // fit the batch: with the lengths of the decode batch the automatic
 // 256-token split leaves 30 of 256 compute units without a live work item
@@ -1304,18 +1305,29 @@ __device__ __forceinline__ void attend_range_q8(const DecodeArgs &a, const Range
 }
 
 template <int D, int G, bool UB>
-__global__ __launch_bounds__(256) void decode_q8_kernel(DecodeArgs a) {
+// Two wavefronts per SIMD: without the hint the compiler takes 272
+// registers (one wavefront per SIMD, half the loads in flight).
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void decode_q8_kernel(DecodeArgs a) {
     using S = MfmaShape<D>;
     static_assert(G >= 1 && G <= 16, "group");
     __shared__ int32_t bt_s[kBtLds];
     __shared__ __attribute__((aligned(16))) char vtiles[4][S::VTILE];
 
-    const Item it = work_item(a);
-    const Range R = split_range(a, it.seq, it.split);
-    const bool direct = a.max_splits == 1;
-    if (!direct && R.hi <= R.lo) {
-        if (a.fused_merge && R.len <= 0 && it.split == 0) zero_outputs<1, D, G>(a, it.seq, it.hg);
-        return;
+    Item it;
+    Range R;
+    int64_t split = a.split_tokens;
+    bool direct;
+    if (a.plan) {
+        if (!plan_item<D, G>(a, bt_s, it, R, split)) return;
+        direct = R.lo == R.off && R.hi == R.off + R.len;  // the sequence's only piece
+    } else {
+        it = work_item(a);
+        R = split_range(a, it.seq, it.split);
+        direct = a.max_splits == 1;
+        if (!direct && R.hi <= R.lo) {
+            if (a.fused_merge && R.len <= 0 && it.split == 0) zero_outputs<1, D, G>(a, it.seq, it.hg);
+            return;
+        }
     }
     const int64_t jb0 = stage_table(a, it.seq, R, bt_s);
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1336,7 +1348,7 @@ __global__ __launch_bounds__(256) void decode_q8_kernel(DecodeArgs a) {
     }
     const int64_t item0 = ((int64_t)it.seq * a.max_splits + it.split) * a.num_q_heads + (int64_t)h * G;
     write_partial<D, G>(a.ws_ml + item0 * 2, a.ws_acc + item0 * D, acc, m_h, l_h);
-    if (a.fused_merge) finish_split<1, D, G>(a, it, R, a.split_tokens);
+    if (a.fused_merge) finish_split<1, D, G>(a, it, R, split);
 }
 
 // ---------------------------------------------------------------------------
@@ -2058,7 +2070,7 @@ typedef hipError_t (*DecodeFn)(const DecodeArgs &, hipStream_t);
 template <int D, int G>
 static hipError_t run_decode_q8(const DecodeArgs &a, hipStream_t s) {
     const dim3 block(64 * a.heads_per_wg);
-    const dim3 grid((unsigned)((int64_t)a.head_groups * a.max_splits * a.num_seqs));
+    const dim3 grid((unsigned)(a.plan > 0 ? a.plan : (int64_t)a.head_groups * a.max_splits * a.num_seqs));
     if (a.pool.lbs >= 4)
         hipLaunchKernelGGL((decode_q8_kernel<D, G, true>), grid, block, 0, s, a);
     else

@@ -243,8 +243,9 @@ bool balanced_refused(int64_t num_seqs, int64_t hkv, int64_t head_dim, int64_t m
            !balanced_possible(num_seqs, hkv, head_dim, max_len, bs, dtype);
 }
 
-// Device-planned split schedule (bf16 pools): the grid is 2 workgroups per
-// compute unit (both resident: the decode kernel's LDS is about 55 KiB),
+// Device-planned split schedule (bf16 and int8 pools): the grid is 2
+// workgroups per compute unit (both resident: the bf16 decode kernel's LDS
+// is about 55 KiB, the int8 one's 21 KiB; both use at most 256 registers),
 // fewer when the pieces at the smallest split cannot fill it; each
 // workgroup picks the split from the actual lengths (kernels_decode.hip).
 // The smallest split keeps every sequence within 16 splits (merged in the
@@ -260,7 +261,7 @@ struct SplitPlan {
 
 bool planned_possible(int64_t num_seqs, int64_t hkv, int64_t max_len, int64_t bs, int32_t dtype,
                       SplitPlan *sp) {
-    if (dtype != PKV_BF16 || num_seqs <= 0 || num_seqs > kPlanMaxSeqs || max_len <= 0 ||
+    if ((dtype != PKV_BF16 && dtype != PKV_I8) || num_seqs <= 0 || num_seqs > kPlanMaxSeqs || max_len <= 0 ||
         !is_pow2(bs))
         return false;
     const int64_t groups = hkv / heads_per_wg(hkv);

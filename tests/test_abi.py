@@ -250,6 +250,7 @@ def test_decode_schedule_choice(lib):
     assert f(32, 8, 32, 128, 2048, 16, BF16, 0) == PLANNED                 # decode batch
     assert f(64, 8, 32, 128, 4096, 16, BF16, 0) == PLANNED                 # prefix sharing
     assert f(32, 8, 32, 128, 2048, 16, F32, 0) == split(32, 8, 2048, 16)
+    assert f(32, 8, 32, 128, 2048, 16, 2, 0) == PLANNED                    # int8 pool
     assert f(65, 8, 32, 128, 4096, 16, BF16, 0) == 0                       # 65 sequences, 1 GiB
     assert f(65, 8, 32, 128, 1024, 16, BF16, 0) == split(65, 8, 1024, 16)  # 65 sequences, 0.27 GiB
     assert f(64, 16, 64, 128, 4096, 16, BF16, 0) == 0                      # 4 head groups: 256 pairs
@@ -375,7 +376,8 @@ def test_quantized_pool_checks(lib):
     assert pre(by(pool(dtype=I8)), 0, A, 32, A, 64, 16, A, 8, A, A, 4, 0.1, A, None) == UNSUP
     f = lib.paged_attn_decode_schedule
     split = lib.paged_attn_decode_split_tokens
-    assert f(32, 8, 32, 128, 2048, 16, I8, 0) == split(32, 8, 2048, 16)
+    assert f(32, 8, 32, 128, 2048, 16, I8, 0) == 1            # the device-planned split
+    assert f(65, 8, 32, 128, 2048, 16, I8, 0) == split(65, 8, 2048, 16)
     assert f(32, 8, 32, 128, 2048, 16, I8, -1) == UNSUP
 
 

@@ -134,7 +134,12 @@ def run(w, k, v, split=0):
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("group", [1, 2, 4, 8])
 def test_int8_decode_grid(dev, d, group):
+    """split 0 takes the device-planned schedule for these batches, 16 and
+    64 fixed splits."""
     w, k, v = workload(dev, 640 + group, d=d, group=group)
+    assert N.paged_attn_decode_schedule(w.num_seqs, w.num_kv_heads, w.num_q_heads, w.head_dim,
+                                        w.max_seq_len, w.block_size, torch.int8,
+                                        0) == N.SCHEDULE_PLANNED
     ref = oracle_decode(w, k, v)
     for split in (0, 16, 64):
         assert max_abs_err(run(w, k, v, split), ref) <= TOL, split
