@@ -378,15 +378,23 @@ __device__ bool plan_item(const DecodeArgs &a, int32_t *scratch, Item &it, Range
 // per RB records.
 template <int DT, int D, int G, typename Slot>
 __device__ void merge_records(char *out_row0, const float *ml, const float *accb, int64_t hstride,
-                              int n, Slot slot) {
+                              int n, Slot slot, char *lds = nullptr, int lds_bytes = 0) {
     constexpr int E = Elem<DT>::kBytes;
     constexpr int PL = D / 64;
     // acc records per batch: 64 values per lane, so the merge needs no more
     // registers than the attention loop (occupancy stays at 2 waves/SIMD)
     constexpr int RB = (64 / (G * PL)) < 16 ? (64 / (G * PL) > 0 ? 64 / (G * PL) : 1) : 16;
     static_assert(PL == 1 || PL == 2, "head_dim");
+    // the G acc rows of one record are contiguous (G * D floats)
+    constexpr int RECB = G * D * 4;
+    // staged only when a record is whole 1 KiB tile-load instructions
+    constexpr bool kStage = RECB % 1024 == 0;
     const int lane = threadIdx.x & 63;
     const float *acc = accb + lane * PL;
+    // Records RB .. RB + LR - 1 go global -> LDS (the wavefront's own free
+    // LDS, lds_bytes of it) in the same memory round trip as the first RB,
+    // with the same device-scope (sc1) loads; past that, batches of RB.
+    const int LR = kStage && n <= 64 ? min(lds_bytes / RECB, max(n - RB, 0)) : 0;
 
     float M[G], w[G], den[G], o[G][PL];
 #pragma unroll
@@ -430,6 +438,14 @@ __device__ void merge_records(char *out_row0, const float *ml, const float *accb
     };
 
     if (n <= 64) {
+        for (int r = 0; r < LR; ++r) {
+            const char *src = reinterpret_cast<const char *>(accb + slot(RB + r) * hstride * D);
+#pragma unroll
+            for (int i = 0; i < (kStage ? RECB / 1024 : 0); ++i)
+                __builtin_amdgcn_global_load_lds(const_cast<char *>(src) + 1024 * i + 16 * lane,
+                                                 (__attribute__((address_space(3))) void *)(lds + r * RECB + 1024 * i),
+                                                 16, 0, 16 /* sc1 */);
+        }
         float mv[G], lv[G];
 #pragma unroll
         for (int g = 0; g < G; ++g) {
@@ -453,7 +469,22 @@ __device__ void merge_records(char *out_row0, const float *ml, const float *accb
             den[g] = lane < n ? lv[g] * w[g] : 0.0f;
         }
         add_batch(0, x, w);
-        for (int b = RB; b < n; b += RB) {
+        if (LR > 0) {
+            // the copy engine's writes are not tracked by the compiler
+            __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));
+            wave_lds_order();
+            for (int r = 0; r < LR; ++r) {
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    const float wk = lane_value(w[g], (RB + r) & 63);
+                    const float *row = reinterpret_cast<const float *>(lds + r * RECB) + g * D + lane * PL;
+#pragma unroll
+                    for (int e = 0; e < PL; ++e) o[g][e] = fmaf(wk != 0.0f ? row[e] : 0.0f, wk, o[g][e]);
+                }
+            }
+            wave_lds_order();
+        }
+        for (int b = RB + LR; b < n; b += RB) {
             load_batch(b, x);
             add_batch(b, x, w);
         }
@@ -519,7 +550,8 @@ __device__ bool count_in(uint32_t *cnt, uint32_t expected) {
 // live splits j0 .. j1 of the sequence, each wavefront the G query heads of
 // its kv head.
 template <int DT, int D, int G>
-__device__ void finish_split(const DecodeArgs &a, const Item &it, const Range &R, int64_t S) {
+__device__ void finish_split(const DecodeArgs &a, const Item &it, const Range &R, int64_t S,
+                             char *lds = nullptr, int lds_bytes = 0) {
     constexpr int E = Elem<DT>::kBytes;
     const int j0 = (int)(R.off / S);
     const int j1 = (int)((R.off + R.len - 1) / S);
@@ -529,7 +561,7 @@ __device__ void finish_split(const DecodeArgs &a, const Item &it, const Range &R
     const int64_t item0 = (int64_t)it.seq * a.max_splits * a.num_q_heads + hq0;
     merge_records<DT, D, G>(a.out + ((int64_t)it.seq * a.num_q_heads + hq0) * D * E, a.ws_ml + item0 * 2,
                             a.ws_acc + item0 * D, a.num_q_heads, j1 - j0 + 1,
-                            [=](int i) { return (int64_t)(j0 + i); });
+                            [=](int i) { return (int64_t)(j0 + i); }, lds, lds_bytes);
 }
 
 // ---------------------------------------------------------------------------
@@ -1025,7 +1057,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     }
     const int64_t item0 = ((int64_t)it.seq * a.max_splits + it.split) * a.num_q_heads + (int64_t)h * G;
     write_partial<D, G>(a.ws_ml + item0 * 2, a.ws_acc + item0 * D, acc, m_h, l_h);
-    if (a.fused_merge) finish_split<1, D, G>(a, it, R, split);
+    // the wave's V ring is free now: it stages merge records
+    if (a.fused_merge) finish_split<1, D, G>(a, it, R, split, vtiles[w][0], S::NSLOT * S::VTILE);
 }
 
 // ---------------------------------------------------------------------------
@@ -1348,7 +1381,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     }
     const int64_t item0 = ((int64_t)it.seq * a.max_splits + it.split) * a.num_q_heads + (int64_t)h * G;
     write_partial<D, G>(a.ws_ml + item0 * 2, a.ws_acc + item0 * D, acc, m_h, l_h);
-    if (a.fused_merge) finish_split<1, D, G>(a, it, R, split);
+    if (a.fused_merge) finish_split<1, D, G>(a, it, R, split, vtiles[w], S::VTILE);
 }
 
 // ---------------------------------------------------------------------------
