@@ -96,14 +96,16 @@ __global__ __launch_bounds__(kCopyThreads) void scatter_kernel(ScatterArgs a) {
                     ch = idx - tt * cpr;
                 }
                 const int64_t t = tok0 + tt;
+                // the row is loaded with its slot, not after it (one memory
+                // round trip instead of two); padding rows are read and
+                // dropped
                 const int64_t slot = a.slots[t];
-                if (slot >= 0 && slot < a.total_slots) {
+                const int64_t src = t * a.row_bytes + ((int64_t)ch << 4);
+                kk[u] = ld16_stream(a.k_src + src);
+                if (has_v) vv[u] = ld16_stream(a.v_src + src);
+                if (slot >= 0 && slot < a.total_slots)
                     dst[u] = (slot >> a.lbs) * a.block_stride + a.layer_off +
                              (slot & bsm) * a.row_bytes + ((int64_t)ch << 4);
-                    const int64_t src = t * a.row_bytes + ((int64_t)ch << 4);
-                    kk[u] = ld16_stream(a.k_src + src);
-                    if (has_v) vv[u] = ld16_stream(a.v_src + src);
-                }
             }
         }
 #pragma unroll
@@ -202,24 +204,29 @@ __global__ __launch_bounds__(kCopyThreads) void gather_kernel(GatherArgs a) {
     __shared__ int32_t bt_s[kBtLds];
     const int seq = blockIdx.x / a.tiles_per_seq;
     const int tile = blockIdx.x - seq * a.tiles_per_seq;
-    const int L = a.seq_lens[seq];
     const int t0 = tile * a.tok_per_wg;
-    if (t0 >= L) return;  // uniform across the workgroup
-    const int t1 = min(L, t0 + a.tok_per_wg);
-    const int64_t off = a.offsets[seq];
     const int lbs = a.pool.lbs;
     const int64_t bsm = (1ll << lbs) - 1;
-    const int64_t jb0 = (off + t0) >> lbs;
-    const int nbt = (int)(((off + t1 - 1) >> lbs) - jb0 + 1);
+    // The table entries this tile can touch for any offset in [0, bs) are
+    // staged together with the length and offset (one memory round trip
+    // instead of two): entries t0 / bs .. (t0 + tok_per_wg - 1 + bs - 1) / bs.
+    // An offset outside [0, bs) breaks the contract and is clamped into it.
+    const int64_t jb0 = (int64_t)t0 >> lbs;
+    const int nbt = (int)((((int64_t)t0 + a.tok_per_wg - 1 + bsm) >> lbs) - jb0 + 1);
+    const int L = a.seq_lens[seq];
+    int64_t off = a.offsets[seq];
     for (int i = threadIdx.x; i < nbt; i += kCopyThreads) {
         const int64_t j = jb0 + i;
         int32_t b = -1;
-        if (j >= 0 && j < a.bt_stride) {
+        if (j < a.bt_stride) {
             b = a.block_tables[(int64_t)seq * a.bt_stride + j];
             if (b < 0 || b >= a.pool.num_blocks) b = -1;
         }
         bt_s[i] = b;
     }
+    if (t0 >= L) return;  // uniform across the workgroup (no barrier passed yet)
+    off = off < 0 ? 0 : (off > bsm ? bsm : off);
+    const int t1 = min(L, t0 + a.tok_per_wg);
     __syncthreads();
 
     const int cpr = a.pool.row_bytes >> 4;
