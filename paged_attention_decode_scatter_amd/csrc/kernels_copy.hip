@@ -268,8 +268,9 @@ __global__ __launch_bounds__(kCopyThreads) void gather_kernel(GatherArgs a) {
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             if (dst[u] >= 0) {
-                st16(a.k_out + dst[u], kk[u]);
-                if (has_v) st16(a.v_out + dst[u], vv[u]);
+                // streaming stores: the call does not read its output back
+                st16_stream(a.k_out + dst[u], kk[u]);
+                if (has_v) st16_stream(a.v_out + dst[u], vv[u]);
             }
         }
     }

@@ -1981,6 +1981,7 @@ template <int DT, int D>
 __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(DecodeArgs a) {
     constexpr int E = Elem<DT>::kBytes;
     constexpr int NG = kReduceThreads / D;  // split groups
+    constexpr int U = 16;                   // acc values per thread in the first batch
     static_assert(NG >= 1 && kReduceThreads % D == 0, "head_dim");
     extern __shared__ float w_s[];          // max_splits weights
     __shared__ float red_s[kReduceThreads / 64];
@@ -1993,13 +1994,35 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(DecodeArgs a) {
     const int ns = a.max_splits;
     const int t = threadIdx.x;
     const int wv = t >> 6;
+    const int d = t % D;
+    const int grp = t / D;
+    const float *src = a.ws_acc + item0 * D + d;
+    const int64_t jstride = step * D;
 
-    // 1. max over live splits (same liveness rule as the partial kernel)
-    float M = kNegInf;
-    for (int j = t; j < ns; j += kReduceThreads) {
-        const Range R = split_range(a, seq, j);
-        if (R.hi > R.lo) M = fmaxf(M, a.ws_ml[(item0 + j * step) * 2]);
+    // One memory round trip for the common case: the length and offset,
+    // the (m, l) of splits t (< kReduceThreads) and this thread's first U
+    // acc values (splits grp, grp + NG, ...), all loaded before any is
+    // used.  Records of empty splits hold stale values; they are loaded
+    // (the workspace holds every split) and get weight 0.
+    const int64_t L = a.seq_lens[seq];
+    const int64_t off = a.offsets[seq];
+    float2 ml0 = make_float2(kNegInf, 0.0f);
+    if (t < ns) ml0 = *reinterpret_cast<const float2 *>(a.ws_ml + (item0 + t * step) * 2);
+    float x0[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int j = grp + u * NG;
+        x0[u] = j < ns ? src[(int64_t)j * jstride] : 0.0f;
     }
+    const int64_t S = a.split_tokens;
+    auto live = [&](int j) {  // split j holds tokens: [jS, (j+1)S) meets [off, off + L)
+        return max((int64_t)j * S, off) < min((int64_t)(j + 1) * S, off + L);
+    };
+
+    // 1. max over live splits
+    float M = t < ns && live(t) ? ml0.x : kNegInf;
+    for (int j = t + kReduceThreads; j < ns; j += kReduceThreads)
+        if (live(j)) M = fmaxf(M, a.ws_ml[(item0 + j * step) * 2]);
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) M = fmaxf(M, __shfl_xor(M, m));
     if ((t & 63) == 0) red_s[wv] = M;
@@ -2011,10 +2034,9 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(DecodeArgs a) {
     // 2. weights and denominator
     float den = 0.0f;
     for (int j = t; j < ns; j += kReduceThreads) {
-        const Range R = split_range(a, seq, j);
         float wj = 0.0f;
-        if (R.hi > R.lo) {
-            const float2 ml = *reinterpret_cast<const float2 *>(a.ws_ml + (item0 + j * step) * 2);
+        if (live(j)) {
+            const float2 ml = j == t ? ml0 : *reinterpret_cast<const float2 *>(a.ws_ml + (item0 + j * step) * 2);
             wj = ml.x == kNegInf ? 0.0f : fast_exp2(ml.x - M);
             den = fmaf(ml.y, wj, den);
         }
@@ -2028,25 +2050,17 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(DecodeArgs a) {
 #pragma unroll
     for (int k = 1; k < kReduceThreads / 64; ++k) den += red_s[k];
 
-    // 3. weighted sum of this thread's splits for element d
-    const int d = t % D;
-    const int grp = t / D;
-    const float *src = a.ws_acc + item0 * D + d;
-    const int64_t jstride = step * D;
+    // 3. weighted sum of this thread's splits for element d, in split order
     float o = 0.0f;
-    int j = grp;
-    constexpr int U = 8;
-    for (; j + (U - 1) * NG < ns; j += U * NG) {
-        float x[U], wu[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            wu[u] = w_s[j + u * NG];
-            x[u] = src[(int64_t)(j + u * NG) * jstride];
+    for (int u = 0; u < U; ++u) {
+        const int j = grp + u * NG;
+        if (j < ns) {
+            const float wj = w_s[j];
+            o = fmaf(wj != 0.0f ? x0[u] : 0.0f, wj, o);
         }
-#pragma unroll
-        for (int u = 0; u < U; ++u) o = fmaf(wu[u] != 0.0f ? x[u] : 0.0f, wu[u], o);
     }
-    for (; j < ns; j += NG) {
+    for (int j = grp + U * NG; j < ns; j += NG) {
         const float wj = w_s[j];
         const float x = src[(int64_t)j * jstride];
         o = fmaf(wj != 0.0f ? x : 0.0f, wj, o);

@@ -188,7 +188,7 @@ def test_workspace_size_and_split_choice(lib):
     assert split(4, 8, 100, 12) == SHAPE
     # the choices on 256 compute units (the count assumed without a device)
     assert split(32, 8, 2048, 16) == 256
-    assert split(8, 8, 32768, 16) == 1024
+    assert split(8, 8, 32768, 16) == 2048
 
 
 def test_append_argument_checks(lib):
