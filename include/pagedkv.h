@@ -228,12 +228,14 @@ PKV_API int kv_gather(const pkv_pool *pool, int32_t layer,
 
 /*
  * paged_attn_decode_split_tokens -- the split size (tokens per work item)
- * of the split schedule when paged_attn_decode is called with
- * split_tokens = 0 and does not take the balanced schedule (see
- * paged_attn_decode_schedule).  Depends on the sizes and on the current
- * device's compute-unit count (256 is assumed when no device can be
- * queried).  Returns a positive multiple of 16, or a negative status for
- * bad sizes.
+ * of the split schedule for a bf16 pool when paged_attn_decode is called
+ * with split_tokens = 0 and takes neither the planned nor the balanced
+ * schedule (see paged_attn_decode_schedule, which also gives the choice
+ * for fp32 and int8 pools: those stop growing the split at 1024 positions
+ * once there are 2 workgroups per compute unit).  Depends on the sizes and
+ * on the current device's compute-unit count (256 is assumed when no
+ * device can be queried).  Returns a positive multiple of 16, or a
+ * negative status for bad sizes.
  */
 PKV_API int32_t paged_attn_decode_split_tokens(int32_t num_seqs, int32_t num_kv_heads,
                                                int32_t max_seq_len, int32_t block_size);

@@ -132,12 +132,13 @@ int64_t max_positions(int64_t max_len, int64_t bs) { return max_len > 0 ? max_le
 // positions while that still leaves at least 2 items per compute unit
 // (shorter splits cost more per token in pipeline start-up and partials
 // than they gain in balance).  Splits of 1024 positions and more keep
-// growing while the items exceed 4 per compute unit: one resident
-// workgroup per compute unit streaming twice as long measured faster (8 x
-// 32768 tokens: 192.9 us at 2048 against 198.3 us at 1024, same process).
-// On the decode batch (32 x <= 2048 tokens) this picks 256; on 8 x 32768
-// tokens, 2048.
-int64_t auto_split(int64_t num_seqs, int64_t hkv, int64_t max_len, int64_t bs) {
+// growing while the items exceed 4 per compute unit (bf16 pools only): one
+// resident workgroup per compute unit streaming twice as long measured
+// faster (8 x 32768 tokens: 192.9 us at 2048 against 198.3 us at 1024, same
+// process); the int8 kernel needs the second workgroup's wavefronts (141.6
+// us at 2048 against 116 us at 1024).  On the decode batch (32 x <= 2048
+// tokens) this picks 256; on 8 x 32768 tokens, 2048 for bf16, else 1024.
+int64_t auto_split(int64_t num_seqs, int64_t hkv, int64_t max_len, int64_t bs, bool long_rule) {
     const int64_t cus = cu_count();
     const int64_t smax = max_split_tokens(bs);
     const int64_t span = max_positions(max_len, bs);
@@ -147,7 +148,7 @@ int64_t auto_split(int64_t num_seqs, int64_t hkv, int64_t max_len, int64_t bs) {
     if (s > smax) s = smax;
     while (s * 2 <= smax && (items(s) > 8 * cus || splits(s) > kMaxSplits ||
                              (s < 256 && items(s * 2) >= 2 * cus) ||
-                             (s >= 1024 && items(s) > 4 * cus)))
+                             (long_rule && s >= 1024 && items(s) > 4 * cus)))
         s *= 2;
     return s;
 }
@@ -162,14 +163,14 @@ struct DecodePlan {
 };
 
 int plan_decode(int64_t num_seqs, int64_t hkv, int64_t hq, int64_t head_dim, int64_t max_len,
-                int64_t bs, int64_t split_req, DecodePlan *p) {
+                int64_t bs, int64_t split_req, DecodePlan *p, int32_t dtype = PKV_BF16) {
     if (num_seqs < 0 || hkv <= 0 || hq <= 0 || head_dim <= 0 || max_len < 0 || !is_pow2(bs))
         return PKV_ERR_SHAPE;
     // 0 (automatic) and a balanced-schedule request plan the automatic
     // split too: it sizes the fallback and the workspace bound
     const int64_t split = split_req == 0 || split_req == PKV_SPLIT_BALANCED ||
                                   split_req == PKV_SPLIT_PLANNED
-                              ? auto_split(num_seqs, hkv, max_len, bs)
+                              ? auto_split(num_seqs, hkv, max_len, bs, dtype == PKV_BF16)
                               : split_req;
     if (!split_ok(split, bs)) return PKV_ERR_SHAPE;
     p->split = split;
@@ -534,12 +535,16 @@ PKV_API size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_kv
                                                 int32_t num_q_heads, int32_t head_dim,
                                                 int32_t max_seq_len, int32_t block_size,
                                                 int32_t split_tokens) {
-    DecodePlan p;
+    DecodePlan p, p8;
     if (num_kv_heads <= 0 || num_q_heads % num_kv_heads) return (size_t)-1;
+    // the automatic split differs between bf16 and the other pool types:
+    // room for either
     if (plan_decode(num_seqs, num_kv_heads, num_q_heads, head_dim, max_seq_len, block_size,
-                    split_tokens, &p))
+                    split_tokens, &p) ||
+        plan_decode(num_seqs, num_kv_heads, num_q_heads, head_dim, max_seq_len, block_size,
+                    split_tokens, &p8, PKV_I8))
         return (size_t)-1;
-    int64_t need = p.total();
+    int64_t need = p.total() > p8.total() ? p.total() : p8.total();
     SplitPlan sp2;
     if ((split_tokens == 0 || split_tokens == PKV_SPLIT_PLANNED) &&
         planned_possible(num_seqs, num_kv_heads, max_seq_len, block_size, PKV_BF16, &sp2)) {
@@ -568,7 +573,7 @@ PKV_API int32_t paged_attn_decode_schedule(int32_t num_seqs, int32_t num_kv_head
     if (num_kv_heads <= 0 || num_q_heads <= 0 || num_q_heads % num_kv_heads) return PKV_ERR_SHAPE;
     DecodePlan p;
     const int st = plan_decode(num_seqs, num_kv_heads, num_q_heads, head_dim, max_seq_len,
-                               block_size, split_tokens, &p);
+                               block_size, split_tokens, &p, dtype);
     if (st) return st;
     if (balanced_refused(num_seqs, num_kv_heads, head_dim, max_seq_len, block_size, dtype,
                          split_tokens))
@@ -616,7 +621,7 @@ int decode_impl(const pkv_pool *pool, int32_t layer, const void *q, int32_t num_
     if (k_new && (!aligned16(k_new) || !aligned16(v_new))) return PKV_ERR_ALIGN;
     DecodePlan p;
     st = plan_decode(num_seqs, pool->num_kv_heads, num_q_heads, pool->head_dim, max_seq_len,
-                     pool->block_size, planned ? (int32_t)spl.smin : split_tokens, &p);
+                     pool->block_size, planned ? (int32_t)spl.smin : split_tokens, &p, pool->dtype);
     if (st) return st;
     const bool balanced = !planned && use_balanced(num_seqs, pool->num_kv_heads, pool->head_dim,
                                                    max_seq_len, pool->block_size, pool->dtype,

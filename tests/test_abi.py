@@ -189,6 +189,12 @@ def test_workspace_size_and_split_choice(lib):
     # the choices on 256 compute units (the count assumed without a device)
     assert split(32, 8, 2048, 16) == 256
     assert split(8, 8, 32768, 16) == 2048
+    sched = lib.paged_attn_decode_schedule
+    assert sched(8, 8, 64, 128, 32768, 16, 1, 0) == 2048   # bf16: one workgroup per CU
+    assert sched(8, 8, 64, 128, 32768, 16, 2, 0) == 1024   # int8: two per CU
+    assert sched(8, 8, 64, 128, 32768, 16, 0, 0) == 1024   # fp32
+    # the workspace for split_tokens = 0 covers the smaller (int8) split
+    assert ws(8, 8, 64, 128, 32768, 16, 0) >= ws(8, 8, 64, 128, 32768, 16, 1024)
 
 
 def test_append_argument_checks(lib):
@@ -258,7 +264,7 @@ def test_decode_schedule_choice(lib):
     assert f(8, 8, 64, 128, 32768, 16, BF16, SPLIT_PLANNED) == UNSUP
     assert f(2, 2, 8, 128, 100, 16, F32, SPLIT_PLANNED) == UNSUP
     assert f(2, 2, 8, 128, 100, 16, BF16, SPLIT_PLANNED) == PLANNED
-    assert f(8, 8, 64, 128, 32768, 16, F32, 0) == split(8, 8, 32768, 16)
+    assert f(8, 8, 64, 128, 32768, 16, F32, 0) == 1024                     # fp32: no long-split rule
     assert f(8, 8, 64, 128, 32768, 16, BF16, 512) == 512
     assert f(5000, 8, 32, 128, 4096, 16, BF16, 0) == split(5000, 8, 4096, 16)
     assert f(8, 8, 64, 128, 32768, 16, 7, 0) == DTYPE
