@@ -177,6 +177,22 @@ __device__ __forceinline__ void wave_lds_order() {
     __builtin_amdgcn_wave_barrier();
 }
 
+// max(v of lane l, v of lane l ^ 16) and the same for l ^ 32, with the
+// gfx950 row swaps (v_permlane16_swap / v_permlane32_swap: VALU operations,
+// no LDS permute in the dependency chain).  With both operands v, the
+// 16-swap leaves lane l holding its own value in one result and that of
+// lane l ^ 16 in the other; likewise for 32.
+__device__ __forceinline__ float max_xor16(float v) {
+    const unsigned u = __float_as_uint(v);
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+    const unsigned u = __float_as_uint(v);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));

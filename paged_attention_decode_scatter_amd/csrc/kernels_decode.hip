@@ -867,8 +867,7 @@ __device__ __forceinline__ void attend_range(const DecodeArgs &a, int seq, const
             s[i] = (full || row_live(4 * g4 + i)) ? sacc[i] * sl2 : kNegInf;
             cm = fmaxf(cm, s[i]);
         }
-        cm = fmaxf(cm, __shfl_xor(cm, 16));
-        cm = fmaxf(cm, __shfl_xor(cm, 32));
+        cm = max_xor32(max_xor16(cm));
         float alpha = 1.0f;
         if (cm > m_h + kLazy) {
             alpha = m_h == kNegInf ? 0.0f : fast_exp2(m_h - cm);
@@ -1278,8 +1277,7 @@ __device__ __forceinline__ void attend_range_q8(const DecodeArgs &a, const Range
             s[i] = (full || row_live(4 * g4 + i)) ? dot * ksf[i] * sl2 : kNegInf;
             cm = fmaxf(cm, s[i]);
         }
-        cm = fmaxf(cm, __shfl_xor(cm, 16));
-        cm = fmaxf(cm, __shfl_xor(cm, 32));
+        cm = max_xor32(max_xor16(cm));
         float alpha = 1.0f;
         if (cm > m_h + kLazy) {
             alpha = m_h == kNegInf ? 0.0f : fast_exp2(m_h - cm);
@@ -1881,8 +1879,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeArgs a) {
                 s[i] = (full || row_live(4 * g4 + i)) ? sacc[i] * sl2 : kNegInf;
                 cm = fmaxf(cm, s[i]);
             }
-            cm = fmaxf(cm, __shfl_xor(cm, 16));
-            cm = fmaxf(cm, __shfl_xor(cm, 32));
+            cm = max_xor32(max_xor16(cm));
             float alpha = 1.0f;
             if (cm > m_h + kLazy) {
                 alpha = m_h == kNegInf ? 0.0f : fast_exp2(m_h - cm);

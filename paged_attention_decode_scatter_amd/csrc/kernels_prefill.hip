@@ -253,8 +253,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per
                             for (int i = 0; i < 4; ++i)
                                 s[i] = (full || (rok[i] && kp0 + i <= qpos[t])) ? sacc[i] * sl2 : kNegInf;
                             float cm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-                            cm = fmaxf(cm, __shfl_xor(cm, 16));
-                            cm = fmaxf(cm, __shfl_xor(cm, 32));
+                            cm = max_xor32(max_xor16(cm));
                             float alpha = 1.0f;
                             if (cm > m_h[t] + kLazy) {
                                 alpha = m_h[t] == kNegInf ? 0.0f : fast_exp2(m_h[t] - cm);
