@@ -394,9 +394,11 @@ def prefill_ops(w_dec, N, W, reps=64):
     return {
         "scatter_prefill": {"rows": rows, "valid_rows": valid, "bytes": scat_bytes,
                             "ms": t_s, "GB/s": scat_bytes / t_s / 1e6,
+                            "frac": scat_bytes / t_s / 1e6 / HBM_PEAK_GBS, "bound": "hbm",
                             "per_call_events_median_ms": t_s_med},
         "gather_prefill": {"rows": total, "bytes": gath_bytes, "ms": t_g,
-                           "GB/s": gath_bytes / t_g / 1e6, "per_call_events_median_ms": t_g_med},
+                           "GB/s": gath_bytes / t_g / 1e6, "frac": gath_bytes / t_g / 1e6 / HBM_PEAK_GBS,
+                           "bound": "hbm", "per_call_events_median_ms": t_g_med},
         "timing": f"{reps} back-to-back C-ABI calls, layer rotated, one event pair around them",
     }
 
@@ -462,6 +464,7 @@ def block_ops(w_dec, N, pairs=64, sets=4, reps=32, swap_blocks=64, swap_reps=6):
     return {
         "copy_blocks": {"pairs": pairs, "block_bytes_per_tensor": block_bytes,
                         "bytes": copy_bytes, "ms": t_c, "GB/s": copy_bytes / t_c / 1e6,
+                        "frac": copy_bytes / t_c / 1e6 / HBM_PEAK_GBS, "bound": "hbm",
                         "timing": f"{reps} back-to-back C-ABI calls over {sets} disjoint pair "
                                   "sets, one event pair around them"},
         "swap_out": {"blocks": swap_blocks, "bytes": swap_bytes, "ms": t_out,
