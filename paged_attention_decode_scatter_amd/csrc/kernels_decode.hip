@@ -277,9 +277,9 @@ __device__ bool plan_item(const DecodeArgs &a, int32_t *scratch, Item &it, Range
         L = L < 0 ? 0 : (L > a.max_len ? a.max_len : L);
         O = O < 0 ? 0 : (O > bsm ? bsm : O);
         if (live) scratch[lane] = L;
-        // total length: below 64 * 2^24, summed as L / 16 and L % 16 to
-        // stay in int32 (its float value's rounding is within the margins)
-        const float totf = 16.0f * (float)wave_total(L >> 4) + (float)wave_total(L & 15);
+        // total length: below 64 * 2^24 < 2^31 (the float value's rounding is
+        // within the bounds' margins)
+        const float totf = (float)wave_total(L);
         // pieces of all pairs at split S
         auto count = [&](int32_t S) -> int32_t {
             const float rcp = __builtin_amdgcn_rcpf((float)S);
