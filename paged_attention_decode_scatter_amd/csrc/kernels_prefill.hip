@@ -10,11 +10,11 @@
 // (more queries than tokens) sees nothing and gets zeros.  n = 1 is decode.
 //
 // bf16 kernel (matrix cores).  Workgroup = (kv head, sequence, query
-// tile), 8 wavefronts; wavefront w handles query head kv*G + w % G and the
-// tile's (w / G)-th group of 32 or 64 queries, in sub-tiles of 16 that are
+// tile), max(4, G) wavefronts; wavefront w handles query head kv*G + w % G and the
+// tile's (w / G)-th group of 48 (head_dim 128) or 64 (64) queries, in sub-tiles of 16 that are
 // its MFMA columns.  Per 16-position chunk of keys:
 //   the workgroup loads the chunk's K rows (registers, then a padded LDS
-//   tile) and V rows (straight into LDS) once for all 8 wavefronts, a ring
+//   tile) and V rows (straight into LDS) once for all its wavefronts, a ring
 //   of kPrefillRing chunks so all but one are in flight; one barrier per
 //   chunk; each
 //   wavefront reads the chunk's K and V operand fragments once, and for
@@ -56,13 +56,13 @@ __device__ __forceinline__ int64_t stage_entries(const PrefillArgs &a, int seq, 
 }  // namespace
 
 template <int D, int G, bool UB>
-__global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per_eu(2))) void prefill_mfma_kernel(
+__global__ __launch_bounds__(64 * kPrefillWaves<G>) __attribute__((amdgpu_waves_per_eu(2))) void prefill_mfma_kernel(
     PrefillArgs a) {
     using S = MfmaShape<D>;
     constexpr int ROWB = S::ROWB, PPR = S::PPR, NP = S::NP, KS = S::KS, NV = S::NV;
     constexpr int VSLAB = S::VSLAB, VTILE = S::VTILE, KROW = S::KROW, KTILE = S::KTILE;
     constexpr int NB = kPrefillRing;            // chunks in the LDS ring
-    constexpr int NW = kPrefillWaves;           // wavefronts: G heads x NW / G query groups
+    constexpr int NW = kPrefillWaves<G>;        // wavefronts: G heads x NW / G query groups
     constexpr int LPW = (NP + NW - 1) / NW;     // tile-load instructions per loading wave
     constexpr int QW = kPrefillWaveQueries<D, G>;   // queries per wavefront
     constexpr int QT = QW / 16;                 // 16-query sub-tiles per wavefront
@@ -454,9 +454,9 @@ hipError_t run_prefill(const PrefillArgs &a, hipStream_t s) {
     if constexpr (DT == 1) {
         const int64_t nwg = (int64_t)a.q_tiles * a.num_seqs * a.num_kv_heads;
         if (a.pool.lbs >= 4)
-            hipLaunchKernelGGL((prefill_mfma_kernel<D, G, true>), dim3((unsigned)nwg), dim3(64 * kPrefillWaves), 0, s, a);
+            hipLaunchKernelGGL((prefill_mfma_kernel<D, G, true>), dim3((unsigned)nwg), dim3(64 * kPrefillWaves<G>), 0, s, a);
         else
-            hipLaunchKernelGGL((prefill_mfma_kernel<D, G, false>), dim3((unsigned)nwg), dim3(64 * kPrefillWaves), 0, s, a);
+            hipLaunchKernelGGL((prefill_mfma_kernel<D, G, false>), dim3((unsigned)nwg), dim3(64 * kPrefillWaves<G>), 0, s, a);
     } else {
         const int64_t nwg = (int64_t)a.num_q_rows * a.head_groups;
         hipLaunchKernelGGL((prefill_valu_kernel<DT, D, G>), dim3((unsigned)nwg), dim3(64 * a.heads_per_wg), 0, s,

@@ -165,15 +165,19 @@ constexpr int kSegMax = 80;
 
 // Prefill / append attention: the last n_s = q_start[s+1] - q_start[s]
 // tokens of sequence s are its queries (rows q_start[s].. of q and out).
-// Prefill (bf16 kernel) workgroups: kPrefillWaves wavefronts, G query heads
-// x kPrefillWaves / G query groups, sharing every staged key chunk.  A
-// wavefront holds kPrefillWaveQueries queries (sub-tiles of 16), as many as
-// fit two wavefronts per SIMD without spills; a workgroup tile is
-// kPrefillTile queries.  Measured on MI355X (prefix-sharing batch, every
-// suffix token a query, head_dim 128, G 4): 16 queries per wavefront
-// 11.2 ms, 32: 8.3 ms, 48: 7.1 ms (64 spills); the depth of the key ring
-// (3 to 8 chunks) changed nothing.
-constexpr int kPrefillWaves = 8;
+// Prefill (bf16 kernel) workgroups: kPrefillWaves<G> = max(4, G)
+// wavefronts, G query heads x kPrefillWaves<G> / G query groups, sharing
+// every staged key chunk.  A wavefront holds kPrefillWaveQueries queries
+// (sub-tiles of 16), as many as fit two wavefronts per SIMD without spills;
+// a workgroup tile is kPrefillTile queries.  Measured on MI355X
+// (prefix-sharing batch, every suffix token a query, head_dim 128, G 4): 16
+// queries per wavefront 11.2 ms, 32: 8.3 ms, 48: 7.1 ms (64 spills); the
+// depth of the key ring (3 to 8 chunks) changed nothing; 4 wavefronts per
+// workgroup (two workgroups per CU, whose barriers do not line up) 6.59 ms
+// against 6.88 ms with 8 (one per CU), same process.
+template <int G>
+inline constexpr int kPrefillWaves = G > 4 ? G : 4;
+inline int prefill_waves(int64_t group) { return group > 4 ? (int)group : 4; }
 #ifndef PKV_PREFILL_WQ64
 #define PKV_PREFILL_WQ64 64
 #endif
@@ -187,9 +191,9 @@ constexpr int kPrefillRing = PKV_PREFILL_RING;   // key chunks staged in LDS (al
 template <int D, int G>
 inline constexpr int kPrefillWaveQueries = D == 64 ? PKV_PREFILL_WQ64 : PKV_PREFILL_WQ128;
 template <int D, int G>
-inline constexpr int kPrefillTile = kPrefillWaveQueries<D, G> * (kPrefillWaves / G);
+inline constexpr int kPrefillTile = kPrefillWaveQueries<D, G> * (kPrefillWaves<G> / G);
 inline int prefill_tile(int64_t head_dim, int64_t group) {
-    return (head_dim == 64 ? PKV_PREFILL_WQ64 : PKV_PREFILL_WQ128) * (kPrefillWaves / (int)group);
+    return (head_dim == 64 ? PKV_PREFILL_WQ64 : PKV_PREFILL_WQ128) * (prefill_waves(group) / (int)group);
 }
 
 struct PrefillArgs {
