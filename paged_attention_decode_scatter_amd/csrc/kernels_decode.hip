@@ -17,14 +17,20 @@
 //   (logical token t sits at flat position offset + t).  A work item is
 //   (sequence, kv head, split); one wavefront owns it and all G query heads
 //   of that kv head, so every K/V row is read from HBM once and used G
-//   times.  A workgroup holds up to 8 wavefronts (4 for fp32) = the kv
-//   heads of one (sequence, split): they share the block-table entries,
-//   staged in LDS once per workgroup, and together read each block's layer
-//   slice (block_size x all heads, contiguous) at the same time.  Workgroups are renumbered so that neighbours in the logical
-//   order (same split, consecutive sequences: a shared prefix) land on the
-//   same XCD and share its L2.
+//   times.  A workgroup holds up to 4 wavefronts = a group of kv heads of
+//   one (sequence, split): they share the block-table entries, staged in
+//   LDS once per workgroup, and read each block's layer slice together.
+//   Three schedules map workgroups to work items:
+//   - split: one workgroup per (sequence, split, head group), split S chosen
+//     by the host from max_seq_len; workgroups are renumbered so that the
+//     splits of one sequence land on different XCDs;
+//   - device-planned split (plan_item below): every workgroup reads all
+//     lengths, picks S so the pieces fit two workgroups per compute unit,
+//     and takes one piece;
+//   - balanced (decode_stream_kernel): equal shares of (head group,
+//     sequence, 16-position chunk) units, several segments per workgroup.
 //
-// bf16 kernel (MFMA QK^T, VALU PV), per 16-position chunk of one block:
+// bf16 kernel, per 16-position chunk of one block:
 //   QK:  S^T = K_chunk (16 x D) . Q^T (D x 16 heads, G real) with
 //        v_mfma_f32_16x16x32_bf16.  Lane l loads K row l%16, elements
 //        32j + 8*(l/16) .. +8 for step j -- exactly the MFMA operand layout,
@@ -35,24 +41,34 @@
 //        exceeds it by more than 8 (so p <= 256; the result is exact
 //        whatever the reference, since acc and l share it); the P.V
 //        accumulators are rescaled only on such a move (a wave-uniform
-//        branch, rare after the first chunks).
-//   PV:  P goes through LDS to the "row layout": lane (r, c) holds 16 bytes
-//        (8 elements) of V row 4i + r for pass i, so every V load
-//        instruction covers whole rows; acc[h][e] += p * V in fp32.
-//   Masked positions (before the offset, past seq_len, invalid table entry)
-//   get score -inf and their rows are never loaded, so poisoned (NaN) pool
-//   slots cannot leak in.
-//   The next chunk's K and V are loaded before the current one is computed.
+//        branch, rare after the first chunks).  The chunk max across the
+//        four 16-lane rows uses the gfx950 row swaps.
+//   PV:  V goes HBM -> LDS directly (global_load_lds, 16 bytes per lane) in
+//        a padded tile; the transposing LDS read gives the B operand and
+//        O (16 heads x D) += P . V runs as v_mfma_f32_16x16x16_bf16, with P
+//        (the score layout is the A-operand layout) rounded to bf16.
+//   Loads are unconditional and in bounds: a missing block reads block 0 and
+//   prefetches past the end re-read the last chunk.  Masked positions
+//   (before the offset, past seq_len, invalid table entry) get score -inf
+//   and their V tile rows are zeroed, so poisoned (NaN) pool slots cannot
+//   leak in.  A ring of chunks keeps the next ones' loads in flight while
+//   one is computed.
+//
+// int8 kernel (decode_q8_kernel): QK^T on the int8 matrix cores over the
+// codes as loaded, V codes converted to bf16 into the same tile layout; see
+// its section below.
 //
 // fp32 kernel (VALU): row layout for K and V, dot products reduced over the
 //   lanes of a row with DPP, per-chunk wave-uniform max; used for the fp32
 //   pool dtype.
 //
 // Split-K: with more than one split per sequence, each work item writes its
-// unnormalised (m, l, acc) to the workspace and a second kernel merges the
-// splits of each (sequence, query head) in split order:
-//   M = max_j m_j,  L = sum_j l_j 2^(m_j - M),  O = sum_j acc_j 2^(m_j - M) / L.
-// With one split the first kernel normalises and writes the output itself.
+// unnormalised (m, l, acc) to the workspace, and the splits of each
+// (sequence, query head) are merged in split order:
+//   M = max_j m_j,  L = sum_j l_j 2^(m_j - M),  O = sum_j acc_j 2^(m_j - M) / L
+// by the work item that finishes last (at most 16 splits) or by a second
+// kernel (reduce_kernel).  With one split the work item normalises and
+// writes the output itself.
 #include "attn_common.h"
 
 namespace pkv {
