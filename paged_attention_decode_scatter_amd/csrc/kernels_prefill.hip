@@ -175,42 +175,16 @@ __global__ __launch_bounds__(64 * kPrefillWaves<G>) __attribute__((amdgpu_waves_
                 return bt_s[(int)((p >> lbs) - jb0)] >= 0;
             };
 
-            u32x4 kring[NB][LPW];
-#pragma unroll
-            for (int q = 0; q < NB - 1; ++q) load_chunk(min(first + 16 * q, last), kring[q], q);
-            bool done = false;
-            for (int64_t pc = first; !done;) {
-#pragma unroll
-                for (int q = 0; q < NB; ++q) {
-                    if (!done) {
-                        // chunk pc's loads done (the next chunk's stay in flight)
-                        if (loader) {
-                            constexpr int ahead = (NB - 2) * 2 * LPW;   // later chunks' loads
-                            static_assert(ahead < 64, "vmcnt range");
-                            __builtin_amdgcn_s_waitcnt((ahead & 15) | ((ahead >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-                        }
-                        wave_lds_order();
-                        if (loader) {
-#pragma unroll
-                            for (int k = 0; k < LPW; ++k) {
-                                const int i = w + NW * k;
-                                if (i < NP) {
-                                    *reinterpret_cast<u32x4 *>(ktile[q] + (i + NP * trow) * KROW + 16 * tpp) =
-                                        kring[q][k];
-                                    if (!row_ok(pc, i + NP * trow))
-                                        *reinterpret_cast<u32x4 *>(vtile[q] + i * VSLAB + 16 * lane) =
-                                            u32x4{0, 0, 0, 0};
-                                }
-                            }
-                        }
-                        __syncthreads();  // chunk pc's tiles complete; slot (q+NB-1)%NB free
-                        const int nq2 = (q + NB - 1) % NB;
-                        load_chunk(min(pc + 16 * (NB - 1), last), kring[nq2], nq2);
-
+            // Two chunks per stage and one barrier per stage: a ring of four
+            // chunk slots holds two stages, one being computed while the next
+            // one's loads are in flight.  (A loop over more chunks per stage
+            // spills: K passes through registers.)
+            static_assert(NB == 4, "two stages of two chunks");
+            auto compute_chunk = [&](int64_t cpc, int qs) {
                         // the chunk's K operand (A) and V operand (B) fragments,
                         // read once and used by every sub-tile
-                        const char *kt = ktile[q];
-                        const char *vt = vtile[q];
+                        const char *kt = ktile[qs];
+                        const char *vt = vtile[qs];
                         u32x4 kf[KS];
 #pragma unroll
                         for (int j = 0; j < KS; ++j)
@@ -229,18 +203,18 @@ __global__ __launch_bounds__(64 * kPrefillWaves<G>) __attribute__((amdgpu_waves_
                         // no mask needed: every row a live token at or before
                         // the wavefront's first query (wave-uniform); the
                         // selects below then keep every score
-                        bool full = nq > 0 && pc >= lo && pc + 16 <= phi && pc + 15 - off <= pmin;
+                        bool full = nq > 0 && cpc >= lo && cpc + 16 <= phi && cpc + 15 - off <= pmin;
                         if constexpr (UB) {
-                            full = full && bt_s[(int)((pc >> lbs) - jb0)] >= 0;
+                            full = full && bt_s[(int)((cpc >> lbs) - jb0)] >= 0;
                         } else {
                             full = false;   // rows may sit in different blocks
                         }
                         // masked chunks: row i of this lane is live and holds the
                         // key at logical position kp0 + i
-                        const int kp0 = (int)(pc - off) + 4 * g4;
+                        const int kp0 = (int)(cpc - off) + 4 * g4;
                         bool rok[4];
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) rok[i] = !full && row_ok(pc, 4 * g4 + i);
+                        for (int i = 0; i < 4; ++i) rok[i] = !full && row_ok(cpc, 4 * g4 + i);
                         auto subtile = [&](int t) {
                             // S^T: lane holds S[token 4*g4 + i][query 16 t + cn]
                             f32x4 sacc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -283,7 +257,41 @@ __global__ __launch_bounds__(64 * kPrefillWaves<G>) __attribute__((amdgpu_waves_
                         };
 #pragma unroll
                         for (int t = 0; t < QT; ++t) subtile(t);
-                        pc += 16;
+            };
+            u32x4 kring[NB][LPW];
+            load_chunk(min(first, last), kring[0], 0);
+            load_chunk(min(first + 16, last), kring[1], 1);
+            bool done = false;
+            for (int64_t pc = first; !done;) {
+#pragma unroll
+                for (int st = 0; st < 2; ++st) {
+                    if (!done) {
+                        // this stage's loads done (the only ones in flight)
+                        if (loader) __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));
+                        wave_lds_order();
+                        if (loader) {
+#pragma unroll
+                            for (int c = 0; c < 2; ++c) {
+                                const int q = 2 * st + c;
+#pragma unroll
+                                for (int k = 0; k < LPW; ++k) {
+                                    const int i = w + NW * k;
+                                    if (i < NP) {
+                                        *reinterpret_cast<u32x4 *>(ktile[q] + (i + NP * trow) * KROW + 16 * tpp) =
+                                            kring[q][k];
+                                        if (!row_ok(pc + 16 * c, i + NP * trow))
+                                            *reinterpret_cast<u32x4 *>(vtile[q] + i * VSLAB + 16 * lane) =
+                                                u32x4{0, 0, 0, 0};
+                                    }
+                                }
+                            }
+                        }
+                        __syncthreads();  // the stage's tiles complete; the other stage's slots free
+                        load_chunk(min(pc + 32, last), kring[2 - 2 * st], 2 - 2 * st);
+                        load_chunk(min(pc + 48, last), kring[3 - 2 * st], 3 - 2 * st);
+                        compute_chunk(pc, 2 * st);
+                        if (pc + 16 <= last) compute_chunk(pc + 16, 2 * st + 1);
+                        pc += 32;
                         done = pc > last;
                     }
                 }
