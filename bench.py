@@ -264,6 +264,47 @@ def int8_decode(w, N, W, reps=32):
     return out
 
 
+def read_ceiling(w, N, reps=32):
+    """The measured read rate for the step's bytes: kv_read_blocks over
+    every block the decode batch's tables use (the K and V layer slices, the
+    bytes paged decode attention reads), back to back with the layer
+    rotated.  No compute, one workgroup per block."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    bt = w.block_tables.cpu().numpy()
+    lens = w.seq_lens.cpu().numpy().astype(np.int64)
+    offs = w.offsets.cpu().numpy().astype(np.int64)
+    used = [bt[s, j] for s in range(w.num_seqs) if lens[s] > 0
+            for j in range(offs[s] // w.block_size, (offs[s] + lens[s] - 1) // w.block_size + 1)]
+    ids_np = np.unique(np.array([b for b in used if b >= 0], np.int32))
+    ids = torch.from_numpy(ids_np).to(w.q.device)
+    out = torch.empty(ids.numel(), dtype=torch.int32, device=w.q.device)
+    lib = N.load_library()
+    pool = N.make_pool(w.k_pool, w.v_pool)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(w.q.device).cuda_stream)
+    args = [(ctypes.byref(pool), l, ctypes.c_void_p(ids.data_ptr()), ids.numel(),
+             ctypes.c_void_p(out.data_ptr()), stream) for l in range(w.num_layers)]
+    for i in range(3):
+        if lib.kv_read_blocks(*args[i]):
+            raise RuntimeError("kv_read_blocks failed")
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for i in range(reps):
+        lib.kv_read_blocks(*args[i % w.num_layers])
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) / reps * 1e3
+    nbytes = int(ids.numel()) * 2 * w.block_size * w.row_bytes
+    return {"blocks": int(ids.numel()), "bytes": nbytes, "us": us, "GB/s": nbytes / us / 1e3,
+            "frac": nbytes / us / 1e3 / HBM_PEAK_GBS, "kernel": "read_blocks_kernel (kv_read_blocks)",
+            "what": "the K and V layer slices of every block the tables use, read and XOR-folded, "
+                    f"{reps} back-to-back calls, layer rotated"}
+
+
 def time_op(fn, reps, layers, warm=3):
     """Median and mean of per-call HIP-event times (ms) of fn(layer), with
     the layer rotated so repeats touch different memory."""
@@ -778,6 +819,7 @@ def main():
             "decode_alone_GBps": alg_bytes / (dec_only * 1e-3) / 1e9,
             "per_call_events_avg_us": dec_avg * 1e3,
             "per_call_events_median_us": dec_med * 1e3,
+            "measured_read_ceiling": read_ceiling(w, N),
         },
     }
     if not args.no_ops:

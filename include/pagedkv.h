@@ -413,6 +413,23 @@ PKV_API int paged_attn_prefill(const pkv_pool *pool, int32_t layer,
                                int32_t num_seqs, float scale, void *out, void *stream);
 
 /*
+ * kv_read_blocks -- a read-rate reference, not part of the pages' method:
+ * for i < num_ids, reads the layer-`layer` slice (block_size rows of all kv
+ * heads, contiguous) of K and of V of block block_ids[i] and writes the
+ * XOR of all their 32-bit words to out[i].  The slices are the bytes paged
+ * decode attention reads for those blocks, so timing this call gives the
+ * read rate the decode kernels are compared with.
+ *   block_ids     device int32 [num_ids]; an id outside [0, num_blocks)
+ *                 reads nothing and gives 0
+ *   out           device uint32 [num_ids]
+ * V is read when pool->v is set.  For a quantised pool the codes are read
+ * (not the scales).  Asynchronous on `stream`.
+ * Errors: PKV_ERR_NULL, _DTYPE, _SHAPE, _LAYER, _ALIGN, _LAUNCH.
+ */
+PKV_API int kv_read_blocks(const pkv_pool *pool, int32_t layer, const int32_t *block_ids,
+                           int64_t num_ids, uint32_t *out, void *stream);
+
+/*
  * kv_copy_blocks -- whole-block copies: for i < num_pairs, every layer of K
  * and of V of block src_blocks[i] is copied to block dst_blocks[i] (codes
  * and scales for a quantised pool).  This

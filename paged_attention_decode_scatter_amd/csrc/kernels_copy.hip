@@ -514,6 +514,54 @@ hipError_t launch_copy_blocks(const CopyBlocksArgs &a, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
+// Read-rate reference (kv_read_blocks): workgroup i reads the layer slice
+// of K and of V of block ids[i] (block_size rows, contiguous) with 16-byte
+// loads, kUnroll per tensor in flight per lane, and writes the XOR of all
+// their 32-bit words -- a value that depends on every byte, so no load can
+// be dropped.  An id outside [0, num_blocks) reads nothing and writes 0.
+// It moves the bytes paged decode attention reads, with no compute, as the
+// measured ceiling its rate is compared with.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kCopyThreads) void read_blocks_kernel(ReadBlocksArgs a) {
+    __shared__ uint32_t part[kCopyThreads / 64];
+    const int64_t b = a.ids[blockIdx.x];
+    uint32_t x = 0;
+    if (b >= 0 && b < a.num_blocks) {
+        const int64_t base = b * a.block_stride + a.layer_off;
+        const char *k = a.k + base;
+        const char *v = a.v ? a.v + base : nullptr;
+        const int n16 = (int)(a.slice_bytes >> 4);
+        for (int i0 = threadIdx.x; i0 < n16; i0 += kCopyThreads * kUnroll) {
+            u32x4 kk[kUnroll], vv[kUnroll];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const int i = i0 + u * kCopyThreads;
+                kk[u] = i < n16 ? ld16(k + ((int64_t)i << 4)) : u32x4{0, 0, 0, 0};
+                vv[u] = (v && i < n16) ? ld16(v + ((int64_t)i << 4)) : u32x4{0, 0, 0, 0};
+            }
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) x ^= kk[u].x ^ kk[u].y ^ kk[u].z ^ kk[u].w ^
+                                                     vv[u].x ^ vv[u].y ^ vv[u].z ^ vv[u].w;
+        }
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) x ^= (uint32_t)__shfl_xor((int)x, d);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = x;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t r = 0;
+#pragma unroll
+        for (int wv = 0; wv < kCopyThreads / 64; ++wv) r ^= part[wv];
+        a.out[blockIdx.x] = r;
+    }
+}
+
+hipError_t launch_read_blocks(const ReadBlocksArgs &a, hipStream_t s) {
+    hipLaunchKernelGGL(read_blocks_kernel, dim3((unsigned)a.n), dim3(kCopyThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Contract validation (debug): counts offsets outside [0, bs), seq_len
 // outside [0, min(capacity, max_seq_len)] with capacity = bt_stride*bs - off
 // [P3 sec. 2.2], used table entries outside [0, num_blocks), and slots that

@@ -747,6 +747,28 @@ PKV_API int paged_attn_prefill(const pkv_pool *pool, int32_t layer, const void *
                                     static_cast<hipStream_t>(stream)));
 }
 
+PKV_API int kv_read_blocks(const pkv_pool *pool, int32_t layer, const int32_t *block_ids,
+                           int64_t num_ids, uint32_t *out, void *stream) {
+    int st = check_pool(pool, false);
+    if (st) return st;
+    if (layer < 0 || layer >= pool->num_layers) return PKV_ERR_LAYER;
+    if (num_ids < 0 || num_ids > INT32_MAX) return PKV_ERR_SHAPE;
+    if (num_ids == 0) return PKV_OK;
+    if (!block_ids || !out) return PKV_ERR_NULL;
+    const PoolView v = make_view(pool, layer);
+    ReadBlocksArgs a{};
+    a.k = v.k;
+    a.v = v.v;
+    a.ids = block_ids;
+    a.out = out;
+    a.n = num_ids;
+    a.num_blocks = pool->num_blocks;
+    a.block_stride = v.block_stride;
+    a.layer_off = v.layer_off;
+    a.slice_bytes = (int64_t)v.row_bytes << v.lbs;
+    return status_of(launch_read_blocks(a, static_cast<hipStream_t>(stream)));
+}
+
 PKV_API int kv_copy_blocks(const pkv_pool *pool, const int32_t *src_blocks,
                            const int32_t *dst_blocks, int64_t num_pairs, void *stream) {
     int st = check_pool(pool, false);

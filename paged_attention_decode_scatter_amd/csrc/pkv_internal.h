@@ -235,6 +235,20 @@ struct CopyBlocksArgs {
     int64_t pieces;        // ceil(block_bytes / kCopyBlockPiece)
 };
 
+// Read-rate reference: the layer slices of listed blocks, read and folded
+// into one checksum per block.
+struct ReadBlocksArgs {
+    const char *k;
+    const char *v;         // may be null
+    const int32_t *ids;
+    uint32_t *out;
+    int64_t n;
+    int64_t num_blocks;
+    int64_t block_stride;
+    int64_t layer_off;
+    int64_t slice_bytes;   // block_size * row_bytes
+};
+
 struct ValidateArgs {
     const int32_t *block_tables;
     const int32_t *seq_lens;
@@ -260,6 +274,7 @@ hipError_t launch_copy_blocks(const CopyBlocksArgs &a, hipStream_t s);
 hipError_t launch_scatter_q8(const ScatterQ8Args &a, hipStream_t s);
 hipError_t launch_gather_q8(const GatherArgs &a, int head_dim, hipStream_t s);
 hipError_t launch_validate(const ValidateArgs &a, hipStream_t s);
+hipError_t launch_read_blocks(const ReadBlocksArgs &a, hipStream_t s);
 // Returns hipErrorInvalidValue when (dtype, head_dim, group) is not built.
 hipError_t launch_decode(const DecodeArgs &a, int dtype, int head_dim, int group,
                          hipStream_t s);

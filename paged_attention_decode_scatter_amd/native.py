@@ -33,6 +33,7 @@ SYMBOLS = (
     "paged_attn_decode_append",
     "paged_attn_prefill",
     "kv_copy_blocks",
+    "kv_read_blocks",
     "kv_swap_out",
     "kv_swap_in",
     "kv_validate",
@@ -112,6 +113,8 @@ def load_library(path: str = LIB_PATH):
                                       sz, p]
     lib.kv_copy_blocks.restype = ctypes.c_int
     lib.kv_copy_blocks.argtypes = [pp, p, p, i64, p]
+    lib.kv_read_blocks.restype = ctypes.c_int
+    lib.kv_read_blocks.argtypes = [pp, i32, p, i64, p, p]
     lib.kv_swap_out.restype = ctypes.c_int
     lib.kv_swap_out.argtypes = [pp, p, i64, p, p, p]
     lib.kv_swap_in.restype = ctypes.c_int
@@ -429,6 +432,21 @@ def paged_attn_prefill(k_pool, v_pool, layer, q, q_start, block_tables, seq_lens
         _ptr(block_tables), block_tables.shape[1], _ptr(seq_lens), _ptr(offsets),
         seq_lens.shape[0], float(scale), _ptr(out), _stream(q))
     _check("paged_attn_prefill", st)
+    return out
+
+
+def kv_read_blocks(k_pool, v_pool, layer, block_ids, out=None):
+    """XOR checksum of the layer slice of K (and V) of each listed block: a
+    read-rate reference (see include/pagedkv.h).  Returns int32 [n] (the
+    uint32 checksums' bits)."""
+    pool = make_pool(k_pool, v_pool)
+    _need(block_ids, torch.int32, "block_ids")
+    n = int(block_ids.numel())
+    if out is None:
+        out = torch.empty(n, dtype=torch.int32, device=block_ids.device)
+    st = load_library().kv_read_blocks(ctypes.byref(pool), int(layer), _ptr(block_ids), n, _ptr(out),
+                                       _stream(block_ids))
+    _check("kv_read_blocks", st)
     return out
 
 

@@ -33,7 +33,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == len(set(names)) == 32
+    assert len(names) == len(set(names)) == 33
     assert set(names) == set(N.SYMBOLS) | set(N.BM_SYMBOLS)
     for n in names:
         assert hasattr(lib, n), n
@@ -271,6 +271,18 @@ def test_decode_schedule_choice(lib):
     assert f(8, 8, 60, 128, 32768, 16, BF16, 0) == SHAPE
     assert f(2, 2, 8, 128, 100, 16, BF16, -1) == 0                         # asked for
     assert f(2, 2, 8, 128, 100, 16, F32, -1) == UNSUP
+
+
+def test_read_blocks_argument_checks(lib):
+    f = lib.kv_read_blocks
+    by = ctypes.byref
+    assert f(None, 0, A, 4, A, None) == NULL
+    assert f(by(pool()), 2, A, 4, A, None) == LAYER
+    assert f(by(pool()), 0, A, -1, A, None) == SHAPE
+    assert f(by(pool()), 0, A, 0, A, None) == OK            # nothing to read
+    assert f(by(pool()), 0, None, 4, A, None) == NULL
+    assert f(by(pool()), 0, A, 4, None, None) == NULL
+    assert f(by(pool(bs=12)), 0, A, 4, A, None) == SHAPE
 
 
 def test_validate_argument_checks(lib):

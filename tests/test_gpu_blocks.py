@@ -260,3 +260,30 @@ def test_copy_on_write_end_to_end(dev, combined):
     ref2 = O.decode(k_ref, v_ref, layer, host(q[1:]), tabs[:1], np.array([40], np.int32),
                     offs[:1], scale)
     assert max_abs_err(out[1:], ref2) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_read_blocks_checksum(dev, dtype):
+    """kv_read_blocks (the read-rate reference the bench times) folds the
+    layer slice of K and V of each listed block into the XOR of its 32-bit
+    words: compared bit for bit with the same fold on the host; ids outside
+    the pool give 0; V omitted reads K only."""
+    g = torch.Generator().manual_seed(77)
+    nb, nl, bs, h, d = 40, 3, 16, 4, 64
+    k = torch.randn((nb, nl, bs, h, d), generator=g).to(dtype).to(dev)
+    v = torch.randn((nb, nl, bs, h, d), generator=g).to(dtype).to(dev)
+    ids = torch.tensor([3, 0, 39, -1, 17, 40, 3, 22], dtype=torch.int32, device=dev)
+    layer = 2
+
+    def fold(t, b):
+        words = t[b, layer].contiguous().view(torch.int32).cpu().numpy().astype(np.uint32)
+        return int(np.bitwise_xor.reduce(words.ravel()))
+
+    got = N.kv_read_blocks(k, v, layer, ids).cpu().numpy().astype(np.uint32)
+    got_k = N.kv_read_blocks(k, None, layer, ids).cpu().numpy().astype(np.uint32)
+    for i, b in enumerate(ids.cpu().tolist()):
+        if 0 <= b < nb:
+            assert got[i] == fold(k, b) ^ fold(v, b), i
+            assert got_k[i] == fold(k, b), i
+        else:
+            assert got[i] == 0 and got_k[i] == 0, i
