@@ -12,18 +12,18 @@
 // bf16 kernel (matrix cores).  Workgroup = (kv head, sequence, query
 // tile), max(4, G) wavefronts; wavefront w handles query head kv*G + w % G and the
 // tile's (w / G)-th group of 48 (head_dim 128) or 64 (64) queries, in sub-tiles of 16 that are
-// its MFMA columns.  Per 16-position chunk of keys:
-//   the workgroup loads the chunk's K rows (registers, then a padded LDS
-//   tile) and V rows (straight into LDS) once for all its wavefronts, a ring
-//   of kPrefillRing chunks so all but one are in flight; one barrier per
-//   chunk; each
-//   wavefront reads the chunk's K and V operand fragments once, and for
-//   each of its sub-tiles does S^T = K . Q^T (v_mfma_f32_16x16x32_bf16),
+// its MFMA columns.  Keys go in stages of two 16-position chunks:
+//   the workgroup loads each chunk's K rows (registers, then a padded LDS
+//   tile) and V rows (straight into LDS) once for all its wavefronts, in a
+//   ring of two stages, one computed while the next one's loads are in
+//   flight, with one barrier per stage; for each of its sub-tiles a
+//   wavefront does S^T = K . Q^T for both chunks (v_mfma_f32_16x16x32_bf16),
 //   masks per element (outside the sequence, missing block, or key after
-//   the query), runs the online softmax per query column (lazy reference
-//   max, exp2 domain) and O += P . V (v_mfma_f32_16x16x16_bf16 with the
-//   transposing LDS read) -- the decode kernel's per-chunk step, with
-//   queries in place of heads.
+//   the query), and runs one online-softmax step per query column over the
+//   32 keys (lazy reference max, exp2 domain); then O += P . V with one
+//   v_mfma_f32_16x16x32_bf16 per sub-tile and 16 output columns, its V
+//   operand the two chunks' transposing LDS reads side by side -- the
+//   decode kernel's per-chunk step, with queries in place of heads.
 // fp32 kernel (VALU): one work item per (query row, group of kv heads), the
 //   decode VALU loop over the keys the query sees.
 #include "attn_common.h"
@@ -180,83 +180,111 @@ __global__ __launch_bounds__(64 * kPrefillWaves<G>) __attribute__((amdgpu_waves_
             // one's loads are in flight.  (A loop over more chunks per stage
             // spills: K passes through registers.)
             static_assert(NB == 4, "two stages of two chunks");
-            auto compute_chunk = [&](int64_t cpc, int qs) {
-                        // the chunk's K operand (A) and V operand (B) fragments,
-                        // read once and used by every sub-tile
-                        const char *kt = ktile[qs];
-                        const char *vt = vtile[qs];
-                        u32x4 kf[KS];
+            // One softmax step over the stage's two chunks, cpc (slot qs)
+            // and cpc + 16 (slot qs + 1).  Lane group g4 holds the scores of
+            // rows 4*g4 .. 4*g4+3 of each chunk; P.V contracts those 8 keys
+            // per lane group with one v_mfma_f32_16x16x32_bf16, whose P
+            // operand (A) and V operand (B) both list the first chunk's rows
+            // then the second's (the same relabelling of the 32 keys in
+            // both operands, so the sum is unchanged).
+            auto compute_stage = [&](int64_t cpc, int qs) {
+                const bool has1 = cpc + 16 <= last;   // wave-uniform
+                u32x4 kf[2][KS];
+#pragma unroll
+                for (int c = 0; c < 2; ++c)
+#pragma unroll
+                    for (int j = 0; j < KS; ++j)
+                        kf[c][j] = *reinterpret_cast<const u32x4 *>(ktile[qs + c] + cn * KROW + 16 * g4 + 64 * j);
+                // no mask needed in a chunk whose rows are all live tokens
+                // at or before the wavefront's first query (wave-uniform);
+                // rows of the second chunk past the piece are not live
+                bool full[2];
+                bool rok[2][4];
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    const int64_t pcc = cpc + 16 * c;
+                    bool f = nq > 0 && pcc >= lo && pcc + 16 <= phi && pcc + 15 - off <= pmin;
+                    if constexpr (UB) {
+                        f = f && bt_s[(int)((pcc >> lbs) - jb0)] >= 0;
+                    } else {
+                        f = false;   // rows may sit in different blocks
+                    }
+                    full[c] = f;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) rok[c][i] = !f && row_ok(pcc, 4 * g4 + i);
+                }
+                // row i of chunk c holds the key at logical position kp0 + 16 c + i
+                const int kp0 = (int)(cpc - off) + 4 * g4;
+                u32x4 pa[QT];
+#pragma unroll
+                for (int t = 0; t < QT; ++t) {
+                    // S^T: lane holds S[token 16 c + 4*g4 + i][query 16 t + cn]
+                    f32x4 sacc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+                    for (int j = 0; j < KS; ++j)
+                        sacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[0][j]), as_bf16x8(qf[t][j]),
+                                                                          sacc[0], 0, 0, 0);
+                    if (has1) {
 #pragma unroll
                         for (int j = 0; j < KS; ++j)
-                            kf[j] = *reinterpret_cast<const u32x4 *>(kt + cn * KROW + 16 * g4 + 64 * j);
-                        s16x4 vb[NV];
-                        {
-                            const int vrow = 4 * g4 + (cn >> 2);
-                            const int vbase = (vrow % NP) * VSLAB + (vrow / NP) * ROWB + 8 * (cn & 3);
+                            sacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[1][j]),
+                                                                              as_bf16x8(qf[t][j]), sacc[1], 0, 0, 0);
+                    }
+                    float s[8];
 #pragma unroll
-                            for (int sl = 0; sl < NV; ++sl)
-                                vb[sl] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                    (__attribute__((address_space(3))) s16x4 *)((__attribute__((address_space(3))) char *)(
-                                                                                   const_cast<char *>(vt)) +
-                                                                               vbase + 32 * sl));
+                    for (int c = 0; c < 2; ++c)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            s[4 * c + i] = (full[c] || (rok[c][i] && kp0 + 16 * c + i <= qpos[t]))
+                                               ? sacc[c][i] * sl2 : kNegInf;
+                    float cm = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])),
+                                     fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+                    cm = max_xor32(max_xor16(cm));
+                    float alpha = 1.0f;
+                    if (cm > m_h[t] + kLazy) {
+                        alpha = m_h[t] == kNegInf ? 0.0f : fast_exp2(m_h[t] - cm);
+                        m_h[t] = cm;
+                    }
+                    // exp2(-inf - m) = 0 for the masked entries; a column with
+                    // no live key so far (m = -inf) subtracts 0 instead
+                    const float mr = m_h[t] == kNegInf ? 0.0f : m_h[t];
+                    uint32_t pp[4];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k)
+                        pp[k] = pack_bf16x2(fast_exp2(s[2 * k] - mr), fast_exp2(s[2 * k + 1] - mr));
+                    l_h[t] = fmaf(l_h[t], alpha,
+                                  ((bf16_lo(pp[0]) + bf16_hi(pp[0])) + (bf16_lo(pp[1]) + bf16_hi(pp[1]))) +
+                                      ((bf16_lo(pp[2]) + bf16_hi(pp[2])) + (bf16_lo(pp[3]) + bf16_hi(pp[3]))));
+                    if (__builtin_amdgcn_readfirstlane((int)__any(alpha != 1.0f))) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const float al = __shfl(alpha, 4 * g4 + i);
+#pragma unroll
+                            for (int sl = 0; sl < NV; ++sl) acc[t][sl][i] *= al;
                         }
-                        // no mask needed: every row a live token at or before
-                        // the wavefront's first query (wave-uniform); the
-                        // selects below then keep every score
-                        bool full = nq > 0 && cpc >= lo && cpc + 16 <= phi && cpc + 15 - off <= pmin;
-                        if constexpr (UB) {
-                            full = full && bt_s[(int)((cpc >> lbs) - jb0)] >= 0;
-                        } else {
-                            full = false;   // rows may sit in different blocks
-                        }
-                        // masked chunks: row i of this lane is live and holds the
-                        // key at logical position kp0 + i
-                        const int kp0 = (int)(cpc - off) + 4 * g4;
-                        bool rok[4];
+                    }
+                    pa[t] = u32x4{pp[0], pp[1], pp[2], pp[3]};
+                }
+                // V operand of slice sl: the transposed 4-row fragments of
+                // both chunks, then every sub-tile
+                const int vrow = 4 * g4 + (cn >> 2);
+                const int vbase = (vrow % NP) * VSLAB + (vrow / NP) * ROWB + 8 * (cn & 3);
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) rok[i] = !full && row_ok(cpc, 4 * g4 + i);
-                        auto subtile = [&](int t) {
-                            // S^T: lane holds S[token 4*g4 + i][query 16 t + cn]
-                            f32x4 sacc = {0.0f, 0.0f, 0.0f, 0.0f};
+                for (int sl = 0; sl < NV; ++sl) {
+                    uint64_t vh2[2];
 #pragma unroll
-                            for (int j = 0; j < KS; ++j)
-                                sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[j]), as_bf16x8(qf[t][j]),
-                                                                               sacc, 0, 0, 0);
-                            float s[4];
+                    for (int c = 0; c < 2; ++c)
+                        vh2[c] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (__attribute__((address_space(3))) s16x4 *)((__attribute__((address_space(3))) char *)(
+                                                                           const_cast<char *>(vtile[qs + c])) +
+                                                                       vbase + 32 * sl)));
+                    const u32x4 vb = {(uint32_t)vh2[0], (uint32_t)(vh2[0] >> 32), (uint32_t)vh2[1],
+                                      (uint32_t)(vh2[1] >> 32)};
 #pragma unroll
-                            for (int i = 0; i < 4; ++i)
-                                s[i] = (full || (rok[i] && kp0 + i <= qpos[t])) ? sacc[i] * sl2 : kNegInf;
-                            float cm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-                            cm = max_xor32(max_xor16(cm));
-                            float alpha = 1.0f;
-                            if (cm > m_h[t] + kLazy) {
-                                alpha = m_h[t] == kNegInf ? 0.0f : fast_exp2(m_h[t] - cm);
-                                m_h[t] = cm;
-                            }
-                            // exp2(-inf - m) = 0 for the masked entries; a column with
-                            // no live key so far (m = -inf) subtracts 0 instead
-                            const float mr = m_h[t] == kNegInf ? 0.0f : m_h[t];
-                            float pr[4];
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(s[i] - mr);
-                            const uint32_t p01 = pack_bf16x2(pr[0], pr[1]);
-                            const uint32_t p23 = pack_bf16x2(pr[2], pr[3]);
-                            l_h[t] = fmaf(l_h[t], alpha, (bf16_lo(p01) + bf16_hi(p01)) + (bf16_lo(p23) + bf16_hi(p23)));
-                            if (__builtin_amdgcn_readfirstlane((int)__any(alpha != 1.0f))) {
-#pragma unroll
-                                for (int i = 0; i < 4; ++i) {
-                                    const float al = __shfl(alpha, 4 * g4 + i);
-#pragma unroll
-                                    for (int sl = 0; sl < NV; ++sl) acc[t][sl][i] *= al;
-                                }
-                            }
-                            const s16x4 pa = __builtin_bit_cast(s16x4, (uint64_t)p01 | ((uint64_t)p23 << 32));
-#pragma unroll
-                            for (int sl = 0; sl < NV; ++sl)
-                                acc[t][sl] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb[sl], acc[t][sl], 0, 0, 0);
-                        };
-#pragma unroll
-                        for (int t = 0; t < QT; ++t) subtile(t);
+                    for (int t = 0; t < QT; ++t)
+                        acc[t][sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(pa[t]), as_bf16x8(vb),
+                                                                             acc[t][sl], 0, 0, 0);
+                }
             };
             u32x4 kring[NB][LPW];
             load_chunk(min(first, last), kring[0], 0);
@@ -289,8 +317,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves<G>) __attribute__((amdgpu_waves_
                         __syncthreads();  // the stage's tiles complete; the other stage's slots free
                         load_chunk(min(pc + 32, last), kring[2 - 2 * st], 2 - 2 * st);
                         load_chunk(min(pc + 48, last), kring[3 - 2 * st], 3 - 2 * st);
-                        compute_chunk(pc, 2 * st);
-                        if (pc + 16 <= last) compute_chunk(pc + 16, 2 * st + 1);
+                        compute_stage(pc, 2 * st);
                         pc += 32;
                         done = pc > last;
                     }
