@@ -318,11 +318,11 @@ PKV_API size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_kv
  *                 in a fixed order; the partition depends only on the
  *                 sizes, the lengths and offsets, and the device's
  *                 compute-unit count, so results are bitwise reproducible
- *                 run to run.  In the planned schedule a sequence longer
- *                 than max_seq_len is attended over its first max_seq_len
- *                 tokens and an offset outside [0, block_size) is clamped
- *                 into it (both break the contract; no access leaves the
- *                 buffers).
+ *                 run to run.  A sequence longer than max_seq_len is
+ *                 attended over its first max_seq_len tokens and an offset
+ *                 outside [0, block_size) is clamped into it, in every
+ *                 schedule (both break the contract; no access leaves the
+ *                 buffers, and the workspace stays reusable).
  *   out           device [num_seqs, num_q_heads, head_dim], pool dtype
  *   workspace     device scratch of at least
  *                 paged_attn_decode_workspace_size(...) bytes (may be NULL
@@ -361,7 +361,9 @@ PKV_API int paged_attn_decode(const pkv_pool *pool, int32_t layer,
  * writes them [P1 "relation to step14_1" scatter]; out is then what
  * paged_attn_decode computes over tokens 0 .. seq_lens[s]-1 of the updated
  * pool.  A table entry of -1 at that position writes nothing (the
- * position is masked, as in decode).  The write happens inside the
+ * position is masked, as in decode), and neither does a sequence whose
+ * length or offset breaks the contract (seq_lens[s] > max_seq_len, offset
+ * outside [0, block_size)): it is attended as paged_attn_decode clamps it.  The write happens inside the
  * attention kernel, by the work item whose range ends the sequence, before
  * it reads that row; no other work item reads it.
  *

@@ -100,15 +100,32 @@ __device__ __forceinline__ Item work_item(const DecodeArgs &a) {
 }
 
 // Flat-position range [lo, hi) of split j: [j*S, (j+1)*S) n [off, off+L).
+// `whole` is false when the caller's length or offset broke the contract
+// (length above max_seq_len, offset outside [0, block_size)) and was clamped.
 struct Range {
     int64_t lo, hi, off, len;
+    bool whole;
 };
+
+// A sequence's length clamped to [0, max_seq_len] and its offset to
+// [0, block_size): the grid and the workspace are sized from max_seq_len,
+// so every split index and merge count stays inside them whatever the
+// device-resident values hold.
+__device__ __forceinline__ void clamp_len_off(const DecodeArgs &a, int64_t &L, int64_t &off, bool &whole) {
+    const int64_t bsm = (1ll << a.pool.lbs) - 1;
+    const int64_t L0 = L, o0 = off;
+    L = L < 0 ? 0 : (L > a.max_len ? (int64_t)a.max_len : L);
+    off = off < 0 ? 0 : (off > bsm ? bsm : off);
+    whole = L == L0 && off == o0;
+}
 
 __device__ __forceinline__ Range split_range(const DecodeArgs &a, int seq, int split) {
     Range R;
-    const int64_t L = a.seq_lens[seq];
+    int64_t L = a.seq_lens[seq];
+    int64_t off = a.offsets[seq];
+    clamp_len_off(a, L, off, R.whole);
     R.len = L;
-    R.off = a.offsets[seq];
+    R.off = off;
     const int64_t S = a.split_tokens;
     R.lo = max((int64_t)split * S, R.off);
     R.hi = min((int64_t)(split + 1) * S, R.off + L);
@@ -268,7 +285,7 @@ __device__ __forceinline__ int32_t wave_total(int32_t v) {
 }
 
 struct PlanOut {
-    int32_t seq, g, j, len, off, S, have;
+    int32_t seq, g, j, len, off, S, have, whole;
 };
 
 // Sets it, R and S of this workgroup; false if it has no piece.  Uses
@@ -290,8 +307,10 @@ __device__ bool plan_item(const DecodeArgs &a, int32_t *scratch, Item &it, Range
         const bool live = lane < n;
         int32_t L = live ? a.seq_lens[lane] : 0;
         int32_t O = live ? a.offsets[lane] : 0;
+        const int32_t L0 = L, O0 = O;
         L = L < 0 ? 0 : (L > a.max_len ? a.max_len : L);
         O = O < 0 ? 0 : (O > bsm ? bsm : O);
+        const int32_t whole = L == L0 && O == O0;
         if (live) scratch[lane] = L;
         // total length: below 64 * 2^24 < 2^31 (the float value's rounding is
         // within the bounds' margins)
@@ -335,7 +354,7 @@ __device__ bool plan_item(const DecodeArgs &a, int32_t *scratch, Item &it, Range
         const int32_t sf = wave_incl_scan(P.nf), sq = wave_incl_scan(P.nq);
         const int32_t Fs = __builtin_amdgcn_readlane(sf, 63), Qs = __builtin_amdgcn_readlane(sq, 63);
         const int32_t b = blockIdx.x;
-        PlanOut r{0, 0, 0, 0, 0, S, 0};
+        PlanOut r{0, 0, 0, 0, 0, S, 0, 1};
         const bool full = b < HG * Fs;
         if (full || b >= nwg - HG * Qs) {
             const int32_t tot_p = full ? Fs : Qs;
@@ -357,6 +376,7 @@ __device__ bool plan_item(const DecodeArgs &a, int32_t *scratch, Item &it, Range
             r.j = full ? jf0 + (k - base) : ((k == base && !(nf > 0 && jf0 == j0)) ? j0 : j1);
             r.len = __builtin_amdgcn_readlane(L, ln);
             r.off = __builtin_amdgcn_readlane(O, ln);
+            r.whole = __builtin_amdgcn_readlane(whole, ln);
             r.have = 1;
         }
         if (lane == 0) po = r;
@@ -373,6 +393,7 @@ __device__ bool plan_item(const DecodeArgs &a, int32_t *scratch, Item &it, Range
         it.split = r.j;
         R.len = r.len;
         R.off = r.off;
+        R.whole = r.whole != 0;
         R.lo = max((int64_t)r.j * r.S, R.off);
         R.hi = min((int64_t)(r.j + 1) * r.S, R.off + R.len);
     }
@@ -635,7 +656,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
     // Decode with append: the work item that ends the sequence first writes
     // the new token's K/V row (logical position len - 1); each piece is
     // stored by the lane whose load below reads it back.
-    if (a.k_new != nullptr && R.len > 0 && R.hi == R.off + R.len) {
+    if (a.k_new != nullptr && R.whole && R.len > 0 && R.hi == R.off + R.len) {
         const int64_t pn = R.hi - 1;
         if (r == (int)((pn - R.lo) % kChunkTokens) % RPI) {
             const int32_t b = bt_s[(int)((pn >> lbs) - jb0)];
@@ -935,7 +956,9 @@ __device__ __forceinline__ void attend_range(const DecodeArgs &a, int seq, const
         // so the load sees it.  The new rows are fetched before the ring's
         // first loads; the store waits only for them, and goes after the
         // first loads unless those already cover chunk `last`.
-        const bool app = a.k_new != nullptr && R.len > 0 && R.hi == R.off + R.len;
+        // (not when the length or offset was clamped: the write would land on
+        // another token's slot)
+        const bool app = a.k_new != nullptr && R.whole && R.len > 0 && R.hi == R.off + R.len;
         const int64_t pn = R.hi - 1;
         const int rn = (int)(pn & 15);               // the new row within its chunk
         const bool k_lane = app && n == rn;          // loads K pieces 4 j + g4 of that row
@@ -1439,6 +1462,7 @@ struct RoundLds {
     int64_t lo[kSegMax], hi[kSegMax];  // flat positions of the segment's tokens
     int64_t ps[kSegMax], pe[kSegMax];  // the pair's unit range
     int32_t seq[kSegMax], hg[kSegMax];
+    int32_t whole[kSegMax];            // the sequence's length and offset were not clamped
     int32_t base[kSegMax + 1];         // first bt_s entry of each segment; base[n] = total
     int32_t step[kSegMax + 1];         // first ring step of each segment; step[n] = total
     int32_t n;                         // segments in the round
@@ -1550,7 +1574,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeArgs a) {
         // arithmetic here runs once per workgroup; it is kept short (no
         // 64-bit divisions, PER sequences per thread) because every
         // instruction of it delays the first K/V load.
-        int32_t ln[PER], of[PER];
+        int32_t ln[PER], of[PER], wh[PER];
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int sq = t * PER + i;
@@ -1560,6 +1584,15 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeArgs a) {
                 ln[i] = a.seq_lens[sq];
                 of[i] = a.offsets[sq];
             }
+        }
+        // lengths clamped to max_seq_len and offsets into [0, block_size):
+        // the host sized the grid so every share fits for those
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int32_t l0 = ln[i], o0 = of[i];
+            ln[i] = l0 < 0 ? 0 : (l0 > a.max_len ? a.max_len : l0);
+            of[i] = o0 < 0 ? 0 : (o0 > (int32_t)bsm ? (int32_t)bsm : o0);
+            wh[i] = ln[i] == l0 && of[i] == o0;
         }
         int64_t cn[PER];
         int64_t mc = 0, mnz = 0;
@@ -1655,6 +1688,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeArgs a) {
                                 R.pe[idx] = pe;
                                 R.lo[idx] = of[i];  // offset and length for now
                                 R.hi[idx] = ln[i];
+                                R.whole[idx] = wh[i];
                                 atomicAdd(&R.n, 1);
                             }
                         }
@@ -1754,7 +1788,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeArgs a) {
                 __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xF << 8));
                 wave_lds_order();
                 for (int i = b0; i < min(nseg, b0 + SBATCH); ++i) {
-                    if (R.pe[i] <= r1) {
+                    if (R.pe[i] <= r1 && R.whole[i]) {
                         const int64_t pn = R.hi[i] - 1;
                         const int bi = R.base[i] + (int)((pn >> lbs) - (R.lo[i] >> lbs));
                         const int32_t b = bi < kBtLds ? bt_s[bi] : -1;
@@ -2020,8 +2054,10 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(DecodeArgs a) {
     // acc values (splits grp, grp + NG, ...), all loaded before any is
     // used.  Records of empty splits hold stale values; they are loaded
     // (the workspace holds every split) and get weight 0.
-    const int64_t L = a.seq_lens[seq];
-    const int64_t off = a.offsets[seq];
+    int64_t L = a.seq_lens[seq];
+    int64_t off = a.offsets[seq];
+    bool whole;
+    clamp_len_off(a, L, off, whole);
     float2 ml0 = make_float2(kNegInf, 0.0f);
     if (t < ns) ml0 = *reinterpret_cast<const float2 *>(a.ws_ml + (item0 + t * step) * 2);
     float x0[U];

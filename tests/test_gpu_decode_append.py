@@ -172,3 +172,76 @@ def test_decode_append_full_size_decode_batch(dev):
     ref = O.decode(k_c, v_c, 0, host(w.q), bt_c, lens, host(w.offsets), w.scale,
                    num_threads=oracle_threads())
     assert max_abs_err(got, ref) <= TOL[w.dtype]
+
+
+def oracle_partial_step(w, kn, vn, lens_attend, write):
+    """Oracle pool after writing the new rows of the sequences in `write`
+    (slot mapping + scatter), and its decode over lens_attend tokens."""
+    k = host(w.k_pool).copy()
+    v = host(w.v_pool).copy()
+    lens = host(w.seq_lens)
+    live = np.array([s for s in range(w.num_seqs) if lens[s] > 0 and write[s]], np.int32)
+    if live.size:
+        slots = O.slot_mapping(host(w.block_tables), host(w.offsets), live,
+                               (lens[live] - 1).astype(np.int32), w.block_size)
+        O.scatter(k, w.layer, host(kn)[live], slots)
+        O.scatter(v, w.layer, host(vn)[live], slots)
+    out = O.decode(k, v, w.layer, host(w.q), host(w.block_tables),
+                   np.asarray(lens_attend, np.int32), host(w.offsets), w.scale,
+                   num_threads=oracle_threads())
+    return k, v, out
+
+
+STALE_CASES = [(torch.bfloat16, 0), (torch.bfloat16, 64), (torch.bfloat16, 16),
+               (torch.bfloat16, N.SPLIT_BALANCED), (torch.bfloat16, N.SPLIT_PLANNED),
+               (torch.float32, 64), (torch.float32, 0)]
+
+
+@pytest.mark.parametrize("dtype,split", STALE_CASES)
+def test_stale_max_seq_len_then_correct_call(dev, dtype, split):
+    """A caller's max_seq_len one below the longest sequence breaks the
+    contract: that sequence is attended over its first max_seq_len tokens
+    and its new row is not written (it would land on a cached token's slot
+    under the clamped length), every other sequence is computed exactly,
+    and the workspace is left reusable -- a correct call on the same
+    workspace afterwards matches the oracle.  Sequence 0 has offset 15 and
+    690 tokens, so at 64-token splits its last split index is one past the
+    splits a 689-token bound provides."""
+    nb = 6 * 46 + 64
+    w = W.decode_batch(device=dev, seed=340, num_seqs=6, min_len=690, max_len=690, num_blocks=nb,
+                       num_layers=3, num_kv_heads=2, head_dim=128, num_q_heads=8, dtype=dtype,
+                       layer=1, offsets=[15, 3, 0, 7, 15, 9])
+    lens = host(w.seq_lens).copy()
+    lens[1:] = [689, 300, 17, 512, 641]
+    w.seq_lens = torch.from_numpy(lens).to(dev)
+    w = W.decode_tokens(w)
+    kn, vn = new_rows_for_all(w)
+    mx = int(lens.max())
+    need = N.paged_attn_decode_workspace_size(w.num_seqs, w.num_kv_heads, w.num_q_heads,
+                                              w.head_dim, mx, w.block_size, split)
+    ws = torch.zeros(max(need, 16), dtype=torch.uint8, device=dev)
+    k0, v0 = w.k_pool.clone(), w.v_pool.clone()
+
+    clamp = np.minimum(lens, mx - 1)
+    k_ref, v_ref, ref = oracle_partial_step(w, kn, vn, clamp, lens <= mx - 1)
+    out = torch.full_like(w.q, float("nan"))
+    N.paged_attn_decode_append(w.k_pool, w.v_pool, w.layer, w.q, kn, vn, w.block_tables,
+                               w.seq_lens, w.offsets, mx - 1, w.scale, split_tokens=split,
+                               out=out, workspace=ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(host(w.k_pool)), bits(k_ref))
+    assert np.array_equal(bits(host(w.v_pool)), bits(v_ref))
+    assert max_abs_err(out, ref) <= TOL[dtype]
+
+    # the correct call, same workspace, from the original pool
+    w.k_pool.copy_(k0)
+    w.v_pool.copy_(v0)
+    k_ref, v_ref, ref = oracle_step(w, kn, vn)
+    out = torch.full_like(w.q, float("nan"))
+    N.paged_attn_decode_append(w.k_pool, w.v_pool, w.layer, w.q, kn, vn, w.block_tables,
+                               w.seq_lens, w.offsets, mx, w.scale, split_tokens=split, out=out,
+                               workspace=ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(host(w.k_pool)), bits(k_ref))
+    assert np.array_equal(bits(host(w.v_pool)), bits(v_ref))
+    assert max_abs_err(out, ref) <= TOL[dtype]
