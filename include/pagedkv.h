@@ -76,6 +76,8 @@ enum {
     PKV_ERR_SEQ = -10,        /* block manager: unknown or duplicate sequence  */
     PKV_ERR_BLOCK = -11,      /* block manager: block id out of range or free  */
     PKV_ERR_HOST = -12,       /* host memory could not be allocated            */
+    PKV_ERR_SCRATCH = -13,    /* paged_attn_decode_noalloc: the sizes need     */
+                              /* more than PKV_NOALLOC_SCRATCH_BYTES           */
     PKV_NO_SPACE = 1          /* block manager: too few free blocks; nothing   */
                               /* was changed (not an error)                    */
 };
@@ -346,6 +348,43 @@ PKV_API int paged_attn_decode(const pkv_pool *pool, int32_t layer,
                               int32_t split_tokens, void *out,
                               void *workspace, size_t workspace_bytes,
                               void *stream);
+
+/* Bytes of the fixed per-device scratch of paged_attn_decode_noalloc. */
+#define PKV_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/*
+ * paged_attn_decode_noalloc -- paged_attn_decode without a workspace
+ * argument, for callers that cannot allocate device memory around a call:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  It allocates nothing (no hipMalloc / hipFree, no allocating
+ * library routine).
+ *
+ * The split partials and merge counters live in a fixed array of
+ * PKV_NOALLOC_SCRATCH_BYTES (32 MiB) of device memory inside the library;
+ * every device the library runs on holds its own copy until the process
+ * ends (its address is looked up once per device, on that device's first
+ * call).  Each call first clears the merge counters it uses (a small fill
+ * kernel on `stream`, not a memset), then runs exactly the kernels and
+ * schedule paged_attn_decode runs for the same arguments: the output is
+ * bitwise the output of paged_attn_decode with a workspace.
+ *
+ * Every call on a device shares that device's array, which keeps the last
+ * call's contents: calls that overlap on one device (issued on different
+ * streams, or from several threads without ordering) race on it and may
+ * return wrong results.  Issue them on one stream.
+ *
+ * Arguments: as paged_attn_decode, without workspace / workspace_bytes.
+ * Errors: as paged_attn_decode; PKV_ERR_SCRATCH (nothing enqueued) when
+ * paged_attn_decode_workspace_size(...) for these sizes and split_tokens
+ * exceeds PKV_NOALLOC_SCRATCH_BYTES; PKV_ERR_DEVICE when the array's device
+ * address cannot be looked up on the current device.
+ */
+PKV_API int paged_attn_decode_noalloc(const pkv_pool *pool, int32_t layer,
+                                      const void *q, int32_t num_q_heads,
+                                      const int32_t *block_tables, int32_t bt_stride,
+                                      const int32_t *seq_lens, const int32_t *offsets,
+                                      int32_t num_seqs, int32_t max_seq_len, float scale,
+                                      int32_t split_tokens, void *out, void *stream);
 
 /*
  * paged_attn_decode_append -- one whole decode step in one launch: each

@@ -602,6 +602,23 @@ __global__ __launch_bounds__(256) void validate_kernel(ValidateArgs a) {
     if (bad) atomicAdd(a.count, bad);
 }
 
+// Clears n 32-bit words (counters that a kernel expects to start at zero);
+// a fill kernel rather than hipMemsetAsync, so a captured graph holds no
+// memset node.
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t *p, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0u;
+}
+
+hipError_t launch_zero_words(uint32_t *p, int64_t n, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 1024) blocks = 1024;
+    hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n);
+    return hipGetLastError();
+}
+
 hipError_t launch_validate(const ValidateArgs &a, hipStream_t s) {
     hipLaunchKernelGGL(zero_u64_kernel, dim3(1), dim3(64), 0, s, a.count);
     hipError_t e = hipGetLastError();

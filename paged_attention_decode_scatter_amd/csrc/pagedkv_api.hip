@@ -3,6 +3,7 @@
 // Every check runs before the first HIP call, so a rejected call enqueues
 // nothing and needs no device.
 #include <atomic>
+#include <mutex>
 #include <stdint.h>
 
 #include "pagedkv.h"
@@ -591,11 +592,14 @@ PKV_API int32_t paged_attn_decode_schedule(int32_t num_seqs, int32_t num_kv_head
 namespace {
 
 // paged_attn_decode, and paged_attn_decode_append when k_new is given.
+// clear_cnt: zero the workspace's merge counters (a fill kernel on the
+// stream) before the decode, for a workspace whose earlier contents are not
+// known to be clean.
 int decode_impl(const pkv_pool *pool, int32_t layer, const void *q, int32_t num_q_heads,
                 const void *k_new, const void *v_new, const int32_t *block_tables, int32_t bt_stride,
                 const int32_t *seq_lens, const int32_t *offsets, int32_t num_seqs,
                 int32_t max_seq_len, float scale, int32_t split_tokens, void *out,
-                void *workspace, size_t workspace_bytes, void *stream) {
+                void *workspace, size_t workspace_bytes, void *stream, bool clear_cnt = false) {
     int st = check_pool(pool, true);
     if (st) return st;
     if (layer < 0 || layer >= pool->num_layers) return PKV_ERR_LAYER;
@@ -670,8 +674,46 @@ int decode_impl(const pkv_pool *pool, int32_t layer, const void *q, int32_t num_
     a.seg_chunks = (int32_t)(max_split_tokens(pool->block_size) / kChunkTokens);
     a.plan = planned ? (int32_t)spl.wgs : 0;
     a.max_len = max_seq_len;
+    if (clear_cnt && ws && cnt_bytes > 0) {
+        const hipError_t e = launch_zero_words(a.ws_cnt, cnt_bytes / 4, static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return status_of(e);
+    }
     return status_of(launch_decode(a, pool->dtype, (int)pool->head_dim, group,
                                    static_cast<hipStream_t>(stream)));
+}
+
+// The fixed device scratch of paged_attn_decode_noalloc: the split
+// partials and merge counters of every call on a device live here (each
+// device holds its own copy for the life of the process; zero when the
+// code object is loaded).  Host code never passes the array's name to a
+// kernel: its device address is looked up once per device below.
+static __device__ __align__(256) unsigned char scratch[PKV_NOALLOC_SCRATCH_BYTES];
+
+// Device address of `scratch` on the current device, looked up with that
+// device current on the first call and kept per device; nullptr if the
+// lookup fails.
+char *scratch_ptr() {
+    constexpr int kMaxDev = 64;
+    static std::atomic<char *> cache[kMaxDev];
+    static std::mutex mu;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    char *p = cache[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    std::lock_guard<std::mutex> lock(mu);
+    p = cache[dev].load(std::memory_order_relaxed);
+    if (p) return p;
+    void *addr = nullptr;
+    if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || !addr) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    p = static_cast<char *>(addr);
+    cache[dev].store(p, std::memory_order_release);
+    return p;
 }
 
 }  // namespace
@@ -686,6 +728,30 @@ PKV_API int paged_attn_decode(const pkv_pool *pool, int32_t layer, const void *q
     return decode_impl(pool, layer, q, num_q_heads, nullptr, nullptr, block_tables, bt_stride,
                        seq_lens, offsets, num_seqs, max_seq_len, scale, split_tokens, out, workspace,
                        workspace_bytes, stream);
+}
+
+PKV_API int paged_attn_decode_noalloc(const pkv_pool *pool, int32_t layer, const void *q,
+                                      int32_t num_q_heads, const int32_t *block_tables,
+                                      int32_t bt_stride, const int32_t *seq_lens,
+                                      const int32_t *offsets, int32_t num_seqs, int32_t max_seq_len,
+                                      float scale, int32_t split_tokens, void *out, void *stream) {
+    int st = check_pool(pool, true);
+    if (st) return st;
+    if (num_seqs < 0 || max_seq_len < 0 || num_q_heads <= 0 || num_q_heads % pool->num_kv_heads)
+        return PKV_ERR_SHAPE;
+    const size_t need = paged_attn_decode_workspace_size(
+        num_seqs, (int32_t)pool->num_kv_heads, num_q_heads, (int32_t)pool->head_dim, max_seq_len,
+        (int32_t)pool->block_size, split_tokens);
+    if (need == (size_t)-1) return PKV_ERR_SHAPE;
+    if (need > (size_t)PKV_NOALLOC_SCRATCH_BYTES) return PKV_ERR_SCRATCH;
+    char *ws = nullptr;
+    if (need > 0 && num_seqs > 0) {
+        ws = scratch_ptr();
+        if (!ws) return PKV_ERR_DEVICE;
+    }
+    return decode_impl(pool, layer, q, num_q_heads, nullptr, nullptr, block_tables, bt_stride,
+                       seq_lens, offsets, num_seqs, max_seq_len, scale, split_tokens, out, ws,
+                       ws ? (size_t)PKV_NOALLOC_SCRATCH_BYTES : 0, stream, /*clear_cnt=*/true);
 }
 
 PKV_API int paged_attn_decode_append(const pkv_pool *pool, int32_t layer, const void *q,
@@ -906,6 +972,9 @@ PKV_API const char *pkv_status_string(int status) {
         case PKV_ERR_SEQ: return "unknown or duplicate sequence id";
         case PKV_ERR_BLOCK: return "block id out of range or free";
         case PKV_ERR_HOST: return "host memory could not be allocated";
+        case PKV_ERR_SCRATCH:
+            return "the decode workspace these sizes need exceeds the fixed device scratch "
+                   "(PKV_NOALLOC_SCRATCH_BYTES)";
         case PKV_NO_SPACE: return "too few free blocks (nothing changed)";
         default: return "unknown status";
     }

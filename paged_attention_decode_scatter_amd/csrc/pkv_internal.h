@@ -275,6 +275,7 @@ hipError_t launch_scatter_q8(const ScatterQ8Args &a, hipStream_t s);
 hipError_t launch_gather_q8(const GatherArgs &a, int head_dim, hipStream_t s);
 hipError_t launch_validate(const ValidateArgs &a, hipStream_t s);
 hipError_t launch_read_blocks(const ReadBlocksArgs &a, hipStream_t s);
+hipError_t launch_zero_words(uint32_t *p, int64_t n, hipStream_t s);
 // Returns hipErrorInvalidValue when (dtype, head_dim, group) is not built.
 hipError_t launch_decode(const DecodeArgs &a, int dtype, int head_dim, int group,
                          hipStream_t s);

@@ -30,6 +30,7 @@ SYMBOLS = (
     "paged_attn_decode_schedule",
     "paged_attn_decode_workspace_size",
     "paged_attn_decode",
+    "paged_attn_decode_noalloc",
     "paged_attn_decode_append",
     "paged_attn_prefill",
     "kv_copy_blocks",
@@ -111,6 +112,9 @@ def load_library(path: str = LIB_PATH):
     lib.paged_attn_decode.restype = ctypes.c_int
     lib.paged_attn_decode.argtypes = [pp, i32, p, i32, p, i32, p, p, i32, i32, f32, i32, p, p,
                                       sz, p]
+    lib.paged_attn_decode_noalloc.restype = ctypes.c_int
+    lib.paged_attn_decode_noalloc.argtypes = [pp, i32, p, i32, p, i32, p, p, i32, i32, f32, i32, p,
+                                              p]
     lib.kv_copy_blocks.restype = ctypes.c_int
     lib.kv_copy_blocks.argtypes = [pp, p, p, i64, p]
     lib.kv_read_blocks.restype = ctypes.c_int
@@ -379,6 +383,31 @@ def paged_attn_decode(k_pool, v_pool, layer, q, block_tables, seq_lens, offsets,
         _ptr(seq_lens), _ptr(offsets), num_seqs, int(max_seq_len), float(scale), split_tokens,
         _ptr(out), _ptr(workspace), ws_bytes, _stream(q))
     _check("paged_attn_decode", st)
+    return out
+
+
+# bytes of the library's fixed per-device scratch (paged_attn_decode_noalloc)
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def paged_attn_decode_noalloc(k_pool, v_pool, layer, q, block_tables, seq_lens, offsets,
+                              max_seq_len, scale, split_tokens=0, out=None):
+    """paged_attn_decode with the library's fixed device scratch as its
+    workspace: the call allocates nothing (pass `out` to keep it so here
+    too).  Calls that overlap on one device race on the scratch."""
+    pool = make_pool(k_pool, v_pool)
+    _need(q, _row_dtype(k_pool), "q")
+    for t, n in ((block_tables, "block_tables"), (seq_lens, "seq_lens"), (offsets, "offsets")):
+        _need(t, torch.int32, n)
+    num_seqs, hq, d = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, _row_dtype(k_pool), "out")
+    st = load_library().paged_attn_decode_noalloc(
+        ctypes.byref(pool), layer, _ptr(q), hq, _ptr(block_tables), block_tables.shape[1],
+        _ptr(seq_lens), _ptr(offsets), num_seqs, int(max_seq_len), float(scale), split_tokens,
+        _ptr(out), _stream(q))
+    _check("paged_attn_decode_noalloc", st)
     return out
 
 

@@ -33,7 +33,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == len(set(names)) == 33
+    assert len(names) == len(set(names)) == 34
     assert set(names) == set(N.SYMBOLS) | set(N.BM_SYMBOLS)
     for n in names:
         assert hasattr(lib, n), n
@@ -140,6 +140,28 @@ def test_decode_argument_checks(lib):
     assert call(split=16, ws=None, wsb=0) == WORKSPACE
     assert call(split=16, wsb=need - 1) == WORKSPACE
     assert call(split=16, ws=A + 4, wsb=need) == ALIGN
+
+
+def test_decode_noalloc_argument_checks(lib):
+    """Rejections that come before the scratch lookup (so no GPU is
+    touched): pool and shape checks, and sizes whose workspace would not fit
+    the fixed scratch."""
+    f = lib.paged_attn_decode_noalloc
+    by = ctypes.byref
+    SCRATCH = -13
+
+    def call(p=None, hq=32, ns=4, mx=100, split=0, q=A, out=A, layer=0):
+        return f(by(p or pool()), layer, q, hq, A, 8, A, A, ns, mx, 0.1, split, out, None)
+
+    assert f(None, 0, A, 32, A, 8, A, A, 4, 100, 0.1, 0, A, None) == NULL
+    assert call(hq=30) == SHAPE
+    assert call(split=24) == SHAPE
+    assert call(ns=-1) == SHAPE
+    # 64 sequences of 32768 tokens at 16-token splits: far beyond 32 MiB
+    need = lib.paged_attn_decode_workspace_size(64, 8, 64, 128, 32768, 16, 16)
+    assert need > N.NOALLOC_SCRATCH_BYTES
+    assert call(p=pool(nb=16384), hq=64, ns=64, mx=32768, split=16) == SCRATCH
+    assert "scratch" in N.status_string(SCRATCH)
 
 
 def test_decode_append_argument_checks(lib):
