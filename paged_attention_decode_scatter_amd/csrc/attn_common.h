@@ -170,6 +170,29 @@ __device__ __forceinline__ void lds_copy16(const char *src, char *lds_wave_base)
                                      (__attribute__((address_space(3))) void *)lds_wave_base, 16, 0, 0);
 }
 
+// Nontemporal reads (global_load ... nt) of pool bytes that one call reads
+// once.  Measured on MI355X (same process, decode_mfma / decode_q8 kernels,
+// microseconds without -> with the hint):
+//   bf16 V, global -> LDS (lds_copy16_nt): decode batch 42.5 -> 40.5,
+//     prefix sharing 96.6 -> 95.0, long context 192.2 -> 168.9;
+//   bf16 K, global -> registers: prefix sharing 96.6 -> 110.9 (the prefix
+//     that 64 sequences share is re-fetched), long context 192.2 -> 174.7;
+//     so bf16 K loads stay ordinary;
+//   int8 codes and scales (ld16_nt): decode batch 30.8 -> 29.4, long
+//     context 112.1 -> 102.8, prefix sharing level (66.8 / 67.4).
+// A plain 1 GiB read in 64 KiB pieces per workgroup moves 5.85 TB/s with
+// ordinary loads and 6.65 TB/s with the hint.
+__device__ __forceinline__ u32x4 ld16_nt(const char *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
+
+// lds_copy16 with the nontemporal hint.
+__device__ __forceinline__ void lds_copy16_nt(const char *src, char *lds_wave_base) {
+    __builtin_amdgcn_global_load_lds(const_cast<char *>(src),
+                                     (__attribute__((address_space(3))) void *)lds_wave_base, 16, 0,
+                                     2 /* nt */);
+}
+
 // Keep the compiler from moving LDS accesses across this point; the LDS
 // unit itself serves one wavefront's requests in order.
 __device__ __forceinline__ void wave_lds_order() {

@@ -429,7 +429,7 @@ __global__ __launch_bounds__(kCopyThreads) void gather_q8_kernel(GatherArgs a) {
             if (!okb) break;
             const char *pool = tsr ? a.pool.v : a.pool.k;
             const float *sc = tsr ? a.pool.vs : a.pool.ks;
-            const u32x4 c = ld16(pool + (int64_t)b * a.pool.block_stride + a.pool.layer_off +
+            const u32x4 c = ld16_stream(pool + (int64_t)b * a.pool.block_stride + a.pool.layer_off +
                                  (p & bsm) * a.pool.row_bytes + 16 * ch);
             const float s = sc[(int64_t)b * a.pool.sc_block + (h << a.pool.lbs) + (p & bsm)];
             const uint32_t w[4] = {c.x, c.y, c.z, c.w};
@@ -536,8 +536,8 @@ __global__ __launch_bounds__(kCopyThreads) void read_blocks_kernel(ReadBlocksArg
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
                 const int i = i0 + u * kCopyThreads;
-                kk[u] = i < n16 ? ld16(k + ((int64_t)i << 4)) : u32x4{0, 0, 0, 0};
-                vv[u] = (v && i < n16) ? ld16(v + ((int64_t)i << 4)) : u32x4{0, 0, 0, 0};
+                kk[u] = i < n16 ? ld16_stream(k + ((int64_t)i << 4)) : u32x4{0, 0, 0, 0};
+                vv[u] = (v && i < n16) ? ld16_stream(v + ((int64_t)i << 4)) : u32x4{0, 0, 0, 0};
             }
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) x ^= kk[u].x ^ kk[u].y ^ kk[u].z ^ kk[u].w ^

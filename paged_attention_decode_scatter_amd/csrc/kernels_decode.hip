@@ -847,7 +847,7 @@ __device__ __forceinline__ void attend_range(const DecodeArgs &a, int seq, const
             for (int j = 0; j < KS; ++j) kx[j] = ld16(kb + 64 * j);
 #pragma unroll
             for (int i = 0; i < NP; ++i)
-                lds_copy16(vb + (uint32_t)((i + NP * trow) * row_bytes + 16 * tpp), dst + i * VSLAB);
+                lds_copy16_nt(vb + (uint32_t)((i + NP * trow) * row_bytes + 16 * tpp), dst + i * VSLAB);
         } else {
             {
                 const int64_t p = pc + n;
@@ -863,7 +863,7 @@ __device__ __forceinline__ void attend_range(const DecodeArgs &a, int seq, const
                 const bool in = p >= R.lo && p < R.hi;
                 const int32_t b = in ? bt_s[(int)((p >> lbs) - jb0)] : -1;
                 const int64_t o = (int64_t)(b >= 0 ? b : 0) * a.pool.block_stride + (p & bsm) * row_bytes + 16 * tpp;
-                lds_copy16(vh + o, dst + i * VSLAB);
+                lds_copy16_nt(vh + o, dst + i * VSLAB);
             }
         }
     };
@@ -1239,13 +1239,13 @@ __device__ __forceinline__ void attend_range_q8(const DecodeArgs &a, const Range
             const int64_t base = bb * a.pool.block_stride + (pc & bsm) * row_bytes;
             const char *kb = kh + base + (uint32_t)(n * row_bytes + KC * g4);
 #pragma unroll
-            for (int i = 0; i < Slot::KL; ++i) sl.k[i] = ld16(kb + 16 * i);
+            for (int i = 0; i < Slot::KL; ++i) sl.k[i] = ld16_nt(kb + 16 * i);
 #pragma unroll
             for (int i = 0; i < Slot::VL; ++i)
-                sl.v[i] = ld16(vh + base + (uint32_t)((i * VRPL + vrow) * row_bytes + 16 * vpc));
+                sl.v[i] = ld16_nt(vh + base + (uint32_t)((i * VRPL + vrow) * row_bytes + 16 * vpc));
             const int64_t so = bb * a.pool.sc_block + (pc & bsm) + 4 * g4;
-            sl.ks = ld16(reinterpret_cast<const char *>(ksh + so));
-            sl.vs = ld16(reinterpret_cast<const char *>(vsh + so));
+            sl.ks = ld16_nt(reinterpret_cast<const char *>(ksh + so));
+            sl.vs = ld16_nt(reinterpret_cast<const char *>(vsh + so));
         } else {
             {
                 const int64_t p = pc + n;
@@ -1253,14 +1253,14 @@ __device__ __forceinline__ void attend_range_q8(const DecodeArgs &a, const Range
                 const int32_t b = in ? bt_s[(int)((p >> lbs) - jb0)] : -1;
                 const char *kb = kh + (int64_t)(b >= 0 ? b : 0) * a.pool.block_stride + (p & bsm) * row_bytes + KC * g4;
 #pragma unroll
-                for (int i = 0; i < Slot::KL; ++i) sl.k[i] = ld16(kb + 16 * i);
+                for (int i = 0; i < Slot::KL; ++i) sl.k[i] = ld16_nt(kb + 16 * i);
             }
 #pragma unroll
             for (int i = 0; i < Slot::VL; ++i) {
                 const int64_t p = pc + i * VRPL + vrow;
                 const bool in = p >= R.lo && p < R.hi;
                 const int32_t b = in ? bt_s[(int)((p >> lbs) - jb0)] : -1;
-                sl.v[i] = ld16(vh + (int64_t)(b >= 0 ? b : 0) * a.pool.block_stride + (p & bsm) * row_bytes + 16 * vpc);
+                sl.v[i] = ld16_nt(vh + (int64_t)(b >= 0 ? b : 0) * a.pool.block_stride + (p & bsm) * row_bytes + 16 * vpc);
             }
             uint32_t kw[4], vw[4];
 #pragma unroll
@@ -1863,7 +1863,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeArgs a) {
                 for (int j = 0; j < KS; ++j) kx[j] = ld16(kb + 64 * j);
 #pragma unroll
                 for (int i = 0; i < NP; ++i)
-                    lds_copy16(vh + bb + (uint32_t)((i + NP * trow) * row_bytes + 16 * tpp), dst + i * VSLAB);
+                    lds_copy16_nt(vh + bb + (uint32_t)((i + NP * trow) * row_bytes + 16 * tpp), dst + i * VSLAB);
             } else {
                 {
                     const int64_t p = pc + n16;
@@ -1881,7 +1881,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(DecodeArgs a) {
                     const bool in = p >= L.lo && p < L.hi && bi < kBtLds;
                     const int32_t b = in ? bt_s[bi] : -1;
                     const int64_t o = (int64_t)(b >= 0 ? b : 0) * a.pool.block_stride + (p & bsm) * row_bytes + 16 * tpp;
-                    lds_copy16(vh + o, dst + i * VSLAB);
+                    lds_copy16_nt(vh + o, dst + i * VSLAB);
                 }
             }
         };
