@@ -2,24 +2,29 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
-Workload: the decode batch -- 32 sequences, seq_len ~ U[128, 2048], block
-size 16, a 16384-block 32-layer bf16 pool (16 GiB each for K and V), 8 kv
-heads, head_dim 128, 32 query heads.  One step is one decode step of the
-serving loop, all on the device and in one launch (paged_attn_decode_append):
-the slot of every sequence's new token, the write of its K/V row into the
-pool, and fused paged decode attention over every cached token, the new one
-included.  The same step as two calls (kv_append, then paged_attn_decode) is
-timed too.
-Step i works on layer i % 32 with the same tables, so consecutive steps read
-disjoint memory (4.5 GB per 32-step cycle) and the 256 MB last-level cache
-cannot serve repeats.
+One step is one decode step of the serving loop, all on the device in one
+C-ABI call (paged_attn_decode_append): the slot of every sequence's new
+token, the write of its K/V row into the pool, and fused paged decode
+attention over every cached token, the new one included.  The pool is
+16384 blocks x 32 layers x block size 16 x 8 kv heads x head_dim 128, bf16
+(16 GiB each for K and V); step i works on layer i % 32 with the same
+tables, so consecutive steps read disjoint memory and the 256 MB last-level
+cache cannot serve repeats.
 
-Printed: one JSON line.  `value` is decode-attention KV bytes per second of
-whole-step time.  `roofline` describes the step's one kernel (timed with HIP
-events on the launch stream, back to back).
-`cpu_baseline` times the CPU oracle on the same decode batch.  `ops` reports
-the scatter and gather rates on the prefill shape (8 x 1024 rows, 10%
-padding) for reference.
+Headline workload: the long-context batch, 8 sequences x 32768 tokens (the
+whole 262,144-token pool), 64 query heads (8 per kv head), randomly
+permuted block tables.  The decode batch (32 sequences, U[128, 2048]
+tokens, 32 query heads) and the prefix-sharing batch (64 sequences sharing a
+512-token prefix from a nonzero first-block offset, up to 4096 tokens) are
+timed the same way, each in its own block of `decode_configs`.
+
+Printed: one JSON line.  `value` is the headline step's KV bytes per second
+of step time.  `roofline` describes the headline step (HIP events on the
+launch stream around the back-to-back timed steps).  `cpu_baseline` times
+the CPU oracle on the headline batch.  `ops` reports the scatter and gather
+rates on the prefill shape (8 x 1024 rows, 10% padding), block copies and
+swaps; `prefill_attention`, `int8_decode` and `block_manager` the other
+entry points.
 """
 import argparse
 import json
@@ -105,59 +110,6 @@ def block_manager_host(N, W, steps=2000):
                     "native manager called from Python"}
 
 
-def other_decode_configs(w, N, W, reps=32):
-    """Decode alone on the prefix-sharing and long-context batches, over the
-    same pools (same geometry), back to back with the layer rotated."""
-    import ctypes
-
-    import torch
-
-    out = {}
-    for name in ("prefix_sharing", "long_context"):
-        o = W.PRESETS[name](device=w.k_pool.device, with_pools=False)
-        o.k_pool, o.v_pool = w.k_pool, w.v_pool
-        lens = o.seq_lens.cpu().numpy()
-        kv, alg = decode_bytes(o, lens)
-        need = N.paged_attn_decode_workspace_size(o.num_seqs, o.num_kv_heads, o.num_q_heads,
-                                                  o.head_dim, o.max_seq_len, o.block_size, 0)
-        ws = torch.zeros(max(need, 16), dtype=torch.uint8, device=o.q.device)
-        res = torch.empty_like(o.q)
-        # arguments marshalled once, as in the timed step
-        lib = N.load_library()
-        pool = N.make_pool(o.k_pool, o.v_pool)
-        stream = ctypes.c_void_p(torch.cuda.current_stream(o.q.device).cuda_stream)
-        P = lambda t: ctypes.c_void_p(t.data_ptr())
-        args = [(ctypes.byref(pool), l, P(o.q), o.num_q_heads, P(o.block_tables),
-                 o.block_tables.shape[1], P(o.seq_lens), P(o.offsets), o.num_seqs, o.max_seq_len,
-                 ctypes.c_float(o.scale), 0, P(res), P(ws), ws.numel(), stream)
-                for l in range(o.num_layers)]
-
-        def f(layer):
-            if lib.paged_attn_decode(*args[layer]):
-                raise RuntimeError(f"paged_attn_decode failed on {name}")
-
-        for i in range(3):
-            f(i)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        a.record()
-        for i in range(reps):
-            f(i % o.num_layers)
-        b.record()
-        torch.cuda.synchronize()
-        us = a.elapsed_time(b) / reps * 1e3
-        sched, label = decode_schedule(N, o, 0)
-        entry = {"us": us, "algorithmic_bytes": alg, "GB/s": alg / us / 1e3,
-                 "frac": alg / us / 1e3 / HBM_PEAK_GBS, "kernel": label}
-        if name == "prefix_sharing":
-            bt = o.block_tables.cpu()
-            uniq = int(torch.unique(bt[bt >= 0]).numel())
-            entry["unique_kv_bytes"] = uniq * o.block_size * o.num_kv_heads * o.head_dim * 4
-        out[name] = entry
-        del o, ws, res
-    return out
-
-
 def prefill_attention(w, N, W, reps=6):
     """Prefill / append attention on the prefix-sharing batch (64 sequences
     whose first 32 blocks are shared, from a common first-block offset):
@@ -207,61 +159,71 @@ def prefill_attention(w, N, W, reps=6):
             "kernel": f"prefill_mfma_kernel<D={o.head_dim},G={g}>"}
 
 
-def int8_decode(w, N, W, reps=32):
-    """Decode over an int8 pool of the decode batch's geometry (16384 blocks
-    x 32 layers x 16 x 8 x 128 codes, one float32 scale per token and kv
-    head), same tables, lengths, offsets and bf16 queries; back to back with
-    the layer rotated.  Algorithmic bytes: every cached token's K and V
-    codes and scales once, q and out (bf16) once, the used table entries,
-    lengths and offsets."""
+def int8_decode(base, N, W, reps=32):
+    """Decode over an int8 pool of the decode workloads' geometry (16384
+    blocks x 32 layers x 16 x 8 x 128 codes, one float32 scale per token and
+    kv head) with each workload's tables, lengths, offsets and bf16 queries;
+    back to back with the layer rotated.  Algorithmic bytes: every cached
+    token's K and V codes and scales once, q and out (bf16) once, the used
+    table entries, lengths and offsets."""
+    import copy
     import ctypes
 
     import torch
 
-    dev = w.q.device
-    shape = (w.num_blocks, w.num_layers, w.block_size, w.num_kv_heads, w.head_dim)
+    dev = base.q.device
+    shape = (base.num_blocks, base.num_layers, base.block_size, base.num_kv_heads, base.head_dim)
     k = N.QuantizedPool(*W.int8_pool_tensors(*shape, dev, 8101))
     v = N.QuantizedPool(*W.int8_pool_tensors(*shape, dev, 8102))
-    lens = w.seq_lens.cpu().numpy()
-    tokens = int(lens.sum())
-    kv = tokens * w.num_kv_heads * (w.head_dim + 4) * 2
-    _, alg_bf16 = decode_bytes(w, lens)
-    kv_bf16 = tokens * w.num_kv_heads * w.head_dim * 2 * 2
-    alg = alg_bf16 - kv_bf16 + kv
-    split = N.paged_attn_decode_schedule(w.num_seqs, w.num_kv_heads, w.num_q_heads, w.head_dim,
-                                         w.max_seq_len, w.block_size, torch.int8, 0)
-    need = N.paged_attn_decode_workspace_size(w.num_seqs, w.num_kv_heads, w.num_q_heads,
-                                              w.head_dim, w.max_seq_len, w.block_size, 0)
-    ws = torch.zeros(max(need, 16), dtype=torch.uint8, device=dev)
-    res = torch.empty_like(w.q)
     lib = N.load_library()
     pool = N.make_pool(k, v)
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
     P = lambda t: ctypes.c_void_p(t.data_ptr())
-    args = [(ctypes.byref(pool), l, P(w.q), w.num_q_heads, P(w.block_tables),
-             w.block_tables.shape[1], P(w.seq_lens), P(w.offsets), w.num_seqs, w.max_seq_len,
-             ctypes.c_float(w.scale), 0, P(res), P(ws), ws.numel(), stream)
-            for l in range(w.num_layers)]
-    for i in range(3):
-        if lib.paged_attn_decode(*args[i]):
-            raise RuntimeError("int8 paged_attn_decode failed")
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    a.record()
-    for i in range(reps):
-        lib.paged_attn_decode(*args[i % w.num_layers])
-    b.record()
-    torch.cuda.synchronize()
-    us = a.elapsed_time(b) / reps * 1e3
-    g = w.num_q_heads // w.num_kv_heads
-    out = {"us": us, "algorithmic_bytes": alg, "GB/s": alg / us / 1e3,
-           "frac": alg / us / 1e3 / HBM_PEAK_GBS,
-           "kernel": f"decode_q8_kernel<D={w.head_dim},G={g}> " + (
-               "(device-planned split)" if split == N.SCHEDULE_PLANNED else f"(split {split})"),
-           "kv_bytes_vs_bf16": kv / kv_bf16}
-    del k, v, ws, res
+    res = {}
+    for name in DECODE_CONFIGS:
+        w = base if name == "decode_batch" else W.PRESETS[name](device=dev, with_pools=False)
+        w = copy.copy(w)
+        w.k_pool, w.v_pool = base.k_pool, base.v_pool   # bf16 geometry for decode_bytes
+        lens = w.seq_lens.cpu().numpy()
+        tokens = int(lens.sum())
+        kv = tokens * w.num_kv_heads * (w.head_dim + 4) * 2
+        kv_bf16, alg_bf16 = decode_bytes(w, lens)
+        alg = alg_bf16 - kv_bf16 + kv
+        sched = N.paged_attn_decode_schedule(w.num_seqs, w.num_kv_heads, w.num_q_heads, w.head_dim,
+                                             w.max_seq_len, w.block_size, torch.int8, 0)
+        need = N.paged_attn_decode_workspace_size(w.num_seqs, w.num_kv_heads, w.num_q_heads,
+                                                  w.head_dim, w.max_seq_len, w.block_size, 0)
+        ws = torch.zeros(max(need, 16), dtype=torch.uint8, device=dev)
+        out = torch.empty_like(w.q)
+        args = [(ctypes.byref(pool), l, P(w.q), w.num_q_heads, P(w.block_tables),
+                 w.block_tables.shape[1], P(w.seq_lens), P(w.offsets), w.num_seqs, w.max_seq_len,
+                 ctypes.c_float(w.scale), 0, P(out), P(ws), ws.numel(), stream)
+                for l in range(w.num_layers)]
+        # three untimed passes over the layers (the int8 pools are freshly
+        # filled: the first passes run slower), then the timed calls
+        for i in range(3 * w.num_layers):
+            if lib.paged_attn_decode(*args[i % w.num_layers]):
+                raise RuntimeError(f"int8 paged_attn_decode failed on {name}")
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for i in range(reps):
+            lib.paged_attn_decode(*args[i % w.num_layers])
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) / reps * 1e3
+        g = w.num_q_heads // w.num_kv_heads
+        max_splits = -(-(w.max_seq_len + w.block_size - 1) // max(sched, 1))
+        label = f"decode_q8_kernel<D={w.head_dim},G={g}> " + (
+            "(device-planned split)" if sched == N.SCHEDULE_PLANNED else
+            f"(split {sched}" + (", + reduce_kernel)" if max_splits > 16 else ")"))
+        res[name] = {"us": us, "algorithmic_bytes": alg, "GB/s": alg / us / 1e3,
+                     "frac": alg / us / 1e3 / HBM_PEAK_GBS, "kernel": label,
+                     "kv_bytes_vs_bf16": kv / kv_bf16}
+        del ws, out
+    del k, v, pool
     torch.cuda.empty_cache()
-    return out
+    return res
 
 
 def read_ceiling(w, N, reps=32):
@@ -323,11 +285,11 @@ def time_op(fn, reps, layers, warm=3):
     return ts[len(ts) // 2], sum(ts) / len(ts)
 
 
-def cpu_baseline(w, lens, min_seconds=10.0, layers=8):
-    """The CPU oracle on the same decode batch: full decode steps over the
-    first `layers` layers in rotation (distinct memory, so host caches do
-    not serve repeats) until at least `min_seconds` of wall time, on all
-    host threads; then one step on one thread.  Host copies of only the
+def cpu_baseline(w, lens, min_seconds=10.0, layers=2):
+    """The CPU oracle on the same batch: full decode steps over the first
+    `layers` layers in rotation (each layer's K/V is far larger than the
+    host caches) until at least `min_seconds` of wall time, on all host
+    threads; then one step on one thread.  Host copies of only the
     referenced blocks are made before the clock starts."""
     import numpy as np
     import torch
@@ -372,8 +334,9 @@ def cpu_baseline(w, lens, min_seconds=10.0, layers=8):
     except OSError:
         pass
     return {"value": kv * n / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} full decode steps of the {w.num_seqs}-sequence batch "
-                      f"({int(lens.sum())} cached tokens each), layers 0-{len(pools) - 1} in "
+            "sample": f"{n} full decode steps of the {w.name} batch ({w.num_seqs} sequences, "
+                      f"{w.num_q_heads} q heads, "
+                      f"{int(lens.sum())} cached tokens each), layers 0-{len(pools) - 1} in "
                       f"rotation, float64 gather-then-attention, {dt:.1f} s wall",
             "seconds": dt, "single_thread_GB/s": kv / dt1 / 1e9,
             "host_cpu": model, "host_cpus_visible": os.cpu_count()}
@@ -515,7 +478,6 @@ def block_ops(w_dec, N, pairs=64, sets=4, reps=32, swap_blocks=64, swap_reps=6):
     }
 
 
-TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "decode_batch_traffic.json")
 DECODE_SOURCES = [os.path.join(ROOT, "paged_attention_decode_scatter_amd", "csrc", f)
                   for f in ("kernels_decode.hip", "attn_common.h", "pagedkv_api.hip", "pkv_internal.h")]
 
@@ -530,12 +492,16 @@ def decode_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per step launch (decode with append) from the committed
-    counter record, or None when the record is missing or the decode sources
-    changed since."""
+def traffic_record(name):
+    return os.path.join(ROOT, "profiles", f"{name}_traffic.json")
+
+
+def measured_traffic(name):
+    """HBM bytes per step (decode with append) on workload `name` from the
+    committed counter record, or None when the record is missing or the
+    decode sources changed since."""
     try:
-        with open(TRAFFIC_RECORD) as f:
+        with open(traffic_record(name)) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
@@ -545,8 +511,8 @@ def measured_traffic():
 
 
 def pmc_target(which, reps):
-    """Run only what a counter pass should see: the decode call on the
-    decode batch (layer rotated), or a plain device copy of 1 GiB (the
+    """Run only what a counter pass should see: the step call on one decode
+    workload (layer rotated), or a plain device copy of 1 GiB (the
     calibration for FETCH_SIZE / WRITE_SIZE)."""
     import torch
 
@@ -565,7 +531,7 @@ def pmc_target(which, reps):
         log(f"copied {reps} x 1 GiB")
         return
     N.load_library()
-    w = W.decode_tokens(W.decode_batch(device=dev))
+    w = config_workload(which, W.decode_batch(device=dev), W)
     mx = w.max_seq_len
     out = torch.empty_like(w.q)
     split = 0  # the automatic schedule, as in the timed run
@@ -579,8 +545,217 @@ def pmc_target(which, reps):
                                    split_tokens=split, out=out, workspace=ws)
     torch.cuda.synchronize()
     _, alg = decode_bytes(w, w.seq_lens.cpu().numpy())
-    log(f"ran {reps} step launches (decode with append), {alg + append_bytes(w)} algorithmic "
-        f"bytes each, split {split}")
+    log(f"ran {reps} step launches (decode with append) on {which}, {alg + append_bytes(w)} "
+        f"algorithmic bytes each, split {split}")
+
+
+DECODE_CONFIGS = ("long_context", "decode_batch", "prefix_sharing")
+HEADLINE = "long_context"
+
+
+def config_workload(name, base, W):
+    """The decode workload `name` over the shared pools of `base` (same
+    geometry: 16384 blocks x 32 layers x 16 x 8 x 128 bf16), with one new
+    K/V row per sequence at position seq_len - 1."""
+    if name == "decode_batch":
+        w = base
+    else:
+        w = W.PRESETS[name](device=base.k_pool.device, with_pools=False)
+        w.k_pool, w.v_pool = base.k_pool, base.v_pool
+    w = W.decode_tokens(w)
+    if int(w.token_seq.numel()) != w.num_seqs:
+        raise RuntimeError(f"{name}: every sequence needs a token for the decode step")
+    return w
+
+
+def unique_live_bytes(w):
+    """K and V bytes of the distinct (block, slot) rows the batch's tables
+    hold live at the layer (a shared prefix counted once)."""
+    import numpy as np
+
+    bt = w.block_tables.cpu().numpy()
+    lens = w.seq_lens.cpu().numpy().astype(np.int64)
+    offs = w.offsets.cpu().numpy().astype(np.int64)
+    rows = set()
+    for s in range(w.num_seqs):
+        p = offs[s] + np.arange(lens[s], dtype=np.int64)
+        b = bt[s, p // w.block_size].astype(np.int64)
+        rows.update((b * w.block_size + p % w.block_size).tolist())
+    return len(rows) * w.row_bytes * 2
+
+
+def schedule_label(N, w, split):
+    """(kernel label, split label) of paged_attn_decode on this batch."""
+    sched, label = decode_schedule(N, w, split)
+    if sched == N.SCHEDULE_PLANNED:
+        return label, "planned (device-planned split)"
+    if sched == 0:
+        return label, "balanced"
+    return label, sched
+
+
+def decode_config(name, w, N, args, lib, stream, headline):
+    """Times the decode step (paged_attn_decode_append: the new token's slot
+    and write, and paged decode attention over every cached token) on one
+    workload, back to back with the layer rotated; also decode alone, one
+    cold step after a 1 GiB flush read, and the read-rate reference over the
+    same blocks.  The headline workload also times the step as HIP graph
+    replays and as two calls (kv_append + paged_attn_decode)."""
+    import ctypes
+
+    import torch
+
+    dev = w.q.device
+    lens = w.seq_lens.cpu().numpy()
+    kv_bytes, alg_bytes = decode_bytes(w, lens)
+    alg_step = alg_bytes + append_bytes(w)
+    split = args.split_tokens
+    kernel, split_label = schedule_label(N, w, split)
+    ws_bytes = N.paged_attn_decode_workspace_size(w.num_seqs, w.num_kv_heads, w.num_q_heads,
+                                                  w.head_dim, w.max_seq_len, w.block_size, split)
+    ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(w.q)
+    kn, vn = w.k_new, w.v_new   # rows in sequence order (every sequence has its token)
+    slots = torch.empty(w.num_seqs, dtype=torch.int64, device=dev)
+    pool = N.make_pool(w.k_pool, w.v_pool)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    L = w.num_layers
+    step_args = [(ctypes.byref(pool), l, P(w.q), w.num_q_heads, P(kn), P(vn), P(w.block_tables),
+                  w.block_tables.shape[1], P(w.seq_lens), P(w.offsets), w.num_seqs, w.max_seq_len,
+                  ctypes.c_float(w.scale), split, P(out), P(ws), ws.numel(), stream)
+                 for l in range(L)]
+    dec_args = [(ctypes.byref(pool), l, P(w.q), w.num_q_heads, P(w.block_tables),
+                 w.block_tables.shape[1], P(w.seq_lens), P(w.offsets), w.num_seqs, w.max_seq_len,
+                 ctypes.c_float(w.scale), split, P(out), P(ws), ws.numel(), stream)
+                for l in range(L)]
+    app_args = [(ctypes.byref(pool), l, P(kn), P(vn), P(w.block_tables), w.block_tables.shape[1],
+                 P(w.offsets), w.num_seqs, P(w.token_seq), P(w.token_pos), w.num_seqs, P(slots),
+                 stream) for l in range(L)]
+    f_step, f_dec, f_app = lib.paged_attn_decode_append, lib.paged_attn_decode, lib.kv_append
+
+    def back_to_back(fn):
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(args.steps):
+            fn(i)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / args.steps
+
+    def step(i):
+        if f_step(*step_args[i % L]):
+            raise RuntimeError(f"paged_attn_decode_append failed on {name}")
+
+    def decode_only(i):
+        if f_dec(*dec_args[i % L]):
+            raise RuntimeError(f"paged_attn_decode failed on {name}")
+
+    def two_call(i):
+        if f_app(*app_args[i % L]) | f_dec(*dec_args[i % L]):
+            raise RuntimeError(f"kv_append / paged_attn_decode failed on {name}")
+
+    # The first passes over the freshly filled 32 GiB pool run slower
+    # (long context: ~350 us per step over the first 20 steps, settled at
+    # ~170 us from about step 100 on): three untimed passes over the 32
+    # layers precede the warmup steps.
+    for i in range(3 * L):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"{name}: timing {args.steps} steps ({kernel})")
+    ms_step = back_to_back(step)
+    # per-call event pairs around the same calls
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    for i in range(args.steps):
+        starts[i].record()
+        step(i)
+        ends[i].record()
+    torch.cuda.synchronize()
+    per_call = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    ms_dec = back_to_back(decode_only)
+    # cold steps: each after a 1 GiB device copy (reads 1 GiB, so no cache
+    # holds the step's bytes), on a layer the previous steps did not touch last
+    flush_src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    flush_dst = torch.empty_like(flush_src)
+    cold = []
+    for i in range(5):
+        flush_dst.copy_(flush_src)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        step(7 * i + 3)
+        b.record()
+        torch.cuda.synchronize()
+        cold.append(a.elapsed_time(b))
+    del flush_src, flush_dst
+    cold.sort()
+    entry = {
+        "kernel": kernel + ", with the new-token write",
+        "split_tokens": split_label,
+        "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
+        "head_dim": w.head_dim, "cached_tokens": int(lens.sum()),
+        "step_us": ms_step * 1e3,
+        "kv_bytes": kv_bytes,
+        "algorithmic_bytes_per_step": alg_step,
+        "achieved_GBps": alg_step / ms_step / 1e6,
+        "frac": alg_step / ms_step / 1e6 / HBM_PEAK_GBS,
+        "per_call_events_median_us": per_call[len(per_call) // 2] * 1e3,
+        "per_call_events_avg_us": sum(per_call) / len(per_call) * 1e3,
+        "decode_alone_us": ms_dec * 1e3,
+        "decode_alone_GBps": alg_bytes / ms_dec / 1e6,
+        "cold_step_us_median_of_5": cold[2] * 1e3,
+        "cold_step_GBps": alg_step / cold[2] / 1e6,
+        "measured_read_ceiling": read_ceiling(w, N),
+        "traffic": measured_traffic(name),
+    }
+    if name == "prefix_sharing":
+        uniq = unique_live_bytes(w)
+        alg_unique = alg_step - kv_bytes + uniq
+        entry["unique_kv_bytes"] = uniq
+        entry["algorithmic_bytes_unique"] = alg_unique
+        entry["achieved_GBps_unique"] = alg_unique / ms_step / 1e6
+        entry["frac_unique"] = alg_unique / ms_step / 1e6 / HBM_PEAK_GBS
+        entry["note"] = ("frac_unique counts the shared prefix once (its 64 readers are served "
+                         "from cache after the first); frac counts it once per sequence")
+    if headline and not args.no_graph:
+        def capture(calls):
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                for i in range(3):
+                    calls(i % L, ctypes.c_void_p(side.cuda_stream))
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            gs = []
+            for layer in range(L):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    calls(layer, ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream))
+                gs.append(g)
+            torch.cuda.synchronize()
+            return gs
+
+        def fused_calls(layer, cs):
+            if f_step(*step_args[layer][:-1], cs):
+                raise RuntimeError("paged_attn_decode_append failed while capturing")
+
+        def two_calls(layer, cs):
+            if f_app(*app_args[layer][:-1], cs) | f_dec(*dec_args[layer][:-1], cs):
+                raise RuntimeError("a library call failed while capturing")
+
+        gs = capture(fused_calls)
+        entry["graph_replay_us"] = back_to_back(lambda i: gs[i % L].replay()) * 1e3
+        del gs
+        entry["two_call_step_us"] = back_to_back(two_call) * 1e3
+        gs = capture(two_calls)
+        entry["two_call_graph_replay_us"] = back_to_back(lambda i: gs[i % L].replay()) * 1e3
+        del gs
+    log(f"{name}: step {ms_step * 1e3:.1f} us, {entry['frac']:.3f} of peak; decode alone "
+        f"{ms_dec * 1e3:.1f} us; cold {cold[2] * 1e3:.1f} us")
+    del ws, out
+    return entry, ms_step
 
 
 def main():
@@ -592,9 +767,12 @@ def main():
     ap.add_argument("--no-ops", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="time the step as eager calls only (no HIP graph replay)")
+    ap.add_argument("--configs", default=",".join(DECODE_CONFIGS),
+                    help="decode workloads to time (the headline, long_context, is always first)")
     ap.add_argument("--split-tokens", type=int, default=0)
-    ap.add_argument("--pmc-target", choices=["decode", "copy"], default=None,
-                    help="run only the decode launches (or a 1 GiB copy) for counter passes")
+    ap.add_argument("--pmc-target", choices=list(DECODE_CONFIGS) + ["copy"], default=None,
+                    help="run only the step launches of one workload (or a 1 GiB copy) for "
+                         "counter passes")
     ap.add_argument("--pmc-reps", type=int, default=20)
     args = ap.parse_args()
     if args.gpus != 1:
@@ -603,7 +781,8 @@ def main():
               "measurement to make here", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np  # noqa: F401
+    import ctypes
+
     import torch
 
     from paged_attention_decode_scatter_amd import native as N
@@ -616,228 +795,80 @@ def main():
         pmc_target(args.pmc_target, args.pmc_reps)
         return
     dev = torch.device("cuda:0")
-    N.load_library()
-    log("building the decode-batch workload (2 x 16 GiB pools)")
-    w = W.decode_tokens(W.decode_batch(device=dev))
-    lens = w.seq_lens.cpu().numpy()
-    mx = w.max_seq_len
-    kv_bytes, alg_bytes = decode_bytes(w, lens)
-    split = args.split_tokens
-    sched, kernel_label = decode_schedule(N, w, split)
-    ws_bytes = N.paged_attn_decode_workspace_size(w.num_seqs, w.num_kv_heads, w.num_q_heads,
-                                                  w.head_dim, mx, w.block_size, split)
-    workspace = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
-    out = torch.empty_like(w.q)
-    slots = torch.empty(w.token_seq.shape[0], dtype=torch.int64, device=dev)
-    dec_start = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    dec_end = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-
-    # The step issues its C-ABI call with arguments marshalled once up
-    # front (the values the binding would pass), so host-side Python does
-    # not starve the ~40 us device step.
-    import ctypes
-
     lib = N.load_library()
-    pool = N.make_pool(w.k_pool, w.v_pool)
+    log("building the pools (2 x 16 GiB) and the decode workloads")
+    base = W.decode_batch(device=dev)
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
-    P = lambda t: ctypes.c_void_p(t.data_ptr())
-    # one new K/V row per sequence (all 32 have tokens), in sequence order
-    assert torch.equal(w.token_seq.cpu(), torch.arange(w.num_seqs, dtype=torch.int32))
-    # the step: the new tokens' slots and writes + decode, one launch
-    step_args = [(ctypes.byref(pool), l, P(w.q), w.num_q_heads, P(w.k_new), P(w.v_new),
-                  P(w.block_tables), w.block_tables.shape[1], P(w.seq_lens), P(w.offsets),
-                  w.num_seqs, mx, ctypes.c_float(w.scale), split, P(out), P(workspace),
-                  workspace.numel(), stream)
-                 for l in range(w.num_layers)]
-    # the same step as two calls: slots + scatter (kv_append), then decode
-    app_args = [(ctypes.byref(pool), l, P(w.k_new), P(w.v_new), P(w.block_tables),
-                 w.block_tables.shape[1], P(w.offsets), w.num_seqs, P(w.token_seq),
-                 P(w.token_pos), w.token_seq.shape[0], P(slots), stream)
-                for l in range(w.num_layers)]
-    dec_args = [(ctypes.byref(pool), l, P(w.q), w.num_q_heads, P(w.block_tables),
-                 w.block_tables.shape[1], P(w.seq_lens), P(w.offsets), w.num_seqs, mx,
-                 ctypes.c_float(w.scale), split, P(out), P(workspace), workspace.numel(), stream)
-                for l in range(w.num_layers)]
-    f_step, f_app, f_dec = lib.paged_attn_decode_append, lib.kv_append, lib.paged_attn_decode
-
-    def step(i, timed=False):
-        layer = i % w.num_layers
-        if timed:
-            dec_start[i].record()
-        rc = f_step(*step_args[layer])
-        if timed:
-            dec_end[i].record()
-        if rc:
-            raise RuntimeError(f"a library call failed in step {i}")
-
-    def two_call_step(i):
-        layer = i % w.num_layers
-        if f_app(*app_args[layer]) | f_dec(*dec_args[layer]):
-            raise RuntimeError(f"a library call failed in step {i}")
-
-    def capture(calls):
-        """One HIP graph per layer holding `calls(layer, stream)`."""
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            for i in range(3):
-                cs = ctypes.c_void_p(side.cuda_stream)
-                calls(i % w.num_layers, cs)
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        gs = []
-        for layer in range(w.num_layers):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                calls(layer, ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream))
-            gs.append(g)
-        torch.cuda.synchronize()
-        return gs
-
-    def fused_calls(layer, cs):
-        if f_step(*step_args[layer][:-1], cs):
-            raise RuntimeError(f"paged_attn_decode_append failed while capturing layer {layer}")
-
-    def two_calls(layer, cs):
-        if f_app(*app_args[layer][:-1], cs) | f_dec(*dec_args[layer][:-1], cs):
-            raise RuntimeError(f"a library call failed while capturing layer {layer}")
-
-    def time_graphs(gs):
-        for i in range(args.warmup):
-            gs[i % w.num_layers].replay()
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for i in range(args.steps):
-            gs[i % w.num_layers].replay()
-        b.record()
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / args.steps
-
-    def time_eager(fn):
-        for i in range(args.warmup):
-            fn(i)
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for i in range(args.steps):
-            fn(i)
-        b.record()
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / args.steps
-
-    log(f"warmup {args.warmup} steps (split_tokens={split}, workspace={ws_bytes} B)")
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    # The timed steps: K calls back to back on the stream (layer rotated),
-    # one event pair around all of them.
-    log(f"timing {args.steps} steps")
-    ms_step = time_eager(step)
-    alg_step = alg_bytes + append_bytes(w)
-    achieved = alg_step / (ms_step * 1e-3) / 1e9
-    log(f"step {ms_step * 1e3:.1f} us ({achieved:.0f} GB/s algorithmic)")
-    # the same calls with an event pair around each (adds per-call latency)
-    for i in range(args.steps):
-        step(i, timed=True)
-    torch.cuda.synchronize()
-    dec_ms = [s.elapsed_time(e) for s, e in zip(dec_start, dec_end)]
-    dec_avg = sum(dec_ms) / len(dec_ms)
-    dec_med = sorted(dec_ms)[len(dec_ms) // 2]
-    # the step replayed as one HIP graph per layer
-    graph_ms = None if args.no_graph else time_graphs(capture(fused_calls))
-    us = lambda ms: "n/a" if ms is None else f"{ms * 1e3:.1f}"
-    log(f"per-call events avg {dec_avg * 1e3:.1f} us (median {dec_med * 1e3:.1f}); graph replay "
-        f"{us(graph_ms)} us")
-
-    # The same step as two calls (append kernel, then decode), for comparison.
-    two_eager = time_eager(two_call_step)
-    two_graph = None if args.no_graph else time_graphs(capture(two_calls))
-    log(f"two-call step: eager {us(two_eager)} us, graph {us(two_graph)} us")
-    dec_b2b = ms_step
-    d_start = torch.cuda.Event(enable_timing=True)
-    d_end = torch.cuda.Event(enable_timing=True)
-    # and decode alone (no append), the same way
-    for i in range(3):
-        f_dec(*dec_args[i % w.num_layers])
-    torch.cuda.synchronize()
-    d_start.record()
-    for i in range(args.steps):
-        f_dec(*dec_args[i % w.num_layers])
-    d_end.record()
-    torch.cuda.synchronize()
-    dec_only = d_start.elapsed_time(d_end) / args.steps
-    log(f"decode alone back to back {dec_only * 1e3:.1f} us per call")
-
+    names = [HEADLINE] + [c for c in args.configs.split(",") if c and c != HEADLINE]
+    configs, head_ms, head_w = {}, None, None
+    for name in names:
+        w = config_workload(name, base, W)
+        configs[name], ms = decode_config(name, w, N, args, lib, stream, name == HEADLINE)
+        if name == HEADLINE:
+            head_ms, head_w = ms, w
+    h = configs[HEADLINE]
     result = {
         "metric": METRIC,
-        "value": kv_bytes / (ms_step * 1e-3) / 1e9,
+        "value": h["kv_bytes"] / (head_ms * 1e-3) / 1e9,
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_step,
+        "ms_per_step": head_ms,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": "decode_batch",
-            "num_seqs": w.num_seqs,
-            "seq_len": "U[128,2048]",
-            "cached_tokens": int(lens.sum()),
-            "block_size": w.block_size,
-            "pool_blocks": w.num_blocks,
-            "num_layers": w.num_layers,
-            "num_kv_heads": w.num_kv_heads,
-            "head_dim": w.head_dim,
-            "num_q_heads": w.num_q_heads,
-            "split_tokens": sched if sched > 0 else "balanced",
-            "kv_bytes_per_step": kv_bytes,
+            "workload": HEADLINE,
+            "num_seqs": head_w.num_seqs,
+            "seq_len": head_w.max_seq_len,
+            "cached_tokens": h["cached_tokens"],
+            "block_size": head_w.block_size,
+            "pool_blocks": head_w.num_blocks,
+            "num_layers": head_w.num_layers,
+            "num_kv_heads": head_w.num_kv_heads,
+            "head_dim": head_w.head_dim,
+            "num_q_heads": head_w.num_q_heads,
+            "split_tokens": h["split_tokens"],
+            "kv_bytes_per_step": h["kv_bytes"],
             "step": "paged_attn_decode_append: slot + write of 1 new K/V row per sequence and "
-                    "paged decode attention in one launch, layer rotated over 32",
+                    "paged decode attention over every cached token, one C-ABI call per step, "
+                    "layer rotated over 32",
             "step_launch": "one C-ABI call per step, issued back to back",
-            "graph_replay_ms_per_step": graph_ms,
-            "two_call_step": {"calls": "kv_append + paged_attn_decode",
-                              "ms_per_step": two_eager, "graph_replay_ms_per_step": two_graph},
             "parallelism": "single GPU",
         },
         "roofline": {
-            "kernel": kernel_label + ", with the new-token write",
+            "kernel": h["kernel"],
             "bound": "hbm",
-            "achieved": achieved,
+            "achieved": h["achieved_GBps"],
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS,
-            "traffic": measured_traffic(),
-            "algorithmic_bytes_per_launch": alg_step,
-            "avg_launch_us": dec_b2b * 1e3,
+            "frac": h["frac"],
+            "traffic": h["traffic"],
+            "algorithmic_bytes_per_launch": h["algorithmic_bytes_per_step"],
+            "avg_launch_us": h["step_us"],
             "timing": f"HIP events around the {args.steps} back-to-back step calls on the launch "
                       "stream (the timed steps themselves)",
-            "decode_alone_us": dec_only * 1e3,
-            "decode_alone_GBps": alg_bytes / (dec_only * 1e-3) / 1e9,
-            "per_call_events_avg_us": dec_avg * 1e3,
-            "per_call_events_median_us": dec_med * 1e3,
-            "measured_read_ceiling": read_ceiling(w, N),
+            "measured_read_ceiling": h["measured_read_ceiling"],
         },
+        "decode_configs": configs,
     }
     if not args.no_ops:
         log("scatter/gather on the prefill shape")
-        result["ops"] = prefill_ops(w, N, W)
+        result["ops"] = prefill_ops(base, N, W)
         log("block copies and swaps")
-        result["ops"].update(block_ops(w, N))
-        log("decode on the prefix-sharing and long-context batches")
-        result["other_decode"] = other_decode_configs(w, N, W)
+        result["ops"].update(block_ops(base, N))
         log("prefill attention on the prefix-sharing batch")
-        result["prefill_attention"] = prefill_attention(w, N, W)
-        log("int8 pool decode on the decode batch")
-        result["int8_decode"] = int8_decode(w, N, W)
+        result["prefill_attention"] = prefill_attention(base, N, W)
+        log("int8 pool decode")
+        result["int8_decode"] = int8_decode(base, N, W)
         log("host block manager")
         result["block_manager"] = block_manager_host(N, W)
     if not args.no_cpu_baseline:
-        log("CPU oracle baseline")
-        result["cpu_baseline"] = cpu_baseline(w, lens)
+        log("CPU oracle baseline on the long-context batch")
+        result["cpu_baseline"] = cpu_baseline(head_w, head_w.seq_lens.cpu().numpy())
     print(json.dumps(result), flush=True)
 
 
