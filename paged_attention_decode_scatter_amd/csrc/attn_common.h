@@ -216,16 +216,26 @@ __device__ __forceinline__ float max_xor32(float v) {
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// Max and sum over all 64 lanes, the result in every lane: DPP within rows
+// of 16 lanes, then the row swaps across rows -- all VALU, no LDS permute
+// round trip in the chain.  Every lane gets the same bits (each step
+// combines two equal partial results in both orders).
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
-    return x;
+    x = fmaxf(x, dpp<0xB1>(x));   // quad_perm [1,0,3,2]
+    x = fmaxf(x, dpp<0x4E>(x));   // quad_perm [2,3,0,1]
+    x = fmaxf(x, dpp<0x141>(x));  // row_half_mirror
+    x = fmaxf(x, dpp<0x140>(x));  // row_mirror
+    return max_xor32(max_xor16(x));
 }
 
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
-    return x;
+    x = row_allsum<16>(x);
+    const unsigned u = __float_as_uint(x);
+    const auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    x = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+    const unsigned v = __float_as_uint(x);
+    const auto r32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
 }
 
 __device__ __forceinline__ float lane_value(float x, int lane) {
