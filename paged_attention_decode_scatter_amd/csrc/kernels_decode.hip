@@ -1134,7 +1134,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
 //      bf16 row pieces into the wave's V tile in the bf16 kernel's tile
 //      layout; P.V then reads it with the same transposing LDS read.  The
 //      value scale folds into the probabilities: P'_t = p_t * vscale_t
-//      (rounded to bf16 as P is); the denominator sums the unscaled p_t.
+//      (rounded to bf16 as P is); the denominator sums P'_t / vscale_t, the
+//      weights the operand carries.
 //   Scales: the 16 tokens of a chunk are contiguous per head (layout
 //      (block, layer, head, slot)), so lane (n, g4) loads the scales of its
 //      four score rows 4 g4 .. 4 g4 + 3 with one 16-byte load each.
@@ -1346,9 +1347,23 @@ __device__ __forceinline__ void attend_range_q8(const DecodeArgs &a, const Range
             pr[i] = s[i] == kNegInf ? 0.0f : fast_exp2(s[i] - m_h);
             pv[i] = s[i] == kNegInf ? 0.0f : pr[i] * vsf[i];
         }
-        const uint32_t p01 = f32_to_bf16_bits(pr[0]) | (f32_to_bf16_bits(pr[1]) << 16);
-        const uint32_t p23 = f32_to_bf16_bits(pr[2]) | (f32_to_bf16_bits(pr[3]) << 16);
-        l_h = fmaf(l_h, alpha, (bf16_lo(p01) + bf16_hi(p01)) + (bf16_lo(p23) + bf16_hi(p23)));
+        const uint32_t q01 = f32_to_bf16_bits(pv[0]) | (f32_to_bf16_bits(pv[1]) << 16);
+        const uint32_t q23 = f32_to_bf16_bits(pv[2]) | (f32_to_bf16_bits(pv[3]) << 16);
+        // The denominator sums the weights the P.V operand actually carries,
+        // bf16(p * vscale) / vscale, so the output is a convex combination of
+        // the stored values code * vscale and a dominant token's rounding
+        // cancels (summing bf16(p) instead left up to 2^-8 relative error on
+        // peaked rows).  A zero (or tiny) scale is a zero row: its weight is
+        // bf16(p).
+        const float qv[4] = {bf16_lo(q01), bf16_hi(q01), bf16_lo(q23), bf16_hi(q23)};
+        float dsum = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float w = vsf[i] > 1e-30f ? qv[i] * __builtin_amdgcn_rcpf(vsf[i])
+                                            : __uint_as_float(f32_to_bf16_bits(pr[i]) << 16);
+            dsum += w;
+        }
+        l_h = fmaf(l_h, alpha, dsum);
         if (__any(n < G && alpha != 1.0f)) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -1357,8 +1372,6 @@ __device__ __forceinline__ void attend_range_q8(const DecodeArgs &a, const Range
                 for (int sl2i = 0; sl2i < NV; ++sl2i) acc[sl2i][i] *= al;
             }
         }
-        const uint32_t q01 = f32_to_bf16_bits(pv[0]) | (f32_to_bf16_bits(pv[1]) << 16);
-        const uint32_t q23 = f32_to_bf16_bits(pv[2]) | (f32_to_bf16_bits(pv[3]) << 16);
         typedef short s16x4 __attribute__((ext_vector_type(4)));
         const s16x4 pa = __builtin_bit_cast(s16x4, (uint64_t)q01 | ((uint64_t)q23 << 32));
         wave_lds_order();
