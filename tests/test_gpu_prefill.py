@@ -202,8 +202,10 @@ def test_prefill_prefix_sharing_full_size(dev):
     """Prefix-sharing batch at full size (64 sequences sharing 32 physical
     blocks at a common first-block offset, ref count 64): every suffix token
     is a query, attending causally to the shared prefix and its own tokens.
-    Sampled rows against the oracle's one-query prefill of the first P + 1
-    tokens."""
+    Every query row of two whole sequences (the one of median query count
+    and the one of smallest count) against the oracle's prefill of those
+    sequences, and sampled rows of 12 others against its one-query prefill of
+    the first P + 1 tokens."""
     w = W.prefix_sharing(device=dev)
     lens = host(w.seq_lens).astype(np.int64)
     prefix = int(w.meta["shared_blocks"]) * w.block_size
@@ -211,6 +213,17 @@ def test_prefill_prefix_sharing_full_size(dev):
     q, qs = queries(w, counts, 250)
     got = run(w, q, qs)
     assert torch.isfinite(got).all()
+    qs_h = host(qs)
+    order = np.argsort(np.array(counts), kind="stable")
+    for s in (int(order[len(order) // 2]), int(order[0])):
+        rows = torch.arange(int(qs_h[s]), int(qs_h[s + 1]), device=dev)
+        k_c, v_c, bt_c, _ = compact(w.k_pool, w.v_pool, w.layer, w.block_tables[s:s + 1])
+        ref = O.prefill(k_c, v_c, 0, host(q[rows]), np.array([0, counts[s]], np.int32), bt_c,
+                        lens[s:s + 1].astype(np.int32), host(w.offsets[s:s + 1]), w.scale,
+                        num_threads=oracle_threads())
+        err = max_abs_err(got[rows], ref)
+        print(f"prefix-sharing prefill, sequence {s}: {counts[s]} query rows, max abs err {err:.3e}")
+        assert err <= TOL[w.dtype]
     rng = np.random.default_rng(251)
     qs_h = host(qs)
     picks = []
