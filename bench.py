@@ -110,14 +110,9 @@ def block_manager_host(N, W, steps=2000):
                     "native manager called from Python"}
 
 
-def prefill_attention(w, N, W, reps=6):
-    """Prefill / append attention on the prefix-sharing batch (64 sequences
-    whose first 32 blocks are shared, from a common first-block offset):
-    every suffix token is a query, attending causally to the shared prefix
-    and its own earlier tokens, read in place.  Over the decode batch's
-    pools (same geometry), layer rotated, back to back.  Algorithmic work:
-    4 * head_dim flops per (query, visible key, query head) -- QK^T and P.V
-    -- against the dense bf16 matrix-core peak."""
+def prefill_setup(w, N, W):
+    """Arguments of paged_attn_prefill on the prefix-sharing batch over the
+    pools of `w`, one tuple per layer, and the workload's size."""
     import ctypes
 
     import numpy as np
@@ -136,27 +131,44 @@ def prefill_attention(w, N, W, reps=6):
     # pairs (query, visible key): query i of n sits at position L - n + i
     pairs = int(sum(n * (l - n) + n * (n + 1) // 2 for n, l in zip(counts, lens)))
     flops = pairs * o.num_q_heads * 4 * o.head_dim
-    lib = N.load_library()
     pool = N.make_pool(w.k_pool, w.v_pool)
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
     P = lambda t: ctypes.c_void_p(t.data_ptr())
     args = [(ctypes.byref(pool), l, P(q), o.num_q_heads, P(q_start), rows, int(counts.max()),
              P(o.block_tables), o.block_tables.shape[1], P(o.seq_lens), P(o.offsets), o.num_seqs,
              ctypes.c_float(o.scale), P(out), stream) for l in range(w.num_layers)]
+    keep = (o, q, q_start, out, pool)
+    g = o.num_q_heads // o.num_kv_heads
+    info = {"query_rows": rows, "query_key_pairs": pairs, "flops": flops,
+            "kernel": f"prefill_mfma_kernel<D={o.head_dim},G={g}>"}
+    return args, info, keep
+
+
+def prefill_attention(w, N, W, reps=6):
+    """Prefill / append attention on the prefix-sharing batch (64 sequences
+    whose first 32 blocks are shared, from a common first-block offset):
+    every suffix token is a query, attending causally to the shared prefix
+    and its own earlier tokens, read in place.  Over the decode batch's
+    pools (same geometry), layer rotated, back to back.  Algorithmic work:
+    4 * head_dim flops per (query, visible key, query head) -- QK^T and P.V
+    -- against the dense bf16 matrix-core peak."""
+    import torch
+
+    lib = N.load_library()
+    args, info, keep = prefill_setup(w, N, W)
     if lib.paged_attn_prefill(*args[0]):
         raise RuntimeError("paged_attn_prefill failed")
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     a.record()
     for i in range(reps):
-        lib.paged_attn_prefill(*args[(i + 1) % w.num_layers])
+        lib.paged_attn_prefill(*args[(i + 1) % len(args)])
     b.record()
     torch.cuda.synchronize()
     ms = a.elapsed_time(b) / reps
-    g = o.num_q_heads // o.num_kv_heads
-    return {"query_rows": rows, "query_key_pairs": pairs, "flops": flops, "ms": ms,
-            "TFLOP/s": flops / ms / 1e9, "frac_of_bf16_mfma_peak": flops / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS,
-            "kernel": f"prefill_mfma_kernel<D={o.head_dim},G={g}>"}
+    flops = info["flops"]
+    return dict(info, ms=ms, **{"TFLOP/s": flops / ms / 1e9,
+                                "frac_of_bf16_mfma_peak": flops / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS})
 
 
 def int8_decode(base, N, W, reps=32):
@@ -530,7 +542,45 @@ def pmc_target(which, reps):
         torch.cuda.synchronize()
         log(f"copied {reps} x 1 GiB")
         return
-    N.load_library()
+    lib = N.load_library()
+    if which == "prefill":
+        base = W.decode_batch(device=dev)
+        args, info, keep = prefill_setup(base, N, W)
+        torch.cuda.synchronize()
+        for i in range(reps):
+            if lib.paged_attn_prefill(*args[i % len(args)]):
+                raise RuntimeError("paged_attn_prefill failed")
+        torch.cuda.synchronize()
+        log(f"ran {reps} prefill launches on the prefix-sharing batch ({info['flops']} flops each)")
+        return
+    if which.startswith("int8_"):
+        import copy
+        import ctypes
+
+        base = W.decode_batch(device=dev)
+        shape = (base.num_blocks, base.num_layers, base.block_size, base.num_kv_heads, base.head_dim)
+        k = N.QuantizedPool(*W.int8_pool_tensors(*shape, dev, 8101))
+        v = N.QuantizedPool(*W.int8_pool_tensors(*shape, dev, 8102))
+        name = which[5:]
+        w = base if name == "decode_batch" else W.PRESETS[name](device=dev, with_pools=False)
+        w = copy.copy(w)
+        ws = torch.zeros(max(16, N.paged_attn_decode_workspace_size(
+            w.num_seqs, w.num_kv_heads, w.num_q_heads, w.head_dim, w.max_seq_len, w.block_size, 0)),
+            dtype=torch.uint8, device=dev)
+        out = torch.empty_like(w.q)
+        pool = N.make_pool(k, v)
+        stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        P = lambda t: ctypes.c_void_p(t.data_ptr())
+        torch.cuda.synchronize()
+        for i in range(reps):
+            if lib.paged_attn_decode(ctypes.byref(pool), i % w.num_layers, P(w.q), w.num_q_heads,
+                                     P(w.block_tables), w.block_tables.shape[1], P(w.seq_lens),
+                                     P(w.offsets), w.num_seqs, w.max_seq_len,
+                                     ctypes.c_float(w.scale), 0, P(out), P(ws), ws.numel(), stream):
+                raise RuntimeError("int8 paged_attn_decode failed")
+        torch.cuda.synchronize()
+        log(f"ran {reps} int8 decode launches on {name}")
+        return
     w = config_workload(which, W.decode_batch(device=dev), W)
     mx = w.max_seq_len
     out = torch.empty_like(w.q)
@@ -770,9 +820,11 @@ def main():
     ap.add_argument("--configs", default=",".join(DECODE_CONFIGS),
                     help="decode workloads to time (the headline, long_context, is always first)")
     ap.add_argument("--split-tokens", type=int, default=0)
-    ap.add_argument("--pmc-target", choices=list(DECODE_CONFIGS) + ["copy"], default=None,
-                    help="run only the step launches of one workload (or a 1 GiB copy) for "
-                         "counter passes")
+    ap.add_argument("--pmc-target", default=None,
+                    choices=list(DECODE_CONFIGS) + ["int8_" + c for c in DECODE_CONFIGS]
+                    + ["prefill", "copy"],
+                    help="run only the step launches of one workload (or int8 decode on it, the "
+                         "prefill launches, or a 1 GiB copy) for counter passes")
     ap.add_argument("--pmc-reps", type=int, default=20)
     args = ap.parse_args()
     if args.gpus != 1:
