@@ -114,15 +114,21 @@ __global__ __launch_bounds__(64 * kPrefillWaves<G>) __attribute__((amdgpu_waves_
 #pragma unroll
         for (int j = 0; j < KS; ++j) qf[t][j] = qi < nq ? ld16(qp + 64 * j) : u32x4{0, 0, 0, 0};
     }
-    float m_h[QT], l_h[QT];
-    f32x4 acc[QT][NV];
+    // m_h[t]: reference max of query column cn (exp2 domain); acc[t][sl]:
+    // O rows 4*g4 + i, columns 16 sl + cn; accl[t]: the denominators of the
+    // same rows, accumulated on the matrix core as P . (a column of ones),
+    // so they sum exactly the bf16 P values the P . V product uses and land
+    // in the output rows' layout
+    float m_h[QT];
+    f32x4 acc[QT][NV], accl[QT];
 #pragma unroll
     for (int t = 0; t < QT; ++t) {
         m_h[t] = kNegInf;
-        l_h[t] = 0.0f;
+        accl[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int sl = 0; sl < NV; ++sl) acc[t][sl] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
+    const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 1.0 pairs
 
     const int lbs = a.pool.lbs;
     const int64_t bsm = (1ll << lbs) - 1;
@@ -195,11 +201,13 @@ __global__ __launch_bounds__(64 * kPrefillWaves<G>) __attribute__((amdgpu_waves_
 #pragma unroll
                     for (int j = 0; j < KS; ++j)
                         kf[c][j] = *reinterpret_cast<const u32x4 *>(ktile[qs + c] + cn * KROW + 16 * g4 + 64 * j);
-                // no mask needed in a chunk whose rows are all live tokens
-                // at or before the wavefront's first query (wave-uniform);
-                // rows of the second chunk past the piece are not live
+                // A chunk needs no mask when all its rows are live tokens at
+                // or before the wavefront's first query.  When both chunks are
+                // such (every stage below the causal diagonal and inside the
+                // piece: nearly all of them), the stage takes the unmasked
+                // path (wave-uniform branch); else the rows' liveness is
+                // found once for the stage and each score is masked.
                 bool full[2];
-                bool rok[2][4];
 #pragma unroll
                 for (int c = 0; c < 2; ++c) {
                     const int64_t pcc = cpc + 16 * c;
@@ -210,8 +218,14 @@ __global__ __launch_bounds__(64 * kPrefillWaves<G>) __attribute__((amdgpu_waves_
                         f = false;   // rows may sit in different blocks
                     }
                     full[c] = f;
+                }
+                const bool unmasked = full[0] && full[1];   // (full[1] is false without a second chunk)
+                bool live[2][4];
+                if (!unmasked) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) rok[c][i] = !f && row_ok(pcc, 4 * g4 + i);
+                    for (int c = 0; c < 2; ++c)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) live[c][i] = full[c] || row_ok(cpc + 16 * c, 4 * g4 + i);
                 }
                 // row i of chunk c holds the key at logical position kp0 + 16 c + i
                 const int kp0 = (int)(cpc - off) + 4 * g4;
@@ -230,35 +244,41 @@ __global__ __launch_bounds__(64 * kPrefillWaves<G>) __attribute__((amdgpu_waves_
                             sacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[1][j]),
                                                                               as_bf16x8(qf[t][j]), sacc[1], 0, 0, 0);
                     }
+                    // raw scores (the scale is applied in the exponent: it is
+                    // positive, so the max commutes with it)
                     float s[8];
+                    if (unmasked) {
 #pragma unroll
-                    for (int c = 0; c < 2; ++c)
+                        for (int c = 0; c < 2; ++c)
 #pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            s[4 * c + i] = (full[c] || (rok[c][i] && kp0 + 16 * c + i <= qpos[t]))
-                                               ? sacc[c][i] * sl2 : kNegInf;
-                    float cm = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])),
-                                     fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
-                    cm = max_xor32(max_xor16(cm));
+                            for (int i = 0; i < 4; ++i) s[4 * c + i] = sacc[c][i];
+                    } else {
+#pragma unroll
+                        for (int c = 0; c < 2; ++c)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                s[4 * c + i] = (live[c][i] && kp0 + 16 * c + i <= qpos[t]) ? sacc[c][i] : kNegInf;
+                    }
+                    float cr = fmaxf(fmaxf(fmaxf(s[0], s[1]), s[2]), fmaxf(fmaxf(s[3], s[4]), s[5]));
+                    cr = fmaxf(cr, fmaxf(s[6], s[7]));
+                    const float cm = max_xor32(max_xor16(cr)) * sl2;
                     float alpha = 1.0f;
                     if (cm > m_h[t] + kLazy) {
                         alpha = m_h[t] == kNegInf ? 0.0f : fast_exp2(m_h[t] - cm);
                         m_h[t] = cm;
                     }
-                    // exp2(-inf - m) = 0 for the masked entries; a column with
+                    // exp2(-inf) = 0 for the masked entries; a column with
                     // no live key so far (m = -inf) subtracts 0 instead
                     const float mr = m_h[t] == kNegInf ? 0.0f : m_h[t];
                     uint32_t pp[4];
 #pragma unroll
                     for (int k = 0; k < 4; ++k)
-                        pp[k] = pack_bf16x2(fast_exp2(s[2 * k] - mr), fast_exp2(s[2 * k + 1] - mr));
-                    l_h[t] = fmaf(l_h[t], alpha,
-                                  ((bf16_lo(pp[0]) + bf16_hi(pp[0])) + (bf16_lo(pp[1]) + bf16_hi(pp[1]))) +
-                                      ((bf16_lo(pp[2]) + bf16_hi(pp[2])) + (bf16_lo(pp[3]) + bf16_hi(pp[3]))));
+                        pp[k] = pack_bf16x2(fast_exp2(fmaf(s[2 * k], sl2, -mr)), fast_exp2(fmaf(s[2 * k + 1], sl2, -mr)));
                     if (__builtin_amdgcn_readfirstlane((int)__any(alpha != 1.0f))) {
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
                             const float al = __shfl(alpha, 4 * g4 + i);
+                            accl[t][i] *= al;
 #pragma unroll
                             for (int sl = 0; sl < NV; ++sl) acc[t][sl][i] *= al;
                         }
@@ -285,6 +305,9 @@ __global__ __launch_bounds__(64 * kPrefillWaves<G>) __attribute__((amdgpu_waves_
                         acc[t][sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(pa[t]), as_bf16x8(vb),
                                                                              acc[t][sl], 0, 0, 0);
                 }
+#pragma unroll
+                for (int t = 0; t < QT; ++t)
+                    accl[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(pa[t]), as_bf16x8(ones), accl[t], 0, 0, 0);
             };
             u32x4 kring[NB][LPW];
             load_chunk(min(first, last), kring[0], 0);
@@ -331,13 +354,10 @@ __global__ __launch_bounds__(64 * kPrefillWaves<G>) __attribute__((amdgpu_waves_
     // out[row, hq, :] = acc / l for the tile's queries (sub-tile t, rows 4*g4 + i)
 #pragma unroll
     for (int t = 0; t < QT; ++t) {
-        float lt = l_h[t];
-        lt += __shfl_xor(lt, 16);
-        lt += __shfl_xor(lt, 32);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int qi = 16 * t + 4 * g4 + i;
-            const float lq = __shfl(lt, 4 * g4 + i);
+            const float lq = accl[t][i];
             if (qi < nq) {
                 uint16_t *o = reinterpret_cast<uint16_t *>(a.out) + ((row0 + q0 + qi) * a.num_q_heads + hq) * D + cn;
 #pragma unroll
