@@ -141,44 +141,66 @@ __global__ __launch_bounds__(64 * kPrefillWaves<G>) __attribute__((amdgpu_waves_
     const bool loader = w < NP;   // waves past NP load nothing (G > NP)
 
     if (pmax >= 0) {
+        // Positions are 32-bit from here on (flat positions of a table stay
+        // below 2^31; 64-bit arithmetic cost registers and spills here).
+        const int32_t off32 = (int32_t)off, pmin32 = (int32_t)pmin;
         // keys: logical 0 .. pmax = flat [off, off + pmax + 1), staged in pieces
-        const int64_t klo = off, khi = off + pmax + 1;
-        for (int64_t plo = klo & ~int64_t(15); plo < khi; plo += 16ll * a.seg_chunks) {
-            const int64_t phi = min(khi, plo + 16ll * a.seg_chunks);
-            const int64_t lo = max(plo, klo);
+        const int32_t klo = off32, khi = (int32_t)(off + pmax + 1);
+        for (int32_t plo = klo & ~15; plo < khi; plo += 16 * a.seg_chunks) {
+            const int32_t phi = min(khi, plo + 16 * a.seg_chunks);
+            const int32_t lo = max(plo, klo);
             __syncthreads();  // the previous piece's entries and tiles are done with
-            const int64_t jb0 = stage_entries(a, seq, lo, phi, bt_s);
-            const int64_t first = lo & ~int64_t(15);
-            const int64_t last = (phi - 1) & ~int64_t(15);
+            const int32_t jb0 = (int32_t)stage_entries(a, seq, lo, phi, bt_s);
+            const int32_t first = lo & ~15;
+            const int32_t last = (phi - 1) & ~15;
 
             // this wave's share of a chunk's loads: instructions i = w, w+G, ..
-            auto load_chunk = [&](int64_t pc, u32x4 *kx, int slot) {
+            auto load_chunk = [&](int32_t pc, u32x4 *kx, int slot) {
                 if (!loader) return;
                 char *dst = vtile[slot];
+                if constexpr (UB) {
+                    // the chunk lies in one block: a wave-uniform base
+                    const int32_t b = __builtin_amdgcn_readfirstlane(bt_s[(pc >> lbs) - jb0]);
+                    const int64_t base = (int64_t)(b >= 0 ? b : 0) * a.pool.block_stride +
+                                         (int64_t)(pc & (int32_t)bsm) * row_bytes;
+                    const char *kb = kh + base;
+                    const char *vb = vh + base;
 #pragma unroll
-                for (int k = 0; k < LPW; ++k) {
-                    const int i = w + NW * k;
-                    if (i < NP) {
-                        const int64_t p = pc + i + NP * trow;
-                        int32_t b;
-                        if constexpr (UB) {
-                            b = bt_s[(int)((pc >> lbs) - jb0)];
-                        } else {
-                            const bool in = p >= lo && p < phi;
-                            b = in ? bt_s[(int)((p >> lbs) - jb0)] : -1;
+                    for (int k = 0; k < LPW; ++k) {
+                        const int i = w + NW * k;
+                        if (i < NP) {
+                            const uint32_t o = (uint32_t)((i + NP * trow) * (int32_t)row_bytes + 16 * tpp);
+                            kx[k] = ld16(kb + o);
+                            lds_copy16(vb + o, dst + i * VSLAB);
                         }
-                        const int64_t o = (int64_t)(b >= 0 ? b : 0) * a.pool.block_stride + (p & bsm) * row_bytes +
-                                          16 * tpp;
-                        kx[k] = ld16(kh + o);
-                        lds_copy16(vh + o, dst + i * VSLAB);
+                    }
+                } else {
+#pragma unroll
+                    for (int k = 0; k < LPW; ++k) {
+                        const int i = w + NW * k;
+                        if (i < NP) {
+                            const int32_t p = pc + i + NP * trow;
+                            const bool in = p >= lo && p < phi;
+                            const int32_t b = in ? bt_s[(p >> lbs) - jb0] : -1;
+                            const int64_t o = (int64_t)(b >= 0 ? b : 0) * a.pool.block_stride +
+                                              (int64_t)(p & (int32_t)bsm) * row_bytes + 16 * tpp;
+                            kx[k] = ld16(kh + o);
+                            lds_copy16(vh + o, dst + i * VSLAB);
+                        }
                     }
                 }
             };
             // rows of chunk pc that hold a token of the sequence
-            auto row_ok = [&](int64_t pc, int row) -> bool {
-                const int64_t p = pc + row;
+            auto row_ok = [&](int32_t pc, int row) -> bool {
+                const int32_t p = pc + row;
                 if (p < lo || p >= phi) return false;
-                return bt_s[(int)((p >> lbs) - jb0)] >= 0;
+                return bt_s[(p >> lbs) - jb0] >= 0;
+            };
+            // every row of chunk pc holds a token (wave-uniform; block
+            // size >= 16 only)
+            auto chunk_live = [&](int32_t pc) -> bool {
+                if constexpr (UB) return pc >= lo && pc + 16 <= phi && bt_s[(pc >> lbs) - jb0] >= 0;
+                return false;
             };
 
             // Two chunks per stage and one barrier per stage: a ring of four
@@ -193,7 +215,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves<G>) __attribute__((amdgpu_waves_
             // operand (A) and V operand (B) both list the first chunk's rows
             // then the second's (the same relabelling of the 32 keys in
             // both operands, so the sum is unchanged).
-            auto compute_stage = [&](int64_t cpc, int qs) {
+            auto compute_stage = [&](int32_t cpc, int qs) {
                 const bool has1 = cpc + 16 <= last;   // wave-uniform
                 u32x4 kf[2][KS];
 #pragma unroll
@@ -210,14 +232,8 @@ __global__ __launch_bounds__(64 * kPrefillWaves<G>) __attribute__((amdgpu_waves_
                 bool full[2];
 #pragma unroll
                 for (int c = 0; c < 2; ++c) {
-                    const int64_t pcc = cpc + 16 * c;
-                    bool f = nq > 0 && pcc >= lo && pcc + 16 <= phi && pcc + 15 - off <= pmin;
-                    if constexpr (UB) {
-                        f = f && bt_s[(int)((pcc >> lbs) - jb0)] >= 0;
-                    } else {
-                        f = false;   // rows may sit in different blocks
-                    }
-                    full[c] = f;
+                    const int32_t pcc = cpc + 16 * c;
+                    full[c] = nq > 0 && pcc + 15 - off32 <= pmin32 && chunk_live(pcc);
                 }
                 const bool unmasked = full[0] && full[1];   // (full[1] is false without a second chunk)
                 bool live[2][4];
@@ -228,7 +244,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves<G>) __attribute__((amdgpu_waves_
                         for (int i = 0; i < 4; ++i) live[c][i] = full[c] || row_ok(cpc + 16 * c, 4 * g4 + i);
                 }
                 // row i of chunk c holds the key at logical position kp0 + 16 c + i
-                const int kp0 = (int)(cpc - off) + 4 * g4;
+                const int kp0 = cpc - off32 + 4 * g4;
                 u32x4 pa[QT];
 #pragma unroll
                 for (int t = 0; t < QT; ++t) {
@@ -313,7 +329,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves<G>) __attribute__((amdgpu_waves_
             load_chunk(min(first, last), kring[0], 0);
             load_chunk(min(first + 16, last), kring[1], 1);
             bool done = false;
-            for (int64_t pc = first; !done;) {
+            for (int32_t pc = first; !done;) {
 #pragma unroll
                 for (int st = 0; st < 2; ++st) {
                     if (!done) {
@@ -324,13 +340,14 @@ __global__ __launch_bounds__(64 * kPrefillWaves<G>) __attribute__((amdgpu_waves_
 #pragma unroll
                             for (int c = 0; c < 2; ++c) {
                                 const int q = 2 * st + c;
+                                const bool whole = chunk_live(pc + 16 * c);   // no V row to zero
 #pragma unroll
                                 for (int k = 0; k < LPW; ++k) {
                                     const int i = w + NW * k;
                                     if (i < NP) {
                                         *reinterpret_cast<u32x4 *>(ktile[q] + (i + NP * trow) * KROW + 16 * tpp) =
                                             kring[q][k];
-                                        if (!row_ok(pc + 16 * c, i + NP * trow))
+                                        if (!whole && !row_ok(pc + 16 * c, i + NP * trow))
                                             *reinterpret_cast<u32x4 *>(vtile[q] + i * VSLAB + 16 * lane) =
                                                 u32x4{0, 0, 0, 0};
                                     }
