@@ -376,10 +376,13 @@ __global__ __launch_bounds__(64 * kPrefillWaves<G>) __attribute__((amdgpu_waves_
             const int qi = 16 * t + 4 * g4 + i;
             const float lq = accl[t][i];
             if (qi < nq) {
+                // one reciprocal per row and the hardware's nearest-even
+                // conversion (a division and a software rounding per element
+                // were a sixth of the kernel's VALU instructions)
+                const float rl = lq > 0.0f ? __builtin_amdgcn_rcpf(lq) : 0.0f;
                 uint16_t *o = reinterpret_cast<uint16_t *>(a.out) + ((row0 + q0 + qi) * a.num_q_heads + hq) * D + cn;
 #pragma unroll
-                for (int sl = 0; sl < NV; ++sl)
-                    o[16 * sl] = (uint16_t)f32_to_bf16_bits(lq > 0.0f ? acc[t][sl][i] / lq : 0.0f);
+                for (int sl = 0; sl < NV; ++sl) o[16 * sl] = (uint16_t)pack_bf16x2(acc[t][sl][i] * rl, 0.0f);
             }
         }
     }
