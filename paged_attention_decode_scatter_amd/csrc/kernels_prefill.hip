@@ -60,16 +60,18 @@ __global__ __launch_bounds__(64 * kPrefillWaves<G>) __attribute__((amdgpu_waves_
     PrefillArgs a) {
     using S = MfmaShape<D>;
     constexpr int ROWB = S::ROWB, PPR = S::PPR, NP = S::NP, KS = S::KS, NV = S::NV;
-    constexpr int VSLAB = S::VSLAB, VTILE = S::VTILE, KROW = S::KROW, KTILE = S::KTILE;
-    constexpr int NB = kPrefillRing;            // chunks in the LDS ring
+    constexpr int VSLAB = S::VSLAB, VTILE = S::VTILE;
+    constexpr int NB = kPrefillRing;            // chunks in the LDS ring (3 stages of 2)
+    constexpr int KFRAG = KS * 1024;            // one chunk's K in A-operand fragment order
     constexpr int NW = kPrefillWaves<G>;        // wavefronts: G heads x NW / G query groups
-    constexpr int LPW = (NP + NW - 1) / NW;     // tile-load instructions per loading wave
+    constexpr int LPW = (NP + NW - 1) / NW;     // V tile-load instructions per wave (at most)
+    constexpr int KPW = (KS + NW - 1) / NW;     // K fragment copies per wave (at most)
     constexpr int QW = kPrefillWaveQueries<D, G>;   // queries per wavefront
     constexpr int QT = QW / 16;                 // 16-query sub-tiles per wavefront
     constexpr float kLazy = 8.0f;
     typedef short s16x4 __attribute__((ext_vector_type(4)));
     __shared__ int32_t bt_s[kBtLds];
-    __shared__ __attribute__((aligned(16))) char ktile[NB][KTILE];
+    __shared__ __attribute__((aligned(16))) char kfrag[NB][KFRAG];
     __shared__ __attribute__((aligned(16))) char vtile[NB][VTILE];
 
     // (kv head, sequence, tile), tile fastest; neighbours share an XCD so
@@ -138,7 +140,10 @@ __global__ __launch_bounds__(64 * kPrefillWaves<G>) __attribute__((amdgpu_waves_
     const char *vh = a.pool.v + a.pool.layer_off + (int64_t)hk * ROWB;
     const int trow = lane / PPR;
     const int tpp = lane % PPR;
-    const bool loader = w < NP;   // waves past NP load nothing (G > NP)
+    // the wavefronts share a chunk's KS + NP copy instructions round robin,
+    // K fragments first: K fragment j by wave j % NW, V instruction i by
+    // wave (KS + i) % NW; this wave's first V instruction:
+    const int iv0 = ((w - KS) % NW + NW) % NW;
 
     if (pmax >= 0) {
         // Positions are 32-bit from here on (flat positions of a table stay
@@ -154,10 +159,14 @@ __global__ __launch_bounds__(64 * kPrefillWaves<G>) __attribute__((amdgpu_waves_
             const int32_t first = lo & ~15;
             const int32_t last = (phi - 1) & ~15;
 
-            // this wave's share of a chunk's loads: instructions i = w, w+G, ..
-            auto load_chunk = [&](int32_t pc, u32x4 *kx, int slot) {
-                if (!loader) return;
-                char *dst = vtile[slot];
+            // This wave's share of a chunk's loads, all global -> LDS: K
+            // fragments j = w, w + NW, .. (lane (cn, g4) copies the 16 bytes
+            // of row cn it later reads as its A operand for step j, so the
+            // tile is in fragment order and its reads are contiguous) and V
+            // tile-load instructions i = iv0, iv0 + NW, .. (row layout).
+            auto load_chunk = [&](int32_t pc, int slot) {
+                char *kd = kfrag[slot];
+                char *vd = vtile[slot];
                 if constexpr (UB) {
                     // the chunk lies in one block: a wave-uniform base
                     const int32_t b = __builtin_amdgcn_readfirstlane(bt_s[(pc >> lbs) - jb0]);
@@ -166,26 +175,40 @@ __global__ __launch_bounds__(64 * kPrefillWaves<G>) __attribute__((amdgpu_waves_
                     const char *kb = kh + base;
                     const char *vb = vh + base;
 #pragma unroll
+                    for (int k = 0; k < KPW; ++k) {
+                        const int j = w + NW * k;
+                        if (j < KS)
+                            lds_copy16(kb + (uint32_t)(cn * (int32_t)row_bytes + 16 * g4 + 64 * j), kd + 1024 * j);
+                    }
+#pragma unroll
                     for (int k = 0; k < LPW; ++k) {
-                        const int i = w + NW * k;
-                        if (i < NP) {
-                            const uint32_t o = (uint32_t)((i + NP * trow) * (int32_t)row_bytes + 16 * tpp);
-                            kx[k] = ld16(kb + o);
-                            lds_copy16(vb + o, dst + i * VSLAB);
-                        }
+                        const int i = iv0 + NW * k;
+                        if (i < NP)
+                            lds_copy16(vb + (uint32_t)((i + NP * trow) * (int32_t)row_bytes + 16 * tpp), vd + i * VSLAB);
                     }
                 } else {
 #pragma unroll
+                    for (int k = 0; k < KPW; ++k) {
+                        const int j = w + NW * k;
+                        if (j < KS) {
+                            const int32_t p = pc + cn;
+                            const bool in = p >= lo && p < phi;
+                            const int32_t b = in ? bt_s[(p >> lbs) - jb0] : -1;
+                            const int64_t o = (int64_t)(b >= 0 ? b : 0) * a.pool.block_stride +
+                                              (int64_t)(p & (int32_t)bsm) * row_bytes + 16 * g4 + 64 * j;
+                            lds_copy16(kh + o, kd + 1024 * j);
+                        }
+                    }
+#pragma unroll
                     for (int k = 0; k < LPW; ++k) {
-                        const int i = w + NW * k;
+                        const int i = iv0 + NW * k;
                         if (i < NP) {
                             const int32_t p = pc + i + NP * trow;
                             const bool in = p >= lo && p < phi;
                             const int32_t b = in ? bt_s[(p >> lbs) - jb0] : -1;
                             const int64_t o = (int64_t)(b >= 0 ? b : 0) * a.pool.block_stride +
                                               (int64_t)(p & (int32_t)bsm) * row_bytes + 16 * tpp;
-                            kx[k] = ld16(kh + o);
-                            lds_copy16(vh + o, dst + i * VSLAB);
+                            lds_copy16(vh + o, vd + i * VSLAB);
                         }
                     }
                 }
@@ -203,11 +226,10 @@ __global__ __launch_bounds__(64 * kPrefillWaves<G>) __attribute__((amdgpu_waves_
                 return false;
             };
 
-            // Two chunks per stage and one barrier per stage: a ring of four
-            // chunk slots holds two stages, one being computed while the next
-            // one's loads are in flight.  (A loop over more chunks per stage
-            // spills: K passes through registers.)
-            static_assert(NB == 4, "two stages of two chunks");
+            // Two chunks per stage and one barrier per stage: a ring of six
+            // chunk slots holds three stages, one being computed while the
+            // next two stages' loads are in flight.
+            static_assert(NB == 6, "three stages of two chunks");
             // One softmax step over the stage's two chunks, cpc (slot qs)
             // and cpc + 16 (slot qs + 1).  Lane group g4 holds the scores of
             // rows 4*g4 .. 4*g4+3 of each chunk; P.V contracts those 8 keys
@@ -222,7 +244,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves<G>) __attribute__((amdgpu_waves_
                 for (int c = 0; c < 2; ++c)
 #pragma unroll
                     for (int j = 0; j < KS; ++j)
-                        kf[c][j] = *reinterpret_cast<const u32x4 *>(ktile[qs + c] + cn * KROW + 16 * g4 + 64 * j);
+                        kf[c][j] = *reinterpret_cast<const u32x4 *>(kfrag[qs + c] + 1024 * j + 16 * lane);
                 // A chunk needs no mask when all its rows are live tokens at
                 // or before the wavefront's first query.  When both chunks are
                 // such (every stage below the causal diagonal and inside the
@@ -325,41 +347,51 @@ __global__ __launch_bounds__(64 * kPrefillWaves<G>) __attribute__((amdgpu_waves_
                 for (int t = 0; t < QT; ++t)
                     accl[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(pa[t]), as_bf16x8(ones), accl[t], 0, 0, 0);
             };
-            u32x4 kring[NB][LPW];
-            load_chunk(min(first, last), kring[0], 0);
-            load_chunk(min(first + 16, last), kring[1], 1);
-            bool done = false;
-            for (int32_t pc = first; !done;) {
+            // the loads of stage st (chunks first + 32 st, + 16; a second
+            // chunk past the last re-reads it, masked in compute_stage)
+            const int nst = ((last - first) >> 5) + 1;
+            auto issue = [&](int st, int slot0) {
+                const int32_t pc = first + 32 * st;
+                load_chunk(pc, slot0);
+                load_chunk(min(pc + 16, last), slot0 + 1);
+            };
+            // this wave's vector-memory operations per stage (wave-uniform)
+            const int ops = 2 * ((KS + NW - 1 - w) / NW + (NP + NW - 1 - iv0) / NW);
+            auto wait_stage = [&](bool next_in_flight) {
+                const int n = next_in_flight ? ops : 0;
+                // the copy engine's LDS writes are not tracked by the
+                // compiler: an explicit wait, immediate per case
+                if (n >= 8) __builtin_amdgcn_s_waitcnt(8 | (0x7 << 4) | (0xF << 8));
+                else if (n >= 4) __builtin_amdgcn_s_waitcnt(4 | (0x7 << 4) | (0xF << 8));
+                else if (n >= 2) __builtin_amdgcn_s_waitcnt(2 | (0x7 << 4) | (0xF << 8));
+                else __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xF << 8));
+            };
+            issue(0, 0);
+            if (nst > 1) issue(1, 2);
+            for (int st0 = 0; st0 < nst; st0 += 3) {
 #pragma unroll
-                for (int st = 0; st < 2; ++st) {
-                    if (!done) {
-                        // this stage's loads done (the only ones in flight)
-                        if (loader) __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));
+                for (int r = 0; r < 3; ++r) {
+                    const int st = st0 + r;
+                    if (st < nst) {
+                        const int32_t pc = first + 32 * st;
+                        wait_stage(st + 1 < nst);   // this stage's loads have landed
                         wave_lds_order();
-                        if (loader) {
+                        // zero the V rows of this wave's pieces that hold no live token
 #pragma unroll
-                            for (int c = 0; c < 2; ++c) {
-                                const int q = 2 * st + c;
-                                const bool whole = chunk_live(pc + 16 * c);   // no V row to zero
+                        for (int c = 0; c < 2; ++c) {
+                            if (!chunk_live(pc + 16 * c)) {
 #pragma unroll
                                 for (int k = 0; k < LPW; ++k) {
-                                    const int i = w + NW * k;
-                                    if (i < NP) {
-                                        *reinterpret_cast<u32x4 *>(ktile[q] + (i + NP * trow) * KROW + 16 * tpp) =
-                                            kring[q][k];
-                                        if (!whole && !row_ok(pc + 16 * c, i + NP * trow))
-                                            *reinterpret_cast<u32x4 *>(vtile[q] + i * VSLAB + 16 * lane) =
-                                                u32x4{0, 0, 0, 0};
-                                    }
+                                    const int i = iv0 + NW * k;
+                                    if (i < NP && !row_ok(pc + 16 * c, i + NP * trow))
+                                        *reinterpret_cast<u32x4 *>(vtile[2 * r + c] + i * VSLAB + 16 * lane) =
+                                            u32x4{0, 0, 0, 0};
                                 }
                             }
                         }
-                        __syncthreads();  // the stage's tiles complete; the other stage's slots free
-                        load_chunk(min(pc + 32, last), kring[2 - 2 * st], 2 - 2 * st);
-                        load_chunk(min(pc + 48, last), kring[3 - 2 * st], 3 - 2 * st);
-                        compute_stage(pc, 2 * st);
-                        pc += 32;
-                        done = pc > last;
+                        __syncthreads();  // the stage's tiles complete; stage st - 1's slots free
+                        if (st + 2 < nst) issue(st + 2, 2 * ((r + 2) % 3));
+                        compute_stage(pc, 2 * r);
                     }
                 }
             }

@@ -185,11 +185,11 @@ inline int prefill_waves(int64_t group) { return group > 4 ? (int)group : 4; }
 #define PKV_PREFILL_WQ128 48
 #endif
 #ifndef PKV_PREFILL_RING
-#define PKV_PREFILL_RING 4
+#define PKV_PREFILL_RING 6
 #endif
-// key chunks staged in LDS: two stages of two 16-key chunks, one barrier
-// per stage (6.30 ms against 6.61 ms with one chunk per barrier and a ring
-// of 3, same process)
+// key chunks staged in LDS: three stages of two 16-key chunks, one barrier
+// per stage, loads issued two stages ahead (two chunks per barrier: 6.30 ms
+// against 6.61 ms with one chunk per barrier and a ring of 3, same process)
 constexpr int kPrefillRing = PKV_PREFILL_RING;
 template <int D, int G>
 inline constexpr int kPrefillWaveQueries = D == 64 ? PKV_PREFILL_WQ64 : PKV_PREFILL_WQ128;
