@@ -69,6 +69,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves<G>) __attribute__((amdgpu_waves_
     constexpr int QW = kPrefillWaveQueries<D, G>;   // queries per wavefront
     constexpr int QT = QW / 16;                 // 16-query sub-tiles per wavefront
     constexpr float kLazy = 8.0f;
+    constexpr float kMinRef = -0x1p127f;
     typedef short s16x4 __attribute__((ext_vector_type(4)));
     __shared__ int32_t bt_s[kBtLds];
     __shared__ __attribute__((aligned(16))) char kfrag[NB][KFRAG];
@@ -120,12 +121,16 @@ __global__ __launch_bounds__(64 * kPrefillWaves<G>) __attribute__((amdgpu_waves_
     // O rows 4*g4 + i, columns 16 sl + cn; accl[t]: the denominators of the
     // same rows, accumulated on the matrix core as P . (a column of ones),
     // so they sum exactly the bf16 P values the P . V product uses and land
-    // in the output rows' layout
+    // in the output rows' layout.  m_h starts at a finite value below any
+    // score (kMinRef): the first live score of a column always moves it,
+    // with the old contribution scaled by exp2(kMinRef - m) = 0, and masked
+    // scores (-inf) still give exp2(-inf) = 0, so no -inf special case
+    // remains in the loop.
     float m_h[QT];
     f32x4 acc[QT][NV], accl[QT];
 #pragma unroll
     for (int t = 0; t < QT; ++t) {
-        m_h[t] = kNegInf;
+        m_h[t] = kMinRef;
         accl[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int sl = 0; sl < NV; ++sl) acc[t][sl] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -238,7 +243,6 @@ __global__ __launch_bounds__(64 * kPrefillWaves<G>) __attribute__((amdgpu_waves_
             // then the second's (the same relabelling of the 32 keys in
             // both operands, so the sum is unchanged).
             auto compute_stage = [&](int32_t cpc, int qs) {
-                const bool has1 = cpc + 16 <= last;   // wave-uniform
                 u32x4 kf[2][KS];
 #pragma unroll
                 for (int c = 0; c < 2; ++c)
@@ -250,14 +254,16 @@ __global__ __launch_bounds__(64 * kPrefillWaves<G>) __attribute__((amdgpu_waves_
                 // such (every stage below the causal diagonal and inside the
                 // piece: nearly all of them), the stage takes the unmasked
                 // path (wave-uniform branch); else the rows' liveness is
-                // found once for the stage and each score is masked.
+                // found once for the stage and each score is masked.  A
+                // stage without a second chunk re-reads the last one into
+                // the second slot, whose rows then fail row_ok: masked.
                 bool full[2];
 #pragma unroll
                 for (int c = 0; c < 2; ++c) {
                     const int32_t pcc = cpc + 16 * c;
                     full[c] = nq > 0 && pcc + 15 - off32 <= pmin32 && chunk_live(pcc);
                 }
-                const bool unmasked = full[0] && full[1];   // (full[1] is false without a second chunk)
+                const bool unmasked = full[0] && full[1];
                 bool live[2][4];
                 if (!unmasked) {
 #pragma unroll
@@ -271,48 +277,45 @@ __global__ __launch_bounds__(64 * kPrefillWaves<G>) __attribute__((amdgpu_waves_
 #pragma unroll
                 for (int t = 0; t < QT; ++t) {
                     // S^T: lane holds S[token 16 c + 4*g4 + i][query 16 t + cn]
-                    f32x4 sacc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+                    // (raw scores: the scale is applied in the exponent; it is
+                    // positive, so maxima commute with it)
+                    f32x4 sacc[2];
 #pragma unroll
-                    for (int j = 0; j < KS; ++j)
-                        sacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[0][j]), as_bf16x8(qf[t][j]),
-                                                                          sacc[0], 0, 0, 0);
-                    if (has1) {
+                    for (int c = 0; c < 2; ++c) {
+                        sacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[c][0]), as_bf16x8(qf[t][0]),
+                                                                          f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
 #pragma unroll
-                        for (int j = 0; j < KS; ++j)
-                            sacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[1][j]),
-                                                                              as_bf16x8(qf[t][j]), sacc[1], 0, 0, 0);
+                        for (int j = 1; j < KS; ++j)
+                            sacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[c][j]),
+                                                                              as_bf16x8(qf[t][j]), sacc[c], 0, 0, 0);
                     }
-                    // raw scores (the scale is applied in the exponent: it is
-                    // positive, so the max commutes with it)
-                    float s[8];
-                    if (unmasked) {
-#pragma unroll
-                        for (int c = 0; c < 2; ++c)
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) s[4 * c + i] = sacc[c][i];
-                    } else {
+                    if (!unmasked) {
 #pragma unroll
                         for (int c = 0; c < 2; ++c)
 #pragma unroll
                             for (int i = 0; i < 4; ++i)
-                                s[4 * c + i] = (live[c][i] && kp0 + 16 * c + i <= qpos[t]) ? sacc[c][i] : kNegInf;
+                                sacc[c][i] = (live[c][i] && kp0 + 16 * c + i <= qpos[t]) ? sacc[c][i] : kNegInf;
                     }
-                    float cr = fmaxf(fmaxf(fmaxf(s[0], s[1]), s[2]), fmaxf(fmaxf(s[3], s[4]), s[5]));
-                    cr = fmaxf(cr, fmaxf(s[6], s[7]));
-                    const float cm = max_xor32(max_xor16(cr)) * sl2;
-                    float alpha = 1.0f;
-                    if (cm > m_h[t] + kLazy) {
-                        alpha = m_h[t] == kNegInf ? 0.0f : fast_exp2(m_h[t] - cm);
-                        m_h[t] = cm;
-                    }
-                    // exp2(-inf) = 0 for the masked entries; a column with
-                    // no live key so far (m = -inf) subtracts 0 instead
-                    const float mr = m_h[t] == kNegInf ? 0.0f : m_h[t];
-                    uint32_t pp[4];
-#pragma unroll
-                    for (int k = 0; k < 4; ++k)
-                        pp[k] = pack_bf16x2(fast_exp2(fmaf(s[2 * k], sl2, -mr)), fast_exp2(fmaf(s[2 * k + 1], sl2, -mr)));
-                    if (__builtin_amdgcn_readfirstlane((int)__any(alpha != 1.0f))) {
+                    // The reference max moves only when a column's max
+                    // exceeds it by more than kLazy (exp2 domain).  A column's
+                    // max does so exactly when one of its lanes' maxima does
+                    // (the scaling is monotone), so the lanes' own maxima
+                    // decide whether the column reduction is needed at all.
+                    // (maximum: the NaN-propagating max, one v_maximum3_f32
+                    // per three inputs without quieting the inputs first)
+                    const float lm = __builtin_elementwise_maximum(
+                        __builtin_elementwise_maximum(
+                            __builtin_elementwise_maximum(__builtin_elementwise_maximum(sacc[0][0], sacc[0][1]), sacc[0][2]),
+                            __builtin_elementwise_maximum(__builtin_elementwise_maximum(sacc[0][3], sacc[1][0]), sacc[1][1])),
+                        __builtin_elementwise_maximum(sacc[1][2], sacc[1][3]));
+                    const float thr = m_h[t] + kLazy;
+                    if (__builtin_amdgcn_ballot_w64(lm * sl2 > thr) != 0) {   // rare; wave-uniform
+                        const float cm = max_xor32(max_xor16(lm)) * sl2;
+                        float alpha = 1.0f;
+                        if (cm > thr) {
+                            alpha = fast_exp2(m_h[t] - cm);
+                            m_h[t] = cm;
+                        }
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
                             const float al = __shfl(alpha, 4 * g4 + i);
@@ -321,6 +324,12 @@ __global__ __launch_bounds__(64 * kPrefillWaves<G>) __attribute__((amdgpu_waves_
                             for (int sl = 0; sl < NV; ++sl) acc[t][sl][i] *= al;
                         }
                     }
+                    // exp2(-inf) = 0 for the masked entries
+                    uint32_t pp[4];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k)
+                        pp[k] = pack_bf16x2(fast_exp2(fmaf(sacc[k >> 1][2 * (k & 1)], sl2, -m_h[t])),
+                                            fast_exp2(fmaf(sacc[k >> 1][2 * (k & 1) + 1], sl2, -m_h[t])));
                     pa[t] = u32x4{pp[0], pp[1], pp[2], pp[3]};
                 }
                 // V operand of slice sl: the transposed 4-row fragments of
@@ -368,32 +377,31 @@ __global__ __launch_bounds__(64 * kPrefillWaves<G>) __attribute__((amdgpu_waves_
             };
             issue(0, 0);
             if (nst > 1) issue(1, 2);
-            for (int st0 = 0; st0 < nst; st0 += 3) {
+            // one loop body (no unrolling over the ring: the copies' register
+            // allocations differed and moved registers between them); r is
+            // stage st's ring position (slots 2r, 2r + 1), wave-uniform
+            int r = 0;
+            for (int st = 0; st < nst; ++st) {
+                const int32_t pc = first + 32 * st;
+                wait_stage(st + 1 < nst);   // this stage's loads have landed
+                wave_lds_order();
+                // zero the V rows of this wave's pieces that hold no live token
 #pragma unroll
-                for (int r = 0; r < 3; ++r) {
-                    const int st = st0 + r;
-                    if (st < nst) {
-                        const int32_t pc = first + 32 * st;
-                        wait_stage(st + 1 < nst);   // this stage's loads have landed
-                        wave_lds_order();
-                        // zero the V rows of this wave's pieces that hold no live token
+                for (int c = 0; c < 2; ++c) {
+                    if (!chunk_live(pc + 16 * c)) {
 #pragma unroll
-                        for (int c = 0; c < 2; ++c) {
-                            if (!chunk_live(pc + 16 * c)) {
-#pragma unroll
-                                for (int k = 0; k < LPW; ++k) {
-                                    const int i = iv0 + NW * k;
-                                    if (i < NP && !row_ok(pc + 16 * c, i + NP * trow))
-                                        *reinterpret_cast<u32x4 *>(vtile[2 * r + c] + i * VSLAB + 16 * lane) =
-                                            u32x4{0, 0, 0, 0};
-                                }
-                            }
+                        for (int k = 0; k < LPW; ++k) {
+                            const int i = iv0 + NW * k;
+                            if (i < NP && !row_ok(pc + 16 * c, i + NP * trow))
+                                *reinterpret_cast<u32x4 *>(vtile[2 * r + c] + i * VSLAB + 16 * lane) =
+                                    u32x4{0, 0, 0, 0};
                         }
-                        __syncthreads();  // the stage's tiles complete; stage st - 1's slots free
-                        if (st + 2 < nst) issue(st + 2, 2 * ((r + 2) % 3));
-                        compute_stage(pc, 2 * r);
                     }
                 }
+                __syncthreads();  // the stage's tiles complete; stage st - 1's slots free
+                if (st + 2 < nst) issue(st + 2, r == 0 ? 4 : 2 * r - 2);
+                compute_stage(pc, 2 * r);
+                r = r == 2 ? 0 : r + 1;
             }
             // drain the copies before the tiles are restaged or released
             __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xF << 8));
