@@ -273,46 +273,62 @@ __global__ __launch_bounds__(64 * kPrefillWaves<G>) __attribute__((amdgpu_waves_
                 }
                 // row i of chunk c holds the key at logical position kp0 + 16 c + i
                 const int kp0 = cpc - off32 + 4 * g4;
-                u32x4 pa[QT];
+                // S^T of every sub-tile first (independent accumulation
+                // chains back to back on the matrix core): lane holds
+                // S[token 16 c + 4*g4 + i][query 16 t + cn] (raw scores: the
+                // scale is applied in the exponent; it is positive, so
+                // maxima commute with it)
+                f32x4 sacc[QT][2];
 #pragma unroll
-                for (int t = 0; t < QT; ++t) {
-                    // S^T: lane holds S[token 16 c + 4*g4 + i][query 16 t + cn]
-                    // (raw scores: the scale is applied in the exponent; it is
-                    // positive, so maxima commute with it)
-                    f32x4 sacc[2];
+                for (int t = 0; t < QT; ++t)
 #pragma unroll
-                    for (int c = 0; c < 2; ++c) {
-                        sacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[c][0]), as_bf16x8(qf[t][0]),
-                                                                          f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+                    for (int c = 0; c < 2; ++c)
+                        sacc[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            as_bf16x8(kf[c][0]), as_bf16x8(qf[t][0]), f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
 #pragma unroll
-                        for (int j = 1; j < KS; ++j)
-                            sacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[c][j]),
-                                                                              as_bf16x8(qf[t][j]), sacc[c], 0, 0, 0);
-                    }
-                    if (!unmasked) {
+                for (int j = 1; j < KS; ++j)
+#pragma unroll
+                    for (int t = 0; t < QT; ++t)
+#pragma unroll
+                        for (int c = 0; c < 2; ++c)
+                            sacc[t][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[c][j]),
+                                                                                 as_bf16x8(qf[t][j]), sacc[t][c], 0, 0, 0);
+                if (!unmasked) {
+#pragma unroll
+                    for (int t = 0; t < QT; ++t)
 #pragma unroll
                         for (int c = 0; c < 2; ++c)
 #pragma unroll
                             for (int i = 0; i < 4; ++i)
-                                sacc[c][i] = (live[c][i] && kp0 + 16 * c + i <= qpos[t]) ? sacc[c][i] : kNegInf;
-                    }
-                    // The reference max moves only when a column's max
-                    // exceeds it by more than kLazy (exp2 domain).  A column's
-                    // max does so exactly when one of its lanes' maxima does
-                    // (the scaling is monotone), so the lanes' own maxima
-                    // decide whether the column reduction is needed at all.
-                    // (maximum: the NaN-propagating max, one v_maximum3_f32
-                    // per three inputs without quieting the inputs first)
-                    const float lm = __builtin_elementwise_maximum(
+                                sacc[t][c][i] =
+                                    (live[c][i] && kp0 + 16 * c + i <= qpos[t]) ? sacc[t][c][i] : kNegInf;
+                }
+                // The reference max moves only when a column's max exceeds
+                // it by more than kLazy (exp2 domain).  A column's max does
+                // so exactly when one of its lanes' maxima does (the scaling
+                // is monotone), so the lanes' own maxima decide, in one
+                // wave-wide vote for all sub-tiles, whether the column
+                // reductions are needed at all.  (maximum: the
+                // NaN-propagating max, one v_maximum3_f32 per three inputs
+                // without quieting them first.)
+                float lm[QT];
+                bool up = false;
+#pragma unroll
+                for (int t = 0; t < QT; ++t) {
+                    const f32x4 &x = sacc[t][0], &y = sacc[t][1];
+                    lm[t] = __builtin_elementwise_maximum(
                         __builtin_elementwise_maximum(
-                            __builtin_elementwise_maximum(__builtin_elementwise_maximum(sacc[0][0], sacc[0][1]), sacc[0][2]),
-                            __builtin_elementwise_maximum(__builtin_elementwise_maximum(sacc[0][3], sacc[1][0]), sacc[1][1])),
-                        __builtin_elementwise_maximum(sacc[1][2], sacc[1][3]));
-                    const float thr = m_h[t] + kLazy;
-                    if (__builtin_amdgcn_ballot_w64(lm * sl2 > thr) != 0) {   // rare; wave-uniform
-                        const float cm = max_xor32(max_xor16(lm)) * sl2;
+                            __builtin_elementwise_maximum(__builtin_elementwise_maximum(x[0], x[1]), x[2]),
+                            __builtin_elementwise_maximum(__builtin_elementwise_maximum(x[3], y[0]), y[1])),
+                        __builtin_elementwise_maximum(y[2], y[3]));
+                    up = up || lm[t] * sl2 > m_h[t] + kLazy;
+                }
+                if (__builtin_amdgcn_ballot_w64(up) != 0) {   // rare; wave-uniform
+#pragma unroll
+                    for (int t = 0; t < QT; ++t) {
+                        const float cm = max_xor32(max_xor16(lm[t])) * sl2;
                         float alpha = 1.0f;
-                        if (cm > thr) {
+                        if (cm > m_h[t] + kLazy) {
                             alpha = fast_exp2(m_h[t] - cm);
                             m_h[t] = cm;
                         }
@@ -324,12 +340,17 @@ __global__ __launch_bounds__(64 * kPrefillWaves<G>) __attribute__((amdgpu_waves_
                             for (int sl = 0; sl < NV; ++sl) acc[t][sl][i] *= al;
                         }
                     }
-                    // exp2(-inf) = 0 for the masked entries
+                }
+                // P = exp2(S * scale - m) in bf16 (exp2(-inf) = 0 for the
+                // masked entries)
+                u32x4 pa[QT];
+#pragma unroll
+                for (int t = 0; t < QT; ++t) {
                     uint32_t pp[4];
 #pragma unroll
                     for (int k = 0; k < 4; ++k)
-                        pp[k] = pack_bf16x2(fast_exp2(fmaf(sacc[k >> 1][2 * (k & 1)], sl2, -m_h[t])),
-                                            fast_exp2(fmaf(sacc[k >> 1][2 * (k & 1) + 1], sl2, -m_h[t])));
+                        pp[k] = pack_bf16x2(fast_exp2(fmaf(sacc[t][k >> 1][2 * (k & 1)], sl2, -m_h[t])),
+                                            fast_exp2(fmaf(sacc[t][k >> 1][2 * (k & 1) + 1], sl2, -m_h[t])));
                     pa[t] = u32x4{pp[0], pp[1], pp[2], pp[3]};
                 }
                 // V operand of slice sl: the transposed 4-row fragments of
