@@ -145,6 +145,13 @@ __global__ __launch_bounds__(64 * kPrefillWaves<G>) __attribute__((amdgpu_waves_
     const char *vh = a.pool.v + a.pool.layer_off + (int64_t)hk * ROWB;
     const int trow = lane / PPR;
     const int tpp = lane % PPR;
+    // V tile swizzle (head_dim 128): a row at an odd position of its slab
+    // holds its 16-byte pieces in the order piece ^ 8, so that the
+    // transposed reads of lane groups g4 = 2h and 2h + 1 (rows at positions
+    // 2h and 2h + 1, the same slabs) fall in opposite 128-byte halves of
+    // the banks.  A copy lane fetches the piece it stores (same row bytes).
+    constexpr bool kVSwz = PKV_PREFILL_VSWZ && D == 128;
+    const int tsrc = kVSwz ? (tpp ^ (8 * (trow & 1))) : tpp;
     // the wavefronts share a chunk's KS + NP copy instructions round robin,
     // K fragments first: K fragment j by wave j % NW, V instruction i by
     // wave (KS + i) % NW; this wave's first V instruction:
@@ -189,7 +196,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves<G>) __attribute__((amdgpu_waves_
                     for (int k = 0; k < LPW; ++k) {
                         const int i = iv0 + NW * k;
                         if (i < NP)
-                            lds_copy16(vb + (uint32_t)((i + NP * trow) * (int32_t)row_bytes + 16 * tpp), vd + i * VSLAB);
+                            lds_copy16(vb + (uint32_t)((i + NP * trow) * (int32_t)row_bytes + 16 * tsrc), vd + i * VSLAB);
                     }
                 } else {
 #pragma unroll
@@ -212,7 +219,7 @@ __global__ __launch_bounds__(64 * kPrefillWaves<G>) __attribute__((amdgpu_waves_
                             const bool in = p >= lo && p < phi;
                             const int32_t b = in ? bt_s[(p >> lbs) - jb0] : -1;
                             const int64_t o = (int64_t)(b >= 0 ? b : 0) * a.pool.block_stride +
-                                              (int64_t)(p & (int32_t)bsm) * row_bytes + 16 * tpp;
+                                              (int64_t)(p & (int32_t)bsm) * row_bytes + 16 * tsrc;
                             lds_copy16(vh + o, vd + i * VSLAB);
                         }
                     }
@@ -357,15 +364,19 @@ __global__ __launch_bounds__(64 * kPrefillWaves<G>) __attribute__((amdgpu_waves_
                 // both chunks, then every sub-tile
                 const int vrow = 4 * g4 + (cn >> 2);
                 const int vbase = (vrow % NP) * VSLAB + (vrow / NP) * ROWB + 8 * (cn & 3);
+                // swizzled rows (odd positions): pieces 0..7 (slices 0..3)
+                // sit 128 bytes later, pieces 8..15 128 bytes earlier
+                const int vodd = kVSwz ? 128 * ((vrow / NP) & 1) : 0;
 #pragma unroll
                 for (int sl = 0; sl < NV; ++sl) {
+                    const int vo = vbase + (sl < NV / 2 ? vodd : -vodd);
                     uint64_t vh2[2];
 #pragma unroll
                     for (int c = 0; c < 2; ++c)
                         vh2[c] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                             (__attribute__((address_space(3))) s16x4 *)((__attribute__((address_space(3))) char *)(
                                                                            const_cast<char *>(vtile[qs + c])) +
-                                                                       vbase + 32 * sl)));
+                                                                       vo + 32 * sl)));
                     const u32x4 vb = {(uint32_t)vh2[0], (uint32_t)(vh2[0] >> 32), (uint32_t)vh2[1],
                                       (uint32_t)(vh2[1] >> 32)};
 #pragma unroll

@@ -184,6 +184,9 @@ inline int prefill_waves(int64_t group) { return group > 4 ? (int)group : 4; }
 #ifndef PKV_PREFILL_WQ128
 #define PKV_PREFILL_WQ128 48
 #endif
+#ifndef PKV_PREFILL_VSWZ
+#define PKV_PREFILL_VSWZ 1
+#endif
 #ifndef PKV_PREFILL_RING
 #define PKV_PREFILL_RING 6
 #endif
