@@ -193,6 +193,69 @@ __device__ __forceinline__ void lds_copy16_nt(const char *src, char *lds_wave_ba
                                      2 /* nt */);
 }
 
+// LDS reads issued from inline asm, complete (lgkmcnt(0)) when the block
+// ends.  Why: the compiler cannot tell which LDS bytes a global -> LDS copy
+// writes, and before an LDS read it cannot separate from the copies in
+// flight it waits for all of them (vmcnt(0)), prefetches issued for later
+// stages included, which puts a whole memory latency into every stage.
+// Kernels using these order each read after the copies it depends on
+// themselves (an s_waitcnt on their own copies, then a barrier).
+__device__ __forceinline__ uint32_t lds_addr(const char *p) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char *)p;
+}
+
+// 16-byte reads (ds_read_b128) at p + S * k, k = 0 .. 7.
+template <int S>
+__device__ __forceinline__ void lds_read16_x8(const char *p, u32x4 (&r)[8]) {
+    asm volatile(
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %8 offset:%9\n\t"
+        "ds_read_b128 %2, %8 offset:%10\n\t"
+        "ds_read_b128 %3, %8 offset:%11\n\t"
+        "ds_read_b128 %4, %8 offset:%12\n\t"
+        "ds_read_b128 %5, %8 offset:%13\n\t"
+        "ds_read_b128 %6, %8 offset:%14\n\t"
+        "ds_read_b128 %7, %8 offset:%15\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+        : "v"(lds_addr(p)), "i"(S), "i"(2 * S), "i"(3 * S), "i"(4 * S), "i"(5 * S), "i"(6 * S), "i"(7 * S)
+        : "memory");
+}
+
+// 16-byte reads (ds_read_b128) at p + S * k, k = 0 .. 3.
+template <int S>
+__device__ __forceinline__ void lds_read16_x4(const char *p, u32x4 (&r)[4]) {
+    asm volatile(
+        "ds_read_b128 %0, %4\n\t"
+        "ds_read_b128 %1, %4 offset:%5\n\t"
+        "ds_read_b128 %2, %4 offset:%6\n\t"
+        "ds_read_b128 %3, %4 offset:%7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+        : "v"(lds_addr(p)), "i"(S), "i"(2 * S), "i"(3 * S)
+        : "memory");
+}
+
+// Transposed reads (ds_read_b64_tr_b16: the B-operand layout of a 16x16x32
+// MFMA from 4 rows of 8 bytes) at p + S * k and p + T + S * k, k = 0 .. 3,
+// into r[k] and r[4 + k].
+template <int S, int T>
+__device__ __forceinline__ void lds_read_tr16_x8(const char *p, uint64_t (&r)[8]) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8\n\t"
+        "ds_read_b64_tr_b16 %1, %8 offset:%9\n\t"
+        "ds_read_b64_tr_b16 %2, %8 offset:%10\n\t"
+        "ds_read_b64_tr_b16 %3, %8 offset:%11\n\t"
+        "ds_read_b64_tr_b16 %4, %8 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %5, %8 offset:%13\n\t"
+        "ds_read_b64_tr_b16 %6, %8 offset:%14\n\t"
+        "ds_read_b64_tr_b16 %7, %8 offset:%15\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+        : "v"(lds_addr(p)), "i"(S), "i"(2 * S), "i"(3 * S), "i"(T), "i"(T + S), "i"(T + 2 * S), "i"(T + 3 * S)
+        : "memory");
+}
+
 // Keep the compiler from moving LDS accesses across this point; the LDS
 // unit itself serves one wavefront's requests in order.
 __device__ __forceinline__ void wave_lds_order() {

@@ -250,12 +250,19 @@ __global__ __launch_bounds__(64 * kPrefillWaves<G>) __attribute__((amdgpu_waves_
             // then the second's (the same relabelling of the 32 keys in
             // both operands, so the sum is unchanged).
             auto compute_stage = [&](int32_t cpc, int qs) {
+                // the two chunks' K fragments: slot qs + 1 follows slot qs,
+                // fragment j of chunk c at 1024 (KS c + j)
+                static_assert(KFRAG == 1024 * KS && (KS == 4 || KS == 2), "K fragment layout");
                 u32x4 kf[2][KS];
+                {
+                    u32x4 kr[2 * KS];
+                    if constexpr (KS == 4) lds_read16_x8<1024>(kfrag[qs] + 16 * lane, kr);
+                    else lds_read16_x4<1024>(kfrag[qs] + 16 * lane, kr);
 #pragma unroll
-                for (int c = 0; c < 2; ++c)
+                    for (int c = 0; c < 2; ++c)
 #pragma unroll
-                    for (int j = 0; j < KS; ++j)
-                        kf[c][j] = *reinterpret_cast<const u32x4 *>(kfrag[qs + c] + 1024 * j + 16 * lane);
+                        for (int j = 0; j < KS; ++j) kf[c][j] = kr[KS * c + j];
+                }
                 // A chunk needs no mask when all its rows are live tokens at
                 // or before the wavefront's first query.  When both chunks are
                 // such (every stage below the causal diagonal and inside the
@@ -367,22 +374,22 @@ __global__ __launch_bounds__(64 * kPrefillWaves<G>) __attribute__((amdgpu_waves_
                 // swizzled rows (odd positions): pieces 0..7 (slices 0..3)
                 // sit 128 bytes later, pieces 8..15 128 bytes earlier
                 const int vodd = kVSwz ? 128 * ((vrow / NP) & 1) : 0;
+                static_assert(NV % 4 == 0, "V slices in groups of four");
 #pragma unroll
-                for (int sl = 0; sl < NV; ++sl) {
-                    const int vo = vbase + (sl < NV / 2 ? vodd : -vodd);
-                    uint64_t vh2[2];
+                for (int sg = 0; sg < NV / 4; ++sg) {
+                    // slices 4 sg .. 4 sg + 3 of both chunks (slot qs + 1
+                    // follows slot qs)
+                    uint64_t vr[8];
+                    lds_read_tr16_x8<32, VTILE>(vtile[qs] + vbase + 128 * sg + (4 * sg < NV / 2 ? vodd : -vodd), vr);
 #pragma unroll
-                    for (int c = 0; c < 2; ++c)
-                        vh2[c] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (__attribute__((address_space(3))) s16x4 *)((__attribute__((address_space(3))) char *)(
-                                                                           const_cast<char *>(vtile[qs + c])) +
-                                                                       vo + 32 * sl)));
-                    const u32x4 vb = {(uint32_t)vh2[0], (uint32_t)(vh2[0] >> 32), (uint32_t)vh2[1],
-                                      (uint32_t)(vh2[1] >> 32)};
+                    for (int k = 0; k < 4; ++k) {
+                        const u32x4 vb = {(uint32_t)vr[k], (uint32_t)(vr[k] >> 32), (uint32_t)vr[4 + k],
+                                          (uint32_t)(vr[4 + k] >> 32)};
 #pragma unroll
-                    for (int t = 0; t < QT; ++t)
-                        acc[t][sl] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(pa[t]), as_bf16x8(vb),
-                                                                             acc[t][sl], 0, 0, 0);
+                        for (int t = 0; t < QT; ++t)
+                            acc[t][4 * sg + k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                as_bf16x8(pa[t]), as_bf16x8(vb), acc[t][4 * sg + k], 0, 0, 0);
+                    }
                 }
 #pragma unroll
                 for (int t = 0; t < QT; ++t)
