@@ -64,13 +64,11 @@ def append_bytes(w):
 
 
 def decode_schedule(N, w, split_req):
-    """(split tokens or 0 for the balanced schedule, kernel label) of one
+    """(split tokens or SCHEDULE_PLANNED, kernel label) of one
     paged_attn_decode call on this batch."""
     sched = N.paged_attn_decode_schedule(w.num_seqs, w.num_kv_heads, w.num_q_heads, w.head_dim,
                                          w.max_seq_len, w.block_size, w.dtype, split_req)
     g = w.num_q_heads // w.num_kv_heads
-    if sched == 0:
-        return sched, f"decode_stream_kernel<D={w.head_dim},G={g}> (balanced schedule)"
     if sched == N.SCHEDULE_PLANNED:
         return sched, (f"decode_mfma_kernel<D={w.head_dim},G={g}> (device-planned split: pieces fit "
                        "2 workgroups per CU, merged in the kernel)")
@@ -639,8 +637,6 @@ def schedule_label(N, w, split):
     sched, label = decode_schedule(N, w, split)
     if sched == N.SCHEDULE_PLANNED:
         return label, "planned (device-planned split)"
-    if sched == 0:
-        return label, "balanced"
     return label, sched
 
 

@@ -221,8 +221,6 @@ PKV_API int kv_gather(const pkv_pool *pool, int32_t layer,
                       int32_t max_seq_len, void *k_out, void *v_out,
                       int64_t out_rows, void *stream);
 
-/* split_tokens value that asks paged_attn_decode for the balanced schedule */
-#define PKV_SPLIT_BALANCED (-1)
 /* split_tokens value that asks paged_attn_decode for the device-planned
  * split schedule, and the value paged_attn_decode_schedule returns for it */
 #define PKV_SPLIT_PLANNED (-2)
@@ -231,20 +229,27 @@ PKV_API int kv_gather(const pkv_pool *pool, int32_t layer,
 /*
  * paged_attn_decode_split_tokens -- the split size (tokens per work item)
  * of the split schedule for a bf16 pool when paged_attn_decode is called
- * with split_tokens = 0 and takes neither the planned nor the balanced
- * schedule (see paged_attn_decode_schedule, which also gives the choice
- * for fp32 and int8 pools: those stop growing the split at 1024 positions
- * once there are 2 workgroups per compute unit).  Depends on the sizes and
- * on the current device's compute-unit count (256 is assumed when no
- * device can be queried).  Returns a positive multiple of 16, or a
- * negative status for bad sizes.
+ * with split_tokens = 0 and does not take the planned schedule (see
+ * paged_attn_decode_schedule, which also gives the choice for fp32 and
+ * int8 pools: with fewer (sequence, kv head) pairs than twice the
+ * compute units, those stop growing the split at 1024 positions once
+ * there are 2 workgroups per compute unit).  A power of two of at least
+ * 64 positions: grown while the work items (sequence, kv head, split of
+ * max_seq_len tokens) exceed 8 per compute unit (32 with at least two
+ * pairs per compute unit), up to 256 positions while at least 2 items per
+ * compute unit remain, and for few pairs past 1024 positions while they
+ * exceed 4 per compute unit; never past the first split that covers
+ * max_seq_len.  Depends on the sizes and on the current device's
+ * compute-unit count (256 is assumed when no device can be queried).
+ * Returns a positive multiple of 16, or a negative status for bad sizes.
  */
 PKV_API int32_t paged_attn_decode_split_tokens(int32_t num_seqs, int32_t num_kv_heads,
                                                int32_t max_seq_len, int32_t block_size);
 
 /*
  * paged_attn_decode_schedule -- which work schedule paged_attn_decode takes
- * for these sizes, pool dtype (PKV_F32 / PKV_BF16) and split_tokens:
+ * for these sizes, pool dtype (PKV_F32 / PKV_BF16 / PKV_I8) and
+ * split_tokens:
  *   > 0  the split schedule with this many tokens per split: one workgroup
  *        per (sequence, split of split_tokens flat positions, group of kv
  *        heads);
@@ -260,17 +265,8 @@ PKV_API int32_t paged_attn_decode_split_tokens(int32_t num_seqs, int32_t num_kv_
  *        compute units / 2 (sequence, kv-head group) pairs, and
  *        max_seq_len / 2 + 32 <= the largest split (split_tokens limit
  *        below);
- *     0  the balanced schedule: one resident generation of workgroups (more
- *        when a share would not fit one pass), each taking an equal share
- *        of all (kv-head group, sequence, 16-position chunk) units.  Taken
- *        for bf16 pools with at most 256 * (kv heads per workgroup: 4, 2
- *        or 1, the largest dividing num_kv_heads) sequences when
- *        split_tokens = PKV_SPLIT_BALANCED, or when split_tokens = 0, the
- *        planned schedule is not possible, and the batch has at least 32
- *        sequences and 512 MiB of K/V at max_seq_len;
  *   < 0  a status for bad sizes or dtype (PKV_ERR_UNSUPPORTED for a
- *        balanced request on an fp32 pool or too many sequences, or a
- *        planned request the batch does not allow).
+ *        planned request the batch or the pool dtype does not allow).
  * All compute the same function; they differ only in fp32 rounding order.
  */
 PKV_API int32_t paged_attn_decode_schedule(int32_t num_seqs, int32_t num_kv_heads,
@@ -281,7 +277,7 @@ PKV_API int32_t paged_attn_decode_schedule(int32_t num_seqs, int32_t num_kv_head
 /*
  * paged_attn_decode_workspace_size -- bytes of device workspace that
  * paged_attn_decode needs for these sizes and this split_tokens.  With
- * split_tokens = 0 it covers either schedule.  0 means no workspace is
+ * split_tokens = 0 it covers the schedule taken for any pool dtype.  0 means no workspace is
  * needed (every sequence fits one split).  Returns (size_t)-1 for bad
  * sizes.
  */
@@ -308,8 +304,6 @@ PKV_API size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_kv
  *   max_seq_len   host bound on every seq_len
  *   scale         softmax scale (e.g. 1/sqrt(head_dim))
  *   split_tokens  0 = automatic (see paged_attn_decode_schedule);
- *                 PKV_SPLIT_BALANCED = the balanced schedule (bf16 pools,
- *                 sequence limit as above, else PKV_ERR_UNSUPPORTED);
  *                 PKV_SPLIT_PLANNED = the device-planned split schedule
  *                 (limits as above, else PKV_ERR_UNSUPPORTED); else the
  *                 tokens per split-K work item, a positive multiple of 16
@@ -334,9 +328,8 @@ PKV_API size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_kv
  *                 as is.  Calls that share a workspace must not overlap
  *                 (issue them on one stream).
  * Supported: head_dim in {64, 128}, G in {1, 2, 4, 8}.  A quantised pool
- * takes bfloat16 q and out, runs the split or the planned schedule
- * (PKV_SPLIT_BALANCED is PKV_ERR_UNSUPPORTED) and attends to the stored
- * values code * scale.
+ * takes bfloat16 q and out, runs the split or the planned schedule and
+ * attends to the stored values code * scale.
  * Errors: PKV_ERR_NULL, _DTYPE, _SHAPE, _LAYER, _ALIGN, _WORKSPACE,
  * _UNSUPPORTED, _LAUNCH.
  */

@@ -20,15 +20,13 @@
 //   times.  A workgroup holds up to 4 wavefronts = a group of kv heads of
 //   one (sequence, split): they share the block-table entries, staged in
 //   LDS once per workgroup, and read each block's layer slice together.
-//   Three schedules map workgroups to work items:
+//   Two schedules map workgroups to work items:
 //   - split: one workgroup per (sequence, split, head group), split S chosen
 //     by the host from max_seq_len; workgroups are renumbered so that the
 //     splits of one sequence land on different XCDs;
 //   - device-planned split (plan_item below): every workgroup reads all
 //     lengths, picks S so the pieces fit two workgroups per compute unit,
-//     and takes one piece;
-//   - balanced (decode_stream_kernel): equal shares of (head group,
-//     sequence, 16-position chunk) units, several segments per workgroup.
+//     and takes one piece.
 //
 // bf16 kernel, per 16-position chunk of one block:
 //   QK:  S^T = K_chunk (16 x D) . Q^T (D x 16 heads, G real) with
@@ -1491,594 +1489,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
 }
 
 // ---------------------------------------------------------------------------
-// Balanced schedule (bf16): the grid is the number of workgroups that stay
-// resident together, and every workgroup takes an equal share of the work.
-// The work is flattened into units (head group, sequence, chunk): chunk c
-// of a sequence with offset off covers the 16 flat positions starting at
-// 16 * (off/16 + c), so a sequence of length L > 0 has
-// ((off + L - 1)/16 - off/16 + 1) chunks; C = their sum, U = head_groups * C.
-// Workgroup w takes units [U w / P, U (w+1) / P), P = min(grid, U).
-//
-// A workgroup walks its units in rounds (almost always one).  A round
-// covers at most kSegMax segments -- one per (head group, sequence) pair it
-// touches -- and as many units as the LDS table buffer can hold.  It costs
-// two memory round trips before its first K/V load: the lengths and offsets
-// of every sequence (each thread reads its share; the chunk counts are
-// scanned over the workgroup and the round's pairs listed in LDS), then the
-// block-table entries of all the round's segments at once.  One ring of
-// loads then runs through all of the round's chunks, so the next segment's
-// loads are in flight while the current one is computed; a segment boundary
-// costs only the load of the new query rows.
-//
-// A segment that holds a whole pair writes the output directly.  Otherwise
-// (the pair began before the range, or runs past its end) the segment's
-// partial goes to one of the workgroup's two record slots (2w: began
-// before, 2w+1: runs past), and at the end the workgroup counts it in for
-// the pair; the contributor that completes the count merges the pair's
-// records in workgroup order.  No workgroup waits on another.
-// ---------------------------------------------------------------------------
-
-// Workgroup whose range holds unit u: the largest w with U w / P <= u.
-__device__ __forceinline__ int64_t owner_of(int64_t u, int64_t U, int64_t P) {
-    return ((u + 1) * P - 1) / U;
-}
-
-// The segments of one round.
-struct RoundLds {
-    int64_t lo[kSegMax], hi[kSegMax];  // flat positions of the segment's tokens
-    int64_t ps[kSegMax], pe[kSegMax];  // the pair's unit range
-    int32_t seq[kSegMax], hg[kSegMax];
-    int32_t whole[kSegMax];            // the sequence's length and offset were not clamped
-    int32_t base[kSegMax + 1];         // first bt_s entry of each segment; base[n] = total
-    int32_t step[kSegMax + 1];         // first ring step of each segment; step[n] = total
-    int32_t n;                         // segments in the round
-    int32_t rank0;                     // pair rank (among nonempty pairs) of segment 0
-    int64_t tot[2][4];                 // per-wave totals: chunks, nonempty sequences
-};
-
-__device__ __forceinline__ int64_t uniform64(int64_t x) {
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
-    return (int64_t)(((uint64_t)hi << 32) | lo);
-}
-__device__ __forceinline__ int32_t uniform32(int32_t x) { return __builtin_amdgcn_readfirstlane(x); }
-
-// floor(n / d) for 0 <= n < 2^62, 0 < d: a double-precision estimate,
-// then corrected to the exact quotient (a few instructions, where the
-// 64-bit integer division is a long routine).
-__device__ __forceinline__ int64_t udiv64(int64_t n, int64_t d) {
-    int64_t q = (int64_t)((double)n / (double)d);
-    while (q > 0 && q * d > n) --q;
-    while ((q + 1) * d <= n) ++q;
-    return q;
-}
-
-template <int D, int G, bool UB>
-__global__ __launch_bounds__(256) void decode_stream_kernel(DecodeArgs a) {
-    using S = MfmaShape<D>;
-    constexpr int ROWB = S::ROWB, PPR = S::PPR, NP = S::NP, KS = S::KS, NV = S::NV;
-    constexpr int VSLAB = S::VSLAB, VTILE = S::VTILE, NSLOT = S::NSLOT;
-    constexpr int LOADS = S::LOADS;
-    constexpr int PER = kStreamSeqsPerThread;  // sequences per thread, at most
-    constexpr int SLOTS = 4;                   // table entries per thread per pass
-    constexpr float kLazy = 8.0f;
-    static_assert(G >= 1 && G <= 16, "group");
-    constexpr int SPI = 64 / (2 * PPR);                 // segments whose new rows one copy stages
-    constexpr int SBATCH = SPI * (NSLOT * VTILE / 1024);  // segments staged at once in the V ring
-    __shared__ int32_t bt_s[kBtLds];
-    __shared__ __attribute__((aligned(16))) char vtiles[4][NSLOT][VTILE];
-    __shared__ RoundLds R;
-
-    const int t = threadIdx.x;
-    const int lane = t & 63;
-    const int wv = t >> 6;
-    const int w = __builtin_amdgcn_readfirstlane(wv);
-    const int nwaves = blockDim.x >> 6;
-    const int ns = a.num_seqs;
-    const int HG = a.head_groups;
-    const int hqw = a.heads_per_wg * G;  // query heads of one head group
-    const int lbs = a.pool.lbs;
-    const int64_t bsm = (1ll << lbs) - 1;
-    const int64_t row_bytes = a.pool.row_bytes;
-    const float sl2 = a.scale_log2;
-    const int n16 = lane & 15;  // MFMA: row / column index
-    const int g4 = lane >> 4;   // MFMA: k group
-    const int trow = lane / PPR;
-    const int tpp = lane % PPR;
-    char *vring = vtiles[w][0];
-    // logical workgroup index: consecutive ranges share an XCD
-    const int nwg = gridDim.x;
-    const int bid = blockIdx.x;
-    const int xcd = bid & 7;
-    const int lw = xcd * (nwg >> 3) + min(xcd, nwg & 7) + (bid >> 3);
-
-    int64_t U = 0, P = 1, u0 = 0, u1 = 0, r0 = 0;
-    // records to count in at the end: the head (pair began before u0) and
-    // the tail (pair runs past u1)
-    int npend = 0;
-    int p0_seq = 0, p0_hg = 0, p1_seq = 0, p1_hg = 0;
-    int64_t p0_wa = 0, p0_wb = 0, p1_wa = 0, p1_wb = 0;
-
-    u32x4 qf[KS];
-    float m_h = kNegInf;  // reference max of head n16 (same in its 4 lanes)
-    float l_h = 0.0f;     // this lane's share of head n16's denominator
-    f32x4 acc[NV];
-#pragma unroll
-    for (int sl = 0; sl < NV; ++sl) acc[sl] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-
-    // Finish the pair (sq, hg) with units [ps, pe): the output of a whole
-    // pair, else a record counted in at the end.
-    auto finish_pair = [&](int sq, int hg, int64_t ps, int64_t pe) {
-        float lrow[4];
-        head_denominators(l_h, lrow);
-        const int h = hg * a.heads_per_wg + w;
-        if (ps >= u0 && pe <= u1) {
-            write_direct<D, G>(a, sq, h, acc, lrow);
-        } else {
-            const int64_t slot = ps < u0 ? 2 * (int64_t)lw : 2 * (int64_t)lw + 1;
-            const int64_t rec = slot * hqw + (int64_t)w * G;
-            write_partial<D, G>(a.ws_ml + rec * 2, a.ws_acc + rec * D, acc, m_h, l_h);
-            const int64_t wa = owner_of(ps, U, P), wb = owner_of(pe - 1, U, P);
-            if (npend == 0) {
-                p0_seq = sq;
-                p0_hg = hg;
-                p0_wa = wa;
-                p0_wb = wb;
-            } else {
-                p1_seq = sq;
-                p1_hg = hg;
-                p1_wa = wa;
-                p1_wb = wb;
-            }
-            ++npend;
-        }
-    };
-
-    {
-        // ---- lengths and offsets of this thread's sequences, chunk counts,
-        // and their scan over the workgroup (first memory round trip).  The
-        // arithmetic here runs once per workgroup; it is kept short (no
-        // 64-bit divisions, PER sequences per thread) because every
-        // instruction of it delays the first K/V load.
-        int32_t ln[PER], of[PER], wh[PER];
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int sq = t * PER + i;
-            ln[i] = 0;
-            of[i] = 0;
-            if (sq < ns) {
-                ln[i] = a.seq_lens[sq];
-                of[i] = a.offsets[sq];
-            }
-        }
-        // lengths clamped to max_seq_len and offsets into [0, block_size):
-        // the host sized the grid so every share fits for those
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int32_t l0 = ln[i], o0 = of[i];
-            ln[i] = l0 < 0 ? 0 : (l0 > a.max_len ? a.max_len : l0);
-            of[i] = o0 < 0 ? 0 : (o0 > (int32_t)bsm ? (int32_t)bsm : o0);
-            wh[i] = ln[i] == l0 && of[i] == o0;
-        }
-        int64_t cn[PER];
-        int64_t mc = 0, mnz = 0;
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            cn[i] = ln[i] > 0 ? (((int64_t)of[i] + ln[i] - 1) >> 4) - ((int64_t)of[i] >> 4) + 1 : 0;
-            mc += cn[i];
-            mnz += cn[i] > 0;
-        }
-        int64_t ic = mc, inz = mnz;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const int64_t y = __shfl_up(ic, d);
-            const int64_t z = __shfl_up(inz, d);
-            if (lane >= d) {
-                ic += y;
-                inz += z;
-            }
-        }
-        if (lane == 63) {
-            R.tot[0][wv] = ic;
-            R.tot[1][wv] = inz;
-        }
-        if (t == 0) R.n = 0;
-        __syncthreads();
-        int64_t C = 0, NZ = 0, bc = 0, bnz = 0;
-        for (int k = 0; k < nwaves; ++k) {
-            if (k < wv) {
-                bc += R.tot[0][k];
-                bnz += R.tot[1][k];
-            }
-            C += R.tot[0][k];
-            NZ += R.tot[1][k];
-        }
-        C = uniform64(C);
-        NZ = uniform64(NZ);
-        const int64_t excl_c = bc + ic - mc, excl_nz = bnz + inz - mnz;
-
-        {
-            // sequences with no tokens attend to nothing: zero rows (the
-            // workgroup whose index is the sequence's, modulo the grid)
-#pragma unroll
-            for (int i = 0; i < PER; ++i) {
-                const int sq = t * PER + i;
-                if (sq < ns && ln[i] <= 0 && (sq == lw || (sq > lw && (sq - lw) % nwg == 0))) {
-                    u32x4 *o = reinterpret_cast<u32x4 *>(a.out + (int64_t)sq * a.num_q_heads * D * 2);
-                    for (int k = 0; k < a.num_q_heads * D * 2 / 16; ++k) o[k] = u32x4{0, 0, 0, 0};
-                }
-            }
-            U = C * HG;
-            P = min((int64_t)nwg, U);
-            if (lw >= P) return;  // uniform: no work for this workgroup
-            u0 = udiv64(U * lw, P);
-            u1 = udiv64(U * (lw + 1), P);
-            r0 = u0;
-        }
-        // [r0, r1) = the whole range: the host sizes the grid so that its
-        // pairs fit kSegMax and its table entries fit bt_s
-        const int64_t r1max = u1;
-
-        // ---- the round's segments: the pairs overlapping [r0, r1max), by rank
-        int64_t hgA = 0;
-        while ((hgA + 1) * C <= r0) ++hgA;
-        int64_t hgB = hgA;
-        while ((hgB + 1) * C <= r1max - 1) ++hgB;
-        {
-            const int64_t rr = r0 - hgA * C;
-            if (rr >= excl_c && rr < excl_c + mc) {
-                int64_t pre = excl_c, nzr = excl_nz;
-#pragma unroll
-                for (int i = 0; i < PER; ++i) {
-                    if (cn[i] > 0 && rr >= pre && rr < pre + cn[i]) R.rank0 = (int32_t)(hgA * NZ + nzr);
-                    pre += cn[i];
-                    nzr += cn[i] > 0;
-                }
-            }
-        }
-        __syncthreads();
-        {
-            const int64_t rank0 = R.rank0;
-            int64_t pre = excl_c, nzr = excl_nz;
-#pragma unroll
-            for (int i = 0; i < PER; ++i) {
-                if (cn[i] > 0) {
-                    for (int64_t hg = hgA; hg <= hgB; ++hg) {
-                        const int64_t ps = hg * C + pre, pe = ps + cn[i];
-                        if (pe > r0 && ps < r1max) {
-                            const int64_t idx = hg * NZ + nzr - rank0;
-                            if (idx < kSegMax) {
-                                R.seq[idx] = t * PER + i;
-                                R.hg[idx] = (int32_t)hg;
-                                R.ps[idx] = ps;
-                                R.pe[idx] = pe;
-                                R.lo[idx] = of[i];  // offset and length for now
-                                R.hi[idx] = ln[i];
-                                R.whole[idx] = wh[i];
-                                atomicAdd(&R.n, 1);
-                            }
-                        }
-                    }
-                }
-                pre += cn[i];
-                nzr += cn[i] > 0;
-            }
-        }
-        __syncthreads();
-        const int nseg = uniform32(R.n);
-        const int64_t r1 = r1max;
-        // wave 0: each segment's flat range, table entries and ring steps
-        // (lane l handles segments l and l + 64)
-        if (wv == 0) {
-            int32_t carry_e = 0, carry_s = 0;
-            for (int i0 = 0; i0 < nseg; i0 += 64) {
-                const int i = i0 + lane;
-                int32_t ne = 0, nst = 0;
-                int64_t lo = 0, hi = 0;
-                if (i < nseg) {
-                    const int64_t off = R.lo[i], len = R.hi[i];
-                    const int64_t ps = R.ps[i], pe = R.pe[i];
-                    const int64_t f0 = off >> 4;
-                    lo = max(16 * (f0 + max(ps, r0) - ps), off);
-                    hi = min(16 * (f0 + min(pe, r1) - ps), off + len);
-                    ne = (int32_t)(((hi - 1) >> lbs) - (lo >> lbs) + 1);
-                    nst = (int32_t)(((hi - 1) >> 4) - (lo >> 4) + 1);
-                }
-                int32_t ie = ne, is = nst;
-#pragma unroll
-                for (int d = 1; d < 64; d <<= 1) {
-                    const int32_t y = __shfl_up(ie, d);
-                    const int32_t z = __shfl_up(is, d);
-                    if (lane >= d) {
-                        ie += y;
-                        is += z;
-                    }
-                }
-                if (i < nseg) {
-                    R.lo[i] = lo;
-                    R.hi[i] = hi;
-                    R.base[i] = carry_e + ie - ne;
-                    R.step[i] = carry_s + is - nst;
-                }
-                if (i == nseg - 1) {
-                    R.base[nseg] = carry_e + ie;
-                    R.step[nseg] = carry_s + is;
-                }
-                carry_e += __shfl(ie, 63);
-                carry_s += __shfl(is, 63);
-            }
-        }
-        __syncthreads();
-
-        // ---- second round trip: the table entries of every segment, the
-        // new rows (decode with append) and the first segment's query rows
-        const int E = min(R.base[nseg], kBtLds);
-        const bool app = a.k_new != nullptr;
-        for (int j0 = 0; j0 < E; j0 += SLOTS * (int)blockDim.x) {
-            int32_t bv[SLOTS];
-#pragma unroll
-            for (int k = 0; k < SLOTS; ++k) {
-                const int j = j0 + t + k * (int)blockDim.x;
-                bv[k] = -1;
-                if (j < E) {
-                    int i = 0;
-                    while (i + 1 < nseg && R.base[i + 1] <= j) ++i;
-                    const int64_t jj = (R.lo[i] >> lbs) + (j - R.base[i]);
-                    if (jj < a.bt_stride) bv[k] = a.block_tables[(int64_t)R.seq[i] * a.bt_stride + jj];
-                }
-            }
-            if (j0 == 0) load_q<D, G>(a, R.seq[0], R.hg[0] * a.heads_per_wg + w, qf);
-#pragma unroll
-            for (int k = 0; k < SLOTS; ++k) {
-                const int j = j0 + t + k * (int)blockDim.x;
-                if (j < E) bt_s[j] = (bv[k] >= 0 && bv[k] < a.pool.num_blocks) ? bv[k] : -1;
-            }
-        }
-        __syncthreads();
-        if (app) {
-            // Decode with append: every segment that reaches its pair's end
-            // holds the sequence's last token.  This wave's new K and V rows
-            // of SBATCH segments at a time are staged in its V ring (one copy
-            // moves SPI segments: lane l takes piece l % (2 PPR), K pieces
-            // then V pieces, of segment i0 + l / (2 PPR)), then each piece is
-            // stored into the pool by the lane whose ring load reads it back
-            // later, so program order makes that load see it.
-            for (int b0 = 0; b0 < nseg; b0 += SBATCH) {
-                for (int i0 = b0; i0 < min(nseg, b0 + SBATCH); i0 += SPI) {
-                    const int i = min(i0 + lane / (2 * PPR), nseg - 1);
-                    const int lp = lane % (2 * PPR);
-                    const int64_t src = ((int64_t)R.seq[i] * a.num_kv_heads + R.hg[i] * a.heads_per_wg + w) * ROWB +
-                                        16 * (lp % PPR);
-                    lds_copy16((lp < PPR ? a.k_new : a.v_new) + src, vring + ((i0 - b0) / SPI) * 1024);
-                }
-                __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xF << 8));
-                wave_lds_order();
-                for (int i = b0; i < min(nseg, b0 + SBATCH); ++i) {
-                    if (R.pe[i] <= r1 && R.whole[i]) {
-                        const int64_t pn = R.hi[i] - 1;
-                        const int bi = R.base[i] + (int)((pn >> lbs) - (R.lo[i] >> lbs));
-                        const int32_t b = bi < kBtLds ? bt_s[bi] : -1;
-                        const int rn = (int)(pn & 15);
-                        if (b >= 0 && (n16 == rn || trow == rn / NP)) {
-                            const int64_t o = a.pool.layer_off + (int64_t)b * a.pool.block_stride +
-                                              (pn & bsm) * row_bytes +
-                                              (int64_t)(R.hg[i] * a.heads_per_wg + w) * ROWB;
-                            const char *st = vring + ((i - b0) / SPI) * 1024 + ((i - b0) % SPI) * (2 * PPR) * 16;
-                            if (n16 == rn) {  // the lanes that load this row's K pieces 4 j + g4
-#pragma unroll
-                                for (int j = 0; j < KS; ++j)
-                                    *reinterpret_cast<u32x4 *>(const_cast<char *>(a.pool.k) + o + 64 * j + 16 * g4) =
-                                        *reinterpret_cast<const u32x4 *>(st + 64 * j + 16 * g4);
-                            }
-                            if (trow == rn / NP)  // the lanes that load this row's V piece tpp
-                                *reinterpret_cast<u32x4 *>(const_cast<char *>(a.pool.v) + o + 16 * tpp) =
-                                    *reinterpret_cast<const u32x4 *>(st + 16 * (PPR + tpp));
-                        }
-                    }
-                }
-                wave_lds_order();
-            }
-        }
-
-        // ---- one ring through the round's chunks
-        const int T = uniform32(R.step[nseg]);
-        // A ring cursor: the segment of a step and its parameters (wave-
-        // uniform), refreshed from LDS only when it enters the next segment.
-        struct Cur {
-            int i;        // segment
-            int knext;    // first step of segment i + 1 (T after the last)
-            int base;     // bt_s entry of block jb0
-            int64_t lo, hi, pc, jb0, hoff;
-        };
-        auto enter = [&](Cur &c, int i) {
-            c.i = i;
-            c.knext = uniform32(R.step[i + 1]);
-            c.lo = uniform64(R.lo[i]);
-            c.hi = uniform64(R.hi[i]);
-            c.pc = c.lo & ~int64_t(15);
-            c.jb0 = c.lo >> lbs;
-            c.base = uniform32(R.base[i]);
-            c.hoff = a.pool.layer_off + (int64_t)(uniform32(R.hg[i]) * a.heads_per_wg + w) * ROWB;
-        };
-        Cur L, Cc;  // loader, compute
-        enter(L, 0);
-        enter(Cc, 0);
-        // Issue the loads of ring step k < T (k = 0, 1, 2, ...).
-        auto issue = [&](int k, u32x4 *kx, int slot) {
-            if (k > 0 && k < T) {
-                if (k == L.knext)
-                    enter(L, L.i + 1);
-                else
-                    L.pc += 16;
-            }
-            const int64_t pc = L.pc;
-            const char *kh = a.pool.k + L.hoff;
-            const char *vh = a.pool.v + L.hoff;
-            char *dst = vring + slot * VTILE;
-            // K straight into registers in the MFMA A-operand layout (lane
-            // (n16, g4): row n16, bytes 64 j + 16 g4 .. +16 of step j), V into
-            // ring slot `slot` in row layout
-            if constexpr (UB) {
-                const int bi = L.base + (int)((pc >> lbs) - L.jb0);
-                const int32_t b = __builtin_amdgcn_readfirstlane(bi < kBtLds ? bt_s[bi] : -1);
-                const int64_t bb = (int64_t)(b >= 0 ? b : 0) * a.pool.block_stride + (pc & bsm) * row_bytes;
-                const char *kb = kh + bb + (uint32_t)(n16 * row_bytes + 16 * g4);
-#pragma unroll
-                for (int j = 0; j < KS; ++j) kx[j] = ld16(kb + 64 * j);
-#pragma unroll
-                for (int i = 0; i < NP; ++i)
-                    lds_copy16_nt(vh + bb + (uint32_t)((i + NP * trow) * row_bytes + 16 * tpp), dst + i * VSLAB);
-            } else {
-                {
-                    const int64_t p = pc + n16;
-                    const int bi = L.base + (int)((p >> lbs) - L.jb0);
-                    const bool in = p >= L.lo && p < L.hi && bi < kBtLds;
-                    const int32_t b = in ? bt_s[bi] : -1;
-                    const char *kb = kh + (int64_t)(b >= 0 ? b : 0) * a.pool.block_stride + (p & bsm) * row_bytes + 16 * g4;
-#pragma unroll
-                    for (int j = 0; j < KS; ++j) kx[j] = ld16(kb + 64 * j);
-                }
-#pragma unroll
-                for (int i = 0; i < NP; ++i) {
-                    const int64_t p = pc + i + NP * trow;
-                    const int bi = L.base + (int)((p >> lbs) - L.jb0);
-                    const bool in = p >= L.lo && p < L.hi && bi < kBtLds;
-                    const int32_t b = in ? bt_s[bi] : -1;
-                    const int64_t o = (int64_t)(b >= 0 ? b : 0) * a.pool.block_stride + (p & bsm) * row_bytes + 16 * tpp;
-                    lds_copy16_nt(vh + o, dst + i * VSLAB);
-                }
-            }
-        };
-        // Finish segment i: the output of a whole pair, else a record.
-        auto finish = [&](int i) {
-            finish_pair(uniform32(R.seq[i]), uniform32(R.hg[i]), uniform64(R.ps[i]), uniform64(R.pe[i]));
-        };
-
-        // Compute ring step k (its loads were issued NSLOT-1 steps ago).
-        auto compute = [&](int k, const u32x4 *kc, int slot) {
-            // the steps after k whose loads are in flight (none past T - 1)
-            wait_chunks_in_flight<LOADS>(min(NSLOT - 1, T - 1 - k));
-            wave_lds_order();
-            const int64_t lo = Cc.lo, hi = Cc.hi, pc = Cc.pc, jb0 = Cc.jb0;
-            const int base = Cc.base;
-            char *vt = vring + slot * VTILE;
-            bool bok = true;
-            if constexpr (UB) {
-                const int bi = base + (int)((pc >> lbs) - jb0);
-                bok = __builtin_amdgcn_readfirstlane(bi < kBtLds ? bt_s[bi] : -1) >= 0;
-            }
-            auto row_live = [&](int row) -> bool {
-                const int64_t p = pc + row;
-                const int bi = base + (int)((p >> lbs) - jb0);
-                const bool in = p >= lo && p < hi && bi < kBtLds;
-                return UB ? (bok && in) : (in && bt_s[bi] >= 0);
-            };
-            const bool full = UB ? (bok && pc >= lo && pc + 16 <= hi) : false;
-            if (!full) {
-#pragma unroll
-                for (int i = 0; i < NP; ++i) {
-                    if (!row_live(i + NP * trow))
-                        *reinterpret_cast<u32x4 *>(vt + i * VSLAB + 16 * lane) = u32x4{0, 0, 0, 0};
-                }
-                wave_lds_order();
-            }
-            f32x4 sacc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int j = 0; j < KS; ++j)
-                sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kc[j]), as_bf16x8(qf[j]), sacc, 0, 0, 0);
-            float s[4];
-            float cm = kNegInf;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                s[i] = (full || row_live(4 * g4 + i)) ? sacc[i] * sl2 : kNegInf;
-                cm = fmaxf(cm, s[i]);
-            }
-            cm = max_xor32(max_xor16(cm));
-            float alpha = 1.0f;
-            if (cm > m_h + kLazy) {
-                alpha = m_h == kNegInf ? 0.0f : fast_exp2(m_h - cm);
-                m_h = cm;
-            }
-            float pr[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) pr[i] = s[i] == kNegInf ? 0.0f : fast_exp2(s[i] - m_h);
-            const uint32_t p01 = f32_to_bf16_bits(pr[0]) | (f32_to_bf16_bits(pr[1]) << 16);
-            const uint32_t p23 = f32_to_bf16_bits(pr[2]) | (f32_to_bf16_bits(pr[3]) << 16);
-            l_h = fmaf(l_h, alpha, (bf16_lo(p01) + bf16_hi(p01)) + (bf16_lo(p23) + bf16_hi(p23)));
-            if (__any(n16 < G && alpha != 1.0f)) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float al = __shfl(alpha, 4 * g4 + i);
-#pragma unroll
-                    for (int sl = 0; sl < NV; ++sl) acc[sl][i] *= al;
-                }
-            }
-            typedef short s16x4 __attribute__((ext_vector_type(4)));
-            const s16x4 pa = __builtin_bit_cast(s16x4, (uint64_t)p01 | ((uint64_t)p23 << 32));
-            const int vrow = 4 * g4 + (n16 >> 2);
-            const int vbase = (vrow % NP) * VSLAB + (vrow / NP) * ROWB + 8 * (n16 & 3);
-#pragma unroll
-            for (int sl = 0; sl < NV; ++sl) {
-                const int off = vbase + 32 * sl;
-                const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) s16x4 *)((__attribute__((address_space(3))) char *)(vt) + off));
-                acc[sl] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, acc[sl], 0, 0, 0);
-            }
-            wave_lds_order();
-        };
-
-        u32x4 kring[NSLOT][KS];
-#pragma unroll
-        for (int q = 0; q < NSLOT - 1; ++q)
-            if (q < T) issue(q, kring[q], q);
-        for (int k = 0; k < T;) {
-#pragma unroll
-            for (int q = 0; q < NSLOT; ++q) {
-                if (k < T) {
-                    if (k > 0) {
-                        if (k == Cc.knext) {
-                            // segment boundary: finish the last one, start the next
-                            finish(Cc.i);
-                            enter(Cc, Cc.i + 1);
-                            load_q<D, G>(a, uniform32(R.seq[Cc.i]), uniform32(R.hg[Cc.i]) * a.heads_per_wg + w,
-                                         qf);
-                            m_h = kNegInf;
-                            l_h = 0.0f;
-#pragma unroll
-                            for (int sl = 0; sl < NV; ++sl) acc[sl] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-                        } else {
-                            Cc.pc += 16;
-                        }
-                    }
-                    const int nq = (q + NSLOT - 1) % NSLOT;
-                    if (k + NSLOT - 1 < T) issue(k + NSLOT - 1, kring[nq], nq);
-                    compute(k, kring[q], q);
-                    ++k;
-                }
-            }
-        }
-        // drain the copies before the tiles and the table are reused
-        __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xF << 8));
-        // the last segment ends the range (the host sizes the grid so that
-        // one round holds every workgroup's range)
-        finish(Cc.i);
-    }
-
-    // count the records in; the contributor that completes a pair merges it
-    for (int k = 0; k < npend; ++k) {
-        const int sq = k ? p1_seq : p0_seq, hg = k ? p1_hg : p0_hg;
-        const int64_t wa = k ? p1_wa : p0_wa, wb = k ? p1_wb : p0_wb;
-        if (count_in(a.ws_cnt + (int64_t)sq * HG + hg, (uint32_t)(wb - wa + 1))) {
-            const int64_t hq0 = (int64_t)(hg * a.heads_per_wg + w) * G;
-            merge_records<1, D, G>(a.out + ((int64_t)sq * a.num_q_heads + hq0) * D * 2,
-                                   a.ws_ml + (int64_t)w * G * 2, a.ws_acc + (int64_t)w * G * D, hqw,
-                                   (int)(wb - wa + 1),
-                                   [=](int i) { return i == 0 ? 2 * wa + 1 : 2 * (wa + i); });
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
 // Merge kernel, used when sequences span many splits: merge the live
 // splits of one (sequence, query head):
 //   M = max_j m_j,  w_j = 2^(m_j - M),  L = sum_j l_j w_j,
@@ -2201,16 +1611,6 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(DecodeArgs a) {
 template <int DT, int D, int G>
 static hipError_t run_decode(const DecodeArgs &a, hipStream_t s) {
     const dim3 block(64 * a.heads_per_wg);
-    if constexpr (DT == 1) {
-        if (a.stream_wgs > 0) {
-            const dim3 sgrid((unsigned)a.stream_wgs);
-            if (a.pool.lbs >= 4)
-                hipLaunchKernelGGL((decode_stream_kernel<D, G, true>), sgrid, block, 0, s, a);
-            else
-                hipLaunchKernelGGL((decode_stream_kernel<D, G, false>), sgrid, block, 0, s, a);
-            return hipGetLastError();
-        }
-    }
     const int64_t nwg = a.plan > 0 ? a.plan : (int64_t)a.head_groups * a.max_splits * a.num_seqs;
     const dim3 grid((unsigned)nwg);
     if constexpr (DT == 1) {

@@ -137,19 +137,30 @@ int64_t max_positions(int64_t max_len, int64_t bs) { return max_len > 0 ? max_le
 // resident workgroup per compute unit streaming twice as long measured
 // faster (8 x 32768 tokens: 192.9 us at 2048 against 198.3 us at 1024, same
 // process); the int8 kernel needs the second workgroup's wavefronts (141.6
-// us at 2048 against 116 us at 1024).  On the decode batch (32 x <= 2048
-// tokens) this picks 256; on 8 x 32768 tokens, 2048 for bf16, else 1024.
+// us at 2048 against 116 us at 1024).  With at least two (sequence, kv head)
+// pairs per compute unit the bound is 32 items per compute unit instead and
+// the long-split rule is off: such batches have many sequences of varied
+// length, and shorter splits balance them (96 sequences of U[128, 4096]
+// tokens, bf16: 172.0 us at 256, 162.9 at 512,
+// 167.0 at 1024, 201.3 at 2048, 243.1 at 4096; 128 x U[128, 3072]: 158.2
+// at 512, 185.7 at 2048; 256 x U[128, 1536]: level from 256 to 4096; int8,
+// 96 x U[128, 4096]: 117.3 us at 512, 131.9 at 1024).  On the decode batch
+// (32 x <= 2048 tokens) this picks 256; on 8 x 32768 tokens, 2048 for bf16,
+// else 1024; on 96 x <= 4096 tokens, 512.  The split stops growing once it
+// covers a whole sequence.
 int64_t auto_split(int64_t num_seqs, int64_t hkv, int64_t max_len, int64_t bs, bool long_rule) {
     const int64_t cus = cu_count();
     const int64_t smax = max_split_tokens(bs);
     const int64_t span = max_positions(max_len, bs);
+    const bool many = num_seqs * hkv >= 2 * cus;
+    const int64_t per_cu = many ? 32 : 8;
     auto items = [&](int64_t s) { return num_seqs * hkv * ((max_len + s - 1) / s); };
     auto splits = [&](int64_t s) { return (span + s - 1) / s; };
     int64_t s = 64;
     if (s > smax) s = smax;
-    while (s * 2 <= smax && (items(s) > 8 * cus || splits(s) > kMaxSplits ||
-                             (s < 256 && items(s * 2) >= 2 * cus) ||
-                             (long_rule && s >= 1024 && items(s) > 4 * cus)))
+    while (s * 2 <= smax && s < span &&
+           (items(s) > per_cu * cus || splits(s) > kMaxSplits || (s < 256 && items(s * 2) >= 2 * cus) ||
+            (long_rule && !many && s >= 1024 && items(s) > 4 * cus)))
         s *= 2;
     return s;
 }
@@ -167,10 +178,9 @@ int plan_decode(int64_t num_seqs, int64_t hkv, int64_t hq, int64_t head_dim, int
                 int64_t bs, int64_t split_req, DecodePlan *p, int32_t dtype = PKV_BF16) {
     if (num_seqs < 0 || hkv <= 0 || hq <= 0 || head_dim <= 0 || max_len < 0 || !is_pow2(bs))
         return PKV_ERR_SHAPE;
-    // 0 (automatic) and a balanced-schedule request plan the automatic
+    // 0 (automatic) and a planned-schedule request plan the automatic
     // split too: it sizes the fallback and the workspace bound
-    const int64_t split = split_req == 0 || split_req == PKV_SPLIT_BALANCED ||
-                                  split_req == PKV_SPLIT_PLANNED
+    const int64_t split = split_req == 0 || split_req == PKV_SPLIT_PLANNED
                               ? auto_split(num_seqs, hkv, max_len, bs, dtype == PKV_BF16)
                               : split_req;
     if (!split_ok(split, bs)) return PKV_ERR_SHAPE;
@@ -197,57 +207,6 @@ int64_t heads_per_wg(int64_t hkv) {
     int64_t hpw = 1;
     while (hpw * 2 <= 4 && hkv % (hpw * 2) == 0) hpw *= 2;
     return hpw;
-}
-
-// Balanced decode schedule (bf16, split_tokens = 0): one resident
-// generation of workgroups (2 per compute unit; the LDS of one workgroup is
-// about 74 KiB), never more than the work units can fill, and the two
-// record slots per workgroup.  Each workgroup reads every sequence length
-// (at most kStreamSeqsPerThread per thread) and handles its share in one
-// pass, which must fit kSegMax pairs and the LDS table buffer; past that
-// the grid grows (more than one generation) until it does.  Chosen
-// automatically for large batches of many sequences: measured on MI355X it
-// beats the automatic split from about 0.5 GB of K/V per call when the
-// lengths vary over at least 32 sequences (64 sequences sharing a prefix,
-// up to 4096 tokens), and loses to it on a few long sequences of equal
-// length (8 x 32768 tokens) and on smaller batches.
-constexpr int64_t kStreamMinBytes = 512ll << 20;
-constexpr int64_t kStreamMinSeqs = 32;
-
-int64_t stream_max_seqs(int64_t hkv) { return kStreamSeqsPerThread * 64 * heads_per_wg(hkv); }
-
-struct StreamPlan {
-    int64_t wgs;
-    int64_t cnt_bytes, ml_bytes, acc_bytes;
-    int64_t total() const { return cnt_bytes + ml_bytes + acc_bytes; }
-};
-
-int plan_stream(int64_t num_seqs, int64_t hkv, int64_t hq, int64_t head_dim, int64_t max_len,
-                int64_t bs, StreamPlan *p);
-
-// Whether the balanced schedule can run this batch: bf16, few enough
-// sequences for the length scan, and a grid that fits every share.
-bool balanced_possible(int64_t num_seqs, int64_t hkv, int64_t head_dim, int64_t max_len,
-                       int64_t bs, int32_t dtype) {
-    if (dtype != PKV_BF16 || num_seqs > stream_max_seqs(hkv)) return false;
-    StreamPlan sp;
-    return plan_stream(num_seqs, hkv, hkv, head_dim, max_len, bs, &sp) == PKV_OK;
-}
-
-bool use_balanced(int64_t num_seqs, int64_t hkv, int64_t head_dim, int64_t max_len, int64_t bs,
-                  int32_t dtype, int64_t split_req) {
-    if (!balanced_possible(num_seqs, hkv, head_dim, max_len, bs, dtype)) return false;
-    if (split_req == PKV_SPLIT_BALANCED) return true;
-    return split_req == 0 && num_seqs >= kStreamMinSeqs &&
-           num_seqs * hkv * max_len * head_dim * 2 * 2 >= kStreamMinBytes;
-}
-
-// A balanced-schedule request that cannot be honoured (fp32 pool, too many
-// sequences, a batch no grid fits).
-bool balanced_refused(int64_t num_seqs, int64_t hkv, int64_t head_dim, int64_t max_len, int64_t bs,
-                      int32_t dtype, int64_t split_req) {
-    return split_req == PKV_SPLIT_BALANCED &&
-           !balanced_possible(num_seqs, hkv, head_dim, max_len, bs, dtype);
 }
 
 // Device-planned split schedule (bf16 and int8 pools): the grid is 2
@@ -295,36 +254,6 @@ bool use_planned(int64_t num_seqs, int64_t hkv, int64_t max_len, int64_t bs, int
                  int64_t split_req, SplitPlan *sp) {
     if (split_req != 0 && split_req != PKV_SPLIT_PLANNED) return false;
     return planned_possible(num_seqs, hkv, max_len, bs, dtype, sp);
-}
-
-int plan_stream(int64_t num_seqs, int64_t hkv, int64_t hq, int64_t head_dim, int64_t max_len,
-                int64_t bs, StreamPlan *p) {
-    if (num_seqs < 0 || hkv <= 0 || hq <= 0 || hq % hkv || head_dim <= 0 || max_len < 0 ||
-        !is_pow2(bs))
-        return PKV_ERR_SHAPE;
-    const int64_t hpw = heads_per_wg(hkv);
-    const int64_t groups = hkv / hpw;
-    const int64_t hqw = hpw * (hq / hkv);
-    // chunks of one sequence: ((off + L - 1) >> 4) - (off >> 4) + 1 <= (L + 14) / 16 + 1
-    const int64_t chunks_max = max_len > 0 ? (max_len + 14) / 16 + 1 : 0;
-    const int64_t units_max = num_seqs * groups * chunks_max;
-    // a workgroup's share of u units spans at most min(u, pairs) pairs and
-    // at most u * (16 / bs) table entries (bs < 16), u entries otherwise
-    const int64_t per_unit = bs >= 16 ? 1 : 16 / bs;
-    int64_t cap = (kBtLds - 1) / per_unit;
-    if (num_seqs * groups > kSegMax && cap > kSegMax) cap = kSegMax;
-    int64_t wgs = 2ll * cu_count();
-    if (units_max > wgs * cap) wgs = (units_max + cap - 1) / cap;
-    if (wgs > units_max) wgs = units_max;
-    if (wgs < 1) wgs = 1;
-    // the kernel forms units * workgroup index products in 64 bits
-    if (wgs > INT32_MAX / 2 || (units_max > 0 && wgs > (int64_t(1) << 62) / units_max))
-        return PKV_ERR_SHAPE;
-    p->wgs = wgs;
-    p->cnt_bytes = (num_seqs * hkv * 4 + 255) / 256 * 256;
-    p->ml_bytes = (2 * wgs * hqw * 2 * 4 + 255) / 256 * 256;
-    p->acc_bytes = 2 * wgs * hqw * head_dim * 4;
-    return PKV_OK;
 }
 
 int status_of(hipError_t e) {
@@ -555,14 +484,6 @@ PKV_API size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_kv
             return (size_t)-1;
         if (pp.total() > need) need = pp.total();
     }
-    if ((split_tokens == 0 || split_tokens == PKV_SPLIT_BALANCED) &&
-        num_seqs <= stream_max_seqs(num_kv_heads)) {
-        // the balanced schedule (bf16 pools) or the automatic split (fp32)
-        StreamPlan sp;
-        if (plan_stream(num_seqs, num_kv_heads, num_q_heads, head_dim, max_seq_len, block_size, &sp))
-            return (size_t)-1;
-        if (sp.total() > need) need = sp.total();
-    }
     return (size_t)need;
 }
 
@@ -576,14 +497,9 @@ PKV_API int32_t paged_attn_decode_schedule(int32_t num_seqs, int32_t num_kv_head
     const int st = plan_decode(num_seqs, num_kv_heads, num_q_heads, head_dim, max_seq_len,
                                block_size, split_tokens, &p, dtype);
     if (st) return st;
-    if (balanced_refused(num_seqs, num_kv_heads, head_dim, max_seq_len, block_size, dtype,
-                         split_tokens))
-        return PKV_ERR_UNSUPPORTED;
     if (use_planned(num_seqs, num_kv_heads, max_seq_len, block_size, dtype, split_tokens, nullptr))
         return PKV_SCHEDULE_PLANNED;
     if (split_tokens == PKV_SPLIT_PLANNED) return PKV_ERR_UNSUPPORTED;
-    if (use_balanced(num_seqs, num_kv_heads, head_dim, max_seq_len, block_size, dtype, split_tokens))
-        return 0;
     return (int32_t)p.split;
 }
 
@@ -605,14 +521,11 @@ int decode_impl(const pkv_pool *pool, int32_t layer, const void *q, int32_t num_
     if (layer < 0 || layer >= pool->num_layers) return PKV_ERR_LAYER;
     if (num_seqs < 0 || max_seq_len < 0 || bt_stride < 0 || num_q_heads <= 0 ||
         num_q_heads % pool->num_kv_heads != 0 ||
-        (split_tokens < 0 && split_tokens != PKV_SPLIT_BALANCED && split_tokens != PKV_SPLIT_PLANNED))
+        (split_tokens < 0 && split_tokens != PKV_SPLIT_PLANNED))
         return PKV_ERR_SHAPE;
     const int group = (int)(num_q_heads / pool->num_kv_heads);
     if (!decode_supported(pool->dtype, (int)pool->head_dim, group)) return PKV_ERR_UNSUPPORTED;
     if (k_new && pool->dtype == PKV_I8) return PKV_ERR_UNSUPPORTED;
-    if (balanced_refused(num_seqs, pool->num_kv_heads, pool->head_dim, max_seq_len, pool->block_size,
-                         pool->dtype, split_tokens))
-        return PKV_ERR_UNSUPPORTED;
     SplitPlan spl{};
     const bool planned = use_planned(num_seqs, pool->num_kv_heads, max_seq_len, pool->block_size,
                                      pool->dtype, split_tokens, &spl);
@@ -627,16 +540,7 @@ int decode_impl(const pkv_pool *pool, int32_t layer, const void *q, int32_t num_
     st = plan_decode(num_seqs, pool->num_kv_heads, num_q_heads, pool->head_dim, max_seq_len,
                      pool->block_size, planned ? (int32_t)spl.smin : split_tokens, &p, pool->dtype);
     if (st) return st;
-    const bool balanced = !planned && use_balanced(num_seqs, pool->num_kv_heads, pool->head_dim,
-                                                   max_seq_len, pool->block_size, pool->dtype,
-                                                   split_tokens);
-    StreamPlan sp{};
-    if (balanced) {
-        st = plan_stream(num_seqs, pool->num_kv_heads, num_q_heads, pool->head_dim, max_seq_len,
-                         pool->block_size, &sp);
-        if (st) return st;
-    }
-    const int64_t need = balanced ? sp.total() : p.total();
+    const int64_t need = p.total();
     if (need > 0) {
         if (!workspace || (int64_t)workspace_bytes < need) return PKV_ERR_WORKSPACE;
         if (!aligned16(workspace)) return PKV_ERR_ALIGN;
@@ -655,8 +559,8 @@ int decode_impl(const pkv_pool *pool, int32_t layer, const void *q, int32_t num_
     a.k_new = static_cast<const char *>(k_new);
     a.v_new = static_cast<const char *>(v_new);
     char *ws = need > 0 ? static_cast<char *>(workspace) : nullptr;
-    const int64_t cnt_bytes = balanced ? sp.cnt_bytes : p.cnt_bytes;
-    const int64_t ml_bytes = balanced ? sp.ml_bytes : p.ml_bytes;
+    const int64_t cnt_bytes = p.cnt_bytes;
+    const int64_t ml_bytes = p.ml_bytes;
     a.ws_cnt = ws ? reinterpret_cast<uint32_t *>(ws) : nullptr;
     a.ws_ml = ws ? reinterpret_cast<float *>(ws + cnt_bytes) : nullptr;
     a.ws_acc = ws ? reinterpret_cast<float *>(ws + cnt_bytes + ml_bytes) : nullptr;
@@ -670,8 +574,6 @@ int decode_impl(const pkv_pool *pool, int32_t layer, const void *q, int32_t num_
     a.heads_per_wg = (int32_t)hpw;
     a.head_groups = (int32_t)groups;
     a.fused_merge = p.max_splits <= kFusedMergeMaxSplits;
-    a.stream_wgs = balanced ? (int32_t)sp.wgs : 0;
-    a.seg_chunks = (int32_t)(max_split_tokens(pool->block_size) / kChunkTokens);
     a.plan = planned ? (int32_t)spl.wgs : 0;
     a.max_len = max_seq_len;
     if (clear_cnt && ws && cnt_bytes > 0) {

@@ -142,8 +142,6 @@ struct DecodeArgs {
     int32_t heads_per_wg;
     int32_t head_groups;
     int32_t fused_merge;   // 1: the last split of a (sequence, head group) merges; 0: merge kernel
-    int32_t stream_wgs;    // > 0: balanced schedule with this many workgroups (bf16)
-    int32_t seg_chunks;    // balanced schedule: most chunks staged at once
     int32_t plan;          // > 0: device-planned split, this many workgroups (split_tokens: the smallest split)
     int32_t max_len;       // the caller's max_seq_len (device-planned split clamps to it)
 };
@@ -155,13 +153,6 @@ constexpr int kFusedMergeMaxSplits = 16;
 // Device-planned split schedule: at most this many sequences (one per lane
 // of the wavefront that plans).
 constexpr int kPlanMaxSeqs = 64;
-
-// Balanced decode schedule: every workgroup reads every sequence length
-// (at most kStreamSeqsPerThread per thread) and lists the (head group,
-// sequence) pairs its share of the work touches, at most kSegMax of them;
-// its share must fit the LDS table buffer (the host sizes the grid so).
-constexpr int kStreamSeqsPerThread = 4;
-constexpr int kSegMax = 80;
 
 // Prefill / append attention: the last n_s = q_start[s+1] - q_start[s]
 // tokens of sequence s are its queries (rows q_start[s].. of q and out).

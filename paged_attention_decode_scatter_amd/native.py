@@ -42,8 +42,6 @@ SYMBOLS = (
 )
 
 
-# split_tokens value asking paged_attn_decode for the balanced schedule
-SPLIT_BALANCED = -1
 # split_tokens value asking for the device-planned split schedule, and the
 # value paged_attn_decode_schedule returns for that schedule
 SPLIT_PLANNED = -2
@@ -336,9 +334,9 @@ def paged_attn_decode_split_tokens(num_seqs, num_kv_heads, max_seq_len, block_si
 
 def paged_attn_decode_schedule(num_seqs, num_kv_heads, num_q_heads, head_dim, max_seq_len,
                                block_size, dtype, split_tokens=0):
-    """Tokens per split of the split schedule, SCHEDULE_PLANNED (1) for the
-    device-planned split schedule, or 0 for the balanced schedule, for a
-    pool of torch dtype `dtype` (torch.int8: a quantised pool)."""
+    """Tokens per split of the split schedule, or SCHEDULE_PLANNED (1) for
+    the device-planned split schedule, for a pool of torch dtype `dtype`
+    (torch.int8: a quantised pool)."""
     code = {torch.float32: 0, torch.bfloat16: 1, torch.int8: 2}.get(dtype)
     if code is None:
         raise PagedKVError("paged_attn_decode_schedule", -2)

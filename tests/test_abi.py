@@ -130,7 +130,7 @@ def test_decode_argument_checks(lib):
     assert call(layer=3) == LAYER
     assert call(split=24) == SHAPE     # not a multiple of 16
     assert call(split=-16) == SHAPE
-    assert call(split=-1, p=pool(dtype=0)) == UNSUP   # balanced schedule: bf16 only
+    assert call(split=-1) == SHAPE     # negative: only the planned-schedule request
     assert call(ns=0) == OK
     assert call(q=None) == NULL
     assert call(out=A + 2) == ALIGN
@@ -188,11 +188,10 @@ def test_workspace_size_and_split_choice(lib):
     ws = lib.paged_attn_decode_workspace_size
     # one split covers everything: no workspace
     assert ws(1, 2, 4, 64, 30, 16, 64) == 0
-    # automatic choice: room for the balanced schedule of bf16 pools (two
-    # record slots per workgroup) or for the automatic split of fp32 pools,
-    # whichever is larger
+    # automatic choice: room for the schedule any pool dtype takes (the
+    # automatic split differs between bf16 and the other pools)
     split = lib.paged_attn_decode_split_tokens
-    assert ws(1, 2, 4, 64, 30, 16, 0) > 0
+    assert ws(1, 2, 4, 64, 30, 16, 0) == 0    # one split in either schedule
     assert ws(8, 8, 64, 128, 32768, 16, 0) >= ws(8, 8, 64, 128, 32768, 16, split(8, 8, 32768, 16))
     # split counters (seqs x kv heads) and the (m, l) block, each padded to
     # 256 bytes, then the fp32 accumulators.  Splits cover flat table
@@ -211,6 +210,13 @@ def test_workspace_size_and_split_choice(lib):
     # the choices on 256 compute units (the count assumed without a device)
     assert split(32, 8, 2048, 16) == 256
     assert split(8, 8, 32768, 16) == 2048
+    # many (sequence, kv head) pairs (>= 2 per compute unit): up to 32 work
+    # items per compute unit, no long-split rule
+    assert split(96, 8, 4096, 16) == 512
+    assert split(128, 8, 3072, 16) == 512
+    assert split(256, 8, 1536, 16) == 512
+    # the split stops growing once it covers max_seq_len
+    assert split(2000, 8, 128, 16) == 256
     sched = lib.paged_attn_decode_schedule
     assert sched(8, 8, 64, 128, 32768, 16, 1, 0) == 2048   # bf16: one workgroup per CU
     assert sched(8, 8, 64, 128, 32768, 16, 2, 0) == 1024   # int8: two per CU
@@ -266,10 +272,8 @@ def test_prefill_argument_checks(lib):
 def test_decode_schedule_choice(lib):
     """The automatic schedule: the device-planned split for bf16 batches of
     at most 64 sequences with at most (compute units / 2) (sequence, head
-    group) pairs and max_seq_len / 2 + 32 within the largest split; else
-    balanced for bf16 batches of at least 32 sequences with at least 512 MiB
-    of K/V at max_seq_len (and few enough sequences for the length scan: 4
-    per thread); the automatic split otherwise; an explicit split is always
+    group) pairs and max_seq_len / 2 + 32 within the largest split (also
+    int8 pools); the automatic split otherwise; an explicit split is always
     kept.  (No device here: 256 compute units are assumed.)"""
     f = lib.paged_attn_decode_schedule
     F32, BF16 = 0, 1
@@ -279,9 +283,9 @@ def test_decode_schedule_choice(lib):
     assert f(64, 8, 32, 128, 4096, 16, BF16, 0) == PLANNED                 # prefix sharing
     assert f(32, 8, 32, 128, 2048, 16, F32, 0) == split(32, 8, 2048, 16)
     assert f(32, 8, 32, 128, 2048, 16, 2, 0) == PLANNED                    # int8 pool
-    assert f(65, 8, 32, 128, 4096, 16, BF16, 0) == 0                       # 65 sequences, 1 GiB
+    assert f(65, 8, 32, 128, 4096, 16, BF16, 0) == split(65, 8, 4096, 16)  # 65 sequences, 1 GiB
     assert f(65, 8, 32, 128, 1024, 16, BF16, 0) == split(65, 8, 1024, 16)  # 65 sequences, 0.27 GiB
-    assert f(64, 16, 64, 128, 4096, 16, BF16, 0) == 0                      # 4 head groups: 256 pairs
+    assert f(64, 16, 64, 128, 4096, 16, BF16, 0) == split(64, 16, 4096, 16)  # 4 head groups: 256 pairs
     assert f(8, 8, 64, 128, 32768, 16, BF16, 0) == split(8, 8, 32768, 16)  # past the largest split
     assert f(8, 8, 64, 128, 32768, 16, BF16, SPLIT_PLANNED) == UNSUP
     assert f(2, 2, 8, 128, 100, 16, F32, SPLIT_PLANNED) == UNSUP
@@ -291,8 +295,8 @@ def test_decode_schedule_choice(lib):
     assert f(5000, 8, 32, 128, 4096, 16, BF16, 0) == split(5000, 8, 4096, 16)
     assert f(8, 8, 64, 128, 32768, 16, 7, 0) == DTYPE
     assert f(8, 8, 60, 128, 32768, 16, BF16, 0) == SHAPE
-    assert f(2, 2, 8, 128, 100, 16, BF16, -1) == 0                         # asked for
-    assert f(2, 2, 8, 128, 100, 16, F32, -1) == UNSUP
+    assert f(2, 2, 8, 128, 100, 16, BF16, -1) == SHAPE
+    assert f(2, 2, 8, 128, 100, 16, F32, -1) == SHAPE
 
 
 def test_read_blocks_argument_checks(lib):
@@ -405,7 +409,7 @@ def test_quantized_pool_checks(lib):
     def decode(p, split=0, hq=32):
         return dec(by(p), 0, A, hq, A, 8, A, A, 4, 100, 0.1, split, A, A, 1 << 30, None)
 
-    assert decode(pool(dtype=I8), split=-1) == UNSUP        # no balanced schedule
+    assert decode(pool(dtype=I8), split=-1) == SHAPE
     assert decode(pool(dtype=I8, d=96)) == UNSUP
     assert decode(pool(dtype=I8), hq=24) == UNSUP
     assert decode(pool(dtype=I8, ks=None)) == NULL
@@ -417,8 +421,8 @@ def test_quantized_pool_checks(lib):
     f = lib.paged_attn_decode_schedule
     split = lib.paged_attn_decode_split_tokens
     assert f(32, 8, 32, 128, 2048, 16, I8, 0) == 1            # the device-planned split
-    assert f(65, 8, 32, 128, 2048, 16, I8, 0) == 1024     # no long-split rule for int8
-    assert f(32, 8, 32, 128, 2048, 16, I8, -1) == UNSUP
+    assert f(65, 8, 32, 128, 2048, 16, I8, 0) == 256      # 520 pairs: up to 32 items per CU
+    assert f(32, 8, 32, 128, 2048, 16, I8, -1) == SHAPE
 
 
 def test_quantized_pool_binding():

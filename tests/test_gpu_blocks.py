@@ -139,7 +139,7 @@ def combined_copy(w):
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_combined_layout_matches_dense(dev, dtype):
-    """Append, gather, decode (split and balanced), the one-launch decode
+    """Append, gather, decode (split and planned), the one-launch decode
     step and prefill on the combined layout: every output and every pool
     byte equals the same call's on separate dense K and V pools."""
     w = W.decode_batch(device=dev, seed=540, num_seqs=7, min_len=1, max_len=600,
@@ -162,7 +162,7 @@ def test_combined_layout_matches_dense(dev, dtype):
         N.kv_gather(kp, vp, w.layer, w.block_tables, w.seq_lens, w.offsets, rs, w.max_seq_len,
                     ko, vo)
         res = [ko, vo]
-        splits = (0, 64, N.SPLIT_BALANCED) if dtype == torch.bfloat16 else (0, 64)
+        splits = (0, 64, N.SPLIT_PLANNED) if dtype == torch.bfloat16 else (0, 64)
         for split in splits:
             res.append(N.paged_attn_decode(kp, vp, w.layer, w.q, w.block_tables, w.seq_lens,
                                            w.offsets, w.max_seq_len, w.scale,

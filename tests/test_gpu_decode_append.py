@@ -72,7 +72,7 @@ def run_append(w, kn, vn, split=0, ws=None):
 
 
 CASES = [(torch.bfloat16, 16), (torch.bfloat16, 64), (torch.bfloat16, 0),
-         (torch.bfloat16, N.SPLIT_BALANCED), (torch.float32, 16), (torch.float32, 0)]
+         (torch.bfloat16, N.SPLIT_PLANNED), (torch.float32, 16), (torch.float32, 0)]
 
 
 @pytest.mark.parametrize("dtype,split", CASES)
@@ -107,7 +107,7 @@ def test_decode_append_other_block_sizes(dev, bs):
         assert max_abs_err(got, ref) <= TOL[dtype]
 
 
-@pytest.mark.parametrize("split", [0, 64, N.SPLIT_BALANCED])
+@pytest.mark.parametrize("split", [0, 64, N.SPLIT_PLANNED])
 def test_decode_append_equals_append_then_decode(dev, split):
     """Same schedule, same bits: the fused step's output is the two-call
     step's output, and both leave the same pool."""
@@ -193,7 +193,7 @@ def oracle_partial_step(w, kn, vn, lens_attend, write):
 
 
 STALE_CASES = [(torch.bfloat16, 0), (torch.bfloat16, 64), (torch.bfloat16, 16),
-               (torch.bfloat16, N.SPLIT_BALANCED), (torch.bfloat16, N.SPLIT_PLANNED),
+               (torch.bfloat16, N.SPLIT_PLANNED),
                (torch.float32, 64), (torch.float32, 0)]
 
 

@@ -96,7 +96,7 @@ def test_block_manager_drives_append_scatter_gather_decode(dev):
 
     q = torch.randn((len(live), hq, d), generator=gen, device=dev).to(torch.bfloat16)
     scale = 1.0 / np.sqrt(d)
-    for split in (0, 64, N.SPLIT_BALANCED):
+    for split in (0, 64, N.SPLIT_PLANNED):
         out = N.paged_attn_decode(k_pool, v_pool, layer, q, bt, sl, of, int(lens.max()), scale,
                                   split_tokens=split)
         ref = O.decode(host(k_pool), host(v_pool), layer, host(q), tab, lens, offs, scale)

@@ -26,7 +26,7 @@ def ibits(t):
 
 
 @pytest.mark.parametrize("fused_append", [False, True])
-@pytest.mark.parametrize("split", [0, 64, N.SPLIT_BALANCED])
+@pytest.mark.parametrize("split", [0, 64, N.SPLIT_PLANNED])
 def test_decode_step_graph_replays_match_eager(dev, split, fused_append):
     w = W.decode_tokens(W.decode_batch(device=dev, seed=81, num_seqs=12, min_len=1, max_len=700,
                                        num_blocks=1024, num_layers=3, num_kv_heads=2,

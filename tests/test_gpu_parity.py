@@ -307,7 +307,7 @@ def test_gather_full_size_bit_exact(dev, name):
 def test_decode_small_grid(dev, dtype, head_dim, group):
     w = small_decode(dev, dtype=dtype, head_dim=head_dim, group=group, seed=30 + group)
     ref = oracle_decode_for(w)
-    for split in (16, 64, 0) + ((N.SPLIT_BALANCED, N.SPLIT_PLANNED) if dtype == torch.bfloat16 else ()):
+    for split in (16, 64, 0) + ((N.SPLIT_PLANNED,) if dtype == torch.bfloat16 else ()):
         got = run_decode(w, split)
         err = max_abs_err(got, ref)
         assert err <= TOL[dtype], (split, err)
@@ -322,14 +322,14 @@ def test_decode_other_block_sizes(dev, bs, dtype):
                        num_blocks=2048 // bs + 64, num_layers=2, num_kv_heads=2, head_dim=128,
                        num_q_heads=8, dtype=dtype, layer=1, offsets="random", block_size=bs)
     ref = oracle_decode_for(w)
-    for split in (16, 64, 0) + ((N.SPLIT_BALANCED, N.SPLIT_PLANNED) if dtype == torch.bfloat16 else ()):
+    for split in (16, 64, 0) + ((N.SPLIT_PLANNED,) if dtype == torch.bfloat16 else ()):
         if split > 0 and split // bs + 2 > 1024:
             continue
         got = run_decode(w, split)
         assert max_abs_err(got, ref) <= TOL[dtype], split
 
 
-@pytest.mark.parametrize("split", [16, 32, 0, N.SPLIT_BALANCED, N.SPLIT_PLANNED])
+@pytest.mark.parametrize("split", [16, 32, 0, N.SPLIT_PLANNED])
 def test_decode_edge_lengths_and_offsets(dev, split):
     w = small_decode(dev, seed=40, num_seqs=18, min_len=40, max_len=40, offsets=None)
     set_lens(w, [0, 1, 15, 16, 17, 33] * 3, [0] * 6 + [1] * 6 + [15] * 6)
@@ -437,7 +437,7 @@ def test_validate_counts_violations(dev):
     assert n == 5 + pad3, (n, pad3)
 
 
-@pytest.mark.parametrize("split", [64, 16, 0, N.SPLIT_BALANCED, N.SPLIT_PLANNED])
+@pytest.mark.parametrize("split", [64, 16, 0, N.SPLIT_PLANNED])
 def test_decode_workspace_reuse_leaves_counters_zero(dev, split):
     """One zeroed workspace serves successive calls of different shapes: each
     call gives the same bits as a call with a fresh workspace and leaves the
@@ -464,36 +464,28 @@ def test_decode_workspace_reuse_leaves_counters_zero(dev, split):
         assert max_abs_err(got, oracle_decode_for(w)) <= TOL[w.dtype]
 
 
-@pytest.mark.parametrize("num_seqs,max_len,num_blocks", [(1, 3000, 256), (3, 5000, 1024),
-                                                         (300, 90, 2400), (40, 2048, 5200)])
-def test_decode_balanced_schedule(dev, num_seqs, max_len, num_blocks):
-    """The balanced schedule (asked for explicitly; split_tokens = 0 takes it
-    only for large batches): every
-    workgroup gets an equal share of the (head group, sequence, chunk) units,
-    so one sequence can be spread over hundreds of workgroups (first case)
-    and one workgroup can hold many sequences (300 sequences: more than the
-    threads of the length scan, with every 7th sequence empty).  A second
-    call on the same workspace gives the same bits and the merge counters
-    are zero after each call."""
-    w = small_decode(dev, seed=70 + num_seqs, num_seqs=num_seqs,
-                     min_len=max_len if num_seqs == 1 else 1, max_len=max_len,
+@pytest.mark.parametrize("num_seqs,max_len,num_blocks", [(300, 90, 2400), (96, 700, 4400)])
+def test_decode_many_sequences_auto_split(dev, num_seqs, max_len, num_blocks):
+    """Batches of more sequences than the device-planned schedule takes (at
+    most 64) run the split schedule with the automatic split (with many
+    (sequence, kv head) pairs: up to 32 work items per compute unit), every
+    7th sequence empty.  A second call on the same workspace gives the same
+    bits and the merge counters are zero after each call."""
+    w = small_decode(dev, seed=70 + num_seqs, num_seqs=num_seqs, min_len=1, max_len=max_len,
                      num_blocks=num_blocks)
-    if num_seqs == 1:
-        set_lens(w, [max_len - 7], [7])
-    if num_seqs > 3:
-        lens = host(w.seq_lens).copy()
-        lens[::7] = 0
-        set_lens(w, lens.tolist(), host(w.offsets).tolist())
-    bal = N.SPLIT_BALANCED
-    assert N.paged_attn_decode_schedule(w.num_seqs, w.num_kv_heads, w.num_q_heads, w.head_dim,
-                                        w.max_seq_len, w.block_size, w.dtype, bal) == 0
+    lens = host(w.seq_lens).copy()
+    lens[::7] = 0
+    set_lens(w, lens.tolist(), host(w.offsets).tolist())
+    sched = N.paged_attn_decode_schedule(w.num_seqs, w.num_kv_heads, w.num_q_heads, w.head_dim,
+                                         w.max_seq_len, w.block_size, w.dtype, 0)
+    assert sched > 0 and sched != N.SCHEDULE_PLANNED and sched % 16 == 0
     need = N.paged_attn_decode_workspace_size(w.num_seqs, w.num_kv_heads, w.num_q_heads,
-                                              w.head_dim, w.max_seq_len, w.block_size, bal)
-    ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+                                              w.head_dim, w.max_seq_len, w.block_size, 0)
+    ws = torch.zeros(max(need, 16), dtype=torch.uint8, device=dev)
     cnt = (w.num_seqs * w.num_kv_heads * 4 + 255) // 256 * 256
-    got = run_decode(w, bal, workspace=ws)
+    got = run_decode(w, 0, workspace=ws)
     assert int(torch.count_nonzero(ws[:cnt])) == 0
-    again = run_decode(w, bal, workspace=ws)
+    again = run_decode(w, 0, workspace=ws)
     assert int(torch.count_nonzero(ws[:cnt])) == 0
     assert torch.equal(got.view(torch.int16), again.view(torch.int16))
     assert max_abs_err(got, oracle_decode_for(w)) <= TOL[w.dtype]

@@ -177,10 +177,10 @@ def test_int8_decode_edges(dev):
     assert max_abs_err(run(w2, k2, v2, 16), oracle_decode(w2, k2, v2)) <= TOL
 
 
-def test_int8_decode_refuses_balanced(dev):
+def test_int8_decode_rejects_negative_split(dev):
     w, k, v = workload(dev, 670, num_seqs=2, max_len=50)
     with pytest.raises(N.PagedKVError):
-        run(w, k, v, N.SPLIT_BALANCED)
+        run(w, k, v, -1)
 
 
 def test_int8_write_then_decode(dev):

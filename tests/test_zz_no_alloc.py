@@ -53,7 +53,7 @@ def same_bits(a, b):
 
 
 CASES = [(torch.bfloat16, 0), (torch.bfloat16, 64), (torch.bfloat16, 16),
-         (torch.bfloat16, N.SPLIT_BALANCED), (torch.float32, 16), (torch.float32, 0)]
+         (torch.bfloat16, N.SPLIT_PLANNED), (torch.float32, 16), (torch.float32, 0)]
 
 
 @pytest.mark.parametrize("dtype,split", CASES)
