@@ -142,7 +142,7 @@ def prefill_setup(w, N, W):
     return args, info, keep
 
 
-def prefill_attention(w, N, W, reps=6):
+def prefill_attention(w, N, W, reps=4):
     """Prefill / append attention on the prefix-sharing batch (64 sequences
     whose first 32 blocks are shared, from a common first-block offset):
     every suffix token is a query, attending causally to the shared prefix
@@ -152,21 +152,31 @@ def prefill_attention(w, N, W, reps=6):
     -- against the dense bf16 matrix-core peak."""
     import torch
 
+    import numpy as np
+
     lib = N.load_library()
     args, info, keep = prefill_setup(w, N, W)
-    if lib.paged_attn_prefill(*args[0]):
-        raise RuntimeError("paged_attn_prefill failed")
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    a.record()
-    for i in range(reps):
-        lib.paged_attn_prefill(*args[(i + 1) % len(args)])
-    b.record()
-    torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / reps
+    for i in range(3):
+        if lib.paged_attn_prefill(*args[i]):
+            raise RuntimeError("paged_attn_prefill failed")
+    # blocks of `reps` back-to-back calls (layer rotated), one event pair
+    # around each block; the median block
+    blocks = []
+    for blk in range(5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for i in range(reps):
+            lib.paged_attn_prefill(*args[(3 + blk * reps + i) % len(args)])
+        b.record()
+        torch.cuda.synchronize()
+        blocks.append(a.elapsed_time(b) / reps)
+    ms = float(np.median(blocks))
     flops = info["flops"]
-    return dict(info, ms=ms, **{"TFLOP/s": flops / ms / 1e9,
-                                "frac_of_bf16_mfma_peak": flops / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS})
+    return dict(info, ms=ms, ms_blocks=blocks,
+                timing=f"3 warm-up calls, then 5 blocks of {reps} back-to-back calls (layer rotated), "
+                       "one event pair per block, median block",
+                **{"TFLOP/s": flops / ms / 1e9, "frac_of_bf16_mfma_peak": flops / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS})
 
 
 def int8_decode(base, N, W, reps=32):
