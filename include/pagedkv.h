@@ -19,7 +19,7 @@
  *   device memory.  One "row" is the num_kv_heads*head_dim elements of one
  *   token at one layer.  block_size must be a power of two.
  * - Element types: PKV_F32 (float) or PKV_BF16 (bfloat16 bit patterns),
- *   or a quantised pool, PKV_I8 (see "Quantised pools" below).
+ *   or a quantised pool, PKV_I8 or PKV_I4 (see "Quantised pools" below).
  * - A block table is a row of int32 physical block ids in logical order
  *   [P3 sec. 2.2]; tables are stored (num_seqs, bt_stride) row-major.  Each
  *   sequence also has a first-block start offset in [0, block_size) (prefix
@@ -58,7 +58,7 @@ extern "C" {
 #define PKV_API __attribute__((visibility("default")))
 
 /* element types */
-enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_I8 = 2 };
+enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_I8 = 2, PKV_I4 = 3 };
 
 /* status codes */
 enum {
@@ -93,7 +93,7 @@ enum {
  * block_stride = two dense blocks.  A nonzero block_stride must be a
  * multiple of 16 and at least one dense block.
  *
- * Quantised pools (dtype PKV_I8) [P3 sec. 6: quantised KV, int8 / int4, as
+ * Quantised pools (dtype PKV_I8, PKV_I4) [P3 sec. 6: quantised KV, int8 / int4, as
  * the next compression step of a paged cache; the pages give no method, so
  * this is the plain symmetric reading]: k / v hold int8 codes in the layout
  * above, and k_scale / v_scale (16-byte aligned, device) one float scale
@@ -102,14 +102,18 @@ enum {
  * head's tokens in a block are contiguous.  A row x (head_dim values) is
  * stored as scale s = max|x| / 127 and codes round-half-even(x / s),
  * clamped to [-127, 127] (s = 0 and codes 0 for a zero row), both
- * computed in IEEE float32; its value is code * s.  The rows written into
- * (k_src / v_src) and the queries and outputs of decode are bfloat16.
+ * computed in IEEE float32; its value is code * s.  PKV_I4 is the same
+ * reading at four bits: s = max|x| / 7, codes in [-7, 7], two codes per
+ * byte -- element 2i of a row in the low nibble of byte i, element 2i + 1
+ * in the high nibble, four-bit two's complement -- so a row is
+ * num_kv_heads * head_dim / 2 bytes in the layout above.  The rows written
+ * into (k_src / v_src) and the queries and outputs of decode are bfloat16.
  * Entry points that take a quantised pool: kv_scatter, kv_append
  * (quantise on write), kv_gather (writes bf16(code * s)),
- * paged_attn_decode (split schedule; dequantises inside the kernel),
- * kv_copy_blocks and kv_swap_out / kv_swap_in (codes and scales).  The
- * others return PKV_ERR_UNSUPPORTED for it.  k_scale / v_scale are ignored
- * for float pools. */
+ * paged_attn_decode (split and planned schedules; dequantises inside the
+ * kernel), kv_copy_blocks and kv_swap_out / kv_swap_in (codes and
+ * scales).  The others return PKV_ERR_UNSUPPORTED for it.  k_scale /
+ * v_scale are ignored for float pools. */
 typedef struct pkv_pool {
     void *k;
     void *v;
@@ -248,7 +252,7 @@ PKV_API int32_t paged_attn_decode_split_tokens(int32_t num_seqs, int32_t num_kv_
 
 /*
  * paged_attn_decode_schedule -- which work schedule paged_attn_decode takes
- * for these sizes, pool dtype (PKV_F32 / PKV_BF16 / PKV_I8) and
+ * for these sizes, pool dtype (PKV_F32 / PKV_BF16 / PKV_I8 / PKV_I4) and
  * split_tokens:
  *   > 0  the split schedule with this many tokens per split: one workgroup
  *        per (sequence, split of split_tokens flat positions, group of kv

@@ -283,19 +283,23 @@ hipError_t launch_gather(const GatherArgs &a, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
-// Quantised pools [P3 sec. 6 names quantised KV; the reading: one float32
-// scale s = max|x| / 127 per (token, kv head) row, codes
-// round-half-even(x / s) clamped to [-127, 127], all in IEEE float32].
+// Quantised pools [P3 sec. 6 names quantised KV, int8 / int4; the reading:
+// one float32 scale s = max|x| / Q per (token, kv head) row, codes
+// round-half-even(x / s) clamped to [-Q, Q], all in IEEE float32; Q = 127
+// for int8, 7 for int4, whose codes are packed two per byte, element 2i of
+// a row in the low nibble of byte i, four-bit two's complement].
 //
 // Quantising scatter / append: LPH = D/8 lanes hold one (token, head) row,
 // 8 bf16 values each; the row's max |x| is reduced over those lanes, and
-// each lane stores its 8 codes (8 bytes); the lane with piece 0 stores the
-// scale.  The slot is given (kv_scatter) or computed as the append does.
+// each lane stores its 8 codes (8 bytes, or 4 for int4); the lane with
+// piece 0 stores the scale.  The slot is given (kv_scatter) or computed as
+// the append does.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
+template <int Q>
 __device__ __forceinline__ uint32_t quant_code(float x, float s) {
-    const float c = s > 0.0f ? fminf(fmaxf(__builtin_rintf(__fdiv_rn(x, s)), -127.0f), 127.0f) : 0.0f;
+    const float c = s > 0.0f ? fminf(fmaxf(__builtin_rintf(__fdiv_rn(x, s)), -(float)Q), (float)Q) : 0.0f;
     return (uint32_t)(int32_t)c & 0xffu;
 }
 
@@ -305,11 +309,25 @@ __device__ __forceinline__ uint2 quant_piece(u32x4 x, float s) {
     uint32_t c[2] = {0, 0};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const uint32_t lo = quant_code(bf16_to_f32(w[i] & 0xffffu), s);
-        const uint32_t hi = quant_code(bf16_to_f32(w[i] >> 16), s);
+        const uint32_t lo = quant_code<127>(bf16_to_f32(w[i] & 0xffffu), s);
+        const uint32_t hi = quant_code<127>(bf16_to_f32(w[i] >> 16), s);
         c[i >> 1] |= (lo | (hi << 8)) << (16 * (i & 1));
     }
     return make_uint2(c[0], c[1]);
+}
+
+// 8 bf16 values -> 8 int4 codes (one word): byte i holds element 2i in its
+// low nibble and element 2i + 1 in its high nibble.
+__device__ __forceinline__ uint32_t quant_piece4(u32x4 x, float s) {
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+    uint32_t c = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = quant_code<7>(bf16_to_f32(w[i] & 0xffffu), s) & 0xfu;
+        const uint32_t hi = quant_code<7>(bf16_to_f32(w[i] >> 16), s) & 0xfu;
+        c |= (lo | (hi << 4)) << (8 * i);
+    }
+    return c;
 }
 
 __device__ __forceinline__ float piece_amax(u32x4 x) {
@@ -321,8 +339,10 @@ __device__ __forceinline__ float piece_amax(u32x4 x) {
     return m;
 }
 
-template <int D>
+template <int D, int QB>
 __global__ __launch_bounds__(256) void scatter_q8_kernel(ScatterQ8Args a) {
+    constexpr int Q = QB == 8 ? 127 : 7;
+    constexpr int HB = D * QB / 8;   // bytes of one (token, head) row of codes
     constexpr int LPH = D / 8;       // lanes per (token, head) row
     constexpr int RPW = 256 / LPH;   // rows per workgroup
     const int p = threadIdx.x % LPH;
@@ -366,11 +386,16 @@ __global__ __launch_bounds__(256) void scatter_q8_kernel(ScatterQ8Args a) {
         vm = fmaxf(vm, __shfl_xor(vm, m));
     }
     if (!ok) return;
-    const float ks = __fdiv_rn(km, 127.0f), vs = __fdiv_rn(vm, 127.0f);
+    const float ks = __fdiv_rn(km, (float)Q), vs = __fdiv_rn(vm, (float)Q);
     const int64_t b = slot >> a.lbs, r = slot & bsm;
-    const int64_t dst = b * a.block_stride + a.layer_off + r * (H * D) + h * D + 8 * p;
-    *reinterpret_cast<uint2 *>(a.kpool + dst) = quant_piece(kx, ks);
-    if (has_v) *reinterpret_cast<uint2 *>(a.vpool + dst) = quant_piece(vx, vs);
+    const int64_t dst = b * a.block_stride + a.layer_off + r * (H * HB) + h * HB + (QB * p);
+    if constexpr (QB == 8) {
+        *reinterpret_cast<uint2 *>(a.kpool + dst) = quant_piece(kx, ks);
+        if (has_v) *reinterpret_cast<uint2 *>(a.vpool + dst) = quant_piece(vx, vs);
+    } else {
+        *reinterpret_cast<uint32_t *>(a.kpool + dst) = quant_piece4(kx, ks);
+        if (has_v) *reinterpret_cast<uint32_t *>(a.vpool + dst) = quant_piece4(vx, vs);
+    }
     if (p == 0) {
         const int64_t so = b * a.sc_block + (h << a.lbs) + r;
         a.ks[so] = ks;
@@ -382,25 +407,31 @@ hipError_t launch_scatter_q8(const ScatterQ8Args &a, hipStream_t s) {
     const int64_t rows = a.num_tokens * a.num_kv_heads;
     const int64_t rpw = 256 / (a.head_dim / 8);
     const dim3 grid((unsigned)((rows + rpw - 1) / rpw));
-    if (a.head_dim == 128)
-        hipLaunchKernelGGL(scatter_q8_kernel<128>, grid, dim3(256), 0, s, a);
-    else if (a.head_dim == 64)
-        hipLaunchKernelGGL(scatter_q8_kernel<64>, grid, dim3(256), 0, s, a);
+    if (a.head_dim == 128 && a.qbits == 8)
+        hipLaunchKernelGGL((scatter_q8_kernel<128, 8>), grid, dim3(256), 0, s, a);
+    else if (a.head_dim == 64 && a.qbits == 8)
+        hipLaunchKernelGGL((scatter_q8_kernel<64, 8>), grid, dim3(256), 0, s, a);
+    else if (a.head_dim == 128 && a.qbits == 4)
+        hipLaunchKernelGGL((scatter_q8_kernel<128, 4>), grid, dim3(256), 0, s, a);
+    else if (a.head_dim == 64 && a.qbits == 4)
+        hipLaunchKernelGGL((scatter_q8_kernel<64, 4>), grid, dim3(256), 0, s, a);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
-// Dequantising gather: each lane turns one 16-code piece of a row into 16
-// bf16 values bf16(code * scale) (float32 product, nearest-even).  Tokens
-// whose table entry is missing or out of range give zero rows.
+// Dequantising gather: each lane turns one 16-byte piece of a row (16 int8
+// codes or 32 int4 codes) into bf16 values bf16(code * scale) (float32
+// product, nearest-even).  Tokens whose table entry is missing or out of
+// range give zero rows.
 __device__ __forceinline__ uint32_t bf16_rne(float f) {
     const uint32_t u = __float_as_uint(f);
     return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
-template <int D>
+template <int D, int QB>
 __global__ __launch_bounds__(kCopyThreads) void gather_q8_kernel(GatherArgs a) {
+    constexpr int CPP = 128 / QB;   // codes per 16-byte piece
     const int seq = blockIdx.x / a.tiles_per_seq;
     const int tile = blockIdx.x - seq * a.tiles_per_seq;
     const int64_t len = a.seq_lens[seq];
@@ -423,8 +454,8 @@ __global__ __launch_bounds__(kCopyThreads) void gather_q8_kernel(GatherArgs a) {
         const int64_t j = p >> a.pool.lbs;
         const int32_t b = j < a.bt_stride ? a.block_tables[(int64_t)seq * a.bt_stride + j] : -1;
         const bool okb = b >= 0 && b < a.pool.num_blocks;
-        const int64_t h = (16 * ch) / D;
-        u32x4 o[2][2] = {};
+        const int64_t h = (CPP * ch) / D;
+        u32x4 o[2][CPP / 8] = {};
         for (int tsr = 0; tsr < (has_v ? 2 : 1); ++tsr) {
             if (!okb) break;
             const char *pool = tsr ? a.pool.v : a.pool.k;
@@ -433,35 +464,49 @@ __global__ __launch_bounds__(kCopyThreads) void gather_q8_kernel(GatherArgs a) {
                                  (p & bsm) * a.pool.row_bytes + 16 * ch);
             const float s = sc[(int64_t)b * a.pool.sc_block + (h << a.pool.lbs) + (p & bsm)];
             const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-            uint32_t r[8];
+            uint32_t r[CPP / 2];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
+                if constexpr (QB == 8) {
 #pragma unroll
-                for (int k = 0; k < 2; ++k) {
-                    const float lo = (float)(int8_t)(w[i] >> (16 * k)) * s;
-                    const float hi = (float)(int8_t)(w[i] >> (16 * k + 8)) * s;
-                    r[2 * i + k] = bf16_rne(lo) | (bf16_rne(hi) << 16);
+                    for (int k = 0; k < 2; ++k) {
+                        const float lo = (float)(int8_t)(w[i] >> (16 * k)) * s;
+                        const float hi = (float)(int8_t)(w[i] >> (16 * k + 8)) * s;
+                        r[2 * i + k] = bf16_rne(lo) | (bf16_rne(hi) << 16);
+                    }
+                } else {
+                    // byte k of the word: elements 2k (low nibble) and 2k + 1
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const float lo = (float)((int32_t)(w[i] << (28 - 8 * k)) >> 28) * s;
+                        const float hi = (float)((int32_t)(w[i] << (24 - 8 * k)) >> 28) * s;
+                        r[4 * i + k] = bf16_rne(lo) | (bf16_rne(hi) << 16);
+                    }
                 }
             }
-            o[tsr][0] = u32x4{r[0], r[1], r[2], r[3]};
-            o[tsr][1] = u32x4{r[4], r[5], r[6], r[7]};
+#pragma unroll
+            for (int k = 0; k < CPP / 8; ++k) o[tsr][k] = u32x4{r[4 * k], r[4 * k + 1], r[4 * k + 2], r[4 * k + 3]};
         }
-        const int64_t dst = (orow * (int64_t)cpr + ch) * 32;
-        st16(a.k_out + dst, o[0][0]);
-        st16(a.k_out + dst + 16, o[0][1]);
+        const int64_t dst = (orow * (int64_t)cpr + ch) * (2 * CPP);
+#pragma unroll
+        for (int k = 0; k < CPP / 8; ++k) st16(a.k_out + dst + 16 * k, o[0][k]);
         if (has_v) {
-            st16(a.v_out + dst, o[1][0]);
-            st16(a.v_out + dst + 16, o[1][1]);
+#pragma unroll
+            for (int k = 0; k < CPP / 8; ++k) st16(a.v_out + dst + 16 * k, o[1][k]);
         }
     }
 }
 
-hipError_t launch_gather_q8(const GatherArgs &a, int head_dim, hipStream_t s) {
+hipError_t launch_gather_q8(const GatherArgs &a, int head_dim, int qbits, hipStream_t s) {
     const dim3 grid((unsigned)((int64_t)a.num_seqs * a.tiles_per_seq));
-    if (head_dim == 128)
-        hipLaunchKernelGGL(gather_q8_kernel<128>, grid, dim3(kCopyThreads), 0, s, a);
-    else if (head_dim == 64)
-        hipLaunchKernelGGL(gather_q8_kernel<64>, grid, dim3(kCopyThreads), 0, s, a);
+    if (head_dim == 128 && qbits == 8)
+        hipLaunchKernelGGL((gather_q8_kernel<128, 8>), grid, dim3(kCopyThreads), 0, s, a);
+    else if (head_dim == 64 && qbits == 8)
+        hipLaunchKernelGGL((gather_q8_kernel<64, 8>), grid, dim3(kCopyThreads), 0, s, a);
+    else if (head_dim == 128 && qbits == 4)
+        hipLaunchKernelGGL((gather_q8_kernel<128, 4>), grid, dim3(kCopyThreads), 0, s, a);
+    else if (head_dim == 64 && qbits == 4)
+        hipLaunchKernelGGL((gather_q8_kernel<64, 4>), grid, dim3(kCopyThreads), 0, s, a);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

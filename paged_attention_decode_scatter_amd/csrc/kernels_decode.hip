@@ -1186,6 +1186,37 @@ __device__ __forceinline__ void i8x16_bf16(u32x4 c, u32x4 &lo, u32x4 &hi) {
     hi = u32x4{i8pair_bf16(c.z, 0), i8pair_bf16(c.z, 16), i8pair_bf16(c.w, 0), i8pair_bf16(c.w, 16)};
 }
 
+// int4: eight codes in a word (byte k: element 2k in the low nibble, 2k + 1
+// in the high nibble) as bytes holding 16 * code, exactly: the nibble moved
+// to the top of its byte is a signed byte of 16 * code.  even: elements 0, 2,
+// 4, 6; odd: elements 1, 3, 5, 7 (byte k = element 2k or 2k + 1).
+__device__ __forceinline__ uint32_t i4_even16(uint32_t w) { return (w << 4) & 0xF0F0F0F0u; }
+__device__ __forceinline__ uint32_t i4_odd16(uint32_t w) { return w & 0xF0F0F0F0u; }
+
+// 16 int4 codes (two words, in element order) -> 16 bf16 values 16 * code
+// (two 16-byte pieces, in element order), exact.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u32x2 ld8_nt(const char *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
+}
+
+__device__ __forceinline__ void i4x16_bf16(u32x2 c, u32x4 &lo, u32x4 &hi) {
+    uint32_t r[8];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t w = h ? c.y : c.x;
+        const uint32_t e = i4_even16(w), o = i4_odd16(w);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float fe = (float)(int32_t)(int8_t)(e >> (8 * k));
+            const float fo = (float)(int32_t)(int8_t)(o >> (8 * k));
+            r[4 * h + k] = __builtin_amdgcn_perm(__float_as_uint(fo), __float_as_uint(fe), 0x07060302u);
+        }
+    }
+    lo = u32x4{r[0], r[1], r[2], r[3]};
+    hi = u32x4{r[4], r[5], r[6], r[7]};
+}
+
 typedef int v4i32 __attribute__((ext_vector_type(4)));
 
 // The query of head n as int8 operands: lane (n, g4), step j holds the hi
@@ -1202,7 +1233,10 @@ __device__ __forceinline__ uint32_t q8_code(float x, float inv) {
     return (uint32_t)(int32_t)fminf(fmaxf(__builtin_rintf(x * inv), -127.0f), 127.0f) & 0xffu;
 }
 
-template <int D, int G>
+// QB = 4 (int4 pool): the K codes arrive as 16 * code with each group of 8
+// elements in the order 0, 2, 4, 6, 1, 3, 5, 7 (i4_even16 / i4_odd16), so
+// the query's codes take the same order and its scales carry the 1/16.
+template <int D, int G, int QB>
 __device__ __forceinline__ void load_q_q8(const DecodeArgs &a, int seq, int h, Q8Query<D> &qq) {
     constexpr int KL = D / 64;
     const int lane = threadIdx.x & 63;
@@ -1233,15 +1267,27 @@ __device__ __forceinline__ void load_q_q8(const DecodeArgs &a, int seq, int h, Q
         for (int e = 0; e < 16; ++e) {
             const uint32_t ch = q8_code(x[j][e], ih);
             const float r = x[j][e] - (float)(int32_t)(int8_t)ch * sh;
-            wh[e >> 2] |= ch << (8 * (e & 3));
-            wl[e >> 2] |= q8_code(r, il) << (8 * (e & 3));
+            const int wi = QB == 8 ? e >> 2 : ((e >> 3) << 1) | (e & 1);
+            const int bi = QB == 8 ? e & 3 : (e & 7) >> 1;
+            wh[wi] |= ch << (8 * bi);
+            wl[wi] |= q8_code(r, il) << (8 * bi);
         }
         qq.hi[j] = v4i32{(int)wh[0], (int)wh[1], (int)wh[2], (int)wh[3]};
         qq.lo[j] = v4i32{(int)wl[0], (int)wl[1], (int)wl[2], (int)wl[3]};
     }
-    qq.sh = sh;
-    qq.sl = sl;
+    qq.sh = QB == 8 ? sh : sh * 0.0625f;
+    qq.sl = QB == 8 ? sl : sl * 0.0625f;
 }
+
+// int4 pool: K codes D/8 bytes per lane (16 at head_dim 128: one load, 8 at
+// 64), V codes 8 bytes per lane per row load.
+template <int D>
+struct Q4Slot {
+    static constexpr int VL = D / 64;
+    u32x4 k;                                 // (head_dim 64: .x, .y only)
+    u32x2 v[VL];
+    u32x4 ks, vs;
+};
 
 template <int D>
 struct Q8Slot {
@@ -1252,19 +1298,25 @@ struct Q8Slot {
     u32x4 ks, vs;                            // scales of tokens 4 g4 .. 4 g4 + 3
 };
 
-template <int D, int G, bool UB>
+// QB: bits per code, 8 (int8 pool) or 4 (int4 pool).  An int4 chunk takes
+// half the loads; its codes are unpacked to 16 * code (exact), with the 1/16
+// in the query's scales (K) and in the value scales (V), so the rest of the
+// chunk's work is the int8 kernel's.
+template <int D, int G, bool UB, int QB>
 __device__ __forceinline__ void attend_range_q8(const DecodeArgs &a, const Range &R, int64_t jb0,
                                                 const int32_t *bt_s, char *vt, int h,
                                                 const Q8Query<D> &qq, float &m_h,
                                                 float &l_h, f32x4 (&acc)[MfmaShape<D>::NV]) {
     using S = MfmaShape<D>;
-    using Slot = Q8Slot<D>;
+    using Slot = std::conditional_t<QB == 8, Q8Slot<D>, Q4Slot<D>>;
+    constexpr int HB = D * QB / 8;   // bytes of one (token, kv head) row of codes
+    constexpr int KB = D * QB / 32;  // K code bytes per lane per chunk
+    constexpr int VB = 2 * QB;       // V code bytes per lane per row load (16 codes)
     constexpr int KS = S::KS, NV = S::NV, NP = S::NP, ROWB = S::ROWB, VSLAB = S::VSLAB;
     // two slots (one chunk in flight while one is computed): measured
     // faster than three on the decode batch (30.8 against 32.0 us, same
     // process), level on the other batches
     constexpr int NSLOT = 2;
-    constexpr int KC = D / 4;        // K codes per lane per chunk
     constexpr int VPR = D / 16;      // 16-code pieces per row
     constexpr int VRPL = 64 / VPR;   // rows per V load
     constexpr float kLazy = 8.0f;
@@ -1274,23 +1326,37 @@ __device__ __forceinline__ void attend_range_q8(const DecodeArgs &a, const Range
     const int64_t bsm = (1ll << lbs) - 1;
     const int64_t row_bytes = a.pool.row_bytes;
     const float sl2 = a.scale_log2;
-    const char *kh = a.pool.k + a.pool.layer_off + (int64_t)h * D;
-    const char *vh = a.pool.v + a.pool.layer_off + (int64_t)h * D;
+    const char *kh = a.pool.k + a.pool.layer_off + (int64_t)h * HB;
+    const char *vh = a.pool.v + a.pool.layer_off + (int64_t)h * HB;
     const float *ksh = a.pool.ks + ((int64_t)h << lbs);
     const float *vsh = a.pool.vs + ((int64_t)h << lbs);
     const int vrow = lane / VPR, vpc = lane % VPR;
+    auto load_k = [&](const char *kb, Slot &sl) {
+        if constexpr (QB == 8) {
+#pragma unroll
+            for (int i = 0; i < Slot::KL; ++i) sl.k[i] = ld16_nt(kb + 16 * i);
+        } else if constexpr (KB == 16) {
+            sl.k = ld16_nt(kb);
+        } else {
+            const u32x2 w = ld8_nt(kb);
+            sl.k = u32x4{w.x, w.y, 0u, 0u};
+        }
+    };
+    auto load_v = [&](const char *vb, Slot &sl, int i) {
+        if constexpr (QB == 8) sl.v[i] = ld16_nt(vb);
+        else sl.v[i] = ld8_nt(vb);
+    };
 
     auto load_chunk = [&](int64_t pc, Slot &sl) {
         if constexpr (UB) {
             const int32_t b = __builtin_amdgcn_readfirstlane(bt_s[(int)((pc >> lbs) - jb0)]);
             const int64_t bb = b >= 0 ? b : 0;
             const int64_t base = bb * a.pool.block_stride + (pc & bsm) * row_bytes;
-            const char *kb = kh + base + (uint32_t)(n * row_bytes + KC * g4);
-#pragma unroll
-            for (int i = 0; i < Slot::KL; ++i) sl.k[i] = ld16_nt(kb + 16 * i);
+            const char *kb = kh + base + (uint32_t)(n * row_bytes + KB * g4);
+            load_k(kb, sl);
 #pragma unroll
             for (int i = 0; i < Slot::VL; ++i)
-                sl.v[i] = ld16_nt(vh + base + (uint32_t)((i * VRPL + vrow) * row_bytes + 16 * vpc));
+                load_v(vh + base + (uint32_t)((i * VRPL + vrow) * row_bytes + VB * vpc), sl, i);
             const int64_t so = bb * a.pool.sc_block + (pc & bsm) + 4 * g4;
             sl.ks = ld16_nt(reinterpret_cast<const char *>(ksh + so));
             sl.vs = ld16_nt(reinterpret_cast<const char *>(vsh + so));
@@ -1299,16 +1365,15 @@ __device__ __forceinline__ void attend_range_q8(const DecodeArgs &a, const Range
                 const int64_t p = pc + n;
                 const bool in = p >= R.lo && p < R.hi;
                 const int32_t b = in ? bt_s[(int)((p >> lbs) - jb0)] : -1;
-                const char *kb = kh + (int64_t)(b >= 0 ? b : 0) * a.pool.block_stride + (p & bsm) * row_bytes + KC * g4;
-#pragma unroll
-                for (int i = 0; i < Slot::KL; ++i) sl.k[i] = ld16_nt(kb + 16 * i);
+                const char *kb = kh + (int64_t)(b >= 0 ? b : 0) * a.pool.block_stride + (p & bsm) * row_bytes + KB * g4;
+                load_k(kb, sl);
             }
 #pragma unroll
             for (int i = 0; i < Slot::VL; ++i) {
                 const int64_t p = pc + i * VRPL + vrow;
                 const bool in = p >= R.lo && p < R.hi;
                 const int32_t b = in ? bt_s[(int)((p >> lbs) - jb0)] : -1;
-                sl.v[i] = ld16_nt(vh + (int64_t)(b >= 0 ? b : 0) * a.pool.block_stride + (p & bsm) * row_bytes + 16 * vpc);
+                load_v(vh + (int64_t)(b >= 0 ? b : 0) * a.pool.block_stride + (p & bsm) * row_bytes + VB * vpc, sl, i);
             }
             uint32_t kw[4], vw[4];
 #pragma unroll
@@ -1339,7 +1404,8 @@ __device__ __forceinline__ void attend_range_q8(const DecodeArgs &a, const Range
         for (int i = 0; i < Slot::VL; ++i) {
             const int row = i * VRPL + vrow;
             u32x4 lo, hi;
-            i8x16_bf16(sl.v[i], lo, hi);
+            if constexpr (QB == 8) i8x16_bf16(sl.v[i], lo, hi);
+            else i4x16_bf16(sl.v[i], lo, hi);
             char *dst = vt + (row % NP) * VSLAB + (row / NP) * ROWB + 32 * vpc;
             *reinterpret_cast<u32x4 *>(dst) = lo;
             *reinterpret_cast<u32x4 *>(dst + 16) = hi;
@@ -1347,15 +1413,25 @@ __device__ __forceinline__ void attend_range_q8(const DecodeArgs &a, const Range
         // scores S[token 4 g4 + i][head n] from the codes as loaded
         v4i32 dh = {0, 0, 0, 0}, dl = {0, 0, 0, 0};
 #pragma unroll
-        for (int j = 0; j < Slot::KL; ++j) {
-            const v4i32 kc = __builtin_bit_cast(v4i32, sl.k[j]);
+        for (int j = 0; j < D / 64; ++j) {
+            v4i32 kc;
+            if constexpr (QB == 8) {
+                kc = __builtin_bit_cast(v4i32, sl.k[j]);
+            } else {
+                // words 2j, 2j + 1: elements 16j .. 16j + 15 of the lane's
+                // range, each group of 8 unpacked as 0, 2, 4, 6, 1, 3, 5, 7
+                const uint32_t w0 = j ? sl.k.z : sl.k.x, w1 = j ? sl.k.w : sl.k.y;
+                kc = v4i32{(int)i4_even16(w0), (int)i4_odd16(w0), (int)i4_even16(w1), (int)i4_odd16(w1)};
+            }
             dh = __builtin_amdgcn_mfma_i32_16x16x64_i8(kc, qq.hi[j], dh, 0, 0, 0);
             dl = __builtin_amdgcn_mfma_i32_16x16x64_i8(kc, qq.lo[j], dl, 0, 0, 0);
         }
         const float ksf[4] = {__uint_as_float(sl.ks.x), __uint_as_float(sl.ks.y),
                               __uint_as_float(sl.ks.z), __uint_as_float(sl.ks.w)};
-        const float vsf[4] = {__uint_as_float(sl.vs.x), __uint_as_float(sl.vs.y),
-                              __uint_as_float(sl.vs.z), __uint_as_float(sl.vs.w)};
+        // (int4: the V tile holds 16 * code, so the value scales take 1/16)
+        constexpr float kVS = QB == 8 ? 1.0f : 0.0625f;
+        const float vsf[4] = {__uint_as_float(sl.vs.x) * kVS, __uint_as_float(sl.vs.y) * kVS,
+                              __uint_as_float(sl.vs.z) * kVS, __uint_as_float(sl.vs.w) * kVS};
         float s[4];
         float cm = kNegInf;
 #pragma unroll
@@ -1441,7 +1517,8 @@ __device__ __forceinline__ void attend_range_q8(const DecodeArgs &a, const Range
     }
 }
 
-template <int D, int G, bool UB>
+// QB: bits per code of the pool, 8 or 4.
+template <int D, int G, bool UB, int QB>
 // Two wavefronts per SIMD: without the hint the compiler takes 272
 // registers (one wavefront per SIMD, half the loads in flight).
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void decode_q8_kernel(DecodeArgs a) {
@@ -1470,13 +1547,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int h = it.hg * a.heads_per_wg + w;
     Q8Query<D> qq;
-    load_q_q8<D, G>(a, it.seq, h, qq);
+    load_q_q8<D, G, QB>(a, it.seq, h, qq);
     float m_h = kNegInf;
     float l_h = 0.0f;
     f32x4 acc[S::NV];
 #pragma unroll
     for (int sl = 0; sl < S::NV; ++sl) acc[sl] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    attend_range_q8<D, G, UB>(a, R, jb0, bt_s, vtiles[w], h, qq, m_h, l_h, acc);
+    attend_range_q8<D, G, UB, QB>(a, R, jb0, bt_s, vtiles[w], h, qq, m_h, l_h, acc);
     float lrow[4];
     head_denominators(l_h, lrow);
     if (direct) {
@@ -1630,15 +1707,16 @@ static hipError_t run_decode(const DecodeArgs &a, hipStream_t s) {
 
 typedef hipError_t (*DecodeFn)(const DecodeArgs &, hipStream_t);
 
-// int8 pools: bf16 queries and outputs, split schedule.
-template <int D, int G>
+// int8 / int4 pools (QB bits per code): bf16 queries and outputs, split
+// and planned schedules.
+template <int D, int G, int QB>
 static hipError_t run_decode_q8(const DecodeArgs &a, hipStream_t s) {
     const dim3 block(64 * a.heads_per_wg);
     const dim3 grid((unsigned)(a.plan > 0 ? a.plan : (int64_t)a.head_groups * a.max_splits * a.num_seqs));
     if (a.pool.lbs >= 4)
-        hipLaunchKernelGGL((decode_q8_kernel<D, G, true>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((decode_q8_kernel<D, G, true, QB>), grid, block, 0, s, a);
     else
-        hipLaunchKernelGGL((decode_q8_kernel<D, G, false>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((decode_q8_kernel<D, G, false, QB>), grid, block, 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.max_splits == 1 || a.fused_merge) return e;
     hipLaunchKernelGGL((reduce_kernel<1, D>), dim3((unsigned)((int64_t)a.num_seqs * a.num_q_heads)),
@@ -1646,13 +1724,13 @@ static hipError_t run_decode_q8(const DecodeArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int D>
+template <int D, int QB>
 static DecodeFn pick_group_q8(int group) {
     switch (group) {
-        case 1: return run_decode_q8<D, 1>;
-        case 2: return run_decode_q8<D, 2>;
-        case 4: return run_decode_q8<D, 4>;
-        case 8: return run_decode_q8<D, 8>;
+        case 1: return run_decode_q8<D, 1, QB>;
+        case 2: return run_decode_q8<D, 2, QB>;
+        case 4: return run_decode_q8<D, 4, QB>;
+        case 8: return run_decode_q8<D, 8, QB>;
         default: return nullptr;
     }
 }
@@ -1681,8 +1759,12 @@ static DecodeFn pick(int dtype, int head_dim, int group) {
     if (dtype == 0) return pick_dim<0>(head_dim, group);
     if (dtype == 1) return pick_dim<1>(head_dim, group);
     if (dtype == 2) {
-        if (head_dim == 64) return pick_group_q8<64>(group);
-        if (head_dim == 128) return pick_group_q8<128>(group);
+        if (head_dim == 64) return pick_group_q8<64, 8>(group);
+        if (head_dim == 128) return pick_group_q8<128, 8>(group);
+    }
+    if (dtype == 3) {
+        if (head_dim == 64) return pick_group_q8<64, 4>(group);
+        if (head_dim == 128) return pick_group_q8<128, 4>(group);
     }
     return nullptr;
 }

@@ -24,20 +24,28 @@ int ilog2(int64_t x) {
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int64_t elem_bytes(int32_t dtype) { return dtype == PKV_BF16 ? 2 : dtype == PKV_I8 ? 1 : 4; }
+bool is_quant(int32_t dtype) { return dtype == PKV_I8 || dtype == PKV_I4; }
+// bits per code of a quantised pool
+int quant_bits(int32_t dtype) { return dtype == PKV_I4 ? 4 : 8; }
+// bytes of one token row (all kv heads) of one tensor
+int64_t row_bytes_of(const pkv_pool *pool) {
+    return pool->dtype == PKV_I4 ? pool->num_kv_heads * pool->head_dim / 2
+                                 : pool->num_kv_heads * pool->head_dim * elem_bytes(pool->dtype);
+}
 
 int64_t pow2_or_neg(int64_t x) { return is_pow2(x) ? ilog2(x) : -1; }
 
 // Common pool checks.  need_v: the call reads or writes V.
 int check_pool(const pkv_pool *pool, bool need_v) {
     if (!pool) return PKV_ERR_NULL;
-    if (pool->dtype != PKV_F32 && pool->dtype != PKV_BF16 && pool->dtype != PKV_I8)
+    if (pool->dtype != PKV_F32 && pool->dtype != PKV_BF16 && !is_quant(pool->dtype))
         return PKV_ERR_DTYPE;
     if (pool->reserved != 0) return PKV_ERR_SHAPE;
     if (pool->num_blocks <= 0 || pool->num_blocks > INT32_MAX || pool->num_layers <= 0 ||
         pool->num_kv_heads <= 0 || pool->head_dim <= 0 || !is_pow2(pool->block_size) ||
-        pool->block_size > (1 << 20))
+        pool->block_size > (1 << 20) || (pool->dtype == PKV_I4 && pool->head_dim % 2))
         return PKV_ERR_SHAPE;
-    const int64_t row = pool->num_kv_heads * pool->head_dim * elem_bytes(pool->dtype);
+    const int64_t row = row_bytes_of(pool);
     if (row > (int64_t(1) << 24)) return PKV_ERR_SHAPE;
     if (row % 16) return PKV_ERR_ALIGN;
     if (!pool->k || (need_v && !pool->v)) return PKV_ERR_NULL;
@@ -46,7 +54,7 @@ int check_pool(const pkv_pool *pool, bool need_v) {
         if (pool->block_stride < pool->num_layers * pool->block_size * row) return PKV_ERR_SHAPE;
         if (pool->block_stride % 16) return PKV_ERR_ALIGN;
     }
-    if (pool->dtype == PKV_I8) {
+    if (is_quant(pool->dtype)) {
         if (!pool->k_scale || (pool->v && !pool->v_scale)) return PKV_ERR_NULL;
         if (!aligned16(pool->k_scale) || (pool->v && !aligned16(pool->v_scale)))
             return PKV_ERR_ALIGN;
@@ -62,8 +70,7 @@ int64_t scale_block(const pkv_pool *pool) {
 // Bytes of one block of one tensor (all layers) and the distance between
 // consecutive blocks.
 int64_t dense_block_bytes(const pkv_pool *pool) {
-    return pool->num_layers * pool->block_size * pool->num_kv_heads * pool->head_dim *
-           elem_bytes(pool->dtype);
+    return pool->num_layers * pool->block_size * row_bytes_of(pool);
 }
 int64_t block_stride_of(const pkv_pool *pool) {
     return pool->block_stride ? pool->block_stride : dense_block_bytes(pool);
@@ -71,7 +78,7 @@ int64_t block_stride_of(const pkv_pool *pool) {
 
 PoolView make_view(const pkv_pool *pool, int32_t layer) {
     PoolView v{};
-    const int64_t row = pool->num_kv_heads * pool->head_dim * elem_bytes(pool->dtype);
+    const int64_t row = row_bytes_of(pool);
     v.k = static_cast<const char *>(pool->k);
     v.v = static_cast<const char *>(pool->v);
     v.row_bytes = (int32_t)row;
@@ -79,7 +86,7 @@ PoolView make_view(const pkv_pool *pool, int32_t layer) {
     v.layer_off = (int64_t)layer * pool->block_size * row;
     v.num_blocks = (int32_t)pool->num_blocks;
     v.lbs = ilog2(pool->block_size);
-    if (pool->dtype == PKV_I8) {
+    if (is_quant(pool->dtype)) {
         const int64_t lo = (int64_t)layer * pool->num_kv_heads * pool->block_size;
         v.ks = static_cast<const float *>(pool->k_scale) + lo;
         v.vs = pool->v_scale ? static_cast<const float *>(pool->v_scale) + lo : nullptr;
@@ -227,7 +234,7 @@ struct SplitPlan {
 
 bool planned_possible(int64_t num_seqs, int64_t hkv, int64_t max_len, int64_t bs, int32_t dtype,
                       SplitPlan *sp) {
-    if ((dtype != PKV_BF16 && dtype != PKV_I8) || num_seqs <= 0 || num_seqs > kPlanMaxSeqs || max_len <= 0 ||
+    if ((dtype != PKV_BF16 && !is_quant(dtype)) || num_seqs <= 0 || num_seqs > kPlanMaxSeqs || max_len <= 0 ||
         !is_pow2(bs))
         return false;
     const int64_t groups = hkv / heads_per_wg(hkv);
@@ -319,6 +326,7 @@ static ScatterQ8Args q8_args(const pkv_pool *pool, const PoolView &v, const void
     a.num_kv_heads = (int32_t)pool->num_kv_heads;
     a.head_dim = (int32_t)pool->head_dim;
     a.lbs = v.lbs;
+    a.qbits = quant_bits(pool->dtype);
     return a;
 }
 
@@ -333,7 +341,7 @@ PKV_API int kv_scatter(const pkv_pool *pool, int32_t layer, const void *k_src, c
     if (!k_src || !slot_mapping) return PKV_ERR_NULL;
     if (!aligned16(k_src) || (has_v && !aligned16(v_src))) return PKV_ERR_ALIGN;
     const PoolView v = make_view(pool, layer);
-    if (pool->dtype == PKV_I8) {
+    if (is_quant(pool->dtype)) {
         if (!q8_dim_ok(pool)) return PKV_ERR_UNSUPPORTED;
         if (num_tokens * pool->num_kv_heads > (int64_t)INT32_MAX * 8) return PKV_ERR_SHAPE;
         ScatterQ8Args a = q8_args(pool, v, k_src, v_src, num_tokens);
@@ -374,7 +382,7 @@ PKV_API int kv_append(const pkv_pool *pool, int32_t layer, const void *k_src, co
         return PKV_ERR_NULL;
     if (!aligned16(k_src) || (has_v && !aligned16(v_src))) return PKV_ERR_ALIGN;
     const PoolView v = make_view(pool, layer);
-    if (pool->dtype == PKV_I8) {
+    if (is_quant(pool->dtype)) {
         if (!q8_dim_ok(pool)) return PKV_ERR_UNSUPPORTED;
         if (num_tokens * pool->num_kv_heads > (int64_t)INT32_MAX * 8) return PKV_ERR_SHAPE;
         ScatterQ8Args a = q8_args(pool, v, k_src, v_src, num_tokens);
@@ -446,9 +454,10 @@ PKV_API int kv_gather(const pkv_pool *pool, int32_t layer, const int32_t *block_
     a.lcpr = (int32_t)pow2_or_neg(cpr);
     if ((int64_t)num_seqs * a.tiles_per_seq > INT32_MAX || cpr * tpw > INT32_MAX / 2)
         return PKV_ERR_SHAPE;
-    if (pool->dtype == PKV_I8) {
+    if (is_quant(pool->dtype)) {
         if (!q8_dim_ok(pool)) return PKV_ERR_UNSUPPORTED;
-        return status_of(launch_gather_q8(a, (int)pool->head_dim, static_cast<hipStream_t>(stream)));
+        return status_of(launch_gather_q8(a, (int)pool->head_dim, quant_bits(pool->dtype),
+                                          static_cast<hipStream_t>(stream)));
     }
     return status_of(launch_gather(a, static_cast<hipStream_t>(stream)));
 }
@@ -491,7 +500,7 @@ PKV_API int32_t paged_attn_decode_schedule(int32_t num_seqs, int32_t num_kv_head
                                            int32_t num_q_heads, int32_t head_dim,
                                            int32_t max_seq_len, int32_t block_size, int32_t dtype,
                                            int32_t split_tokens) {
-    if (dtype != PKV_F32 && dtype != PKV_BF16 && dtype != PKV_I8) return PKV_ERR_DTYPE;
+    if (dtype != PKV_F32 && dtype != PKV_BF16 && !is_quant(dtype)) return PKV_ERR_DTYPE;
     if (num_kv_heads <= 0 || num_q_heads <= 0 || num_q_heads % num_kv_heads) return PKV_ERR_SHAPE;
     DecodePlan p;
     const int st = plan_decode(num_seqs, num_kv_heads, num_q_heads, head_dim, max_seq_len,
@@ -525,7 +534,7 @@ int decode_impl(const pkv_pool *pool, int32_t layer, const void *q, int32_t num_
         return PKV_ERR_SHAPE;
     const int group = (int)(num_q_heads / pool->num_kv_heads);
     if (!decode_supported(pool->dtype, (int)pool->head_dim, group)) return PKV_ERR_UNSUPPORTED;
-    if (k_new && pool->dtype == PKV_I8) return PKV_ERR_UNSUPPORTED;
+    if (k_new && is_quant(pool->dtype)) return PKV_ERR_UNSUPPORTED;
     SplitPlan spl{};
     const bool planned = use_planned(num_seqs, pool->num_kv_heads, max_seq_len, pool->block_size,
                                      pool->dtype, split_tokens, &spl);
@@ -756,7 +765,7 @@ PKV_API int kv_copy_blocks(const pkv_pool *pool, const int32_t *src_blocks,
     a.pieces = (a.block_bytes + kCopyBlockPiece - 1) / kCopyBlockPiece;
     if (a.pieces * num_pairs > INT32_MAX) return PKV_ERR_SHAPE;
     st = status_of(launch_copy_blocks(a, static_cast<hipStream_t>(stream)));
-    if (st || pool->dtype != PKV_I8) return st;
+    if (st || !is_quant(pool->dtype)) return st;
     // the scales of a quantised pool: one dense range per block as well
     a.k = static_cast<char *>(pool->k_scale);
     a.v = pool->v ? static_cast<char *>(pool->v_scale) : nullptr;
@@ -798,7 +807,7 @@ int swap_impl(const pkv_pool *pool, const int32_t *ids, int64_t n, char *kh, cha
         }
         i = j;
     }
-    if (pool->dtype != PKV_I8) return PKV_OK;
+    if (!is_quant(pool->dtype)) return PKV_OK;
     // quantised pool: the n blocks' scales follow the n blocks' codes
     const int64_t sb = scale_block(pool) * 4;
     for (int64_t i = 0; i < n;) {

@@ -101,7 +101,7 @@ struct ScatterQ8Args {
     int32_t lbs;
     int32_t bt_stride;
     int32_t num_seqs;
-    int32_t pad_;
+    int32_t qbits;         // bits per code: 8 (int8 pool) or 4 (int4 pool)
 };
 
 struct GatherArgs {
@@ -266,7 +266,7 @@ hipError_t launch_prefill(const PrefillArgs &a, int dtype, int head_dim, int gro
 hipError_t launch_gather(const GatherArgs &a, hipStream_t s);
 hipError_t launch_copy_blocks(const CopyBlocksArgs &a, hipStream_t s);
 hipError_t launch_scatter_q8(const ScatterQ8Args &a, hipStream_t s);
-hipError_t launch_gather_q8(const GatherArgs &a, int head_dim, hipStream_t s);
+hipError_t launch_gather_q8(const GatherArgs &a, int head_dim, int qbits, hipStream_t s);
 hipError_t launch_validate(const ValidateArgs &a, hipStream_t s);
 hipError_t launch_read_blocks(const ReadBlocksArgs &a, hipStream_t s);
 hipError_t launch_zero_words(uint32_t *p, int64_t n, hipStream_t s);

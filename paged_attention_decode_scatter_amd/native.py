@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
 PKV_F32 = 0
 PKV_BF16 = 1
 PKV_I8 = 2
+PKV_I4 = 3
 
 _DTYPES = {torch.float32: PKV_F32, torch.bfloat16: PKV_BF16}
 
@@ -158,15 +159,19 @@ def _need(t, dtype, name):
 
 
 class QuantizedPool:
-    """One tensor of an int8 pool: codes (num_blocks, num_layers,
-    block_size, num_kv_heads, head_dim) int8 and one float32 scale per
-    (token, kv head) row, scales (num_blocks, num_layers, num_kv_heads,
-    block_size).  Passed wherever a K or V pool goes; the rows written into
-    it and the queries and outputs of decode are bfloat16."""
+    """One tensor of a quantised pool and one float32 scale per (token, kv
+    head) row, scales (num_blocks, num_layers, num_kv_heads, block_size).
+    int8 pool: codes (num_blocks, num_layers, block_size, num_kv_heads,
+    head_dim) int8.  int4 pool: codes (..., head_dim / 2) uint8, two codes per
+    byte (element 2i in the low nibble, four-bit two's complement).  Passed
+    wherever a K or V pool goes; the rows written into it and the queries and
+    outputs of decode are bfloat16.  `shape` is the logical (num_blocks,
+    num_layers, block_size, num_kv_heads, head_dim)."""
 
     def __init__(self, codes, scales):
-        if codes.dim() != 5 or codes.dtype != torch.int8:
-            raise ValueError("codes must be int8 (num_blocks, num_layers, block_size, heads, head_dim)")
+        if codes.dim() != 5 or codes.dtype not in (torch.int8, torch.uint8):
+            raise ValueError("codes must be int8 (num_blocks, num_layers, block_size, heads, head_dim) "
+                             "or packed int4 as uint8 (..., head_dim / 2)")
         nb, nl, bs, h, _ = codes.shape
         if scales.dtype != torch.float32 or tuple(scales.shape) != (nb, nl, h, bs) \
                 or not scales.is_contiguous() or scales.device != codes.device:
@@ -174,16 +179,19 @@ class QuantizedPool:
                              "num_kv_heads, block_size) on the codes' device")
         self.codes = codes
         self.scales = scales
+        self.bits = 8 if codes.dtype == torch.int8 else 4
 
     @classmethod
-    def empty(cls, num_blocks, num_layers, block_size, num_kv_heads, head_dim, device):
-        codes = torch.zeros((num_blocks, num_layers, block_size, num_kv_heads, head_dim),
-                            dtype=torch.int8, device=device)
+    def empty(cls, num_blocks, num_layers, block_size, num_kv_heads, head_dim, device, bits=8):
+        last = head_dim if bits == 8 else head_dim // 2
+        codes = torch.zeros((num_blocks, num_layers, block_size, num_kv_heads, last),
+                            dtype=torch.int8 if bits == 8 else torch.uint8, device=device)
         scales = torch.zeros((num_blocks, num_layers, num_kv_heads, block_size),
                              dtype=torch.float32, device=device)
         return cls(codes, scales)
 
-    shape = property(lambda self: self.codes.shape)
+    shape = property(lambda self: torch.Size(tuple(self.codes.shape[:4]) +
+                                             (self.codes.shape[4] * (8 // self.bits),)))
     dtype = property(lambda self: self.codes.dtype)
     device = property(lambda self: self.codes.device)
     is_cuda = property(lambda self: self.codes.is_cuda)
@@ -224,8 +232,11 @@ def make_pool(k_pool, v_pool=None) -> PkvPool:
     if not quant and k_pool.dtype not in _DTYPES:
         raise TypeError(f"pool dtype must be float32 or bfloat16, got {k_pool.dtype}")
     nb, nl, bs, h, d = k_pool.shape
-    inner = (bs * h * d, h * d, d, 1)
-    dense = nl * bs * h * d
+    # strides are checked on the stored tensor (the codes for a quantised
+    # pool: head_dim / 2 bytes per row for int4)
+    dc = k_pool.codes.shape[4] if quant else d
+    inner = (bs * h * dc, h * dc, dc, 1)
+    dense = nl * bs * h * dc
     for t, name in ((k_pool, "k_pool"), (v_pool, "v_pool")):
         if t is None:
             continue
@@ -240,7 +251,7 @@ def make_pool(k_pool, v_pool=None) -> PkvPool:
         raise ValueError("k_pool and v_pool block strides differ")
     stride = k_pool.stride(0) if nb > 1 else dense
     block_stride = 0 if stride == dense else stride * k_pool.element_size()
-    dt = PKV_I8 if quant else _DTYPES[k_pool.dtype]
+    dt = (PKV_I8 if k_pool.bits == 8 else PKV_I4) if quant else _DTYPES[k_pool.dtype]
     return PkvPool(k_pool.data_ptr(), None if v_pool is None else v_pool.data_ptr(),
                    nb, nl, bs, h, d, dt, 0, block_stride,
                    k_pool.scales.data_ptr() if quant else None,
@@ -336,8 +347,9 @@ def paged_attn_decode_schedule(num_seqs, num_kv_heads, num_q_heads, head_dim, ma
                                block_size, dtype, split_tokens=0):
     """Tokens per split of the split schedule, or SCHEDULE_PLANNED (1) for
     the device-planned split schedule, for a pool of torch dtype `dtype`
-    (torch.int8: a quantised pool)."""
-    code = {torch.float32: 0, torch.bfloat16: 1, torch.int8: 2}.get(dtype)
+    (torch.int8: an int8 pool; torch.uint8: an int4 pool, two codes per
+    byte)."""
+    code = {torch.float32: 0, torch.bfloat16: 1, torch.int8: 2, torch.uint8: 3}.get(dtype)
     if code is None:
         raise PagedKVError("paged_attn_decode_schedule", -2)
     v = load_library().paged_attn_decode_schedule(num_seqs, num_kv_heads, num_q_heads, head_dim,
@@ -514,7 +526,7 @@ def split_swapped_q8(buf, k_pool, n):
     """(codes (n, layers, bs, H, D) int8, scales (n, layers, H, bs) float32)
     views of a quantised pool's swap buffer."""
     cb = k_pool.codes[0].numel()
-    codes = buf[:n * cb].view(torch.int8).view((n,) + tuple(k_pool.shape[1:]))
+    codes = buf[:n * cb].view(k_pool.codes.dtype).view((n,) + tuple(k_pool.codes.shape[1:]))
     scales = buf[n * cb:].view(torch.float32).view((n,) + tuple(k_pool.scales.shape[1:]))
     return codes, scales
 

@@ -116,6 +116,27 @@ def int8_pool_tensors(num_blocks, num_layers, block_size, num_kv_heads, head_dim
     return codes, scales
 
 
+def int4_pool_tensors(num_blocks, num_layers, block_size, num_kv_heads, head_dim, device, seed,
+                      amax=3.0, chunk=1 << 28):
+    """Random stored contents of one tensor of an int4 pool: uniformly
+    random bytes (uint8, the pool layout with head_dim / 2 bytes per head
+    row; every byte value, so every pair of four-bit codes, -8 included)
+    and one float32 scale per (block, layer, kv head, slot) drawn as
+    amax / 7 * U(0.5, 1.5).  Chunked like fill_normal_."""
+    gen = torch.Generator(device=device).manual_seed(seed)
+    codes = torch.empty((num_blocks, num_layers, block_size, num_kv_heads, head_dim // 2),
+                        dtype=torch.uint8, device=device)
+    flat = codes.view(-1)
+    for i in range(0, flat.numel(), chunk):
+        m = min(chunk, flat.numel() - i)
+        flat[i:i + m].copy_(torch.randint(0, 256, (m,), generator=gen, device=device,
+                                          dtype=torch.int32))
+    u = torch.rand((num_blocks, num_layers, num_kv_heads, block_size), generator=gen,
+                   device=device, dtype=torch.float32)
+    scales = (u + 0.5) * (amax / 7.0)
+    return codes, scales
+
+
 def _tables_from_counts(counts, perm, stride=None):
     """Consecutive slices of `perm` as block tables, padded with -1."""
     stride = stride or max(1, max(counts) if counts else 1)

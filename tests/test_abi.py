@@ -425,6 +425,35 @@ def test_quantized_pool_checks(lib):
     assert f(32, 8, 32, 128, 2048, 16, I8, -1) == SHAPE
 
 
+def test_int4_pool_checks(lib):
+    """An int4 pool (two codes per byte) needs an even head_dim and its scale
+    arrays; decode and the copies take it like int8; prefill and the fused
+    append-and-decode refuse it."""
+    by = ctypes.byref
+    I4 = 3
+    sc = lib.kv_scatter
+    assert sc(by(pool(dtype=I4, ks=None)), 0, A, A, A, 4, None) == NULL
+    assert sc(by(pool(dtype=I4, d=63)), 0, A, A, A, 4, None) == SHAPE
+    assert sc(by(pool(dtype=I4, d=96)), 0, A, A, A, 4, None) == UNSUP
+    assert sc(by(pool(dtype=I4)), 0, A, A, A, 0, None) == OK
+    dec = lib.paged_attn_decode
+
+    def decode(p, split=0, hq=32):
+        return dec(by(p), 0, A, hq, A, 8, A, A, 4, 100, 0.1, split, A, A, 1 << 30, None)
+
+    assert decode(pool(dtype=I4), split=-1) == SHAPE
+    assert decode(pool(dtype=I4, d=96)) == UNSUP
+    assert decode(pool(dtype=I4, vs=None)) == NULL
+    app = lib.paged_attn_decode_append
+    assert app(by(pool(dtype=I4)), 0, A, 32, A, A, A, 8, A, A, 4, 100, 0.1, 0, A, A, 1 << 30,
+               None) == UNSUP
+    pre = lib.paged_attn_prefill
+    assert pre(by(pool(dtype=I4)), 0, A, 32, A, 64, 16, A, 8, A, A, 4, 0.1, A, None) == UNSUP
+    f = lib.paged_attn_decode_schedule
+    assert f(32, 8, 32, 128, 2048, 16, I4, 0) == 1
+    assert f(65, 8, 32, 128, 2048, 16, I4, 0) == 256
+
+
 def test_quantized_pool_binding():
     """QuantizedPool pairs describe an int8 pool (scale pointers set, dtype
     PKV_I8); their rows, queries and outputs are bf16; a quantised K with a
@@ -443,3 +472,14 @@ def test_quantized_pool_binding():
     buf = torch.zeros(3 * (2 * 16 * 2 * 64 + 2 * 2 * 16 * 4), dtype=torch.uint8)
     codes, scales = N.split_swapped_q8(buf, k, 3)
     assert codes.shape == (3, 2, 16, 2, 64) and scales.shape == (3, 2, 2, 16)
+    k4 = N.QuantizedPool.empty(6, 2, 16, 2, 64, "cpu", bits=4)
+    v4 = N.QuantizedPool.empty(6, 2, 16, 2, 64, "cpu", bits=4)
+    assert k4.codes.shape == (6, 2, 16, 2, 32) and k4.codes.dtype == torch.uint8
+    assert tuple(k4.shape) == (6, 2, 16, 2, 64) and k4.bits == 4
+    p4 = N.make_pool(k4, v4)
+    assert p4.dtype == 3 and p4.head_dim == 64
+    with pytest.raises(TypeError):
+        N.make_pool(k4, v)                            # int4 K with int8 V
+    buf4 = torch.zeros(3 * (2 * 16 * 2 * 32 + 2 * 2 * 16 * 4), dtype=torch.uint8)
+    codes, scales = N.split_swapped_q8(buf4, k4, 3)
+    assert codes.shape == (3, 2, 16, 2, 32) and codes.dtype == torch.uint8
