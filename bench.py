@@ -23,8 +23,8 @@ of step time.  `roofline` describes the headline step (HIP events on the
 launch stream around the back-to-back timed steps).  `cpu_baseline` times
 the CPU oracle on the headline batch.  `ops` reports the scatter and gather
 rates on the prefill shape (8 x 1024 rows, 10% padding), block copies and
-swaps; `prefill_attention`, `int8_decode` and `block_manager` the other
-entry points.
+swaps; `prefill_attention`, `int8_decode`, `int4_decode` and
+`block_manager` the other entry points.
 """
 import argparse
 import json
@@ -179,13 +179,14 @@ def prefill_attention(w, N, W, reps=4):
                 **{"TFLOP/s": flops / ms / 1e9, "frac_of_bf16_mfma_peak": flops / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS})
 
 
-def int8_decode(base, N, W, reps=32):
-    """Decode over an int8 pool of the decode workloads' geometry (16384
-    blocks x 32 layers x 16 x 8 x 128 codes, one float32 scale per token and
-    kv head) with each workload's tables, lengths, offsets and bf16 queries;
-    back to back with the layer rotated.  Algorithmic bytes: every cached
-    token's K and V codes and scales once, q and out (bf16) once, the used
-    table entries, lengths and offsets."""
+def quant_decode(base, N, W, bits=8, reps=32):
+    """Decode over a quantised pool of the decode workloads' geometry (16384
+    blocks x 32 layers x 16 x 8 x 128 codes; int8: one byte per element,
+    int4: two elements per byte; one float32 scale per token and kv head)
+    with each workload's tables, lengths, offsets and bf16 queries; back to
+    back with the layer rotated.  Algorithmic bytes: every cached token's K
+    and V codes and scales once, q and out (bf16) once, the used table
+    entries, lengths and offsets."""
     import copy
     import ctypes
 
@@ -193,8 +194,7 @@ def int8_decode(base, N, W, reps=32):
 
     dev = base.q.device
     shape = (base.num_blocks, base.num_layers, base.block_size, base.num_kv_heads, base.head_dim)
-    k = N.QuantizedPool(*W.int8_pool_tensors(*shape, dev, 8101))
-    v = N.QuantizedPool(*W.int8_pool_tensors(*shape, dev, 8102))
+    k, v = quant_pools(W, N, shape, dev, bits)
     lib = N.load_library()
     pool = N.make_pool(k, v)
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
@@ -206,11 +206,12 @@ def int8_decode(base, N, W, reps=32):
         w.k_pool, w.v_pool = base.k_pool, base.v_pool   # bf16 geometry for decode_bytes
         lens = w.seq_lens.cpu().numpy()
         tokens = int(lens.sum())
-        kv = tokens * w.num_kv_heads * (w.head_dim + 4) * 2
+        kv = tokens * w.num_kv_heads * (w.head_dim * bits // 8 + 4) * 2
         kv_bf16, alg_bf16 = decode_bytes(w, lens)
         alg = alg_bf16 - kv_bf16 + kv
         sched = N.paged_attn_decode_schedule(w.num_seqs, w.num_kv_heads, w.num_q_heads, w.head_dim,
-                                             w.max_seq_len, w.block_size, torch.int8, 0)
+                                             w.max_seq_len, w.block_size,
+                                             torch.int8 if bits == 8 else torch.uint8, 0)
         need = N.paged_attn_decode_workspace_size(w.num_seqs, w.num_kv_heads, w.num_q_heads,
                                                   w.head_dim, w.max_seq_len, w.block_size, 0)
         ws = torch.zeros(max(need, 16), dtype=torch.uint8, device=dev)
@@ -219,11 +220,11 @@ def int8_decode(base, N, W, reps=32):
                  w.block_tables.shape[1], P(w.seq_lens), P(w.offsets), w.num_seqs, w.max_seq_len,
                  ctypes.c_float(w.scale), 0, P(out), P(ws), ws.numel(), stream)
                 for l in range(w.num_layers)]
-        # three untimed passes over the layers (the int8 pools are freshly
-        # filled: the first passes run slower), then the timed calls
+        # three untimed passes over the layers (the quantised pools are
+        # freshly filled: the first passes run slower), then the timed calls
         for i in range(3 * w.num_layers):
             if lib.paged_attn_decode(*args[i % w.num_layers]):
-                raise RuntimeError(f"int8 paged_attn_decode failed on {name}")
+                raise RuntimeError(f"int{bits} paged_attn_decode failed on {name}")
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         a.record()
@@ -234,7 +235,7 @@ def int8_decode(base, N, W, reps=32):
         us = a.elapsed_time(b) / reps * 1e3
         g = w.num_q_heads // w.num_kv_heads
         max_splits = -(-(w.max_seq_len + w.block_size - 1) // max(sched, 1))
-        label = f"decode_q8_kernel<D={w.head_dim},G={g}> " + (
+        label = f"decode_q8_kernel<D={w.head_dim},G={g},QB={bits}> " + (
             "(device-planned split)" if sched == N.SCHEDULE_PLANNED else
             f"(split {sched}" + (", + reduce_kernel)" if max_splits > 16 else ")"))
         res[name] = {"us": us, "algorithmic_bytes": alg, "GB/s": alg / us / 1e3,
@@ -244,6 +245,14 @@ def int8_decode(base, N, W, reps=32):
     del k, v, pool
     torch.cuda.empty_cache()
     return res
+
+
+def quant_pools(W, N, shape, dev, bits):
+    """K and V QuantizedPools of `shape` (random codes and positive scales),
+    int8 or packed int4."""
+    make = W.int8_pool_tensors if bits == 8 else W.int4_pool_tensors
+    return (N.QuantizedPool(*make(*shape, dev, 8101)),
+            N.QuantizedPool(*make(*shape, dev, 8102)))
 
 
 def read_ceiling(w, N, reps=32):
@@ -561,14 +570,14 @@ def pmc_target(which, reps):
         torch.cuda.synchronize()
         log(f"ran {reps} prefill launches on the prefix-sharing batch ({info['flops']} flops each)")
         return
-    if which.startswith("int8_"):
+    if which.startswith(("int8_", "int4_")):
         import copy
         import ctypes
 
+        bits = int(which[3])
         base = W.decode_batch(device=dev)
         shape = (base.num_blocks, base.num_layers, base.block_size, base.num_kv_heads, base.head_dim)
-        k = N.QuantizedPool(*W.int8_pool_tensors(*shape, dev, 8101))
-        v = N.QuantizedPool(*W.int8_pool_tensors(*shape, dev, 8102))
+        k, v = quant_pools(W, N, shape, dev, bits)
         name = which[5:]
         w = base if name == "decode_batch" else W.PRESETS[name](device=dev, with_pools=False)
         w = copy.copy(w)
@@ -585,9 +594,9 @@ def pmc_target(which, reps):
                                      P(w.block_tables), w.block_tables.shape[1], P(w.seq_lens),
                                      P(w.offsets), w.num_seqs, w.max_seq_len,
                                      ctypes.c_float(w.scale), 0, P(out), P(ws), ws.numel(), stream):
-                raise RuntimeError("int8 paged_attn_decode failed")
+                raise RuntimeError(f"int{bits} paged_attn_decode failed")
         torch.cuda.synchronize()
-        log(f"ran {reps} int8 decode launches on {name}")
+        log(f"ran {reps} int{bits} decode launches on {name}")
         return
     w = config_workload(which, W.decode_batch(device=dev), W)
     mx = w.max_seq_len
@@ -828,8 +837,8 @@ def main():
     ap.add_argument("--split-tokens", type=int, default=0)
     ap.add_argument("--pmc-target", default=None,
                     choices=list(DECODE_CONFIGS) + ["int8_" + c for c in DECODE_CONFIGS]
-                    + ["prefill", "copy"],
-                    help="run only the step launches of one workload (or int8 decode on it, the "
+                    + ["int4_" + c for c in DECODE_CONFIGS] + ["prefill", "copy"],
+                    help="run only the step launches of one workload (or int8 / int4 decode on it, the "
                          "prefill launches, or a 1 GiB copy) for counter passes")
     ap.add_argument("--pmc-reps", type=int, default=20)
     args = ap.parse_args()
@@ -921,7 +930,9 @@ def main():
         log("prefill attention on the prefix-sharing batch")
         result["prefill_attention"] = prefill_attention(base, N, W)
         log("int8 pool decode")
-        result["int8_decode"] = int8_decode(base, N, W)
+        result["int8_decode"] = quant_decode(base, N, W, 8)
+        log("int4 pool decode")
+        result["int4_decode"] = quant_decode(base, N, W, 4)
         log("host block manager")
         result["block_manager"] = block_manager_host(N, W)
     if not args.no_cpu_baseline:

@@ -37,6 +37,13 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
     return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Two floats as a bf16 pair (lo in bits 0..15), rounded to nearest even by
+// the gfx950 packed conversion (v_cvt_pk_bf16_f32; NaN stays NaN).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+
 // A 32-bit word as a pair of bf16.  The word is passed by value on
 // purpose: applying __builtin_bit_cast directly to an ext_vector element
 // (q.y, q.z, ...) makes this compiler read element .x every time.

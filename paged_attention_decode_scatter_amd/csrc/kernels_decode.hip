@@ -1147,9 +1147,9 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Quantised (int8) pools, split schedule [P3 sec. 6 names quantised KV; the
-// stored value of a (token, kv head) row is code * scale].  The pipeline of
-// decode_mfma_kernel with half the bytes per token:
+// Quantised pools (int8, int4), split schedule [P3 sec. 6 names quantised KV;
+// the stored value of a (token, kv head) row is code * scale].  One 16-token
+// chunk per step, as decode_mfma_kernel, with the codes' bytes:
 //   K: QK^T runs on the int8 matrix cores (v_mfma_i32_16x16x64_i8) on the
 //      codes as loaded: lane (n, g4) loads row n's codes [D/4 g4, D/4 (g4+1))
 //      and step j (64 codes) takes 16 of them; the query operand holds the
@@ -1159,32 +1159,26 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
 //      sl = sh / 254: |error| <= max|q| / 64516 per element, finer than the
 //      bf16 query itself), so a score is
 //      (sh * (qh . code_t) + sl * (ql . code_t)) * kscale_t * scale.
-//   V: each lane loads 16 codes of a row, converts them and writes the
-//      bf16 row pieces into the wave's V tile in the bf16 kernel's tile
-//      layout; P.V then reads it with the same transposing LDS read.  The
-//      value scale folds into the probabilities: P'_t = p_t * vscale_t
-//      (rounded to bf16 as P is); the denominator sums P'_t / vscale_t, the
-//      weights the operand carries.
+//   V: P.V runs on the bf16 matrix cores (v_mfma_f32_16x16x16_bf16) with
+//      the V codes as the B operand straight from registers: lane (n, g4)
+//      loads columns [C n, C n + C) (C = D / 16) of its four tokens
+//      4 g4 .. 4 g4 + 3, the rows whose probabilities its score lanes already
+//      hold, and converts code c of each to bf16 for the product of column
+//      C n + c.  No LDS tile: the chunk's chain is loads, conversions, matrix
+//      products.  Lane (n, g4) accumulates columns [C n, C n + C) of heads
+//      4 g4 .. 4 g4 + 3, so one store instruction of the outputs or partials
+//      covers a head row.  The value scale folds into the probabilities:
+//      P'_t = p_t * vscale_t (rounded to bf16 as P is); the denominator sums
+//      P'_t / vscale_t, the weights the operand carries.
 //   Scales: the 16 tokens of a chunk are contiguous per head (layout
 //      (block, layer, head, slot)), so lane (n, g4) loads the scales of its
-//      four score rows 4 g4 .. 4 g4 + 3 with one 16-byte load each.
+//      four tokens 4 g4 .. 4 g4 + 3 with one 16-byte load each.
+//   int4: a nibble moved to the top of its byte is the signed byte 16 * code,
+//      so both operands use the int8 paths above; the 1/16 goes into the
+//      query's scales (K) and the value scales (V).
 //   Codes are always finite, so rows without a live token need no zeroing:
 //   their score is -inf and their P' exactly 0.
 // ---------------------------------------------------------------------------
-
-// Two int8 codes (bytes sh/8, sh/8 + 1 of w) as a bf16 pair: the high
-// halves of their exact float values.
-__device__ __forceinline__ uint32_t i8pair_bf16(uint32_t w, int sh) {
-    const float lo = (float)(int32_t)(int8_t)(w >> sh);
-    const float hi = (float)(int32_t)(int8_t)(w >> (sh + 8));
-    return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
-}
-
-// 16 codes -> 16 bf16 values (two 16-byte pieces, in order).
-__device__ __forceinline__ void i8x16_bf16(u32x4 c, u32x4 &lo, u32x4 &hi) {
-    lo = u32x4{i8pair_bf16(c.x, 0), i8pair_bf16(c.x, 16), i8pair_bf16(c.y, 0), i8pair_bf16(c.y, 16)};
-    hi = u32x4{i8pair_bf16(c.z, 0), i8pair_bf16(c.z, 16), i8pair_bf16(c.w, 0), i8pair_bf16(c.w, 16)};
-}
 
 // int4: eight codes in a word (byte k: element 2k in the low nibble, 2k + 1
 // in the high nibble) as bytes holding 16 * code, exactly: the nibble moved
@@ -1193,28 +1187,15 @@ __device__ __forceinline__ void i8x16_bf16(u32x4 c, u32x4 &lo, u32x4 &hi) {
 __device__ __forceinline__ uint32_t i4_even16(uint32_t w) { return (w << 4) & 0xF0F0F0F0u; }
 __device__ __forceinline__ uint32_t i4_odd16(uint32_t w) { return w & 0xF0F0F0F0u; }
 
-// 16 int4 codes (two words, in element order) -> 16 bf16 values 16 * code
-// (two 16-byte pieces, in element order), exact.
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ u32x2 ld8_nt(const char *p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
 }
-
-__device__ __forceinline__ void i4x16_bf16(u32x2 c, u32x4 &lo, u32x4 &hi) {
-    uint32_t r[8];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const uint32_t w = h ? c.y : c.x;
-        const uint32_t e = i4_even16(w), o = i4_odd16(w);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const float fe = (float)(int32_t)(int8_t)(e >> (8 * k));
-            const float fo = (float)(int32_t)(int8_t)(o >> (8 * k));
-            r[4 * h + k] = __builtin_amdgcn_perm(__float_as_uint(fo), __float_as_uint(fe), 0x07060302u);
-        }
-    }
-    lo = u32x4{r[0], r[1], r[2], r[3]};
-    hi = u32x4{r[4], r[5], r[6], r[7]};
+__device__ __forceinline__ uint32_t ld4_nt(const char *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(p));
+}
+__device__ __forceinline__ uint32_t ld2_nt(const char *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(p));
 }
 
 typedef int v4i32 __attribute__((ext_vector_type(4)));
@@ -1279,46 +1260,71 @@ __device__ __forceinline__ void load_q_q8(const DecodeArgs &a, int seq, int h, Q
     qq.sl = QB == 8 ? sl : sl * 0.0625f;
 }
 
-// int4 pool: K codes D/8 bytes per lane (16 at head_dim 128: one load, 8 at
-// 64), V codes 8 bytes per lane per row load.
+
+// int8 V: two codes (bytes sh/8, sh/8 + 1 of w) as a bf16 pair, the high
+// halves of their exact float values; 16 codes -> 16 bf16 values (two
+// 16-byte pieces, in order).
+__device__ __forceinline__ uint32_t i8pair_bf16(uint32_t w, int sh) {
+    const float lo = (float)(int32_t)(int8_t)(w >> sh);
+    const float hi = (float)(int32_t)(int8_t)(w >> (sh + 8));
+    return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+__device__ __forceinline__ void i8x16_bf16(u32x4 c, u32x4 &lo, u32x4 &hi) {
+    lo = u32x4{i8pair_bf16(c.x, 0), i8pair_bf16(c.x, 16), i8pair_bf16(c.y, 0), i8pair_bf16(c.y, 16)};
+    hi = u32x4{i8pair_bf16(c.z, 0), i8pair_bf16(c.z, 16), i8pair_bf16(c.w, 0), i8pair_bf16(c.w, 16)};
+}
+
+// int4 V: the B operand of column C n + c for the lane's four rows, as bf16
+// of 16 * code, two per register.  e[r] holds i4_even16 and i4_odd16 of row
+// r's code word, so element c is byte c >> 1 of word c & 1.
+__device__ __forceinline__ uint64_t i4_operand(const uint32_t (&e)[4][2], int c) {
+    float f[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) f[r] = (float)(int32_t)(int8_t)(e[r][c & 1] >> (8 * (c >> 1)));
+    const uint32_t lo = __builtin_amdgcn_perm(__float_as_uint(f[1]), __float_as_uint(f[0]), 0x07060302u);
+    const uint32_t hi = __builtin_amdgcn_perm(__float_as_uint(f[3]), __float_as_uint(f[2]), 0x07060302u);
+    return (uint64_t)lo | ((uint64_t)hi << 32);
+}
+
+// One chunk's loads.  int8: K, the lane's D/4 codes of row n (D/64 16-byte
+// loads); V, D/64 16-byte pieces of tile rows (lane: codes 16 (lane % (D/16))
+// .. + 16 of row i (64 / (D/16)) + lane / (D/16)).  int4: K, the lane's D/8
+// bytes of row n; V, the lane's C = D/16 columns [C n, C n + C) of each of
+// its four rows 4 g4 .. 4 g4 + 3, C/2 bytes each.  Both: the K and V scales
+// of tokens 4 g4 .. 4 g4 + 3.
+template <int D, int QB>
+struct QSlot {
+    static constexpr int KL = D / 64;
+    u32x4 k[KL];
+    u32x4 v[D / 64];
+    u32x4 ks, vs;
+};
 template <int D>
-struct Q4Slot {
-    static constexpr int VL = D / 64;
-    u32x4 k;                                 // (head_dim 64: .x, .y only)
-    u32x2 v[VL];
+struct QSlot<D, 4> {
+    u32x4 k;                                 // head_dim 64: .x, .y only
+    uint32_t v[4];
     u32x4 ks, vs;
 };
 
-template <int D>
-struct Q8Slot {
-    static constexpr int KL = D / 64;        // K loads (16 codes) per lane per chunk
-    static constexpr int VL = D / 64;        // V loads per lane per chunk
-    u32x4 k[KL];
-    u32x4 v[VL];
-    u32x4 ks, vs;                            // scales of tokens 4 g4 .. 4 g4 + 3
-};
-
-// QB: bits per code, 8 (int8 pool) or 4 (int4 pool).  An int4 chunk takes
-// half the loads; its codes are unpacked to 16 * code (exact), with the 1/16
-// in the query's scales (K) and in the value scales (V), so the rest of the
-// chunk's work is the int8 kernel's.
+// QB: bits per code, 8 (int8 pool: V through the wave's LDS tile, in the
+// bf16 kernel's layout) or 4 (int4 pool: V as a register operand).
 template <int D, int G, bool UB, int QB>
 __device__ __forceinline__ void attend_range_q8(const DecodeArgs &a, const Range &R, int64_t jb0,
                                                 const int32_t *bt_s, char *vt, int h,
                                                 const Q8Query<D> &qq, float &m_h,
-                                                float &l_h, f32x4 (&acc)[MfmaShape<D>::NV]) {
+                                                float &l_h, f32x4 (&acc)[D / 16]) {
     using S = MfmaShape<D>;
-    using Slot = std::conditional_t<QB == 8, Q8Slot<D>, Q4Slot<D>>;
+    using Slot = QSlot<D, QB>;
     constexpr int HB = D * QB / 8;   // bytes of one (token, kv head) row of codes
     constexpr int KB = D * QB / 32;  // K code bytes per lane per chunk
-    constexpr int VB = 2 * QB;       // V code bytes per lane per row load (16 codes)
-    constexpr int KS = S::KS, NV = S::NV, NP = S::NP, ROWB = S::ROWB, VSLAB = S::VSLAB;
+    constexpr int C = D / 16;        // P.V column slabs (int4: V columns per lane)
+    constexpr int NP = S::NP, ROWB = S::ROWB, VSLAB = S::VSLAB;
     // two slots (one chunk in flight while one is computed): measured
     // faster than three on the decode batch (30.8 against 32.0 us, same
     // process), level on the other batches
     constexpr int NSLOT = 2;
-    constexpr int VPR = D / 16;      // 16-code pieces per row
-    constexpr int VRPL = 64 / VPR;   // rows per V load
+    constexpr int VPR = D / 16;      // int8: 16-code pieces per row
+    constexpr int VRPL = 64 / VPR;   // int8: rows per V load
     constexpr float kLazy = 8.0f;
     const int lane = threadIdx.x & 63;
     const int n = lane & 15, g4 = lane >> 4;
@@ -1342,9 +1348,10 @@ __device__ __forceinline__ void attend_range_q8(const DecodeArgs &a, const Range
             sl.k = u32x4{w.x, w.y, 0u, 0u};
         }
     };
-    auto load_v = [&](const char *vb, Slot &sl, int i) {
-        if constexpr (QB == 8) sl.v[i] = ld16_nt(vb);
-        else sl.v[i] = ld8_nt(vb);
+    // int4 V row r of the lane: C/2 bytes at column C n
+    auto load_v4 = [&](const char *row, Slot &sl, int r) {
+        if constexpr (D == 128) sl.v[r] = ld4_nt(row + 4 * n);
+        else sl.v[r] = ld2_nt(row + 2 * n);
     };
 
     auto load_chunk = [&](int64_t pc, Slot &sl) {
@@ -1352,38 +1359,41 @@ __device__ __forceinline__ void attend_range_q8(const DecodeArgs &a, const Range
             const int32_t b = __builtin_amdgcn_readfirstlane(bt_s[(int)((pc >> lbs) - jb0)]);
             const int64_t bb = b >= 0 ? b : 0;
             const int64_t base = bb * a.pool.block_stride + (pc & bsm) * row_bytes;
-            const char *kb = kh + base + (uint32_t)(n * row_bytes + KB * g4);
-            load_k(kb, sl);
+            load_k(kh + base + (uint32_t)(n * row_bytes + KB * g4), sl);
+            if constexpr (QB == 8) {
 #pragma unroll
-            for (int i = 0; i < Slot::VL; ++i)
-                load_v(vh + base + (uint32_t)((i * VRPL + vrow) * row_bytes + VB * vpc), sl, i);
+                for (int i = 0; i < D / 64; ++i)
+                    sl.v[i] = ld16_nt(vh + base + (uint32_t)((i * VRPL + vrow) * row_bytes + 16 * vpc));
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) load_v4(vh + base + (uint32_t)((4 * g4 + r) * row_bytes), sl, r);
+            }
             const int64_t so = bb * a.pool.sc_block + (pc & bsm) + 4 * g4;
             sl.ks = ld16_nt(reinterpret_cast<const char *>(ksh + so));
             sl.vs = ld16_nt(reinterpret_cast<const char *>(vsh + so));
         } else {
-            {
-                const int64_t p = pc + n;
+            auto row_at = [&](int64_t p, int64_t &bb) {
                 const bool in = p >= R.lo && p < R.hi;
                 const int32_t b = in ? bt_s[(int)((p >> lbs) - jb0)] : -1;
-                const char *kb = kh + (int64_t)(b >= 0 ? b : 0) * a.pool.block_stride + (p & bsm) * row_bytes + KB * g4;
-                load_k(kb, sl);
-            }
+                bb = b >= 0 ? b : 0;
+                return bb * a.pool.block_stride + (p & bsm) * row_bytes;
+            };
+            int64_t bb;
+            load_k(kh + row_at(pc + n, bb) + KB * g4, sl);
+            if constexpr (QB == 8) {
 #pragma unroll
-            for (int i = 0; i < Slot::VL; ++i) {
-                const int64_t p = pc + i * VRPL + vrow;
-                const bool in = p >= R.lo && p < R.hi;
-                const int32_t b = in ? bt_s[(int)((p >> lbs) - jb0)] : -1;
-                load_v(vh + (int64_t)(b >= 0 ? b : 0) * a.pool.block_stride + (p & bsm) * row_bytes + VB * vpc, sl, i);
+                for (int i = 0; i < D / 64; ++i)
+                    sl.v[i] = ld16_nt(vh + row_at(pc + i * VRPL + vrow, bb) + 16 * vpc);
             }
             uint32_t kw[4], vw[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int64_t p = pc + 4 * g4 + e;
-                const bool in = p >= R.lo && p < R.hi;
-                const int32_t b = in ? bt_s[(int)((p >> lbs) - jb0)] : -1;
-                const int64_t so = (int64_t)(b >= 0 ? b : 0) * a.pool.sc_block + (p & bsm);
-                kw[e] = __float_as_uint(ksh[so]);
-                vw[e] = __float_as_uint(vsh[so]);
+            for (int r = 0; r < 4; ++r) {
+                const int64_t p = pc + 4 * g4 + r;
+                const int64_t off = row_at(p, bb);
+                if constexpr (QB == 4) load_v4(vh + off, sl, r);
+                const int64_t so = bb * a.pool.sc_block + (p & bsm);
+                kw[r] = __float_as_uint(ksh[so]);
+                vw[r] = __float_as_uint(vsh[so]);
             }
             sl.ks = u32x4{kw[0], kw[1], kw[2], kw[3]};
             sl.vs = u32x4{vw[0], vw[1], vw[2], vw[3]};
@@ -1391,24 +1401,30 @@ __device__ __forceinline__ void attend_range_q8(const DecodeArgs &a, const Range
     };
 
     auto compute = [&](int64_t pc, const Slot &sl) {
-        bool bok = true;
-        if constexpr (UB) bok = __builtin_amdgcn_readfirstlane(bt_s[(int)((pc >> lbs) - jb0)]) >= 0;
+        // live rows of the chunk: [rlo, rhi) relative to pc (32-bit, wave
+        // uniform), and (block size < 16) a table entry per row
+        const int64_t dlo = R.lo - pc, dhi = R.hi - pc;
+        const int32_t rlo = dlo > 0 ? (int32_t)dlo : 0;
+        int32_t rhi = dhi < 16 ? (int32_t)dhi : 16;
+        if constexpr (UB) {
+            if (__builtin_amdgcn_readfirstlane(bt_s[(int)((pc >> lbs) - jb0)]) < 0) rhi = 0;
+        }
         auto row_live = [&](int row) -> bool {
-            const int64_t p = pc + row;
-            const bool in = p >= R.lo && p < R.hi;
-            return UB ? (bok && in) : (in && bt_s[(int)((p >> lbs) - jb0)] >= 0);
+            const bool in = row >= rlo && row < rhi;
+            if constexpr (UB) return in;
+            else return in && bt_s[(int)(((pc + row) >> lbs) - jb0)] >= 0;
         };
-        const bool full = UB ? (bok && pc >= R.lo && pc + 16 <= R.hi) : false;
-        // V codes -> bf16 rows of the tile (the bf16 kernel's slab layout)
+        if constexpr (QB == 8) {
+            // V codes -> bf16 rows of the tile (the bf16 kernel's slab layout)
 #pragma unroll
-        for (int i = 0; i < Slot::VL; ++i) {
-            const int row = i * VRPL + vrow;
-            u32x4 lo, hi;
-            if constexpr (QB == 8) i8x16_bf16(sl.v[i], lo, hi);
-            else i4x16_bf16(sl.v[i], lo, hi);
-            char *dst = vt + (row % NP) * VSLAB + (row / NP) * ROWB + 32 * vpc;
-            *reinterpret_cast<u32x4 *>(dst) = lo;
-            *reinterpret_cast<u32x4 *>(dst + 16) = hi;
+            for (int i = 0; i < D / 64; ++i) {
+                const int row = i * VRPL + vrow;
+                u32x4 lo, hi;
+                i8x16_bf16(sl.v[i], lo, hi);
+                char *dst = vt + (row % NP) * VSLAB + (row / NP) * ROWB + 32 * vpc;
+                *reinterpret_cast<u32x4 *>(dst) = lo;
+                *reinterpret_cast<u32x4 *>(dst + 16) = hi;
+            }
         }
         // scores S[token 4 g4 + i][head n] from the codes as loaded
         v4i32 dh = {0, 0, 0, 0}, dl = {0, 0, 0, 0};
@@ -1428,7 +1444,7 @@ __device__ __forceinline__ void attend_range_q8(const DecodeArgs &a, const Range
         }
         const float ksf[4] = {__uint_as_float(sl.ks.x), __uint_as_float(sl.ks.y),
                               __uint_as_float(sl.ks.z), __uint_as_float(sl.ks.w)};
-        // (int4: the V tile holds 16 * code, so the value scales take 1/16)
+        // (int4: the V operand holds 16 * code, so the value scales take 1/16)
         constexpr float kVS = QB == 8 ? 1.0f : 0.0625f;
         const float vsf[4] = {__uint_as_float(sl.vs.x) * kVS, __uint_as_float(sl.vs.y) * kVS,
                               __uint_as_float(sl.vs.z) * kVS, __uint_as_float(sl.vs.w) * kVS};
@@ -1437,7 +1453,8 @@ __device__ __forceinline__ void attend_range_q8(const DecodeArgs &a, const Range
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const float dot = fmaf((float)dh[i], qq.sh, (float)dl[i] * qq.sl);
-            s[i] = (full || row_live(4 * g4 + i)) ? dot * ksf[i] * sl2 : kNegInf;
+            const float x = dot * ksf[i] * sl2;
+            s[i] = row_live(4 * g4 + i) ? x : kNegInf;
             cm = fmaxf(cm, s[i]);
         }
         cm = max_xor32(max_xor16(cm));
@@ -1452,44 +1469,53 @@ __device__ __forceinline__ void attend_range_q8(const DecodeArgs &a, const Range
             pr[i] = s[i] == kNegInf ? 0.0f : fast_exp2(s[i] - m_h);
             pv[i] = s[i] == kNegInf ? 0.0f : pr[i] * vsf[i];
         }
-        const uint32_t q01 = f32_to_bf16_bits(pv[0]) | (f32_to_bf16_bits(pv[1]) << 16);
-        const uint32_t q23 = f32_to_bf16_bits(pv[2]) | (f32_to_bf16_bits(pv[3]) << 16);
+        const uint32_t q01 = bf16x2_rne(pv[0], pv[1]);
+        const uint32_t q23 = bf16x2_rne(pv[2], pv[3]);
         // The denominator sums the weights the P.V operand actually carries,
         // bf16(p * vscale) / vscale, so the output is a convex combination of
         // the stored values code * vscale and a dominant token's rounding
         // cancels (summing bf16(p) instead left up to 2^-8 relative error on
         // peaked rows).  A zero (or tiny) scale is a zero row: its weight is
-        // bf16(p).
+        // p.
         const float qv[4] = {bf16_lo(q01), bf16_hi(q01), bf16_lo(q23), bf16_hi(q23)};
         float dsum = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float w = vsf[i] > 1e-30f ? qv[i] * __builtin_amdgcn_rcpf(vsf[i])
-                                            : __uint_as_float(f32_to_bf16_bits(pr[i]) << 16);
-            dsum += w;
-        }
+        for (int i = 0; i < 4; ++i) dsum += vsf[i] > 1e-30f ? qv[i] * __builtin_amdgcn_rcpf(vsf[i]) : pr[i];
         l_h = fmaf(l_h, alpha, dsum);
         if (__any(n < G && alpha != 1.0f)) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float al = __shfl(alpha, 4 * g4 + i);
 #pragma unroll
-                for (int sl2i = 0; sl2i < NV; ++sl2i) acc[sl2i][i] *= al;
+                for (int c = 0; c < C; ++c) acc[c][i] *= al;
             }
         }
         typedef short s16x4 __attribute__((ext_vector_type(4)));
         const s16x4 pa = __builtin_bit_cast(s16x4, (uint64_t)q01 | ((uint64_t)q23 << 32));
-        wave_lds_order();
-        const int orow = 4 * g4 + (n >> 2);
-        const int vbase = (orow % NP) * VSLAB + (orow / NP) * ROWB + 8 * (n & 3);
+        if constexpr (QB == 8) {
+            wave_lds_order();
+            const int orow = 4 * g4 + (n >> 2);
+            const int vbase = (orow % NP) * VSLAB + (orow / NP) * ROWB + 8 * (n & 3);
 #pragma unroll
-        for (int sl = 0; sl < NV; ++sl) {
-            const int off = vbase + 32 * sl;
-            const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4 *)((__attribute__((address_space(3))) char *)(vt) + off));
-            acc[sl] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, acc[sl], 0, 0, 0);
+            for (int c = 0; c < C; ++c) {
+                const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) s16x4 *)((__attribute__((address_space(3))) char *)(vt) +
+                                                                 vbase + 32 * c));
+                acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, acc[c], 0, 0, 0);
+            }
+            wave_lds_order();
+        } else {
+            uint32_t e[4][2];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                e[r][0] = i4_even16(sl.v[r]);
+                e[r][1] = i4_odd16(sl.v[r]);
+            }
+#pragma unroll
+            for (int c = 0; c < C; ++c)
+                acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, __builtin_bit_cast(s16x4, i4_operand(e, c)),
+                                                                   acc[c], 0, 0, 0);
         }
-        wave_lds_order();
     };
 
     const int64_t first = R.lo & ~int64_t(15);
@@ -1517,6 +1543,65 @@ __device__ __forceinline__ void attend_range_q8(const DecodeArgs &a, const Range
     }
 }
 
+// int4 path: lane (n, g4) holds columns C n .. C n + C - 1 (C = D / 16) of
+// head 4 g4 + i in acc[0..C)[i].  out[seq, h*G + hd, :] = acc / l, rounded
+// to bf16: one store of the lane's C columns per head.
+template <int D, int G>
+__device__ __forceinline__ void write_direct_i4(const DecodeArgs &a, int seq, int h,
+                                                const f32x4 (&acc)[D / 16], const float (&lrow)[4]) {
+    constexpr int C = D / 16;
+    const int lane = threadIdx.x & 63;
+    const int n = lane & 15, g4 = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int hd = 4 * g4 + i;
+        if (hd >= G) continue;
+        const float l = lrow[i];
+        uint32_t w[C / 2];
+#pragma unroll
+        for (int c = 0; c < C; c += 2)
+            w[c / 2] = bf16x2_rne(l > 0.0f ? acc[c][i] / l : 0.0f, l > 0.0f ? acc[c + 1][i] / l : 0.0f);
+        char *o = a.out + (((int64_t)seq * a.num_q_heads + (int64_t)h * G + hd) * D + C * n) * 2;
+        if constexpr (C == 8) *reinterpret_cast<u32x4 *>(o) = u32x4{w[0], w[1], w[2], w[3]};
+        else *reinterpret_cast<u32x2 *>(o) = u32x2{w[0], w[1]};
+    }
+}
+
+// int4 path: the unnormalised partial of the wave's G heads, acc rows at
+// accp + hd*D and (m, l) pairs at ml + 2*hd.  The acc rows go out as 16-byte
+// buffer stores with the device-scope cache policy of st_dev (sc1: through
+// this XCD's L2), bounds-checked by the resource to the G rows; their
+// completion is awaited with everything else before the split is counted in.
+template <int D, int G>
+__device__ __forceinline__ void write_partial_i4(float *ml, float *accp, const f32x4 (&acc)[D / 16],
+                                                 float m_h, float l_h) {
+    constexpr int C = D / 16;
+    constexpr int kSC1 = 16;  // cache-policy bit sc1 of a buffer access
+    const int lane = threadIdx.x & 63;
+    const int n = lane & 15, g4 = lane >> 4;
+    // accp is the same in every lane; the resource takes it from SGPRs.
+    // (readfirstlane returns a signed int: each half is widened through
+    // uint32_t, or a low half with bit 31 set would sign-extend into the
+    // high half.)
+    const uint64_t u = reinterpret_cast<uint64_t>(accp);
+    const uint32_t ulo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)u);
+    const uint32_t uhi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+    float *base = reinterpret_cast<float *>(((uint64_t)uhi << 32) | ulo);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(base, 0, G * D * 4, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int hd = 4 * g4 + i;
+        if (hd >= G) continue;
+#pragma unroll
+        for (int c = 0; c < C; c += 4) {
+            const u32x4 v = {__float_as_uint(acc[c][i]), __float_as_uint(acc[c + 1][i]),
+                             __float_as_uint(acc[c + 2][i]), __float_as_uint(acc[c + 3][i])};
+            __builtin_amdgcn_raw_buffer_store_b128(v, rs, (hd * D + C * n + c) * 4, 0, kSC1);
+        }
+    }
+    if (g4 == 0 && n < G) st_dev2(ml + 2 * n, m_h, l_h);
+}
+
 // QB: bits per code of the pool, 8 or 4.
 template <int D, int G, bool UB, int QB>
 // Two wavefronts per SIMD: without the hint the compiler takes 272
@@ -1525,6 +1610,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     using S = MfmaShape<D>;
     static_assert(G >= 1 && G <= 16, "group");
     __shared__ int32_t bt_s[kBtLds];
+    // int8: the wave's V tile; both: merge records of the fused merge
     __shared__ __attribute__((aligned(16))) char vtiles[4][S::VTILE];
 
     Item it;
@@ -1550,18 +1636,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     load_q_q8<D, G, QB>(a, it.seq, h, qq);
     float m_h = kNegInf;
     float l_h = 0.0f;
-    f32x4 acc[S::NV];
+    f32x4 acc[D / 16];
 #pragma unroll
-    for (int sl = 0; sl < S::NV; ++sl) acc[sl] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int c = 0; c < D / 16; ++c) acc[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     attend_range_q8<D, G, UB, QB>(a, R, jb0, bt_s, vtiles[w], h, qq, m_h, l_h, acc);
     float lrow[4];
     head_denominators(l_h, lrow);
-    if (direct) {
-        write_direct<D, G>(a, it.seq, h, acc, lrow);
-        return;
-    }
     const int64_t item0 = ((int64_t)it.seq * a.max_splits + it.split) * a.num_q_heads + (int64_t)h * G;
-    write_partial<D, G>(a.ws_ml + item0 * 2, a.ws_acc + item0 * D, acc, m_h, l_h);
+    if constexpr (QB == 8) {
+        if (direct) {
+            write_direct<D, G>(a, it.seq, h, acc, lrow);
+            return;
+        }
+        write_partial<D, G>(a.ws_ml + item0 * 2, a.ws_acc + item0 * D, acc, m_h, l_h);
+    } else {
+        if (direct) {
+            write_direct_i4<D, G>(a, it.seq, h, acc, lrow);
+            return;
+        }
+        write_partial_i4<D, G>(a.ws_ml + item0 * 2, a.ws_acc + item0 * D, acc, m_h, l_h);
+    }
     if (a.fused_merge) finish_split<1, D, G>(a, it, R, split, vtiles[w], S::VTILE);
 }
 

@@ -249,3 +249,31 @@ def test_int4_decode_batch_full_size(dev):
     err = max_abs_err(got, ref)
     print(f"int4 decode batch, all {w.num_seqs} sequences: max abs err {err:.3e}")
     assert err <= TOL
+
+
+@pytest.mark.parametrize("d,group", [(64, 1), (128, 8)])
+def test_int4_partials_at_high_workspace_addresses(dev, d, group):
+    """Split partials written through a workspace whose address has bit 31
+    of its low word set, and one where it is clear: the int4 partial writer
+    builds a buffer resource from the workspace address, so both halves of
+    that address must reach it unchanged."""
+    w, k, v = workload(dev, 910 + group, d=d, group=group, num_seqs=4, max_len=300)
+    ref = oracle_decode(w, k, v)
+    need = N.paged_attn_decode_workspace_size(w.num_seqs, w.num_kv_heads, w.num_q_heads, w.head_dim,
+                                              w.max_seq_len, w.block_size, 16)
+    big = torch.zeros((1 << 32) + need + 4096, dtype=torch.uint8, device=dev)
+    base = big.data_ptr()
+    for want_bit in (True, False):
+        # the first 256-byte aligned offset whose address has bit 31 set (or clear)
+        off = 0
+        while bool((base + off) & 0x80000000) != want_bit:
+            off += 1 << 28
+        off += (-(base + off)) % 256
+        assert bool((base + off) & 0x80000000) == want_bit and off + need <= big.numel()
+        ws = big[off:off + need]
+        got = N.paged_attn_decode(k, v, w.layer, w.q, w.block_tables, w.seq_lens, w.offsets,
+                                  w.max_seq_len, w.scale, split_tokens=16,
+                                  out=torch.full_like(w.q, float("nan")), workspace=ws)
+        assert max_abs_err(got, ref) <= TOL, want_bit
+    del big
+    torch.cuda.empty_cache()
