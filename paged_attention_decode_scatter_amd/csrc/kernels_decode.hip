@@ -1214,24 +1214,41 @@ __device__ __forceinline__ uint32_t q8_code(float x, float inv) {
     return (uint32_t)(int32_t)fminf(fmaxf(__builtin_rintf(x * inv), -127.0f), 127.0f) & 0xffu;
 }
 
+// The bf16 query elements the lane quantises: lane (n, g4), elements
+// D/4 g4 .. D/4 (g4 + 1) of head n, as D/64 pairs of 16-byte loads.  Issued
+// before the first chunk's loads, so the quantisation runs while those are
+// in flight.  Lanes of heads n >= G load head G - 1 (no branch around the
+// loads, whose merge would wait for them) and quantise zeros.
+template <int D>
+struct QRaw {
+    u32x4 w[D / 64][2];
+};
+
+template <int D, int G>
+__device__ __forceinline__ void load_q_raw(const DecodeArgs &a, int seq, int h, QRaw<D> &raw) {
+    const int lane = threadIdx.x & 63;
+    const int n = lane & 15, g4 = lane >> 4;
+    const int hn = n < G ? n : G - 1;
+    const char *qp = a.q + (((int64_t)seq * a.num_q_heads + (int64_t)h * G + hn) * D + (D / 4) * g4) * 2;
+#pragma unroll
+    for (int j = 0; j < D / 64; ++j)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) raw.w[j][c] = ld16(qp + 32 * j + 16 * c);
+}
+
 // QB = 4 (int4 pool): the K codes arrive as 16 * code with each group of 8
 // elements in the order 0, 2, 4, 6, 1, 3, 5, 7 (i4_even16 / i4_odd16), so
 // the query's codes take the same order and its scales carry the 1/16.
 template <int D, int G, int QB>
-__device__ __forceinline__ void load_q_q8(const DecodeArgs &a, int seq, int h, Q8Query<D> &qq) {
+__device__ __forceinline__ void quantize_q(const QRaw<D> &raw, Q8Query<D> &qq) {
     constexpr int KL = D / 64;
-    const int lane = threadIdx.x & 63;
-    const int n = lane & 15, g4 = lane >> 4;
-    const char *qp = a.q + (((int64_t)seq * a.num_q_heads + (int64_t)h * G + n) * D + (D / 4) * g4) * 2;
+    const bool live = (threadIdx.x & 15) < G;
     float x[KL][16];
     float amax = 0.0f;
 #pragma unroll
     for (int j = 0; j < KL; ++j) {
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            const u32x4 w = n < G ? ld16(qp + 32 * j + 16 * c) : u32x4{0, 0, 0, 0};
-            unpack16<1>(w, &x[j][8 * c]);
-        }
+        for (int c = 0; c < 2; ++c) unpack16<1>(live ? raw.w[j][c] : u32x4{0, 0, 0, 0}, &x[j][8 * c]);
 #pragma unroll
         for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(x[j][e]));
     }
@@ -1259,7 +1276,6 @@ __device__ __forceinline__ void load_q_q8(const DecodeArgs &a, int seq, int h, Q
     qq.sh = QB == 8 ? sh : sh * 0.0625f;
     qq.sl = QB == 8 ? sl : sl * 0.0625f;
 }
-
 
 // int8 V: two codes (bytes sh/8, sh/8 + 1 of w) as a bf16 pair, the high
 // halves of their exact float values; 16 codes -> 16 bf16 values (two
@@ -1311,7 +1327,7 @@ struct QSlot<D, 4> {
 template <int D, int G, bool UB, int QB>
 __device__ __forceinline__ void attend_range_q8(const DecodeArgs &a, const Range &R, int64_t jb0,
                                                 const int32_t *bt_s, char *vt, int h,
-                                                const Q8Query<D> &qq, float &m_h,
+                                                const QRaw<D> &qraw, float &m_h,
                                                 float &l_h, f32x4 (&acc)[D / 16]) {
     using S = MfmaShape<D>;
     using Slot = QSlot<D, QB>;
@@ -1332,6 +1348,7 @@ __device__ __forceinline__ void attend_range_q8(const DecodeArgs &a, const Range
     const int64_t bsm = (1ll << lbs) - 1;
     const int64_t row_bytes = a.pool.row_bytes;
     const float sl2 = a.scale_log2;
+    Q8Query<D> qq;
     const char *kh = a.pool.k + a.pool.layer_off + (int64_t)h * HB;
     const char *vh = a.pool.v + a.pool.layer_off + (int64_t)h * HB;
     const float *ksh = a.pool.ks + ((int64_t)h << lbs);
@@ -1528,6 +1545,10 @@ __device__ __forceinline__ void attend_range_q8(const DecodeArgs &a, const Range
         // ring registers) made the compiler's waits conservative, measured
         // 67 -> 75 us on prefix sharing.
         for (int q = 0; q < NSLOT - 1; ++q) load_chunk(min(first + 16 * q, last), ring[q]);
+        // the query's int8 parts, while the first chunk is in flight (the
+        // barrier keeps the scheduler from hoisting them above its loads)
+        __builtin_amdgcn_sched_barrier(0);
+        quantize_q<D, G, QB>(qraw, qq);
         bool done = false;
         for (int64_t pc = first; !done;) {
 #pragma unroll
@@ -1632,14 +1653,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     const int64_t jb0 = stage_table(a, it.seq, R, bt_s);
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int h = it.hg * a.heads_per_wg + w;
-    Q8Query<D> qq;
-    load_q_q8<D, G, QB>(a, it.seq, h, qq);
+    QRaw<D> qraw;
+    load_q_raw<D, G>(a, it.seq, h, qraw);
     float m_h = kNegInf;
     float l_h = 0.0f;
     f32x4 acc[D / 16];
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) acc[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    attend_range_q8<D, G, UB, QB>(a, R, jb0, bt_s, vtiles[w], h, qq, m_h, l_h, acc);
+    attend_range_q8<D, G, UB, QB>(a, R, jb0, bt_s, vtiles[w], h, qraw, m_h, l_h, acc);
     float lrow[4];
     head_denominators(l_h, lrow);
     const int64_t item0 = ((int64_t)it.seq * a.max_splits + it.split) * a.num_q_heads + (int64_t)h * G;
