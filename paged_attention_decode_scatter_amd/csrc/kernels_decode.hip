@@ -1650,11 +1650,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
             return;
         }
     }
-    const int64_t jb0 = stage_table(a, it.seq, R, bt_s);
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int h = it.hg * a.heads_per_wg + w;
+    // the query's loads go out before the table's, so it has arrived by the
+    // time the first chunk's loads are issued and its quantisation starts
     QRaw<D> qraw;
     load_q_raw<D, G>(a, it.seq, h, qraw);
+    const int64_t jb0 = stage_table(a, it.seq, R, bt_s);
     float m_h = kNegInf;
     float l_h = 0.0f;
     f32x4 acc[D / 16];
