@@ -1290,16 +1290,23 @@ __device__ __forceinline__ void i8x16_bf16(u32x4 c, u32x4 &lo, u32x4 &hi) {
     hi = u32x4{i8pair_bf16(c.z, 0), i8pair_bf16(c.z, 16), i8pair_bf16(c.w, 0), i8pair_bf16(c.w, 16)};
 }
 
-// int4 V: the B operand of column C n + c for the lane's four rows, as bf16
-// of 16 * code, two per register.  e[r] holds i4_even16 and i4_odd16 of row
-// r's code word, so element c is byte c >> 1 of word c & 1.
-__device__ __forceinline__ uint64_t i4_operand(const uint32_t (&e)[4][2], int c) {
-    float f[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) f[r] = (float)(int32_t)(int8_t)(e[r][c & 1] >> (8 * (c >> 1)));
-    const uint32_t lo = __builtin_amdgcn_perm(__float_as_uint(f[1]), __float_as_uint(f[0]), 0x07060302u);
-    const uint32_t hi = __builtin_amdgcn_perm(__float_as_uint(f[3]), __float_as_uint(f[2]), 0x07060302u);
-    return (uint64_t)lo | ((uint64_t)hi << 32);
+// int4 V: the B operands of columns C n + 2k and C n + 2k + 1 for the
+// lane's four rows, as bf16 of kI4Bias + code, two rows per register.  A
+// nibble XOR 8 is code + 8 in [0, 15]; OR-ed into the mantissa of bf16 128
+// (0x4300) it is the bf16 value 128 + code + 8, exactly.  b[r] is row r's
+// code word XOR 0x88888888; one byte permute gathers byte k of two rows (the
+// low and the high nibble are columns 2k and 2k + 1), one AND-OR per column
+// makes the pair.
+constexpr float kI4Bias = 136.0f;
+// kM = 0x000F000F and kOne = 0x43004300 come in registers (see the caller).
+__device__ __forceinline__ void i4_operands(const uint32_t (&b)[4], int k, uint32_t kM, uint32_t kOne,
+                                            uint64_t &even, uint64_t &odd) {
+    // byte k of b[r0] to byte 0, byte k of b[r1] to byte 2, zeros elsewhere
+    const uint32_t sel = (uint32_t)k | (0x0cu << 8) | ((uint32_t)(4 + k) << 16) | (0x0cu << 24);
+    const uint32_t p01 = __builtin_amdgcn_perm(b[1], b[0], sel);
+    const uint32_t p23 = __builtin_amdgcn_perm(b[3], b[2], sel);
+    even = (uint64_t)((p01 & kM) | kOne) | ((uint64_t)((p23 & kM) | kOne) << 32);
+    odd = (uint64_t)(((p01 >> 4) & kM) | kOne) | ((uint64_t)(((p23 >> 4) & kM) | kOne) << 32);
 }
 
 // One chunk's loads.  int8: K, the lane's D/4 codes of row n (D/64 16-byte
@@ -1328,7 +1335,7 @@ template <int D, int G, bool UB, int QB>
 __device__ __forceinline__ void attend_range_q8(const DecodeArgs &a, const Range &R, int64_t jb0,
                                                 const int32_t *bt_s, char *vt, int h,
                                                 const QRaw<D> &qraw, float &m_h,
-                                                float &l_h, f32x4 (&acc)[D / 16]) {
+                                                float &l_h, float &p_h, f32x4 (&acc)[D / 16]) {
     using S = MfmaShape<D>;
     using Slot = QSlot<D, QB>;
     constexpr int HB = D * QB / 8;   // bytes of one (token, kv head) row of codes
@@ -1349,6 +1356,12 @@ __device__ __forceinline__ void attend_range_q8(const DecodeArgs &a, const Range
     const int64_t row_bytes = a.pool.row_bytes;
     const float sl2 = a.scale_log2;
     Q8Query<D> qq;
+    // int4 operand constants, held in registers for the whole range: an
+    // AND-OR of three registers is one VOP3 instruction, and VOP3 takes no
+    // 32-bit literal on this target (the empty asm keeps them from being
+    // folded back into literals)
+    uint32_t kI4M = 0x000F000Fu, kI4One = 0x43004300u;
+    if constexpr (QB == 4) asm("" : "+v"(kI4M), "+v"(kI4One));
     const char *kh = a.pool.k + a.pool.layer_off + (int64_t)h * HB;
     const char *vh = a.pool.v + a.pool.layer_off + (int64_t)h * HB;
     const float *ksh = a.pool.ks + ((int64_t)h << lbs);
@@ -1461,10 +1474,8 @@ __device__ __forceinline__ void attend_range_q8(const DecodeArgs &a, const Range
         }
         const float ksf[4] = {__uint_as_float(sl.ks.x), __uint_as_float(sl.ks.y),
                               __uint_as_float(sl.ks.z), __uint_as_float(sl.ks.w)};
-        // (int4: the V operand holds 16 * code, so the value scales take 1/16)
-        constexpr float kVS = QB == 8 ? 1.0f : 0.0625f;
-        const float vsf[4] = {__uint_as_float(sl.vs.x) * kVS, __uint_as_float(sl.vs.y) * kVS,
-                              __uint_as_float(sl.vs.z) * kVS, __uint_as_float(sl.vs.w) * kVS};
+        const float vsf[4] = {__uint_as_float(sl.vs.x), __uint_as_float(sl.vs.y), __uint_as_float(sl.vs.z),
+                              __uint_as_float(sl.vs.w)};
         float s[4];
         float cm = kNegInf;
 #pragma unroll
@@ -1499,6 +1510,8 @@ __device__ __forceinline__ void attend_range_q8(const DecodeArgs &a, const Range
 #pragma unroll
         for (int i = 0; i < 4; ++i) dsum += vsf[i] > 1e-30f ? qv[i] * __builtin_amdgcn_rcpf(vsf[i]) : pr[i];
         l_h = fmaf(l_h, alpha, dsum);
+        // int4: the sum of P' the products carry, for the bias kI4Bias * sum
+        if constexpr (QB == 4) p_h = fmaf(p_h, alpha, (qv[0] + qv[1]) + (qv[2] + qv[3]));
         if (__any(n < G && alpha != 1.0f)) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -1522,16 +1535,18 @@ __device__ __forceinline__ void attend_range_q8(const DecodeArgs &a, const Range
             }
             wave_lds_order();
         } else {
-            uint32_t e[4][2];
+            uint32_t b[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                e[r][0] = i4_even16(sl.v[r]);
-                e[r][1] = i4_odd16(sl.v[r]);
+            for (int r = 0; r < 4; ++r) b[r] = sl.v[r] ^ 0x88888888u;
+#pragma unroll
+            for (int k = 0; k < C / 2; ++k) {
+                uint64_t ev, od;
+                i4_operands(b, k, kI4M, kI4One, ev, od);
+                acc[2 * k] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, __builtin_bit_cast(s16x4, ev),
+                                                                       acc[2 * k], 0, 0, 0);
+                acc[2 * k + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, __builtin_bit_cast(s16x4, od),
+                                                                           acc[2 * k + 1], 0, 0, 0);
             }
-#pragma unroll
-            for (int c = 0; c < C; ++c)
-                acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, __builtin_bit_cast(s16x4, i4_operand(e, c)),
-                                                                   acc[c], 0, 0, 0);
         }
     };
 
@@ -1659,12 +1674,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     const int64_t jb0 = stage_table(a, it.seq, R, bt_s);
     float m_h = kNegInf;
     float l_h = 0.0f;
+    float p_h = 0.0f;
     f32x4 acc[D / 16];
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) acc[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    attend_range_q8<D, G, UB, QB>(a, R, jb0, bt_s, vtiles[w], h, qraw, m_h, l_h, acc);
+    attend_range_q8<D, G, UB, QB>(a, R, jb0, bt_s, vtiles[w], h, qraw, m_h, l_h, p_h, acc);
     float lrow[4];
     head_denominators(l_h, lrow);
+    if constexpr (QB == 4) {
+        // remove the operand bias: acc row i (head 4 g4 + i) minus
+        // kI4Bias * (sum of that head's P'), before the partials or outputs
+        float prow[4];
+        head_denominators(p_h, prow);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int c = 0; c < D / 16; ++c) acc[c][i] = fmaf(-kI4Bias, prow[i], acc[c][i]);
+    }
     const int64_t item0 = ((int64_t)it.seq * a.max_splits + it.split) * a.num_q_heads + (int64_t)h * G;
     if constexpr (QB == 8) {
         if (direct) {
