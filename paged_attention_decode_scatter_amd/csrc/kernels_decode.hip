@@ -919,14 +919,20 @@ __device__ __forceinline__ void attend_range(const DecodeArgs &a, int seq, const
         wait_chunks_in_flight<LOADS>(ahead);
         wave_lds_order();
         char *vt = vring + slot * VTILE;
-        bool bok = true;
-        if constexpr (UB) bok = __builtin_amdgcn_readfirstlane(bt_s[(int)((pc >> lbs) - jb0)]) >= 0;
+        // live rows of the chunk: [rlo, rhi) relative to pc (32-bit, wave
+        // uniform), and (block size < 16) a table entry per row
+        const int64_t dlo = R.lo - pc, dhi = R.hi - pc;
+        const int32_t rlo = dlo > 0 ? (int32_t)dlo : 0;
+        int32_t rhi = dhi < 16 ? (int32_t)dhi : 16;
+        if constexpr (UB) {
+            if (__builtin_amdgcn_readfirstlane(bt_s[(int)((pc >> lbs) - jb0)]) < 0) rhi = 0;
+        }
         auto row_live = [&](int row) -> bool {
-            const int64_t p = pc + row;
-            const bool in = p >= R.lo && p < R.hi;
-            return UB ? (bok && in) : (in && bt_s[(int)((p >> lbs) - jb0)] >= 0);
+            const bool in = row >= rlo && row < rhi;
+            if constexpr (UB) return in;
+            else return in && bt_s[(int)(((pc + row) >> lbs) - jb0)] >= 0;
         };
-        const bool full = UB ? (bok && pc >= R.lo && pc + 16 <= R.hi) : false;
+        const bool full = UB ? (rlo == 0 && rhi == 16) : false;
         if (!full) {
             // zero the tile rows that hold no live token
 #pragma unroll
@@ -945,7 +951,8 @@ __device__ __forceinline__ void attend_range(const DecodeArgs &a, int seq, const
         float cm = kNegInf;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            s[i] = (full || row_live(4 * g4 + i)) ? sacc[i] * sl2 : kNegInf;
+            const float x = sacc[i] * sl2;
+            s[i] = row_live(4 * g4 + i) ? x : kNegInf;
             cm = fmaxf(cm, s[i]);
         }
         cm = max_xor32(max_xor16(cm));
@@ -959,8 +966,8 @@ __device__ __forceinline__ void attend_range(const DecodeArgs &a, int seq, const
         for (int i = 0; i < 4; ++i) pr[i] = s[i] == kNegInf ? 0.0f : fast_exp2(s[i] - m_h);
         // P in bf16 (the P.V A operand); the denominator uses the same
         // rounded values
-        const uint32_t p01 = f32_to_bf16_bits(pr[0]) | (f32_to_bf16_bits(pr[1]) << 16);
-        const uint32_t p23 = f32_to_bf16_bits(pr[2]) | (f32_to_bf16_bits(pr[3]) << 16);
+        const uint32_t p01 = bf16x2_rne(pr[0], pr[1]);
+        const uint32_t p23 = bf16x2_rne(pr[2], pr[3]);
         l_h = fmaf(l_h, alpha, (bf16_lo(p01) + bf16_hi(p01)) + (bf16_lo(p23) + bf16_hi(p23)));
         if (__any(n < G && alpha != 1.0f)) {
             // rescale O rows (heads 4*g4 + i) by their heads' alpha
