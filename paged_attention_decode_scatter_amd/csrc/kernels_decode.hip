@@ -1166,23 +1166,26 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
 //      sl = sh / 254: |error| <= max|q| / 64516 per element, finer than the
 //      bf16 query itself), so a score is
 //      (sh * (qh . code_t) + sl * (ql . code_t)) * kscale_t * scale.
-//   V: P.V runs on the bf16 matrix cores (v_mfma_f32_16x16x16_bf16) with
-//      the V codes as the B operand straight from registers: lane (n, g4)
-//      loads columns [C n, C n + C) (C = D / 16) of its four tokens
-//      4 g4 .. 4 g4 + 3, the rows whose probabilities its score lanes already
-//      hold, and converts code c of each to bf16 for the product of column
-//      C n + c.  No LDS tile: the chunk's chain is loads, conversions, matrix
-//      products.  Lane (n, g4) accumulates columns [C n, C n + C) of heads
-//      4 g4 .. 4 g4 + 3, so one store instruction of the outputs or partials
-//      covers a head row.  The value scale folds into the probabilities:
-//      P'_t = p_t * vscale_t (rounded to bf16 as P is); the denominator sums
-//      P'_t / vscale_t, the weights the operand carries.
+//   V: P.V runs on the bf16 matrix cores (v_mfma_f32_16x16x16_bf16).
+//      int8: each lane converts 16 codes of a row to bf16 and writes them to
+//      the wave's V tile in the bf16 kernel's layout; the product reads the
+//      tile with the same transposing LDS read.  int4: the codes are the B
+//      operand straight from registers: lane (n, g4) loads columns
+//      [C n, C n + C) (C = D / 16) of its four tokens 4 g4 .. 4 g4 + 3, the
+//      rows whose probabilities its score lanes already hold, and unpacks
+//      them into bf16 operands of 136 + code (see i4_operands); no LDS sits
+//      between the loads and the product, and lane (n, g4) accumulates
+//      columns [C n, C n + C) of heads 4 g4 .. 4 g4 + 3, so one store
+//      instruction of the outputs or partials covers a head row.  The value
+//      scale folds into the probabilities: P'_t = p_t * vscale_t (rounded to
+//      bf16 as P is); the denominator sums P'_t / vscale_t, the weights the
+//      operand carries; int4 subtracts 136 * sum(P') per head at the end.
 //   Scales: the 16 tokens of a chunk are contiguous per head (layout
 //      (block, layer, head, slot)), so lane (n, g4) loads the scales of its
 //      four tokens 4 g4 .. 4 g4 + 3 with one 16-byte load each.
-//   int4: a nibble moved to the top of its byte is the signed byte 16 * code,
-//      so both operands use the int8 paths above; the 1/16 goes into the
-//      query's scales (K) and the value scales (V).
+//   int4 K: a nibble moved to the top of its byte is the signed byte
+//      16 * code, so the int8 score path applies; the 1/16 goes into the
+//      query's scales.
 //   Codes are always finite, so rows without a live token need no zeroing:
 //   their score is -inf and their P' exactly 0.
 // ---------------------------------------------------------------------------
