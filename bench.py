@@ -511,6 +511,105 @@ DECODE_SOURCES = [os.path.join(ROOT, "paged_attention_decode_scatter_amd", "csrc
                   for f in ("kernels_decode.hip", "attn_common.h", "pagedkv_api.hip", "pkv_internal.h")]
 
 
+def torch_context(w, W, reps=3):
+    """The pages' own PyTorch forms on the same GPU, for context only (they
+    are not the library's path): over the decode batch, P1's per-block
+    loop-and-cat gather and its flattened advanced-index gather of every
+    sequence's K and V, each followed by standard attention (torch's
+    scaled_dot_product_attention per sequence, kv heads repeated for the
+    query groups, in float32: bf16 batched products on a transposed operand
+    have faulted on these GPUs); and P1's index-put scatter of the prefill
+    shape's rows at slots computed with the slot formula.  Medians of `reps`
+    runs, each bracketed by device synchronisations; tables, lengths and
+    offsets are host lists, as the loop form reads them."""
+    import time
+
+    import torch
+    import torch.nn.functional as F
+
+    dev = w.k_pool.device
+    bs, layer = w.block_size, w.layer
+    bt = w.block_tables.cpu().tolist()
+    lens = w.seq_lens.cpu().tolist()
+    offs = w.offsets.cpu().tolist()
+    G = w.num_q_heads // w.num_kv_heads
+
+    def gather_loop_cat(pool, s):
+        out, off, left = [], offs[s], lens[s]
+        for j, b in enumerate(bt[s]):
+            if left <= 0:
+                break
+            start = off if j == 0 else 0
+            take = min(bs - start, left)
+            out.append(pool[b, layer, start:start + take])
+            left -= take
+        return torch.cat(out) if out else pool[0, layer, :0]
+
+    bt_d = w.block_tables.to(torch.int64)
+
+    def gather_index(pool, s):
+        p = offs[s] + torch.arange(lens[s], device=dev)
+        return pool[bt_d[s, p // bs], layer, p % bs]
+
+    def attend(s, k, v):
+        q = w.q[s].float().unsqueeze(0).unsqueeze(2)                       # (1, Hq, 1, D)
+        kk = k.float().permute(1, 0, 2).repeat_interleave(G, 0).unsqueeze(0).contiguous()
+        vv = v.float().permute(1, 0, 2).repeat_interleave(G, 0).unsqueeze(0).contiguous()
+        return F.scaled_dot_product_attention(q, kk, vv, scale=w.scale)
+
+    def timed(fn):
+        ts = []
+        for _ in range(reps):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            fn()
+            torch.cuda.synchronize()
+            ts.append(time.perf_counter() - t0)
+        return sorted(ts)[len(ts) // 2] * 1e3
+
+    live = [s for s in range(w.num_seqs) if lens[s] > 0]
+    res = {}
+    first = {}
+    for name, g in (("loop_cat", gather_loop_cat), ("index", gather_index)):
+        kv = {}
+
+        def gather_all():
+            for s in live:
+                kv[s] = (g(w.k_pool, s), g(w.v_pool, s))
+
+        gather_all()
+        first[name] = dict(kv)
+        res[f"gather_{name}_ms"] = timed(gather_all)
+        res[f"gather_{name}_then_attention_ms"] = timed(lambda: [attend(s, *g_kv) for s in live
+                                                             for g_kv in [(g(w.k_pool, s), g(w.v_pool, s))]])
+    res["attention_only_ms"] = timed(lambda: [attend(s, *kv[s]) for s in live])
+    res["gathers_agree"] = all(torch.equal(first["loop_cat"][s][i], first["index"][s][i])
+                               for s in live for i in (0, 1))
+    del first
+    # index-put scatter on the prefill shape (8 x 1024 rows, 10 % padding)
+    pf = W.prefill(device=dev, with_pools=False)
+    seq = pf.token_seq.to(torch.int64)
+    valid = seq >= 0
+    p = pf.offsets.to(torch.int64)[seq.clamp(min=0)] + pf.token_pos.to(torch.int64)
+    blk = pf.block_tables.to(torch.int64)[seq.clamp(min=0), p // bs]
+    slot = torch.where(valid, blk * bs + p % bs, torch.full_like(blk, -1))
+    m = slot >= 0
+    rows_k, rows_v, sl = pf.k_new[m], pf.v_new[m], slot[m]
+    lay = [0]
+
+    def scatter():
+        l = lay[0] = (lay[0] + 1) % w.num_layers
+        w.k_pool[sl // bs, l, sl % bs] = rows_k
+        w.v_pool[sl // bs, l, sl % bs] = rows_v
+
+    scatter()
+    res["scatter_index_put_ms"] = timed(scatter)
+    res["what"] = ("the pages' PyTorch forms on this GPU, context only: loop-and-cat and flattened-index gather of "
+                   f"all {len(live)} decode-batch sequences (K and V), attention by torch SDPA per sequence in "
+                   f"float32, and index-put scatter of the prefill shape's rows; medians of {reps} synchronised runs")
+    return res
+
+
 def decode_source_hash():
     import hashlib
 
@@ -933,6 +1032,8 @@ def main():
         result["int8_decode"] = quant_decode(base, N, W, 8)
         log("int4 pool decode")
         result["int4_decode"] = quant_decode(base, N, W, 4)
+        log("the pages' PyTorch forms (context)")
+        result["torch_context"] = torch_context(base, W)
         log("host block manager")
         result["block_manager"] = block_manager_host(N, W)
     if not args.no_cpu_baseline:
