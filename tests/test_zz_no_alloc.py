@@ -98,3 +98,36 @@ def test_noalloc_rejects_sizes_beyond_the_scratch(dev):
     assert e.value.status == -13
     torch.cuda.synchronize()
     assert torch.isnan(out).all()
+
+
+def qbatch(dev, bits, num_seqs, max_len, seed, group=4, head_dim=128, num_kv_heads=2):
+    """A decode batch over a quantised pool (int8 or int4 codes, one float32
+    scale per token and kv head), bf16 queries."""
+    nb = (num_seqs * (max_len + 32)) // 16 + 64
+    w = W.decode_batch(device=dev, seed=seed, num_seqs=num_seqs, min_len=1, max_len=max_len,
+                       num_blocks=nb, num_layers=3, num_kv_heads=num_kv_heads,
+                       head_dim=head_dim, num_q_heads=num_kv_heads * group,
+                       dtype=torch.bfloat16, layer=1, offsets="random", with_pools=False)
+    make = W.int8_pool_tensors if bits == 8 else W.int4_pool_tensors
+    shape = (nb, 3, 16, num_kv_heads, head_dim)
+    w.k_pool = N.QuantizedPool(*make(*shape, dev, seed * 3))
+    w.v_pool = N.QuantizedPool(*make(*shape, dev, seed * 3 + 1))
+    return w
+
+
+@pytest.mark.parametrize("bits,split", [(8, 0), (8, 16), (4, 0), (4, 16)])
+def test_noalloc_quantised_pools_two_calls(dev, bits, split):
+    """Quantised pools through the scratch: the int4 partials are written by
+    buffer stores whose resource is built from the partials' address, here
+    the library's scratch."""
+    from oracle import quant as Q
+    from tests.pkv_testlib import host
+
+    dec = Q.decode_q8 if bits == 8 else Q.decode_q4
+    for w in (qbatch(dev, bits, 9, 1500, 420 + bits), qbatch(dev, bits, 4, 300, 421 + bits)):
+        got, ref = both(w, split)
+        assert same_bits(got, ref)
+        want = dec(host(w.k_pool.codes), host(w.k_pool.scales), host(w.v_pool.codes),
+                   host(w.v_pool.scales), w.layer, host(w.q), host(w.block_tables),
+                   host(w.seq_lens), host(w.offsets), w.scale)
+        assert max_abs_err(got, want) <= 2e-2
