@@ -384,9 +384,9 @@ PKV_API int paged_attn_decode_noalloc(const pkv_pool *pool, int32_t layer,
                                       int32_t split_tokens, void *out, void *stream);
 
 /*
- * paged_attn_decode_append -- one whole decode step in one launch: each
- * sequence's new token is written into the pool, then attended to with the
- * rest.  For every sequence s with seq_lens[s] > 0, the new token sits at
+ * paged_attn_decode_append -- one whole decode step in one call (one launch
+ * on a float pool): each sequence's new token is written into the pool, then
+ * attended to with the rest.  For every sequence s with seq_lens[s] > 0, the new token sits at
  * logical position seq_lens[s] - 1 (its K/V row is already counted in
  * seq_lens): its slot is block_tables[s][(p)/block_size] * block_size +
  * p % block_size with p = offsets[s] + seq_lens[s] - 1 [P2 sec. 2.2 slot
@@ -402,12 +402,15 @@ PKV_API int paged_attn_decode_noalloc(const pkv_pool *pool, int32_t layer,
  * outside [0, block_size)): it is attended as paged_attn_decode clamps it.  The write happens inside the
  * attention kernel, by the work item whose range ends the sequence, before
  * it reads that row; no other work item reads it.
+ * On a quantised pool the new rows are quantised as kv_append quantises
+ * them (one scale per row and kv head, round-half-even codes) and written
+ * by a first launch, which skips the same sequences; decode then runs as a
+ * second launch on the same stream.
  *
- *   k_new, v_new  device [num_seqs, num_kv_heads, head_dim], pool dtype,
- *                 16-byte aligned; both required
+ *   k_new, v_new  device [num_seqs, num_kv_heads, head_dim], 16-byte aligned,
+ *                 both required: the pool dtype (float pools) or bf16
+ *                 (quantised pools)
  *   everything else as for paged_attn_decode (same workspace size)
- * Float pools only (PKV_ERR_UNSUPPORTED for a quantised pool: write with
- * kv_append, then call paged_attn_decode).
  * Errors: as paged_attn_decode; PKV_ERR_NULL when k_new or v_new is NULL.
  */
 PKV_API int paged_attn_decode_append(const pkv_pool *pool, int32_t layer,

@@ -356,6 +356,17 @@ __global__ __launch_bounds__(256) void scatter_q8_kernel(ScatterQ8Args a) {
     if (live) {
         if (a.slots) {
             slot = a.slots[tok];
+        } else if (a.step_lens) {
+            const int64_t L = a.step_lens[tok];
+            const int64_t off = a.offsets[tok];
+            if (L >= 1 && L <= a.step_max_len && off >= 0 && off <= bsm) {
+                const int64_t q = off + L - 1;
+                const int64_t j = q >> a.lbs;
+                if (j < a.bt_stride) {
+                    const int32_t b = a.block_tables[tok * a.bt_stride + j];
+                    if (b >= 0) slot = ((int64_t)b << a.lbs) | (q & bsm);
+                }
+            }
         } else {
             const int32_t seq = a.token_seq[tok];
             if (seq >= 0 && seq < a.num_seqs) {

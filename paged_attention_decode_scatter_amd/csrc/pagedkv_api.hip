@@ -534,7 +534,6 @@ int decode_impl(const pkv_pool *pool, int32_t layer, const void *q, int32_t num_
         return PKV_ERR_SHAPE;
     const int group = (int)(num_q_heads / pool->num_kv_heads);
     if (!decode_supported(pool->dtype, (int)pool->head_dim, group)) return PKV_ERR_UNSUPPORTED;
-    if (k_new && is_quant(pool->dtype)) return PKV_ERR_UNSUPPORTED;
     SplitPlan spl{};
     const bool planned = use_planned(num_seqs, pool->num_kv_heads, max_seq_len, pool->block_size,
                                      pool->dtype, split_tokens, &spl);
@@ -588,6 +587,23 @@ int decode_impl(const pkv_pool *pool, int32_t layer, const void *q, int32_t num_
     if (clear_cnt && ws && cnt_bytes > 0) {
         const hipError_t e = launch_zero_words(a.ws_cnt, cnt_bytes / 4, static_cast<hipStream_t>(stream));
         if (e != hipSuccess) return status_of(e);
+    }
+    if (k_new && is_quant(pool->dtype)) {
+        // quantised pool: the new rows are quantised and written by the
+        // append kernel in decode-step mode, then decode runs over the pool
+        // (two launches on the stream; the row's quantisation needs the
+        // whole row, which the attention kernel's work item does not hold)
+        ScatterQ8Args w = q8_args(pool, a.pool, k_new, v_new, num_seqs);
+        w.block_tables = block_tables;
+        w.offsets = offsets;
+        w.step_lens = seq_lens;
+        w.step_max_len = max_seq_len;
+        w.bt_stride = bt_stride;
+        w.num_seqs = num_seqs;
+        const hipError_t e = launch_scatter_q8(w, static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return status_of(e);
+        a.k_new = nullptr;
+        a.v_new = nullptr;
     }
     return status_of(launch_decode(a, pool->dtype, (int)pool->head_dim, group,
                                    static_cast<hipStream_t>(stream)));

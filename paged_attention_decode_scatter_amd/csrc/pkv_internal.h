@@ -91,6 +91,11 @@ struct ScatterQ8Args {
     const int32_t *token_seq;
     const int32_t *token_pos;
     int64_t *slots_out;    // may be null
+    // decode-step mode (slots and token_seq null): token s is sequence s's
+    // new token, at position step_lens[s] - 1; nothing is written for a
+    // length outside [1, step_max_len] or an offset outside [0, block_size)
+    const int32_t *step_lens;
+    int32_t step_max_len;
     int64_t num_tokens;
     int64_t total_slots;
     int64_t block_stride;

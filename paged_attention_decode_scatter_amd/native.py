@@ -424,9 +424,11 @@ def paged_attn_decode_noalloc(k_pool, v_pool, layer, q, block_tables, seq_lens, 
 def paged_attn_decode_append(k_pool, v_pool, layer, q, k_new, v_new, block_tables, seq_lens,
                              offsets, max_seq_len, scale, split_tokens=0, out=None,
                              workspace=None):
-    """One decode step in one launch: write k_new[s]/v_new[s] at logical
+    """One decode step in one call: write k_new[s]/v_new[s] at logical
     position seq_lens[s] - 1 of each sequence, then paged_attn_decode over
-    its tokens (the new one included)."""
+    its tokens (the new one included).  One launch on a float pool; on a
+    quantised pool (QuantizedPool, bf16 k_new/v_new) the quantising append,
+    then decode."""
     pool = make_pool(k_pool, v_pool)
     _need(q, _row_dtype(k_pool), "q")
     _need(k_new, _row_dtype(k_pool), "k_new")

@@ -390,9 +390,8 @@ def test_make_pool_combined_layout():
 
 
 def test_quantized_pool_checks(lib):
-    """An int8 pool needs 16-byte aligned scale arrays; the entry points
-    without an int8 path refuse it; decode takes it on the split schedule
-    only."""
+    """An int8 pool needs 16-byte aligned scale arrays; prefill refuses it;
+    decode and decode with append take it (checked like a float pool)."""
     by = ctypes.byref
     I8 = 2
     sc = lib.kv_scatter
@@ -414,7 +413,11 @@ def test_quantized_pool_checks(lib):
     assert decode(pool(dtype=I8), hq=24) == UNSUP
     assert decode(pool(dtype=I8, ks=None)) == NULL
     app = lib.paged_attn_decode_append
-    assert app(by(pool(dtype=I8)), 0, A, 32, A, A, A, 8, A, A, 4, 100, 0.1, 0, A, A, 1 << 30,
+    assert app(by(pool(dtype=I8)), 0, A, 32, None, A, A, 8, A, A, 4, 100, 0.1, 0, A, A, 1 << 30,
+               None) == NULL                                # accepted: the new rows are checked
+    assert app(by(pool(dtype=I8)), 0, A, 32, A + 4, A, A, 8, A, A, 4, 100, 0.1, 0, A, A, 1 << 30,
+               None) == ALIGN
+    assert app(by(pool(dtype=I8, d=96)), 0, A, 32, A, A, A, 8, A, A, 4, 100, 0.1, 0, A, A, 1 << 30,
                None) == UNSUP
     pre = lib.paged_attn_prefill
     assert pre(by(pool(dtype=I8)), 0, A, 32, A, 64, 16, A, 8, A, A, 4, 0.1, A, None) == UNSUP
@@ -427,8 +430,8 @@ def test_quantized_pool_checks(lib):
 
 def test_int4_pool_checks(lib):
     """An int4 pool (two codes per byte) needs an even head_dim and its scale
-    arrays; decode and the copies take it like int8; prefill and the fused
-    append-and-decode refuse it."""
+    arrays; decode, decode with append and the copies take it like int8;
+    prefill refuses it."""
     by = ctypes.byref
     I4 = 3
     sc = lib.kv_scatter
@@ -445,8 +448,10 @@ def test_int4_pool_checks(lib):
     assert decode(pool(dtype=I4, d=96)) == UNSUP
     assert decode(pool(dtype=I4, vs=None)) == NULL
     app = lib.paged_attn_decode_append
-    assert app(by(pool(dtype=I4)), 0, A, 32, A, A, A, 8, A, A, 4, 100, 0.1, 0, A, A, 1 << 30,
-               None) == UNSUP
+    assert app(by(pool(dtype=I4)), 0, A, 32, A, None, A, 8, A, A, 4, 100, 0.1, 0, A, A, 1 << 30,
+               None) == NULL
+    assert app(by(pool(dtype=I4, d=63)), 0, A, 32, A, A, A, 8, A, A, 4, 100, 0.1, 0, A, A, 1 << 30,
+               None) == SHAPE
     pre = lib.paged_attn_prefill
     assert pre(by(pool(dtype=I4)), 0, A, 32, A, 64, 16, A, 8, A, A, 4, 0.1, A, None) == UNSUP
     f = lib.paged_attn_decode_schedule

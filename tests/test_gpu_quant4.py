@@ -277,3 +277,60 @@ def test_int4_partials_at_high_workspace_addresses(dev, d, group):
         assert max_abs_err(got, ref) <= TOL, want_bit
     del big
     torch.cuda.empty_cache()
+
+
+def _clone(pool):
+    return N.QuantizedPool(pool.codes.clone(), pool.scales.clone())
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("split", [0, 16])
+def test_quantised_decode_append_is_append_then_decode(dev, bits, split):
+    """paged_attn_decode_append on a quantised pool leaves the pool bit for
+    bit as kv_append writes it (each sequence's new token at position
+    len - 1) and gives paged_attn_decode's output over that pool, bit for
+    bit, within 2e-2 of the oracle.  Sequences with length 0, with no block
+    at the new position (-1), or with a length above max_seq_len write
+    nothing."""
+    make = W.int8_pool_tensors if bits == 8 else W.int4_pool_tensors
+    w = W.decode_batch(device=dev, seed=930 + bits, num_seqs=7, min_len=1, max_len=400,
+                       num_blocks=260, num_layers=3, num_kv_heads=2, head_dim=128,
+                       num_q_heads=8, dtype=torch.bfloat16, layer=1, offsets="random",
+                       block_size=16, with_pools=False)
+    shape = (260, 3, 16, 2, 128)
+    k = N.QuantizedPool(*make(*shape, dev, 931))
+    v = N.QuantizedPool(*make(*shape, dev, 932))
+    lens = host(w.seq_lens).copy()
+    offs = host(w.offsets)
+    bt = host(w.block_tables).copy()
+    mx = int(lens.max())
+    lens[0] = 0                                            # empty: nothing written
+    bt[1, (offs[1] + lens[1] - 1) // 16] = -1              # no block at the new position
+    lens[2] = mx + 5                                       # above max_seq_len: clamped, nothing written
+    w.seq_lens = torch.from_numpy(lens).to(dev)
+    w.block_tables = torch.from_numpy(bt).to(dev)
+    kn = bf16_rows(dev, w.num_seqs, 2, 128, 933, spread=False)
+    vn = bf16_rows(dev, w.num_seqs, 2, 128, 934, spread=False)
+    k2, v2 = _clone(k), _clone(v)
+    got = N.paged_attn_decode_append(k, v, w.layer, w.q, kn, vn, w.block_tables, w.seq_lens,
+                                     w.offsets, mx, w.scale, split_tokens=split,
+                                     out=torch.full_like(w.q, float("nan")))
+    write = [s for s in range(w.num_seqs) if 1 <= lens[s] <= mx]
+    ts = torch.tensor(write, dtype=torch.int32, device=dev)
+    tp = torch.tensor([int(lens[s]) - 1 for s in write], dtype=torch.int32, device=dev)
+    N.kv_append(k2, v2, w.layer, kn[ts.long()].contiguous(), vn[ts.long()].contiguous(),
+                w.block_tables, w.offsets, ts, tp)
+    ref = N.paged_attn_decode(k2, v2, w.layer, w.q, w.block_tables, w.seq_lens, w.offsets, mx,
+                              w.scale, split_tokens=split, out=torch.full_like(w.q, float("nan")))
+    torch.cuda.synchronize()
+    for a, b in ((k, k2), (v, v2)):
+        assert torch.equal(a.codes, b.codes)
+        assert torch.equal(a.scales.view(torch.int32), b.scales.view(torch.int32))
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+    # the oracle over the written pool, for the sequences whose tables cover
+    # their (clamped) lengths
+    keep = [s for s in range(w.num_seqs) if s not in (1, 2)]
+    dec = Q.decode_q8 if bits == 8 else Q.decode_q4
+    want = dec(host(k.codes), host(k.scales), host(v.codes), host(v.scales), w.layer,
+               host(w.q)[keep], bt[keep], np.minimum(lens, mx)[keep], offs[keep], w.scale)
+    assert max_abs_err(got[keep], want) <= TOL
