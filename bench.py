@@ -183,10 +183,12 @@ def quant_decode(base, N, W, bits=8, reps=32):
     """Decode over a quantised pool of the decode workloads' geometry (16384
     blocks x 32 layers x 16 x 8 x 128 codes; int8: one byte per element,
     int4: two elements per byte; one float32 scale per token and kv head)
-    with each workload's tables, lengths, offsets and bf16 queries; back to
-    back with the layer rotated.  Algorithmic bytes: every cached token's K
-    and V codes and scales once, q and out (bf16) once, the used table
-    entries, lengths and offsets."""
+    with each workload's tables, lengths, offsets and bf16 queries: decode
+    alone, and the step (paged_attn_decode_append); blocks of `reps` back-to-
+    back calls with the layer rotated, the two in turn, the upper median of
+    4 blocks each.  Algorithmic bytes: every cached token's K and V codes
+    and scales once, q and out (bf16) once, the used table entries, lengths
+    and offsets."""
     import copy
     import ctypes
 
@@ -220,19 +222,38 @@ def quant_decode(base, N, W, bits=8, reps=32):
                  w.block_tables.shape[1], P(w.seq_lens), P(w.offsets), w.num_seqs, w.max_seq_len,
                  ctypes.c_float(w.scale), 0, P(out), P(ws), ws.numel(), stream)
                 for l in range(w.num_layers)]
+        # the step: paged_attn_decode_append (the quantising append of each
+        # sequence's new row at position len - 1, then decode)
+        kn = torch.zeros((w.num_seqs, w.num_kv_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
+        W.fill_normal_(kn, 8103)
+        vn = kn.flip(0).contiguous()
+        sargs = [(ctypes.byref(pool), l, P(w.q), w.num_q_heads, P(kn), P(vn), P(w.block_tables),
+                  w.block_tables.shape[1], P(w.seq_lens), P(w.offsets), w.num_seqs, w.max_seq_len,
+                  ctypes.c_float(w.scale), 0, P(out), P(ws), ws.numel(), stream)
+                 for l in range(w.num_layers)]
         # three untimed passes over the layers (the quantised pools are
-        # freshly filled: the first passes run slower), then the timed calls
+        # freshly filled: the first passes run slower), one of the step,
+        # then blocks of decode and of the step in turn; medians of blocks
         for i in range(3 * w.num_layers):
             if lib.paged_attn_decode(*args[i % w.num_layers]):
                 raise RuntimeError(f"int{bits} paged_attn_decode failed on {name}")
+        for i in range(w.num_layers):
+            if lib.paged_attn_decode_append(*sargs[i]):
+                raise RuntimeError(f"int{bits} paged_attn_decode_append failed on {name}")
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        a.record()
-        for i in range(reps):
-            lib.paged_attn_decode(*args[i % w.num_layers])
-        b.record()
-        torch.cuda.synchronize()
-        us = a.elapsed_time(b) / reps * 1e3
+        blocks = {"decode": [], "step": []}
+        for _ in range(4):
+            for kind, f, fa in (("decode", lib.paged_attn_decode, args),
+                                ("step", lib.paged_attn_decode_append, sargs)):
+                torch.cuda.synchronize()
+                a.record()
+                for i in range(reps):
+                    f(*fa[i % w.num_layers])
+                b.record()
+                torch.cuda.synchronize()
+                blocks[kind].append(a.elapsed_time(b) / reps * 1e3)
+        us = sorted(blocks["decode"])[2]
+        step_us = sorted(blocks["step"])[2]
         g = w.num_q_heads // w.num_kv_heads
         max_splits = -(-(w.max_seq_len + w.block_size - 1) // max(sched, 1))
         label = f"decode_q8_kernel<D={w.head_dim},G={g},QB={bits}> " + (
@@ -240,8 +261,10 @@ def quant_decode(base, N, W, bits=8, reps=32):
             f"(split {sched}" + (", + reduce_kernel)" if max_splits > 16 else ")"))
         res[name] = {"us": us, "algorithmic_bytes": alg, "GB/s": alg / us / 1e3,
                      "frac": alg / us / 1e3 / HBM_PEAK_GBS, "kernel": label,
-                     "kv_bytes_vs_bf16": kv / kv_bf16}
-        del ws, out
+                     "kv_bytes_vs_bf16": kv / kv_bf16,
+                     "step_us": step_us,
+                     "step": "paged_attn_decode_append: scatter_q8_kernel (decode-step mode) then decode"}
+        del ws, out, kn, vn
     del k, v, pool
     torch.cuda.empty_cache()
     return res
