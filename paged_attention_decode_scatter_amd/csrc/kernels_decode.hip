@@ -66,7 +66,9 @@
 //   M = max_j m_j,  L = sum_j l_j 2^(m_j - M),  O = sum_j acc_j 2^(m_j - M) / L
 // by the work item that finishes last (at most 16 splits) or by a second
 // kernel (reduce_kernel).  With one split the work item normalises and
-// writes the output itself.
+// writes the output itself.  The MFMA kernels at head_dim 128 keep the acc
+// rows for the in-kernel merge in half precision, each row re-referenced by
+// a power of two (see "Split records in half precision").
 #include "attn_common.h"
 
 namespace pkv {
@@ -188,6 +190,72 @@ __device__ __forceinline__ float2 ld_dev2(const float *p) {
     const uint64_t u = __hip_atomic_load(reinterpret_cast<uint64_t *>(const_cast<float *>(p)),
                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return make_float2(__uint_as_float((uint32_t)u), __uint_as_float((uint32_t)(u >> 32)));
+}
+__device__ __forceinline__ uint64_t ld_dev_u64(const void *p) {
+    return __hip_atomic_load(reinterpret_cast<uint64_t *>(const_cast<void *>(p)), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------------------
+// Split records in half precision (the MFMA kernels at head_dim 128).
+//
+// A record is (m, l, acc) per query head: the reference max, the
+// denominator and the unnormalised accumulator row.  For any integer k,
+// (m + k, l * 2^-k, acc * 2^-k) merges exactly like (m, l, acc), since the
+// merge weighs a record's acc and l by the same 2^(m - M).  Each head row
+// takes k from its largest finite magnitude, which puts that element in
+// [2^14, 2^15): the row then fits half precision, and every element is
+// stored to within 2^-12 of the row's largest (round to nearest even).  k
+// is clamped to [-100, 110], so l * 2^-k stays a normal float (l lies in
+// [1, 2^24]).  Infinities and NaNs are carried through.  The rows then move
+// half the bytes of single precision through the split hand-over, whose
+// stores and loads are what the in-kernel merge waits on.
+// ---------------------------------------------------------------------------
+// Which records use them: those of the MFMA kernels (bf16, int8 and int4
+// pools) at head_dim 128 that the in-kernel merge reads (at most 16 splits
+// per sequence).  Records for reduce_kernel stay in single precision: half
+// precision there measured slower on 8 x 32768 tokens (bf16 175.8 -> 178.6
+// us, int8 101.0 -> 104.1 us), against 27.6 -> 26.85 us for int8 and 24.9 ->
+// 24.15 us for int4 on 32 x U[128, 2048] tokens, where the in-kernel merge
+// runs (same process).
+template <int D>
+constexpr bool kRecordsHalf = D == 128;
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t f16x2_rne(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), f16x2));
+}
+__device__ __forceinline__ f32x2 f16x2_to_f32(uint32_t u) {
+    return __builtin_convertvector(__builtin_bit_cast(f16x2, u), f32x2);
+}
+__device__ __forceinline__ float finite_abs(float x) {
+    const float a = fabsf(x);
+    return a != __builtin_huge_valf() ? a : 0.0f;
+}
+// max over the 16 lanes of a row (NaN-ignoring)
+__device__ __forceinline__ float row_max16(float x) {
+    x = fmaxf(x, dpp<0xB1>(x));   // quad_perm [1,0,3,2]
+    x = fmaxf(x, dpp<0x4E>(x));   // quad_perm [2,3,0,1]
+    x = fmaxf(x, dpp<0x141>(x));  // row_half_mirror
+    x = fmaxf(x, dpp<0x140>(x));  // row_mirror
+    return x;
+}
+// exponent shift k of a row whose largest finite magnitude is amax
+__device__ __forceinline__ int rec_shift(float amax) {
+    const int e = __builtin_amdgcn_frexp_expf(amax);  // amax = f 2^e, f in [0.5, 1); 0 for 0
+    return min(max(e - 15, -100), 110);
+}
+// (m, l) of head n (lane n of row 0) after the rows of heads 4r + i took
+// shifts k[i] in the lanes of row r: the record's re-referenced pair.
+__device__ __forceinline__ void store_ml_shifted(float *ml, const int (&k)[4], float m_h, float l_h, int G) {
+    const int lane = threadIdx.x & 63;
+    const int n = lane & 15;
+    const int src = (n >> 2) << 4;
+    const int k0 = __shfl(k[0], src), k1 = __shfl(k[1], src), k2 = __shfl(k[2], src), k3 = __shfl(k[3], src);
+    const int kk = (n & 3) == 0 ? k0 : (n & 3) == 1 ? k1 : (n & 3) == 2 ? k2 : k3;
+    if (lane < 16 && n < G) st_dev2(ml + 2 * n, m_h + (float)kk, __builtin_amdgcn_ldexpf(l_h, -kk));
 }
 
 // A sequence with no tokens attends to nothing: its output rows are zero.
@@ -578,6 +646,108 @@ __device__ void merge_records(char *out_row0, const float *ml, const float *accb
     }
 }
 
+// merge_records for half-precision records (head_dim 128, n <= 64): record
+// i's row of query head g is D halves at rec + (slot(i) * hstride + g) * D,
+// its (m, l) as above.  An 8-byte load covers two 256-byte rows: lane
+// (hh, c) holds columns 4c .. 4c+3 of head 2q + hh of each head pair q.
+// The (m, l) pairs (lane i: record i) and the first RB records' rows are
+// loaded together; with G <= 4 every fused merge (at most 16 records) is
+// one memory round trip.  Summed in record order, like merge_records.
+template <int DT, int D, int G, typename Slot>
+__device__ void merge_records_h(char *out_row0, const float *ml, const uint16_t *rec, int64_t hstride, int n,
+                                Slot slot) {
+    static_assert(D == 128, "half-precision records: head_dim 128");
+    constexpr int E = Elem<DT>::kBytes;
+    constexpr int HP = (G + 1) / 2;                              // head pairs
+    constexpr int RB = 32 / HP < 16 ? (32 / HP > 0 ? 32 / HP : 1) : 16;  // 2 registers per record and pair
+    const int lane = threadIdx.x & 63;
+    const int hh = lane >> 5;
+    const int c0 = 4 * (lane & 31);
+
+    float mv[G], lv[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        mv[g] = kNegInf;
+        lv[g] = 0.0f;
+    }
+    if (lane < n) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const float2 v = ld_dev2(ml + (slot(lane) * hstride + g) * 2);
+            mv[g] = v.x;
+            lv[g] = v.y;
+        }
+    }
+    auto load_batch = [&](int b, u32x2v (&x)[RB][HP]) {
+#pragma unroll
+        for (int k = 0; k < RB; ++k) {
+            const int64_t r = slot(min(b + k, n - 1)) * hstride;
+#pragma unroll
+            for (int q = 0; q < HP; ++q) {
+                const int g = 2 * q + hh;
+                if (b + k < n && g < G) {
+                    const uint64_t u = ld_dev_u64(rec + (r + g) * D + c0);
+                    x[k][q] = u32x2v{(uint32_t)u, (uint32_t)(u >> 32)};
+                } else {
+                    x[k][q] = u32x2v{0u, 0u};
+                }
+            }
+        }
+    };
+    u32x2v x[RB][HP];
+    load_batch(0, x);
+    float w[G], den[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        const float M = wave_max(mv[g]);
+        w[g] = mv[g] != kNegInf ? fast_exp2(mv[g] - M) : 0.0f;
+        den[g] = lane < n ? lv[g] * w[g] : 0.0f;
+    }
+    float o[HP][4];
+#pragma unroll
+    for (int q = 0; q < HP; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[q][e] = 0.0f;
+    for (int b = 0; b < n; b += RB) {
+        if (b > 0) load_batch(b, x);
+#pragma unroll
+        for (int k = 0; k < RB; ++k) {
+#pragma unroll
+            for (int q = 0; q < HP; ++q) {
+                // weight of record b + k for this lane's head: lane (b + k) % 64 holds it
+                const float wa = b + k < n ? lane_value(w[2 * q], (b + k) & 63) : 0.0f;
+                const float wb = b + k < n && 2 * q + 1 < G ? lane_value(w[2 * q + 1 < G ? 2 * q + 1 : 0], (b + k) & 63)
+                                                          : 0.0f;
+                const float wk = hh ? wb : wa;
+                const f32x2 lo = f16x2_to_f32(x[k][q][0]), hi = f16x2_to_f32(x[k][q][1]);
+                const float xv[4] = {lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[q][e] = fmaf(wk != 0.0f ? xv[e] : 0.0f, wk, o[q][e]);
+            }
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < HP; ++q) {
+        // both denominators as scalars (a select between two elements of an
+        // array became an indexed stack access)
+        const float La = wave_sum(den[2 * q]);
+        const float Lb = 2 * q + 1 < G ? wave_sum(den[2 * q + 1 < G ? 2 * q + 1 : 0]) : 0.0f;
+        const int g = 2 * q + hh;
+        if (g >= G) continue;
+        const float Lg = hh ? Lb : La;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = Lg > 0.0f ? o[q][e] / Lg : 0.0f;
+        char *dst = out_row0 + ((int64_t)g * D + c0) * E;
+        if constexpr (DT == 1) {
+            *reinterpret_cast<u32x2v *>(dst) = u32x2v{f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16),
+                                                      f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16)};
+        } else {
+            *reinterpret_cast<f32x4 *>(dst) = f32x4{v[0], v[1], v[2], v[3]};
+        }
+    }
+}
+
 // Count one finished contribution to a merge group; true, in every thread,
 // for the workgroup that completes the count of `expected`.  Partials are
 // written with device-scope stores and each wavefront waits until its
@@ -613,7 +783,9 @@ __device__ bool count_in(uint32_t *cnt, uint32_t expected) {
 // (sequence, head group); the workgroup that completes the count merges the
 // live splits j0 .. j1 of the sequence, each wavefront the G query heads of
 // its kv head.
-template <int DT, int D, int G>
+// H: the records are in half precision (see "Split records in half
+// precision").
+template <int DT, int D, int G, bool H = false>
 __device__ void finish_split(const DecodeArgs &a, const Item &it, const Range &R, int64_t S,
                              char *lds = nullptr, int lds_bytes = 0) {
     constexpr int E = Elem<DT>::kBytes;
@@ -623,9 +795,14 @@ __device__ void finish_split(const DecodeArgs &a, const Item &it, const Range &R
     const int h = it.hg * a.heads_per_wg + (threadIdx.x >> 6);
     const int64_t hq0 = (int64_t)h * G;
     const int64_t item0 = (int64_t)it.seq * a.max_splits * a.num_q_heads + hq0;
-    merge_records<DT, D, G>(a.out + ((int64_t)it.seq * a.num_q_heads + hq0) * D * E, a.ws_ml + item0 * 2,
-                            a.ws_acc + item0 * D, a.num_q_heads, j1 - j0 + 1,
-                            [=](int i) { return (int64_t)(j0 + i); }, lds, lds_bytes);
+    char *out0 = a.out + ((int64_t)it.seq * a.num_q_heads + hq0) * D * E;
+    if constexpr (H) {
+        merge_records_h<DT, D, G>(out0, a.ws_ml + item0 * 2, reinterpret_cast<const uint16_t *>(a.ws_acc) + item0 * D,
+                                  a.num_q_heads, j1 - j0 + 1, [=](int i) { return (int64_t)(j0 + i); });
+    } else {
+        merge_records<DT, D, G>(out0, a.ws_ml + item0 * 2, a.ws_acc + item0 * D, a.num_q_heads, j1 - j0 + 1,
+                                [=](int i) { return (int64_t)(j0 + i); }, lds, lds_bytes);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -786,7 +963,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
             if (c == 0) st_dev2(a.ws_ml + item * 2, m[g], l[g]);
         }
     }
-    if (a.fused_merge) finish_split<DT, D, G>(a, it, R, a.split_tokens);
+    if (a.fused_merge) finish_split<DT, D, G, false>(a, it, R, a.split_tokens);
 }
 
 // ---------------------------------------------------------------------------
@@ -1105,6 +1282,63 @@ __device__ __forceinline__ void write_partial(float *ml, float *accp, const f32x
     if (g4 == 0 && n < G) st_dev2(ml + 2 * n, m_h, l_h);
 }
 
+// The same partial as a half-precision record (head_dim 128): G rows of D
+// halves at rec, (m, l) re-referenced by each row's exponent shift.  In the
+// P.V output layout lane (n, g4) holds column n + 16*sl of heads 4*g4 ..
+// 4*g4+3, 4 bytes from the next lane's; the scaled rows are assembled in
+// the wave's free LDS (G*D floats at lds, no longer used by the attention
+// loop) and leave as 16-byte buffer stores with the device-scope cache
+// policy of st_dev (sc1: through this XCD's L2), from every lane.  Their
+// completion is awaited with everything else before the split is counted.
+template <int D, int G>
+__device__ __forceinline__ void write_partial_h(float *ml, uint16_t *rec, const f32x4 (&acc)[MfmaShape<D>::NV],
+                                                float m_h, float l_h, char *lds) {
+    static_assert(D == 128, "half-precision records: head_dim 128");
+    constexpr int NV = MfmaShape<D>::NV;
+    constexpr int NPC = G * D / 8;  // 16-byte pieces of the G half-precision rows
+    constexpr int kSC1 = 16;        // cache-policy bit sc1 of a buffer access
+    const int lane = threadIdx.x & 63;
+    const int n = lane & 15, g4 = lane >> 4;
+    int k[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float mx = 0.0f;
+#pragma unroll
+        for (int sl = 0; sl < NV; ++sl) mx = fmaxf(mx, finite_abs(acc[sl][i]));
+        k[i] = rec_shift(row_max16(mx));
+    }
+    float *t = reinterpret_cast<float *>(lds);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int hd = 4 * g4 + i;
+        if (hd < G) {
+#pragma unroll
+            for (int sl = 0; sl < NV; ++sl) t[hd * D + n + 16 * sl] = __builtin_amdgcn_ldexpf(acc[sl][i], -k[i]);
+        }
+    }
+    wave_lds_order();
+    // (readfirstlane returns a signed int: each half of the address is
+    // widened through uint32_t.)
+    const uint64_t u = reinterpret_cast<uint64_t>(rec);
+    const uint32_t ulo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)u);
+    const uint32_t uhi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+    uint16_t *base = reinterpret_cast<uint16_t *>(((uint64_t)uhi << 32) | ulo);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(base, 0, G * D * 2, 0x00020000);
+#pragma unroll
+    for (int r = 0; r < (NPC + 63) / 64; ++r) {
+        const int p = lane + 64 * r;
+        if (NPC % 64 == 0 || p < NPC) {
+            const f32x4 x0 = *reinterpret_cast<const f32x4 *>(lds + 32 * p);
+            const f32x4 x1 = *reinterpret_cast<const f32x4 *>(lds + 32 * p + 16);
+            const u32x4 v = {f16x2_rne(x0[0], x0[1]), f16x2_rne(x0[2], x0[3]), f16x2_rne(x1[0], x1[1]),
+                             f16x2_rne(x1[2], x1[3])};
+            __builtin_amdgcn_raw_buffer_store_b128(v, rs, 16 * p, 0, kSC1);
+        }
+    }
+    wave_lds_order();
+    store_ml_shifted(ml, k, m_h, l_h, G);
+}
+
 // Split schedule: one workgroup per (sequence, split, head group).
 template <int D, int G, bool UB>
 __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
@@ -1112,6 +1346,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     static_assert(G >= 1 && G <= 16, "group");
     __shared__ int32_t bt_s[kBtLds];
     __shared__ __attribute__((aligned(16))) char vtiles[4][S::NSLOT][S::VTILE];
+    static_assert(!kRecordsHalf<D> || G * D * 4 <= S::NSLOT * S::VTILE, "record assembly fits the V ring");
 
     Item it;
     Range R;
@@ -1148,9 +1383,18 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
         return;
     }
     const int64_t item0 = ((int64_t)it.seq * a.max_splits + it.split) * a.num_q_heads + (int64_t)h * G;
-    write_partial<D, G>(a.ws_ml + item0 * 2, a.ws_acc + item0 * D, acc, m_h, l_h);
-    // the wave's V ring is free now: it stages merge records
-    if (a.fused_merge) finish_split<1, D, G>(a, it, R, split, vtiles[w][0], S::NSLOT * S::VTILE);
+    // the wave's V ring is free now: it assembles the half-precision record
+    // (head_dim 128) or stages merge records (64)
+    bool half_rec = false;
+    if constexpr (kRecordsHalf<D>) {
+        half_rec = a.fused_merge;
+        if (half_rec)
+            write_partial_h<D, G>(a.ws_ml + item0 * 2, reinterpret_cast<uint16_t *>(a.ws_acc) + item0 * D, acc, m_h,
+                                  l_h, vtiles[w][0]);
+    }
+    if (!half_rec) write_partial<D, G>(a.ws_ml + item0 * 2, a.ws_acc + item0 * D, acc, m_h, l_h);
+    if (a.fused_merge)
+        finish_split<1, D, G, kRecordsHalf<D>>(a, it, R, split, vtiles[w][0], S::NSLOT * S::VTILE);
 }
 
 // ---------------------------------------------------------------------------
@@ -1648,6 +1892,45 @@ __device__ __forceinline__ void write_partial_i4(float *ml, float *accp, const f
     if (g4 == 0 && n < G) st_dev2(ml + 2 * n, m_h, l_h);
 }
 
+// int4 path, half-precision record (head_dim 128): lane (n, g4) holds the
+// C = 8 contiguous columns C*n .. C*n+7 of heads 4*g4 .. 4*g4+3, so each
+// scaled row piece is one 16-byte buffer store (sc1, as above).
+template <int D, int G>
+__device__ __forceinline__ void write_partial_i4_h(float *ml, uint16_t *rec, const f32x4 (&acc)[D / 16],
+                                                   float m_h, float l_h) {
+    static_assert(D == 128, "half-precision records: head_dim 128");
+    constexpr int C = D / 16;
+    constexpr int kSC1 = 16;  // cache-policy bit sc1 of a buffer access
+    const int lane = threadIdx.x & 63;
+    const int n = lane & 15, g4 = lane >> 4;
+    int k[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float mx = 0.0f;
+#pragma unroll
+        for (int c = 0; c < C; ++c) mx = fmaxf(mx, finite_abs(acc[c][i]));
+        k[i] = rec_shift(row_max16(mx));
+    }
+    // (readfirstlane returns a signed int: each half of the address is
+    // widened through uint32_t.)
+    const uint64_t u = reinterpret_cast<uint64_t>(rec);
+    const uint32_t ulo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)u);
+    const uint32_t uhi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+    uint16_t *base = reinterpret_cast<uint16_t *>(((uint64_t)uhi << 32) | ulo);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(base, 0, G * D * 2, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int hd = 4 * g4 + i;
+        if (hd >= G) continue;
+        float y[C];
+#pragma unroll
+        for (int c = 0; c < C; ++c) y[c] = __builtin_amdgcn_ldexpf(acc[c][i], -k[i]);
+        const u32x4 v = {f16x2_rne(y[0], y[1]), f16x2_rne(y[2], y[3]), f16x2_rne(y[4], y[5]), f16x2_rne(y[6], y[7])};
+        __builtin_amdgcn_raw_buffer_store_b128(v, rs, (hd * D + C * n) * 2, 0, kSC1);
+    }
+    store_ml_shifted(ml, k, m_h, l_h, G);
+}
+
 // QB: bits per code of the pool, 8 or 4.
 template <int D, int G, bool UB, int QB>
 // Two wavefronts per SIMD: without the hint the compiler takes 272
@@ -1658,6 +1941,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     __shared__ int32_t bt_s[kBtLds];
     // int8: the wave's V tile; both: merge records of the fused merge
     __shared__ __attribute__((aligned(16))) char vtiles[4][S::VTILE];
+    static_assert(!kRecordsHalf<D> || QB == 4 || G * D * 4 <= S::VTILE, "record assembly fits the V tile");
 
     Item it;
     Range R;
@@ -1702,20 +1986,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
             for (int c = 0; c < D / 16; ++c) acc[c][i] = fmaf(-kI4Bias, prow[i], acc[c][i]);
     }
     const int64_t item0 = ((int64_t)it.seq * a.max_splits + it.split) * a.num_q_heads + (int64_t)h * G;
+    uint16_t *rec = reinterpret_cast<uint16_t *>(a.ws_acc) + item0 * D;
     if constexpr (QB == 8) {
         if (direct) {
             write_direct<D, G>(a, it.seq, h, acc, lrow);
             return;
         }
-        write_partial<D, G>(a.ws_ml + item0 * 2, a.ws_acc + item0 * D, acc, m_h, l_h);
+        // the wave's V tile is free now
+        bool half_rec = false;
+        if constexpr (kRecordsHalf<D>) {
+            half_rec = a.fused_merge;
+            if (half_rec) write_partial_h<D, G>(a.ws_ml + item0 * 2, rec, acc, m_h, l_h, vtiles[w]);
+        }
+        if (!half_rec) write_partial<D, G>(a.ws_ml + item0 * 2, a.ws_acc + item0 * D, acc, m_h, l_h);
     } else {
         if (direct) {
             write_direct_i4<D, G>(a, it.seq, h, acc, lrow);
             return;
         }
-        write_partial_i4<D, G>(a.ws_ml + item0 * 2, a.ws_acc + item0 * D, acc, m_h, l_h);
+        bool half_rec = false;
+        if constexpr (kRecordsHalf<D>) {
+            half_rec = a.fused_merge;
+            if (half_rec) write_partial_i4_h<D, G>(a.ws_ml + item0 * 2, rec, acc, m_h, l_h);
+        }
+        if (!half_rec) write_partial_i4<D, G>(a.ws_ml + item0 * 2, a.ws_acc + item0 * D, acc, m_h, l_h);
     }
-    if (a.fused_merge) finish_split<1, D, G>(a, it, R, split, vtiles[w], S::VTILE);
+    if (a.fused_merge) finish_split<1, D, G, kRecordsHalf<D>>(a, it, R, split, vtiles[w], S::VTILE);
 }
 
 // ---------------------------------------------------------------------------
