@@ -247,16 +247,6 @@ __device__ __forceinline__ int rec_shift(float amax) {
     const int e = __builtin_amdgcn_frexp_expf(amax);  // amax = f 2^e, f in [0.5, 1); 0 for 0
     return min(max(e - 15, -100), 110);
 }
-// (m, l) of head n (lane n of row 0) after the rows of heads 4r + i took
-// shifts k[i] in the lanes of row r: the record's re-referenced pair.
-__device__ __forceinline__ void store_ml_shifted(float *ml, const int (&k)[4], float m_h, float l_h, int G) {
-    const int lane = threadIdx.x & 63;
-    const int n = lane & 15;
-    const int src = (n >> 2) << 4;
-    const int k0 = __shfl(k[0], src), k1 = __shfl(k[1], src), k2 = __shfl(k[2], src), k3 = __shfl(k[3], src);
-    const int kk = (n & 3) == 0 ? k0 : (n & 3) == 1 ? k1 : (n & 3) == 2 ? k2 : k3;
-    if (lane < 16 && n < G) st_dev2(ml + 2 * n, m_h + (float)kk, __builtin_amdgcn_ldexpf(l_h, -kk));
-}
 
 // A sequence with no tokens attends to nothing: its output rows are zero.
 // Written by the split-0 workgroup of each head group (multi-split case).
@@ -646,20 +636,24 @@ __device__ void merge_records(char *out_row0, const float *ml, const float *accb
     }
 }
 
-// merge_records for half-precision records (head_dim 128, n <= 64): record
-// i's row of query head g is D halves at rec + (slot(i) * hstride + g) * D,
-// its (m, l) as above.  An 8-byte load covers two 256-byte rows: lane
-// (hh, c) holds columns 4c .. 4c+3 of head 2q + hh of each head pair q.
-// The (m, l) pairs (lane i: record i) and the first RB records' rows are
-// loaded together; with G <= 4 every fused merge (at most 16 records) is
-// one memory round trip.  Summed in record order, like merge_records.
-template <int DT, int D, int G, typename Slot>
-__device__ void merge_records_h(char *out_row0, const float *ml, const uint16_t *rec, int64_t hstride, int n,
-                                Slot slot) {
+// merge_records for half-precision records (head_dim 128) of the in-kernel
+// merge: n <= kFusedMergeMaxSplits records, record i's row of query head g
+// at rec0 + (i * hstride + g) * D halves, its (m, l) at ml + (i * hstride +
+// g) * 2.  An 8-byte load covers two 256-byte rows: lane (hh, c) holds
+// columns 4c .. 4c+3 of head 2q + hh of each head pair q.  All
+// kFusedMergeMaxSplits slots are loaded, unrolled and without branches:
+// slot k reads record min(k, n - 1) (a scalar offset), and slots past n
+// weigh 0, their words zeroed like any zero-weight record's (as
+// merge_records does).  The (m, l) pairs (lane i: record i) and all rows
+// are loaded together: at G <= 4 the merge is one memory round trip.
+// Summed in record order, like merge_records.
+template <int DT, int D, int G>
+__device__ void merge_records_h(char *out_row0, const float *ml, const uint16_t *rec0, int64_t hstride, int n) {
     static_assert(D == 128, "half-precision records: head_dim 128");
     constexpr int E = Elem<DT>::kBytes;
-    constexpr int HP = (G + 1) / 2;                              // head pairs
-    constexpr int RB = 32 / HP < 16 ? (32 / HP > 0 ? 32 / HP : 1) : 16;  // 2 registers per record and pair
+    constexpr int HP = (G + 1) / 2;  // head pairs
+    constexpr int NS = kFusedMergeMaxSplits;
+    constexpr int kSC1 = 16;  // cache-policy bit sc1 of a buffer access (device scope, as ld_dev)
     const int lane = threadIdx.x & 63;
     const int hh = lane >> 5;
     const int c0 = 4 * (lane & 31);
@@ -673,29 +667,32 @@ __device__ void merge_records_h(char *out_row0, const float *ml, const uint16_t 
     if (lane < n) {
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-            const float2 v = ld_dev2(ml + (slot(lane) * hstride + g) * 2);
+            const float2 v = ld_dev2(ml + ((int64_t)lane * hstride + g) * 2);
             mv[g] = v.x;
             lv[g] = v.y;
         }
     }
-    auto load_batch = [&](int b, u32x2v (&x)[RB][HP]) {
+    // (readfirstlane returns a signed int: each half of the address is
+    // widened through uint32_t.)
+    const uint64_t u = reinterpret_cast<uint64_t>(rec0);
+    const uint32_t ulo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)u);
+    const uint32_t uhi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+    const uint32_t stride = (uint32_t)hstride * D * 2;  // bytes between records
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<void *>(((uint64_t)uhi << 32) | ulo), 0, (int)(n * stride), 0x00020000);
+    // lanes of a missing second head (odd G) read head G - 1 and are not stored
+    uint32_t voff[HP];
 #pragma unroll
-        for (int k = 0; k < RB; ++k) {
-            const int64_t r = slot(min(b + k, n - 1)) * hstride;
+    for (int q = 0; q < HP; ++q) voff[q] = (uint32_t)(min(2 * q + hh, G - 1) * D + c0) * 2;
+    u32x2v x[NS][HP];
 #pragma unroll
-            for (int q = 0; q < HP; ++q) {
-                const int g = 2 * q + hh;
-                if (b + k < n && g < G) {
-                    const uint64_t u = ld_dev_u64(rec + (r + g) * D + c0);
-                    x[k][q] = u32x2v{(uint32_t)u, (uint32_t)(u >> 32)};
-                } else {
-                    x[k][q] = u32x2v{0u, 0u};
-                }
-            }
-        }
-    };
-    u32x2v x[RB][HP];
-    load_batch(0, x);
+    for (int k = 0; k < NS; ++k) {
+        const uint32_t rk = (uint32_t)min(k, n - 1) * stride;
+#pragma unroll
+        for (int q = 0; q < HP; ++q)
+            x[k][q] = __builtin_bit_cast(u32x2v,
+                                         __builtin_amdgcn_raw_buffer_load_b64(rs, voff[q] + rk, 0, kSC1));
+    }
     float w[G], den[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -708,22 +705,21 @@ __device__ void merge_records_h(char *out_row0, const float *ml, const uint16_t 
     for (int q = 0; q < HP; ++q)
 #pragma unroll
         for (int e = 0; e < 4; ++e) o[q][e] = 0.0f;
-    for (int b = 0; b < n; b += RB) {
-        if (b > 0) load_batch(b, x);
 #pragma unroll
-        for (int k = 0; k < RB; ++k) {
+    for (int k = 0; k < NS; ++k) {
 #pragma unroll
-            for (int q = 0; q < HP; ++q) {
-                // weight of record b + k for this lane's head: lane (b + k) % 64 holds it
-                const float wa = b + k < n ? lane_value(w[2 * q], (b + k) & 63) : 0.0f;
-                const float wb = b + k < n && 2 * q + 1 < G ? lane_value(w[2 * q + 1 < G ? 2 * q + 1 : 0], (b + k) & 63)
-                                                          : 0.0f;
-                const float wk = hh ? wb : wa;
-                const f32x2 lo = f16x2_to_f32(x[k][q][0]), hi = f16x2_to_f32(x[k][q][1]);
-                const float xv[4] = {lo[0], lo[1], hi[0], hi[1]};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) o[q][e] = fmaf(wk != 0.0f ? xv[e] : 0.0f, wk, o[q][e]);
-            }
+        for (int q = 0; q < HP; ++q) {
+            // weight of record k for this lane's head (lane k holds it; 0 past
+            // the n records)
+            const float wa = lane_value(w[2 * q], k);
+            const float wb = 2 * q + 1 < G ? lane_value(w[2 * q + 1 < G ? 2 * q + 1 : 0], k) : 0.0f;
+            const float wk = hh ? wb : wa;
+            const bool use = wk != 0.0f;
+            const f32x2 lo = f16x2_to_f32(use ? x[k][q][0] : 0u), hi = f16x2_to_f32(use ? x[k][q][1] : 0u);
+            o[q][0] = fmaf(lo[0], wk, o[q][0]);
+            o[q][1] = fmaf(lo[1], wk, o[q][1]);
+            o[q][2] = fmaf(hi[0], wk, o[q][2]);
+            o[q][3] = fmaf(hi[1], wk, o[q][3]);
         }
     }
 #pragma unroll
@@ -797,8 +793,9 @@ __device__ void finish_split(const DecodeArgs &a, const Item &it, const Range &R
     const int64_t item0 = (int64_t)it.seq * a.max_splits * a.num_q_heads + hq0;
     char *out0 = a.out + ((int64_t)it.seq * a.num_q_heads + hq0) * D * E;
     if constexpr (H) {
-        merge_records_h<DT, D, G>(out0, a.ws_ml + item0 * 2, reinterpret_cast<const uint16_t *>(a.ws_acc) + item0 * D,
-                                  a.num_q_heads, j1 - j0 + 1, [=](int i) { return (int64_t)(j0 + i); });
+        const int64_t r0 = item0 + (int64_t)j0 * a.num_q_heads;  // record j0
+        merge_records_h<DT, D, G>(out0, a.ws_ml + r0 * 2, reinterpret_cast<const uint16_t *>(a.ws_acc) + r0 * D,
+                                  a.num_q_heads, j1 - j0 + 1);
     } else {
         merge_records<DT, D, G>(out0, a.ws_ml + item0 * 2, a.ws_acc + item0 * D, a.num_q_heads, j1 - j0 + 1,
                                 [=](int i) { return (int64_t)(j0 + i); }, lds, lds_bytes);
@@ -1282,61 +1279,87 @@ __device__ __forceinline__ void write_partial(float *ml, float *accp, const f32x
     if (g4 == 0 && n < G) st_dev2(ml + 2 * n, m_h, l_h);
 }
 
-// The same partial as a half-precision record (head_dim 128): G rows of D
-// halves at rec, (m, l) re-referenced by each row's exponent shift.  In the
-// P.V output layout lane (n, g4) holds column n + 16*sl of heads 4*g4 ..
-// 4*g4+3, 4 bytes from the next lane's; the scaled rows are assembled in
-// the wave's free LDS (G*D floats at lds, no longer used by the attention
-// loop) and leave as 16-byte buffer stores with the device-scope cache
-// policy of st_dev (sc1: through this XCD's L2), from every lane.  Their
-// completion is awaited with everything else before the split is counted.
+// Half-precision record from G unscaled acc rows (D floats each, row
+// order) in the wave's LDS at lds.  Lane p takes the 8 elements [8p, 8p+8)
+// (piece p; 16 lanes per head row, so a 16-lane row of the wavefront holds
+// one head row), finds the row's shift with one DPP pass, and stores the
+// scaled halves as one 16-byte buffer store with the device-scope cache
+// policy of st_dev (sc1: through this XCD's L2).  (m, l) of head n (lane n,
+// as the attention loop leaves them) are stored re-referenced by the
+// shift of its row.  Their completion is awaited with everything else
+// before the split is counted in.
+template <int D, int G>
+__device__ __forceinline__ void store_record_h(float *ml, uint16_t *rec, const char *lds, float m_h, float l_h) {
+    static_assert(D == 128, "half-precision records: head_dim 128");
+    constexpr int NPC = G * D / 8;       // pieces of 8 elements
+    constexpr int NR = (NPC + 63) / 64;  // pieces per lane: 1 for G <= 4, 2 for G = 8
+    constexpr int kSC1 = 16;             // cache-policy bit sc1 of a buffer access
+    const int lane = threadIdx.x & 63;
+    // (readfirstlane returns a signed int: each half of the address is
+    // widened through uint32_t.)
+    const uint64_t u = reinterpret_cast<uint64_t>(rec);
+    const uint32_t ulo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)u);
+    const uint32_t uhi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<void *>(((uint64_t)uhi << 32) | ulo), 0, G * D * 2, 0x00020000);
+    int kr[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        const int p = lane + 64 * r;
+        const bool valid = NPC % 64 == 0 || p < NPC;  // whole 16-lane rows
+        f32x4 x0 = {0.0f, 0.0f, 0.0f, 0.0f}, x1 = x0;
+        if (valid) {
+            x0 = *reinterpret_cast<const f32x4 *>(lds + 32 * p);
+            x1 = *reinterpret_cast<const f32x4 *>(lds + 32 * p + 16);
+        }
+        float mx = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fmaxf(finite_abs(x0[e]), finite_abs(x1[e])));
+        const int k = rec_shift(row_max16(mx));
+        kr[r] = k;
+        if (valid) {
+            float y[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                y[e] = __builtin_amdgcn_ldexpf(x0[e], -k);
+                y[4 + e] = __builtin_amdgcn_ldexpf(x1[e], -k);
+            }
+            const u32x4 v = {f16x2_rne(y[0], y[1]), f16x2_rne(y[2], y[3]), f16x2_rne(y[4], y[5]),
+                             f16x2_rne(y[6], y[7])};
+            __builtin_amdgcn_raw_buffer_store_b128(v, rs, 16 * p, 0, kSC1);
+        }
+    }
+    // the row of head n is lanes 16 (n % 4) .. of piece n / 4
+    const int n = lane & 15;
+    const int k0 = __shfl(kr[0], 16 * (n & 3));
+    const int k1 = __shfl(kr[NR - 1], 16 * (n & 3));
+    const int kk = (n >> 2) == 0 ? k0 : k1;
+    if (lane < 16 && n < G) st_dev2(ml + 2 * n, m_h + (float)kk, __builtin_amdgcn_ldexpf(l_h, -kk));
+}
+
+// The partial of the P.V output layout as a half-precision record (head_dim
+// 128).  Lane (n, g4) holds column n + 16*sl of heads 4*g4 .. 4*g4+3, 4
+// bytes from the next lane's: the rows are put in record order in the
+// wave's free LDS (G*D floats at lds, no longer used by the attention loop)
+// and stored from there.
 template <int D, int G>
 __device__ __forceinline__ void write_partial_h(float *ml, uint16_t *rec, const f32x4 (&acc)[MfmaShape<D>::NV],
                                                 float m_h, float l_h, char *lds) {
-    static_assert(D == 128, "half-precision records: head_dim 128");
     constexpr int NV = MfmaShape<D>::NV;
-    constexpr int NPC = G * D / 8;  // 16-byte pieces of the G half-precision rows
-    constexpr int kSC1 = 16;        // cache-policy bit sc1 of a buffer access
     const int lane = threadIdx.x & 63;
     const int n = lane & 15, g4 = lane >> 4;
-    int k[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        float mx = 0.0f;
-#pragma unroll
-        for (int sl = 0; sl < NV; ++sl) mx = fmaxf(mx, finite_abs(acc[sl][i]));
-        k[i] = rec_shift(row_max16(mx));
-    }
     float *t = reinterpret_cast<float *>(lds);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int hd = 4 * g4 + i;
         if (hd < G) {
 #pragma unroll
-            for (int sl = 0; sl < NV; ++sl) t[hd * D + n + 16 * sl] = __builtin_amdgcn_ldexpf(acc[sl][i], -k[i]);
+            for (int sl = 0; sl < NV; ++sl) t[hd * D + n + 16 * sl] = acc[sl][i];
         }
     }
     wave_lds_order();
-    // (readfirstlane returns a signed int: each half of the address is
-    // widened through uint32_t.)
-    const uint64_t u = reinterpret_cast<uint64_t>(rec);
-    const uint32_t ulo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)u);
-    const uint32_t uhi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
-    uint16_t *base = reinterpret_cast<uint16_t *>(((uint64_t)uhi << 32) | ulo);
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(base, 0, G * D * 2, 0x00020000);
-#pragma unroll
-    for (int r = 0; r < (NPC + 63) / 64; ++r) {
-        const int p = lane + 64 * r;
-        if (NPC % 64 == 0 || p < NPC) {
-            const f32x4 x0 = *reinterpret_cast<const f32x4 *>(lds + 32 * p);
-            const f32x4 x1 = *reinterpret_cast<const f32x4 *>(lds + 32 * p + 16);
-            const u32x4 v = {f16x2_rne(x0[0], x0[1]), f16x2_rne(x0[2], x0[3]), f16x2_rne(x1[0], x1[1]),
-                             f16x2_rne(x1[2], x1[3])};
-            __builtin_amdgcn_raw_buffer_store_b128(v, rs, 16 * p, 0, kSC1);
-        }
-    }
+    store_record_h<D, G>(ml, rec, lds, m_h, l_h);
     wave_lds_order();
-    store_ml_shifted(ml, k, m_h, l_h, G);
 }
 
 // Split schedule: one workgroup per (sequence, split, head group).
@@ -1893,42 +1916,28 @@ __device__ __forceinline__ void write_partial_i4(float *ml, float *accp, const f
 }
 
 // int4 path, half-precision record (head_dim 128): lane (n, g4) holds the
-// C = 8 contiguous columns C*n .. C*n+7 of heads 4*g4 .. 4*g4+3, so each
-// scaled row piece is one 16-byte buffer store (sc1, as above).
+// C = 8 contiguous columns C*n .. C*n+7 of heads 4*g4 .. 4*g4+3; the rows go
+// to the wave's free LDS (G*D floats at lds) in two 16-byte writes per
+// head and are stored from there.
 template <int D, int G>
 __device__ __forceinline__ void write_partial_i4_h(float *ml, uint16_t *rec, const f32x4 (&acc)[D / 16],
-                                                   float m_h, float l_h) {
-    static_assert(D == 128, "half-precision records: head_dim 128");
+                                                   float m_h, float l_h, char *lds) {
     constexpr int C = D / 16;
-    constexpr int kSC1 = 16;  // cache-policy bit sc1 of a buffer access
+    static_assert(C == 8, "half-precision records: head_dim 128");
     const int lane = threadIdx.x & 63;
     const int n = lane & 15, g4 = lane >> 4;
-    int k[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        float mx = 0.0f;
-#pragma unroll
-        for (int c = 0; c < C; ++c) mx = fmaxf(mx, finite_abs(acc[c][i]));
-        k[i] = rec_shift(row_max16(mx));
-    }
-    // (readfirstlane returns a signed int: each half of the address is
-    // widened through uint32_t.)
-    const uint64_t u = reinterpret_cast<uint64_t>(rec);
-    const uint32_t ulo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)u);
-    const uint32_t uhi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
-    uint16_t *base = reinterpret_cast<uint16_t *>(((uint64_t)uhi << 32) | ulo);
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(base, 0, G * D * 2, 0x00020000);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int hd = 4 * g4 + i;
-        if (hd >= G) continue;
-        float y[C];
-#pragma unroll
-        for (int c = 0; c < C; ++c) y[c] = __builtin_amdgcn_ldexpf(acc[c][i], -k[i]);
-        const u32x4 v = {f16x2_rne(y[0], y[1]), f16x2_rne(y[2], y[3]), f16x2_rne(y[4], y[5]), f16x2_rne(y[6], y[7])};
-        __builtin_amdgcn_raw_buffer_store_b128(v, rs, (hd * D + C * n) * 2, 0, kSC1);
+        if (hd < G) {
+            f32x4 *t = reinterpret_cast<f32x4 *>(lds + (hd * D + C * n) * 4);
+            t[0] = f32x4{acc[0][i], acc[1][i], acc[2][i], acc[3][i]};
+            t[1] = f32x4{acc[4][i], acc[5][i], acc[6][i], acc[7][i]};
+        }
     }
-    store_ml_shifted(ml, k, m_h, l_h, G);
+    wave_lds_order();
+    store_record_h<D, G>(ml, rec, lds, m_h, l_h);
+    wave_lds_order();
 }
 
 // QB: bits per code of the pool, 8 or 4.
@@ -1941,7 +1950,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     __shared__ int32_t bt_s[kBtLds];
     // int8: the wave's V tile; both: merge records of the fused merge
     __shared__ __attribute__((aligned(16))) char vtiles[4][S::VTILE];
-    static_assert(!kRecordsHalf<D> || QB == 4 || G * D * 4 <= S::VTILE, "record assembly fits the V tile");
+    static_assert(!kRecordsHalf<D> || G * D * 4 <= S::VTILE, "record assembly fits the V tile");
 
     Item it;
     Range R;
@@ -2007,7 +2016,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
         bool half_rec = false;
         if constexpr (kRecordsHalf<D>) {
             half_rec = a.fused_merge;
-            if (half_rec) write_partial_i4_h<D, G>(a.ws_ml + item0 * 2, rec, acc, m_h, l_h);
+            if (half_rec) write_partial_i4_h<D, G>(a.ws_ml + item0 * 2, rec, acc, m_h, l_h, vtiles[w]);
         }
         if (!half_rec) write_partial_i4<D, G>(a.ws_ml + item0 * 2, a.ws_acc + item0 * D, acc, m_h, l_h);
     }
