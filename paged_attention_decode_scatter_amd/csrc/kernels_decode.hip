@@ -640,13 +640,15 @@ __device__ void merge_records(char *out_row0, const float *ml, const float *accb
 // merge: n <= kFusedMergeMaxSplits records, record i's row of query head g
 // at rec0 + (i * hstride + g) * D halves, its (m, l) at ml + (i * hstride +
 // g) * 2.  An 8-byte load covers two 256-byte rows: lane (hh, c) holds
-// columns 4c .. 4c+3 of head 2q + hh of each head pair q.  All
-// kFusedMergeMaxSplits slots are loaded, unrolled and without branches:
-// slot k reads record min(k, n - 1) (a scalar offset), and slots past n
-// weigh 0, their words zeroed like any zero-weight record's (as
-// merge_records does).  The (m, l) pairs (lane i: record i) and all rows
+// columns 4c .. 4c+3 of head 2q + hh of each head pair q.  The
+// kFusedMergeMaxSplits slots are unrolled in groups of 4; a group past the
+// n records is skipped whole.  Slot k reads record min(k, n - 1) (a scalar
+// offset), and slots past n weigh 0, their words zeroed like any
+// zero-weight record's (as merge_records does).  The (m, l) pairs (lane i: record i) and all rows
 // are loaded together: at G <= 4 the merge is one memory round trip.
 // Summed in record order, like merge_records.
+constexpr int kMergeGroup = 4;
+
 template <int DT, int D, int G>
 __device__ void merge_records_h(char *out_row0, const float *ml, const uint16_t *rec0, int64_t hstride, int n) {
     static_assert(D == 128, "half-precision records: head_dim 128");
@@ -684,14 +686,21 @@ __device__ void merge_records_h(char *out_row0, const float *ml, const uint16_t 
     uint32_t voff[HP];
 #pragma unroll
     for (int q = 0; q < HP; ++q) voff[q] = (uint32_t)(min(2 * q + hh, G - 1) * D + c0) * 2;
+    // slots in groups of kMergeGroup: a group past the n records is neither
+    // loaded nor summed (one wave-uniform test on n per group)
+    const int nu = __builtin_amdgcn_readfirstlane(n);
     u32x2v x[NS][HP];
 #pragma unroll
-    for (int k = 0; k < NS; ++k) {
-        const uint32_t rk = (uint32_t)min(k, n - 1) * stride;
+    for (int k0 = 0; k0 < NS; k0 += kMergeGroup) {
+        if (k0 >= nu) break;
 #pragma unroll
-        for (int q = 0; q < HP; ++q)
-            x[k][q] = __builtin_bit_cast(u32x2v,
-                                         __builtin_amdgcn_raw_buffer_load_b64(rs, voff[q] + rk, 0, kSC1));
+        for (int k = k0; k < k0 + kMergeGroup; ++k) {
+            const uint32_t rk = (uint32_t)min(k, nu - 1) * stride;
+#pragma unroll
+            for (int q = 0; q < HP; ++q)
+                x[k][q] = __builtin_bit_cast(u32x2v,
+                                             __builtin_amdgcn_raw_buffer_load_b64(rs, voff[q] + rk, 0, kSC1));
+        }
     }
     float w[G], den[G];
 #pragma unroll
@@ -707,6 +716,7 @@ __device__ void merge_records_h(char *out_row0, const float *ml, const uint16_t 
         for (int e = 0; e < 4; ++e) o[q][e] = 0.0f;
 #pragma unroll
     for (int k = 0; k < NS; ++k) {
+        if (k % kMergeGroup == 0 && k >= nu) break;
 #pragma unroll
         for (int q = 0; q < HP; ++q) {
             // weight of record k for this lane's head (lane k holds it; 0 past
