@@ -725,11 +725,13 @@ __device__ void merge_records_h(char *out_row0, const float *ml, const uint16_t 
             const float wb = 2 * q + 1 < G ? lane_value(w[2 * q + 1 < G ? 2 * q + 1 : 0], k) : 0.0f;
             const float wk = hh ? wb : wa;
             const bool use = wk != 0.0f;
-            const f32x2 lo = f16x2_to_f32(use ? x[k][q][0] : 0u), hi = f16x2_to_f32(use ? x[k][q][1] : 0u);
-            o[q][0] = fmaf(lo[0], wk, o[q][0]);
-            o[q][1] = fmaf(lo[1], wk, o[q][1]);
-            o[q][2] = fmaf(hi[0], wk, o[q][2]);
-            o[q][3] = fmaf(hi[1], wk, o[q][3]);
+            // each half widened inside the fma (v_fma_mix_f32)
+            const f16x2 lo = __builtin_bit_cast(f16x2, use ? x[k][q][0] : 0u);
+            const f16x2 hi = __builtin_bit_cast(f16x2, use ? x[k][q][1] : 0u);
+            o[q][0] = fmaf((float)lo[0], wk, o[q][0]);
+            o[q][1] = fmaf((float)lo[1], wk, o[q][1]);
+            o[q][2] = fmaf((float)hi[0], wk, o[q][2]);
+            o[q][3] = fmaf((float)hi[1], wk, o[q][3]);
         }
     }
 #pragma unroll
