@@ -286,6 +286,19 @@ __device__ __forceinline__ float max_xor32(float v) {
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// v of lane l plus v of lane l ^ 16 (then ^ 32), with the row swaps; both
+// lanes of a pair get the same bits.
+__device__ __forceinline__ float sum_xor16(float v) {
+    const unsigned u = __float_as_uint(v);
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+    const unsigned u = __float_as_uint(v);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Max and sum over all 64 lanes, the result in every lane: DPP within rows
 // of 16 lanes, then the row swaps across rows -- all VALU, no LDS permute
 // round trip in the chain.  Every lane gets the same bits (each step

@@ -1248,8 +1248,7 @@ __device__ __forceinline__ void attend_range(const DecodeArgs &a, int seq, const
 // in l_h), and lrow[i] = l of head 4*g4 + i, the head of this lane's O row i.
 __device__ __forceinline__ void head_denominators(float &l_h, float (&lrow)[4]) {
     const int g4 = (threadIdx.x & 63) >> 4;
-    l_h += __shfl_xor(l_h, 16);
-    l_h += __shfl_xor(l_h, 32);
+    l_h = sum_xor32(sum_xor16(l_h));  // row swaps: no LDS permute round trip
 #pragma unroll
     for (int i = 0; i < 4; ++i) lrow[i] = __shfl(l_h, 4 * g4 + i);
 }
@@ -1341,12 +1340,15 @@ __device__ __forceinline__ void store_record_h(float *ml, uint16_t *rec, const c
             __builtin_amdgcn_raw_buffer_store_b128(v, rs, 16 * p, 0, kSC1);
         }
     }
-    // the row of head n is lanes 16 (n % 4) .. of piece n / 4
-    const int n = lane & 15;
-    const int k0 = __shfl(kr[0], 16 * (n & 3));
-    const int k1 = __shfl(kr[NR - 1], 16 * (n & 3));
-    const int kk = (n >> 2) == 0 ? k0 : k1;
-    if (lane < 16 && n < G) st_dev2(ml + 2 * n, m_h + (float)kk, __builtin_amdgcn_ldexpf(l_h, -kk));
+    // the row of head g is lanes 16 (g % 4) .. of piece g / 4; lane g takes
+    // its shift by readlane (no LDS permute round trip)
+    int kk = 0;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        const int kg = __builtin_amdgcn_readlane(kr[g >> 2 < NR ? g >> 2 : 0], 16 * (g & 3));
+        kk = lane == g ? kg : kk;
+    }
+    if (lane < G) st_dev2(ml + 2 * lane, m_h + (float)kk, __builtin_amdgcn_ldexpf(l_h, -kk));
 }
 
 // The partial of the P.V output layout as a half-precision record (head_dim
@@ -1541,8 +1543,7 @@ __device__ __forceinline__ void quantize_q(const QRaw<D> &raw, Q8Query<D> &qq) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(x[j][e]));
     }
-    amax = fmaxf(amax, __shfl_xor(amax, 16));
-    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    amax = max_xor32(max_xor16(amax));
     const float sh = amax / 127.0f;
     const float sl = sh / 254.0f;
     const float ih = amax > 0.0f ? 1.0f / sh : 0.0f;
