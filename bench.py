@@ -846,11 +846,16 @@ def decode_config(name, w, N, args, lib, stream, headline):
 
     # The first passes over the freshly filled 32 GiB pool run slower
     # (long context: ~350 us per step over the first 20 steps, settled at
-    # ~170 us from about step 100 on): three untimed passes over the 32
-    # layers precede the warmup steps.
-    for i in range(3 * L):
-        step(i)
-    torch.cuda.synchronize()
+    # ~170 us from about step 100 on), and a short step settles in time
+    # rather than in calls: untimed passes over the 32 layers, at least
+    # three and at least 0.2 s of them, precede the warmup steps.
+    t0 = time.perf_counter()
+    passes = 0
+    while passes < 3 or time.perf_counter() - t0 < 0.2:
+        for i in range(L):
+            step(i)
+        torch.cuda.synchronize()
+        passes += 1
     log(f"{name}: timing {args.steps} steps ({kernel})")
     ms_step = back_to_back(step)
     # per-call event pairs around the same calls
