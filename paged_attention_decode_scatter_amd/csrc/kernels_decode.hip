@@ -213,11 +213,12 @@ __device__ __forceinline__ uint64_t ld_dev_u64(const void *p) {
 // ---------------------------------------------------------------------------
 // Which records use them: those of the MFMA kernels (bf16, int8 and int4
 // pools) at head_dim 128 that the in-kernel merge reads (at most 16 splits
-// per sequence).  Records for reduce_kernel stay in single precision: half
-// precision there measured slower on 8 x 32768 tokens (bf16 175.8 -> 178.6
-// us, int8 101.0 -> 104.1 us), against 27.6 -> 26.85 us for int8 and 24.9 ->
-// 24.15 us for int4 on 32 x U[128, 2048] tokens, where the in-kernel merge
-// runs (same process).
+// per sequence).  With the writer and merge below, the 32 x U[128, 2048]
+// token batch, where the in-kernel merge runs, went from 38.8 to 36.1 us
+// (bf16) and from 28.5 to 25.4 us (int8) against single-precision records.
+// Records for reduce_kernel stay in single precision: half precision there
+// measured slower on 8 x 32768 tokens (bf16 175.8 -> 178.6 us, int8 101.0
+// -> 104.1 us, same process).
 template <int D>
 constexpr bool kRecordsHalf = D == 128;
 
@@ -468,11 +469,12 @@ __device__ bool plan_item(const DecodeArgs &a, int32_t *scratch, Item &it, Range
 // result does not depend on which workgroup runs the merge.  Up to 64
 // records, the (m, l) pairs (lane i: record i) and the first RB records'
 // acc rows are loaded together, so the merge costs one memory round trip
-// per RB records.  Measured on the decode batch (13 records, per-workgroup
-// timestamps): the merge takes 3.6 us from the count to its stores, of which
-// about 2.5 us is the wait for the device-scope loads; the cross-lane max and
-// sum as DPP + row swaps, and staged records read four at a time, took it
-// from 4.3 us.
+// per RB records.  (This single-precision merge serves head_dim 64 and the
+// fp32 pools; at head_dim 128 the MFMA kernels use merge_records_h.  When
+// it served the decode batch, 13 records, per-workgroup timestamps put it
+// at 3.6 us from the count to its stores, about 2.5 us of that the wait for
+// the device-scope loads; the cross-lane max and sum as DPP + row swaps,
+// and staged records read four at a time, had taken it from 4.3 us.)
 template <int DT, int D, int G, typename Slot>
 __device__ void merge_records(char *out_row0, const float *ml, const float *accb, int64_t hstride,
                               int n, Slot slot, char *lds = nullptr, int lds_bytes = 0) {
@@ -644,9 +646,9 @@ __device__ void merge_records(char *out_row0, const float *ml, const float *accb
 // kFusedMergeMaxSplits slots are unrolled in groups of 4; a group past the
 // n records is skipped whole.  Slot k reads record min(k, n - 1) (a scalar
 // offset), and slots past n weigh 0, their words zeroed like any
-// zero-weight record's (as merge_records does).  The (m, l) pairs (lane i: record i) and all rows
-// are loaded together: at G <= 4 the merge is one memory round trip.
-// Summed in record order, like merge_records.
+// zero-weight record's (as merge_records does).  The (m, l) pairs (lane i:
+// record i) and all rows are loaded together: at G <= 4 the merge is one
+// memory round trip.  Summed in record order, like merge_records.
 constexpr int kMergeGroup = 4;
 
 template <int DT, int D, int G>

@@ -136,7 +136,8 @@ struct DecodeArgs {
     const char *v_new;     //   (position seq_len - 1); null for plain decode
     uint32_t *ws_cnt;      // [num_seqs][head_groups] finished splits (zero between calls)
     float *ws_ml;          // [num_seqs][max_splits][num_q_heads][2]  (m, l)
-    float *ws_acc;         // [num_seqs][max_splits][num_q_heads][head_dim]
+    float *ws_acc;         // [num_seqs][max_splits][num_q_heads][head_dim] floats; the in-kernel merge's
+                           // records of the MFMA kernels at head_dim 128 use the same indexing in halves
     float scale_log2;      // scale * log2(e): scores live in the exp2 domain
     int32_t bt_stride;
     int32_t num_seqs;
