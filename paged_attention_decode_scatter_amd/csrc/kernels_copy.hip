@@ -339,6 +339,24 @@ __device__ __forceinline__ float piece_amax(u32x4 x) {
     return m;
 }
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// max over each aligned group of W lanes (W = 8 or 16), in every lane of the
+// group: DPP within the 16-lane rows (quad swaps, then the half-row and row
+// mirrors), no LDS permute round trips
+template <int W>
+__device__ __forceinline__ float group_max(float x) {
+    static_assert(W == 8 || W == 16, "group");
+    x = fmaxf(x, dpp_f<0xB1>(x));   // quad_perm [1,0,3,2]
+    x = fmaxf(x, dpp_f<0x4E>(x));   // quad_perm [2,3,0,1]
+    x = fmaxf(x, dpp_f<0x141>(x));  // row_half_mirror
+    if constexpr (W == 16) x = fmaxf(x, dpp_f<0x140>(x));  // row_mirror
+    return x;
+}
+
 template <int D, int QB>
 __global__ __launch_bounds__(256) void scatter_q8_kernel(ScatterQ8Args a) {
     constexpr int Q = QB == 8 ? 127 : 7;
@@ -390,12 +408,7 @@ __global__ __launch_bounds__(256) void scatter_q8_kernel(ScatterQ8Args a) {
         if (has_v) vx = ld16_stream(a.v_src + src);
     }
     // every lane takes part in the reductions (rows are LPH-lane aligned)
-    float km = piece_amax(kx), vm = piece_amax(vx);
-#pragma unroll
-    for (int m = 1; m < LPH; m <<= 1) {
-        km = fmaxf(km, __shfl_xor(km, m));
-        vm = fmaxf(vm, __shfl_xor(vm, m));
-    }
+    const float km = group_max<LPH>(piece_amax(kx)), vm = group_max<LPH>(piece_amax(vx));
     if (!ok) return;
     const float ks = __fdiv_rn(km, (float)Q), vs = __fdiv_rn(vm, (float)Q);
     const int64_t b = slot >> a.lbs, r = slot & bsm;

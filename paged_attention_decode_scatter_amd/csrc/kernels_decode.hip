@@ -2100,8 +2100,7 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(DecodeArgs a) {
     float M = t < ns && live(t) ? ml0.x : kNegInf;
     for (int j = t + kReduceThreads; j < ns; j += kReduceThreads)
         if (live(j)) M = fmaxf(M, a.ws_ml[(item0 + j * step) * 2]);
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) M = fmaxf(M, __shfl_xor(M, m));
+    M = wave_max(M);  // DPP and row swaps: no LDS permute round trips
     if ((t & 63) == 0) red_s[wv] = M;
     __syncthreads();
     M = red_s[0];
@@ -2119,8 +2118,7 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(DecodeArgs a) {
         }
         w_s[j] = wj;
     }
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) den += __shfl_xor(den, m);
+    den = wave_sum(den);  // a fixed order, so the result does not depend on timing
     if ((t & 63) == 0) red_s[wv] = den;
     __syncthreads();
     den = red_s[0];
