@@ -1507,66 +1507,107 @@ __device__ __forceinline__ uint32_t q8_code(float x, float inv) {
     return (uint32_t)(int32_t)fminf(fmaxf(__builtin_rintf(x * inv), -127.0f), 127.0f) & 0xffu;
 }
 
-// The bf16 query elements the lane quantises: lane (n, g4), elements
-// D/4 g4 .. D/4 (g4 + 1) of head n, as D/64 pairs of 16-byte loads.  Issued
-// before the first chunk's loads, so the quantisation runs while those are
-// in flight.  Lanes of heads n >= G load head G - 1 (no branch around the
-// loads, whose merge would wait for them) and quantise zeros.
-template <int D>
+// The bf16 query elements a lane quantises: lane l takes the 8 elements
+// 8 (l % LPH) .. +8 of head l / LPH + HPP i in pass i (LPH = D / 8 lanes per
+// head, HPP = 64 / LPH heads per pass), so every lane works and a head's
+// lanes are one aligned group of a 16-lane row.  Issued before the first
+// chunk's loads, so the quantisation runs while those are in flight.
+// Lanes past the G heads load head G - 1 (no branch around the loads,
+// whose merge would wait for them) and quantise zeros.
+template <int D, int G>
 struct QRaw {
-    u32x4 w[D / 64][2];
+    static constexpr int LPH = D / 8, HPP = 64 / LPH, NPASS = (G + HPP - 1) / HPP;
+    u32x4 w[NPASS];
 };
 
 template <int D, int G>
-__device__ __forceinline__ void load_q_raw(const DecodeArgs &a, int seq, int h, QRaw<D> &raw) {
+__device__ __forceinline__ void load_q_raw(const DecodeArgs &a, int seq, int h, QRaw<D, G> &raw) {
+    using R = QRaw<D, G>;
     const int lane = threadIdx.x & 63;
-    const int n = lane & 15, g4 = lane >> 4;
-    const int hn = n < G ? n : G - 1;
-    const char *qp = a.q + (((int64_t)seq * a.num_q_heads + (int64_t)h * G + hn) * D + (D / 4) * g4) * 2;
 #pragma unroll
-    for (int j = 0; j < D / 64; ++j)
-#pragma unroll
-        for (int c = 0; c < 2; ++c) raw.w[j][c] = ld16(qp + 32 * j + 16 * c);
+    for (int i = 0; i < R::NPASS; ++i) {
+        const int r = lane / R::LPH + R::HPP * i;
+        const int hr = r < G ? r : G - 1;
+        raw.w[i] = ld16(a.q + (((int64_t)seq * a.num_q_heads + (int64_t)h * G + hr) * D + 8 * (lane % R::LPH)) * 2);
+    }
 }
 
+// max over each aligned group of W lanes (W = 8 or 16) of a 16-lane row, in
+// every lane of the group (DPP: quad swaps, then the half-row and row mirrors)
+template <int W>
+__device__ __forceinline__ float lane_group_max(float x) {
+    static_assert(W == 8 || W == 16, "group");
+    x = fmaxf(x, dpp<0xB1>(x));   // quad_perm [1,0,3,2]
+    x = fmaxf(x, dpp<0x4E>(x));   // quad_perm [2,3,0,1]
+    x = fmaxf(x, dpp<0x141>(x));  // row_half_mirror
+    if constexpr (W == 16) x = fmaxf(x, dpp<0x140>(x));  // row_mirror
+    return x;
+}
+
+// The query in two int8 parts per head: q ~ qh sh + ql sl, sh = max|q| / 127,
+// sl = sh / 254, codes round-half-even.  Each lane codes its 8 elements,
+// the codes go to the wave's LDS at lds (2 G D + 8 G bytes, free until the
+// first chunk is computed) in row order with the heads' (sh, sl), and each
+// lane (n, g4) then reads its operand fragment of head n: elements D/4 g4 +
+// 16 j .. +16 for step j (heads n >= G: zeros).
 // QB = 4 (int4 pool): the K codes arrive as 16 * code with each group of 8
 // elements in the order 0, 2, 4, 6, 1, 3, 5, 7 (i4_even16 / i4_odd16), so
 // the query's codes take the same order and its scales carry the 1/16.
 template <int D, int G, int QB>
-__device__ __forceinline__ void quantize_q(const QRaw<D> &raw, Q8Query<D> &qq) {
+__device__ __forceinline__ void quantize_q(const QRaw<D, G> &raw, Q8Query<D> &qq, char *lds) {
+    using R = QRaw<D, G>;
     constexpr int KL = D / 64;
-    const bool live = (threadIdx.x & 15) < G;
-    float x[KL][16];
-    float amax = 0.0f;
+    const int lane = threadIdx.x & 63;
+    char *hib = lds;
+    char *lob = lds + G * D;
+    float *scl = reinterpret_cast<float *>(lds + 2 * G * D);
 #pragma unroll
-    for (int j = 0; j < KL; ++j) {
+    for (int i = 0; i < R::NPASS; ++i) {
+        const int r = lane / R::LPH + R::HPP * i;
+        const bool live = r < G;
+        float x[8];
+        unpack16<1>(live ? raw.w[i] : u32x4{0, 0, 0, 0}, x);
+        float am = 0.0f;
 #pragma unroll
-        for (int c = 0; c < 2; ++c) unpack16<1>(live ? raw.w[j][c] : u32x4{0, 0, 0, 0}, &x[j][8 * c]);
+        for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(x[e]));
+        const float amax = lane_group_max<R::LPH>(am);
+        const float sh = amax / 127.0f;
+        const float sl = sh / 254.0f;
+        const float ih = amax > 0.0f ? 1.0f / sh : 0.0f;
+        const float il = amax > 0.0f ? 1.0f / sl : 0.0f;
+        uint32_t wh[2] = {0, 0}, wl[2] = {0, 0};
 #pragma unroll
-        for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(x[j][e]));
-    }
-    amax = max_xor32(max_xor16(amax));
-    const float sh = amax / 127.0f;
-    const float sl = sh / 254.0f;
-    const float ih = amax > 0.0f ? 1.0f / sh : 0.0f;
-    const float il = amax > 0.0f ? 1.0f / sl : 0.0f;
-#pragma unroll
-    for (int j = 0; j < KL; ++j) {
-        uint32_t wh[4] = {0, 0, 0, 0}, wl[4] = {0, 0, 0, 0};
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const uint32_t ch = q8_code(x[j][e], ih);
-            const float r = x[j][e] - (float)(int32_t)(int8_t)ch * sh;
-            const int wi = QB == 8 ? e >> 2 : ((e >> 3) << 1) | (e & 1);
-            const int bi = QB == 8 ? e & 3 : (e & 7) >> 1;
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t ch = q8_code(x[e], ih);
+            const float rr = x[e] - (float)(int32_t)(int8_t)ch * sh;
+            const int wi = QB == 8 ? e >> 2 : e & 1;
+            const int bi = QB == 8 ? e & 3 : e >> 1;
             wh[wi] |= ch << (8 * bi);
-            wl[wi] |= q8_code(r, il) << (8 * bi);
+            wl[wi] |= q8_code(rr, il) << (8 * bi);
         }
-        qq.hi[j] = v4i32{(int)wh[0], (int)wh[1], (int)wh[2], (int)wh[3]};
-        qq.lo[j] = v4i32{(int)wl[0], (int)wl[1], (int)wl[2], (int)wl[3]};
+        if (live) {
+            const int off = r * D + 8 * (lane % R::LPH);
+            *reinterpret_cast<u32x2 *>(hib + off) = u32x2{wh[0], wh[1]};
+            *reinterpret_cast<u32x2 *>(lob + off) = u32x2{wl[0], wl[1]};
+            if (lane % R::LPH == 0) *reinterpret_cast<f32x2 *>(scl + 2 * r) = f32x2{sh, sl};
+        }
     }
-    qq.sh = QB == 8 ? sh : sh * 0.0625f;
-    qq.sl = QB == 8 ? sl : sl * 0.0625f;
+    wave_lds_order();
+    const int n = lane & 15, g4 = lane >> 4;
+    const int hn = n < G ? n : G - 1;
+    const v4i32 z = {0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < KL; ++j) {
+        const int off = hn * D + (D / 4) * g4 + 16 * j;
+        const v4i32 h4 = *reinterpret_cast<const v4i32 *>(hib + off);
+        const v4i32 l4 = *reinterpret_cast<const v4i32 *>(lob + off);
+        qq.hi[j] = n < G ? h4 : z;
+        qq.lo[j] = n < G ? l4 : z;
+    }
+    const f32x2 s2 = *reinterpret_cast<const f32x2 *>(scl + 2 * hn);
+    qq.sh = QB == 8 ? s2[0] : s2[0] * 0.0625f;
+    qq.sl = QB == 8 ? s2[1] : s2[1] * 0.0625f;
+    wave_lds_order();  // the tile is written again once the first chunk is computed
 }
 
 // int8 V: two codes (bytes sh/8, sh/8 + 1 of w) as a bf16 pair, the high
@@ -1626,7 +1667,7 @@ struct QSlot<D, 4> {
 template <int D, int G, bool UB, int QB>
 __device__ __forceinline__ void attend_range_q8(const DecodeArgs &a, const Range &R, int64_t jb0,
                                                 const int32_t *bt_s, char *vt, int h,
-                                                const QRaw<D> &qraw, float &m_h,
+                                                const QRaw<D, G> &qraw, float &m_h,
                                                 float &l_h, float &p_h, f32x4 (&acc)[D / 16]) {
     using S = MfmaShape<D>;
     using Slot = QSlot<D, QB>;
@@ -1855,7 +1896,7 @@ __device__ __forceinline__ void attend_range_q8(const DecodeArgs &a, const Range
         // the query's int8 parts, while the first chunk is in flight (the
         // barrier keeps the scheduler from hoisting them above its loads)
         __builtin_amdgcn_sched_barrier(0);
-        quantize_q<D, G, QB>(qraw, qq);
+        quantize_q<D, G, QB>(qraw, qq, vt);
         bool done = false;
         for (int64_t pc = first; !done;) {
 #pragma unroll
@@ -1966,6 +2007,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     // int8: the wave's V tile; both: merge records of the fused merge
     __shared__ __attribute__((aligned(16))) char vtiles[4][S::VTILE];
     static_assert(!kRecordsHalf<D> || G * D * 4 <= S::VTILE, "record assembly fits the V tile");
+    static_assert(2 * G * D + 8 * G <= S::VTILE, "the query's codes fit the V tile");
 
     Item it;
     Range R;
@@ -1987,7 +2029,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     const int h = it.hg * a.heads_per_wg + w;
     // the query's loads go out before the table's, so it has arrived by the
     // time the first chunk's loads are issued and its quantisation starts
-    QRaw<D> qraw;
+    QRaw<D, G> qraw;
     load_q_raw<D, G>(a, it.seq, h, qraw);
     const int64_t jb0 = stage_table(a, it.seq, R, bt_s);
     float m_h = kNegInf;
