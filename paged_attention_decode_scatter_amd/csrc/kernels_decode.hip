@@ -2234,20 +2234,64 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(DecodeArgs a) {
     }
 }
 
-template <int DT, int D, int G>
-static hipError_t run_decode(const DecodeArgs &a, hipStream_t s) {
+// ---------------------------------------------------------------------------
+// The bf16 decode kernels at head_dim 128 with G <= 4 are built in a second
+// object from this file (PKV_DECODE_ACC_VGPR, compiled with LLVM's
+// -amdgpu-mfma-vgpr-form), so their matrix-core accumulators live in
+// ordinary vector registers.  In AGPRs they are copied into vector
+// registers at the top of each ring iteration, some of which pending ring
+// loads still target, so the compiler waited for every load in flight
+// there.  Same process: decode batch 35.45 -> 34.95 us, prefix sharing 89.6
+// -> 88.9 us.  The G = 8 kernel (long context) measured slower that way
+// (167.3 -> 169.4 us) and stays in this object.  Each kernel instance is
+// built in exactly one of the two objects.
+// ---------------------------------------------------------------------------
+template <int D, int G>
+constexpr bool kAccVgprObject = D == 128 && G <= 4;
+
+hipError_t launch_decode_mfma_vgpr(const DecodeArgs &a, int group, hipStream_t s);
+
+template <int D, int G>
+static void launch_decode_mfma(const DecodeArgs &a, hipStream_t s) {
     const dim3 block(64 * a.heads_per_wg);
     const int64_t nwg = a.plan > 0 ? a.plan : (int64_t)a.head_groups * a.max_splits * a.num_seqs;
     const dim3 grid((unsigned)nwg);
-    if constexpr (DT == 1) {
-        if (a.pool.lbs >= 4)
-            hipLaunchKernelGGL((decode_mfma_kernel<D, G, true>), grid, block, 0, s, a);
-        else
-            hipLaunchKernelGGL((decode_mfma_kernel<D, G, false>), grid, block, 0, s, a);
-    } else {
-        hipLaunchKernelGGL((decode_valu_kernel<DT, D, G>), grid, block, 0, s, a);
+    if (a.pool.lbs >= 4)
+        hipLaunchKernelGGL((decode_mfma_kernel<D, G, true>), grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL((decode_mfma_kernel<D, G, false>), grid, block, 0, s, a);
+}
+
+#ifdef PKV_DECODE_ACC_VGPR
+
+hipError_t launch_decode_mfma_vgpr(const DecodeArgs &a, int group, hipStream_t s) {
+    switch (group) {
+        case 1: launch_decode_mfma<128, 1>(a, s); break;
+        case 2: launch_decode_mfma<128, 2>(a, s); break;
+        case 4: launch_decode_mfma<128, 4>(a, s); break;
+        default: return hipErrorInvalidValue;
     }
-    hipError_t e = hipGetLastError();
+    return hipGetLastError();
+}
+
+#else
+
+template <int DT, int D, int G>
+static hipError_t run_decode(const DecodeArgs &a, hipStream_t s) {
+    hipError_t e = hipSuccess;
+    if constexpr (DT == 1) {
+        if constexpr (kAccVgprObject<D, G>) {
+            e = launch_decode_mfma_vgpr(a, G, s);
+        } else {
+            launch_decode_mfma<D, G>(a, s);
+            e = hipGetLastError();
+        }
+    } else {
+        const dim3 block(64 * a.heads_per_wg);
+        const int64_t nwg = a.plan > 0 ? a.plan : (int64_t)a.head_groups * a.max_splits * a.num_seqs;
+        hipLaunchKernelGGL((decode_valu_kernel<DT, D, G>), dim3((unsigned)nwg), block, 0, s, a);
+        e = hipGetLastError();
+    }
     if (e != hipSuccess || a.max_splits == 1 || a.fused_merge) return e;
     hipLaunchKernelGGL((reduce_kernel<DT, D>), dim3((unsigned)((int64_t)a.num_seqs * a.num_q_heads)),
                        dim3(kReduceThreads), (size_t)a.max_splits * sizeof(float), s, a);
@@ -2327,5 +2371,7 @@ hipError_t launch_decode(const DecodeArgs &a, int dtype, int head_dim, int group
     if (!f) return hipErrorInvalidValue;
     return f(a, s);
 }
+
+#endif  // PKV_DECODE_ACC_VGPR
 
 }  // namespace pkv
