@@ -530,8 +530,11 @@ def block_ops(w_dec, N, pairs=64, sets=4, reps=32, swap_blocks=64, swap_reps=6):
     }
 
 
+# the files that decide the decode kernels' code: their sources and the
+# build (which compiles part of them with their own flags)
 DECODE_SOURCES = [os.path.join(ROOT, "paged_attention_decode_scatter_amd", "csrc", f)
-                  for f in ("kernels_decode.hip", "attn_common.h", "pagedkv_api.hip", "pkv_internal.h")]
+                  for f in ("kernels_decode.hip", "attn_common.h", "pagedkv_api.hip", "pkv_internal.h")] + [
+    os.path.join(ROOT, "paged_attention_decode_scatter_amd", "build.py")]
 
 
 def torch_context(w, W, reps=3):
